@@ -1,0 +1,125 @@
+"""Simulator of the GPU expert cache: one LRU over (layer, expert) entries.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What the pages fix:
+* a cache entry is one whole logical (layer, expert) pair, with the same
+  mapping on the CPU and the GPU (FreeToken rtx 4090 page, "Cómo funciona la
+  jerarquía de memoria MoE");
+* one LRU policy is shared by all MoE layers, keeps recently selected experts
+  resident for later tokens, and follows the router rather than being frozen
+  at start-up (FreeToken linux page, "Cómo gestiona FreeToken la memoria MoE";
+  rtx 4090 page, same section);
+* hits run from the GPU copy; misses are filled into the GPU cache over PCIe
+  from pinned host memory (FreeToken quantization page, "Cómo se desplazan los
+  pesos MoE cuantizados por la memoria");
+* the miss rate is misses over routed expert reads (FreeToken 290b model page,
+  "Limitaciones, lista de comprobación y buenas prácticas", metrics table).
+
+The order of updates inside one (layer, step) is not on the pages.  Reading
+taken here:  the needed set S is the distinct experts of the step's routing,
+visited in ascending expert id.  Phase 1 refreshes every hit.  Phase 2 gives
+each miss the least recently used slot not holding a member of S (empty slots
+have stamp 0, so they fill lowest index first; stamps are otherwise unique).
+Refreshing all hits before any eviction means a miss can never evict an expert
+that the same step still needs.  If |S| exceeds the capacity the step is
+refused and nothing changes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+class CapacityError(RuntimeError):
+    """More distinct experts in one step than the cache has slots."""
+
+
+@dataclass(frozen=True)
+class Event:
+    expert: int
+    hit: bool
+    slot: int
+    evicted: tuple | None   # (layer, expert) that left the slot, or None
+
+    def short(self) -> str:
+        s = f"{self.expert}:{'H' if self.hit else 'M'}@{self.slot}"
+        if self.evicted is not None:
+            s += f" evicts {self.evicted[0]}/{self.evicted[1]}"
+        return s
+
+
+class ExpertLRU:
+    """Slot table (layer, expert) -> slot with least-recently-used replacement."""
+
+    def __init__(self, n_layers: int, n_experts: int, capacity: int):
+        if n_layers < 1 or n_experts < 1 or capacity < 1:
+            raise ValueError("n_layers, n_experts and capacity must be positive")
+        self.n_layers = n_layers
+        self.n_experts = n_experts
+        self.capacity = capacity
+        self.owner: list[tuple | None] = [None] * capacity   # slot -> key
+        self.stamp: list[int] = [0] * capacity                # 0 = never used
+        self.where: dict[tuple, int] = {}                     # key -> slot
+        self.clock = 0
+        self.accesses = 0
+        self.hits = 0
+        self.misses = 0
+        self.evictions = 0
+
+    def lookup(self, layer: int, expert: int) -> int:
+        """Slot holding (layer, expert), or -1."""
+        return self.where.get((layer, expert), -1)
+
+    def step(self, layer: int, ids) -> list[Event]:
+        """Serve one layer of one step; returns events in ascending expert id."""
+        if not 0 <= layer < self.n_layers:
+            raise ValueError("layer out of range")
+        needed = sorted({int(e) for e in list(ids)})
+        for e in needed:
+            if not 0 <= e < self.n_experts:
+                raise ValueError("expert id out of range")
+        if len(needed) > self.capacity:
+            raise CapacityError(f"{len(needed)} distinct experts > {self.capacity} slots")
+
+        events: dict[int, Event] = {}
+        # Phase 1: every hit becomes most recently used, ascending expert id.
+        for e in needed:
+            s = self.where.get((layer, e))
+            if s is not None:
+                self.clock += 1
+                self.stamp[s] = self.clock
+                events[e] = Event(e, True, s, None)
+        # Phase 2: each miss takes the least recently used slot that holds no
+        # member of the needed set, ascending expert id.
+        needed_keys = {(layer, e) for e in needed}
+        for e in needed:
+            if e in events:
+                continue
+            best = None
+            for s in range(self.capacity):
+                if self.owner[s] in needed_keys:
+                    continue
+                if best is None or (self.stamp[s], s) < (self.stamp[best], best):
+                    best = s
+            evicted = self.owner[best]
+            if evicted is not None:
+                del self.where[evicted]
+                self.evictions += 1
+            self.owner[best] = (layer, e)
+            self.where[(layer, e)] = best
+            self.clock += 1
+            self.stamp[best] = self.clock
+            events[e] = Event(e, False, best, evicted)
+
+        self.accesses += len(needed)
+        self.hits += sum(1 for ev in events.values() if ev.hit)
+        self.misses += sum(1 for ev in events.values() if not ev.hit)
+        return [events[e] for e in needed]
+
+    def slot_of_expert(self, layer: int) -> list[int]:
+        """Slot of every expert of ``layer`` (-1 if not resident)."""
+        return [self.where.get((layer, e), -1) for e in range(self.n_experts)]
+
+    def stats(self) -> dict:
+        return dict(accesses=self.accesses, hits=self.hits, misses=self.misses,
+                    evictions=self.evictions)

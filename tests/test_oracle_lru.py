@@ -1,0 +1,151 @@
+"""Pins of the LRU simulator: hand traces, textbook LRU, compulsory misses, capacity."""
+import os
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+
+from oracle.lru import CapacityError, ExpertLRU
+from oracle import policy
+
+
+def _traces(golden_dir):
+    traces = []
+    cur = None
+    with open(os.path.join(golden_dir, "lru_traces.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            w = line.split()
+            if w[0] == "trace":
+                kv = dict(p.split("=") for p in w[2:])
+                cur = dict(name=w[1], C=int(kv["capacity"]), L=int(kv["layers"]),
+                           E=int(kv["experts"]), steps=[])
+            elif w[0] == "step":
+                left, right = line.split(":", 1)
+                lw = left.split()
+                ids = [int(v) for v in lw[5].split(",")]
+                evs = []
+                for tok in right.split():
+                    e, rest = tok.split(":")
+                    hm, rest = rest.split("@")
+                    if "/" in rest:
+                        s, ev = rest.split("/")
+                        evl, eve = ev.split(".")
+                        evicted = (int(evl), int(eve))
+                    else:
+                        s, evicted = rest, None
+                    evs.append((int(e), hm == "H", int(s), evicted))
+                cur["steps"].append((int(lw[1]), int(lw[3]), ids, evs))
+            elif w[0] == "totals":
+                cur["totals"] = {k: int(v) for k, v in (p.split("=") for p in w[1:])}
+            elif w[0] == "stamps":
+                cur["stamps"] = [int(v) for v in w[1].split(",")]
+            elif w[0] == "end":
+                traces.append(cur)
+    return traces
+
+
+def test_hand_traced_sequences(golden_dir):
+    traces = _traces(golden_dir)
+    assert [t["name"] for t in traces] == ["A", "B", "C", "D"]
+    for tr in traces:
+        lru = ExpertLRU(tr["L"], tr["E"], tr["C"])
+        for step, layer, ids, want in tr["steps"]:
+            got = lru.step(layer, ids)
+            assert [(e.expert, e.hit, e.slot, e.evicted) for e in got] == want, (tr["name"], step, layer)
+        assert lru.stats() == tr["totals"], tr["name"]
+        assert lru.stamp == tr["stamps"], tr["name"]
+
+
+def _textbook_lru(accesses, capacity):
+    """Plain LRU with an OrderedDict; returns the hit/miss sequence."""
+    od = OrderedDict()
+    seq = []
+    for key in accesses:
+        if key in od:
+            od.move_to_end(key)
+            seq.append(True)
+        else:
+            if len(od) >= capacity:
+                od.popitem(last=False)
+            od[key] = True
+            seq.append(False)
+    return seq
+
+
+def test_single_access_steps_equal_textbook_lru():
+    rng = np.random.default_rng(0)
+    for trial in range(20):
+        L, E, C = int(rng.integers(1, 4)), int(rng.integers(2, 12)), int(rng.integers(1, 8))
+        acc = [(int(rng.integers(L)), int(rng.integers(E))) for _ in range(300)]
+        lru = ExpertLRU(L, E, C)
+        ours = [lru.step(l, [e])[0].hit for l, e in acc]
+        assert ours == _textbook_lru(acc, C)
+        # resident set equals the textbook's most recent distinct keys
+        recent = list(OrderedDict.fromkeys(reversed(acc)))[:C]
+        assert set(lru.where) == set(recent)
+
+
+def test_compulsory_misses_only_when_everything_fits():
+    rng = np.random.default_rng(1)
+    L, E, k = 3, 10, 3
+    lru = ExpertLRU(L, E, L * E)
+    seen = set()
+    for s in range(50):
+        for l in range(L):
+            ids = rng.choice(E, size=k, replace=False)
+            for ev in lru.step(l, ids):
+                assert ev.hit == ((l, ev.expert) in seen)
+                seen.add((l, ev.expert))
+    assert lru.misses == len(seen) and lru.evictions == 0
+
+
+def test_capacity_error_leaves_state_unchanged():
+    lru = ExpertLRU(1, 8, 2)
+    lru.step(0, [1])
+    before = (list(lru.owner), list(lru.stamp), dict(lru.where), lru.clock, lru.stats())
+    with pytest.raises(CapacityError):
+        lru.step(0, [2, 3, 4])
+    assert (list(lru.owner), list(lru.stamp), dict(lru.where), lru.clock, lru.stats()) == before
+
+
+def test_a_miss_never_evicts_a_needed_expert():
+    rng = np.random.default_rng(2)
+    lru = ExpertLRU(2, 16, 6)
+    for s in range(400):
+        l = int(rng.integers(2))
+        ids = rng.choice(16, size=int(rng.integers(1, 7)), replace=False)
+        evs = lru.step(l, ids)
+        needed = {(l, int(e)) for e in ids}
+        for ev in evs:
+            assert ev.evicted not in needed
+        assert all(lru.lookup(l, int(e)) >= 0 for e in ids)
+        slots = [ev.slot for ev in evs]
+        assert len(set(slots)) == len(slots)
+
+
+def test_miss_split_policy():
+    # equal bandwidths split evenly; monotone in B_p, antitone in B_h; clamped to 0..m
+    assert policy.miss_split(6, 1.0, 1.0) == 3
+    assert policy.miss_split(0, 5.0, 1.0) == 0
+    assert policy.miss_split(4, 1.0, 0.0) == 4 and policy.miss_split(4, 0.0, 1.0) == 0
+    prev = -1
+    for bp in [0.1, 0.5, 1, 2, 5, 10, 50]:
+        q = policy.miss_split(10, bp, 5.0)
+        assert 0 <= q <= 10 and q >= prev
+        prev = q
+    # the integer split sits next to the balance point q* = m Bp / (Bp + Bh)
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        m = int(rng.integers(1, 40))
+        bp, bh = float(rng.uniform(0.1, 100)), float(rng.uniform(0.1, 100))
+        q = policy.miss_split(m, bp, bh)
+        assert abs(q - m * bp / (bp + bh)) < 1.0
+    # worked example: m=7, Bp=3, Bh=11 -> q*=1.5; q=1 gives max(1/3, 6/11)=0.545,
+    # q=2 gives max(2/3, 5/11)=0.667, so one fill
+    assert policy.miss_split(7, 3.0, 11.0) == 1
+    # m=7, Bp=Bh: q=3 -> max(3, 4)=4, q=4 -> max(4, 3)=4: tie -> more fills
+    assert policy.miss_split(7, 1.0, 1.0) == 4
+    assert policy.split_misses([9, 2, 5], 1.0, 1.0) == ([2, 5], [9])
