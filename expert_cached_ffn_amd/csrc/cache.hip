@@ -1,0 +1,398 @@
+// The GPU expert cache: one LRU over (layer, expert) entries shared by every
+// MoE layer, with its slot table updated on the device and misses filled from
+// pinned host memory on a side stream.
+//
+// What the pages fix: GPU memory holds a cache of whole (layer, expert)
+// entries while host memory holds the full expert set, the source of truth
+// (FreeToken linux page, "Cómo gestiona FreeToken la memoria MoE", memory-tier
+// table; FreeToken rtx 4090 page, "Cómo funciona la jerarquía de memoria
+// MoE"); one LRU policy is shared across the MoE layers and follows the
+// router's recent choices (same sections); hits run on the GPU and misses are
+// moved over PCIe from pinned host memory (FreeToken quantization page, "Cómo
+// se desplazan los pesos MoE cuantizados por la memoria").
+//
+// Update order inside one (layer, step), fixed here because the pages do not:
+// distinct experts ascending; all hits refreshed first; then each miss takes
+// the least recently used slot that holds no member of the step's set (empty
+// slots are oldest, lowest index first).
+#include <algorithm>
+#include <vector>
+
+#include "ft_internal.hpp"
+
+namespace ft {
+
+constexpr int kLruThreads = 1024;
+constexpr int kLruMaxE = 4096;
+constexpr int kLruMaxC = 65536;
+
+enum { LRU_OK = 0, LRU_CAPACITY = 1, LRU_BAD_ID = 2 };
+
+// Written by the LRU kernel into pinned host memory; read by the host after
+// the kernel has finished.
+struct LruResult {
+  int32_t status;
+  int32_t n_needed, n_hits, n_misses, n_evictions;
+  int32_t pad[3];
+  int32_t ev[kLruMaxE][4];  // expert, hit, slot, evicted key (-1 none); ascending expert
+};
+
+struct LruState {
+  int32_t *map;      // [L*E] key -> slot or -1
+  int32_t *owner;    // [C]   slot -> key or -1
+  uint64_t *stamp;   // [C]   last use (0 = never)
+  uint64_t *clock;   // [1]
+};
+
+__device__ __forceinline__ bool older(uint64_t sa, int a, uint64_t sb, int b) {
+  return sa < sb || (sa == sb && a < b);
+}
+
+// One workgroup.  Stamps and the slot table are read before any of them is
+// written (selection works on the pre-step stamps plus an LDS "taken" bitmap),
+// so the kernel never reads its own global writes.
+__global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int layer, const int32_t *__restrict__ ids,
+                                                              int R, int E, int C,
+                                                              int32_t *__restrict__ slot_of_expert,
+                                                              LruResult *__restrict__ res) {
+  __shared__ int s_need[kLruMaxE];     // flag, then position in the needed list
+  __shared__ int s_list[kLruMaxE];     // needed experts, ascending
+  __shared__ int s_slot[kLruMaxE];     // slot of needed expert i (hit) or victim (miss)
+  __shared__ int s_evk[kLruMaxE];      // evicted key of needed expert i, or -1
+  __shared__ uint8_t s_hit[kLruMaxE];  // needed expert i was resident
+  __shared__ int s_out[kLruMaxE];      // slot table of the layer after the step
+  __shared__ uint32_t s_taken[kLruMaxC / 32];
+  __shared__ int s_wcnt[kLruThreads / 64 + 1];
+  __shared__ uint64_t s_wst[kLruThreads / 64];
+  __shared__ int s_wsl[kLruThreads / 64];
+  __shared__ int s_bad, s_n, s_h;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NW = kLruThreads / 64;
+  const int32_t *lmap = st.map + int64_t(layer) * E;
+  if (tid == 0) s_bad = 0;
+  for (int e = tid; e < E; e += kLruThreads) {
+    s_need[e] = 0;
+    s_out[e] = lmap[e];
+  }
+  for (int w = tid; w < (C + 31) / 32; w += kLruThreads) s_taken[w] = 0u;
+  __syncthreads();
+  for (int r = tid; r < R; r += kLruThreads) {
+    const int e = ids[r];
+    if (e < 0 || e >= E) s_bad = 1;
+    else s_need[e] = 1;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) res->status = LRU_BAD_ID;
+    return;
+  }
+  // Compact the needed set in ascending expert order.
+  int base = 0;
+  for (int c0 = 0; c0 < E; c0 += kLruThreads) {
+    const int e = c0 + tid;
+    const bool f = e < E && s_need[e];
+    const uint64_t m = __ballot(f);
+    if (lane == 0) s_wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = base;
+    for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+    if (f) s_list[before + __popcll(m & ((uint64_t(1) << lane) - 1))] = e;
+    for (int w = 0; w < NW; ++w) base += s_wcnt[w];
+    __syncthreads();
+  }
+  const int n = base;
+  if (n > C) {
+    if (tid == 0) {
+      res->n_needed = n;
+      res->status = LRU_CAPACITY;
+    }
+    return;
+  }
+  // Phase 1: hits, in list order; hit rank decides the new stamp.
+  const uint64_t clk = *st.clock;
+  int hbase = 0;
+  for (int c0 = 0; c0 < n; c0 += kLruThreads) {
+    const int i = c0 + tid;
+    int s = -1;
+    if (i < n) {
+      s = lmap[s_list[i]];
+      s_slot[i] = s;
+      s_evk[i] = -1;
+      s_hit[i] = s >= 0 ? 1 : 0;
+      if (s >= 0) atomicOr(&s_taken[s >> 5], 1u << (s & 31));
+    }
+    const bool hit = i < n && s >= 0;
+    const uint64_t m = __ballot(hit);
+    if (lane == 0) s_wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = hbase;
+    for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+    if (hit) st.stamp[s] = clk + uint64_t(before + __popcll(m & ((uint64_t(1) << lane) - 1))) + 1;
+    for (int w = 0; w < NW; ++w) hbase += s_wcnt[w];
+    __syncthreads();
+  }
+  const int h = hbase;
+  // Phase 2: misses in ascending expert order, each taking the oldest free slot.
+  int mi = 0;
+  for (int i = 0; i < n; ++i) {
+    if (s_hit[i]) continue;  // uniform across the workgroup
+    uint64_t bs = ~uint64_t(0);
+    int bsl = 0x7fffffff;
+    for (int s = tid; s < C; s += kLruThreads) {
+      if (s_taken[s >> 5] & (1u << (s & 31))) continue;
+      const uint64_t v = st.stamp[s];
+      if (older(v, s, bs, bsl)) {
+        bs = v;
+        bsl = s;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t ov = __shfl_xor(bs, off);
+      const int os = __shfl_xor(bsl, off);
+      if (older(ov, os, bs, bsl)) {
+        bs = ov;
+        bsl = os;
+      }
+    }
+    if (lane == 0) {
+      s_wst[wave] = bs;
+      s_wsl[wave] = bsl;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t b = s_wst[0];
+      int v = s_wsl[0];
+      for (int w = 1; w < NW; ++w)
+        if (older(s_wst[w], s_wsl[w], b, v)) {
+          b = s_wst[w];
+          v = s_wsl[w];
+        }
+      s_slot[i] = v;
+      s_taken[v >> 5] |= 1u << (v & 31);
+      s_evk[i] = st.owner[v];
+    }
+    __syncthreads();
+    ++mi;
+  }
+  // Apply: stamps of victims, owner / map updates, the layer's slot table.
+  int n_evict = 0;
+  if (tid == 0) {
+    int j = 0;
+    for (int i = 0; i < n; ++i) {
+      const int e = s_list[i];
+      const int s = s_slot[i];
+      const bool hit = s_hit[i] != 0;
+      res->ev[i][0] = e;
+      res->ev[i][1] = hit ? 1 : 0;
+      res->ev[i][2] = s;
+      res->ev[i][3] = s_evk[i];
+      if (!hit) {
+        st.stamp[s] = clk + uint64_t(h + j) + 1;
+        ++j;
+        const int ek = s_evk[i];
+        if (ek >= 0) {
+          st.map[ek] = -1;
+          ++n_evict;
+          if (ek / E == layer) s_out[ek % E] = -1;
+        }
+        st.owner[s] = layer * E + e;
+        st.map[int64_t(layer) * E + e] = s;
+        s_out[e] = s;
+      }
+    }
+    *st.clock = clk + uint64_t(n);
+    res->n_needed = n;
+    res->n_hits = h;
+    res->n_misses = mi;
+    res->n_evictions = n_evict;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kLruThreads) slot_of_expert[e] = s_out[e];
+  if (tid == 0) {
+    __threadfence_system();
+    res->status = LRU_OK;
+  }
+}
+
+}  // namespace ft
+
+using namespace ft;
+
+struct ft_expert_cache {
+  ft_expert_layout L;
+  int n_layers, E, C;
+  uint8_t *pool;
+  const uint8_t *bank;
+  hipStream_t copy_stream;
+  LruState st;
+  void *dev_state;
+  LruResult *res_host;   // pinned
+  LruResult *res_dev;    // its device address
+  hipEvent_t ev_lru, ev_copy;
+  int device;
+  ft_cache_stats stats;
+  std::vector<ft_cache_event> log;
+  std::vector<int32_t> map_mirror;
+};
+
+extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n_layers, int32_t E,
+                                            int32_t capacity, void *slot_pool, const void *host_bank,
+                                            hipStream_t copy_stream, ft_expert_cache **out) {
+  FT_REQUIRE(out != nullptr, "ft_expert_cache_create: out is NULL");
+  *out = nullptr;
+  FT_REQUIRE(L != nullptr && L->expert_bytes > 0, "ft_expert_cache_create: layout not initialised");
+  FT_REQUIRE(n_layers >= 1 && E >= 1 && capacity >= 1, "ft_expert_cache_create: sizes must be positive");
+  FT_SUPPORTED(E <= kLruMaxE, "ft_expert_cache_create: E > 4096");
+  FT_SUPPORTED(capacity <= kLruMaxC, "ft_expert_cache_create: capacity > 65536");
+  FT_SUPPORTED(int64_t(n_layers) * E <= (int64_t(1) << 20), "ft_expert_cache_create: n_layers*E > 2^20");
+  FT_REQUIRE(slot_pool != nullptr && host_bank != nullptr, "ft_expert_cache_create: NULL pool or bank");
+  FT_REQUIRE(aligned(slot_pool, 256) && L->expert_bytes % 256 == 0,
+             "ft_expert_cache_create: slot_pool must be 256-byte aligned");
+  FT_REQUIRE(copy_stream != nullptr, "ft_expert_cache_create: copy_stream must not be the NULL stream");
+  hipPointerAttribute_t pa{}, ba{};
+  FT_HIP(hipPointerGetAttributes(&pa, slot_pool));
+  FT_REQUIRE(pa.type == hipMemoryTypeDevice, "ft_expert_cache_create: slot_pool is not device memory");
+  if (hipPointerGetAttributes(&ba, host_bank) != hipSuccess || ba.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(FT_EINVAL, "ft_expert_cache_create: host_bank is not pinned host memory (use hipHostMalloc)");
+  }
+  int dev = 0;
+  FT_HIP(hipGetDevice(&dev));
+
+  ft_expert_cache *c = new ft_expert_cache();
+  c->L = *L;
+  c->n_layers = n_layers;
+  c->E = E;
+  c->C = capacity;
+  c->pool = static_cast<uint8_t *>(slot_pool);
+  c->bank = static_cast<const uint8_t *>(host_bank);
+  c->copy_stream = copy_stream;
+  c->device = dev;
+  const size_t keys = size_t(n_layers) * E;
+  const size_t bytes = keys * 4 + size_t(capacity) * 4 + size_t(capacity) * 8 + 64;
+  auto cleanup = [&](ft_status st, const std::string &msg) {
+    if (c->dev_state) (void)hipFree(c->dev_state);
+    if (c->res_host) (void)hipHostFree(c->res_host);
+    if (c->ev_lru) (void)hipEventDestroy(c->ev_lru);
+    if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+    delete c;
+    return fail(st, msg);
+  };
+  if (hipMalloc(&c->dev_state, bytes) != hipSuccess) return cleanup(FT_EHIP, "ft_expert_cache_create: hipMalloc failed");
+  uint8_t *p = static_cast<uint8_t *>(c->dev_state);
+  c->st.stamp = reinterpret_cast<uint64_t *>(p);
+  c->st.clock = reinterpret_cast<uint64_t *>(p + size_t(capacity) * 8);
+  c->st.map = reinterpret_cast<int32_t *>(p + size_t(capacity) * 8 + 64);
+  c->st.owner = c->st.map + keys;
+  // Empty cache: every key unmapped, every slot free with stamp 0, clock 0.
+  if (hipMemset(c->st.map, 0xff, (keys + capacity) * 4) != hipSuccess ||
+      hipMemset(c->dev_state, 0, size_t(capacity) * 8 + 64) != hipSuccess)
+    return cleanup(FT_EHIP, "ft_expert_cache_create: hipMemset failed");
+  if (hipHostMalloc(reinterpret_cast<void **>(&c->res_host), sizeof(LruResult), hipHostMallocMapped) != hipSuccess)
+    return cleanup(FT_EHIP, "ft_expert_cache_create: hipHostMalloc failed");
+  if (hipHostGetDevicePointer(reinterpret_cast<void **>(&c->res_dev), c->res_host, 0) != hipSuccess)
+    return cleanup(FT_EHIP, "ft_expert_cache_create: hipHostGetDevicePointer failed");
+  if (hipEventCreateWithFlags(&c->ev_lru, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming) != hipSuccess)
+    return cleanup(FT_EHIP, "ft_expert_cache_create: hipEventCreate failed");
+  if (hipDeviceSynchronize() != hipSuccess) return cleanup(FT_EHIP, "ft_expert_cache_create: sync failed");
+  c->stats = ft_cache_stats{};
+  c->map_mirror.assign(keys, -1);
+  *out = c;
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids, int32_t T,
+                                          int32_t k, int32_t *slot_of_expert, hipStream_t compute_stream) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_step: cache is NULL");
+  FT_REQUIRE(layer >= 0 && layer < c->n_layers, "ft_expert_cache_step: layer out of range");
+  FT_REQUIRE(T >= 0 && k >= 1, "ft_expert_cache_step: need T >= 0, k >= 1");
+  FT_REQUIRE(int64_t(T) * k < (int64_t(1) << 31), "ft_expert_cache_step: T*k too large");
+  FT_REQUIRE(slot_of_expert != nullptr, "ft_expert_cache_step: slot_of_expert is NULL");
+  const int R = T * k;
+  FT_REQUIRE(R == 0 || topk_ids != nullptr, "ft_expert_cache_step: topk_ids is NULL");
+  c->res_host->status = -1;
+  hipLaunchKernelGGL(lru_step_kernel, dim3(1), dim3(kLruThreads), 0, compute_stream, c->st, layer, topk_ids, R,
+                     c->E, c->C, slot_of_expert, c->res_dev);
+  FT_LAUNCHED("lru_step_kernel");
+  FT_HIP(hipEventRecord(c->ev_lru, compute_stream));
+  FT_HIP(hipEventSynchronize(c->ev_lru));
+  const LruResult &r = *c->res_host;
+  if (r.status == LRU_BAD_ID) return fail(FT_EINVAL, "ft_expert_cache_step: expert id out of range");
+  if (r.status == LRU_CAPACITY)
+    return fail(FT_ECAPACITY, "ft_expert_cache_step: " + std::to_string(r.n_needed) + " distinct experts > " +
+                                  std::to_string(c->C) + " slots");
+  if (r.status != LRU_OK) return fail(FT_EHIP, "ft_expert_cache_step: LRU kernel did not report");
+  const int32_t step = int32_t(c->stats.steps);
+  const uint64_t eb = c->L.expert_bytes;
+  int fills = 0;
+  for (int i = 0; i < r.n_needed; ++i) {
+    const int e = r.ev[i][0], hit = r.ev[i][1], s = r.ev[i][2], ek = r.ev[i][3];
+    c->log.push_back(ft_cache_event{step, layer, e, hit, s, ek});
+    if (hit) continue;
+    if (ek >= 0) c->map_mirror[size_t(ek)] = -1;
+    c->map_mirror[size_t(layer) * c->E + e] = s;
+    const uint8_t *src = c->bank + (uint64_t(layer) * c->E + e) * eb;
+    FT_HIP(hipMemcpyAsync(c->pool + uint64_t(s) * eb, src, eb, hipMemcpyHostToDevice, c->copy_stream));
+    ++fills;
+  }
+  if (fills) {
+    FT_HIP(hipEventRecord(c->ev_copy, c->copy_stream));
+    FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_copy, 0));
+  }
+  c->stats.accesses += uint64_t(r.n_needed);
+  c->stats.hits += uint64_t(r.n_hits);
+  c->stats.misses += uint64_t(r.n_misses);
+  c->stats.evictions += uint64_t(r.n_evictions);
+  c->stats.bytes_h2d += uint64_t(fills) * eb;
+  c->stats.steps += 1;
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_stats(const ft_expert_cache *c, ft_cache_stats *out) {
+  FT_REQUIRE(c != nullptr && out != nullptr, "ft_expert_cache_stats: NULL argument");
+  *out = c->stats;
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_trace(const ft_expert_cache *c, void *host_buf, size_t bytes, size_t *needed) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_trace: cache is NULL");
+  const size_t all = c->log.size() * sizeof(ft_cache_event);
+  if (needed) *needed = all;
+  if (host_buf != nullptr && bytes > 0) {
+    const size_t n = std::min(c->log.size(), bytes / sizeof(ft_cache_event));
+    std::copy(c->log.begin(), c->log.begin() + n, static_cast<ft_cache_event *>(host_buf));
+  }
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_lookup(const ft_expert_cache *c, int32_t layer, int32_t expert, int32_t *slot) {
+  FT_REQUIRE(c != nullptr && slot != nullptr, "ft_expert_cache_lookup: NULL argument");
+  FT_REQUIRE(layer >= 0 && layer < c->n_layers && expert >= 0 && expert < c->E,
+             "ft_expert_cache_lookup: layer or expert out of range");
+  *slot = c->map_mirror[size_t(layer) * c->E + expert];
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_destroy(ft_expert_cache *c) {
+  if (c == nullptr) {
+    clear_error();
+    return FT_OK;
+  }
+  hipError_t e1 = hipStreamSynchronize(c->copy_stream);
+  (void)hipFree(c->dev_state);
+  (void)hipHostFree(c->res_host);
+  (void)hipEventDestroy(c->ev_lru);
+  (void)hipEventDestroy(c->ev_copy);
+  delete c;
+  if (e1 != hipSuccess) return fail(FT_EHIP, std::string("ft_expert_cache_destroy: ") + hipGetErrorString(e1));
+  clear_error();
+  return FT_OK;
+}

@@ -1,0 +1,358 @@
+// ft_moe_grouped_ffn: the SwiGLU expert FFN over per-expert segments, with the
+// weights of every expert read through the resident-expert slot table.
+//
+// Hits run on the GPU straight from the cached copy (FreeToken quantization
+// page, "Cómo se desplazan los pesos MoE cuantizados por la memoria"); the
+// expert network itself is the textbook SwiGLU FFN (Shazeer 2020), since the
+// pages call it an "expert network" and no more.
+//
+// Two launches per call on one stream:
+//   stage 1  h = silu(x Wg^T) * (x Wu^T)   -> bf16 (fp32 for fp32 weights) workspace rows
+//   stage 2  y = h Wd^T                    -> fp32 y_rows / y_shared
+// bf16 / MXFP4 weights use the weight-streaming MFMA tile (stream_gemm.hpp);
+// fp32 weights use a plain FMA kernel.
+#include "ft_internal.hpp"
+#include "stream_gemm.hpp"
+
+namespace ft {
+
+size_t ffn_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+  (void)E;
+  (void)H;
+  const uint64_t rows = uint64_t(T) * uint64_t(k) + uint64_t(T);
+  const uint64_t b = rows * uint64_t(I) * 4;  // fp32 hidden rows (bf16 paths use half)
+  return size_t((b + 255) / 256 * 256);
+}
+
+// Block-wide: index of the aidx-th expert with a non-empty segment (ascending
+// expert id), or -1; *n_active = number of non-empty segments.
+__device__ int find_active_expert(const int32_t *__restrict__ off, int E, int aidx, int *n_active) {
+  __shared__ int s_cnt[4];
+  __shared__ int s_found;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) s_found = -1;
+  int base = 0;
+  for (int c0 = 0; c0 < E; c0 += kStreamThreads) {
+    const int e = c0 + tid;
+    const bool f = e < E && off[e + 1] > off[e];
+    const uint64_t mask = __ballot(f);
+    const int lp = __popcll(mask & ((uint64_t(1) << lane) - 1));
+    if (lane == 0) s_cnt[wave] = __popcll(mask);
+    __syncthreads();
+    int before = base;
+    for (int w = 0; w < wave; ++w) before += s_cnt[w];
+    if (f && before + lp == aidx) s_found = e;
+    base += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    __syncthreads();
+  }
+  *n_active = base;
+  return s_found;
+}
+
+struct FfnArgs {
+  const uint8_t *pool;
+  const int32_t *slot_of_expert;
+  uint64_t expert_bytes;
+  const uint8_t *shared_blob;
+  uint64_t off_w0, off_w1, off_s0, off_s1;
+  int K, N;
+  const int32_t *offsets;
+  int E, T, k;
+  const int32_t *sorted_rows;  // stage 1: token of permuted row p is sorted_rows[p] / k
+  const uint16_t *X;           // stage 1: x; stage 2: h rows
+  int64_t ldx;
+  void *out;                   // stage 1: h rows (bf16); stage 2: y_rows (fp32)
+  int64_t ldo;
+  float *out_shared;           // stage 2: y_shared
+  int n_tiles;
+  int has_shared;
+};
+
+// Grid: (upper bound of active experts incl. shared) x n_tiles workgroups.
+template <int WF, bool STAGE1>
+__global__ __launch_bounds__(kStreamThreads) void ffn_stream_kernel(FfnArgs a) {
+  __shared__ int s_tok[kStreamMaxTok], s_orow[kStreamMaxTok];
+  __shared__ float s_red[stream_red_floats<STAGE1, 4>()];
+  const int tid = threadIdx.x;
+  const int aidx = blockIdx.x / a.n_tiles, tile = blockIdx.x % a.n_tiles;
+  int n_act;
+  const int e = find_active_expert(a.offsets, a.E, aidx, &n_act);
+  const bool is_shared = e < 0 && a.has_shared && aidx == n_act;
+  if (e < 0 && !is_shared) return;
+
+  const uint8_t *blob;
+  int pos0, m;
+  if (is_shared) {
+    blob = a.shared_blob;
+    pos0 = a.T * a.k;
+    m = a.T;
+  } else {
+    const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    pos0 = a.offsets[e];
+    m = a.offsets[e + 1] - pos0;
+    if (slot < 0) {
+      // Caller error: the expert is not resident.  Mark its rows NaN.
+      const int row0 = tile * 16;
+      for (int u = tid; u < m * 16; u += kStreamThreads) {
+        const int j = u / 16, n = row0 + (u % 16);
+        if (n >= a.N) continue;
+        if (STAGE1)
+          reinterpret_cast<uint16_t *>(a.out)[int64_t(pos0 + j) * a.ldo + n] = 0x7fc0;
+        else
+          reinterpret_cast<float *>(a.out)[int64_t(pos0 + j) * a.ldo + n] = __builtin_nanf("");
+      }
+      return;
+    }
+    blob = a.pool + uint64_t(slot) * a.expert_bytes;
+  }
+  const uint8_t *w0 = blob + a.off_w0, *s0 = blob + a.off_s0;
+  const uint8_t *w1 = blob + a.off_w1, *s1 = blob + a.off_s1;
+  void *out = a.out;
+  if (!STAGE1 && is_shared) out = a.out_shared;
+
+  for (int g0 = 0; g0 < m; g0 += kStreamMaxTok) {
+    const int mm = min(kStreamMaxTok, m - g0);
+    if (tid < mm) {
+      const int p = pos0 + g0 + tid;
+      if (STAGE1) {
+        s_tok[tid] = is_shared ? (g0 + tid) : (a.sorted_rows[p] / a.k);
+        s_orow[tid] = p;
+      } else {
+        s_tok[tid] = p;
+        s_orow[tid] = is_shared ? (g0 + tid) : p;
+      }
+    }
+    __syncthreads();
+    stream_tile_any<WF, STAGE1>(w0, s0, w1, s1, a.K, tile * 16, a.N, a.X, a.ldx, s_tok, mm, s_red, out,
+                                a.ldo, s_orow);
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+
+struct FfnF32Args {
+  const uint8_t *pool;
+  const int32_t *slot_of_expert;
+  uint64_t expert_bytes;
+  const uint8_t *shared_blob;
+  uint64_t off_gate, off_up, off_down;
+  int H, I;
+  const int32_t *offsets;
+  int E, T, k;
+  const int32_t *sorted_rows;
+  const float *x;
+  float *h;  // [T*k (+T), I]
+  float *y_rows;
+  float *y_shared;
+  int rows;  // T*k (+T)
+};
+
+// Expert of permuted row p (p < T*k): offsets[e] <= p < offsets[e+1].
+__device__ __forceinline__ int expert_of_row(const int32_t *off, int E, int p) {
+  int lo = 0, hi = E;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ const float *f32_blob(const FfnF32Args &a, int p, int *tok, bool *ok) {
+  const int routed = a.T * a.k;
+  *ok = true;
+  if (p >= routed) {
+    *tok = p - routed;
+    return reinterpret_cast<const float *>(a.shared_blob);
+  }
+  const int e = expert_of_row(a.offsets, a.E, p);
+  *tok = a.sorted_rows[p] / a.k;
+  const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+  if (slot < 0) {
+    *ok = false;
+    return nullptr;
+  }
+  return reinterpret_cast<const float *>(a.pool + uint64_t(slot) * a.expert_bytes);
+}
+
+__global__ __launch_bounds__(256) void ffn_f32_stage1(FfnF32Args a) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(a.rows) * a.I) return;
+  const int p = int(idx / a.I), i = int(idx % a.I);
+  int tok;
+  bool ok;
+  const float *b = f32_blob(a, p, &tok, &ok);
+  if (!ok) {
+    a.h[idx] = __builtin_nanf("");
+    return;
+  }
+  const float *wg = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(b) + a.off_gate) + int64_t(i) * a.H;
+  const float *wu = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(b) + a.off_up) + int64_t(i) * a.H;
+  const float *xr = a.x + int64_t(tok) * a.H;
+  float g = 0.f, u = 0.f;
+  for (int c = 0; c < a.H; ++c) {
+    g = fmaf(xr[c], wg[c], g);
+    u = fmaf(xr[c], wu[c], u);
+  }
+  a.h[idx] = g / (1.0f + expf(-g)) * u;
+}
+
+__global__ __launch_bounds__(256) void ffn_f32_stage2(FfnF32Args a) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(a.rows) * a.H) return;
+  const int p = int(idx / a.H), n = int(idx % a.H);
+  int tok;
+  bool ok;
+  const float *b = f32_blob(a, p, &tok, &ok);
+  const int routed = a.T * a.k;
+  float *dst = p >= routed ? (a.y_shared + int64_t(tok) * a.H + n) : (a.y_rows + int64_t(p) * a.H + n);
+  if (!ok) {
+    *dst = __builtin_nanf("");
+    return;
+  }
+  const float *wd = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(b) + a.off_down) + int64_t(n) * a.I;
+  const float *hr = a.h + int64_t(p) * a.I;
+  float y = 0.f;
+  for (int c = 0; c < a.I; ++c) y = fmaf(hr[c], wd[c], y);
+  *dst = y;
+}
+
+}  // namespace ft
+
+using namespace ft;
+
+extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
+                                        const int32_t *slot_of_expert, const void *shared_blob,
+                                        const void *x, int32_t x_dtype, int32_t T, int32_t k,
+                                        int32_t E, const int32_t *expert_offsets,
+                                        const int32_t *sorted_rows, float *y_rows, float *y_shared,
+                                        int32_t mode, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  FT_REQUIRE(L != nullptr, "ft_moe_grouped_ffn: layout is NULL");
+  FT_REQUIRE(T >= 0 && k >= 1 && E >= 1, "ft_moe_grouped_ffn: need T >= 0, k >= 1, E >= 1");
+  FT_REQUIRE(int64_t(T) * (k + 1) < (int64_t(1) << 31), "ft_moe_grouped_ffn: T*k too large");
+  FT_SUPPORTED(k <= E, "ft_moe_grouped_ffn: k > E");
+  FT_SUPPORTED(E <= 4096, "ft_moe_grouped_ffn: E > 4096");
+  FT_SUPPORTED(mode == 0, "ft_moe_grouped_ffn: only mode 0 (exact bf16 MFMA path) is implemented");
+  const int H = L->H, I = L->I;
+  FT_REQUIRE(H >= 1 && I >= 1 && L->expert_bytes > 0, "ft_moe_grouped_ffn: layout not initialised");
+  const int wd = L->wdtype;
+  if (wd == FT_F32) {
+    FT_REQUIRE(x_dtype == FT_F32, "ft_moe_grouped_ffn: fp32 weights need fp32 activations");
+  } else if (wd == FT_BF16) {
+    FT_REQUIRE(x_dtype == FT_BF16, "ft_moe_grouped_ffn: bf16 weights need bf16 activations");
+    FT_SUPPORTED(H % 128 == 0 && I % 128 == 0, "ft_moe_grouped_ffn: bf16 weights need H, I multiples of 128");
+  } else if (wd == FT_MXFP4) {
+    FT_REQUIRE(x_dtype == FT_BF16, "ft_moe_grouped_ffn: MXFP4 weights need bf16 activations");
+    FT_SUPPORTED(H % 512 == 0 && I % 512 == 0, "ft_moe_grouped_ffn: MXFP4 weights need H, I multiples of 512");
+  } else {
+    return fail(FT_EINVAL, "ft_moe_grouped_ffn: unknown weight dtype in layout");
+  }
+  if (T == 0) {
+    clear_error();
+    return FT_OK;
+  }
+  FT_REQUIRE(slot_pool && x && expert_offsets && sorted_rows && y_rows,
+             "ft_moe_grouped_ffn: NULL pointer argument");
+  FT_REQUIRE((shared_blob == nullptr) == (y_shared == nullptr),
+             "ft_moe_grouped_ffn: shared_blob and y_shared must both be given or both be NULL");
+  FT_REQUIRE(aligned(slot_pool, 256) && (!shared_blob || aligned(shared_blob, 256)) &&
+                 L->expert_bytes % 256 == 0,
+             "ft_moe_grouped_ffn: slot_pool / shared_blob must be 256-byte aligned");
+  FT_REQUIRE(aligned(x, 16) && aligned(y_rows, 16) && (!y_shared || aligned(y_shared, 16)) &&
+                 aligned(workspace, 16),
+             "ft_moe_grouped_ffn: x, y_rows, y_shared, workspace must be 16-byte aligned");
+  const size_t need = ffn_workspace_bytes(T, k, E, H, I);
+  FT_REQUIRE(workspace != nullptr && workspace_bytes >= need,
+             "ft_moe_grouped_ffn: workspace too small (see ft_workspace_bytes)");
+
+  const bool has_shared = shared_blob != nullptr;
+  const int routed = T * k;
+  const int rows = routed + (has_shared ? T : 0);
+
+  if (wd == FT_F32) {
+    FfnF32Args a{};
+    a.pool = static_cast<const uint8_t *>(slot_pool);
+    a.slot_of_expert = slot_of_expert;
+    a.expert_bytes = L->expert_bytes;
+    a.shared_blob = static_cast<const uint8_t *>(shared_blob);
+    a.off_gate = L->off_gate;
+    a.off_up = L->off_up;
+    a.off_down = L->off_down;
+    a.H = H;
+    a.I = I;
+    a.offsets = expert_offsets;
+    a.E = E;
+    a.T = T;
+    a.k = k;
+    a.sorted_rows = sorted_rows;
+    a.x = static_cast<const float *>(x);
+    a.h = static_cast<float *>(workspace);
+    a.y_rows = y_rows;
+    a.y_shared = y_shared;
+    a.rows = rows;
+    const int64_t n1 = int64_t(rows) * I, n2 = int64_t(rows) * H;
+    hipLaunchKernelGGL(ffn_f32_stage1, dim3(unsigned(cdiv<int64_t>(n1, 256))), dim3(256), 0, stream, a);
+    FT_LAUNCHED("ffn_f32_stage1");
+    hipLaunchKernelGGL(ffn_f32_stage2, dim3(unsigned(cdiv<int64_t>(n2, 256))), dim3(256), 0, stream, a);
+    FT_LAUNCHED("ffn_f32_stage2");
+    clear_error();
+    return FT_OK;
+  }
+
+  const int a_max = std::min(E, routed) + (has_shared ? 1 : 0);
+  FfnArgs a{};
+  a.pool = static_cast<const uint8_t *>(slot_pool);
+  a.slot_of_expert = slot_of_expert;
+  a.expert_bytes = L->expert_bytes;
+  a.shared_blob = static_cast<const uint8_t *>(shared_blob);
+  a.offsets = expert_offsets;
+  a.E = E;
+  a.T = T;
+  a.k = k;
+  a.sorted_rows = sorted_rows;
+  a.has_shared = has_shared ? 1 : 0;
+  uint16_t *hbuf = static_cast<uint16_t *>(workspace);
+
+  // stage 1: gate/up + SwiGLU -> h [rows, I] bf16
+  FfnArgs s1 = a;
+  s1.off_w0 = L->off_gate;
+  s1.off_w1 = L->off_up;
+  s1.off_s0 = L->off_sgate;
+  s1.off_s1 = L->off_sup;
+  s1.K = H;
+  s1.N = I;
+  s1.X = static_cast<const uint16_t *>(x);
+  s1.ldx = H;
+  s1.out = hbuf;
+  s1.ldo = I;
+  s1.n_tiles = cdiv(I, 16);
+  // stage 2: down -> y_rows / y_shared fp32
+  FfnArgs s2 = a;
+  s2.off_w0 = L->off_down;
+  s2.off_w1 = L->off_down;
+  s2.off_s0 = L->off_sdown;
+  s2.off_s1 = L->off_sdown;
+  s2.K = I;
+  s2.N = H;
+  s2.X = hbuf;
+  s2.ldx = I;
+  s2.out = y_rows;
+  s2.ldo = H;
+  s2.out_shared = y_shared;
+  s2.n_tiles = cdiv(H, 16);
+
+  const dim3 blk(kStreamThreads);
+  if (wd == FT_BF16) {
+    hipLaunchKernelGGL((ffn_stream_kernel<WF_BF16, true>), dim3(a_max * s1.n_tiles), blk, 0, stream, s1);
+    FT_LAUNCHED("ffn_stream_kernel<bf16, gate_up>");
+    hipLaunchKernelGGL((ffn_stream_kernel<WF_BF16, false>), dim3(a_max * s2.n_tiles), blk, 0, stream, s2);
+    FT_LAUNCHED("ffn_stream_kernel<bf16, down>");
+  } else {
+    hipLaunchKernelGGL((ffn_stream_kernel<WF_FP4, true>), dim3(a_max * s1.n_tiles), blk, 0, stream, s1);
+    FT_LAUNCHED("ffn_stream_kernel<mxfp4, gate_up>");
+    hipLaunchKernelGGL((ffn_stream_kernel<WF_FP4, false>), dim3(a_max * s2.n_tiles), blk, 0, stream, s2);
+    FT_LAUNCHED("ffn_stream_kernel<mxfp4, down>");
+  }
+  clear_error();
+  return FT_OK;
+}

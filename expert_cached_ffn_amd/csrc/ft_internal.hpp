@@ -1,0 +1,114 @@
+// Internal helpers shared by the gfx950 kernels and the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string>
+
+#include "../../include/ft_moe.h"
+
+// ---------------------------------------------------------------------------
+// host-side status handling
+// ---------------------------------------------------------------------------
+namespace ft {
+
+void set_error(const std::string &msg);
+void clear_error();
+
+inline ft_status fail(ft_status st, const std::string &msg) {
+  set_error(msg);
+  return st;
+}
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Workspace sizes (bytes) of the calls that take one.
+size_t permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
+size_t ffn_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I);
+
+}  // namespace ft
+
+#define FT_REQUIRE(cond, msg)                                   \
+  do {                                                          \
+    if (!(cond)) return ft::fail(FT_EINVAL, std::string(msg));  \
+  } while (0)
+
+#define FT_SUPPORTED(cond, msg)                                  \
+  do {                                                           \
+    if (!(cond)) return ft::fail(FT_ENOTSUP, std::string(msg));  \
+  } while (0)
+
+#define FT_HIP(expr)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return ft::fail(FT_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));      \
+  } while (0)
+
+// Check the launch that was just enqueued.
+#define FT_LAUNCHED(name)                                                               \
+  do {                                                                                  \
+    hipError_t e_ = hipGetLastError();                                                  \
+    if (e_ != hipSuccess)                                                               \
+      return ft::fail(FT_EHIP, std::string("launch of ") + name + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// device-side types and helpers
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+namespace ft {
+
+// fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return static_cast<uint16_t>(b >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// E8M0 scale byte -> fp32 2^(s-127) for s in 1..254 (the exponent field itself).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Eight FP4 E2M1 codes (one dword, element 2i in the low nibble of byte i)
+// times a power-of-two scale -> eight bf16, in element order.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t codes, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// 16-byte global load/store helpers.
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+template <typename T>
+__host__ __device__ __forceinline__ T cdiv(T a, T b) { return (a + b - 1) / b; }
+
+}  // namespace ft

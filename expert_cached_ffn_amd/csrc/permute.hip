@@ -1,0 +1,210 @@
+// ft_moe_permute: group the routed rows by expert (counting sort, stable).
+//
+// Each flat row r = t*k + j (token t's j-th pick) goes to segment ids[r];
+// segments are laid out in expert order and keep rows ascending inside a
+// segment.  The per-expert segments are what the grouped expert FFN walks:
+// one contiguous block of rows per cached (layer, expert) entry (FreeToken
+// rtx 4090 page, "Cómo funciona la jerarquía de memoria MoE": the runtime
+// executes whole experts).
+//
+// Small inputs: one workgroup -- LDS histogram, exclusive scan, then one wave
+// scatters 64 rows at a time, ranking equal keys with per-bit ballots.
+// Large inputs: count per 1024-row block -> one-workgroup scan over blocks ->
+// per-block scatter from the block's own bases.
+#include "ft_internal.hpp"
+
+namespace ft {
+
+constexpr int kPermSmallRows = 2048;  // one workgroup up to this many rows
+constexpr int kPermChunk = 1024;      // rows per block of the multi-block path
+constexpr int kPermMaxE = 4096;
+
+size_t permute_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  const int64_t R = int64_t(T) * k;
+  if (R <= kPermSmallRows) return 0;
+  const int64_t B = (R + kPermChunk - 1) / kPermChunk;
+  return size_t(((B * E * 4) + 255) / 256 * 256);
+}
+
+__device__ __forceinline__ int bits_for(int E) {
+  int b = 1;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+// Stable scatter of rows [r0, r1) by one wave.  s_base[e] holds the next
+// free position of expert e and is advanced as rows are placed.
+__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, int r0, int r1, int E,
+                                             int *s_base, int32_t *__restrict__ sorted_rows,
+                                             int32_t *__restrict__ row_pos) {
+  const int lane = threadIdx.x & 63;
+  const int nb = bits_for(E);
+  const uint64_t lt = (uint64_t(1) << lane) - 1;
+  for (int c = r0; c < r1; c += 64) {
+    const int r = c + lane;
+    const bool act = r < r1;
+    int key = act ? ids[r] : 0;
+    const bool ok = act && key >= 0 && key < E;
+    const uint64_t active = __ballot(ok);
+    uint64_t same = active;
+    for (int b = 0; b < nb; ++b) {
+      const uint64_t ones = __ballot((key >> b) & 1);
+      same &= ((key >> b) & 1) ? ones : ~ones;
+    }
+    if (ok) {
+      const int rank = __popcll(same & lt);
+      const int pos = s_base[key] + rank;
+      sorted_rows[pos] = r;
+      row_pos[r] = pos;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ok && (same >> lane) == 1) s_base[key] += __popcll(same);  // last lane of its key
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Block-wide exclusive scan of s[0..n) in place (n <= 4096); returns the total.
+__device__ int block_exclusive_scan(int *s, int n, int *s_tmp /* >= 32 ints */) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int a = min(n, tid * per), b = min(n, a + per);
+  int local = 0;
+  for (int i = a; i < b; ++i) local += s[i];
+  // inclusive scan of `local` across the block
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  int v = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = s_tmp[w];
+      s_tmp[w] = run;
+      run += t;
+    }
+    s_tmp[nw] = run;
+  }
+  __syncthreads();
+  int excl = s_tmp[wave] + v - local;
+  for (int i = a; i < b; ++i) {
+    const int t = s[i];
+    s[i] = excl;
+    excl += t;
+  }
+  const int total = s_tmp[nw];
+  __syncthreads();
+  return total;
+}
+
+// One workgroup (256 threads) does everything.
+__global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *__restrict__ ids, int R, int E,
+                                                            int32_t *__restrict__ offsets,
+                                                            int32_t *__restrict__ sorted_rows,
+                                                            int32_t *__restrict__ row_pos) {
+  __shared__ int s_cnt[kPermMaxE];
+  __shared__ int s_tmp[32];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
+  __syncthreads();
+  for (int r = tid; r < R; r += 256) {
+    const int key = ids[r];
+    if (key >= 0 && key < E) atomicAdd(&s_cnt[key], 1);
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_cnt, E, s_tmp);
+  for (int e = tid; e < E; e += 256) offsets[e] = s_cnt[e];
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  if (tid < 64) wave_scatter(ids, 0, R, E, s_cnt, sorted_rows, row_pos);
+}
+
+// Multi-block pass 1: per-block histogram -> counts[b][e].
+__global__ __launch_bounds__(256) void permute_count_kernel(const int32_t *__restrict__ ids, int R, int E,
+                                                            int32_t *__restrict__ counts) {
+  __shared__ int s_cnt[kPermMaxE];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
+  __syncthreads();
+  const int r0 = b * kPermChunk, r1 = min(R, r0 + kPermChunk);
+  for (int r = r0 + tid; r < r1; r += 256) {
+    const int key = ids[r];
+    if (key >= 0 && key < E) atomicAdd(&s_cnt[key], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) counts[int64_t(b) * E + e] = s_cnt[e];
+}
+
+// Multi-block pass 2 (one workgroup): counts[b][e] := sum_{b'<b} counts[b'][e];
+// offsets = exclusive scan of the per-expert totals.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t *__restrict__ counts, int B, int E,
+                                                            int32_t *__restrict__ offsets) {
+  __shared__ int s_tot[kPermMaxE];
+  __shared__ int s_tmp[32];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int b = 0; b < B; ++b) {
+      const int c = counts[int64_t(b) * E + e];
+      counts[int64_t(b) * E + e] = run;
+      run += c;
+    }
+    s_tot[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_tot, E, s_tmp);
+  for (int e = tid; e < E; e += 1024) offsets[e] = s_tot[e];
+  if (tid == 0) offsets[E] = total;
+}
+
+// Multi-block pass 3: block b scatters its rows from offsets[e] + counts[b][e].
+__global__ __launch_bounds__(64) void permute_scatter_kernel(const int32_t *__restrict__ ids, int R, int E,
+                                                             const int32_t *__restrict__ counts,
+                                                             const int32_t *__restrict__ offsets,
+                                                             int32_t *__restrict__ sorted_rows,
+                                                             int32_t *__restrict__ row_pos) {
+  __shared__ int s_base[kPermMaxE];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 64) s_base[e] = offsets[e] + counts[int64_t(b) * E + e];
+  __syncthreads();
+  const int r0 = b * kPermChunk, r1 = min(R, r0 + kPermChunk);
+  wave_scatter(ids, r0, r1, E, s_base, sorted_rows, row_pos);
+}
+
+}  // namespace ft
+
+using namespace ft;
+
+extern "C" ft_status ft_moe_permute(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                                    int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  FT_REQUIRE(T >= 0 && k >= 1 && E >= 1, "ft_moe_permute: need T >= 0, k >= 1, E >= 1");
+  FT_SUPPORTED(E <= kPermMaxE, "ft_moe_permute: E > 4096");
+  FT_REQUIRE(int64_t(T) * k < (int64_t(1) << 31), "ft_moe_permute: T*k too large");
+  FT_REQUIRE(expert_offsets != nullptr, "ft_moe_permute: expert_offsets is NULL");
+  const int R = T * k;
+  if (R > 0) FT_REQUIRE(topk_ids && sorted_rows && row_pos, "ft_moe_permute: NULL pointer argument");
+  const size_t need = permute_workspace_bytes(T, k, E);
+  FT_REQUIRE(need == 0 || (workspace != nullptr && workspace_bytes >= need && aligned(workspace, 4)),
+             "ft_moe_permute: workspace too small (see ft_workspace_bytes)");
+  if (R <= kPermSmallRows) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(256), 0, stream, topk_ids, R, E, expert_offsets,
+                       sorted_rows, row_pos);
+    FT_LAUNCHED("permute_small_kernel");
+  } else {
+    const int B = cdiv(R, kPermChunk);
+    int32_t *counts = static_cast<int32_t *>(workspace);
+    hipLaunchKernelGGL(permute_count_kernel, dim3(B), dim3(256), 0, stream, topk_ids, R, E, counts);
+    FT_LAUNCHED("permute_count_kernel");
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, B, E, expert_offsets);
+    FT_LAUNCHED("permute_scan_kernel");
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(B), dim3(64), 0, stream, topk_ids, R, E, counts,
+                       expert_offsets, sorted_rows, row_pos);
+    FT_LAUNCHED("permute_scatter_kernel");
+  }
+  clear_error();
+  return FT_OK;
+}

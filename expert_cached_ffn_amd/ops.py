@@ -1,0 +1,132 @@
+"""Thin Python binding of the C ABI: one function per entry point, same names.
+
+Arguments are torch tensors (device memory, or pinned host memory for the
+cache's host bank) or ``None`` for nullable pointers; the current torch stream
+is used unless ``stream`` is given.  Every call only marshals arguments: all
+arithmetic runs in the HIP library, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import ExpertLayout, CacheStats, CacheEvent
+
+
+class FtError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        self.status = status
+        super().__init__(f"{_lib.STATUS_NAMES.get(status, status)}: {text}")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FtError(status, _lib.lib().ft_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def version() -> str:
+    return _lib.lib().ft_version().decode()
+
+
+def ft_expert_layout_init(wdtype: int, H: int, I: int) -> ExpertLayout:
+    L = ExpertLayout()
+    _check(_lib.lib().ft_expert_layout_init(wdtype, H, I, C.byref(L)))
+    return L
+
+
+def ft_workspace_bytes(which: int, T: int, k: int, E: int, H: int = 0, I: int = 0) -> int:
+    return int(_lib.lib().ft_workspace_bytes(which, T, k, E, H, I))
+
+
+def ft_moe_route(x, x_dtype: int, w_router, logits, T: int, H: int, E: int, k: int, gating: int,
+                 renormalize: bool, topk_ids, topk_w, stream=None) -> None:
+    _check(_lib.lib().ft_moe_route(_ptr(x), x_dtype, _ptr(w_router), _ptr(logits), T, H, E, k, gating,
+                                   int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+
+
+def ft_moe_permute(topk_ids, T: int, k: int, E: int, expert_offsets, sorted_rows, row_pos,
+                   workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    _check(_lib.lib().ft_moe_permute(_ptr(topk_ids), T, k, E, _ptr(expert_offsets), _ptr(sorted_rows),
+                                     _ptr(row_pos), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def ft_moe_grouped_ffn(layout: ExpertLayout, slot_pool, slot_of_expert, shared_blob, x, x_dtype: int,
+                       T: int, k: int, E: int, expert_offsets, sorted_rows, y_rows, y_shared,
+                       mode: int = 0, workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    _check(_lib.lib().ft_moe_grouped_ffn(C.byref(layout), _ptr(slot_pool), _ptr(slot_of_expert),
+                                         _ptr(shared_blob), _ptr(x), x_dtype, T, k, E, _ptr(expert_offsets),
+                                         _ptr(sorted_rows), _ptr(y_rows), _ptr(y_shared), mode,
+                                         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def ft_moe_combine(y_rows, topk_w, row_pos, y_shared, T: int, k: int, H: int, out_dtype: int, out,
+                   stream=None) -> None:
+    _check(_lib.lib().ft_moe_combine(_ptr(y_rows), _ptr(topk_w), _ptr(row_pos), _ptr(y_shared), T, k, H,
+                                     out_dtype, _ptr(out), _stream(stream)))
+
+
+class ExpertCache:
+    """Owner of one ``ft_expert_cache`` handle (create / step / stats / trace / destroy)."""
+
+    def __init__(self, layout: ExpertLayout, n_layers: int, E: int, capacity: int, slot_pool, host_bank,
+                 copy_stream):
+        self.layout = layout
+        self.n_layers, self.E, self.capacity = n_layers, E, capacity
+        self._keep = (slot_pool, host_bank, copy_stream)
+        h = C.c_void_p()
+        _check(_lib.lib().ft_expert_cache_create(C.byref(layout), n_layers, E, capacity, _ptr(slot_pool),
+                                                 _ptr(host_bank), _stream(copy_stream), C.byref(h)))
+        self._h = h
+
+    def ft_expert_cache_step(self, layer: int, topk_ids, T: int, k: int, slot_of_expert, stream=None) -> None:
+        _check(_lib.lib().ft_expert_cache_step(self._h, layer, _ptr(topk_ids), T, k, _ptr(slot_of_expert),
+                                               _stream(stream)))
+
+    step = ft_expert_cache_step
+
+    def stats(self) -> dict:
+        s = CacheStats()
+        _check(_lib.lib().ft_expert_cache_stats(self._h, C.byref(s)))
+        return {n: int(getattr(s, n)) for n, _ in CacheStats._fields_}
+
+    def trace(self) -> list[tuple]:
+        need = C.c_size_t()
+        _check(_lib.lib().ft_expert_cache_trace(self._h, None, 0, C.byref(need)))
+        n = need.value // C.sizeof(CacheEvent)
+        buf = (CacheEvent * max(n, 1))()
+        _check(_lib.lib().ft_expert_cache_trace(self._h, C.cast(buf, C.c_void_p), need.value, None))
+        return [(e.step, e.layer, e.expert, e.hit, e.slot, e.evicted) for e in buf[:n]]
+
+    def lookup(self, layer: int, expert: int) -> int:
+        s = C.c_int32()
+        _check(_lib.lib().ft_expert_cache_lookup(self._h, layer, expert, C.byref(s)))
+        return s.value
+
+    def destroy(self) -> None:
+        if self._h:
+            _check(_lib.lib().ft_expert_cache_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

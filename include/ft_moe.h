@@ -1,0 +1,299 @@
+/*
+ * ft_moe.h -- C ABI of the routed MoE FFN layer with a resident-expert cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, one call per step:
+ *   ft_moe_route        router logits (optional) + top-k + gating weights
+ *   ft_moe_permute      token-to-expert permutation into per-expert segments
+ *   ft_moe_grouped_ffn  SwiGLU expert FFN over the segments, weights read
+ *                       through a resident-expert slot table
+ *   ft_moe_combine      weighted combine of the expert rows back to tokens
+ *   ft_expert_cache_*   the shared (layer, expert) LRU slot table on the
+ *                       device, with misses filled from pinned host memory
+ *
+ * Source of the method: the FreeToken pages.  A router activates a small
+ * subset of the experts for each token (6 of 256 routed experts per layer in
+ * their example); the full expert set lives in host memory and GPU memory is
+ * an elastic cache of whole (layer, expert) entries under one LRU policy
+ * shared by every MoE layer; hits run on the GPU from the cached copy and
+ * misses are moved over PCIe from pinned host memory (FreeToken linux page,
+ * "Cómo gestiona FreeToken la memoria MoE"; FreeToken quantization page,
+ * "Cómo se desplazan los pesos MoE cuantizados por la memoria"; FreeToken
+ * rtx 4090 page, "Cómo funciona la jerarquía de memoria MoE").  The pages do
+ * not write the layer arithmetic; the textbook reading used here is stated at
+ * each call.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *    buffer; a call borrows its buffers until the work it enqueued finishes.
+ *  - Arguments are validated synchronously before anything is enqueued.  On an
+ *    error nothing is enqueued and no state changes.  Work is enqueued on
+ *    `stream` and the call returns without waiting, except
+ *    ft_expert_cache_step, which waits once for its miss list (see there).
+ *  - Return value: FT_OK (0) or a negative ft_status.  ft_last_error() gives a
+ *    text for the last failing call on the calling host thread.  Faults of
+ *    enqueued work surface at the caller's next synchronisation.
+ *  - Hot-path calls never allocate device or host memory.  Scratch memory is
+ *    passed in as `workspace`, sized by ft_workspace_bytes().
+ *  - Row-major layouts throughout; [a, b] means a rows of b contiguous elements.
+ */
+#ifndef FT_MOE_H
+#define FT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ft_status;
+enum {
+  FT_OK = 0,
+  FT_EINVAL = -1,     /* null pointer, bad shape, bad enum, misaligned buffer */
+  FT_ENOTSUP = -2,    /* valid request outside what the kernels implement     */
+  FT_ECAPACITY = -3,  /* a cache step needs more distinct experts than slots  */
+  FT_EHIP = -4        /* a HIP runtime call failed                            */
+};
+
+/* Text of the last error on this host thread ("" if none).  Owned by the library. */
+const char *ft_last_error(void);
+
+/* Library version string, e.g. "ftmoe 0.1 gfx950". */
+const char *ft_version(void);
+
+typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2 } ft_dtype;
+typedef enum { FT_SOFTMAX = 0, FT_SIGMOID = 1 } ft_gating;
+
+/* ------------------------------------------------------------------------ */
+/* Expert blob layout                                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * One cache entry is one whole (layer, expert) pair, stored as one contiguous
+ * blob with the same layout in host memory and in a GPU slot (FreeToken rtx
+ * 4090 page, "Cómo funciona la jerarquía de memoria MoE": an entry is a whole
+ * expert under one logical mapping on CPU and GPU).
+ *
+ * Blob = [gate][up][down] (+ for MXFP4: [gate scales][up scales][down scales]),
+ * each part starting at a 256-byte boundary, expert_bytes rounded up to 4 KiB.
+ *   gate, up : [I, H]   (contraction axis H contiguous)
+ *   down     : [H, I]   (contraction axis I contiguous)
+ * FT_F32 / FT_BF16: elements of that type.
+ * FT_MXFP4 (OCP Microscaling v1.0): codes [rows, K/2] bytes, element 2i in
+ *   bits 3:0 and element 2i+1 in bits 7:4 of byte i, FP4 E2M1 values;
+ *   scales [rows, K/32] bytes, E8M0 (2^(byte-127)), one per 32 consecutive
+ *   elements of a row along its contraction axis K.
+ */
+typedef struct {
+  int32_t wdtype;        /* ft_dtype of the expert weights                     */
+  int32_t H, I;          /* hidden size, expert intermediate size              */
+  int32_t reserved;
+  uint64_t expert_bytes; /* bytes of one blob (a multiple of 4096)             */
+  uint64_t off_gate, off_up, off_down;      /* byte offsets of the three parts */
+  uint64_t off_sgate, off_sup, off_sdown;   /* MXFP4 scale parts (0 otherwise) */
+} ft_expert_layout;
+
+/* Fill *out for experts of type wdtype.  Host only, pure.
+ * Errors: FT_EINVAL (out NULL, H or I < 1, unknown dtype, MXFP4 with H or I
+ * not a multiple of 32). */
+ft_status ft_expert_layout_init(int32_t wdtype, int32_t H, int32_t I, ft_expert_layout *out);
+
+/* ------------------------------------------------------------------------ */
+/* Routing                                                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * ft_moe_route -- a router picks k of the E routed experts per token (FreeToken
+ * linux page, "Cómo gestiona FreeToken la memoria MoE").
+ *
+ * If w_router != NULL: logits[t, e] = sum_h x[t, h] * w_router[e, h] is computed
+ *   with fp32 accumulation and written to `logits` [T, E] fp32.
+ *   x [T, H] and w_router [E, H] are both of type x_dtype (FT_F32 or FT_BF16).
+ * If w_router == NULL: `logits` [T, E] fp32 is read (x and H are ignored).
+ * topk_ids [T, k] int32: per token the k largest logits in descending order,
+ *   the lower expert index first on equal logits (-0.0 equals +0.0).
+ * topk_w [T, k] fp32: FT_SOFTMAX -> softmax over all E of the token's logits,
+ *   taken at the picked experts; FT_SIGMOID -> sigmoid of the picked logits.
+ *   renormalize != 0 divides the k weights by their sum.
+ * Limits: 1 <= k <= E <= 1024 (else FT_ENOTSUP).  T = 0 is a no-op.
+ * Buffers 16-byte aligned; with w_router, H must be a multiple of 8.
+ * NaN or infinite logits are outside the contract.
+ */
+ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_router, float *logits,
+                       int32_t T, int32_t H, int32_t E, int32_t k, int32_t gating,
+                       int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                       hipStream_t stream);
+
+/*
+ * ft_moe_permute -- group the routed rows by expert.  Flat row r = t*k + j is
+ * token t's j-th pick.  expert_offsets [E+1]: exclusive prefix sum of the
+ * per-expert row counts (expert_offsets[E] = T*k).  sorted_rows [T*k]: the rows
+ * of expert 0, then expert 1, ..., ascending within each segment.  row_pos
+ * [T*k]: the inverse, row_pos[sorted_rows[i]] = i.
+ * topk_ids must hold values in 0..E-1 (out-of-range ids are a caller error: the
+ * kernel ignores such rows and the outputs are then unspecified).
+ * workspace: ft_workspace_bytes(FT_WS_PERMUTE, T, k, E, 0, 0) bytes (may be 0
+ * for small T*k, then workspace may be NULL).
+ * Limits: 1 <= E <= 4096, T*k < 2^31.
+ */
+ft_status ft_moe_permute(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E,
+                         int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Expert FFN                                                                 */
+/* ------------------------------------------------------------------------ */
+/*
+ * ft_moe_grouped_ffn -- every routed row runs its expert from the expert's
+ * resident copy (FreeToken quantization page, "Cómo se desplazan los pesos MoE
+ * cuantizados por la memoria": hits run on the GPU from the cache).  The
+ * expert is a SwiGLU FFN (Shazeer 2020, no biases):
+ *     y = (silu(x Wg^T) * (x Wu^T)) Wd^T,   silu(z) = z / (1 + e^-z).
+ *
+ * Segment e = rows expert_offsets[e] .. expert_offsets[e+1]-1 of the permuted
+ * order; its row i is token sorted_rows[i] / k.  Expert e's blob starts at
+ *   slot_pool + slot_of_expert[e] * L->expert_bytes
+ * (slot_of_expert == NULL means slot e).  A non-empty segment whose slot is
+ * negative is a caller error; its y rows are written as NaN.
+ * x [T, H] of x_dtype (FT_F32 with FT_F32 weights, FT_BF16 with FT_BF16 or
+ *   FT_MXFP4 weights).
+ * y_rows [T*k, H] fp32, permuted order (row i belongs to sorted_rows[i]).
+ * shared_blob (nullable): one more expert in the same layout, applied to every
+ *   token with weight 1, written to y_shared [T, H] fp32 (required iff
+ *   shared_blob != NULL).
+ * mode 0: exact path -- MXFP4 weights decoded exactly to bf16, bf16 MFMA,
+ *   fp32 accumulation; the SwiGLU hidden vector is rounded to bf16 before
+ *   the down projection.  Other modes: FT_ENOTSUP.
+ * workspace: ft_workspace_bytes(FT_WS_FFN, T, k, E, H, I) bytes.
+ * Limits: FT_BF16 weights need H, I multiples of 128; FT_MXFP4 multiples of
+ *   512; E <= 4096.  MXFP4 scale bytes must lie in 2..252 (every decoded value
+ *   is then an exact bf16).  Buffers 16-byte aligned, slot_pool and blobs
+ *   256-byte aligned.
+ */
+ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
+                             const int32_t *slot_of_expert, const void *shared_blob,
+                             const void *x, int32_t x_dtype, int32_t T, int32_t k, int32_t E,
+                             const int32_t *expert_offsets, const int32_t *sorted_rows,
+                             float *y_rows, float *y_shared, int32_t mode,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ft_moe_combine -- out[t] = sum_{j<k} topk_w[t, j] * y_rows[row_pos[t*k + j]]
+ * (+ y_shared[t] when y_shared != NULL), summed in j order and then the shared
+ * row, in fp32; written as out_dtype (FT_F32, or FT_BF16 rounded to nearest
+ * even).  y_rows [T*k, H] fp32, out [T, H].  H a multiple of 4; buffers
+ * 16-byte aligned.
+ */
+ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t *row_pos,
+                         const float *y_shared, int32_t T, int32_t k, int32_t H,
+                         int32_t out_dtype, void *out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Expert cache                                                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * One LRU over (layer, expert) entries, shared by all MoE layers, following the
+ * router rather than fixed at start-up (FreeToken linux page, "Cómo gestiona
+ * FreeToken la memoria MoE"; FreeToken rtx 4090 page, "Cómo funciona la
+ * jerarquía de memoria MoE").  Hits run from the slot; misses are copied over
+ * PCIe from the pinned host bank, the source of truth for every expert
+ * (FreeToken quantization page, "Cómo se desplazan los pesos MoE cuantizados
+ * por la memoria").  Miss rate = misses / routed expert reads (FreeToken 290b
+ * model page, "Limitaciones, lista de comprobación y buenas prácticas").
+ *
+ * Update order inside one (layer, step) -- not on the pages, fixed here: the
+ * needed set S = the distinct experts of the step's topk_ids, ascending.
+ * Phase 1: every hit becomes most recently used (ascending expert id).
+ * Phase 2: each miss (ascending) takes the least recently used slot holding
+ * no member of S; empty slots count as oldest, lowest index first.
+ */
+typedef struct ft_expert_cache ft_expert_cache;  /* opaque */
+
+typedef struct {
+  uint64_t accesses;   /* distinct (layer, expert) reads, summed over steps */
+  uint64_t hits, misses, evictions;
+  uint64_t bytes_h2d;  /* bytes copied host -> device by miss fills         */
+  uint64_t steps;      /* successful ft_expert_cache_step calls             */
+} ft_cache_stats;
+
+/* One cache event, as recorded by the step that produced it. */
+typedef struct {
+  int32_t step;        /* index of the ft_expert_cache_step call (from 0)    */
+  int32_t layer;
+  int32_t expert;
+  int32_t hit;         /* 1 hit, 0 miss                                      */
+  int32_t slot;
+  int32_t evicted;     /* key layer*E + expert of the entry evicted, or -1    */
+} ft_cache_event;
+
+/*
+ * Create a cache of `capacity` slots over n_layers x E experts of layout L.
+ * slot_pool: device, capacity * L->expert_bytes bytes, 256-byte aligned,
+ *   caller-owned, borrowed for the cache's lifetime.
+ * host_bank: host, PINNED (hipHostMalloc), n_layers * E * L->expert_bytes
+ *   bytes, blob of (layer l, expert e) at (l*E + e) * expert_bytes;
+ *   caller-owned, borrowed for the cache's lifetime.
+ * copy_stream: the stream the miss fills are enqueued on (not the NULL stream).
+ * The cache allocates its small device state (about 16 B per key and slot)
+ * and one pinned miss-list buffer here, and frees them in destroy.  It starts
+ * empty.  Errors: FT_EINVAL (bad sizes, NULLs, host_bank not pinned host
+ * memory, slot_pool not device memory), FT_EHIP.
+ * Limits: capacity <= 65536, n_layers * E <= 2^20, E <= 4096.
+ */
+ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n_layers, int32_t E,
+                                 int32_t capacity, void *slot_pool, const void *host_bank,
+                                 hipStream_t copy_stream, ft_expert_cache **out);
+
+/*
+ * Serve layer `layer` for the routing topk_ids [T, k] (device).
+ * On return slot_of_expert [E] (device) holds, for every expert of the layer,
+ * its slot or -1 if not resident; every expert in topk_ids is resident.
+ * Synchronisation:
+ *   1. the LRU kernel is enqueued on compute_stream; it writes the step's miss
+ *      list into a pinned host buffer;
+ *   2. the host waits for it (one host wait per call; it also drains earlier
+ *      work of compute_stream, so no earlier kernel still reads a victim slot);
+ *   3. one hipMemcpyAsync host->device per miss is enqueued on copy_stream;
+ *   4. compute_stream is made to wait for those copies, and the call returns.
+ * Kernels that read the slot pool must run on compute_stream (or be ordered
+ * before the next ft_expert_cache_step call on it).
+ * Errors: FT_EINVAL (bad layer, T, k, NULLs); FT_ECAPACITY if the step needs
+ * more distinct experts than there are slots -- detected by the kernel; the
+ * cache state is then unchanged; FT_EHIP.  topk_ids out of 0..E-1 -> FT_EINVAL
+ * (detected by the kernel, state unchanged).
+ */
+ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids,
+                               int32_t T, int32_t k, int32_t *slot_of_expert,
+                               hipStream_t compute_stream);
+
+/* Totals since create (host).  */
+ft_status ft_expert_cache_stats(const ft_expert_cache *c, ft_cache_stats *out);
+
+/* Copy the event log into host_buf (host) as ft_cache_event records, events of
+ * one step in ascending expert id.  *needed (host, optional) receives the bytes
+ * the whole log takes; at most `bytes` are written (whole records only). */
+ft_status ft_expert_cache_trace(const ft_expert_cache *c, void *host_buf, size_t bytes,
+                                size_t *needed);
+
+/* Current slot of (layer, expert) according to the host mirror of the last
+ * completed step (-1 if not resident), written to *slot (host). */
+ft_status ft_expert_cache_lookup(const ft_expert_cache *c, int32_t layer, int32_t expert,
+                                 int32_t *slot);
+
+/* Free the cache's own state.  Waits for its pending copies first. */
+ft_status ft_expert_cache_destroy(ft_expert_cache *c);
+
+/* ------------------------------------------------------------------------ */
+/* Workspace sizes                                                            */
+/* ------------------------------------------------------------------------ */
+enum { FT_WS_PERMUTE = 1, FT_WS_FFN = 2 };
+
+/* Bytes of workspace the call `which` needs for these sizes (0 if none).
+ * For FT_WS_FFN, H and I are those of the layout and the shared expert is
+ * assumed present (an upper bound either way). */
+size_t ft_workspace_bytes(int32_t which, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FT_MOE_H */

@@ -1,0 +1,215 @@
+"""Parity of the device LRU expert cache and its miss fills against the oracle simulator."""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth
+from oracle import formats, moe
+from oracle.lru import CapacityError, ExpertLRU
+from tests.helpers import Experts, check_close
+from tests.test_oracle_lru import _traces
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from expert_cached_ffn_amd import layer, ops
+    ops.version()
+    return ops, layer
+
+
+class Rig:
+    """A cache over n_layers x E small experts with an identifiable pinned host bank."""
+
+    def __init__(self, ops, n_layers, E, C, H=128, I=128, wdtype=1, fill=True):
+        self.ops = ops
+        self.lay = ops.ft_expert_layout_init(wdtype, H, I)
+        self.eb = int(self.lay.expert_bytes)
+        self.n_layers, self.E, self.C = n_layers, E, C
+        self.bank = torch.empty((n_layers * E, self.eb), dtype=torch.uint8, pin_memory=True)
+        if fill:
+            rng = np.random.default_rng(n_layers * 1000 + E)
+            self.bank.numpy()[:] = rng.integers(0, 256, size=self.bank.shape, dtype=np.uint8)
+        self.pool = torch.zeros((C, self.eb), dtype=torch.uint8, device="cuda")
+        self.copy_stream = torch.cuda.Stream()
+        self.cache = ops.ExpertCache(self.lay, n_layers, E, C, self.pool, self.bank, self.copy_stream)
+        self.slot_of = torch.empty(E, dtype=torch.int32, device="cuda")
+
+    def step(self, layer, ids):
+        ids = np.asarray(ids, np.int32).reshape(-1)
+        d = torch.from_numpy(ids).cuda() if ids.size else torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.cache.step(layer, d, ids.size, 1, self.slot_of)
+
+
+def events_by_step(trace):
+    out = {}
+    for step, layer, e, hit, slot, ev in trace:
+        out.setdefault(step, []).append((e, bool(hit), slot, None if ev < 0 else ev))
+    return out
+
+
+def test_hand_traced_sequences_on_device(env, golden_dir):
+    ops, _ = env
+    for tr in _traces(golden_dir):
+        print(f"trace {tr['name']}", flush=True)
+        rig = Rig(ops, tr["L"], tr["E"], tr["C"], fill=False)
+        for _, layer, ids, _ in tr["steps"]:
+            rig.step(layer, ids)
+        got = events_by_step(rig.cache.trace())
+        E = tr["E"]
+        for i, (_, layer, ids, want) in enumerate(tr["steps"]):
+            want_k = [(e, h, s, None if ev is None else ev[0] * E + ev[1]) for e, h, s, ev in want]
+            assert got[i] == want_k, (tr["name"], i)
+        st = rig.cache.stats()
+        assert {k: st[k] for k in ("accesses", "hits", "misses", "evictions")} == tr["totals"]
+        rig.cache.destroy()
+
+
+def _compare_run(rig, steps):
+    """steps: list of (layer, ids). Runs both; checks events, slot tables, stats and filled bytes."""
+    sim = ExpertLRU(rig.n_layers, rig.E, rig.C)
+    E = rig.E
+    n_ok = 0
+    for layer, ids in steps:
+        try:
+            want = sim.step(layer, ids)
+            cap = False
+        except CapacityError:
+            cap = True
+        if cap:
+            with pytest.raises(rig.ops.FtError) as ei:
+                rig.step(layer, ids)
+            assert ei.value.status == -3
+            continue
+        rig.step(layer, ids)
+        torch.cuda.synchronize()
+        table = rig.slot_of.cpu().numpy()
+        assert table.tolist() == sim.slot_of_expert(layer)
+        n_ok += 1
+        # the filled slots hold exactly the host blobs of their (layer, expert)
+        for ev in want:
+            if not ev.hit:
+                src = rig.bank[layer * E + ev.expert]
+                assert torch.equal(rig.pool[ev.slot].cpu(), src)
+    got = events_by_step(rig.cache.trace())
+    want_all = {}
+    sim2 = ExpertLRU(rig.n_layers, rig.E, rig.C)
+    i = 0
+    for layer, ids in steps:
+        try:
+            evs = sim2.step(layer, ids)
+        except CapacityError:
+            continue
+        want_all[i] = [(e.expert, e.hit, e.slot, None if e.evicted is None else e.evicted[0] * E + e.evicted[1])
+                       for e in evs]
+        i += 1
+    assert got == want_all
+    st = rig.cache.stats()
+    assert (st["accesses"], st["hits"], st["misses"], st["evictions"]) == \
+        (sim.accesses, sim.hits, sim.misses, sim.evictions)
+    assert st["steps"] == n_ok
+    assert st["bytes_h2d"] == sim.misses * rig.eb
+    return sim
+
+
+def test_random_multi_token_traces(env):
+    ops, _ = env
+    rng = np.random.default_rng(5)
+    rig = Rig(ops, 3, 20, 9)
+    steps = []
+    for s in range(150):
+        layer = int(rng.integers(3))
+        T = int(rng.integers(0, 4))
+        ids = [rng.choice(20, size=2, replace=False) for _ in range(T)]
+        steps.append((layer, np.array(ids, np.int32).reshape(-1)))
+    steps.insert(40, (1, np.arange(12, dtype=np.int32)))   # 12 distinct > 9 slots -> capacity error
+    _compare_run(rig, steps)
+    rig.cache.destroy()
+
+
+def test_bad_expert_id_is_rejected_without_state_change(env):
+    ops, _ = env
+    rig = Rig(ops, 1, 8, 4)
+    rig.step(0, [1, 2])
+    with pytest.raises(ops.FtError) as ei:
+        rig.step(0, [3, 8])
+    assert ei.value.status == -1
+    rig.step(0, [2, 3])
+    evs = events_by_step(rig.cache.trace())
+    assert evs[1] == [(2, True, 1, None), (3, False, 2, None)]
+    rig.cache.destroy()
+
+
+def test_full_decode_trace_exact(env):
+    """The whole 8-layer x 512-step Zipf + reuse trace at 25 % capacity (small experts)."""
+    ops, _ = env
+    cfg = synth.CONFIGS[5]
+    tr = synth.cache_trace(cfg)
+    rig = Rig(ops, cfg.n_layers, cfg.E, cfg.capacity, fill=False)
+    steps = [(l, tr.ids[s, l]) for s in range(cfg.steps) for l in range(cfg.n_layers)]
+    print(f"trace of {len(steps)} layer-steps", flush=True)
+    sim = ExpertLRU(cfg.n_layers, cfg.E, cfg.capacity)
+    for layer, ids in steps:
+        sim.step(layer, ids)
+        rig.step(layer, ids)
+    got = rig.cache.trace()
+    st = rig.cache.stats()
+    assert (st["accesses"], st["hits"], st["misses"], st["evictions"]) == \
+        (sim.accesses, sim.hits, sim.misses, sim.evictions)
+    assert st["accesses"] == cfg.steps * cfg.n_layers * cfg.k
+    # event-by-event equality with a fresh simulator run
+    sim2 = ExpertLRU(cfg.n_layers, cfg.E, cfg.capacity)
+    want = []
+    for i, (layer, ids) in enumerate(steps):
+        for e in sim2.step(layer, ids):
+            want.append((i, layer, e.expert, int(e.hit), e.slot,
+                         -1 if e.evicted is None else e.evicted[0] * cfg.E + e.evicted[1]))
+    assert got == want
+    print(f"hit rate {st['hits'] / st['accesses']:.4f}", flush=True)
+    rig.cache.destroy()
+
+
+def test_layer_outputs_through_the_cache(env):
+    """Reduced decode trace: route (given logits) -> cache step -> permute -> FFN from slots -> combine."""
+    ops, Lm = env
+    cfg = synth.shrink(synth.CONFIGS[5], H=512, I=512, E=32, n_layers=2, capacity=10, steps=24)
+    tr = synth.cache_trace(cfg)
+    shape = Lm.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize, True)
+    layer = Lm.MoELayer(shape, 1)
+    lay = layer.layout
+    eb = int(lay.expert_bytes)
+    ex = [Experts(cfg, l) for l in range(cfg.n_layers)]
+    bank = torch.empty((cfg.n_layers * cfg.E, eb), dtype=torch.uint8, pin_memory=True)
+    for l in range(cfg.n_layers):
+        for e in range(cfg.E):
+            Lm.pack_expert(lay, ex[l].raw(e).arrays, bank.numpy()[l * cfg.E + e])
+    shared = [Lm.as_device_u8([Lm.pack_expert(lay, ex[l].raw(cfg.E).arrays)])[0] for l in range(cfg.n_layers)]
+    pool = torch.zeros((cfg.capacity, eb), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    cache = ops.ExpertCache(lay, cfg.n_layers, cfg.E, cfg.capacity, pool, bank, cs)
+    slot_of = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    for s in range(cfg.steps):
+        for l in range(cfg.n_layers):
+            x = synth.tokens(cfg, 1, layer=l, step=s)
+            layer.route(1, logits=Lm.to_device(tr.logits[s, l][None, :]))
+            cache.step(l, layer.ids, 1, cfg.k, slot_of)
+            layer.permute(1)
+            layer.ffn(1, Lm.to_device(x), pool, slot_of_expert=slot_of, shared_blob=shared[l])
+            layer.combine(1)
+            torch.cuda.synchronize()
+            got = formats.bf16_to_f64(layer.out[:1].cpu().numpy().view(np.uint16))[0]
+            ids = tr.ids[s, l]
+            assert layer.ids[0].cpu().numpy().tolist() == ids.tolist()
+            w = moe.gating_weights(tr.logits[s, l][None, :], ids[None, :], cfg.gating, cfg.renormalize)[0]
+            x64 = formats.activations_to_f64(cfg.xdtype, x)[0]
+            ref = moe.token_output(x64, ids, w, ex[l].f64, ex[l].f64(cfg.E))
+            check_close(got[None, :], ref[None, :], bf16_out=True, what=f"step {s} layer {l}")
+    st = cache.stats()
+    assert st["misses"] > 0 and st["hits"] > 0
+    cache.destroy()

@@ -1,0 +1,105 @@
+"""End-to-end parity of the whole layer (route -> permute -> FFN -> combine) on every workload shape."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth
+from oracle import formats, moe
+from tests.helpers import Experts, check_close, route_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from expert_cached_ffn_amd import layer as _layer
+    from expert_cached_ffn_amd import ops
+    ops.version()
+    return _layer
+
+
+def make_layer(Lm, cfg, T):
+    shape = Lm.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize,
+                          cfg.shared)
+    return Lm.MoELayer(shape, T)
+
+
+def build_pool(Lm, layer, ex, experts, n_slots):
+    """Device pool with expert e in slot e for e in `experts` (other slots zero, never read)."""
+    eb = int(layer.layout.expert_bytes)
+    pool = torch.zeros((n_slots, eb), dtype=torch.uint8, device="cuda")
+    buf = np.zeros(eb, np.uint8)
+    for e in experts:
+        buf[:] = 0
+        Lm.pack_expert(layer.layout, ex.raw(e).arrays, buf)
+        pool[e].copy_(torch.from_numpy(buf))
+    return pool
+
+
+def out_f64(layer, cfg, T):
+    o = layer.out[:T].cpu().numpy()
+    return formats.bf16_to_f64(o.view(np.uint16)) if cfg.xdtype == "bf16" else o.astype(np.float64)
+
+
+@pytest.mark.parametrize("cfg_id,T,sample", [(1, 8, None), (2, 1, None), (2, 16, None), (2, 64, 12),
+                                             (3, 1, None), (3, 8, 4), (3, 32, 4)])
+def test_layer_router_gemv(L, cfg_id, T, sample):
+    cfg = synth.CONFIGS[cfg_id]
+    print(f"layer cfg{cfg_id} T={T}", flush=True)
+    ex = Experts(cfg)
+    x = synth.tokens(cfg, T)
+    wr = synth.router_weight(cfg)
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    wr64 = formats.activations_to_f64(cfg.xdtype, wr)
+    logits, ids, w, margin = route_oracle(cfg, x64, wr64)
+    layer = make_layer(L, cfg, T)
+    pool = build_pool(L, layer, ex, sorted(set(ids.ravel().tolist())), cfg.E)
+    shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
+    layer.forward(T, L.to_device(x), pool, w_router=L.to_device(wr), shared_blob=shared)
+    torch.cuda.synchronize()
+    got = out_f64(layer, cfg, T)
+    got_ids = layer.ids[:T].cpu().numpy()
+    sure = np.flatnonzero(margin > 1e-4)
+    assert len(sure) >= 0.9 * T
+    assert np.array_equal(got_ids[sure], ids[sure])
+    toks = sure if sample is None else np.random.default_rng(T).choice(sure, size=min(sample, len(sure)), replace=False)
+    ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E) if cfg.shared else None)
+                    for t in toks])
+    check_close(got[toks], ref, bf16_out=cfg.xdtype == "bf16", what=f"cfg{cfg_id} T={T} out")
+
+
+def test_layer_prefill_given_logits(L):
+    """Prefill workload (8192 tokens, Zipf-skewed segments), sampled tokens + whole-output properties."""
+    cfg = synth.CONFIGS[4]
+    T = 8192
+    ex = Experts(cfg)
+    x = synth.tokens(cfg, T)
+    logits = synth.prefill_logits(cfg, T)
+    ids = moe.topk(logits, cfg.k)
+    w = moe.gating_weights(logits, ids, cfg.gating, cfg.renormalize)
+    layer = make_layer(L, cfg, T)
+    print("prefill: packing 257 experts", flush=True)
+    pool = build_pool(L, layer, ex, range(cfg.E), cfg.E)
+    shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0]
+    print("prefill: running", flush=True)
+    layer.forward(T, L.to_device(x), pool, logits=L.to_device(logits), shared_blob=shared)
+    torch.cuda.synchronize()
+    assert np.array_equal(layer.ids[:T].cpu().numpy(), ids)
+    off_ref, rows_ref, _ = moe.permute(ids, cfg.E)
+    assert np.array_equal(layer.offsets.cpu().numpy(), off_ref)
+    got = out_f64(layer, cfg, T)
+    assert np.all(np.isfinite(got))
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    toks = [0, 4097, T - 1]
+    ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E)) for t in toks])
+    check_close(got[toks], ref, bf16_out=True, what="prefill sampled tokens")
+    # one expert's whole segment in the permuted expert rows (the least popular non-empty expert)
+    sizes = np.diff(off_ref)
+    e = int(np.argmin(np.where(sizes > 0, sizes, 10 ** 9)))
+    a, b = int(off_ref[e]), int(off_ref[e + 1])
+    yr = layer.y_rows[a:b].cpu().numpy()
+    yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
+    check_close(yr, yref, what=f"prefill segment of expert {e}")
