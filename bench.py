@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X, with the roofline of its dominant kernel.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode-bf16|decode-mxfp4|prefill-mxfp4|cache-trace]
+
+A step is one pass of the whole layer -- route, permute, grouped SwiGLU FFN
+(weights through the slot table), combine; plus the cache step for the
+cache-trace workload -- over one batch of synthetic tokens whose inputs are
+already resident in HBM.  The default workload is the Qwen3-A3B-shaped bf16
+decode layer (H=2048, I=768, 128 experts, top-8 softmax renormalised) at a
+decode batch of 64 tokens; batches 1 and 16 are reported beside it.  Input
+sets rotate (8 different token batches, hence different routings) so the
+activated experts change every step.
+
+Prints one JSON line.  ``roofline`` is computed for the dominant kernel (the
+gate/up + SwiGLU stage of the grouped FFN) from its average duration measured
+with HIP events on the launch stream inside the timed region, against its
+algorithmic bytes.  ``cpu_baseline`` times the CPU oracle (float64 NumPy) on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (decode, prefill) + % HBM BW / % MFMA peak, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA bf16
+N_INPUT_SETS = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def build_pool(L, layer, cfg, experts, n_slots, layer_idx=0):
+    """All given experts packed into a device pool, expert e in slot e."""
+    import torch
+    import synth
+    eb = int(layer.layout.expert_bytes)
+    pool = torch.empty((n_slots, eb), dtype=torch.uint8, device="cuda")
+    buf = np.zeros(eb, np.uint8)
+    for e in experts:
+        L.pack_expert(layer.layout, synth.expert_weights(cfg, layer_idx, e).arrays, buf)
+        pool[e].copy_(torch.from_numpy(buf))
+    return pool
+
+
+def expert_weight_bytes(cfg, part):
+    """Bytes of one expert's gate+up ('gate_up') or down ('down') weights incl. scales."""
+    n = cfg.H * cfg.I
+    if cfg.wdtype == "mxfp4":
+        one = n // 2 + n // 32
+    elif cfg.wdtype == "bf16":
+        one = 2 * n
+    else:
+        one = 4 * n
+    return 2 * one if part == "gate_up" else one
+
+
+# ----------------------------------------------------------------------------- timing
+
+class Timer:
+    """HIP events on the current stream."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.ev = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.ev.append(e)
+        return e
+
+
+def run_decode(args, cfg, batches, main_T):
+    import torch
+    import synth
+    from expert_cached_ffn_amd import layer as L
+    from expert_cached_ffn_amd import _lib
+
+    torch.cuda.set_device(0)
+    shape = L.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize,
+                         cfg.shared)
+    probe = L.MoELayer(shape, 1)
+    t0 = time.time()
+    pool = build_pool(L, probe, cfg, range(cfg.E), cfg.E)
+    shared = None
+    if cfg.shared:
+        shared = L.as_device_u8([L.pack_expert(probe.layout, synth.expert_weights(cfg, 0, cfg.E).arrays)])[0]
+    wr = L.to_device(synth.router_weight(cfg))
+    torch.cuda.synchronize()
+    log(f"pool of {cfg.E} experts ({pool.numel() / 1e9:.2f} GB) built in {time.time() - t0:.1f}s")
+
+    results = {}
+    for T in batches:
+        layer = L.MoELayer(shape, T)
+        xs = [L.to_device(synth.tokens(cfg, T, case=r)) for r in range(N_INPUT_SETS)]
+        # distinct routed experts of every input set (for the algorithmic bytes)
+        n_act = []
+        for r in range(N_INPUT_SETS):
+            layer.forward(T, xs[r], pool, w_router=wr, shared_blob=shared)
+            torch.cuda.synchronize()
+            n_act.append(len(np.unique(layer.ids[:T].cpu().numpy())))
+
+        def step(i, tm=None):
+            x = xs[i % N_INPUT_SETS]
+            layer.route(T, x=x, w_router=wr)
+            layer.permute(T)
+            if tm is not None:
+                tm.mark()
+            layer.ffn(T, x, pool, shared_blob=shared, mode=_lib.FT_FFN_GATE_UP_ONLY)
+            if tm is not None:
+                tm.mark()
+            layer.ffn(T, x, pool, shared_blob=shared, mode=_lib.FT_FFN_DOWN_ONLY)
+            layer.combine(T, with_shared=shared is not None)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        tm = Timer()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(args.steps):
+            step(i, tm)
+        end.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        ms = total_ms / args.steps
+        k_ms = [tm.ev[2 * i].elapsed_time(tm.ev[2 * i + 1]) for i in range(args.steps)]
+        k_avg = float(np.mean(k_ms))
+        act = np.array([n_act[i % N_INPUT_SETS] for i in range(args.steps)], np.float64)
+        bytes_gu = float(np.mean((act + (1 if cfg.shared else 0)) * expert_weight_bytes(cfg, "gate_up")))
+        bytes_gu += T * cfg.H * 2 + (T * cfg.k + (T if cfg.shared else 0)) * cfg.I * 2
+        layer_bytes = float(np.mean((act + (1 if cfg.shared else 0)) *
+                                    (expert_weight_bytes(cfg, "gate_up") + expert_weight_bytes(cfg, "down"))))
+
+        # HIP-graph replay of the same step (one graph per input set)
+        graph_ms = None
+        if not args.no_graph:
+            graphs = []
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for r in range(N_INPUT_SETS):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=s):
+                        step(r)
+                    graphs.append(g)
+            torch.cuda.current_stream().wait_stream(s)
+            for i in range(args.warmup):
+                graphs[i % N_INPUT_SETS].replay()
+            torch.cuda.synchronize()
+            start.record()
+            for i in range(args.steps):
+                graphs[i % N_INPUT_SETS].replay()
+            end.record()
+            torch.cuda.synchronize()
+            graph_ms = start.elapsed_time(end) / args.steps
+        results[T] = dict(ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), gate_up_ms=k_avg,
+                          gate_up_bytes=bytes_gu, layer_weight_bytes=layer_bytes,
+                          distinct_experts=float(np.mean(n_act)), graph_ms_per_step=graph_ms)
+        gtxt = f"{graph_ms * 1e3:.1f} us" if graph_ms is not None else "n/a"
+        log(f"T={T}: {ms * 1e3:.1f} us/step ({T / (ms * 1e-3):,.0f} tok/s), gate/up {k_avg * 1e3:.1f} us "
+            f"= {bytes_gu / (k_avg * 1e-3) / 1e9:,.0f} GB/s, graph {gtxt}, "
+            f"layer weights {layer_bytes / (ms * 1e-3) / 1e9:,.0f} GB/s")
+        del layer, xs
+    if args.copy_calibration:
+        copy_calibration()
+    return results
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, so HBM counters can be scaled."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} x {nbytes} B device copy")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline_decode(cfg, T):
+    """The oracle on one layer call of the workload (input set 0), timed on this host."""
+    import synth
+    from oracle import formats, moe
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    x = synth.tokens(cfg, T, case=0)
+    wr = synth.router_weight(cfg)
+    raw = {}
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    wr64 = formats.activations_to_f64(cfg.xdtype, wr)
+    ids = moe.topk(moe.router_logits(x64, wr64), cfg.k)
+    for e in sorted(set(ids.ravel().tolist())) + ([cfg.E] if cfg.shared else []):
+        raw[e] = synth.expert_weights(cfg, 0, e).arrays        # input generation: not timed
+    t0 = time.perf_counter()
+    r = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                      experts=lambda e: formats.expert_to_f64(cfg.wdtype, raw[e]),
+                      shared=formats.expert_to_f64(cfg.wdtype, raw[cfg.E]) if cfg.shared else None,
+                      w_router=wr64)
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(r["out"]))
+    return dict(value=T / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"one {T}-token layer call (input set 0): route, permute, {len(raw)} expert FFNs "
+                       f"with weight decode, combine; {dt:.2f} s")
+
+
+# ----------------------------------------------------------------------------- main
+
+WORKLOADS = {
+    "decode-bf16": (2, "qwen3-a3b-shaped bf16 decode MoE layer (H=2048, I=768, 128 experts, top-8 softmax "
+                       "renormalised, SwiGLU)"),
+    "decode-mxfp4": (3, "dsv4-flash-shaped MXFP4 decode MoE layer (H=4096, I=2048, 256 experts top-6 sigmoid "
+                        "+ 1 shared, SwiGLU)"),
+}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode-bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--batch", type=int, default=None, help="main decode batch (default: largest of the workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (to scale HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import synth
+    cfg_id, desc = WORKLOADS[args.workload]
+    cfg = synth.CONFIGS[cfg_id]
+    batches = list(cfg.batches)
+    main_T = args.batch or max(batches)
+    if main_T not in batches:
+        batches.append(main_T)
+    res = run_decode(args, cfg, batches, main_T)
+    m = res[main_T]
+    ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.wdtype == "bf16" else "mxfp4-w/bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "batch_tokens": main_T, "input_sets": N_INPUT_SETS,
+                   "distinct_experts_per_step": m["distinct_experts"]},
+        "roofline": {"bound": "hbm", "kernel": f"ffn_stream_kernel<{'bf16' if cfg.wdtype == 'bf16' else 'mxfp4'}, gate_up>",
+                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                     "traffic": None, "avg_launch_us": m["gate_up_ms"] * 1e3,
+                     "algorithmic_bytes_per_launch": m["gate_up_bytes"]},
+        "layer_weight_GBps": m["layer_weight_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9,
+        "graph_ms_per_step": m["graph_ms_per_step"],
+        "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                             "graph_ms_per_step": r["graph_ms_per_step"],
+                             "gate_up_GBps": r["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9,
+                             "layer_weight_GBps": r["layer_weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9}
+                    for T, r in sorted(res.items())},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(cfg, main_T)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

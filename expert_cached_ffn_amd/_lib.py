@@ -14,6 +14,7 @@ STATUS_NAMES = {0: "FT_OK", -1: "FT_EINVAL", -2: "FT_ENOTSUP", -3: "FT_ECAPACITY
 FT_F32, FT_BF16, FT_MXFP4 = 0, 1, 2
 FT_SOFTMAX, FT_SIGMOID = 0, 1
 FT_WS_PERMUTE, FT_WS_FFN = 1, 2
+FT_FFN_GATE_UP_ONLY, FT_FFN_DOWN_ONLY = 0x100, 0x200
 
 EXPORTS = [
     "ft_last_error", "ft_version", "ft_expert_layout_init", "ft_moe_route", "ft_moe_permute",

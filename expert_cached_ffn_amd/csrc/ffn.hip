@@ -11,8 +11,12 @@
 //   stage 2  y = h Wd^T                    -> fp32 y_rows / y_shared
 // bf16 / MXFP4 weights use the weight-streaming MFMA tile (stream_gemm.hpp);
 // fp32 weights use a plain FMA kernel.
+#include <mutex>
+#include <unordered_map>
+
 #include "ft_internal.hpp"
 #include "stream_gemm.hpp"
+#include "stream_persist.hpp"
 
 namespace ft {
 
@@ -26,23 +30,29 @@ size_t ffn_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I
 
 // Block-wide: index of the aidx-th expert with a non-empty segment (ascending
 // expert id), or -1; *n_active = number of non-empty segments.
+template <int THREADS>
 __device__ int find_active_expert(const int32_t *__restrict__ off, int E, int aidx, int *n_active) {
-  __shared__ int s_cnt[4];
+  constexpr int NW = THREADS / 64;
+  __shared__ int s_cnt[NW];
   __shared__ int s_found;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (tid == 0) s_found = -1;
   int base = 0;
-  for (int c0 = 0; c0 < E; c0 += kStreamThreads) {
+  for (int c0 = 0; c0 < E; c0 += THREADS) {
     const int e = c0 + tid;
     const bool f = e < E && off[e + 1] > off[e];
     const uint64_t mask = __ballot(f);
     const int lp = __popcll(mask & ((uint64_t(1) << lane) - 1));
     if (lane == 0) s_cnt[wave] = __popcll(mask);
     __syncthreads();
-    int before = base;
-    for (int w = 0; w < wave; ++w) before += s_cnt[w];
+    int before = base, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) before += s_cnt[w];
+      total += s_cnt[w];
+    }
     if (f && before + lp == aidx) s_found = e;
-    base += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    base += total;
     __syncthreads();
   }
   *n_active = base;
@@ -61,6 +71,7 @@ struct FfnArgs {
   const int32_t *sorted_rows;  // stage 1: token of permuted row p is sorted_rows[p] / k
   const uint16_t *X;           // stage 1: x; stage 2: h rows
   int64_t ldx;
+  uint32_t x_bytes;            // bytes of X
   void *out;                   // stage 1: h rows (bf16); stage 2: y_rows (fp32)
   int64_t ldo;
   float *out_shared;           // stage 2: y_shared
@@ -68,15 +79,17 @@ struct FfnArgs {
   int has_shared;
 };
 
-// Grid: (upper bound of active experts incl. shared) x n_tiles workgroups.
-template <int WF, bool STAGE1>
-__global__ __launch_bounds__(kStreamThreads) void ffn_stream_kernel(FfnArgs a) {
-  __shared__ int s_tok[kStreamMaxTok], s_orow[kStreamMaxTok];
-  __shared__ float s_red[stream_red_floats<STAGE1, 4>()];
+// Grid: (upper bound of active experts incl. shared) x n_tiles workgroups of
+// WAVES waves; tokens of a segment are processed 16*NTMAX at a time.
+template <int WF, bool STAGE1, int NTMAX, int WAVES, bool PIPE>
+__global__ __launch_bounds__(WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
+  constexpr int THREADS = WAVES * 64, GROUP = 16 * NTMAX;
+  __shared__ int s_tok[GROUP], s_orow[GROUP];
+  __shared__ float s_red[stream_red_floats<STAGE1, NTMAX, WAVES>()];
   const int tid = threadIdx.x;
   const int aidx = blockIdx.x / a.n_tiles, tile = blockIdx.x % a.n_tiles;
   int n_act;
-  const int e = find_active_expert(a.offsets, a.E, aidx, &n_act);
+  const int e = find_active_expert<THREADS>(a.offsets, a.E, aidx, &n_act);
   const bool is_shared = e < 0 && a.has_shared && aidx == n_act;
   if (e < 0 && !is_shared) return;
 
@@ -93,7 +106,7 @@ __global__ __launch_bounds__(kStreamThreads) void ffn_stream_kernel(FfnArgs a) {
     if (slot < 0) {
       // Caller error: the expert is not resident.  Mark its rows NaN.
       const int row0 = tile * 16;
-      for (int u = tid; u < m * 16; u += kStreamThreads) {
+      for (int u = tid; u < m * 16; u += THREADS) {
         const int j = u / 16, n = row0 + (u % 16);
         if (n >= a.N) continue;
         if (STAGE1)
@@ -110,8 +123,8 @@ __global__ __launch_bounds__(kStreamThreads) void ffn_stream_kernel(FfnArgs a) {
   void *out = a.out;
   if (!STAGE1 && is_shared) out = a.out_shared;
 
-  for (int g0 = 0; g0 < m; g0 += kStreamMaxTok) {
-    const int mm = min(kStreamMaxTok, m - g0);
+  for (int g0 = 0; g0 < m; g0 += GROUP) {
+    const int mm = min(GROUP, m - g0);
     if (tid < mm) {
       const int p = pos0 + g0 + tid;
       if (STAGE1) {
@@ -123,9 +136,106 @@ __global__ __launch_bounds__(kStreamThreads) void ffn_stream_kernel(FfnArgs a) {
       }
     }
     __syncthreads();
-    stream_tile_any<WF, STAGE1>(w0, s0, w1, s1, a.K, tile * 16, a.N, a.X, a.ldx, s_tok, mm, s_red, out,
-                                a.ldo, s_orow);
+    stream_tile_any<WF, STAGE1, NTMAX, WAVES, PIPE>(w0, s0, w1, s1, a.K, tile * 16, a.N, a.X, a.ldx, a.x_bytes,
+                                                    s_tok, mm, s_red, out, a.ldo, s_orow);
   }
+}
+
+// Launch one stage with the wave count / token grouping suited to T and K.
+template <int WF, bool STAGE1>
+static ft_status launch_stream(const FfnArgs &a, int a_max, int T, hipStream_t stream, const char *name) {
+  const dim3 grid(unsigned(a_max * a.n_tiles));
+  const StreamShape sh = stream_shape(T, a.K / stream_kblock<WF>());
+#define FT_STREAM(NT, W, P)                                                                                   \
+  if (sh.ntmax == NT && sh.waves == W && sh.pipe == P)                                                        \
+    hipLaunchKernelGGL((ffn_stream_kernel<WF, STAGE1, NT, W, P>), grid, dim3(W * 64), 0, stream, a);
+  FT_STREAM(1, 16, false)
+  FT_STREAM(1, 16, true)
+  FT_STREAM(1, 8, false)
+  FT_STREAM(1, 8, true)
+  FT_STREAM(1, 6, false)
+  FT_STREAM(1, 6, true)
+  FT_STREAM(1, 4, false)
+  FT_STREAM(1, 4, true)
+  FT_STREAM(2, 16, false)
+  FT_STREAM(2, 16, true)
+  FT_STREAM(2, 8, false)
+  FT_STREAM(2, 8, true)
+  FT_STREAM(2, 6, false)
+  FT_STREAM(2, 6, true)
+  FT_STREAM(2, 4, false)
+  FT_STREAM(2, 4, true)
+#undef FT_STREAM
+  FT_LAUNCHED(name);
+  return FT_OK;
+}
+
+// ------------------------------------------------------------------ persistent decode path
+
+template <int WF, bool GLU, int WAVES, int KPW>
+__global__ __launch_bounds__(WAVES * 64) void ffn_persist_kernel(PersistArgs a) {
+  __shared__ float s_red[WAVES * (GLU ? 2 : 1) * 256];
+  stream_persist<WF, GLU, WAVES, KPW>(a, s_red);
+}
+
+// Resident workgroups per CU of a kernel (cached) times the CU count.
+static int resident_grid(const void *kernel, int threads) {
+  static std::mutex mu;
+  static std::unordered_map<const void *, int> cache;
+  static int cus = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  auto it = cache.find(kernel);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0) {
+    (void)hipGetLastError();
+    per_cu = 1;
+  }
+  const int g = per_cu * cus;
+  cache[kernel] = g;
+  return g;
+}
+
+// Waves per workgroup x k-blocks per wave covering nkb exactly, or {0, 0}.
+static void persist_shape(int nkb, int *waves, int *kpw) {
+  *waves = 0;
+  *kpw = 0;
+  for (int c : {1, 2})
+    for (int w : {16, 12, 8, 6, 4})
+      if (w * c == nkb && (c == 1 || w <= 8)) {  // wider 2-block shapes exceed the register budget
+        *waves = w;
+        *kpw = c;
+        return;
+      }
+}
+
+template <int WF, bool GLU>
+static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stream) {
+  int waves, kpw;
+  persist_shape(a.K / stream_kblock<WF>(), &waves, &kpw);
+#define FT_PERSIST(W, C)                                                                    \
+  if (waves == W && kpw == C) {                                                             \
+    const void *kern = reinterpret_cast<const void *>(&ffn_persist_kernel<WF, GLU, W, C>); \
+    const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));           \
+    hipLaunchKernelGGL((ffn_persist_kernel<WF, GLU, W, C>), dim3(g), dim3(W * 64), 0, stream, a); \
+    return true;                                                                            \
+  }
+  FT_PERSIST(16, 1)
+  FT_PERSIST(12, 1)
+  FT_PERSIST(8, 1)
+  FT_PERSIST(6, 1)
+  FT_PERSIST(4, 1)
+  FT_PERSIST(8, 2)
+  FT_PERSIST(6, 2)
+  FT_PERSIST(4, 2)
+#undef FT_PERSIST
+  return false;
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -230,9 +340,17 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   FT_REQUIRE(L != nullptr, "ft_moe_grouped_ffn: layout is NULL");
   FT_REQUIRE(T >= 0 && k >= 1 && E >= 1, "ft_moe_grouped_ffn: need T >= 0, k >= 1, E >= 1");
   FT_REQUIRE(int64_t(T) * (k + 1) < (int64_t(1) << 31), "ft_moe_grouped_ffn: T*k too large");
+  FT_SUPPORTED((int64_t(T) * (k + 1)) * L->I * 2 < (int64_t(1) << 31) && int64_t(T) * L->H * 2 < (int64_t(1) << 31) &&
+                   int64_t(L->H) * L->I * 2 < (int64_t(1) << 31),
+               "ft_moe_grouped_ffn: activation, hidden or weight matrix above 2 GiB");
   FT_SUPPORTED(k <= E, "ft_moe_grouped_ffn: k > E");
   FT_SUPPORTED(E <= 4096, "ft_moe_grouped_ffn: E > 4096");
-  FT_SUPPORTED(mode == 0, "ft_moe_grouped_ffn: only mode 0 (exact bf16 MFMA path) is implemented");
+  const int stages = mode & (FT_FFN_GATE_UP_ONLY | FT_FFN_DOWN_ONLY);
+  FT_REQUIRE(stages != (FT_FFN_GATE_UP_ONLY | FT_FFN_DOWN_ONLY),
+             "ft_moe_grouped_ffn: FT_FFN_GATE_UP_ONLY and FT_FFN_DOWN_ONLY together");
+  FT_REQUIRE((mode & ~0x3ff) == 0, "ft_moe_grouped_ffn: unknown mode bits");
+  FT_SUPPORTED((mode & 0xff) == 0, "ft_moe_grouped_ffn: only mode 0 (exact bf16 MFMA path) is implemented");
+  const bool run1 = stages != FT_FFN_DOWN_ONLY, run2 = stages != FT_FFN_GATE_UP_ONLY;
   const int H = L->H, I = L->I;
   FT_REQUIRE(H >= 1 && I >= 1 && L->expert_bytes > 0, "ft_moe_grouped_ffn: layout not initialised");
   const int wd = L->wdtype;
@@ -243,7 +361,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     FT_SUPPORTED(H % 128 == 0 && I % 128 == 0, "ft_moe_grouped_ffn: bf16 weights need H, I multiples of 128");
   } else if (wd == FT_MXFP4) {
     FT_REQUIRE(x_dtype == FT_BF16, "ft_moe_grouped_ffn: MXFP4 weights need bf16 activations");
-    FT_SUPPORTED(H % 512 == 0 && I % 512 == 0, "ft_moe_grouped_ffn: MXFP4 weights need H, I multiples of 512");
+    FT_SUPPORTED(H % 256 == 0 && I % 256 == 0, "ft_moe_grouped_ffn: MXFP4 weights need H, I multiples of 256");
   } else {
     return fail(FT_EINVAL, "ft_moe_grouped_ffn: unknown weight dtype in layout");
   }
@@ -291,10 +409,14 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     a.y_shared = y_shared;
     a.rows = rows;
     const int64_t n1 = int64_t(rows) * I, n2 = int64_t(rows) * H;
-    hipLaunchKernelGGL(ffn_f32_stage1, dim3(unsigned(cdiv<int64_t>(n1, 256))), dim3(256), 0, stream, a);
-    FT_LAUNCHED("ffn_f32_stage1");
-    hipLaunchKernelGGL(ffn_f32_stage2, dim3(unsigned(cdiv<int64_t>(n2, 256))), dim3(256), 0, stream, a);
-    FT_LAUNCHED("ffn_f32_stage2");
+    if (run1) {
+      hipLaunchKernelGGL(ffn_f32_stage1, dim3(unsigned(cdiv<int64_t>(n1, 256))), dim3(256), 0, stream, a);
+      FT_LAUNCHED("ffn_f32_stage1");
+    }
+    if (run2) {
+      hipLaunchKernelGGL(ffn_f32_stage2, dim3(unsigned(cdiv<int64_t>(n2, 256))), dim3(256), 0, stream, a);
+      FT_LAUNCHED("ffn_f32_stage2");
+    }
     clear_error();
     return FT_OK;
   }
@@ -323,6 +445,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   s1.N = I;
   s1.X = static_cast<const uint16_t *>(x);
   s1.ldx = H;
+  s1.x_bytes = uint32_t(uint64_t(T) * H * 2);
   s1.out = hbuf;
   s1.ldo = I;
   s1.n_tiles = cdiv(I, 16);
@@ -336,22 +459,85 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   s2.N = H;
   s2.X = hbuf;
   s2.ldx = I;
+  s2.x_bytes = uint32_t(uint64_t(rows) * I * 2);
   s2.out = y_rows;
   s2.ldo = H;
   s2.out_shared = y_shared;
   s2.n_tiles = cdiv(H, 16);
 
-  const dim3 blk(kStreamThreads);
+  // Decode batches: persistent weight-streaming kernels.
+  if (T <= 64 && E <= kPersistMaxE) {
+    PersistArgs p1{};
+    p1.pool = a.pool;
+    p1.slot_of_expert = slot_of_expert;
+    p1.expert_bytes = L->expert_bytes;
+    p1.shared_blob = a.shared_blob;
+    p1.offsets = expert_offsets;
+    p1.E = E;
+    p1.T = T;
+    p1.k = k;
+    PersistArgs p2 = p1;
+    p1.off_w0 = L->off_gate;
+    p1.off_w1 = L->off_up;
+    p1.off_s0 = L->off_sgate;
+    p1.off_s1 = L->off_sup;
+    p1.K = H;
+    p1.N = I;
+    p1.sorted_rows = sorted_rows;
+    p1.X = static_cast<const uint16_t *>(x);
+    p1.ldx = H;
+    p1.x_bytes = uint32_t(uint64_t(T) * H * 2);
+    p1.out = hbuf;
+    p1.ldo = I;
+    p1.n_tiles = cdiv(I, 16);
+    p2.off_w0 = p2.off_w1 = L->off_down;
+    p2.off_s0 = p2.off_s1 = L->off_sdown;
+    p2.K = I;
+    p2.N = H;
+    p2.sorted_rows = nullptr;
+    p2.X = hbuf;
+    p2.ldx = I;
+    p2.x_bytes = uint32_t(uint64_t(rows) * I * 2);
+    p2.out = y_rows;
+    p2.ldo = H;
+    p2.out_shared = y_shared;
+    p2.n_tiles = cdiv(H, 16);
+    const int groups = cdiv(T, 16);
+    // stage by stage; a contraction length no persistent shape covers uses the general kernel
+    if (wd == FT_BF16) {
+      if (run1 && !launch_persist<WF_BF16, true>(p1, a_max * p1.n_tiles * groups, stream)) {
+        const ft_status st = launch_stream<WF_BF16, true>(s1, a_max, T, stream, "ffn_stream_kernel<bf16, gate_up>");
+        if (st != FT_OK) return st;
+      }
+      if (run2 && !launch_persist<WF_BF16, false>(p2, a_max * p2.n_tiles * groups, stream)) {
+        const ft_status st = launch_stream<WF_BF16, false>(s2, a_max, T, stream, "ffn_stream_kernel<bf16, down>");
+        if (st != FT_OK) return st;
+      }
+    } else {
+      if (run1 && !launch_persist<WF_FP4, true>(p1, a_max * p1.n_tiles * groups, stream)) {
+        const ft_status st = launch_stream<WF_FP4, true>(s1, a_max, T, stream, "ffn_stream_kernel<mxfp4, gate_up>");
+        if (st != FT_OK) return st;
+      }
+      if (run2 && !launch_persist<WF_FP4, false>(p2, a_max * p2.n_tiles * groups, stream)) {
+        const ft_status st = launch_stream<WF_FP4, false>(s2, a_max, T, stream, "ffn_stream_kernel<mxfp4, down>");
+        if (st != FT_OK) return st;
+      }
+    }
+    FT_LAUNCHED("ffn_persist_kernel");
+    clear_error();
+    return FT_OK;
+  }
+  ft_status st = FT_OK;
   if (wd == FT_BF16) {
-    hipLaunchKernelGGL((ffn_stream_kernel<WF_BF16, true>), dim3(a_max * s1.n_tiles), blk, 0, stream, s1);
-    FT_LAUNCHED("ffn_stream_kernel<bf16, gate_up>");
-    hipLaunchKernelGGL((ffn_stream_kernel<WF_BF16, false>), dim3(a_max * s2.n_tiles), blk, 0, stream, s2);
-    FT_LAUNCHED("ffn_stream_kernel<bf16, down>");
+    if (run1 && (st = launch_stream<WF_BF16, true>(s1, a_max, T, stream, "ffn_stream_kernel<bf16, gate_up>")) != FT_OK)
+      return st;
+    if (run2 && (st = launch_stream<WF_BF16, false>(s2, a_max, T, stream, "ffn_stream_kernel<bf16, down>")) != FT_OK)
+      return st;
   } else {
-    hipLaunchKernelGGL((ffn_stream_kernel<WF_FP4, true>), dim3(a_max * s1.n_tiles), blk, 0, stream, s1);
-    FT_LAUNCHED("ffn_stream_kernel<mxfp4, gate_up>");
-    hipLaunchKernelGGL((ffn_stream_kernel<WF_FP4, false>), dim3(a_max * s2.n_tiles), blk, 0, stream, s2);
-    FT_LAUNCHED("ffn_stream_kernel<mxfp4, down>");
+    if (run1 && (st = launch_stream<WF_FP4, true>(s1, a_max, T, stream, "ffn_stream_kernel<mxfp4, gate_up>")) != FT_OK)
+      return st;
+    if (run2 && (st = launch_stream<WF_FP4, false>(s2, a_max, T, stream, "ffn_stream_kernel<mxfp4, down>")) != FT_OK)
+      return st;
   }
   clear_error();
   return FT_OK;

@@ -16,18 +16,21 @@ namespace ft {
 // ------------------------------------------------------------------ logits
 
 // bf16: logits[t, e] = sum_h x[t, h] W_r[e, h] on MFMA; one workgroup per
-// (16 experts, 64 tokens).
-__global__ __launch_bounds__(kStreamThreads) void router_logits_bf16(const uint16_t *__restrict__ x,
-                                                                     const uint8_t *__restrict__ wr,
-                                                                     float *__restrict__ logits, int T,
-                                                                     int H, int E) {
-  __shared__ int s_tok[kStreamMaxTok];
-  __shared__ float s_red[stream_red_floats<false, 4>()];
-  const int tile = blockIdx.x, g0 = blockIdx.y * kStreamMaxTok;
-  const int mm = min(kStreamMaxTok, T - g0);
+// (16 experts, 16*NTMAX tokens), its waves splitting the hidden axis.
+template <int NTMAX, int WAVES, bool PIPE>
+__global__ __launch_bounds__(WAVES * 64) void router_logits_bf16(const uint16_t *__restrict__ x,
+                                                                 const uint8_t *__restrict__ wr,
+                                                                 float *__restrict__ logits, int T, int H, int E) {
+  constexpr int GROUP = 16 * NTMAX;
+  __shared__ int s_tok[GROUP];
+  __shared__ float s_red[stream_red_floats<false, NTMAX, WAVES>()];
+  const int tile = blockIdx.x, g0 = blockIdx.y * GROUP;
+  const int mm = min(GROUP, T - g0);
   if (threadIdx.x < mm) s_tok[threadIdx.x] = g0 + threadIdx.x;
   __syncthreads();
-  stream_tile_any<WF_BF16, false>(wr, wr, wr, wr, H, tile * 16, E, x, H, s_tok, mm, s_red, logits, E, s_tok);
+  stream_tile_any<WF_BF16, false, NTMAX, WAVES, PIPE>(wr, wr, wr, wr, H, tile * 16, E, x, H,
+                                                      uint32_t(uint64_t(T) * H * 2), s_tok, mm, s_red, logits, E,
+                                                      s_tok);
 }
 
 // fp32: one thread per (token, expert).
@@ -53,101 +56,85 @@ __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-// One wave per token: k rounds of a wave-wide arg-max over the lanes'
-// remaining logits, then the gating weights of the picked experts.  Pick j is
-// kept by lane j % 64 (slot j / 64); no LDS and no barrier.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// One wave per token.  The token's logits go to LDS; every lane ranks its own
+// logits against all E (rank = number of logits that come before it in the
+// order (-logit, index)), so pick j is the logit of rank j -- no serial
+// arg-max rounds.  Then the gating weights of the picked experts.
 template <int VPL>
 __global__ __launch_bounds__(64 * kTopkWaves) void topk_gating_kernel(const float *__restrict__ logits,
                                                                        int T, int E, int k, int gating,
                                                                        int renorm, int32_t *__restrict__ ids,
                                                                        float *__restrict__ w) {
-  constexpr int KPL = kMaxK / 64;
+  __shared__ float s_l[kTopkWaves][kMaxE];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkWaves + wave;
-  if (t >= T) return;  // whole wave leaves together
-  const float *lr = logits + int64_t(t) * E;
+  const bool active = t < T;
+  const float *lr = logits + int64_t(active ? t : 0) * E;
   float v[VPL];
-  bool live[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    live[i] = e < E;
-    float x = live[i] ? lr[e] : -INFINITY;
+    float x = (active && e < E) ? lr[e] : -INFINITY;
     if (x == 0.0f) x = 0.0f;  // -0.0 and +0.0 are the same key
     v[i] = x;
+    if (e < E) s_l[wave][e] = x;
   }
-  float kv[KPL];
-  int ki[KPL];
+  __syncthreads();
+  if (!active) return;
+  int rank[VPL];
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    kv[s] = 0.f;
-    ki[s] = 0;
+  for (int i = 0; i < VPL; ++i) rank[i] = 0;
+  const int E4 = E & ~3;
+  for (int e = 0; e < E4; e += 4) {
+    const f32x4 o = *reinterpret_cast<const f32x4 *>(&s_l[wave][e]);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int me = lane + 64 * i;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rank[i] += int(o[c] > v[i]) + (int(o[c] == v[i]) & int(e + c < me));
+    }
   }
-  float mx = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  for (int e = E4; e < E; ++e) {
+    const float o = s_l[wave][e];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (live[i] && better(v[i], lane + 64 * i, bv, bi)) {
-        bv = v[i];
-        bi = lane + 64 * i;
-      }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (j == 0) mx = bv;  // the largest logit of the token
-    if ((bi & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (bi == lane + 64 * i) live[i] = false;
-    }
-    if ((j & 63) == lane) {
-#pragma unroll
-      for (int s = 0; s < KPL; ++s)
-        if ((j >> 6) == s) {
-          kv[s] = bv;
-          ki[s] = bi;
-        }
-    }
+    for (int i = 0; i < VPL; ++i) rank[i] += int(o > v[i]) + (int(o == v[i]) & int(e < lane + 64 * i));
   }
   // Gating.  softmax: p_e = exp(l_e - max) / sum_E exp(l - max); sigmoid: 1/(1+exp(-l)).
+  float mx = v[0];
+#pragma unroll
+  for (int i = 1; i < VPL; ++i) mx = fmaxf(mx, v[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float denom = 1.0f;
   if (gating == FT_SOFTMAX) {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
       if (lane + 64 * i < E) s += expf(v[i] - mx);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    denom = s;
+    denom = wave_sum(s);
   }
-  float p[KPL];
+  float p[VPL];
   float local = 0.f;
 #pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    const int j = s * 64 + lane;
-    p[s] = 0.f;
-    if (j < k) {
-      p[s] = gating == FT_SOFTMAX ? expf(kv[s] - mx) / denom : 1.0f / (1.0f + expf(-kv[s]));
-      local += p[s];
+  for (int i = 0; i < VPL; ++i) {
+    p[i] = 0.f;
+    if (lane + 64 * i < E && rank[i] < k) {
+      p[i] = gating == FT_SOFTMAX ? expf(v[i] - mx) / denom : 1.0f / (1.0f + expf(-v[i]));
+      local += p[i];
     }
   }
-  float wsum = local;
+  const float wsum = renorm ? wave_sum(local) : 1.0f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
-#pragma unroll
-  for (int s = 0; s < KPL; ++s) {
-    const int j = s * 64 + lane;
-    if (j < k) {
-      ids[int64_t(t) * k + j] = ki[s];
-      w[int64_t(t) * k + j] = renorm ? p[s] / wsum : p[s];
+  for (int i = 0; i < VPL; ++i) {
+    if (lane + 64 * i < E && rank[i] < k) {
+      ids[int64_t(t) * k + rank[i]] = lane + 64 * i;
+      w[int64_t(t) * k + rank[i]] = renorm ? p[i] / wsum : p[i];
     }
   }
 }
@@ -169,7 +156,11 @@ extern "C" ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_
   if (w_router != nullptr) {
     FT_REQUIRE(H >= 1, "ft_moe_route: H must be positive");
     FT_REQUIRE(x_dtype == FT_F32 || x_dtype == FT_BF16, "ft_moe_route: x_dtype must be FT_F32 or FT_BF16");
-    if (x_dtype == FT_BF16) FT_SUPPORTED(H % 128 == 0, "ft_moe_route: bf16 router needs H multiple of 128");
+    if (x_dtype == FT_BF16) {
+      FT_SUPPORTED(H % 128 == 0, "ft_moe_route: bf16 router needs H multiple of 128");
+      FT_SUPPORTED(int64_t(T) * H * 2 < (int64_t(1) << 31) && int64_t(E) * H * 2 < (int64_t(1) << 31),
+                   "ft_moe_route: x or w_router above 2 GiB");
+    }
   }
   if (T == 0) {
     clear_error();
@@ -182,10 +173,23 @@ extern "C" ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_
     FT_REQUIRE(x != nullptr, "ft_moe_route: x is NULL");
     FT_REQUIRE(aligned(x, 16) && aligned(w_router, 16), "ft_moe_route: x / w_router must be 16-byte aligned");
     if (x_dtype == FT_BF16) {
-      dim3 grid(unsigned(cdiv(E, 16)), unsigned(cdiv(T, kStreamMaxTok)));
-      hipLaunchKernelGGL(router_logits_bf16, grid, dim3(kStreamThreads), 0, stream,
-                         static_cast<const uint16_t *>(x), static_cast<const uint8_t *>(w_router), logits,
-                         T, H, E);
+      const uint16_t *xb = static_cast<const uint16_t *>(x);
+      const uint8_t *wb = static_cast<const uint8_t *>(w_router);
+      // all the waves of a workgroup split the hidden axis; 16 tokens per workgroup
+      const dim3 g1(unsigned(cdiv(E, 16)), unsigned(cdiv(T, 16)));
+      const StreamShape sh = stream_shape(1, H / stream_kblock<WF_BF16>());
+#define FT_ROUTER(W, P)                                                                                  \
+  if (sh.waves == W && sh.pipe == P)                                                                     \
+    hipLaunchKernelGGL((router_logits_bf16<1, W, P>), g1, dim3(W * 64), 0, stream, xb, wb, logits, T, H, E);
+      FT_ROUTER(16, false)
+      FT_ROUTER(16, true)
+      FT_ROUTER(8, false)
+      FT_ROUTER(8, true)
+      FT_ROUTER(6, false)
+      FT_ROUTER(6, true)
+      FT_ROUTER(4, false)
+      FT_ROUTER(4, true)
+#undef FT_ROUTER
       FT_LAUNCHED("router_logits_bf16");
     } else {
       const int64_t n = int64_t(T) * E;

@@ -3,21 +3,34 @@
 //   Y[tok][n] = sum_k W[n][k] * X[tok][k]      (one matrix), or
 //   h[tok][n] = silu(G) * U with G, U the same product for two matrices.
 //
-// Work split: one 256-thread workgroup owns 16 weight rows (per matrix) and up
-// to 64 tokens; its four waves take interleaved k-blocks of the contraction
-// axis and their partial tiles are summed in LDS.  Weights stream straight
-// from HBM into MFMA A-operand registers; each lane reads one contiguous run
-// of its row per k-block (64 bytes: 32 bf16 or 128 FP4 codes plus their four
-// E8M0 scales), four lanes cover 256 contiguous bytes of a row.  The
-// contraction index is permuted identically on the A (weights) and B
-// (activations) side: in MFMA step d a lane supplies elements [8d, 8d+8) of
-// its own run, so the A and B lanes that meet in one k-slot always hold the
-// same k.  Activations are bf16, read from L2 (they are small and shared by
-// every weight tile).
+// Work split: one workgroup of WAVES waves owns 16 weight rows (per matrix)
+// and up to 16*NT tokens; the waves take interleaved k-blocks of the
+// contraction axis and their partial tiles are summed in LDS.  Weights stream
+// from HBM straight into MFMA A-operand registers.  In one load instruction
+// the four lanes of a row read 64 contiguous bytes, 16 rows at once.
+// Activations are bf16 and are read from L2 (small, shared by every weight
+// tile).
 //
-// MFMA v_mfma_f32_16x16x32_bf16 operand layout (CDNA3/CDNA4 ISA):
+// All loads are raw buffer loads with 32-bit offsets.  Rows past N and token
+// columns past m get an out-of-range offset, so they load zeros without a
+// branch and without memory traffic.  All loads of a k-block are issued
+// before its first MFMA; with two k-blocks in flight, the activation loads of
+// this k-block go out before the next k-block's weights, so the in-order
+// vector-memory counter lets this k-block's MFMAs start while the next
+// weights are still in flight.
+//
+// v_mfma_f32_16x16x32_bf16 operand layout (CDNA3/CDNA4 ISA):
 //   A: lane l holds A[l%16][8*(l/16) .. +7], B: lane l holds B[8*(l/16) .. +7][l%16],
 //   D: lane l holds D[4*(l/16) + v][l%16], v = 0..3.
+//
+// k-block = DL 16-byte loads per lane (4 lanes per row):
+//   bf16: 256 bytes of a row = 128 elements; load d (0..3) gives lane (r, q)
+//         elements 32d + 8q .. +7 -- exactly its A operand of MFMA d.
+//   FP4 : 128 bytes of a row = 256 elements; load d (0..1) gives lane (r, q)
+//         the 32 elements 128d + 32q .. +31 (one E8M0 block); MFMA (d, m),
+//         m = 0..3, takes elements 128d + 32q + 8m .. +7.  The 8 scale bytes of
+//         the k-block come in one 8-byte load; lane q uses byte 4d + q.
+// The activations are read with the same index map, so each MFMA pairs equal k.
 #pragma once
 
 #include "ft_internal.hpp"
@@ -26,35 +39,47 @@ namespace ft {
 
 enum { WF_BF16 = 0, WF_FP4 = 1 };
 
-constexpr int kStreamThreads = 256;
-constexpr int kStreamMaxTok = 64;   // tokens per pass (4 MFMA column tiles)
+constexpr int kStreamMaxTok = 64;  // tokens per pass (4 MFMA column tiles)
 
-// LDS floats needed by stream_tile<.., GLU, NT>.
-template <bool GLU, int NT>
-constexpr int stream_red_floats() { return 4 * (GLU ? 2 : 1) * NT * 256; }
+// Elements of the contraction axis per k-block.
+template <int WF>
+constexpr int stream_kblock() { return WF == WF_BF16 ? 128 : 256; }
 
-// One 16-row x (16*NT)-token tile.  All 256 threads must call it.
+// LDS floats needed by stream_tile<.., GLU, NT, WAVES>.
+template <bool GLU, int NT, int WAVES>
+constexpr int stream_red_floats() { return WAVES * (GLU ? 2 : 1) * NT * 256; }
+
+template <int WF, int MATS>
+struct WFrag {
+  static constexpr int DL = WF == WF_BF16 ? 4 : 2;  // 16-byte weight loads per lane per k-block
+  u32x4 w[MATS][DL];
+  u32x2 s[MATS];
+};
+
+// One 16-row x (16*NT)-token tile.  All WAVES*64 threads must call it.
 //  w0/s0, w1/s1 : weight (codes) and scale bases of matrix 0 and 1 (row 0).
 //  K            : contraction length (multiple of the k-block).
 //  row0, N      : first weight row of the tile and the number of rows.
-//  X, ldx       : bf16 activations; token j of the tile is row s_tok[j].
+//  X, ldx       : bf16 activations; token j of the tile is row s_tok[j];
+//  x_bytes      : bytes of the whole activation buffer (bounds the offsets).
 //  m            : valid tokens (1..16*NT).
 //  out, ldo     : GLU -> bf16 h, else fp32; token j goes to row s_orow[j].
-template <int WF, bool GLU, int NT>
+template <int WF, bool GLU, int NT, int WAVES, bool PIPE>
 __device__ __forceinline__ void stream_tile(const uint8_t *__restrict__ w0,
                                             const uint8_t *__restrict__ s0,
                                             const uint8_t *__restrict__ w1,
                                             const uint8_t *__restrict__ s1, int K, int row0, int N,
-                                            const uint16_t *__restrict__ X, int64_t ldx,
+                                            const uint16_t *__restrict__ X, int64_t ldx, uint32_t x_bytes,
                                             const int *__restrict__ s_tok, int m,
                                             float *__restrict__ s_red, void *__restrict__ out,
                                             int64_t ldo, const int *__restrict__ s_orow) {
+  constexpr int THREADS = WAVES * 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
   constexpr int MATS = GLU ? 2 : 1;
-  constexpr int KB = (WF == WF_BF16) ? 128 : 512;  // elements per k-block
-  constexpr int RUN = KB / 4;                      // elements per lane per k-block
-  constexpr int DSTEPS = RUN / 8;                  // MFMA steps per k-block
+  constexpr int KB = stream_kblock<WF>();
+  constexpr int DL = WFrag<WF, MATS>::DL;
+  constexpr int DX = WF == WF_BF16 ? 4 : 8;  // 16-byte activation loads per lane per k-block per column tile
   const int nkb = K / KB;
 
   f32x4 acc[MATS][NT];
@@ -63,84 +88,118 @@ __device__ __forceinline__ void stream_tile(const uint8_t *__restrict__ w0,
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[mt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t *xrow[NT];
-  bool xok[NT];
+  // byte offset of token column r of tile tt (out of range past m)
+  const rsrc_t xres = make_rsrc(X, x_bytes);
+  uint32_t xo[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int j = tt * 16 + r;
-    xok[tt] = j < m;
-    xrow[tt] = X + int64_t(s_tok[xok[tt] ? j : 0]) * ldx;
+    xo[tt] = j < m ? uint32_t(s_tok[j]) * uint32_t(ldx) * 2u : kOOB;
   }
 
-  const int wrow = row0 + r;
-  const bool rok = wrow < N;
-  const int64_t crow = rok ? wrow : 0;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // byte pitch of one weight row and of its scale row
+  const uint32_t wpitch = (WF == WF_BF16) ? uint32_t(K) * 2 : uint32_t(K) / 2;
+  const uint32_t spitch = uint32_t(K) / 32;
+  const int wrow = row0 + r;  // rows past N fall outside the buffer
+  rsrc_t wres[MATS], sres[MATS];
+  wres[0] = make_rsrc(w0, uint32_t(N) * wpitch);
+  sres[0] = make_rsrc(s0, uint32_t(N) * spitch);
+  if constexpr (GLU) {
+    wres[MATS - 1] = make_rsrc(w1, uint32_t(N) * wpitch);
+    sres[MATS - 1] = make_rsrc(s1, uint32_t(N) * spitch);
+  }
+  const uint32_t wo = uint32_t(wrow) * wpitch + uint32_t(q) * 16;
+  const uint32_t so = uint32_t(wrow) * spitch;
 
-  if constexpr (WF == WF_BF16) {
-    const uint8_t *wr0 = w0 + crow * int64_t(K) * 2;
-    const uint8_t *wr1 = GLU ? (w1 + crow * int64_t(K) * 2) : nullptr;
-    for (int kb = wave; kb < nkb; kb += 4) {
-      const int kofs = kb * KB + q * RUN;
-      u32x4 a0[4], a1[4];
+  auto load_w = [&](int kb, WFrag<WF, MATS> &f) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        a0[d] = rok ? ld16(wr0 + int64_t(kofs + 8 * d) * 2) : zero4;
-        if constexpr (GLU) a1[d] = rok ? ld16(wr1 + int64_t(kofs + 8 * d) * 2) : zero4;
-      }
+    for (int mt = 0; mt < MATS; ++mt) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int d = 0; d < DL; ++d) f.w[mt][d] = bld16(wres[mt], wo + uint32_t(kb) * (DL * 64) + d * 64);
+      if constexpr (WF == WF_FP4) f.s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);
+    }
+  };
+  // activation element offset of this lane's load dx of k-block kb
+  auto xoff = [&](int kb, int dx) {
+    return WF == WF_BF16 ? kb * KB + 32 * dx + 8 * q : kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3);
+  };
+  auto load_x = [&](int kb, u32x4 (&xb)[NT][DX]) {
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          const u32x4 xb = xok[tt] ? ld16(xrow[tt] + kofs + 8 * d) : zero4;
-          acc[0][tt] = mfma16(as_bf16x8(a0[d]), as_bf16x8(xb), acc[0][tt]);
-          if constexpr (GLU) acc[MATS - 1][tt] = mfma16(as_bf16x8(a1[d]), as_bf16x8(xb), acc[MATS - 1][tt]);
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int dx = 0; dx < DX; ++dx) xb[tt][dx] = bld16(xres, xo[tt] + uint32_t(xoff(kb, dx)) * 2u);
+  };
+  auto compute = [&](const WFrag<WF, MATS> &f, const u32x4 (&xb)[NT][DX]) {
+    if constexpr (WF == WF_BF16) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (int mt = 0; mt < MATS; ++mt)
+            acc[mt][tt] = mfma16(as_bf16x8(f.w[mt][d]), as_bf16x8(xb[tt][d]), acc[mt][tt]);
+    } else {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        float sc[MATS];
+#pragma unroll
+        for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32((f.s[mt][d] >> (8 * q)) & 0xffu);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          bf16x8 a[MATS];
+#pragma unroll
+          for (int mt = 0; mt < MATS; ++mt) a[mt] = fp4x8_to_bf16x8(f.w[mt][d][mm], sc[mt]);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int mt = 0; mt < MATS; ++mt)
+              acc[mt][tt] = mfma16(a[mt], as_bf16x8(xb[tt][4 * d + mm]), acc[mt][tt]);
         }
       }
+    }
+  };
+
+  if constexpr (PIPE) {
+    // The next k-block's weights are in flight while this one is multiplied.
+    WFrag<WF, MATS> fa, fb;
+    u32x4 xb[NT][DX];
+    int kb = wave;
+    if (kb < nkb) load_w(kb, fa);
+    while (kb < nkb) {
+      const int k1 = kb + WAVES;
+      load_x(kb, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k1 < nkb) load_w(k1, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(fa, xb);
+      if (k1 >= nkb) break;
+      const int k2 = k1 + WAVES;
+      load_x(k1, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k2 < nkb) load_w(k2, fa);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(fb, xb);
+      kb = k2;
     }
   } else {
-    const uint8_t *cr0 = w0 + crow * int64_t(K / 2);
-    const uint8_t *sr0 = s0 + crow * int64_t(K / 32);
-    const uint8_t *cr1 = GLU ? (w1 + crow * int64_t(K / 2)) : nullptr;
-    const uint8_t *sr1 = GLU ? (s1 + crow * int64_t(K / 32)) : nullptr;
-    for (int kb = wave; kb < nkb; kb += 4) {
-      const int kofs = kb * KB + q * RUN;
-      u32x4 c0[4], c1[4];
-      uint32_t sc0 = 0, sc1 = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c0[i] = rok ? ld16(cr0 + kofs / 2 + 16 * i) : zero4;
-        if constexpr (GLU) c1[i] = rok ? ld16(cr1 + kofs / 2 + 16 * i) : zero4;
-      }
-      sc0 = rok ? *reinterpret_cast<const uint32_t *>(sr0 + kofs / 32) : 0u;
-      if constexpr (GLU) sc1 = rok ? *reinterpret_cast<const uint32_t *>(sr1 + kofs / 32) : 0u;
-#pragma unroll
-      for (int d = 0; d < DSTEPS; ++d) {
-        const float f0 = e8m0_to_f32((sc0 >> (8 * (d / 4))) & 0xffu);
-        const bf16x8 a0 = fp4x8_to_bf16x8(c0[d / 4][d % 4], f0);
-        bf16x8 a1;
-        if constexpr (GLU) {
-          const float f1 = e8m0_to_f32((sc1 >> (8 * (d / 4))) & 0xffu);
-          a1 = fp4x8_to_bf16x8(c1[d / 4][d % 4], f1);
-        }
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          const u32x4 xb = xok[tt] ? ld16(xrow[tt] + kofs + 8 * d) : zero4;
-          acc[0][tt] = mfma16(a0, as_bf16x8(xb), acc[0][tt]);
-          if constexpr (GLU) acc[MATS - 1][tt] = mfma16(a1, as_bf16x8(xb), acc[MATS - 1][tt]);
-        }
-      }
+    for (int kb = wave; kb < nkb; kb += WAVES) {
+      WFrag<WF, MATS> fa;
+      u32x4 xb[NT][DX];
+      load_w(kb, fa);
+      load_x(kb, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(fa, xb);
     }
   }
 
-  // Sum the four waves' partial tiles.
+  // Sum the waves' partial tiles.
 #pragma unroll
   for (int mt = 0; mt < MATS; ++mt)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
       *reinterpret_cast<f32x4 *>(&s_red[(((wave * MATS + mt) * NT + tt) * 64 + lane) * 4]) = acc[mt][tt];
   __syncthreads();
-  for (int u = tid; u < NT * 64; u += kStreamThreads) {
+  for (int u = tid; u < NT * 64; u += THREADS) {
     const int tt = u >> 6, ln = u & 63;
     const int j = tt * 16 + (ln & 15);
     const int n = row0 + 4 * (ln >> 4);
@@ -148,7 +207,7 @@ __device__ __forceinline__ void stream_tile(const uint8_t *__restrict__ w0,
     f32x4 g = {0.f, 0.f, 0.f, 0.f};
     f32x4 uu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
       g += *reinterpret_cast<const f32x4 *>(&s_red[(((w * MATS + 0) * NT + tt) * 64 + ln) * 4]);
       if constexpr (GLU)
         uu += *reinterpret_cast<const f32x4 *>(&s_red[(((w * MATS + 1) * NT + tt) * 64 + ln) * 4]);
@@ -177,18 +236,43 @@ __device__ __forceinline__ void stream_tile(const uint8_t *__restrict__ w0,
   __syncthreads();
 }
 
-// Dispatch on the number of 16-token column tiles (1..4).
-template <int WF, bool GLU>
+// Dispatch on the number of 16-token column tiles (1..NTMAX).
+template <int WF, bool GLU, int NTMAX, int WAVES, bool PIPE>
 __device__ __forceinline__ void stream_tile_any(const uint8_t *w0, const uint8_t *s0, const uint8_t *w1,
                                                 const uint8_t *s1, int K, int row0, int N,
-                                                const uint16_t *X, int64_t ldx, const int *s_tok, int m,
-                                                float *s_red, void *out, int64_t ldo, const int *s_orow) {
-  switch ((m + 15) >> 4) {
-    case 1: stream_tile<WF, GLU, 1>(w0, s0, w1, s1, K, row0, N, X, ldx, s_tok, m, s_red, out, ldo, s_orow); break;
-    case 2: stream_tile<WF, GLU, 2>(w0, s0, w1, s1, K, row0, N, X, ldx, s_tok, m, s_red, out, ldo, s_orow); break;
-    case 3: stream_tile<WF, GLU, 3>(w0, s0, w1, s1, K, row0, N, X, ldx, s_tok, m, s_red, out, ldo, s_orow); break;
-    default: stream_tile<WF, GLU, 4>(w0, s0, w1, s1, K, row0, N, X, ldx, s_tok, m, s_red, out, ldo, s_orow); break;
+                                                const uint16_t *X, int64_t ldx, uint32_t x_bytes, const int *s_tok,
+                                                int m, float *s_red, void *out, int64_t ldo, const int *s_orow) {
+  const int nt = (m + 15) >> 4;
+  if (NTMAX == 1 || nt <= 1) {
+    stream_tile<WF, GLU, 1, WAVES, PIPE>(w0, s0, w1, s1, K, row0, N, X, ldx, x_bytes, s_tok, m, s_red, out, ldo, s_orow);
+  } else if (NTMAX == 2 || nt == 2) {
+    stream_tile<WF, GLU, (NTMAX >= 2 ? 2 : 1), WAVES, PIPE>(w0, s0, w1, s1, K, row0, N, X, ldx, x_bytes, s_tok, m,
+                                                            s_red, out, ldo, s_orow);
+  } else if (nt == 3) {
+    stream_tile<WF, GLU, (NTMAX >= 3 ? 3 : 1), WAVES, PIPE>(w0, s0, w1, s1, K, row0, N, X, ldx, x_bytes, s_tok, m,
+                                                            s_red, out, ldo, s_orow);
+  } else {
+    stream_tile<WF, GLU, NTMAX, WAVES, PIPE>(w0, s0, w1, s1, K, row0, N, X, ldx, x_bytes, s_tok, m, s_red, out,
+                                             ldo, s_orow);
   }
+}
+
+// Launch shape of a streaming tile: tokens per pass (16*NTMAX), waves per
+// workgroup, and whether each wave keeps two k-blocks in flight.
+struct StreamShape {
+  int ntmax, waves;
+  bool pipe;
+};
+
+// T bounds the tokens of any segment; nkb = k-blocks of the contraction axis.
+// Decode batches (T <= 64) use one 16-token column tile per pass (longer
+// segments take several passes); each wave gets one k-block when the
+// contraction axis has at most 16 of them, else two or more in flight.
+inline StreamShape stream_shape(int T, int nkb) {
+  const int ntmax = T <= 64 ? 1 : 2;
+  for (int w : {16, 8, 6, 4})
+    if (nkb % w == 0) return {ntmax, w, nkb > w};
+  return {ntmax, 4, nkb > 4};
 }
 
 }  // namespace ft

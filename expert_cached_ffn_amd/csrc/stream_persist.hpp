@@ -1,0 +1,268 @@
+// Persistent weight-streaming kernel body for the decode regime (segments of at
+// most a few dozen tokens).
+//
+// One workgroup of WAVES waves stays resident and walks a strided list of
+// units.  A unit is (active expert, 16-row weight tile, group of <= 16 tokens
+// of that expert's segment).  The waves split the contraction axis (KPW
+// k-blocks each, interleaved) and meet in LDS to sum their partial 16x16
+// tiles.  While a unit is multiplied, the weights and token indices of the
+// workgroup's next unit are already in flight, so HBM latency is overlapped
+// with MFMA work and the epilogue instead of being paid per workgroup.
+//
+// The active-expert table (experts with a non-empty segment, ascending, then
+// the shared expert) is built once per workgroup in LDS from the segment
+// offsets.  Loads, index maps and masking are those of stream_gemm.hpp (raw
+// buffer loads; out-of-range offsets return zero without memory traffic).
+#pragma once
+
+#include "stream_gemm.hpp"
+
+namespace ft {
+
+constexpr int kPersistMaxE = 1024;  // experts the LDS table holds (larger E uses the plain kernel)
+
+struct PersistArgs {
+  const uint8_t *pool;
+  const int32_t *slot_of_expert;  // NULL: slot e
+  uint64_t expert_bytes;
+  const uint8_t *shared_blob;     // NULL: none
+  uint64_t off_w0, off_w1, off_s0, off_s1;
+  int K, N;                       // contraction length, weight rows
+  const int32_t *offsets;         // [E+1]
+  int E, T, k;
+  const int32_t *sorted_rows;     // gather: token of permuted row p = sorted_rows[p] / k (NULL: row p itself)
+  const uint16_t *X;              // bf16 activations (x or hidden rows)
+  int64_t ldx;
+  uint32_t x_bytes;
+  void *out;                      // GLU: bf16 hidden rows; else fp32 rows
+  int64_t ldo;
+  float *out_shared;              // non-GLU: rows of the shared expert go here (by token)
+  int n_tiles;                    // ceil(N / 16)
+};
+
+// A value every lane of the wave holds (an LDS table entry read at a uniform
+// index) moved to a scalar register, so descriptors built from it stay scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int WF, bool GLU, int WAVES, int KPW>
+__device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_red) {
+  constexpr int THREADS = WAVES * 64;
+  constexpr int NW = WAVES;
+  constexpr int MATS = GLU ? 2 : 1;
+  constexpr int KB = stream_kblock<WF>();
+  constexpr int DL = WFrag<WF, MATS>::DL;
+  constexpr int DX = WF == WF_BF16 ? 4 : 8;
+  __shared__ int s_e[kPersistMaxE + 1];    // expert id (E = shared expert)
+  __shared__ int s_pos[kPersistMaxE + 1];  // first permuted row of its segment
+  __shared__ int s_m[kPersistMaxE + 1];    // rows of its segment
+  __shared__ int s_slot[kPersistMaxE + 1];
+  __shared__ int s_cnt[NW];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, q = lane >> 4;
+
+  // ---- active-expert table
+  int base = 0;
+  for (int c0 = 0; c0 < a.E; c0 += THREADS) {
+    const int e = c0 + tid;
+    int lo = 0, cnt = 0;
+    if (e < a.E) {
+      lo = a.offsets[e];
+      cnt = a.offsets[e + 1] - lo;
+    }
+    const bool f = cnt > 0;
+    const uint64_t mask = __ballot(f);
+    if (lane == 0) s_cnt[wave] = __popcll(mask);
+    __syncthreads();
+    int before = base, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) before += s_cnt[w];
+      total += s_cnt[w];
+    }
+    if (f) {
+      const int i = before + __popcll(mask & ((uint64_t(1) << lane) - 1));
+      s_e[i] = e;
+      s_pos[i] = lo;
+      s_m[i] = cnt;
+      s_slot[i] = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    }
+    base += total;
+    __syncthreads();
+  }
+  int n_act = base;
+  if (a.shared_blob != nullptr) {
+    if (tid == 0) {
+      s_e[n_act] = a.E;
+      s_pos[n_act] = a.T * a.k;
+      s_m[n_act] = a.T;
+      s_slot[n_act] = 0;
+    }
+    ++n_act;
+    __syncthreads();
+  }
+  const int n_items = n_act * a.n_tiles;
+
+  // ---- per-unit state
+  struct Unit {
+    int item, g0;  // item = active index * n_tiles + tile; g0 = first token of the group
+  };
+  auto valid = [&](const Unit &u) { return u.item < n_items; };
+  auto first_unit = [&]() { return Unit{int(blockIdx.x), 0}; };
+  auto next_unit = [&](const Unit &u) {
+    const int ai = u.item / a.n_tiles;
+    if (u.g0 + 16 < uniform(s_m[ai])) return Unit{u.item, u.g0 + 16};
+    return Unit{u.item + int(gridDim.x), 0};
+  };
+
+  const uint32_t wpitch = (WF == WF_BF16) ? uint32_t(a.K) * 2 : uint32_t(a.K) / 2;
+  const uint32_t spitch = uint32_t(a.K) / 32;
+  const uint32_t wbytes = uint32_t(a.N) * wpitch, sbytes = uint32_t(a.N) * spitch;
+  const rsrc_t xres = make_rsrc(a.X, a.x_bytes);
+  const int nkb = a.K / KB;
+
+  struct UnitRegs {
+    WFrag<WF, MATS> f[KPW];
+    uint32_t tok;  // raw sorted_rows entry of this lane's token (gather mode)
+  };
+  const rsrc_t rres = make_rsrc(a.sorted_rows, a.sorted_rows ? uint32_t(a.T) * uint32_t(a.k) * 4u : 0u);
+  // Issue the weight loads of unit u (this wave's k-blocks), then this lane's token load.
+  auto issue = [&](const Unit &u, UnitRegs &R) {
+    if (!valid(u)) return;
+    const int ai = u.item / a.n_tiles, tile = u.item % a.n_tiles;
+    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
+    const uint8_t *blob = e == a.E ? a.shared_blob : a.pool + uint64_t(max(slot, 0)) * a.expert_bytes;
+    rsrc_t wres[MATS], sres[MATS];
+    wres[0] = make_rsrc(blob + a.off_w0, wbytes);
+    sres[0] = make_rsrc(blob + a.off_s0, sbytes);
+    if constexpr (GLU) {
+      wres[MATS - 1] = make_rsrc(blob + a.off_w1, wbytes);
+      sres[MATS - 1] = make_rsrc(blob + a.off_s1, sbytes);
+    }
+    const uint32_t wo = uint32_t(tile * 16 + r) * wpitch + uint32_t(q) * 16;
+    const uint32_t so = uint32_t(tile * 16 + r) * spitch;
+#pragma unroll
+    for (int c = 0; c < KPW; ++c) {
+      const int kb = wave + c * WAVES;
+#pragma unroll
+      for (int mt = 0; mt < MATS; ++mt) {
+#pragma unroll
+        for (int d = 0; d < DL; ++d) R.f[c].w[mt][d] = bld16(wres[mt], wo + uint32_t(kb) * (DL * 64) + d * 64);
+        if constexpr (WF == WF_FP4) R.f[c].s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);
+      }
+    }
+    const int j = u.g0 + r;
+    const bool gather = e != a.E && a.sorted_rows != nullptr;
+    R.tok = bld4(rres, gather && j < m ? uint32_t(pos + j) * 4u : kOOB);
+  };
+
+  auto step = [&](const Unit &u, UnitRegs &cur, UnitRegs &nxt) -> Unit {
+    const Unit un = next_unit(u);
+    const int ai = u.item / a.n_tiles, tile = u.item % a.n_tiles;
+    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
+    const bool shared = e == a.E;
+    const bool missing = !shared && slot < 0;
+    // activation row of this lane's token: gathered x row, the token itself
+    // (shared expert, gather mode) or the permuted/hidden row p
+    const int j = u.g0 + r;
+    int row = -1;
+    if (j < m) {
+      if (a.sorted_rows == nullptr) row = pos + j;
+      else row = shared ? j : int(cur.tok) / a.k;
+    }
+    const uint32_t xo = row >= 0 ? uint32_t(row) * uint32_t(a.ldx) * 2u : kOOB;
+    // activations of this unit, then the next unit's weights
+    u32x4 xb[KPW][DX];
+#pragma unroll
+    for (int c = 0; c < KPW; ++c) {
+      const int kb = wave + c * WAVES;
+#pragma unroll
+      for (int dx = 0; dx < DX; ++dx) {
+        const int ko = WF == WF_BF16 ? kb * KB + 32 * dx + 8 * q : kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3);
+        xb[c][dx] = bld16(xres, xo + uint32_t(ko) * 2u);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue(un, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[MATS];
+#pragma unroll
+    for (int mt = 0; mt < MATS; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KPW; ++c) {
+      const WFrag<WF, MATS> &f = cur.f[c];
+      if constexpr (WF == WF_BF16) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int mt = 0; mt < MATS; ++mt) acc[mt] = mfma16(as_bf16x8(f.w[mt][d]), as_bf16x8(xb[c][d]), acc[mt]);
+      } else {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          float sc[MATS];
+#pragma unroll
+          for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32((f.s[mt][d] >> (8 * q)) & 0xffu);
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+            for (int mt = 0; mt < MATS; ++mt)
+              acc[mt] = mfma16(fp4x8_to_bf16x8(f.w[mt][d][mm], sc[mt]), as_bf16x8(xb[c][4 * d + mm]), acc[mt]);
+        }
+      }
+    }
+    // sum the waves' partial tiles
+#pragma unroll
+    for (int mt = 0; mt < MATS; ++mt)
+      *reinterpret_cast<f32x4 *>(&s_red[((wave * MATS + mt) * 64 + lane) * 4]) = acc[mt];
+    __syncthreads();
+    if (tid < 64) {
+      const int ln = tid;
+      const int jj = u.g0 + (ln & 15);
+      const int n = tile * 16 + 4 * (ln >> 4);
+      if (jj < m && n < a.N) {
+        f32x4 g = {0.f, 0.f, 0.f, 0.f}, uu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int w = 0; w < WAVES; ++w) {  // partial unroll: keeps LDS reads from hoarding registers
+          g += *reinterpret_cast<const f32x4 *>(&s_red[((w * MATS + 0) * 64 + ln) * 4]);
+          if constexpr (GLU) uu += *reinterpret_cast<const f32x4 *>(&s_red[((w * MATS + 1) * 64 + ln) * 4]);
+        }
+        // output row: permuted row p (hidden rows of the shared expert follow the routed ones)
+        const int p = pos + jj;
+        if constexpr (GLU) {
+          uint16_t hv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) hv[v] = missing ? uint16_t(0x7fc0) : f32_to_bf16_rne(silu(g[v]) * uu[v]);
+          uint16_t *hp = reinterpret_cast<uint16_t *>(a.out) + int64_t(p) * a.ldo + n;
+          if (n + 3 < a.N) {
+            *reinterpret_cast<u32x2 *>(hp) =
+                u32x2{uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16)};
+          } else {
+            for (int v = 0; v < 4 && n + v < a.N; ++v) hp[v] = hv[v];
+          }
+        } else {
+          if (missing) g = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+          float *yp = shared ? a.out_shared + int64_t(jj) * a.ldo + n
+                             : reinterpret_cast<float *>(a.out) + int64_t(p) * a.ldo + n;
+          if (n + 3 < a.N) {
+            *reinterpret_cast<f32x4 *>(yp) = g;
+          } else {
+            for (int v = 0; v < 4 && n + v < a.N; ++v) yp[v] = g[v];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    return un;
+  };
+
+  // Two register sets alternate: while one unit is multiplied the next one loads.
+  Unit u = first_unit();
+  UnitRegs ra, rb;
+  issue(u, ra);
+  while (valid(u)) {
+    u = step(u, ra, rb);
+    if (!valid(u)) break;
+    u = step(u, rb, ra);
+  }
+}
+
+}  // namespace ft

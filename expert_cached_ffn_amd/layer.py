@@ -99,11 +99,11 @@ class MoELayer:
         ops.ft_moe_permute(ids, T, self.s.k, self.s.E, self.offsets, self.sorted_rows, self.row_pos,
                            self.ws_perm, self.ws_perm_bytes, stream=stream)
 
-    def ffn(self, T, x, pool, slot_of_expert=None, shared_blob=None, stream=None):
+    def ffn(self, T, x, pool, slot_of_expert=None, shared_blob=None, stream=None, mode=0):
         s = self.s
         ops.ft_moe_grouped_ffn(self.layout, pool, slot_of_expert, shared_blob, x, DTYPES[s.xdtype], T, s.k,
                                s.E, self.offsets, self.sorted_rows, self.y_rows,
-                               self.y_shared if shared_blob is not None else None, 0, self.ws_ffn,
+                               self.y_shared if shared_blob is not None else None, mode, self.ws_ffn,
                                self.ws_ffn_bytes, stream=stream)
 
     def combine(self, T, w=None, with_shared=True, stream=None):

@@ -116,7 +116,8 @@ ft_status ft_expert_layout_init(int32_t wdtype, int32_t H, int32_t I, ft_expert_
  *   taken at the picked experts; FT_SIGMOID -> sigmoid of the picked logits.
  *   renormalize != 0 divides the k weights by their sum.
  * Limits: 1 <= k <= E <= 1024 (else FT_ENOTSUP).  T = 0 is a no-op.
- * Buffers 16-byte aligned; with w_router, H must be a multiple of 8.
+ * Buffers 16-byte aligned; with w_router and FT_BF16, H must be a multiple
+ * of 128 (FT_ENOTSUP otherwise).
  * NaN or infinite logits are outside the contract.
  */
 ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_router, float *logits,
@@ -161,15 +162,21 @@ ft_status ft_moe_permute(const int32_t *topk_ids, int32_t T, int32_t k, int32_t 
  * shared_blob (nullable): one more expert in the same layout, applied to every
  *   token with weight 1, written to y_shared [T, H] fp32 (required iff
  *   shared_blob != NULL).
- * mode 0: exact path -- MXFP4 weights decoded exactly to bf16, bf16 MFMA,
- *   fp32 accumulation; the SwiGLU hidden vector is rounded to bf16 before
- *   the down projection.  Other modes: FT_ENOTSUP.
+ * mode, low byte: 0 = exact path -- MXFP4 weights decoded exactly to bf16,
+ *   bf16 MFMA, fp32 accumulation; the SwiGLU hidden vector is rounded to
+ *   bf16 before the down projection.  Other values: FT_ENOTSUP.
+ * mode, stage bits: FT_FFN_GATE_UP_ONLY runs only the gate/up + SwiGLU stage
+ *   (the hidden rows stay in `workspace`, y is not written);
+ *   FT_FFN_DOWN_ONLY runs only the down projection from the hidden rows a
+ *   previous FT_FFN_GATE_UP_ONLY call with the same arguments and workspace
+ *   left there.  Neither bit: both stages.  Both bits: FT_EINVAL.
  * workspace: ft_workspace_bytes(FT_WS_FFN, T, k, E, H, I) bytes.
  * Limits: FT_BF16 weights need H, I multiples of 128; FT_MXFP4 multiples of
- *   512; E <= 4096.  MXFP4 scale bytes must lie in 2..252 (every decoded value
+ *   256; E <= 4096.  MXFP4 scale bytes must lie in 2..252 (every decoded value
  *   is then an exact bf16).  Buffers 16-byte aligned, slot_pool and blobs
  *   256-byte aligned.
  */
+enum { FT_FFN_GATE_UP_ONLY = 0x100, FT_FFN_DOWN_ONLY = 0x200 };
 ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
                              const int32_t *slot_of_expert, const void *shared_blob,
                              const void *x, int32_t x_dtype, int32_t T, int32_t k, int32_t E,

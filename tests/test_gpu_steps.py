@@ -100,7 +100,7 @@ def test_permute_bit_exact(ops, T, k, E, kind):
         ids = moe.topk(synth.prefill_logits(synth.CONFIGS[4], T), k).astype(np.int32)
     else:
         rng = np.random.default_rng(T * 7 + E)
-        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32).reshape(T, k)
+        ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], np.int32).reshape(T, k)
     off_ref, rows_ref, pos_ref = moe.permute(ids, E)
     n = max(1, T * k)
     off = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
