@@ -243,6 +243,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode-bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=None, help="main decode batch (default: largest of the workload)")
+    ap.add_argument("--only-main-batch", action="store_true",
+                    help="time only the main batch (profiling runs: one kernel shape per kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -259,6 +261,8 @@ def main():
     main_T = args.batch or max(batches)
     if main_T not in batches:
         batches.append(main_T)
+    if args.only_main_batch:
+        batches = [main_T]
     res = run_decode(args, cfg, batches, main_T)
     m = res[main_T]
     ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9

@@ -175,7 +175,11 @@ static ft_status launch_stream(const FfnArgs &a, int a_max, int T, hipStream_t s
 template <int WF, bool GLU, int WAVES, int KPW>
 __global__ __launch_bounds__(WAVES * 64) void ffn_persist_kernel(PersistArgs a) {
   __shared__ float s_red[WAVES * (GLU ? 2 : 1) * 256];
-  stream_persist<WF, GLU, WAVES, KPW>(a, s_red);
+  // Units in flight: a 16-wave gate/up tile leaves no registers for a second
+  // activation set (128 per lane in a 1024-thread workgroup); the smaller
+  // down-projection tiles need a deeper ring to cover HBM latency.
+  constexpr int NB = GLU ? (WAVES * KPW >= 16 ? 1 : 2) : (WAVES * KPW >= 16 ? 2 : 3);
+  stream_persist<WF, GLU, WAVES, KPW, NB>(a, s_red);
 }
 
 // Resident workgroups per CU of a kernel (cached) times the CU count.
@@ -466,7 +470,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   s2.n_tiles = cdiv(H, 16);
 
   // Decode batches: persistent weight-streaming kernels.
-  if (T <= 64 && E <= kPersistMaxE) {
+  if (T <= 64 && E <= kPersistMaxE && T * k <= kPersistMaxRows) {
     PersistArgs p1{};
     p1.pool = a.pool;
     p1.slot_of_expert = slot_of_expert;

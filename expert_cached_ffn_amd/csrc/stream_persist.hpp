@@ -19,7 +19,8 @@
 
 namespace ft {
 
-constexpr int kPersistMaxE = 1024;  // experts the LDS table holds (larger E uses the plain kernel)
+constexpr int kPersistMaxE = 1024;     // experts the LDS table holds (larger E uses the plain kernel)
+constexpr int kPersistMaxRows = 4096;  // routed rows whose token indices fit the LDS copy
 
 struct PersistArgs {
   const uint8_t *pool;
@@ -44,7 +45,11 @@ struct PersistArgs {
 // index) moved to a scalar register, so descriptors built from it stay scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int WF, bool GLU, int WAVES, int KPW>
+// NB: units in flight per wave (a ring of NB register sets; the loads of unit
+// i+NB-1 are issued before unit i is multiplied).  NB = 1 issues a unit's
+// activations at its own start, still ahead of the next unit's weights,
+// which saves registers.
+template <int WF, bool GLU, int WAVES, int KPW, int NB>
 __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_red) {
   constexpr int THREADS = WAVES * 64;
   constexpr int NW = WAVES;
@@ -57,7 +62,10 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
   __shared__ int s_m[kPersistMaxE + 1];    // rows of its segment
   __shared__ int s_slot[kPersistMaxE + 1];
   __shared__ int s_cnt[NW];
+  __shared__ int s_tok[kPersistMaxRows];  // token of every routed row (gather mode)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (a.sorted_rows != nullptr)
+    for (int p = tid; p < a.T * a.k; p += THREADS) s_tok[p] = a.sorted_rows[p] / a.k;
   const int r = lane & 15, q = lane >> 4;
 
   // ---- active-expert table
@@ -118,18 +126,17 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
   const uint32_t spitch = uint32_t(a.K) / 32;
   const uint32_t wbytes = uint32_t(a.N) * wpitch, sbytes = uint32_t(a.N) * spitch;
   const rsrc_t xres = make_rsrc(a.X, a.x_bytes);
-  const int nkb = a.K / KB;
 
+  // Register set of one unit: its weights and activations.
   struct UnitRegs {
     WFrag<WF, MATS> f[KPW];
-    uint32_t tok;  // raw sorted_rows entry of this lane's token (gather mode)
+    u32x4 xb[KPW][DX];
   };
-  const rsrc_t rres = make_rsrc(a.sorted_rows, a.sorted_rows ? uint32_t(a.T) * uint32_t(a.k) * 4u : 0u);
-  // Issue the weight loads of unit u (this wave's k-blocks), then this lane's token load.
-  auto issue = [&](const Unit &u, UnitRegs &R) {
+
+  auto issue_w = [&](const Unit &u, UnitRegs &R) {
     if (!valid(u)) return;
     const int ai = u.item / a.n_tiles, tile = u.item % a.n_tiles;
-    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
+    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]);
     const uint8_t *blob = e == a.E ? a.shared_blob : a.pool + uint64_t(max(slot, 0)) * a.expert_bytes;
     rsrc_t wres[MATS], sres[MATS];
     wres[0] = make_rsrc(blob + a.off_w0, wbytes);
@@ -150,28 +157,19 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
         if constexpr (WF == WF_FP4) R.f[c].s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);
       }
     }
-    const int j = u.g0 + r;
-    const bool gather = e != a.E && a.sorted_rows != nullptr;
-    R.tok = bld4(rres, gather && j < m ? uint32_t(pos + j) * 4u : kOOB);
   };
-
-  auto step = [&](const Unit &u, UnitRegs &cur, UnitRegs &nxt) -> Unit {
-    const Unit un = next_unit(u);
-    const int ai = u.item / a.n_tiles, tile = u.item % a.n_tiles;
-    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
-    const bool shared = e == a.E;
-    const bool missing = !shared && slot < 0;
-    // activation row of this lane's token: gathered x row, the token itself
-    // (shared expert, gather mode) or the permuted/hidden row p
+  // Activations of unit u (this lane's token row from the LDS copy).
+  auto issue_x = [&](const Unit &u, u32x4 (&xb)[KPW][DX]) {
+    if (!valid(u)) return;
+    const int ai = u.item / a.n_tiles;
+    const int e = uniform(s_e[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
     const int j = u.g0 + r;
     int row = -1;
     if (j < m) {
-      if (a.sorted_rows == nullptr) row = pos + j;
-      else row = shared ? j : int(cur.tok) / a.k;
+      if (a.sorted_rows == nullptr) row = pos + j;      // hidden row p
+      else row = e == a.E ? j : s_tok[pos + j];         // token of the shared / routed expert
     }
     const uint32_t xo = row >= 0 ? uint32_t(row) * uint32_t(a.ldx) * 2u : kOOB;
-    // activations of this unit, then the next unit's weights
-    u32x4 xb[KPW][DX];
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
       const int kb = wave + c * WAVES;
@@ -181,9 +179,15 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
         xb[c][dx] = bld16(xres, xo + uint32_t(ko) * 2u);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    issue(un, nxt);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Multiply unit u (weights in cur, activations in xcur), sum the wave
+  // partials in LDS and write its 16x16 output tile.
+  auto finish = [&](const Unit &u, const UnitRegs &cur, const u32x4 (&xcur)[KPW][DX]) {
+    const int ai = u.item / a.n_tiles, tile = u.item % a.n_tiles;
+    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
+    const bool shared = e == a.E;
+    const bool missing = !shared && slot < 0;
     f32x4 acc[MATS];
 #pragma unroll
     for (int mt = 0; mt < MATS; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -194,7 +198,7 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
 #pragma unroll
         for (int d = 0; d < 4; ++d)
 #pragma unroll
-          for (int mt = 0; mt < MATS; ++mt) acc[mt] = mfma16(as_bf16x8(f.w[mt][d]), as_bf16x8(xb[c][d]), acc[mt]);
+          for (int mt = 0; mt < MATS; ++mt) acc[mt] = mfma16(as_bf16x8(f.w[mt][d]), as_bf16x8(xcur[c][d]), acc[mt]);
       } else {
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
@@ -205,63 +209,83 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
           for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
             for (int mt = 0; mt < MATS; ++mt)
-              acc[mt] = mfma16(fp4x8_to_bf16x8(f.w[mt][d][mm], sc[mt]), as_bf16x8(xb[c][4 * d + mm]), acc[mt]);
+              acc[mt] = mfma16(fp4x8_to_bf16x8(f.w[mt][d][mm], sc[mt]), as_bf16x8(xcur[c][4 * d + mm]), acc[mt]);
         }
       }
     }
-    // sum the waves' partial tiles
+    // Sum the waves' partial tiles: thread t < 256 owns element (lane t/4, value t%4).
 #pragma unroll
     for (int mt = 0; mt < MATS; ++mt)
       *reinterpret_cast<f32x4 *>(&s_red[((wave * MATS + mt) * 64 + lane) * 4]) = acc[mt];
     __syncthreads();
-    if (tid < 64) {
-      const int ln = tid;
+    if (tid < 256) {
+      const int ln = tid >> 2, v = tid & 3;
       const int jj = u.g0 + (ln & 15);
-      const int n = tile * 16 + 4 * (ln >> 4);
-      if (jj < m && n < a.N) {
-        f32x4 g = {0.f, 0.f, 0.f, 0.f}, uu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int w = 0; w < WAVES; ++w) {  // partial unroll: keeps LDS reads from hoarding registers
-          g += *reinterpret_cast<const f32x4 *>(&s_red[((w * MATS + 0) * 64 + ln) * 4]);
-          if constexpr (GLU) uu += *reinterpret_cast<const f32x4 *>(&s_red[((w * MATS + 1) * 64 + ln) * 4]);
-        }
-        // output row: permuted row p (hidden rows of the shared expert follow the routed ones)
-        const int p = pos + jj;
-        if constexpr (GLU) {
-          uint16_t hv[4];
+      const int n = tile * 16 + 4 * (ln >> 4) + v;
+      float g = 0.f, uu = 0.f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) hv[v] = missing ? uint16_t(0x7fc0) : f32_to_bf16_rne(silu(g[v]) * uu[v]);
-          uint16_t *hp = reinterpret_cast<uint16_t *>(a.out) + int64_t(p) * a.ldo + n;
-          if (n + 3 < a.N) {
-            *reinterpret_cast<u32x2 *>(hp) =
-                u32x2{uint32_t(hv[0]) | (uint32_t(hv[1]) << 16), uint32_t(hv[2]) | (uint32_t(hv[3]) << 16)};
-          } else {
-            for (int v = 0; v < 4 && n + v < a.N; ++v) hp[v] = hv[v];
-          }
+      for (int w = 0; w < WAVES; ++w) {
+        g += s_red[((w * MATS + 0) * 64 + ln) * 4 + v];
+        if constexpr (GLU) uu += s_red[((w * MATS + 1) * 64 + ln) * 4 + v];
+      }
+      if (jj < m && n < a.N) {
+        const int p = pos + jj;  // permuted row; hidden rows of the shared expert follow the routed ones
+        if constexpr (GLU) {
+          reinterpret_cast<uint16_t *>(a.out)[int64_t(p) * a.ldo + n] =
+              missing ? uint16_t(0x7fc0) : f32_to_bf16_rne(silu(g) * uu);
         } else {
-          if (missing) g = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-          float *yp = shared ? a.out_shared + int64_t(jj) * a.ldo + n
-                             : reinterpret_cast<float *>(a.out) + int64_t(p) * a.ldo + n;
-          if (n + 3 < a.N) {
-            *reinterpret_cast<f32x4 *>(yp) = g;
-          } else {
-            for (int v = 0; v < 4 && n + v < a.N; ++v) yp[v] = g[v];
-          }
+          float *yp = shared ? a.out_shared + int64_t(jj) * a.ldo : reinterpret_cast<float *>(a.out) + int64_t(p) * a.ldo;
+          yp[n] = missing ? __builtin_nanf("") : g;
         }
       }
     }
     __syncthreads();
-    return un;
   };
 
-  // Two register sets alternate: while one unit is multiplied the next one loads.
   Unit u = first_unit();
-  UnitRegs ra, rb;
-  issue(u, ra);
-  while (valid(u)) {
-    u = step(u, ra, rb);
-    if (!valid(u)) break;
-    u = step(u, rb, ra);
+  if constexpr (NB == 1) {
+    // This unit's activations, then the next unit's weights, then the multiply
+    // (which waits for the activations only).
+    UnitRegs ra, rb;
+    u32x4 xcur[KPW][DX];
+    auto step = [&](const Unit &uc, UnitRegs &cur, UnitRegs &nxt) {
+      issue_x(uc, xcur);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(next_unit(uc), nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      finish(uc, cur, xcur);
+    };
+    issue_w(u, ra);
+    while (valid(u)) {
+      step(u, ra, rb);
+      u = next_unit(u);
+      if (!valid(u)) break;
+      step(u, rb, ra);
+      u = next_unit(u);
+    }
+  } else {
+    // Ring of NB register sets: unit i+NB-1 is issued before unit i is multiplied.
+    UnitRegs ring[NB];
+    Unit ahead = u;
+#pragma unroll
+    for (int s = 0; s < NB - 1; ++s) {
+      issue_w(ahead, ring[s]);
+      issue_x(ahead, ring[s].xb);
+      ahead = next_unit(ahead);
+    }
+    while (valid(u)) {
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        if (valid(u)) {
+          issue_w(ahead, ring[(s + NB - 1) % NB]);
+          issue_x(ahead, ring[(s + NB - 1) % NB].xb);
+          ahead = next_unit(ahead);
+          __builtin_amdgcn_sched_barrier(0);
+          finish(u, ring[s], ring[s].xb);
+          u = next_unit(u);
+        }
+      }
+    }
   }
 }
 
