@@ -194,6 +194,64 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     log(f"copy calibration: {reps} x {nbytes} B device copy")
 
 
+def run_prefill(args, cfg, T):
+    """Prefill layer: given Zipf-skewed logits, grouped MFMA GEMM over ragged segments."""
+    import torch
+    import synth
+    from expert_cached_ffn_amd import layer as L
+    from expert_cached_ffn_amd import _lib
+
+    torch.cuda.set_device(0)
+    shape = L.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize,
+                         cfg.shared)
+    layer = L.MoELayer(shape, T)
+    t0 = time.time()
+    pool = build_pool(L, layer, cfg, range(cfg.E), cfg.E)
+    shared = L.as_device_u8([L.pack_expert(layer.layout, synth.expert_weights(cfg, 0, cfg.E).arrays)])[0]
+    n_sets = 2
+    xs = [L.to_device(synth.tokens(cfg, T, case=r)) for r in range(n_sets)]
+    lg = [L.to_device(synth.prefill_logits(cfg, T, case=r)) for r in range(n_sets)]
+    torch.cuda.synchronize()
+    log(f"prefill inputs built in {time.time() - t0:.1f}s")
+    rows = T * cfg.k + T
+    flops_gu = 2.0 * 2 * cfg.H * cfg.I * rows
+    flops_all = 3.0 * 2 * cfg.H * cfg.I * rows
+
+    def step(i, tm=None):
+        r = i % n_sets
+        layer.route(T, logits=lg[r])
+        layer.permute(T)
+        if tm is not None:
+            tm.mark()
+        layer.ffn(T, xs[r], pool, shared_blob=shared, mode=_lib.FT_FFN_GATE_UP_ONLY)
+        if tm is not None:
+            tm.mark()
+        layer.ffn(T, xs[r], pool, shared_blob=shared, mode=_lib.FT_FFN_DOWN_ONLY)
+        if tm is not None:
+            tm.mark()
+        layer.combine(T)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm = Timer()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i, tm)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    gu = float(np.mean([tm.ev[3 * i].elapsed_time(tm.ev[3 * i + 1]) for i in range(args.steps)]))
+    dn = float(np.mean([tm.ev[3 * i + 1].elapsed_time(tm.ev[3 * i + 2]) for i in range(args.steps)]))
+    log(f"prefill T={T}: {ms:.3f} ms/step ({T / (ms * 1e-3):,.0f} tok/s); gate/up {gu:.3f} ms = "
+        f"{flops_gu / (gu * 1e-3) / 1e12:.0f} TFLOP/s, down {dn:.3f} ms = "
+        f"{flops_all / 3 / (dn * 1e-3) / 1e12:.0f} TFLOP/s; FFN {flops_all / ((gu + dn) * 1e-3) / 1e12:.0f} TFLOP/s")
+    return dict(ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), gate_up_ms=gu, down_ms=dn,
+                flops_gate_up=flops_gu, flops_ffn=flops_all)
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline_decode(cfg, T):
@@ -229,6 +287,8 @@ def cpu_baseline_decode(cfg, T):
 # ----------------------------------------------------------------------------- main
 
 WORKLOADS = {
+    "prefill-mxfp4": (4, "dsv4-flash-shaped MXFP4 prefill MoE layer (8192 tokens, H=4096, I=2048, 256 experts "
+                         "top-6 sigmoid with Zipf(1.1) popularity + 1 shared, SwiGLU)"),
     "decode-bf16": (2, "qwen3-a3b-shaped bf16 decode MoE layer (H=2048, I=768, 128 experts, top-8 softmax "
                        "renormalised, SwiGLU)"),
     "decode-mxfp4": (3, "dsv4-flash-shaped MXFP4 decode MoE layer (H=4096, I=2048, 256 experts top-6 sigmoid "
@@ -263,36 +323,23 @@ def main():
         batches.append(main_T)
     if args.only_main_batch:
         batches = [main_T]
+    if args.workload.startswith("prefill"):
+        T = cfg.batches[0]
+        p = run_prefill(args, cfg, T)
+        ach = p["flops_gate_up"] / (p["gate_up_ms"] * 1e-3) / 1e12
+        out = {
+            "metric": METRIC, "value": p["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": p["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "mxfp4-w/bf16", "data": "synthetic",
+            "config": {"workload": desc, "batch_tokens": T},
+            "roofline": {"bound": "mfma", "kernel": "ffn_gemm_kernel<mxfp4, gate_up>", "achieved": ach,
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                         "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"]},
+            "ffn_TFLOPs": p["flops_ffn"] / ((p["gate_up_ms"] + p["down_ms"]) * 1e-3) / 1e12,
+        }
+        print(json.dumps(out), flush=True)
+        return
     res = run_decode(args, cfg, batches, main_T)
-    m = res[main_T]
-    ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
-    out = {
-        "metric": METRIC,
-        "value": m["tokens_per_s"],
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": m["ms_per_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if cfg.wdtype == "bf16" else "mxfp4-w/bf16",
-        "data": "synthetic",
-        "config": {"workload": desc, "batch_tokens": main_T, "input_sets": N_INPUT_SETS,
-                   "distinct_experts_per_step": m["distinct_experts"]},
-        "roofline": {"bound": "hbm", "kernel": f"ffn_stream_kernel<{'bf16' if cfg.wdtype == 'bf16' else 'mxfp4'}, gate_up>",
-                     "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_us": m["gate_up_ms"] * 1e3,
-                     "algorithmic_bytes_per_launch": m["gate_up_bytes"]},
-        "layer_weight_GBps": m["layer_weight_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9,
-        "graph_ms_per_step": m["graph_ms_per_step"],
-        "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                             "graph_ms_per_step": r["graph_ms_per_step"],
-                             "gate_up_GBps": r["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9,
-                             "layer_weight_GBps": r["layer_weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9}
-                    for T, r in sorted(res.items())},
-    }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(cfg, main_T)
     print(json.dumps(out), flush=True)

@@ -17,6 +17,7 @@
 #include "ft_internal.hpp"
 #include "stream_gemm.hpp"
 #include "stream_persist.hpp"
+#include "gemm_prefill.hpp"
 
 namespace ft {
 
@@ -240,6 +241,32 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
   FT_PERSIST(4, 2)
 #undef FT_PERSIST
   return false;
+}
+
+// ------------------------------------------------------------------ prefill grouped GEMM
+
+template <int WF, bool GLU>
+__global__ __launch_bounds__(kGemmThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kGemmBM * kGemmPitch];
+  gemm_tile<WF, GLU>(a, lds);
+}
+
+// Upper bound of token tiles over all segments (+ the shared expert).
+static int gemm_mtiles_bound(int T, int k, int E, bool shared) {
+  const int64_t routed = int64_t(T) * k;
+  return int(routed / kGemmBM + std::min<int64_t>(E, routed) + (shared ? cdiv(T, kGemmBM) : 0));
+}
+
+template <int WF, bool GLU>
+static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
+  const int nt = GLU ? cdiv(a.N, kGemmBN / 2) : cdiv(a.N, kGemmBN);
+  const int mb = gemm_mtiles_bound(a.T, a.k, a.E, a.shared_blob != nullptr);
+  a.n_ntiles = nt;
+  a.n_items = nt * mb;
+  const int grid = cdiv(a.n_items, 8) * 8;
+  hipLaunchKernelGGL((ffn_gemm_kernel<WF, GLU>), dim3(unsigned(grid)), dim3(kGemmThreads), 0, stream, a);
+  FT_LAUNCHED(name);
+  return FT_OK;
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -528,6 +555,52 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
       }
     }
     FT_LAUNCHED("ffn_persist_kernel");
+    clear_error();
+    return FT_OK;
+  }
+  // Prefill: grouped MFMA GEMM tiles (K a multiple of the 128-element chunk).
+  if (H % kGemmBK == 0 && I % kGemmBK == 0) {
+    GemmArgs g1{};
+    g1.pool = a.pool;
+    g1.slot_of_expert = slot_of_expert;
+    g1.expert_bytes = L->expert_bytes;
+    g1.shared_blob = a.shared_blob;
+    g1.offsets = expert_offsets;
+    g1.E = E;
+    g1.T = T;
+    g1.k = k;
+    GemmArgs g2 = g1;
+    g1.off_w0 = L->off_gate;
+    g1.off_w1 = L->off_up;
+    g1.off_s0 = L->off_sgate;
+    g1.off_s1 = L->off_sup;
+    g1.K = H;
+    g1.N = I;
+    g1.sorted_rows = sorted_rows;
+    g1.X = static_cast<const uint16_t *>(x);
+    g1.ldx = H;
+    g1.x_bytes = s1.x_bytes;
+    g1.out = hbuf;
+    g1.ldo = I;
+    g2.off_w0 = g2.off_w1 = L->off_down;
+    g2.off_s0 = g2.off_s1 = L->off_sdown;
+    g2.K = I;
+    g2.N = H;
+    g2.sorted_rows = nullptr;
+    g2.X = hbuf;
+    g2.ldx = I;
+    g2.x_bytes = s2.x_bytes;
+    g2.out = y_rows;
+    g2.ldo = H;
+    g2.out_shared = y_shared;
+    ft_status st = FT_OK;
+    if (wd == FT_BF16) {
+      if (run1 && (st = launch_gemm<WF_BF16, true>(g1, stream, "ffn_gemm_kernel<bf16, gate_up>")) != FT_OK) return st;
+      if (run2 && (st = launch_gemm<WF_BF16, false>(g2, stream, "ffn_gemm_kernel<bf16, down>")) != FT_OK) return st;
+    } else {
+      if (run1 && (st = launch_gemm<WF_FP4, true>(g1, stream, "ffn_gemm_kernel<mxfp4, gate_up>")) != FT_OK) return st;
+      if (run2 && (st = launch_gemm<WF_FP4, false>(g2, stream, "ffn_gemm_kernel<mxfp4, down>")) != FT_OK) return st;
+    }
     clear_error();
     return FT_OK;
   }

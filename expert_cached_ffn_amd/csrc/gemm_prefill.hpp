@@ -1,0 +1,304 @@
+// Grouped MFMA GEMM for the prefill regime (segments of hundreds to thousands
+// of tokens per expert).
+//
+//   stage 1: h[p][i] = silu(sum_k X[p][k] Wg[i][k]) * (sum_k X[p][k] Wu[i][k])
+//   stage 2: y[p][n] = sum_k h[p][k] Wd[n][k]
+//
+// Workgroup = 4 waves; tile = 128 segment rows (tokens) x 256 weight rows.
+// Stage 1 gives each wave 32 gate rows and the same 32 up rows, so every
+// thread holds G and U of the same outputs for the SwiGLU epilogue.  Per wave
+// the MFMA register block is 8 token tiles x 4 weight tiles of
+// v_mfma_f32_16x16x32_bf16 (A = tokens, B = weights).
+//
+// The token rows of the tile are gathered through the segment's row list into
+// LDS, 128 contraction elements at a time, double buffered, by direct
+// buffer-to-LDS loads (lane i of a load writes 16 bytes at base + 16 i); every
+// wave reads them from LDS.  Within a row, 16-byte chunk j is stored in slot
+// j ^ (row % 16), so the 16 rows an MFMA operand reads hit distinct banks.  Weights are read by each wave straight from global memory
+// (each weight row is used by exactly one wave) and, for FP4, decoded in
+// registers; the next chunk's weights and tokens are in flight while the
+// current chunk is multiplied.
+//
+// Index maps per 128-element chunk c (bf16 weights and FP4 weights differ):
+//   FP4 : lane (n, q) of a weight tile loads 16 bytes = elements 32q..32q+31 of
+//         row n (one E8M0 block); MFMA mm (0..3) uses elements 32q + 8mm .. +7.
+//   bf16: lane (n, q) loads 16 bytes at elements 32d + 8q .. +7 for MFMA d.
+//   Token lane (m, q) supplies the same element indices of row m from LDS.
+//
+// Work items: (weight tile, token tile) pairs, token tiles counted per expert
+// segment (ragged: the last tile of a segment is partial, rows past it load
+// zeros and are not written).  Block ids are remapped so that consecutive
+// items -- the token tiles of one weight tile -- run on the same XCD and share
+// its L2.
+#pragma once
+
+#include "ft_internal.hpp"
+
+namespace ft {
+
+constexpr int kGemmBM = 128;      // token rows per tile
+constexpr int kGemmBN = 256;      // weight rows per tile (stage 1: 128 gate + 128 up)
+constexpr int kGemmBK = 128;      // contraction elements per chunk
+constexpr int kGemmPitch = 256;   // LDS bytes per token row (one chunk, XOR-swizzled)
+constexpr int kGemmThreads = 256;
+
+struct GemmArgs {
+  const uint8_t *pool;
+  const int32_t *slot_of_expert;  // NULL: slot e
+  uint64_t expert_bytes;
+  const uint8_t *shared_blob;     // NULL: none
+  uint64_t off_w0, off_w1, off_s0, off_s1;
+  int K, N;                       // contraction length, weight rows of one matrix
+  const int32_t *offsets;         // [E+1]
+  int E, T, k;
+  const int32_t *sorted_rows;     // stage 1: token of permuted row p = sorted_rows[p] / k; NULL: row p
+  const uint16_t *X;
+  int64_t ldx;
+  uint32_t x_bytes;
+  void *out;                      // stage 1: bf16 hidden rows; stage 2: fp32 rows
+  int64_t ldo;
+  float *out_shared;              // stage 2: shared-expert rows by token
+  int n_ntiles;                   // weight tiles
+  int n_items;                    // grid size (upper bound of items)
+};
+
+// Block-wide: map token-tile index mi (counted over the experts' segments in
+// ascending expert order, then the shared expert) to its expert and first row.
+template <int THREADS>
+__device__ bool gemm_find_mtile(const GemmArgs &a, int mi, int *e_out, int *row0_out, int *m_out) {
+  constexpr int NW = THREADS / 64;
+  __shared__ int s_cnt[NW];
+  __shared__ int s_e, s_r0, s_m;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) s_e = -1;
+  int base = 0;
+  for (int c0 = 0; c0 < a.E; c0 += THREADS) {
+    const int e = c0 + tid;
+    int lo = 0, cnt = 0;
+    if (e < a.E) {
+      lo = a.offsets[e];
+      cnt = a.offsets[e + 1] - lo;
+    }
+    const int tiles = (cnt + kGemmBM - 1) / kGemmBM;
+    // inclusive wave scan of tiles
+    int v = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(v, off);
+      if (lane >= off) v += o;
+    }
+    if (lane == 63) s_cnt[wave] = v;
+    __syncthreads();
+    int before = base, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) before += s_cnt[w];
+      total += s_cnt[w];
+    }
+    const int first = before + v - tiles;  // exclusive
+    if (tiles > 0 && mi >= first && mi < first + tiles) {
+      s_e = e;
+      s_r0 = lo + (mi - first) * kGemmBM;
+      s_m = min(kGemmBM, cnt - (mi - first) * kGemmBM);
+    }
+    base += total;
+    __syncthreads();
+  }
+  if (s_e < 0 && a.shared_blob != nullptr) {
+    const int ms = mi - base;
+    if (ms >= 0 && ms * kGemmBM < a.T) {
+      *e_out = a.E;
+      *row0_out = ms * kGemmBM;  // token index of the first row
+      *m_out = min(kGemmBM, a.T - ms * kGemmBM);
+      return true;
+    }
+    return false;
+  }
+  if (s_e < 0) return false;
+  *e_out = s_e;
+  *row0_out = s_r0;
+  *m_out = s_m;
+  return true;
+}
+
+template <int WF, bool GLU>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, uint8_t *lds) {
+  constexpr int NT = 4;   // weight tiles (16 rows) per wave
+  constexpr int MT = 8;   // token tiles (16 rows) per wave
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, q = lane >> 4;
+
+  // ---- work item: block ids go round-robin over the 8 XCDs; give each XCD a
+  // contiguous range of items (the grid is a multiple of 8)
+  const int G = int(gridDim.x), b = int(blockIdx.x);
+  const int per = G / 8;
+  const int logical = (b % 8) * per + b / 8;
+  if (logical >= a.n_items) return;
+  const int n_m = a.n_items / a.n_ntiles;  // token tiles (upper bound) per weight tile
+  const int nt_idx = logical / n_m, mi = logical % n_m;
+  int e, row0, m;
+  if (!gemm_find_mtile<kGemmThreads>(a, mi, &e, &row0, &m)) return;
+  const bool shared = e == a.E;
+  const uint8_t *blob;
+  if (shared) {
+    blob = a.shared_blob;
+  } else {
+    const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    if (slot < 0) {
+      // not resident: mark this tile's outputs NaN
+      const int cols = GLU ? kGemmBN / 2 : kGemmBN;
+      const int c0 = nt_idx * cols;
+      for (int u = tid; u < m * cols; u += kGemmThreads) {
+        const int rr = u / cols, cc = c0 + u % cols;
+        if (cc >= a.N) continue;
+        if (GLU) reinterpret_cast<uint16_t *>(a.out)[int64_t(row0 + rr) * a.ldo + cc] = 0x7fc0;
+        else reinterpret_cast<float *>(a.out)[int64_t(row0 + rr) * a.ldo + cc] = __builtin_nanf("");
+      }
+      return;
+    }
+    blob = a.pool + uint64_t(slot) * a.expert_bytes;
+  }
+
+  // ---- token rows: wave w fills rows 32w..32w+31 of a chunk buffer with 8
+  // direct loads of 4 rows each; lane i covers row 4t + i/16, slot i%16
+  const rsrc_t xres = make_rsrc(a.X, a.x_bytes);
+  uint32_t xsrc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int rr = wave * 32 + t * 4 + (lane >> 4);
+    int src = -1;
+    if (rr < m) {
+      if (a.sorted_rows == nullptr) src = (shared ? a.T * a.k : 0) + row0 + rr;  // hidden row
+      else if (shared) src = row0 + rr;                                        // token
+      else src = a.sorted_rows[row0 + rr] / a.k;                               // gathered token
+    }
+    const int j = (lane & 15) ^ (rr & 15);  // global chunk stored in this lane's slot
+    xsrc[t] = src >= 0 ? uint32_t(src) * uint32_t(a.ldx) * 2u + uint32_t(j) * 16u : kOOB;
+  }
+
+  // ---- weights of this wave
+  const uint32_t wpitch = (WF == WF_BF16) ? uint32_t(a.K) * 2 : uint32_t(a.K) / 2;
+  const uint32_t spitch = uint32_t(a.K) / 32;
+  const uint32_t wbytes = uint32_t(a.N) * wpitch, sbytes = uint32_t(a.N) * spitch;
+  rsrc_t wres[NT], sres[NT];
+  uint32_t wrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int row;
+    const uint8_t *wb, *sb;
+    if (GLU) {
+      // tiles 0,1: gate rows; tiles 2,3: the same up rows
+      row = nt_idx * (kGemmBN / 2) + wave * 32 + (t & 1) * 16 + r;
+      wb = blob + (t < 2 ? a.off_w0 : a.off_w1);
+      sb = blob + (t < 2 ? a.off_s0 : a.off_s1);
+    } else {
+      row = nt_idx * kGemmBN + wave * 64 + t * 16 + r;
+      wb = blob + a.off_w0;
+      sb = blob + a.off_s0;
+    }
+    wres[t] = make_rsrc(wb, wbytes);
+    sres[t] = make_rsrc(sb, sbytes);
+    wrow[t] = uint32_t(row);  // rows past N fall outside the buffer
+  }
+  constexpr int DLW = WF == WF_BF16 ? 4 : 1;  // 16-byte weight loads per tile per chunk
+  struct BFrag {
+    u32x4 w[NT][DLW];
+    uint32_t s[NT];
+  };
+  auto load_b = [&](int c, BFrag &f) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (WF == WF_BF16) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) f.w[t][d] = bld16(wres[t], wrow[t] * wpitch + uint32_t(c) * 256u + d * 64 + q * 16);
+      } else {
+        f.w[t][0] = bld16(wres[t], wrow[t] * wpitch + uint32_t(c) * 64u + q * 16);
+        f.s[t] = bld4(sres[t], wrow[t] * spitch + uint32_t(c) * 4u);
+      }
+    }
+  };
+  auto load_a = [&](int c, int buf) {
+    uint8_t *base = lds + buf * (kGemmBM * kGemmPitch) + wave * 32 * kGemmPitch;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void *)(base + t * 4 * kGemmPitch), 16,
+          xsrc[t] == kOOB ? kOOB : xsrc[t] + uint32_t(c) * 256u, 0, 0, 0);
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nch = a.K / kGemmBK;
+  // One chunk: the next chunk goes in flight (tokens straight to the other LDS
+  // buffer -- last read in the previous chunk, before the barrier that ended
+  // it -- and weights to the other register set), then this chunk is multiplied.
+  auto chunk = [&](int c, int buf, const BFrag &f, BFrag &fn) {
+    if (c + 1 < nch) {
+      load_a(c + 1, buf ^ 1);
+      load_b(c + 1, fn);
+    }
+    const uint8_t *abuf = lds + buf * (kGemmBM * kGemmPitch);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 bw[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (WF == WF_BF16) bw[t] = as_bf16x8(f.w[t][ks]);
+        else bw[t] = fp4x8_to_bf16x8(f.w[t][0][ks], e8m0_to_f32((f.s[t] >> (8 * q)) & 0xffu));
+      }
+      const int j = WF == WF_BF16 ? 4 * ks + q : 4 * q + ks;  // 16-byte chunk of the row
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const u32x4 af = *reinterpret_cast<const u32x4 *>(abuf + (i * 16 + r) * kGemmPitch + ((j ^ r) << 4));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[i][t] = mfma16(as_bf16x8(af), bw[t], acc[i][t]);
+      }
+    }
+    if (c + 1 < nch) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+      __syncthreads();                // and everyone's
+    }
+  };
+  BFrag f0, f1;
+  load_a(0, 0);
+  load_b(0, f0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, 0, f0, f1);
+    if (c + 1 < nch) chunk(c + 1, 1, f1, f0);
+  }
+
+  // ---- epilogue: lane holds D[token 4q+v][weight row r] of each tile
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int rr = i * 16 + 4 * q + v;
+      if (rr >= m) continue;
+      if constexpr (GLU) {
+        const int hrow = shared ? a.T * a.k + row0 + rr : row0 + rr;
+        uint16_t *hp = reinterpret_cast<uint16_t *>(a.out) + int64_t(hrow) * a.ldo;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int col = nt_idx * (kGemmBN / 2) + wave * 32 + t * 16 + r;
+          if (col < a.N) hp[col] = f32_to_bf16_rne(silu(acc[i][t][v]) * acc[i][t + 2][v]);
+        }
+      } else {
+        float *yp = shared ? a.out_shared + int64_t(row0 + rr) * a.ldo
+                           : reinterpret_cast<float *>(a.out) + int64_t(row0 + rr) * a.ldo;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int col = nt_idx * kGemmBN + wave * 64 + t * 16 + r;
+          if (col < a.N) yp[col] = acc[i][t][v];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace ft
