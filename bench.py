@@ -41,6 +41,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_sources_hash():
+    """Short sha256 over the HIP sources (names and contents) of the library."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "expert_cached_ffn_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(profile, kernel_prefix):
+    """HBM bytes per launch from a committed counter summary, if it belongs to these sources."""
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        with open(path) as f:
+            doc = json.load(f)
+    except OSError:
+        return None
+    if doc.get("csrc_sha256_16") != kernel_sources_hash():
+        return None  # kernels changed since the counters were taken
+    for name, v in doc.get("kernels", {}).items():
+        if name.startswith(kernel_prefix):
+            return v["traffic_bytes"]
+    return None
+
+
 # ----------------------------------------------------------------------------- inputs
 
 def build_pool(L, layer, cfg, experts, n_slots, layer_idx=0):
@@ -252,6 +280,96 @@ def run_prefill(args, cfg, T):
                 flops_gate_up=flops_gu, flops_ffn=flops_all)
 
 
+def pinned_h2d_bandwidth(expert_bytes, n=32):
+    """B_p: pinned host -> device copies of one expert blob each, back to back on one stream."""
+    import torch
+    src = torch.empty((n, expert_bytes), dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty((n, expert_bytes), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for i in range(n):
+            dst[i].copy_(src[i], non_blocking=True)
+    s.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        a.record()
+        for i in range(n):
+            dst[i].copy_(src[i], non_blocking=True)
+        b.record()
+    s.synchronize()
+    return n * expert_bytes / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def run_cache_trace(args, cfg):
+    """8-layer decode trace at batch 1 through the device LRU cache with pinned-host miss fills."""
+    import concurrent.futures as cf
+    import torch
+    import synth
+    from expert_cached_ffn_amd import layer as L
+    from expert_cached_ffn_amd import ops
+
+    torch.cuda.set_device(0)
+    Lyr, E, C, S = cfg.n_layers, cfg.E, cfg.capacity, cfg.steps
+    shape = L.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize, True)
+    layer = L.MoELayer(shape, 1)
+    eb = int(layer.layout.expert_bytes)
+    t0 = time.time()
+    bank = torch.empty((Lyr * E, eb), dtype=torch.uint8, pin_memory=True)
+    hb = bank.numpy()
+
+    def fill(key):
+        l, e = divmod(key, E)
+        L.pack_expert(layer.layout, synth.expert_weights(cfg, l, e).arrays, hb[key])
+    with cf.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(Lyr * E)))
+    shared = torch.stack([L.as_device_u8([L.pack_expert(layer.layout, synth.expert_weights(cfg, l, E).arrays)])[0]
+                          for l in range(Lyr)])
+    tr = synth.cache_trace(cfg)
+    logits = L.to_device(tr.logits.reshape(S * Lyr, E))
+    xs = torch.stack([L.to_device(synth.tokens(cfg, 1, layer=l, step=st)) for st in range(S) for l in range(Lyr)])
+    pool = torch.empty((C, eb), dtype=torch.uint8, device="cuda")
+    slot_of = torch.empty(E, dtype=torch.int32, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    log(f"cache trace: host bank {bank.numel() / 1e9:.1f} GB pinned and filled in {time.time() - t0:.1f}s")
+    b_p = pinned_h2d_bandwidth(eb)
+    log(f"pinned H2D bandwidth B_p = {b_p:.1f} GB/s")
+
+    def run(steps, cache):
+        for st in range(steps):
+            for l in range(Lyr):
+                i = st * Lyr + l
+                layer.route(1, logits=logits[i:i + 1])
+                cache.step(l, layer.ids, 1, cfg.k, slot_of)
+                layer.permute(1)
+                layer.ffn(1, xs[i], pool, slot_of_expert=slot_of, shared_blob=shared[l])
+                layer.combine(1)
+
+    warm = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
+    run(min(args.warmup, S), warm)
+    torch.cuda.synchronize()
+    warm.destroy()
+    cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)  # cold start
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    run(S, cache)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t1
+    st = cache.stats()
+    cache.destroy()
+    hit = st["hits"] / max(1, st["accesses"])
+    # lower bound of a step: resident expert reads at 8 TB/s vs fills at the measured B_p
+    resident = Lyr * (cfg.k + 1) * eb
+    bound = max(resident / (HBM_PEAK_GBS * 1e9), st["bytes_h2d"] / S / (b_p * 1e9))
+    res = dict(tokens_per_s=S / dt, ms_per_step=dt / S * 1e3, hit_rate=hit, misses_per_step=st["misses"] / S,
+               bytes_h2d=st["bytes_h2d"], h2d_GBps=st["bytes_h2d"] / dt / 1e9, b_p_GBps=b_p,
+               bound_ms_per_step=bound * 1e3, frac_of_bound=bound / (dt / S), stats=st)
+    log(f"cache trace: {S} steps x {Lyr} layers in {dt:.2f}s = {S / dt:.1f} tok/s, hit rate {hit:.4f}, "
+        f"{res['misses_per_step']:.2f} misses/step, fills {res['h2d_GBps']:.1f} GB/s (B_p {b_p:.1f}), "
+        f"bound {bound * 1e3:.3f} ms/step -> {100 * res['frac_of_bound']:.0f} % of it")
+    return res
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline_decode(cfg, T):
@@ -287,6 +405,8 @@ def cpu_baseline_decode(cfg, T):
 # ----------------------------------------------------------------------------- main
 
 WORKLOADS = {
+    "cache-trace": (5, "dsv4-flash-shaped expert-cache decode trace (8 layers x 256 MXFP4 experts + shared, "
+                       "512 cache slots = 25 %, 512 steps of batch 1, Zipf(1.1) + 60 % reuse routing)"),
     "prefill-mxfp4": (4, "dsv4-flash-shaped MXFP4 prefill MoE layer (8192 tokens, H=4096, I=2048, 256 experts "
                          "top-6 sigmoid with Zipf(1.1) popularity + 1 shared, SwiGLU)"),
     "decode-bf16": (2, "qwen3-a3b-shaped bf16 decode MoE layer (H=2048, I=768, 128 experts, top-8 softmax "
@@ -323,6 +443,17 @@ def main():
         batches.append(main_T)
     if args.only_main_batch:
         batches = [main_T]
+    if args.workload == "cache-trace":
+        c = run_cache_trace(args, cfg)
+        out = {
+            "metric": METRIC, "value": c["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": cfg.steps,
+            "warmup": min(args.warmup, cfg.steps), "ms_per_step": c["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4-w/bf16", "data": "synthetic",
+            "config": {"workload": desc, "batch_tokens": 1},
+            "cache": {k: v for k, v in c.items() if k not in ("tokens_per_s", "ms_per_step")},
+        }
+        print(json.dumps(out), flush=True)
+        return
     if args.workload.startswith("prefill"):
         T = cfg.batches[0]
         p = run_prefill(args, cfg, T)
@@ -340,6 +471,38 @@ def main():
         print(json.dumps(out), flush=True)
         return
     res = run_decode(args, cfg, batches, main_T)
+    m = res[main_T]
+    ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
+    kname = "ffn_persist_kernel<%s, gate_up>" % ("bf16" if cfg.wdtype == "bf16" else "mxfp4")
+    traffic = None
+    if args.workload == "decode-bf16" and main_T == 64:
+        traffic = measured_traffic("decode-bf16-T64_hbm_traffic.json", "void ft::ffn_persist_kernel<0, true,")
+    out = {
+        "metric": METRIC,
+        "value": m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.wdtype == "bf16" else "mxfp4-w/bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "batch_tokens": main_T, "input_sets": N_INPUT_SETS,
+                   "distinct_experts_per_step": m["distinct_experts"]},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "avg_launch_us": m["gate_up_ms"] * 1e3,
+                     "algorithmic_bytes_per_launch": m["gate_up_bytes"]},
+        "layer_weight_GBps": m["layer_weight_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9,
+        "graph_ms_per_step": m["graph_ms_per_step"],
+        "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                             "graph_ms_per_step": r["graph_ms_per_step"],
+                             "gate_up_GBps": r["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9,
+                             "layer_weight_GBps": r["layer_weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9}
+                    for T, r in sorted(res.items())},
+    }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(cfg, main_T)
     print(json.dumps(out), flush=True)
