@@ -16,9 +16,10 @@ in the repository's design notes.
 
 Modules:
   formats -- bfloat16 and OCP MXFP4 (E2M1 codes + E8M0 scales) decoding.
+  mx      -- MXFP8 E4M3 activation quantization (native MXFP4 mode).
   moe     -- router logits, top-k, gating, permutation, SwiGLU expert,
              combine, and the whole layer.
   lru     -- the shared (layer, expert) LRU slot-table simulator.
   policy  -- the bandwidth-derived miss split.
 """
-from . import formats, moe, lru, policy  # noqa: F401
+from . import formats, mx, moe, lru, policy  # noqa: F401

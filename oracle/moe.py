@@ -24,6 +24,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import mx
+
 
 def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
     """logits[t, e] = sum_h x[t, h] W_r[e, h], summed in float64, stored as float32."""
@@ -128,12 +130,31 @@ def swiglu_expert(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
     return Y
 
 
+def swiglu_expert_mx(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
+                     return_hidden: bool = False):
+    """The SwiGLU expert as a scaled matrix unit computes it (native MXFP4 mode).
+
+    Both products take MXFP8 E4M3 activations (mx.mxfp8_round_trip): X is
+    quantized as given; the hidden vector h = silu(G) * U is rounded to bf16,
+    then quantized.  Weights are used exactly as decoded; sums are exact.
+    """
+    Xq = mx.mxfp8_round_trip(np.asarray(X, np.float64))
+    G = Xq @ Wg.T
+    U = Xq @ Wu.T
+    h = mx.round_to_bf16(G * sigmoid(G) * U)
+    Y = mx.mxfp8_round_trip(h) @ Wd.T
+    if return_hidden:
+        return Y, h
+    return Y
+
+
 def grouped_ffn(x: np.ndarray, k: int, offsets: np.ndarray, sorted_rows: np.ndarray,
-                experts) -> np.ndarray:
+                experts, expert_fn=swiglu_expert) -> np.ndarray:
     """Expert outputs in permuted order: y_rows[i] = FFN_e(x[sorted_rows[i] // k]).
 
     ``experts(e)`` returns (Wg, Wu, Wd) of expert e as float64.  Segment e is
-    the rows offsets[e] .. offsets[e+1]-1.
+    the rows offsets[e] .. offsets[e+1]-1.  ``expert_fn`` is swiglu_expert
+    (exact) or swiglu_expert_mx (native MXFP4 mode).
     """
     x = np.asarray(x, np.float64)
     n = int(offsets[-1])
@@ -144,7 +165,7 @@ def grouped_ffn(x: np.ndarray, k: int, offsets: np.ndarray, sorted_rows: np.ndar
         if a == b:
             continue
         tok = np.asarray(sorted_rows[a:b], dtype=np.int64) // k
-        y[a:b] = swiglu_expert(x[tok], *experts(e))
+        y[a:b] = expert_fn(x[tok], *experts(e))
     return y
 
 
@@ -165,14 +186,16 @@ def combine(y_rows: np.ndarray, w: np.ndarray, row_pos: np.ndarray,
 
 def moe_layer(x: np.ndarray, *, k: int, E: int, gating: str, renormalize: bool,
               experts, shared=None, w_router: np.ndarray | None = None,
-              logits: np.ndarray | None = None) -> dict:
+              logits: np.ndarray | None = None, native_mx: bool = False) -> dict:
     """The whole layer: route, permute, expert FFN, combine.
 
     x: [T, H] float64.  Either ``w_router`` [E, H] (logits computed) or
     ``logits`` [T, E] (given).  ``experts(e)`` -> (Wg, Wu, Wd) float64;
     ``shared`` is the shared expert's (Wg, Wu, Wd) or None.
+    ``native_mx`` selects the native MXFP4 mode's expert (swiglu_expert_mx).
     Returns a dict with every intermediate.
     """
+    expert_fn = swiglu_expert_mx if native_mx else swiglu_expert
     x = np.asarray(x, np.float64)
     T = x.shape[0]
     if logits is None:
@@ -180,20 +203,22 @@ def moe_layer(x: np.ndarray, *, k: int, E: int, gating: str, renormalize: bool,
     ids = topk(logits, k)
     w = gating_weights(logits, ids, gating, renormalize)
     offsets, sorted_rows, row_pos = permute(ids, E)
-    y_rows = grouped_ffn(x, k, offsets, sorted_rows, experts)
-    y_shared = swiglu_expert(x, *shared) if shared is not None else None
+    y_rows = grouped_ffn(x, k, offsets, sorted_rows, experts, expert_fn)
+    y_shared = expert_fn(x, *shared) if shared is not None else None
     out = combine(y_rows, w, row_pos, y_shared, T, k)
     return dict(logits=np.asarray(logits, np.float32), ids=ids, w=w, offsets=offsets,
                 sorted_rows=sorted_rows, row_pos=row_pos, y_rows=y_rows,
                 y_shared=y_shared, out=out, margin=topk_margin(logits, k))
 
 
-def token_output(x_t: np.ndarray, ids_t, w_t, experts, shared=None) -> np.ndarray:
+def token_output(x_t: np.ndarray, ids_t, w_t, experts, shared=None,
+                 native_mx: bool = False) -> np.ndarray:
     """One token's layer output from its routing: sum_j w_j FFN_{id_j}(x) (+ shared)."""
+    expert_fn = swiglu_expert_mx if native_mx else swiglu_expert
     x_t = np.asarray(x_t, np.float64)[None, :]
     out = np.zeros(x_t.shape[1])
     for e, wj in zip(ids_t, w_t):
-        out += float(wj) * swiglu_expert(x_t, *experts(int(e)))[0]
+        out += float(wj) * expert_fn(x_t, *experts(int(e)))[0]
     if shared is not None:
-        out += swiglu_expert(x_t, *shared)[0]
+        out += expert_fn(x_t, *shared)[0]
     return out
