@@ -18,15 +18,37 @@
 #include "stream_gemm.hpp"
 #include "stream_persist.hpp"
 #include "gemm_prefill.hpp"
+#include "gemm_mx.hpp"
 
 namespace ft {
 
+ft_status mx_quantize_launch(const uint16_t *x, int64_t ldx, int n, int K, uint8_t *q, uint8_t *s,
+                             hipStream_t stream);
+
+// Workspace of the native MXFP4 mode: bf16 hidden rows, their MXFP8 codes and
+// scales, and the MXFP8 codes and scales of the input tokens (256-B aligned parts).
+struct MxWorkspace {
+  uint64_t h, hq, hs, xq, xs, total;
+};
+static MxWorkspace mx_workspace_layout(int64_t T, int64_t k, int64_t H, int64_t I) {
+  auto al = [](uint64_t b) { return (b + 255) / 256 * 256; };
+  const uint64_t rows = uint64_t(T * k + T);
+  MxWorkspace w;
+  w.h = 0;
+  w.hq = al(rows * I * 2);
+  w.hs = w.hq + al(rows * I);
+  w.xq = w.hs + al(rows * I / 32);
+  w.xs = w.xq + al(uint64_t(T * H));
+  w.total = w.xs + al(uint64_t(T * H / 32));
+  return w;
+}
+
 size_t ffn_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
   (void)E;
-  (void)H;
   const uint64_t rows = uint64_t(T) * uint64_t(k) + uint64_t(T);
-  const uint64_t b = rows * uint64_t(I) * 4;  // fp32 hidden rows (bf16 paths use half)
-  return size_t((b + 255) / 256 * 256);
+  const uint64_t b = (rows * uint64_t(I) * 4 + 255) / 256 * 256;  // fp32 hidden rows (bf16 paths use half)
+  const uint64_t mx = mx_workspace_layout(T, k, H, I).total;
+  return size_t(b > mx ? b : mx);
 }
 
 // Block-wide: index of the aidx-th expert with a non-empty segment (ascending
@@ -269,6 +291,26 @@ static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
   return FT_OK;
 }
 
+// ------------------------------------------------------------------ native MXFP4 mode GEMM
+
+template <bool GLU>
+__global__ __launch_bounds__(kGemmThreads, 1) void ffn_mx_gemm_kernel(MxGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMxBufBytes];
+  gemm_mx_tile<GLU>(a, lds);
+}
+
+template <bool GLU>
+static ft_status launch_mx_gemm(MxGemmArgs a, hipStream_t stream, const char *name) {
+  const int nt = GLU ? cdiv(a.g.N, kGemmBN / 2) : cdiv(a.g.N, kGemmBN);
+  const int mb = gemm_mtiles_bound(a.g.T, a.g.k, a.g.E, a.g.shared_blob != nullptr);
+  a.g.n_ntiles = nt;
+  a.g.n_items = nt * mb;
+  const int grid = cdiv(a.g.n_items, 8) * 8;
+  hipLaunchKernelGGL((ffn_mx_gemm_kernel<GLU>), dim3(unsigned(grid)), dim3(kGemmThreads), 0, stream, a);
+  FT_LAUNCHED(name);
+  return FT_OK;
+}
+
 // ------------------------------------------------------------------ fp32 path
 
 struct FfnF32Args {
@@ -380,7 +422,8 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   FT_REQUIRE(stages != (FT_FFN_GATE_UP_ONLY | FT_FFN_DOWN_ONLY),
              "ft_moe_grouped_ffn: FT_FFN_GATE_UP_ONLY and FT_FFN_DOWN_ONLY together");
   FT_REQUIRE((mode & ~0x3ff) == 0, "ft_moe_grouped_ffn: unknown mode bits");
-  FT_SUPPORTED((mode & 0xff) == 0, "ft_moe_grouped_ffn: only mode 0 (exact bf16 MFMA path) is implemented");
+  const int variant = mode & 0xff;
+  FT_SUPPORTED(variant == FT_FFN_EXACT || variant == FT_FFN_NATIVE_MX, "ft_moe_grouped_ffn: unknown mode");
   const bool run1 = stages != FT_FFN_DOWN_ONLY, run2 = stages != FT_FFN_GATE_UP_ONLY;
   const int H = L->H, I = L->I;
   FT_REQUIRE(H >= 1 && I >= 1 && L->expert_bytes > 0, "ft_moe_grouped_ffn: layout not initialised");
@@ -396,6 +439,8 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   } else {
     return fail(FT_EINVAL, "ft_moe_grouped_ffn: unknown weight dtype in layout");
   }
+  FT_SUPPORTED(variant == FT_FFN_EXACT || wd == FT_MXFP4,
+               "ft_moe_grouped_ffn: the native scaled-MFMA mode needs MXFP4 weights");
   if (T == 0) {
     clear_error();
     return FT_OK;
@@ -417,6 +462,54 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   const bool has_shared = shared_blob != nullptr;
   const int routed = T * k;
   const int rows = routed + (has_shared ? T : 0);
+
+  if (variant == FT_FFN_NATIVE_MX) {
+    const MxWorkspace W = mx_workspace_layout(T, k, H, I);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    GemmArgs g1{};
+    g1.pool = static_cast<const uint8_t *>(slot_pool);
+    g1.slot_of_expert = slot_of_expert;
+    g1.expert_bytes = L->expert_bytes;
+    g1.shared_blob = static_cast<const uint8_t *>(shared_blob);
+    g1.offsets = expert_offsets;
+    g1.E = E;
+    g1.T = T;
+    g1.k = k;
+    GemmArgs g2 = g1;
+    g1.off_w0 = L->off_gate;
+    g1.off_w1 = L->off_up;
+    g1.off_s0 = L->off_sgate;
+    g1.off_s1 = L->off_sup;
+    g1.K = H;
+    g1.N = I;
+    g1.sorted_rows = sorted_rows;
+    g1.out = ws + W.h;
+    g1.ldo = I;
+    g2.off_w0 = g2.off_w1 = L->off_down;
+    g2.off_s0 = g2.off_s1 = L->off_sdown;
+    g2.K = I;
+    g2.N = H;
+    g2.sorted_rows = nullptr;
+    g2.out = y_rows;
+    g2.ldo = H;
+    g2.out_shared = y_shared;
+    MxGemmArgs m1{g1, ws + W.xq, ws + W.xs, uint32_t(uint64_t(T) * H), uint32_t(uint64_t(T) * H / 32)};
+    MxGemmArgs m2{g2, ws + W.hq, ws + W.hs, uint32_t(uint64_t(rows) * I), uint32_t(uint64_t(rows) * I / 32)};
+    ft_status st = FT_OK;
+    if (run1) {
+      if ((st = mx_quantize_launch(static_cast<const uint16_t *>(x), H, T, H, ws + W.xq, ws + W.xs, stream)) != FT_OK)
+        return st;
+      if ((st = launch_mx_gemm<true>(m1, stream, "ffn_mx_gemm_kernel<gate_up>")) != FT_OK) return st;
+    }
+    if (run2) {
+      if ((st = mx_quantize_launch(reinterpret_cast<const uint16_t *>(ws + W.h), I, rows, I, ws + W.hq, ws + W.hs,
+                                   stream)) != FT_OK)
+        return st;
+      if ((st = launch_mx_gemm<false>(m2, stream, "ffn_mx_gemm_kernel<down>")) != FT_OK) return st;
+    }
+    clear_error();
+    return FT_OK;
+  }
 
   if (wd == FT_F32) {
     FfnF32Args a{};

@@ -63,6 +63,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
 
 namespace ft {
 
@@ -100,6 +101,19 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Block-scaled MFMA (OCP MX): D += (A * 2^(sa-127)) (B * 2^(sb-127)) over 128
+// contraction elements, A = 16 rows of FP8 E4M3, B = 16 columns of FP4 E2M1.
+// Operand lanes (l = 16 g + r): A lane holds row r at elements 16g..16g+15
+// (bytes 0..15) and 64+16g..64+16g+15 (bytes 16..31); B lane holds column r at
+// elements 32g..32g+31 (16 bytes, element 2i in the low nibble of byte i; the
+// upper four dwords are unused); the scale byte OPA of `sa` / OPB of `sb` in
+// lane (r, g) is the E8M0 scale of row / column r, elements 32g..32g+31.
+// Output lane (r, g) holds D[4g + v][r], v = 0..3.
+template <int OPA = 0, int OPB = 0>
+__device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, OPA, sa, OPB, sb);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

@@ -1,0 +1,238 @@
+// Grouped block-scaled MFMA GEMM: the native MXFP4 expert mode.
+//
+//   stage 1: h[p][i] = silu(sum_k X[p][k] Wg[i][k]) * (sum_k X[p][k] Wu[i][k])
+//   stage 2: y[p][n] = sum_k h[p][k] Wd[n][k]
+//
+// with X (and h) as MXFP8 E4M3 rows and the weights as stored, MXFP4 E2M1 with
+// their E8M0 block scales, both fed straight to
+// v_mfma_scale_f32_16x16x128_f8f6f4 (A = tokens, B = weights); nothing is
+// decoded in registers.
+//
+// Workgroup = 4 waves; tile = 128 segment rows (tokens) x 256 weight rows, the
+// same split as the exact-mode GEMM: stage 1 gives each wave 32 gate rows and
+// the same 32 up rows, stage 2 64 weight rows; per wave 8 token tiles x 4
+// weight tiles of 16x16 accumulators.  A chunk is 128 contraction elements, one
+// MFMA step.  Token codes of a chunk (128 rows x 128 bytes) and their scales
+// (128 rows x 4 bytes) are gathered into LDS by direct buffer-to-LDS loads,
+// double buffered; within a row, 16-byte slot j holds chunk piece
+// j ^ ((row / 2) % 8), so the 16 rows an MFMA operand reads hit distinct banks.
+// Weights go from global memory straight to registers (each weight row is
+// used by one wave), the next chunk's in flight while this one is multiplied.
+//
+// Index maps per chunk c, lane (r, g):
+//   token operand: row r of the 16-row tile, chunk bytes 16 g .. +15 and
+//                  64 + 16 g .. +15; scale = block g of the chunk.
+//   weight operand: row r of the tile, code bytes 64 c + 16 g .. +15
+//                   (elements 128 c + 32 g .. +31); scale byte 4 c + g of the row.
+// Token tiles whose 16 rows all lie past the segment skip their MFMAs.
+#pragma once
+
+#include "ft_internal.hpp"
+#include "gemm_prefill.hpp"
+
+namespace ft {
+
+constexpr int kMxBK = 128;                               // contraction elements per chunk
+constexpr int kMxPitch = 128;                            // LDS bytes per token row (codes of one chunk)
+constexpr int kMxCodeBytes = kGemmBM * kMxPitch;         // 16 KiB per buffer
+constexpr int kMxScaleBytes = 4 * 256;                   // per wave: 32 rows x 4 B + 128 B unused
+constexpr int kMxBufBytes = kMxCodeBytes + kMxScaleBytes;
+
+struct MxGemmArgs {
+  GemmArgs g;          // shapes, weights, segments and outputs (g.X, g.ldx, g.x_bytes unused)
+  const uint8_t *Xq;   // E4M3 codes [rows, K]
+  const uint8_t *Xs;   // E8M0 scales [rows, K / 32]
+  uint32_t xq_bytes, xs_bytes;
+};
+
+template <bool GLU>
+__device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, uint8_t *lds) {
+  const GemmArgs &a = ma.g;
+  constexpr int NT = 4;  // weight tiles (16 rows) per wave
+  constexpr int MT = 8;  // token tiles (16 rows) per wave
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, q = lane >> 4;
+
+  // ---- work item (XCD-contiguous ranges, as in the exact-mode GEMM)
+  const int G = int(gridDim.x), b = int(blockIdx.x);
+  const int per = G / 8;
+  const int logical = (b % 8) * per + b / 8;
+  if (logical >= a.n_items) return;
+  const int n_m = a.n_items / a.n_ntiles;
+  const int nt_idx = logical / n_m, mi = logical % n_m;
+  int e, row0, m;
+  if (!gemm_find_mtile<kGemmThreads>(a, mi, &e, &row0, &m)) return;
+  const bool shared = e == a.E;
+  const uint8_t *blob;
+  if (shared) {
+    blob = a.shared_blob;
+  } else {
+    const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    if (slot < 0) {
+      const int cols = GLU ? kGemmBN / 2 : kGemmBN;
+      const int c0 = nt_idx * cols;
+      for (int u = tid; u < m * cols; u += kGemmThreads) {
+        const int rr = u / cols, cc = c0 + u % cols;
+        if (cc >= a.N) continue;
+        if (GLU) reinterpret_cast<uint16_t *>(a.out)[int64_t(row0 + rr) * a.ldo + cc] = 0x7fc0;
+        else reinterpret_cast<float *>(a.out)[int64_t(row0 + rr) * a.ldo + cc] = __builtin_nanf("");
+      }
+      return;
+    }
+    blob = a.pool + uint64_t(slot) * a.expert_bytes;
+  }
+
+  auto src_row = [&](int rr) -> int {
+    if (rr >= m) return -1;
+    if (a.sorted_rows == nullptr) return (shared ? a.T * a.k : 0) + row0 + rr;  // hidden row
+    if (shared) return row0 + rr;                                             // token
+    return a.sorted_rows[row0 + rr] / a.k;                                    // gathered token
+  };
+
+  // ---- token codes: wave w fills rows 32w..32w+31 with 4 direct loads of 8
+  // rows each (lane i: row 8t + i/8, slot i%8); scales: one 4-byte direct
+  // load per wave into its own 256-byte area (lane i < 32: row 32w + i; lanes
+  // 32..63 load nothing and fill the unused upper half with zeros)
+  const uint32_t kq = uint32_t(a.K), ks32 = uint32_t(a.K) / 32;
+  const rsrc_t qres = make_rsrc(ma.Xq, ma.xq_bytes);
+  const rsrc_t sres_x = make_rsrc(ma.Xs, ma.xs_bytes);
+  uint32_t qsrc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int rr = wave * 32 + t * 8 + (lane >> 3);
+    const int src = src_row(rr);
+    const int j = (lane & 7) ^ ((rr >> 1) & 7);
+    qsrc[t] = src >= 0 ? uint32_t(src) * kq + uint32_t(j) * 16u : kOOB;
+  }
+  uint32_t ssrc = kOOB;
+  {
+    const int src = lane < 32 ? src_row(wave * 32 + lane) : -1;
+    ssrc = src >= 0 ? uint32_t(src) * ks32 : kOOB;
+  }
+
+  // ---- weights of this wave
+  const uint32_t wpitch = uint32_t(a.K) / 2, spitch = uint32_t(a.K) / 32;
+  const uint32_t wbytes = uint32_t(a.N) * wpitch, sbytes = uint32_t(a.N) * spitch;
+  rsrc_t wres[NT], sres[NT];
+  uint32_t wrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int row;
+    const uint8_t *wb, *sb;
+    if (GLU) {
+      row = nt_idx * (kGemmBN / 2) + wave * 32 + (t & 1) * 16 + r;
+      wb = blob + (t < 2 ? a.off_w0 : a.off_w1);
+      sb = blob + (t < 2 ? a.off_s0 : a.off_s1);
+    } else {
+      row = nt_idx * kGemmBN + wave * 64 + t * 16 + r;
+      wb = blob + a.off_w0;
+      sb = blob + a.off_s0;
+    }
+    wres[t] = make_rsrc(wb, wbytes);
+    sres[t] = make_rsrc(sb, sbytes);
+    wrow[t] = uint32_t(row);
+  }
+  struct BFrag {
+    u32x4 w[NT];
+    uint32_t s[NT];
+  };
+  auto load_b = [&](int c, BFrag &f) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f.w[t] = bld16(wres[t], wrow[t] * wpitch + uint32_t(c) * 64u + q * 16);
+      f.s[t] = bld4(sres[t], wrow[t] * spitch + uint32_t(c) * 4u);
+    }
+  };
+  auto load_a = [&](int c, int buf) {
+    uint8_t *base = lds + buf * kMxBufBytes;
+    uint8_t *cb = base + wave * 32 * kMxPitch;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qres, (__attribute__((address_space(3))) void *)(cb + t * 8 * kMxPitch), 16,
+          qsrc[t] == kOOB ? kOOB : qsrc[t] + uint32_t(c) * 128u, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        sres_x, (__attribute__((address_space(3))) void *)(base + kMxCodeBytes + wave * 256), 4,
+        ssrc == kOOB ? kOOB : ssrc + uint32_t(c) * 4u, 0, 0, 0);
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nch = a.K / kMxBK;
+  // this lane's LDS read addresses in buffer 0, tile 0: the two 16-byte pieces
+  // of its row and the row's scale dword; tile i adds i * 16 rows
+  const int sw = (r >> 1) & 7;
+  const uint8_t *pa_lo = lds + r * kMxPitch + ((q ^ sw) << 4);
+  const uint8_t *pa_hi = lds + r * kMxPitch + (((4 + q) ^ sw) << 4);
+  const uint8_t *pa_s = lds + kMxCodeBytes + r * 4;
+  BFrag f;
+  load_a(0, 0);
+  load_b(0, f);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int boff = (c & 1) * kMxBufBytes;
+    BFrag fn;
+    if (c + 1 < nch) {
+      load_a(c + 1, (c & 1) ^ 1);
+      load_b(c + 1, fn);
+    }
+    i32x8 bw[NT];
+    int bs[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      // FP4 operands use the low four dwords only
+      bw[t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(f.w[t], f.w[t], 0, 1, 2, 3, -1, -1, -1, -1));
+      bs[t] = int(f.s[t] >> (8 * q));
+    }
+    const uint8_t *plo = pa_lo + boff, *phi = pa_hi + boff, *ps = pa_s + boff;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const u32x4 lo = *reinterpret_cast<const u32x4 *>(plo + i * 16 * kMxPitch);
+      const u32x4 hi = *reinterpret_cast<const u32x4 *>(phi + i * 16 * kMxPitch);
+      // scales: wave area (row / 32) * 256, row (row % 32) * 4
+      const int as = int(*reinterpret_cast<const uint32_t *>(ps + (i >> 1) * 256 + (i & 1) * 64) >> (8 * q));
+      const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[i][t] = mfma_mx(av, bw[t], acc[i][t], as, bs[t]);
+    }
+    if (c + 1 < nch) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      f = fn;
+    }
+  }
+
+  // ---- epilogue: lane holds D[token 4q+v][weight row r] of each tile
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int rr = i * 16 + 4 * q + v;
+      if (rr >= m) continue;
+      if constexpr (GLU) {
+        const int hrow = shared ? a.T * a.k + row0 + rr : row0 + rr;
+        uint16_t *hp = reinterpret_cast<uint16_t *>(a.out) + int64_t(hrow) * a.ldo;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int col = nt_idx * (kGemmBN / 2) + wave * 32 + t * 16 + r;
+          if (col < a.N) hp[col] = f32_to_bf16_rne(silu(acc[i][t][v]) * acc[i][t + 2][v]);
+        }
+      } else {
+        float *yp = shared ? a.out_shared + int64_t(row0 + rr) * a.ldo
+                           : reinterpret_cast<float *>(a.out) + int64_t(row0 + rr) * a.ldo;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int col = nt_idx * kGemmBN + wave * 64 + t * 16 + r;
+          if (col < a.N) yp[col] = acc[i][t][v];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace ft

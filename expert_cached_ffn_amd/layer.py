@@ -114,10 +114,11 @@ class MoELayer:
         ops.ft_moe_combine(self.y_rows, w, self.row_pos, ys, T, s.k, s.H, out_dt, self.out, stream=stream)
 
     def forward(self, T, x, pool, w_router=None, logits=None, slot_of_expert=None, shared_blob=None,
-                stream=None):
+                stream=None, mode=0):
         """route -> permute -> grouped FFN -> combine, all enqueued on one stream."""
         self.route(T, x=x, w_router=w_router, logits=logits, stream=stream)
         self.permute(T, stream=stream)
-        self.ffn(T, x, pool, slot_of_expert=slot_of_expert, shared_blob=shared_blob, stream=stream)
+        self.ffn(T, x, pool, slot_of_expert=slot_of_expert, shared_blob=shared_blob, stream=stream,
+                 mode=mode)
         self.combine(T, with_shared=shared_blob is not None, stream=stream)
         return self.out[:T]

@@ -77,6 +77,10 @@ def ft_moe_grouped_ffn(layout: ExpertLayout, slot_pool, slot_of_expert, shared_b
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def ft_mxfp8_quantize(x, ldx: int, n: int, K: int, codes, scales, stream=None) -> None:
+    _check(_lib.lib().ft_mxfp8_quantize(_ptr(x), ldx, n, K, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
 def ft_moe_combine(y_rows, topk_w, row_pos, y_shared, T: int, k: int, H: int, out_dtype: int, out,
                    stream=None) -> None:
     _check(_lib.lib().ft_moe_combine(_ptr(y_rows), _ptr(topk_w), _ptr(row_pos), _ptr(y_shared), T, k, H,

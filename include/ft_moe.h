@@ -162,20 +162,33 @@ ft_status ft_moe_permute(const int32_t *topk_ids, int32_t T, int32_t k, int32_t 
  * shared_blob (nullable): one more expert in the same layout, applied to every
  *   token with weight 1, written to y_shared [T, H] fp32 (required iff
  *   shared_blob != NULL).
- * mode, low byte: 0 = exact path -- MXFP4 weights decoded exactly to bf16,
- *   bf16 MFMA, fp32 accumulation; the SwiGLU hidden vector is rounded to
- *   bf16 before the down projection.  Other values: FT_ENOTSUP.
+ * mode, low byte:
+ *   FT_FFN_EXACT (0) -- MXFP4 weights decoded exactly to bf16, bf16 MFMA,
+ *     fp32 accumulation; the SwiGLU hidden vector is rounded to bf16 before
+ *     the down projection.
+ *   FT_FFN_NATIVE_MX (1, FT_MXFP4 weights only; otherwise FT_ENOTSUP) -- the
+ *     matrix unit takes the MXFP4 weights as stored: x and the bf16-rounded
+ *     hidden vector are quantized to MXFP8 E4M3 exactly as ft_mxfp8_quantize
+ *     does, and both products run as block-scaled FP8 x FP4 MFMA with fp32
+ *     accumulation.  The results differ from FT_FFN_EXACT by the activation
+ *     quantization (a few percent); they match a float64 evaluation of the
+ *     same quantized operands.
+ *   Other values: FT_ENOTSUP.
  * mode, stage bits: FT_FFN_GATE_UP_ONLY runs only the gate/up + SwiGLU stage
- *   (the hidden rows stay in `workspace`, y is not written);
- *   FT_FFN_DOWN_ONLY runs only the down projection from the hidden rows a
- *   previous FT_FFN_GATE_UP_ONLY call with the same arguments and workspace
- *   left there.  Neither bit: both stages.  Both bits: FT_EINVAL.
+ *   (y is not written); FT_FFN_DOWN_ONLY runs only the down projection from
+ *   the hidden rows in `workspace` (left there by a FT_FFN_GATE_UP_ONLY call
+ *   with the same arguments, or written by the caller).  Neither bit: both
+ *   stages.  Both bits: FT_EINVAL.  For bf16 and MXFP4 weights the hidden
+ *   rows are bf16 [T*k (+T), I] at the start of the workspace: row p of the
+ *   permuted order, then the shared expert's row of token t at T*k + t; fp32
+ *   weights keep fp32 rows there.
  * workspace: ft_workspace_bytes(FT_WS_FFN, T, k, E, H, I) bytes.
  * Limits: FT_BF16 weights need H, I multiples of 128; FT_MXFP4 multiples of
  *   256; E <= 4096.  MXFP4 scale bytes must lie in 2..252 (every decoded value
  *   is then an exact bf16).  Buffers 16-byte aligned, slot_pool and blobs
  *   256-byte aligned.
  */
+enum { FT_FFN_EXACT = 0, FT_FFN_NATIVE_MX = 1 };
 enum { FT_FFN_GATE_UP_ONLY = 0x100, FT_FFN_DOWN_ONLY = 0x200 };
 ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
                              const int32_t *slot_of_expert, const void *shared_blob,
@@ -183,6 +196,24 @@ ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
                              const int32_t *expert_offsets, const int32_t *sorted_rows,
                              float *y_rows, float *y_shared, int32_t mode,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ft_mxfp8_quantize -- bf16 rows to MXFP8, the activation format of the native
+ * MXFP4 mode (the pages name natively MXFP4-quantized routed experts, FreeToken
+ * quantization page, "Formatos compatibles, hardware y perfil de rendimiento";
+ * the format is OCP Microscaling Formats v1.0).  Each block of 32 consecutive
+ * elements of a row gets the E8M0 scale byte b = floor(log2 amax) - 8 + 127
+ * (amax = largest magnitude of the block; 0 for an all-zero block; clamped to
+ * 0..254), and element v the FP8 E4M3 code nearest to v / 2^(b-127), ties to
+ * the even code, magnitudes above 448 saturating to 448, the sign kept when v
+ * rounds to zero.
+ * x [n, K] bf16 with row pitch ldx elements (ldx >= K, a multiple of 8);
+ * codes [n, K] bytes (row pitch K); scales [n, K / 32] bytes, scale j of a row
+ * covering elements 32j .. 32j+31.  K a multiple of 32; x and codes 16-byte
+ * aligned.  NaN or infinite inputs are outside the contract.
+ */
+ft_status ft_mxfp8_quantize(const void *x, int64_t ldx, int32_t n, int32_t K, uint8_t *codes,
+                            uint8_t *scales, hipStream_t stream);
 
 /*
  * ft_moe_combine -- out[t] = sum_{j<k} topk_w[t, j] * y_rows[row_pos[t*k + j]]

@@ -102,7 +102,10 @@ def test_ffn_validation():
     Lb = ops.ft_expert_layout_init(1, 384, 200)   # I not a multiple of 128
     f = ops.ft_moe_grouped_ffn
     ok = dict(workspace=256, workspace_bytes=1 << 30, stream=0)
-    assert _err(f, L4, 256, None, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 1, **ok) == -2   # mode 1
+    Lbf = ops.ft_expert_layout_init(1, 256, 256)
+    assert _err(f, Lbf, 256, None, None, 256, 1, 1, 2, 2, 256, 256, 256, None, 1, **ok) == -2   # mode 1, bf16
+    assert _err(f, L4, 256, None, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 2, **ok) == -2   # mode 2
+    assert _err(f, L4, 256, None, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 0x400, **ok) == -1  # mode bits
     assert _err(f, L4, 256, None, None, 256, 0, 1, 6, 256, 256, 256, 256, None, 0, **ok) == -1   # x dtype
     assert _err(f, Lb, 256, None, None, 256, 1, 1, 2, 8, 256, 256, 256, None, 0, **ok) == -2     # I % 128
     assert _err(f, L4, 256, None, 256, 256, 1, 1, 6, 256, 256, 256, 256, None, 0, **ok) == -1    # shared w/o y_shared
@@ -110,6 +113,16 @@ def test_ffn_validation():
     assert _err(f, L4, 256, None, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 0,
                 workspace=256, workspace_bytes=16, stream=0) == -1                                # workspace
     assert _err(f, L4, 256, None, None, 256, 1, 1, 7, 6, 256, 256, 256, None, 0, **ok) == -2     # k > E
+
+
+def test_mxfp8_quantize_validation():
+    from expert_cached_ffn_amd import ops
+    f = ops.ft_mxfp8_quantize
+    assert _err(f, 16, 48, 2, 48, 16, 16, stream=0) == -1     # K % 32
+    assert _err(f, 16, 16, 2, 32, 16, 16, stream=0) == -1     # ldx < K
+    assert _err(f, 16, 36, 2, 32, 16, 16, stream=0) == -1     # ldx % 8
+    assert _err(f, None, 32, 2, 32, 16, 16, stream=0) == -1   # NULL input
+    f(None, 32, 0, 32, None, None, stream=0)                  # n = 0: no-op
 
 
 def test_combine_validation():

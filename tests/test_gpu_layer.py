@@ -6,7 +6,7 @@ torch = pytest.importorskip("torch")
 
 import synth
 from oracle import formats, moe
-from tests.helpers import Experts, check_close, route_oracle
+from tests.helpers import Experts, check_close, native_mx_expert, native_mx_token, route_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -84,22 +84,30 @@ def test_layer_prefill_given_logits(L):
     print("prefill: packing 257 experts", flush=True)
     pool = build_pool(L, layer, ex, range(cfg.E), cfg.E)
     shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0]
-    print("prefill: running", flush=True)
-    layer.forward(T, L.to_device(x), pool, logits=L.to_device(logits), shared_blob=shared)
-    torch.cuda.synchronize()
-    assert np.array_equal(layer.ids[:T].cpu().numpy(), ids)
-    off_ref, rows_ref, _ = moe.permute(ids, cfg.E)
-    assert np.array_equal(layer.offsets.cpu().numpy(), off_ref)
-    got = out_f64(layer, cfg, T)
-    assert np.all(np.isfinite(got))
     x64 = formats.activations_to_f64(cfg.xdtype, x)
-    toks = [0, 4097, T - 1]
-    ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E)) for t in toks])
-    check_close(got[toks], ref, bf16_out=True, what="prefill sampled tokens")
-    # one expert's whole segment in the permuted expert rows (the least popular non-empty expert)
+    off_ref, rows_ref, _ = moe.permute(ids, cfg.E)
     sizes = np.diff(off_ref)
-    e = int(np.argmin(np.where(sizes > 0, sizes, 10 ** 9)))
+    e = int(np.argmin(np.where(sizes > 0, sizes, 10 ** 9)))   # the least popular non-empty expert
     a, b = int(off_ref[e]), int(off_ref[e + 1])
-    yr = layer.y_rows[a:b].cpu().numpy()
-    yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
-    check_close(yr, yref, what=f"prefill segment of expert {e}")
+    toks = [0, 4097, T - 1]
+    for mode in (0, 1):      # exact bf16 MFMA, then the native MXFP4 scaled MFMA
+        print(f"prefill: running mode {mode}", flush=True)
+        layer.forward(T, L.to_device(x), pool, logits=L.to_device(logits), shared_blob=shared, mode=mode)
+        torch.cuda.synchronize()
+        assert np.array_equal(layer.ids[:T].cpu().numpy(), ids)
+        assert np.array_equal(layer.offsets.cpu().numpy(), off_ref)
+        got = out_f64(layer, cfg, T)
+        assert np.all(np.isfinite(got))
+        yr = layer.y_rows[a:b].cpu().numpy()
+        if mode == 0:
+            ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E)) for t in toks])
+            check_close(got[toks], ref, bf16_out=True, what="prefill mode 0 sampled tokens")
+            # one expert's whole segment in the permuted expert rows
+            yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
+            check_close(yr, yref, what=f"prefill mode 0 segment of expert {e}")
+        else:
+            pairs = [native_mx_token(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E)) for t in toks]
+            check_close(got[toks], np.stack([p[0] for p in pairs]), bf16_out=True,
+                        what="prefill mode 1 sampled tokens", allow=np.stack([p[1] for p in pairs]))
+            yref, allow = native_mx_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
+            check_close(yr, yref, what=f"prefill mode 1 segment of expert {e}", allow=allow)

@@ -119,40 +119,61 @@ def test_permute_bit_exact(ops, T, k, E, kind):
 
 # ----------------------------------------------------------------------------- grouped FFN
 
-def _ffn_case(ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None):
-    """Run the GPU grouped FFN on oracle permutation data; return (gpu y_rows, y_shared, oracle ...)."""
-    from expert_cached_ffn_amd.layer import DTYPES, pack_expert
-    with_shared = cfg.shared if with_shared is None else with_shared
-    ex = Experts(cfg)
-    lay = ops.ft_expert_layout_init(DTYPES[cfg.wdtype], cfg.H, cfg.I)
-    off, rows, pos = moe.permute(ids, cfg.E)
-    used = sorted(set(ids.ravel().tolist()))
-    rng = np.random.default_rng(99)
-    n_slots = len(used) + 3
-    slot_ids = rng.permutation(n_slots)[:len(used)] if shuffle_slots else np.arange(len(used))
-    slot_of = np.full(cfg.E, -1, np.int32)
-    pool = np.zeros((n_slots, int(lay.expert_bytes)), np.uint8)
-    for e, s in zip(used, slot_ids):
-        slot_of[e] = s
-        pack_expert(lay, ex.raw(e).arrays, pool[s])
-    if missing is not None:
-        slot_of[missing] = -1
-    x = synth.tokens(cfg, T)
-    x64 = formats.activations_to_f64(cfg.xdtype, x)
-    shared_blob = None
-    if with_shared:
-        shared_blob = dev(pack_expert(lay, ex.raw(cfg.E).arrays))
-    R = T * cfg.k
-    y = torch.full((R, cfg.H), np.nan, dtype=torch.float32, device="cuda")
-    ys = torch.full((T, cfg.H), np.nan, dtype=torch.float32, device="cuda") if with_shared else None
-    wsb = ops.ft_workspace_bytes(2, T, cfg.k, cfg.E, cfg.H, cfg.I)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    ops.ft_moe_grouped_ffn(lay, dev(pool), dev(slot_of), shared_blob, dev(x), DTYPES[cfg.xdtype], T, cfg.k,
-                           cfg.E, dev(off), dev(rows), y, ys, 0, ws, wsb)
-    torch.cuda.synchronize()
-    y_ref = moe.grouped_ffn(x64, cfg.k, off, rows, ex.f64)
-    ys_ref = moe.swiglu_expert(x64, *ex.f64(cfg.E)) if with_shared else None
-    return y.cpu().numpy(), (ys.cpu().numpy() if with_shared else None), y_ref, ys_ref, off
+class _FfnRig:
+    """Device inputs of one grouped-FFN case built from oracle permutation data."""
+
+    def __init__(self, ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None):
+        from expert_cached_ffn_amd.layer import DTYPES, pack_expert
+        self.ops, self.cfg, self.T = ops, cfg, T
+        self.with_shared = cfg.shared if with_shared is None else with_shared
+        self.ex = ex = Experts(cfg)
+        self.lay = lay = ops.ft_expert_layout_init(DTYPES[cfg.wdtype], cfg.H, cfg.I)
+        self.off, self.rows, _ = moe.permute(ids, cfg.E)
+        used = sorted(set(ids.ravel().tolist()))
+        rng = np.random.default_rng(99)
+        n_slots = len(used) + 3
+        slot_ids = rng.permutation(n_slots)[:len(used)] if shuffle_slots else np.arange(len(used))
+        slot_of = np.full(cfg.E, -1, np.int32)
+        pool = np.zeros((n_slots, int(lay.expert_bytes)), np.uint8)
+        for e, s in zip(used, slot_ids):
+            slot_of[e] = s
+            pack_expert(lay, ex.raw(e).arrays, pool[s])
+        if missing is not None:
+            slot_of[missing] = -1
+        self.x = synth.tokens(cfg, T)
+        self.x64 = formats.activations_to_f64(cfg.xdtype, self.x)
+        self.shared_blob = dev(pack_expert(lay, ex.raw(cfg.E).arrays)) if self.with_shared else None
+        R = T * cfg.k
+        self.y = torch.full((R, cfg.H), np.nan, dtype=torch.float32, device="cuda")
+        self.ys = torch.full((T, cfg.H), np.nan, dtype=torch.float32, device="cuda") if self.with_shared else None
+        self.wsb = ops.ft_workspace_bytes(2, T, cfg.k, cfg.E, cfg.H, cfg.I)
+        self.ws = torch.zeros(self.wsb, dtype=torch.uint8, device="cuda")
+        self.dev = (dev(pool), dev(slot_of), dev(self.x), dev(self.off), dev(self.rows))
+
+    def run(self, mode):
+        from expert_cached_ffn_amd.layer import DTYPES
+        c = self.cfg
+        pool, slot_of, x, off, rows = self.dev
+        self.ops.ft_moe_grouped_ffn(self.lay, pool, slot_of, self.shared_blob, x, DTYPES[c.xdtype], self.T, c.k,
+                                    c.E, off, rows, self.y, self.ys, mode, self.ws, self.wsb)
+        torch.cuda.synchronize()
+
+    def hidden(self, n_rows):
+        """The bf16 hidden rows the gate/up stage left at the start of the workspace."""
+        b = self.ws[:n_rows * self.cfg.I * 2].cpu().numpy().view(np.uint16)
+        return formats.bf16_to_f64(b.reshape(n_rows, self.cfg.I))
+
+
+def _ffn_case(ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None, mode=0):
+    """Run the GPU grouped FFN on oracle permutation data; return (gpu y_rows, y_shared, oracle ...).
+
+    mode 1 (native MXFP4) is compared with the oracle's native-mode expert."""
+    rig = _FfnRig(ops, cfg, T, ids, shuffle_slots, with_shared, missing)
+    rig.run(mode)
+    fn = moe.swiglu_expert_mx if mode == 1 else moe.swiglu_expert
+    y_ref = moe.grouped_ffn(rig.x64, cfg.k, rig.off, rig.rows, rig.ex.f64, fn)
+    ys_ref = fn(rig.x64, *rig.ex.f64(cfg.E)) if rig.with_shared else None
+    return (rig.y.cpu().numpy(), (rig.ys.cpu().numpy() if rig.with_shared else None), y_ref, ys_ref, rig.off)
 
 
 FFN_CASES = [
@@ -186,6 +207,128 @@ def test_grouped_ffn_missing_slot_gives_nan(ops):
     assert np.all(np.isnan(y[a:b]))
     keep = np.r_[0:a, b:len(y)]
     check_close(y[keep], y_ref[keep], what="other experts")
+
+
+# ----------------------------------------------------------------------------- native MXFP4 mode
+
+def _bf16_rows(rng, n, K):
+    """bf16 bit patterns spanning many binades, with the special cases of the quantizer."""
+    mag = rng.standard_normal((n, K)) * np.exp2(rng.integers(-20, 20, size=(n, K // 32)).repeat(32, axis=1))
+    v = np.asarray(mag, np.float32).view(np.uint32)
+    bits = ((v + 0x7FFF + ((v >> 16) & 1)) >> 16).astype(np.uint16)
+    bits[0, :32] = 0                      # an all-zero block
+    bits[0, 32:64] = 0x8000               # all -0.0
+    bits[1, :32] = np.arange(1, 33)       # bf16 subnormals
+    if K >= 128:
+        bits[1, 64:96] = 0x4380           # 256.0 everywhere: amax a power of two
+        bits[1, 96:128] = rng.integers(0, 65536, 32).astype(np.uint16) & 0x7F7F  # finite mixed signs
+    return bits
+
+
+@pytest.mark.parametrize("n,K,ldx", [(1, 32, 32), (7, 96, 104), (64, 2048, 2048), (257, 4096, 4096)])
+def test_mxfp8_quantize_bit_exact(ops, n, K, ldx):
+    from oracle import mx
+    rng = np.random.default_rng(n * 1000 + K)
+    bits = np.zeros((n, ldx), np.uint16)
+    bits[:, :K] = _bf16_rows(rng, max(n, 2), K)[:n]
+    codes = torch.empty((n, K), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, K // 32), dtype=torch.uint8, device="cuda")
+    ops.ft_mxfp8_quantize(dev(bits), ldx, n, K, codes, scales)
+    torch.cuda.synchronize()
+    q_ref, s_ref = mx.mxfp8_quantize(formats.bf16_to_f64(bits[:, :K]))
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+
+
+MX_CASES = [
+    ("mx-small", dict(H=1024, I=512, E=6, k=2), 37),
+    ("mx-long-segment", dict(H=512, I=1024, E=2, k=1), 150),
+    ("mx-ragged-tiles", dict(H=512, I=768, E=5, k=3), 300),
+    ("mx-cfg3-T1", {}, 1),
+    ("mx-cfg3-T8", {}, 8),
+]
+
+
+@pytest.mark.parametrize("name,over,T", MX_CASES, ids=[c[0] for c in MX_CASES])
+def test_grouped_ffn_native_mx_parity(ops, name, over, T):
+    from tests.helpers import native_mx_expert
+    print(f"ffn {name}", flush=True)
+    cfg = synth.shrink(synth.CONFIGS[3], **over)
+    ids = synth.routing_ids_uniform(cfg, T)
+    rig = _FfnRig(ops, cfg, T, ids)
+    rig.run(1)
+    y = rig.y.cpu().numpy()
+    y_ref = np.zeros_like(y, dtype=np.float64)
+    allow = np.zeros_like(y_ref)
+    for e in range(cfg.E):
+        a, b = int(rig.off[e]), int(rig.off[e + 1])
+        if a < b:
+            y_ref[a:b], allow[a:b] = native_mx_expert(rig.x64[rig.rows[a:b] // cfg.k], *rig.ex.f64(e))
+    check_close(y, y_ref, what=f"{name} y_rows", allow=allow)
+    if rig.with_shared:
+        ys_ref, ys_allow = native_mx_expert(rig.x64, *rig.ex.f64(cfg.E))
+        check_close(rig.ys.cpu().numpy(), ys_ref, what=f"{name} y_shared", allow=ys_allow)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_grouped_ffn_stages_through_the_workspace(ops, mode):
+    """Gate/up alone leaves the bf16 hidden rows in the workspace; down alone reads them.
+    The down stage gets hidden rows written by the test, so both sides quantize the
+    same bf16 values (native mode: bit-identical codes) and the bound is the plain one."""
+    from oracle import mx
+    cfg = synth.shrink(synth.CONFIGS[3], H=1024, I=512, E=6, k=2)
+    T = 37
+    ids = synth.routing_ids_uniform(cfg, T)
+    rig = _FfnRig(ops, cfg, T, ids)
+    R, rows_all = T * cfg.k, T * cfg.k + T
+    rig.run(mode | 0x100)
+    h = rig.hidden(rows_all)
+    assert np.all(np.isnan(rig.y.cpu().numpy()))          # gate/up alone writes no output
+    x_in = mx.mxfp8_round_trip(rig.x64) if mode == 1 else rig.x64
+    h_ref = np.zeros((rows_all, cfg.I))
+    for e in range(cfg.E + 1):
+        if e < cfg.E:
+            a, b = int(rig.off[e]), int(rig.off[e + 1])
+            X = x_in[rig.rows[a:b] // cfg.k]
+        else:
+            a, b = R, rows_all
+            X = x_in
+        if a < b:
+            Wg, Wu, _ = rig.ex.f64(e)
+            G, U = X @ Wg.T, X @ Wu.T
+            h_ref[a:b] = G * moe.sigmoid(G) * U
+    check_close(h, h_ref, bf16_out=True, what=f"mode {mode} hidden rows")
+    # down stage from hidden rows of the test's own (seeded, synthetic) making
+    rng = np.random.default_rng(7 + mode)
+    hv = (rng.standard_normal((rows_all, cfg.I)) * 20).astype(np.float32).view(np.uint32)
+    hb = ((hv + 0x7FFF + ((hv >> 16) & 1)) >> 16).astype(np.uint16)
+    rig.ws[:hb.nbytes].copy_(torch.from_numpy(hb.view(np.uint8).ravel()))
+    rig.run(mode | 0x200)
+    h_in = formats.bf16_to_f64(hb)
+    if mode == 1:
+        h_in = mx.mxfp8_round_trip(h_in)
+    y_ref = np.zeros((R, cfg.H))
+    for e in range(cfg.E):
+        a, b = int(rig.off[e]), int(rig.off[e + 1])
+        if a < b:
+            y_ref[a:b] = h_in[a:b] @ rig.ex.f64(e)[2].T
+    check_close(rig.y.cpu().numpy(), y_ref, what=f"mode {mode} down stage")
+    check_close(rig.ys.cpu().numpy(), h_in[R:] @ rig.ex.f64(cfg.E)[2].T, what=f"mode {mode} shared down")
+
+
+def test_grouped_ffn_native_mx_missing_slot_gives_nan(ops):
+    from tests.helpers import native_mx_expert
+    cfg = synth.shrink(synth.CONFIGS[3], H=512, I=512, E=4, k=1, shared=False)
+    ids = np.array([[0], [1], [2], [1]], np.int32)
+    rig = _FfnRig(ops, cfg, 4, ids, missing=1)
+    rig.run(1)
+    y = rig.y.cpu().numpy()
+    a, b = int(rig.off[1]), int(rig.off[2])
+    assert np.all(np.isnan(y[a:b]))
+    for e in (0, 2):
+        a, b = int(rig.off[e]), int(rig.off[e + 1])
+        ref, allow = native_mx_expert(rig.x64[rig.rows[a:b]], *rig.ex.f64(e))
+        check_close(y[a:b], ref, what=f"expert {e}", allow=allow)
 
 
 # ----------------------------------------------------------------------------- combine
