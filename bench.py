@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s (decode, prefill) + % HBM BW / % MFMA peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense MFMA bf16
+FP8_PEAK_TFLOPS = 5000.0       # dense MFMA fp8 (and fp8 x fp4 block-scaled)
 N_INPUT_SETS = 8
 
 
@@ -222,8 +223,10 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     log(f"copy calibration: {reps} x {nbytes} B device copy")
 
 
-def run_prefill(args, cfg, T):
-    """Prefill layer: given Zipf-skewed logits, grouped MFMA GEMM over ragged segments."""
+def run_prefill(args, cfg, T, mode=0):
+    """Prefill layer: given Zipf-skewed logits, grouped MFMA GEMM over ragged segments.
+
+    mode 0: exact (MXFP4 decoded to bf16, bf16 MFMA); mode 1: native (MXFP8 x MXFP4 scaled MFMA)."""
     import torch
     import synth
     from expert_cached_ffn_amd import layer as L
@@ -251,10 +254,10 @@ def run_prefill(args, cfg, T):
         layer.permute(T)
         if tm is not None:
             tm.mark()
-        layer.ffn(T, xs[r], pool, shared_blob=shared, mode=_lib.FT_FFN_GATE_UP_ONLY)
+        layer.ffn(T, xs[r], pool, shared_blob=shared, mode=mode | _lib.FT_FFN_GATE_UP_ONLY)
         if tm is not None:
             tm.mark()
-        layer.ffn(T, xs[r], pool, shared_blob=shared, mode=_lib.FT_FFN_DOWN_ONLY)
+        layer.ffn(T, xs[r], pool, shared_blob=shared, mode=mode | _lib.FT_FFN_DOWN_ONLY)
         if tm is not None:
             tm.mark()
         layer.combine(T)
@@ -273,7 +276,7 @@ def run_prefill(args, cfg, T):
     ms = start.elapsed_time(end) / args.steps
     gu = float(np.mean([tm.ev[3 * i].elapsed_time(tm.ev[3 * i + 1]) for i in range(args.steps)]))
     dn = float(np.mean([tm.ev[3 * i + 1].elapsed_time(tm.ev[3 * i + 2]) for i in range(args.steps)]))
-    log(f"prefill T={T}: {ms:.3f} ms/step ({T / (ms * 1e-3):,.0f} tok/s); gate/up {gu:.3f} ms = "
+    log(f"prefill mode {mode} T={T}: {ms:.3f} ms/step ({T / (ms * 1e-3):,.0f} tok/s); gate/up {gu:.3f} ms = "
         f"{flops_gu / (gu * 1e-3) / 1e12:.0f} TFLOP/s, down {dn:.3f} ms = "
         f"{flops_all / 3 / (dn * 1e-3) / 1e12:.0f} TFLOP/s; FFN {flops_all / ((gu + dn) * 1e-3) / 1e12:.0f} TFLOP/s")
     return dict(ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), gate_up_ms=gu, down_ms=dn,
@@ -409,6 +412,9 @@ WORKLOADS = {
                        "512 cache slots = 25 %, 512 steps of batch 1, Zipf(1.1) + 60 % reuse routing)"),
     "prefill-mxfp4": (4, "dsv4-flash-shaped MXFP4 prefill MoE layer (8192 tokens, H=4096, I=2048, 256 experts "
                          "top-6 sigmoid with Zipf(1.1) popularity + 1 shared, SwiGLU)"),
+    "prefill-mxfp4-native": (4, "dsv4-flash-shaped MXFP4 prefill MoE layer (8192 tokens, H=4096, I=2048, 256 "
+                                "experts top-6 sigmoid with Zipf(1.1) popularity + 1 shared, SwiGLU), native "
+                                "MXFP8 x MXFP4 scaled-MFMA mode"),
     "decode-bf16": (2, "qwen3-a3b-shaped bf16 decode MoE layer (H=2048, I=768, 128 experts, top-8 softmax "
                        "renormalised, SwiGLU)"),
     "decode-mxfp4": (3, "dsv4-flash-shaped MXFP4 decode MoE layer (H=4096, I=2048, 256 experts top-6 sigmoid "
@@ -456,15 +462,18 @@ def main():
         return
     if args.workload.startswith("prefill"):
         T = cfg.batches[0]
-        p = run_prefill(args, cfg, T)
+        native = args.workload.endswith("native")
+        p = run_prefill(args, cfg, T, mode=1 if native else 0)
         ach = p["flops_gate_up"] / (p["gate_up_ms"] * 1e-3) / 1e12
+        peak = FP8_PEAK_TFLOPS if native else BF16_PEAK_TFLOPS
         out = {
             "metric": METRIC, "value": p["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": p["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "mxfp4-w/bf16", "data": "synthetic",
+            "vs_baseline": None, "dtype": "mxfp8-a/mxfp4-w" if native else "mxfp4-w/bf16", "data": "synthetic",
             "config": {"workload": desc, "batch_tokens": T},
-            "roofline": {"bound": "mfma", "kernel": "ffn_gemm_kernel<mxfp4, gate_up>", "achieved": ach,
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+            "roofline": {"bound": "mfma",
+                         "kernel": "ffn_mx_gemm_kernel<gate_up>" if native else "ffn_gemm_kernel<mxfp4, gate_up>",
+                         "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
                          "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"]},
             "ffn_TFLOPs": p["flops_ffn"] / ((p["gate_up_ms"] + p["down_ms"]) * 1e-3) / 1e12,
         }

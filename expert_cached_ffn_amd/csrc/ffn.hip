@@ -267,10 +267,17 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
 
 // ------------------------------------------------------------------ prefill grouped GEMM
 
+// Two pipeline stages.  MXFP4 weights: two workgroups per CU (measured
+// faster than four stages at one workgroup per CU: the second wave on each
+// SIMD hides the FP4 decode and the MFMA dependency chains).  bf16 weights
+// need four times the weight registers: one workgroup per CU, so that
+// nothing spills.
 template <int WF, bool GLU>
-__global__ __launch_bounds__(kGemmThreads, 2) void ffn_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kGemmBM * kGemmPitch];
-  gemm_tile<WF, GLU>(a, lds);
+__global__ __launch_bounds__(kGemmThreads, WF == WF_BF16 ? 1 : 2) void ffn_gemm_kernel(GemmArgs a) {
+  constexpr int B = kGemmBM * kGemmPitch;
+  __shared__ __attribute__((aligned(16))) uint8_t l0[B];
+  __shared__ __attribute__((aligned(16))) uint8_t l1[B];
+  gemm_tile<WF, GLU, 2>(a, LdsRing<2>{{l0, l1}});
 }
 
 // Upper bound of token tiles over all segments (+ the shared expert).
@@ -284,7 +291,8 @@ static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
   const int nt = GLU ? cdiv(a.N, kGemmBN / 2) : cdiv(a.N, kGemmBN);
   const int mb = gemm_mtiles_bound(a.T, a.k, a.E, a.shared_blob != nullptr);
   a.n_ntiles = nt;
-  a.n_items = nt * mb;
+  a.n_mtiles = mb;
+  a.n_items = gemm_item_count(mb, nt);
   const int grid = cdiv(a.n_items, 8) * 8;
   hipLaunchKernelGGL((ffn_gemm_kernel<WF, GLU>), dim3(unsigned(grid)), dim3(kGemmThreads), 0, stream, a);
   FT_LAUNCHED(name);
@@ -293,10 +301,16 @@ static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
 
 // ------------------------------------------------------------------ native MXFP4 mode GEMM
 
+// Four pipeline stages at one workgroup per CU (68 KiB of LDS; three stages at
+// two workgroups per CU would spill).
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mx_gemm_kernel(MxGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMxBufBytes];
-  gemm_mx_tile<GLU>(a, lds);
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kMxBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kMxBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[kMxBufBytes];
+  static_assert(kMxStages == 4, "one array per stage");
+  gemm_mx_tile<GLU>(a, LdsRing<kMxStages>{{lds0, lds1, lds2, lds3}});
 }
 
 template <bool GLU>
@@ -304,7 +318,8 @@ static ft_status launch_mx_gemm(MxGemmArgs a, hipStream_t stream, const char *na
   const int nt = GLU ? cdiv(a.g.N, kGemmBN / 2) : cdiv(a.g.N, kGemmBN);
   const int mb = gemm_mtiles_bound(a.g.T, a.g.k, a.g.E, a.g.shared_blob != nullptr);
   a.g.n_ntiles = nt;
-  a.g.n_items = nt * mb;
+  a.g.n_mtiles = mb;
+  a.g.n_items = gemm_item_count(mb, nt);
   const int grid = cdiv(a.g.n_items, 8) * 8;
   hipLaunchKernelGGL((ffn_mx_gemm_kernel<GLU>), dim3(unsigned(grid)), dim3(kGemmThreads), 0, stream, a);
   FT_LAUNCHED(name);

@@ -130,6 +130,28 @@ __device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) { return __builtin
 __device__ __forceinline__ uint32_t bld4(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer used here
 
+// s_waitcnt for vector-memory operations only: at most N still outstanding
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the vector-memory part of __syncthreads()'s fence:
+// that would wait for every direct-to-LDS load in flight, including those
+// meant to stay in flight across the barrier.  Callers wait (vmcnt) for the
+// loads the other waves must see before calling it.  This wave's own LDS
+// reads do complete first (lgkmcnt 0): another wave may overwrite the buffer
+// as soon as it passes.  The empty asm statements keep the compiler from
+// moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // 16-byte global load/store helpers.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }

@@ -13,11 +13,12 @@
 // the same 32 up rows, stage 2 64 weight rows; per wave 8 token tiles x 4
 // weight tiles of 16x16 accumulators.  A chunk is 128 contraction elements, one
 // MFMA step.  Token codes of a chunk (128 rows x 128 bytes) and their scales
-// (128 rows x 4 bytes) are gathered into LDS by direct buffer-to-LDS loads,
-// double buffered; within a row, 16-byte slot j holds chunk piece
-// j ^ ((row / 2) % 8), so the 16 rows an MFMA operand reads hit distinct banks.
-// Weights go from global memory straight to registers (each weight row is
-// used by one wave), the next chunk's in flight while this one is multiplied.
+// (128 rows x 4 bytes) are gathered into LDS by direct buffer-to-LDS loads;
+// within a row, 16-byte slot j holds chunk piece j ^ ((row / 2) % 8), so the
+// 16 rows an MFMA operand reads hit distinct banks.  Weights go from global
+// memory straight to registers (each weight row is used by one wave).  Three
+// chunks are in flight while one is multiplied (four LDS buffers, four weight
+// register sets); one workgroup per CU, the accumulators in AGPRs.
 //
 // Index maps per chunk c, lane (r, g):
 //   token operand: row r of the 16-row tile, chunk bytes 16 g .. +15 and
@@ -26,6 +27,8 @@
 //                   (elements 128 c + 32 g .. +31); scale byte 4 c + g of the row.
 // Token tiles whose 16 rows all lie past the segment skip their MFMAs.
 #pragma once
+
+#include <type_traits>
 
 #include "ft_internal.hpp"
 #include "gemm_prefill.hpp"
@@ -37,6 +40,7 @@ constexpr int kMxPitch = 128;                            // LDS bytes per token 
 constexpr int kMxCodeBytes = kGemmBM * kMxPitch;         // 16 KiB per buffer
 constexpr int kMxScaleBytes = 4 * 256;                   // per wave: 32 rows x 4 B + 128 B unused
 constexpr int kMxBufBytes = kMxCodeBytes + kMxScaleBytes;
+constexpr int kMxStages = 4;                             // LDS buffers (chunks in flight + 1)
 
 struct MxGemmArgs {
   GemmArgs g;          // shapes, weights, segments and outputs (g.X, g.ldx, g.x_bytes unused)
@@ -45,8 +49,9 @@ struct MxGemmArgs {
   uint32_t xq_bytes, xs_bytes;
 };
 
+
 template <bool GLU>
-__device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, uint8_t *lds) {
+__device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, LdsRing<kMxStages> L) {
   const GemmArgs &a = ma.g;
   constexpr int NT = 4;  // weight tiles (16 rows) per wave
   constexpr int MT = 8;  // token tiles (16 rows) per wave
@@ -58,8 +63,8 @@ __device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, uint8_t *lds)
   const int per = G / 8;
   const int logical = (b % 8) * per + b / 8;
   if (logical >= a.n_items) return;
-  const int n_m = a.n_items / a.n_ntiles;
-  const int nt_idx = logical / n_m, mi = logical % n_m;
+  int nt_idx, mi;
+  if (!gemm_item(a, logical, &nt_idx, &mi)) return;
   int e, row0, m;
   if (!gemm_find_mtile<kGemmThreads>(a, mi, &e, &row0, &m)) return;
   const bool shared = e == a.E;
@@ -136,24 +141,29 @@ __device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, uint8_t *lds)
     u32x4 w[NT];
     uint32_t s[NT];
   };
+  const int nch = a.K / kMxBK;
+  // A chunk past the end is still issued, with out-of-range offsets (no memory
+  // traffic, zeros): every step then has the same loads in flight, and the
+  // vmcnt arithmetic below holds on every path.
   auto load_b = [&](int c, BFrag &f) {
+    const bool live = c < nch;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      f.w[t] = bld16(wres[t], wrow[t] * wpitch + uint32_t(c) * 64u + q * 16);
-      f.s[t] = bld4(sres[t], wrow[t] * spitch + uint32_t(c) * 4u);
+      f.w[t] = bld16(wres[t], live ? wrow[t] * wpitch + uint32_t(c) * 64u + q * 16 : kOOB);
+      f.s[t] = bld4(sres[t], live ? wrow[t] * spitch + uint32_t(c) * 4u : kOOB);
     }
   };
-  auto load_a = [&](int c, int buf) {
-    uint8_t *base = lds + buf * kMxBufBytes;
+  auto load_a = [&](int c, uint8_t *base) {
+    const bool live = c < nch;
     uint8_t *cb = base + wave * 32 * kMxPitch;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           qres, (__attribute__((address_space(3))) void *)(cb + t * 8 * kMxPitch), 16,
-          qsrc[t] == kOOB ? kOOB : qsrc[t] + uint32_t(c) * 128u, 0, 0, 0);
+          (qsrc[t] == kOOB || !live) ? kOOB : qsrc[t] + uint32_t(c) * 128u, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         sres_x, (__attribute__((address_space(3))) void *)(base + kMxCodeBytes + wave * 256), 4,
-        ssrc == kOOB ? kOOB : ssrc + uint32_t(c) * 4u, 0, 0, 0);
+        (ssrc == kOOB || !live) ? kOOB : ssrc + uint32_t(c) * 4u, 0, 0, 0);
   };
 
   f32x4 acc[MT][NT];
@@ -162,50 +172,60 @@ __device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, uint8_t *lds)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nch = a.K / kMxBK;
   // this lane's LDS read addresses in buffer 0, tile 0: the two 16-byte pieces
   // of its row and the row's scale dword; tile i adds i * 16 rows
   const int sw = (r >> 1) & 7;
-  const uint8_t *pa_lo = lds + r * kMxPitch + ((q ^ sw) << 4);
-  const uint8_t *pa_hi = lds + r * kMxPitch + (((4 + q) ^ sw) << 4);
-  const uint8_t *pa_s = lds + kMxCodeBytes + r * 4;
-  BFrag f;
-  load_a(0, 0);
-  load_b(0, f);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int boff = (c & 1) * kMxBufBytes;
-    BFrag fn;
-    if (c + 1 < nch) {
-      load_a(c + 1, (c & 1) ^ 1);
-      load_b(c + 1, fn);
-    }
-    i32x8 bw[NT];
-    int bs[NT];
+  const int oa_lo = r * kMxPitch + ((q ^ sw) << 4);
+  const int oa_hi = r * kMxPitch + (((4 + q) ^ sw) << 4);
+  const int oa_s = kMxCodeBytes + r * 4;
+  // ---- pipeline: P chunks in flight ahead of the one being multiplied, in
+  // P + 1 LDS buffers and P + 1 weight register sets (a ring, unrolled so the
+  // register set of every step is fixed at compile time)
+  constexpr int NBUF = kMxStages;
+  constexpr int P = NBUF - 1;
+  constexpr int LOADS = 4 + 1 + 2 * NT;  // vector-memory instructions per chunk and wave
+  BFrag fr[NBUF];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      // FP4 operands use the low four dwords only
-      bw[t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(f.w[t], f.w[t], 0, 1, 2, 3, -1, -1, -1, -1));
-      bs[t] = int(f.s[t] >> (8 * q));
-    }
-    const uint8_t *plo = pa_lo + boff, *phi = pa_hi + boff, *ps = pa_s + boff;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const u32x4 lo = *reinterpret_cast<const u32x4 *>(plo + i * 16 * kMxPitch);
-      const u32x4 hi = *reinterpret_cast<const u32x4 *>(phi + i * 16 * kMxPitch);
-      // scales: wave area (row / 32) * 256, row (row % 32) * 4
-      const int as = int(*reinterpret_cast<const uint32_t *>(ps + (i >> 1) * 256 + (i & 1) * 64) >> (8 * q));
-      const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[i][t] = mfma_mx(av, bw[t], acc[i][t], as, bs[t]);
-    }
-    if (c + 1 < nch) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      f = fn;
-    }
+  for (int p = 0; p < P; ++p) {
+    load_a(p, L.b[p]);
+    load_b(p, fr[p]);
   }
+  wait_vmcnt<(P - 1) * LOADS>();  // chunk 0 has landed
+  lds_barrier();
+
+  auto body = [&](auto jc, int c) {
+    constexpr int J = decltype(jc)::value;
+    load_a(c + P, L.b[(J + P) % NBUF]);  // the buffer and registers the previous chunk used
+    load_b(c + P, fr[(J + P) % NBUF]);
+    if (c < nch) {
+      const BFrag &f = fr[J];
+      i32x8 bw[NT];
+      int bs[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        // FP4 operands use the low four dwords only
+        bw[t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(f.w[t], f.w[t], 0, 1, 2, 3, -1, -1, -1, -1));
+        bs[t] = int(f.s[t] >> (8 * q));
+      }
+      const uint8_t *buf = L.b[J];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(buf + oa_lo + i * 16 * kMxPitch);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(buf + oa_hi + i * 16 * kMxPitch);
+        // scales: wave area (row / 32) * 256, row (row % 32) * 4
+        const int as = int(*reinterpret_cast<const uint32_t *>(buf + oa_s + (i >> 1) * 256 + (i & 1) * 64) >> (8 * q));
+        const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[i][t] = mfma_mx(av, bw[t], acc[i][t], as, bs[t]);
+      }
+    }
+    wait_vmcnt<(P - 1) * LOADS>();  // chunk c + 1 has landed; c + 2 .. c + P may still fly
+    lds_barrier();
+  };
+  static_assert((P - 1) * LOADS < 64, "vmcnt is six bits");
+  for (int c = 0; c < nch; c += NBUF)
+    unroll_ring([&](auto jc) { body(jc, c + decltype(jc)::value); }, std::make_integer_sequence<int, NBUF>{});
+  wait_vmcnt<0>();
 
   // ---- epilogue: lane holds D[token 4q+v][weight row r] of each tile
 #pragma unroll

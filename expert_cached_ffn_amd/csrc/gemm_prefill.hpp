@@ -32,6 +32,9 @@
 // its L2.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "ft_internal.hpp"
 
 namespace ft {
@@ -59,8 +62,21 @@ struct GemmArgs {
   int64_t ldo;
   float *out_shared;              // stage 2: shared-expert rows by token
   int n_ntiles;                   // weight tiles
-  int n_items;                    // grid size (upper bound of items)
+  int n_mtiles;                   // token tiles (upper bound over the segments)
+  int n_items;                    // work items
 };
+
+// Work items are weight-tile major: consecutive items are the token tiles of
+// one weight tile, so the workgroups an XCD runs at once share that weight
+// tile through its L2 and the weights stream from HBM about once.  (Blocks of
+// 8 token x 4 weight tiles were measured slower: the weights of the large
+// experts are then re-read, and the tokens come from the MALL anyway.)
+__host__ __device__ inline int gemm_item_count(int n_mtiles, int n_ntiles) { return n_mtiles * n_ntiles; }
+__device__ inline bool gemm_item(const GemmArgs &a, int logical, int *nt, int *mi) {
+  *nt = logical / a.n_mtiles;
+  *mi = logical % a.n_mtiles;
+  return *nt < a.n_ntiles;
+}
 
 // Block-wide: map token-tile index mi (counted over the experts' segments in
 // ascending expert order, then the shared expert) to its expert and first row.
@@ -121,8 +137,21 @@ __device__ bool gemm_find_mtile(const GemmArgs &a, int mi, int *e_out, int *row0
   return true;
 }
 
-template <int WF, bool GLU>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &a, uint8_t *lds) {
+// LDS buffers of a pipelined GEMM: one distinct array per stage, so that the
+// compiler can tell a direct load into one buffer from reads of another.
+template <int N>
+struct LdsRing {
+  uint8_t *b[N];
+};
+
+// Calls f(std::integral_constant<int, J>) for J = 0 .. N-1.
+template <typename F, int... J>
+__device__ __forceinline__ void unroll_ring(F &&f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+
+template <int WF, bool GLU, int NBUF>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
   constexpr int NT = 4;   // weight tiles (16 rows) per wave
   constexpr int MT = 8;   // token tiles (16 rows) per wave
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -134,8 +163,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, uint8_t *lds) {
   const int per = G / 8;
   const int logical = (b % 8) * per + b / 8;
   if (logical >= a.n_items) return;
-  const int n_m = a.n_items / a.n_ntiles;  // token tiles (upper bound) per weight tile
-  const int nt_idx = logical / n_m, mi = logical % n_m;
+  int nt_idx, mi;
+  if (!gemm_item(a, logical, &nt_idx, &mi)) return;
   int e, row0, m;
   if (!gemm_find_mtile<kGemmThreads>(a, mi, &e, &row0, &m)) return;
   const bool shared = e == a.E;
@@ -205,25 +234,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, uint8_t *lds) {
     u32x4 w[NT][DLW];
     uint32_t s[NT];
   };
+  const int nch = a.K / kGemmBK;
+  // A chunk past the end is still issued, with out-of-range offsets (no memory
+  // traffic, zeros): every step then has the same loads in flight, and the
+  // vmcnt arithmetic below holds on every path.
   auto load_b = [&](int c, BFrag &f) {
+    const bool live = c < nch;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if constexpr (WF == WF_BF16) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) f.w[t][d] = bld16(wres[t], wrow[t] * wpitch + uint32_t(c) * 256u + d * 64 + q * 16);
+        for (int d = 0; d < 4; ++d)
+          f.w[t][d] = bld16(wres[t], live ? wrow[t] * wpitch + uint32_t(c) * 256u + d * 64 + q * 16 : kOOB);
       } else {
-        f.w[t][0] = bld16(wres[t], wrow[t] * wpitch + uint32_t(c) * 64u + q * 16);
-        f.s[t] = bld4(sres[t], wrow[t] * spitch + uint32_t(c) * 4u);
+        f.w[t][0] = bld16(wres[t], live ? wrow[t] * wpitch + uint32_t(c) * 64u + q * 16 : kOOB);
+        f.s[t] = bld4(sres[t], live ? wrow[t] * spitch + uint32_t(c) * 4u : kOOB);
       }
     }
   };
-  auto load_a = [&](int c, int buf) {
-    uint8_t *base = lds + buf * (kGemmBM * kGemmPitch) + wave * 32 * kGemmPitch;
+  auto load_a = [&](int c, uint8_t *buf) {
+    const bool live = c < nch;
+    uint8_t *base = buf + wave * 32 * kGemmPitch;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void *)(base + t * 4 * kGemmPitch), 16,
-          xsrc[t] == kOOB ? kOOB : xsrc[t] + uint32_t(c) * 256u, 0, 0, 0);
+          (xsrc[t] == kOOB || !live) ? kOOB : xsrc[t] + uint32_t(c) * 256u, 0, 0, 0);
   };
 
   f32x4 acc[MT][NT];
@@ -232,46 +268,57 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, uint8_t *lds) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nch = a.K / kGemmBK;
-  // One chunk: the next chunk goes in flight (tokens straight to the other LDS
-  // buffer -- last read in the previous chunk, before the barrier that ended
-  // it -- and weights to the other register set), then this chunk is multiplied.
-  auto chunk = [&](int c, int buf, const BFrag &f, BFrag &fn) {
-    if (c + 1 < nch) {
-      load_a(c + 1, buf ^ 1);
-      load_b(c + 1, fn);
-    }
-    const uint8_t *abuf = lds + buf * (kGemmBM * kGemmPitch);
+  // ---- pipeline: P = NBUF - 1 chunks in flight ahead of the one being
+  // multiplied, in NBUF LDS buffers and NBUF weight register sets (a ring,
+  // unrolled so the register set of every step is fixed at compile time).
+  // Step c issues chunk c + P into the buffer and registers step c - 1 used
+  // (every wave passed the barrier that ended step c - 1), multiplies chunk c,
+  // then waits until chunk c + 1 has landed and meets the other waves.
+  constexpr int P = NBUF - 1;
+  constexpr int LOADS = 8 + NT * (WF == WF_BF16 ? 4 : 2);  // vector-memory instructions per chunk and wave
+  static_assert((P - 1) * LOADS < 64, "vmcnt is six bits");
+  BFrag fr[NBUF];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 bw[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if constexpr (WF == WF_BF16) bw[t] = as_bf16x8(f.w[t][ks]);
-        else bw[t] = fp4x8_to_bf16x8(f.w[t][0][ks], e8m0_to_f32((f.s[t] >> (8 * q)) & 0xffu));
-      }
-      const int j = WF == WF_BF16 ? 4 * ks + q : 4 * q + ks;  // 16-byte chunk of the row
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const u32x4 af = *reinterpret_cast<const u32x4 *>(abuf + (i * 16 + r) * kGemmPitch + ((j ^ r) << 4));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[i][t] = mfma16(as_bf16x8(af), bw[t], acc[i][t]);
-      }
-    }
-    if (c + 1 < nch) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-      __syncthreads();                // and everyone's
-    }
-  };
-  BFrag f0, f1;
-  load_a(0, 0);
-  load_b(0, f0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    chunk(c, 0, f0, f1);
-    if (c + 1 < nch) chunk(c + 1, 1, f1, f0);
+  for (int p = 0; p < P; ++p) {
+    load_a(p, L.b[p]);
+    load_b(p, fr[p]);
   }
+  wait_vmcnt<(P - 1) * LOADS>();  // chunk 0 has landed
+  lds_barrier();
+  auto step = [&](auto jc, int c) {
+    constexpr int J = decltype(jc)::value;
+    // with one chunk in flight every wait is a full one, so the past-the-end
+    // chunk need not be issued
+    if (P > 1 || c + P < nch) {
+      load_a(c + P, L.b[(J + P) % NBUF]);
+      load_b(c + P, fr[(J + P) % NBUF]);
+    }
+    if (c < nch) {
+      const BFrag &f = fr[J];
+      const uint8_t *abuf = L.b[J];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 bw[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (WF == WF_BF16) bw[t] = as_bf16x8(f.w[t][ks]);
+          else bw[t] = fp4x8_to_bf16x8(f.w[t][0][ks], e8m0_to_f32((f.s[t] >> (8 * q)) & 0xffu));
+        }
+        const int j = WF == WF_BF16 ? 4 * ks + q : 4 * q + ks;  // 16-byte chunk of the row
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const u32x4 af = *reinterpret_cast<const u32x4 *>(abuf + (i * 16 + r) * kGemmPitch + ((j ^ r) << 4));
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[i][t] = mfma16(as_bf16x8(af), bw[t], acc[i][t]);
+        }
+      }
+    }
+    wait_vmcnt<(P - 1) * LOADS>();  // chunk c + 1 has landed; c + 2 .. c + P may still fly
+    lds_barrier();
+  };
+  for (int c = 0; c < nch; c += NBUF)
+    unroll_ring([&](auto jc) { step(jc, c + decltype(jc)::value); }, std::make_integer_sequence<int, NBUF>{});
+  wait_vmcnt<0>();
 
   // ---- epilogue: lane holds D[token 4q+v][weight row r] of each tile
 #pragma unroll
