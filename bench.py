@@ -146,8 +146,7 @@ def run_decode(args, cfg, batches, main_T):
 
         def step(i, tm=None):
             x = xs[i % N_INPUT_SETS]
-            layer.route(T, x=x, w_router=wr)
-            layer.permute(T)
+            layer.route_permute(T, x=x, w_router=wr)
             if tm is not None:
                 tm.mark()
             layer.ffn(T, x, pool, shared_blob=shared, mode=_lib.FT_FFN_GATE_UP_ONLY)
@@ -342,9 +341,8 @@ def run_cache_trace(args, cfg):
         for st in range(steps):
             for l in range(Lyr):
                 i = st * Lyr + l
-                layer.route(1, logits=logits[i:i + 1])
+                layer.route_permute(1, logits=logits[i:i + 1])
                 cache.step(l, layer.ids, 1, cfg.k, slot_of)
-                layer.permute(1)
                 layer.ffn(1, xs[i], pool, slot_of_expert=slot_of, shared_blob=shared[l])
                 layer.combine(1)
 

@@ -13,7 +13,7 @@ STATUS_NAMES = {0: "FT_OK", -1: "FT_EINVAL", -2: "FT_ENOTSUP", -3: "FT_ECAPACITY
 # dtypes / gating / workspace selectors
 FT_F32, FT_BF16, FT_MXFP4 = 0, 1, 2
 FT_SOFTMAX, FT_SIGMOID = 0, 1
-FT_WS_PERMUTE, FT_WS_FFN = 1, 2
+FT_WS_PERMUTE, FT_WS_FFN, FT_WS_ROUTE_PERMUTE = 1, 2, 3
 FT_FFN_EXACT, FT_FFN_NATIVE_MX = 0, 1
 FT_FFN_GATE_UP_ONLY, FT_FFN_DOWN_ONLY = 0x100, 0x200
 
@@ -21,7 +21,7 @@ EXPORTS = [
     "ft_last_error", "ft_version", "ft_expert_layout_init", "ft_moe_route", "ft_moe_permute",
     "ft_moe_grouped_ffn", "ft_moe_combine", "ft_expert_cache_create", "ft_expert_cache_step",
     "ft_expert_cache_stats", "ft_expert_cache_trace", "ft_expert_cache_lookup",
-    "ft_expert_cache_destroy", "ft_workspace_bytes", "ft_mxfp8_quantize",
+    "ft_expert_cache_destroy", "ft_workspace_bytes", "ft_mxfp8_quantize", "ft_moe_route_permute",
 ]
 
 
@@ -72,6 +72,8 @@ def lib() -> C.CDLL:
     L.ft_moe_grouped_ffn.restype = i32
     L.ft_moe_grouped_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, p, p, i32, i32, i32, i32, p, p, p, p,
                                      i32, p, sz, p]
+    L.ft_moe_route_permute.restype = i32
+    L.ft_moe_route_permute.argtypes = [p, i32, p, p, i32, i32, i32, i32, i32, i32, p, p, p, p, p, p, sz, p]
     L.ft_mxfp8_quantize.restype = i32
     L.ft_mxfp8_quantize.argtypes = [p, C.c_int64, i32, i32, p, p, p]
     L.ft_moe_combine.restype = i32

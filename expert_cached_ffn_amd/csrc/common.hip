@@ -73,6 +73,8 @@ extern "C" size_t ft_workspace_bytes(int32_t which, int32_t T, int32_t k, int32_
       return ft::permute_workspace_bytes(T, k, E);
     case FT_WS_FFN:
       return ft::ffn_workspace_bytes(T, k, E, H, I);
+    case FT_WS_ROUTE_PERMUTE:
+      return ft::permute_workspace_bytes(T, k, E);
     default:
       return 0;
   }

@@ -11,6 +11,8 @@
 //   stage 2  y = h Wd^T                    -> fp32 y_rows / y_shared
 // bf16 / MXFP4 weights use the weight-streaming MFMA tile (stream_gemm.hpp);
 // fp32 weights use a plain FMA kernel.
+#include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <unordered_map>
 
@@ -233,6 +235,11 @@ static int resident_grid(const void *kernel, int threads) {
 static void persist_shape(int nkb, int *waves, int *kpw) {
   *waves = 0;
   *kpw = 0;
+  if (nkb == 16) {  // 8 waves x 2 k-blocks: two workgroups per CU, measured faster than 16 x 1
+    *waves = 8;
+    *kpw = 2;
+    return;
+  }
   for (int c : {1, 2})
     for (int w : {16, 12, 8, 6, 4})
       if (w * c == nkb && (c == 1 || w <= 8)) {  // wider 2-block shapes exceed the register budget
@@ -242,10 +249,22 @@ static void persist_shape(int nkb, int *waves, int *kpw) {
       }
 }
 
+// Shape override for tuning: FTMOE_PERSIST_GU / FTMOE_PERSIST_DN = "waves,kpw"
+// (used only when waves * kpw equals the stage's k-block count).
+static void persist_override(bool glu, int nkb, int *waves, int *kpw) {
+  const char *v = getenv(glu ? "FTMOE_PERSIST_GU" : "FTMOE_PERSIST_DN");
+  int w = 0, c = 0;
+  if (v && sscanf(v, "%d,%d", &w, &c) == 2 && w * c == nkb) {
+    *waves = w;
+    *kpw = c;
+  }
+}
+
 template <int WF, bool GLU>
 static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stream) {
   int waves, kpw;
   persist_shape(a.K / stream_kblock<WF>(), &waves, &kpw);
+  persist_override(GLU, a.K / stream_kblock<WF>(), &waves, &kpw);
 #define FT_PERSIST(W, C)                                                                    \
   if (waves == W && kpw == C) {                                                             \
     const void *kern = reinterpret_cast<const void *>(&ffn_persist_kernel<WF, GLU, W, C>); \

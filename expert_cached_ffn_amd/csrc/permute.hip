@@ -12,6 +12,7 @@
 // Large inputs: count per 1024-row block -> one-workgroup scan over blocks ->
 // per-block scatter from the block's own bases.
 #include "ft_internal.hpp"
+#include "permute_util.hpp"
 
 namespace ft {
 
@@ -26,80 +27,6 @@ size_t permute_workspace_bytes(int32_t T, int32_t k, int32_t E) {
   return size_t(((B * E * 4) + 255) / 256 * 256);
 }
 
-__device__ __forceinline__ int bits_for(int E) {
-  int b = 1;
-  while ((1 << b) < E) ++b;
-  return b;
-}
-
-// Stable scatter of rows [r0, r1) by one wave.  s_base[e] holds the next
-// free position of expert e and is advanced as rows are placed.
-__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, int r0, int r1, int E,
-                                             int *s_base, int32_t *__restrict__ sorted_rows,
-                                             int32_t *__restrict__ row_pos) {
-  const int lane = threadIdx.x & 63;
-  const int nb = bits_for(E);
-  const uint64_t lt = (uint64_t(1) << lane) - 1;
-  for (int c = r0; c < r1; c += 64) {
-    const int r = c + lane;
-    const bool act = r < r1;
-    int key = act ? ids[r] : 0;
-    const bool ok = act && key >= 0 && key < E;
-    const uint64_t active = __ballot(ok);
-    uint64_t same = active;
-    for (int b = 0; b < nb; ++b) {
-      const uint64_t ones = __ballot((key >> b) & 1);
-      same &= ((key >> b) & 1) ? ones : ~ones;
-    }
-    if (ok) {
-      const int rank = __popcll(same & lt);
-      const int pos = s_base[key] + rank;
-      sorted_rows[pos] = r;
-      row_pos[r] = pos;
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (ok && (same >> lane) == 1) s_base[key] += __popcll(same);  // last lane of its key
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-// Block-wide exclusive scan of s[0..n) in place (n <= 4096); returns the total.
-__device__ int block_exclusive_scan(int *s, int n, int *s_tmp /* >= 32 ints */) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = (n + nt - 1) / nt;
-  const int a = min(n, tid * per), b = min(n, a + per);
-  int local = 0;
-  for (int i = a; i < b; ++i) local += s[i];
-  // inclusive scan of `local` across the block
-  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
-  int v = local;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63) s_tmp[wave] = v;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int t = s_tmp[w];
-      s_tmp[w] = run;
-      run += t;
-    }
-    s_tmp[nw] = run;
-  }
-  __syncthreads();
-  int excl = s_tmp[wave] + v - local;
-  for (int i = a; i < b; ++i) {
-    const int t = s[i];
-    s[i] = excl;
-    excl += t;
-  }
-  const int total = s_tmp[nw];
-  __syncthreads();
-  return total;
-}
-
 // One workgroup (256 threads) does everything.
 __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *__restrict__ ids, int R, int E,
                                                             int32_t *__restrict__ offsets,
@@ -107,19 +34,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *__res
                                                             int32_t *__restrict__ row_pos) {
   __shared__ int s_cnt[kPermMaxE];
   __shared__ int s_tmp[32];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
-  __syncthreads();
-  for (int r = tid; r < R; r += 256) {
-    const int key = ids[r];
-    if (key >= 0 && key < E) atomicAdd(&s_cnt[key], 1);
-  }
-  __syncthreads();
-  const int total = block_exclusive_scan(s_cnt, E, s_tmp);
-  for (int e = tid; e < E; e += 256) offsets[e] = s_cnt[e];
-  if (tid == 0) offsets[E] = total;
-  __syncthreads();
-  if (tid < 64) wave_scatter(ids, 0, R, E, s_cnt, sorted_rows, row_pos);
+  permute_block(ids, R, E, s_cnt, s_tmp, offsets, sorted_rows, row_pos);
 }
 
 // Multi-block pass 1: per-block histogram -> counts[b][e].

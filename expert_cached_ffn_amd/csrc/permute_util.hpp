@@ -1,0 +1,105 @@
+// Block-level pieces of the stable counting sort of routed rows by expert,
+// shared by ft_moe_permute and the fused decode routing call.
+#pragma once
+
+#include "ft_internal.hpp"
+
+namespace ft {
+
+__device__ __forceinline__ int bits_for(int E) {
+  int b = 1;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+// Stable scatter of rows [r0, r1) by one wave.  s_base[e] holds the next
+// free position of expert e and is advanced as rows are placed.
+__device__ __forceinline__ void wave_scatter(const int32_t *__restrict__ ids, int r0, int r1, int E,
+                                             int *s_base, int32_t *__restrict__ sorted_rows,
+                                             int32_t *__restrict__ row_pos) {
+  const int lane = threadIdx.x & 63;
+  const int nb = bits_for(E);
+  const uint64_t lt = (uint64_t(1) << lane) - 1;
+  for (int c = r0; c < r1; c += 64) {
+    const int r = c + lane;
+    const bool act = r < r1;
+    int key = act ? ids[r] : 0;
+    const bool ok = act && key >= 0 && key < E;
+    const uint64_t active = __ballot(ok);
+    uint64_t same = active;
+    for (int b = 0; b < nb; ++b) {
+      const uint64_t ones = __ballot((key >> b) & 1);
+      same &= ((key >> b) & 1) ? ones : ~ones;
+    }
+    if (ok) {
+      const int rank = __popcll(same & lt);
+      const int pos = s_base[key] + rank;
+      sorted_rows[pos] = r;
+      row_pos[r] = pos;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ok && (same >> lane) == 1) s_base[key] += __popcll(same);  // last lane of its key
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Block-wide exclusive scan of s[0..n) in place (n <= 4096); returns the total.
+__device__ inline int block_exclusive_scan(int *s, int n, int *s_tmp /* >= 32 ints */) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int a = min(n, tid * per), b = min(n, a + per);
+  int local = 0;
+  for (int i = a; i < b; ++i) local += s[i];
+  // inclusive scan of `local` across the block
+  const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  int v = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = s_tmp[w];
+      s_tmp[w] = run;
+      run += t;
+    }
+    s_tmp[nw] = run;
+  }
+  __syncthreads();
+  int excl = s_tmp[wave] + v - local;
+  for (int i = a; i < b; ++i) {
+    const int t = s[i];
+    s[i] = excl;
+    excl += t;
+  }
+  const int total = s_tmp[nw];
+  __syncthreads();
+  return total;
+}
+
+// The whole permutation of R routed rows by one workgroup: LDS histogram,
+// exclusive scan, then one wave scatters 64 rows at a time, ranking equal keys
+// with per-bit ballots (so rows stay ascending inside a segment).  s_cnt holds
+// E ints; ids may be global or LDS.
+__device__ inline void permute_block(const int32_t *ids, int R, int E, int *s_cnt, int *s_tmp,
+                                     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
+                                     int32_t *__restrict__ row_pos) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int e = tid; e < E; e += nt) s_cnt[e] = 0;
+  __syncthreads();
+  for (int r = tid; r < R; r += nt) {
+    const int key = ids[r];
+    if (key >= 0 && key < E) atomicAdd(&s_cnt[key], 1);
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_cnt, E, s_tmp);
+  for (int e = tid; e < E; e += nt) offsets[e] = s_cnt[e];
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  if (tid < 64) wave_scatter(ids, 0, R, E, s_cnt, sorted_rows, row_pos);
+}
+
+}  // namespace ft

@@ -9,6 +9,7 @@
 #include <math.h>
 
 #include "ft_internal.hpp"
+#include "permute_util.hpp"
 #include "stream_gemm.hpp"
 
 namespace ft {
@@ -62,48 +63,57 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per token.  The token's logits go to LDS; every lane ranks its own
-// logits against all E (rank = number of logits that come before it in the
-// order (-logit, index)), so pick j is the logit of rank j -- no serial
-// arg-max rounds.  Then the gating weights of the picked experts.
+// One wave per token.  Lane l holds the token's logits l, l+64, ... as 64-bit
+// keys: the logit mapped to an unsigned integer of the same order (-0.0 taken
+// as +0.0) in the high half, the complement of the expert index in the low
+// half, so that the largest key is the largest logit and, among equal logits,
+// the lowest index; all keys differ.  Pick j is found by one wave-wide max
+// (a lane-local max, then six butterfly steps) and its owner then drops it:
+// k rounds.  Then the gating weights of the picked experts.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  if (x == 0.0f) x = 0.0f;  // -0.0 and +0.0 are the same key
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-k and gating of token t by one wave (all 64 lanes call it).  ids / w
+// receive the picks at [t * k + j]; ids_lds (nullable) gets the same ids.
 template <int VPL>
-__global__ __launch_bounds__(64 * kTopkWaves) void topk_gating_kernel(const float *__restrict__ logits,
-                                                                       int T, int E, int k, int gating,
-                                                                       int renorm, int32_t *__restrict__ ids,
-                                                                       float *__restrict__ w) {
-  __shared__ float s_l[kTopkWaves][kMaxE];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kTopkWaves + wave;
-  const bool active = t < T;
-  const float *lr = logits + int64_t(active ? t : 0) * E;
+__device__ __forceinline__ void topk_token(const float *__restrict__ logits, int t, int E, int k, int gating,
+                                           int renorm, int32_t *__restrict__ ids, float *__restrict__ w,
+                                           int32_t *ids_lds) {
+  const int lane = threadIdx.x & 63;
+  const float *lr = logits + int64_t(t) * E;
   float v[VPL];
+  uint64_t key[VPL];
+  static_assert(kMaxK % 64 == 0, "picks are held 64 per slot");
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    float x = (active && e < E) ? lr[e] : -INFINITY;
-    if (x == 0.0f) x = 0.0f;  // -0.0 and +0.0 are the same key
-    v[i] = x;
-    if (e < E) s_l[wave][e] = x;
+    v[i] = e < E ? lr[e] : -INFINITY;
+    key[i] = e < E ? (uint64_t(order_key(v[i])) << 32) | uint32_t(~e) : 0;  // 0: below every real key
   }
-  __syncthreads();
-  if (!active) return;
-  int rank[VPL];
+  // k rounds of wave arg-max; pick j ends up in lane j % 64, slot j / 64
+  constexpr int KS = kMaxK / 64;
+  int pid[KS];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) rank[i] = 0;
-  const int E4 = E & ~3;
-  for (int e = 0; e < E4; e += 4) {
-    const f32x4 o = *reinterpret_cast<const f32x4 *>(&s_l[wave][e]);
+  for (int s2 = 0; s2 < KS; ++s2) pid[s2] = -1;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int me = lane + 64 * i;
+    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) rank[i] += int(o[c] > v[i]) + (int(o[c] == v[i]) & int(e + c < me));
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t o = __shfl_xor(best, off);
+      best = o > best ? o : best;
     }
-  }
-  for (int e = E4; e < E; ++e) {
-    const float o = s_l[wave][e];
+    const int e = int(~uint32_t(best));
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) rank[i] += int(o > v[i]) + (int(o == v[i]) & int(e < lane + 64 * i));
+    for (int i = 0; i < VPL; ++i)
+      if (key[i] == best) key[i] = 0;  // the owner drops its pick
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2)
+      if ((j >> 6) == s2 && lane == (j & 63)) pid[s2] = e;
   }
   // Gating.  softmax: p_e = exp(l_e - max) / sum_E exp(l - max); sigmoid: 1/(1+exp(-l)).
   float mx = v[0];
@@ -119,34 +129,83 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_gating_kernel(const floa
       if (lane + 64 * i < E) s += expf(v[i] - mx);
     denom = wave_sum(s);
   }
-  float p[VPL];
+  float p[KS];
   float local = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    p[i] = 0.f;
-    if (lane + 64 * i < E && rank[i] < k) {
-      p[i] = gating == FT_SOFTMAX ? expf(v[i] - mx) / denom : 1.0f / (1.0f + expf(-v[i]));
-      local += p[i];
+  for (int s2 = 0; s2 < KS; ++s2) {
+    p[s2] = 0.f;
+    if (pid[s2] >= 0) {
+      float x = lr[pid[s2]];
+      if (x == 0.0f) x = 0.0f;
+      p[s2] = gating == FT_SOFTMAX ? expf(x - mx) / denom : 1.0f / (1.0f + expf(-x));
+      local += p[s2];
     }
   }
   const float wsum = renorm ? wave_sum(local) : 1.0f;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (lane + 64 * i < E && rank[i] < k) {
-      ids[int64_t(t) * k + rank[i]] = lane + 64 * i;
-      w[int64_t(t) * k + rank[i]] = renorm ? p[i] / wsum : p[i];
+  for (int s2 = 0; s2 < KS; ++s2) {
+    if (pid[s2] >= 0) {
+      const int jj = lane + 64 * s2;
+      ids[int64_t(t) * k + jj] = pid[s2];
+      w[int64_t(t) * k + jj] = renorm ? p[s2] / wsum : p[s2];
+      if (ids_lds) ids_lds[t * k + jj] = pid[s2];
     }
   }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_gating_kernel(const float *__restrict__ logits,
+                                                                       int T, int E, int k, int gating,
+                                                                       int renorm, int32_t *__restrict__ ids,
+                                                                       float *__restrict__ w) {
+  const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
+  if (t < T) topk_token<VPL>(logits, t, E, k, gating, renorm, ids, w, nullptr);
+}
+
+// ------------------------------------------------------------------ fused decode routing
+
+constexpr int kFusedMaxT = 16;      // tokens of the fused path (one per wave; more is slower than two launches)
+constexpr int kFusedMaxRows = 2048; // routed rows (T * k) of the fused path
+
+struct FusedRouteArgs {
+  const float *logits;       // [T, E]
+  int T, E, k, gating, renorm;
+  int32_t *ids;
+  float *w;
+  int32_t *offsets, *sorted_rows, *row_pos;
+};
+
+// Top-k, gating and the permutation of all T tokens by one workgroup.
+template <int VPL>
+__device__ __forceinline__ void route_tail(const FusedRouteArgs &a, int32_t *s_ids, int *s_cnt, int *s_tmp) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int t = wave; t < a.T; t += nw) topk_token<VPL>(a.logits, t, a.E, a.k, a.gating, a.renorm, a.ids, a.w, s_ids);
+  __syncthreads();
+  permute_block(s_ids, a.T * a.k, a.E, s_cnt, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
+}
+
+// Top-k, gating and permutation of all T tokens in one workgroup (small decode
+// batches, T <= 16): one launch after the router instead of two.  (A single
+// launch with the router, its last workgroup doing this, was measured
+// slower: the device-scope fences that publish the logits write back and
+// invalidate the L2 of every XCD.)
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_tail_kernel(FusedRouteArgs a) {
+  __shared__ int32_t s_ids[kFusedMaxRows];
+  __shared__ int s_cnt[kMaxE];
+  __shared__ int s_tmp[32];
+  route_tail<VPL>(a, s_ids, s_cnt, s_tmp);
 }
 
 }  // namespace ft
 
 using namespace ft;
 
-extern "C" ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_router, float *logits,
-                                  int32_t T, int32_t H, int32_t E, int32_t k, int32_t gating,
-                                  int32_t renormalize, int32_t *topk_ids, float *topk_w,
-                                  hipStream_t stream) {
+// Checks the arguments of a routing call and launches the router logits
+// kernel when there is a router (FT_OK with nothing launched when T == 0).
+static ft_status route_logits(const void *x, int32_t x_dtype, const void *w_router, float *logits, int32_t T,
+                              int32_t H, int32_t E, int32_t k, int32_t gating, int32_t *topk_ids, float *topk_w,
+                              hipStream_t stream) {
   FT_REQUIRE(T >= 0 && E >= 1 && k >= 1, "ft_moe_route: need T >= 0, E >= 1, k >= 1");
   FT_SUPPORTED(k <= E, "ft_moe_route: k > E");
   FT_SUPPORTED(E <= kMaxE, "ft_moe_route: E > 1024");
@@ -199,6 +258,19 @@ extern "C" ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_
       FT_LAUNCHED("router_logits_f32");
     }
   }
+  return FT_OK;
+}
+
+extern "C" ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_router, float *logits,
+                                  int32_t T, int32_t H, int32_t E, int32_t k, int32_t gating,
+                                  int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                                  hipStream_t stream) {
+  const ft_status st = route_logits(x, x_dtype, w_router, logits, T, H, E, k, gating, topk_ids, topk_w, stream);
+  if (st != FT_OK) return st;
+  if (T == 0) {
+    clear_error();
+    return FT_OK;
+  }
   const dim3 grid(unsigned(cdiv(T, kTopkWaves))), blk(64 * kTopkWaves);
   const int vpl = cdiv(E, 64);
 #define FT_TOPK(V)                                                                                     \
@@ -211,6 +283,48 @@ extern "C" ft_status ft_moe_route(const void *x, int32_t x_dtype, const void *w_
   else FT_TOPK(16);
 #undef FT_TOPK
   FT_LAUNCHED("topk_gating_kernel");
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_moe_route_permute(const void *x, int32_t x_dtype, const void *w_router, float *logits,
+                                          int32_t T, int32_t H, int32_t E, int32_t k, int32_t gating,
+                                          int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                                          int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const bool fused = T >= 1 && T <= kFusedMaxT && int64_t(T) * k <= kFusedMaxRows && k >= 1 && k <= E &&
+                     E <= kMaxE && (gating == FT_SOFTMAX || gating == FT_SIGMOID);
+  if (!fused) {
+    // the two calls, one after the other (they validate their own arguments)
+    const ft_status st = ft_moe_route(x, x_dtype, w_router, logits, T, H, E, k, gating, renormalize, topk_ids,
+                                      topk_w, stream);
+    if (st != FT_OK) return st;
+    return ft_moe_permute(topk_ids, T, k, E, expert_offsets, sorted_rows, row_pos, workspace, workspace_bytes,
+                          stream);
+  }
+  FT_REQUIRE(expert_offsets && sorted_rows && row_pos && aligned(expert_offsets, 4) && aligned(sorted_rows, 4) &&
+                 aligned(row_pos, 4),
+             "ft_moe_route_permute: NULL or misaligned permutation output");
+  // validation of the routing arguments and the router logits (if any); the tail replaces the top-k kernel
+  const ft_status st = route_logits(x, x_dtype, w_router, logits, T, H, E, k, gating, topk_ids, topk_w, stream);
+  if (st != FT_OK) return st;
+  FusedRouteArgs a{};
+  a.logits = logits;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.gating = gating;
+  a.renorm = renormalize ? 1 : 0;
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.offsets = expert_offsets;
+  a.sorted_rows = sorted_rows;
+  a.row_pos = row_pos;
+  const int vpl = cdiv(E, 64);
+  if (vpl <= 2) hipLaunchKernelGGL(route_tail_kernel<2>, dim3(1), dim3(1024), 0, stream, a);
+  else if (vpl <= 4) hipLaunchKernelGGL(route_tail_kernel<4>, dim3(1), dim3(1024), 0, stream, a);
+  else hipLaunchKernelGGL(route_tail_kernel<16>, dim3(1), dim3(1024), 0, stream, a);
+  FT_LAUNCHED("route_tail_kernel");
   clear_error();
   return FT_OK;
 }

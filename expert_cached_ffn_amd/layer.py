@@ -84,6 +84,8 @@ class MoELayer:
         self.ws_perm_bytes = ops.ft_workspace_bytes(_lib.FT_WS_PERMUTE, T_max, k, E)
         self.ws_ffn_bytes = ops.ft_workspace_bytes(_lib.FT_WS_FFN, T_max, k, E, H, shape.I)
         self.ws_perm = torch.empty(max(256, self.ws_perm_bytes), dtype=torch.uint8, device=dev)
+        self.ws_rp_bytes = ops.ft_workspace_bytes(_lib.FT_WS_ROUTE_PERMUTE, T_max, k, E)
+        self.ws_rp = torch.empty(max(256, self.ws_rp_bytes), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty(max(256, self.ws_ffn_bytes), dtype=torch.uint8, device=dev)
 
     def route(self, T, x=None, w_router=None, logits=None, stream=None):
@@ -93,6 +95,16 @@ class MoELayer:
             x, w_router = None, None
         ops.ft_moe_route(x, DTYPES[s.xdtype], w_router, self.logits, T, s.H, s.E, s.k, GATING[s.gating],
                          s.renormalize, self.ids, self.w, stream=stream)
+
+    def route_permute(self, T, x=None, w_router=None, logits=None, stream=None):
+        """route + permute through ft_moe_route_permute (one launch in the decode regime)."""
+        s = self.s
+        if logits is not None:
+            self.logits[:T].copy_(logits[:T])
+            x, w_router = None, None
+        ops.ft_moe_route_permute(x, DTYPES[s.xdtype], w_router, self.logits, T, s.H, s.E, s.k, GATING[s.gating],
+                                 s.renormalize, self.ids, self.w, self.offsets, self.sorted_rows, self.row_pos,
+                                 self.ws_rp, self.ws_rp_bytes, stream=stream)
 
     def permute(self, T, ids=None, stream=None):
         ids = self.ids if ids is None else ids
@@ -116,8 +128,7 @@ class MoELayer:
     def forward(self, T, x, pool, w_router=None, logits=None, slot_of_expert=None, shared_blob=None,
                 stream=None, mode=0):
         """route -> permute -> grouped FFN -> combine, all enqueued on one stream."""
-        self.route(T, x=x, w_router=w_router, logits=logits, stream=stream)
-        self.permute(T, stream=stream)
+        self.route_permute(T, x=x, w_router=w_router, logits=logits, stream=stream)
         self.ffn(T, x, pool, slot_of_expert=slot_of_expert, shared_blob=shared_blob, stream=stream,
                  mode=mode)
         self.combine(T, with_shared=shared_blob is not None, stream=stream)

@@ -62,6 +62,15 @@ def ft_moe_route(x, x_dtype: int, w_router, logits, T: int, H: int, E: int, k: i
                                    int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
 
 
+def ft_moe_route_permute(x, x_dtype: int, w_router, logits, T: int, H: int, E: int, k: int, gating: int,
+                         renormalize: bool, topk_ids, topk_w, expert_offsets, sorted_rows, row_pos,
+                         workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    _check(_lib.lib().ft_moe_route_permute(_ptr(x), x_dtype, _ptr(w_router), _ptr(logits), T, H, E, k, gating,
+                                           int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w),
+                                           _ptr(expert_offsets), _ptr(sorted_rows), _ptr(row_pos),
+                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def ft_moe_permute(topk_ids, T: int, k: int, E: int, expert_offsets, sorted_rows, row_pos,
                    workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     _check(_lib.lib().ft_moe_permute(_ptr(topk_ids), T, k, E, _ptr(expert_offsets), _ptr(sorted_rows),

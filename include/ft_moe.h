@@ -141,6 +141,21 @@ ft_status ft_moe_permute(const int32_t *topk_ids, int32_t T, int32_t k, int32_t 
                          int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * ft_moe_route_permute -- ft_moe_route followed by ft_moe_permute on the same
+ * stream, with the same arguments, results and errors.  When 1 <= T <= 16 and
+ * T*k <= 2048 (small decode batches, where per-launch latency is most of the
+ * cost of routing) top-k, gating and the permutation run as one launch after
+ * the router logits; otherwise it makes the two calls.
+ * workspace: ft_workspace_bytes(FT_WS_ROUTE_PERMUTE, T, k, E, 0, 0) bytes
+ * (ft_moe_permute's; may be 0, then workspace may be NULL).
+ */
+ft_status ft_moe_route_permute(const void *x, int32_t x_dtype, const void *w_router, float *logits,
+                               int32_t T, int32_t H, int32_t E, int32_t k, int32_t gating,
+                               int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                               int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Expert FFN                                                                 */
 /* ------------------------------------------------------------------------ */
@@ -324,7 +339,7 @@ ft_status ft_expert_cache_destroy(ft_expert_cache *c);
 /* ------------------------------------------------------------------------ */
 /* Workspace sizes                                                            */
 /* ------------------------------------------------------------------------ */
-enum { FT_WS_PERMUTE = 1, FT_WS_FFN = 2 };
+enum { FT_WS_PERMUTE = 1, FT_WS_FFN = 2, FT_WS_ROUTE_PERMUTE = 3 };
 
 /* Bytes of workspace the call `which` needs for these sizes (0 if none).
  * For FT_WS_FFN, H and I are those of the layout and the shared expert is

@@ -89,6 +89,81 @@ def test_route_given_logits_bit_exact_ids(ops, gating, renorm, E, k, T):
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=2e-6, atol=1e-7)
 
 
+# ----------------------------------------------------------------------------- route + permute, one call
+
+def _check_permutation(ids, off, rows, pos, E, ids_ref=None):
+    """Bit-exact against the oracle's permutation when the ids agree, else the
+    defining properties of a stable counting sort of the GPU's own ids."""
+    ids = np.asarray(ids)
+    if ids_ref is not None and np.array_equal(ids, ids_ref):
+        o, r, p = moe.permute(ids_ref, E)
+        assert np.array_equal(off, o) and np.array_equal(rows, r) and np.array_equal(pos, p)
+        return
+    flat = ids.ravel()
+    assert np.array_equal(np.diff(off), np.bincount(flat, minlength=E))
+    assert np.array_equal(np.sort(rows), np.arange(flat.size))
+    assert np.array_equal(pos[rows], np.arange(flat.size))
+    for e in range(E):
+        seg = rows[off[e]:off[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+def _route_permute(ops, cfg, T, x=None, wr=None, logits=None, ws=None):
+    from expert_cached_ffn_amd.layer import GATING
+    E, k = cfg.E, cfg.k
+    lg = dev(logits) if logits is not None else torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    rows = torch.empty(max(1, T * k), dtype=torch.int32, device="cuda")
+    pos = torch.empty(max(1, T * k), dtype=torch.int32, device="cuda")
+    wsb = ops.ft_workspace_bytes(3, T, k, E)
+    if ws is None:
+        ws = torch.zeros(max(256, wsb), dtype=torch.uint8, device="cuda")
+    ops.ft_moe_route_permute(None if x is None else dev(x), x_dtype(cfg), None if wr is None else dev(wr), lg,
+                             T, cfg.H, E, k, GATING[cfg.gating], cfg.renormalize, ids, w, off, rows, pos, ws, wsb)
+    torch.cuda.synchronize()
+    return (lg.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), off.cpu().numpy(), rows.cpu().numpy()[:T * k],
+            pos.cpu().numpy()[:T * k], ws)
+
+
+@pytest.mark.parametrize("cfg_id,T", [(2, 1), (2, 16), (2, 64), (3, 1), (3, 8), (3, 32), (3, 100), (2, 65)])
+def test_route_permute_with_router(ops, cfg_id, T):
+    """Router + one routing launch up to 64 tokens, the two calls above."""
+    cfg = synth.CONFIGS[cfg_id]
+    print(f"route+permute cfg{cfg_id} T={T}", flush=True)
+    ws = None
+    for rep in range(3):  # back to back on one workspace
+        x = synth.tokens(cfg, T, case=rep)
+        wr = synth.router_weight(cfg)
+        x64 = formats.activations_to_f64(cfg.xdtype, x)
+        wr64 = formats.activations_to_f64(cfg.xdtype, wr)
+        l_ref, ids_ref, w_ref, margin = route_oracle(cfg, x64, wr64)
+        lg, ids, w, off, rows, pos, ws = _route_permute(ops, cfg, T, x=x, wr=wr, ws=ws)
+        scale = np.abs(x64) @ np.abs(wr64).T
+        assert np.all(np.abs(lg - l_ref) <= 3e-5 * scale + 1e-6)
+        sure = margin > 1e-4
+        assert np.array_equal(ids[sure], ids_ref[sure])
+        w_at = moe.gating_weights(l_ref, ids, cfg.gating, cfg.renormalize)
+        np.testing.assert_allclose(w[sure], w_at[sure], rtol=1e-4, atol=1e-6)
+        _check_permutation(ids, off, rows, pos, cfg.E, ids_ref)
+
+
+@pytest.mark.parametrize("E,k,T", [(128, 8, 1), (256, 6, 64), (16, 16, 9), (1000, 2, 33), (256, 6, 300)])
+def test_route_permute_given_logits_bit_exact(ops, E, k, T):
+    cfg = synth.shrink(synth.CONFIGS[3], E=E, k=k, shared=False)
+    rng = np.random.default_rng(E + k + T)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, :] = 0.0
+    logits[0, ::3] = -0.0
+    ids_ref = moe.topk(logits, k)
+    w_ref = moe.gating_weights(logits, ids_ref, cfg.gating, cfg.renormalize)
+    _, ids, w, off, rows, pos, _ = _route_permute(ops, cfg, T, logits=logits)
+    assert np.array_equal(ids, ids_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=2e-6, atol=1e-7)
+    _check_permutation(ids, off, rows, pos, E, ids_ref)
+
+
 # ----------------------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,k,E,kind", [(1, 8, 128, "u"), (16, 8, 128, "u"), (64, 8, 128, "u"), (5, 2, 16, "u"),
