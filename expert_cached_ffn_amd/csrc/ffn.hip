@@ -201,9 +201,11 @@ template <int WF, bool GLU, int WAVES, int KPW>
 __global__ __launch_bounds__(WAVES * 64) void ffn_persist_kernel(PersistArgs a) {
   __shared__ float s_red[WAVES * (GLU ? 2 : 1) * 256];
   // Units in flight: a 16-wave gate/up tile leaves no registers for a second
-  // activation set (128 per lane in a 1024-thread workgroup); the smaller
-  // down-projection tiles need a deeper ring to cover HBM latency.
-  constexpr int NB = GLU ? (WAVES * KPW >= 16 ? 1 : 2) : (WAVES * KPW >= 16 ? 2 : 3);
+  // activation set (128 per lane in a 1024-thread workgroup); 8-wave bf16
+  // gate/up tiles take two (measured faster; MXFP4 tiles were slower with two);
+  // the smaller down-projection tiles need a deeper ring to cover HBM latency.
+  constexpr int NB = GLU ? (WAVES * KPW >= 16 ? (WAVES <= 8 && WF == WF_BF16 ? 2 : 1) : 2)
+                         : (WAVES * KPW >= 16 ? 2 : 3);
   stream_persist<WF, GLU, WAVES, KPW, NB>(a, s_red);
 }
 
