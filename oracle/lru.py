@@ -24,6 +24,16 @@ have stamp 0, so they fill lowest index first; stamps are otherwise unique).
 Refreshing all hits before any eviction means a miss can never evict an expert
 that the same step still needs.  If |S| exceeds the capacity the step is
 refused and nothing changes.
+
+Resizing: the runtime can resize and rebuild the GPU expert cache at safe
+points of its scheduler when the available GPU memory changes (FreeToken
+quantization page, "Flujo de configuración de la cuantización de FreeToken";
+FreeToken 290b model page, "Caché elástica").  Reading taken here (the pages
+give no rule): between steps, the cache keeps the min(new capacity, resident)
+most recently used entries and drops the rest (counted as evictions); the
+kept entries move to slots 0, 1, ... in ascending order of their old slot
+(never to a higher slot, so the move is safe in place), keep their stamps,
+and the clock is unchanged; new slots are empty.
 """
 from __future__ import annotations
 
@@ -115,6 +125,30 @@ class ExpertLRU:
         self.hits += sum(1 for ev in events.values() if ev.hit)
         self.misses += sum(1 for ev in events.values() if not ev.hit)
         return [events[e] for e in needed]
+
+    def resize(self, capacity: int) -> tuple[list[tuple[int, int]], list[tuple]]:
+        """Change the number of slots; returns (moves old slot -> new slot, dropped keys)."""
+        if capacity < 1:
+            raise ValueError("capacity must be positive")
+        used = [s for s in range(self.capacity) if self.owner[s] is not None]
+        keep = set(sorted(used, key=lambda s: self.stamp[s], reverse=True)[:capacity])
+        moves, dropped = [], []
+        owner: list[tuple | None] = [None] * capacity
+        stamp = [0] * capacity
+        nxt = 0
+        for s in used:                        # ascending old slot
+            key = self.owner[s]
+            if s in keep:
+                owner[nxt], stamp[nxt] = key, self.stamp[s]
+                self.where[key] = nxt
+                moves.append((s, nxt))
+                nxt += 1
+            else:
+                del self.where[key]
+                dropped.append(key)
+        self.evictions += len(dropped)
+        self.capacity, self.owner, self.stamp = capacity, owner, stamp
+        return moves, dropped
 
     def slot_of_expert(self, layer: int) -> list[int]:
         """Slot of every expert of ``layer`` (-1 if not resident)."""

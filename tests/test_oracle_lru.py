@@ -38,6 +38,13 @@ def _traces(golden_dir):
                         s, evicted = rest, None
                     evs.append((int(e), hm == "H", int(s), evicted))
                 cur["steps"].append((int(lw[1]), int(lw[3]), ids, evs))
+            elif w[0] == "resize":
+                left, right = line.split(":", 1)
+                rw = right.split()
+                i = rw.index("drops")
+                keeps = [tuple(int(v) for v in t.split(">")) for t in rw[1:i]]
+                drops = [tuple(int(v) for v in t.split(".")) for t in rw[i + 1:]]
+                cur["steps"].append(("resize", int(left.split()[1]), keeps, drops))
             elif w[0] == "totals":
                 cur["totals"] = {k: int(v) for k, v in (p.split("=") for p in w[1:])}
             elif w[0] == "stamps":
@@ -49,10 +56,13 @@ def _traces(golden_dir):
 
 def test_hand_traced_sequences(golden_dir):
     traces = _traces(golden_dir)
-    assert [t["name"] for t in traces] == ["A", "B", "C", "D"]
+    assert [t["name"] for t in traces] == ["A", "B", "C", "D", "E"]
     for tr in traces:
         lru = ExpertLRU(tr["L"], tr["E"], tr["C"])
         for step, layer, ids, want in tr["steps"]:
+            if step == "resize":
+                assert lru.resize(layer) == (ids, want), (tr["name"], "resize", layer)
+                continue
             got = lru.step(layer, ids)
             assert [(e.expert, e.hit, e.slot, e.evicted) for e in got] == want, (tr["name"], step, layer)
         assert lru.stats() == tr["totals"], tr["name"]
@@ -124,6 +134,51 @@ def test_a_miss_never_evicts_a_needed_expert():
         assert all(lru.lookup(l, int(e)) >= 0 for e in ids)
         slots = [ev.slot for ev in evs]
         assert len(set(slots)) == len(slots)
+
+
+def test_resize_keeps_the_most_recent_entries_like_a_textbook_lru():
+    # one access per step: the cache is a textbook LRU, and shrinking it keeps
+    # exactly the most recently used keys (then it goes on as the smaller LRU)
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        C0, C1 = int(rng.integers(2, 9)), int(rng.integers(1, 12))
+        lru = ExpertLRU(1, 12, C0)
+        od = OrderedDict()
+        seq = rng.integers(0, 12, size=60)
+        cut = int(rng.integers(1, 59))
+        for t, e in enumerate(seq):
+            if t == cut:
+                _, dropped = lru.resize(C1)
+                while len(od) > C1:
+                    k, _ = od.popitem(last=False)
+                    assert (0, k) in dropped
+                assert sorted(lru.where) == sorted((0, k) for k in od)
+                # kept entries sit in slots 0.. in ascending old-slot order
+                assert sorted(lru.where.values()) == list(range(len(od)))
+            e = int(e)
+            ev = lru.step(0, [e])[0]
+            hit = e in od
+            assert ev.hit == hit
+            if hit:
+                od.move_to_end(e)
+            else:
+                if len(od) == lru.capacity:
+                    od.popitem(last=False)
+                od[e] = True
+            assert sorted(k[1] for k in lru.where) == sorted(od)
+
+
+def test_resize_grow_moves_nothing_and_shrink_never_moves_up():
+    rng = np.random.default_rng(12)
+    lru = ExpertLRU(2, 50, 20)
+    for t in range(40):
+        lru.step(t % 2, rng.choice(50, size=5, replace=False))
+    before = dict(lru.where)
+    moves, dropped = lru.resize(30)
+    assert dropped == [] and all(a == b for a, b in moves) and lru.where == before
+    moves, dropped = lru.resize(7)
+    assert len(dropped) == 13 and all(b <= a for a, b in moves)
+    assert lru.evictions >= 13 and len(lru.where) == 7 and lru.owner.count(None) == 0
 
 
 def test_miss_split_policy():
