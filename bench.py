@@ -282,23 +282,30 @@ def run_prefill(args, cfg, T, mode=0):
                 flops_gate_up=flops_gu, flops_ffn=flops_all)
 
 
-def pinned_h2d_bandwidth(expert_bytes, n=32):
-    """B_p: pinned host -> device copies of one expert blob each, back to back on one stream."""
+def pinned_h2d_bandwidth(expert_bytes, n=32, n_streams=1):
+    """B_p: pinned host -> device copies of one expert blob each, spread over n_streams queues."""
     import torch
     src = torch.empty((n, expert_bytes), dtype=torch.uint8, pin_memory=True)
     dst = torch.empty((n, expert_bytes), dtype=torch.uint8, device="cuda")
-    s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
+    streams = [torch.cuda.Stream() for _ in range(n_streams)]
+    main = torch.cuda.current_stream()
+
+    def go():
+        for s in streams:
+            s.wait_stream(main)
         for i in range(n):
-            dst[i].copy_(src[i], non_blocking=True)
-    s.synchronize()
+            with torch.cuda.stream(streams[i % n_streams]):
+                dst[i].copy_(src[i], non_blocking=True)
+        for s in streams:
+            main.wait_stream(s)
+
+    go()
+    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        a.record()
-        for i in range(n):
-            dst[i].copy_(src[i], non_blocking=True)
-        b.record()
-    s.synchronize()
+    a.record()
+    go()
+    b.record()
+    torch.cuda.synchronize()
     return n * expert_bytes / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
@@ -334,8 +341,22 @@ def run_cache_trace(args, cfg):
     copy_stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     log(f"cache trace: host bank {bank.numel() / 1e9:.1f} GB pinned and filled in {time.time() - t0:.1f}s")
-    b_p = pinned_h2d_bandwidth(eb)
-    log(f"pinned H2D bandwidth B_p = {b_p:.1f} GB/s")
+    b_p1 = pinned_h2d_bandwidth(eb)
+    # B_p as the cache's own fill path achieves it: layer-steps whose k experts all miss, nothing else
+    probe = ops.ExpertCache(layer.layout, Lyr, E, 64, pool, bank, copy_stream)
+    n_probe = 64
+    pids = torch.tensor([[(i * cfg.k + j) % E for j in range(cfg.k)] for i in range(n_probe)], dtype=torch.int32,
+                        device="cuda")
+    torch.cuda.synchronize()
+    tp = time.perf_counter()
+    for i in range(n_probe):
+        probe.step((i * 7) % Lyr, pids[i], 1, cfg.k, slot_of)
+    torch.cuda.synchronize()
+    b_p = probe.stats()["bytes_h2d"] / (time.perf_counter() - tp) / 1e9
+    assert probe.stats()["misses"] == n_probe * cfg.k
+    probe.destroy()
+    log(f"pinned H2D bandwidth B_p = {b_p:.1f} GB/s through the cache's fills "
+        f"({b_p1:.1f} GB/s for back-to-back torch copies on one stream)")
 
     def run(steps, cache):
         for st in range(steps):
@@ -357,6 +378,21 @@ def run_cache_trace(args, cfg):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t1
     st = cache.stats()
+    # elastic resize at a safe point: halve the slots in place (the most recent
+    # entries stay), run the first 64 steps again, grow back in the same pool
+    t2 = time.perf_counter()
+    cache.resize(C // 2, pool)
+    shrink_ms = (time.perf_counter() - t2) * 1e3
+    before = cache.stats()
+    run(min(64, S), cache)
+    torch.cuda.synchronize()
+    after = cache.stats()
+    t3 = time.perf_counter()
+    cache.resize(C, pool)
+    grow_ms = (time.perf_counter() - t3) * 1e3
+    half_hit = (after["hits"] - before["hits"]) / max(1, after["accesses"] - before["accesses"])
+    log(f"elastic resize: {C} -> {C // 2} slots in place {shrink_ms:.1f} ms, back to {C} {grow_ms:.1f} ms; "
+        f"hit rate over 64 steps at {C // 2} slots {half_hit:.4f}")
     cache.destroy()
     hit = st["hits"] / max(1, st["accesses"])
     # lower bound of a step: resident expert reads at 8 TB/s vs fills at the measured B_p
@@ -364,7 +400,9 @@ def run_cache_trace(args, cfg):
     bound = max(resident / (HBM_PEAK_GBS * 1e9), st["bytes_h2d"] / S / (b_p * 1e9))
     res = dict(tokens_per_s=S / dt, ms_per_step=dt / S * 1e3, hit_rate=hit, misses_per_step=st["misses"] / S,
                bytes_h2d=st["bytes_h2d"], h2d_GBps=st["bytes_h2d"] / dt / 1e9, b_p_GBps=b_p,
-               bound_ms_per_step=bound * 1e3, frac_of_bound=bound / (dt / S), stats=st)
+               bound_ms_per_step=bound * 1e3, frac_of_bound=bound / (dt / S), stats=st, b_p_torch_copy_GBps=b_p1,
+               resize={"shrink_ms": shrink_ms, "grow_ms": grow_ms, "from_slots": C, "to_slots": C // 2,
+                       "hit_rate_64_steps_at_half": half_hit})
     log(f"cache trace: {S} steps x {Lyr} layers in {dt:.2f}s = {S / dt:.1f} tok/s, hit rate {hit:.4f}, "
         f"{res['misses_per_step']:.2f} misses/step, fills {res['h2d_GBps']:.1f} GB/s (B_p {b_p:.1f}), "
         f"bound {bound * 1e3:.3f} ms/step -> {100 * res['frac_of_bound']:.0f} % of it")

@@ -22,6 +22,7 @@ EXPORTS = [
     "ft_moe_grouped_ffn", "ft_moe_combine", "ft_expert_cache_create", "ft_expert_cache_step",
     "ft_expert_cache_stats", "ft_expert_cache_trace", "ft_expert_cache_lookup",
     "ft_expert_cache_destroy", "ft_workspace_bytes", "ft_mxfp8_quantize", "ft_moe_route_permute",
+    "ft_expert_cache_resize",
 ]
 
 
@@ -72,6 +73,8 @@ def lib() -> C.CDLL:
     L.ft_moe_grouped_ffn.restype = i32
     L.ft_moe_grouped_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, p, p, i32, i32, i32, i32, p, p, p, p,
                                      i32, p, sz, p]
+    L.ft_expert_cache_resize.restype = i32
+    L.ft_expert_cache_resize.argtypes = [p, i32, p, p]
     L.ft_moe_route_permute.restype = i32
     L.ft_moe_route_permute.argtypes = [p, i32, p, p, i32, i32, i32, i32, i32, i32, p, p, p, p, p, p, sz, p]
     L.ft_mxfp8_quantize.restype = i32

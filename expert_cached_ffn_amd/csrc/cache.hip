@@ -23,6 +23,7 @@
 namespace ft {
 
 constexpr int kLruThreads = 1024;
+constexpr int kFillStreams = 4;  // miss fills spread over this many copy queues (the caller's + 3 own)
 constexpr int kLruMaxE = 4096;
 constexpr int kLruMaxC = 65536;
 
@@ -226,6 +227,8 @@ struct ft_expert_cache {
   uint8_t *pool;
   const uint8_t *bank;
   hipStream_t copy_stream;
+  hipStream_t fill[kFillStreams];   // fill[0] = copy_stream; the others are the cache's own
+  hipEvent_t ev_fill[kFillStreams];
   LruState st;
   void *dev_state;
   LruResult *res_host;   // pinned
@@ -273,6 +276,10 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
   const size_t keys = size_t(n_layers) * E;
   const size_t bytes = keys * 4 + size_t(capacity) * 4 + size_t(capacity) * 8 + 64;
   auto cleanup = [&](ft_status st, const std::string &msg) {
+    for (int i = 0; i < kFillStreams; ++i) {
+      if (i > 0 && c->fill[i]) (void)hipStreamDestroy(c->fill[i]);
+      if (c->ev_fill[i]) (void)hipEventDestroy(c->ev_fill[i]);
+    }
     if (c->dev_state) (void)hipFree(c->dev_state);
     if (c->res_host) (void)hipHostFree(c->res_host);
     if (c->ev_lru) (void)hipEventDestroy(c->ev_lru);
@@ -297,6 +304,13 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
   if (hipEventCreateWithFlags(&c->ev_lru, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming) != hipSuccess)
     return cleanup(FT_EHIP, "ft_expert_cache_create: hipEventCreate failed");
+  c->fill[0] = copy_stream;
+  for (int i = 0; i < kFillStreams; ++i) {
+    // default priority (the same as every other stream of the library)
+    if ((i > 0 && hipStreamCreateWithFlags(&c->fill[i], hipStreamNonBlocking) != hipSuccess) ||
+        hipEventCreateWithFlags(&c->ev_fill[i], hipEventDisableTiming) != hipSuccess)
+      return cleanup(FT_EHIP, "ft_expert_cache_create: stream or event creation failed");
+  }
   if (hipDeviceSynchronize() != hipSuccess) return cleanup(FT_EHIP, "ft_expert_cache_create: sync failed");
   c->stats = ft_cache_stats{};
   c->map_mirror.assign(keys, -1);
@@ -328,7 +342,12 @@ extern "C" ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, con
   if (r.status != LRU_OK) return fail(FT_EHIP, "ft_expert_cache_step: LRU kernel did not report");
   const int32_t step = int32_t(c->stats.steps);
   const uint64_t eb = c->L.expert_bytes;
+  // Fills go round-robin over kFillStreams copy queues (one queue does not
+  // reach the host link's bandwidth).  Each queue first waits for the compute
+  // stream up to the LRU kernel: a victim slot may still be read by earlier
+  // work enqueued there.  The compute stream then waits for every queue used.
   int fills = 0;
+  bool used[kFillStreams] = {};
   for (int i = 0; i < r.n_needed; ++i) {
     const int e = r.ev[i][0], hit = r.ev[i][1], s = r.ev[i][2], ek = r.ev[i][3];
     c->log.push_back(ft_cache_event{step, layer, e, hit, s, ek});
@@ -336,12 +355,18 @@ extern "C" ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, con
     if (ek >= 0) c->map_mirror[size_t(ek)] = -1;
     c->map_mirror[size_t(layer) * c->E + e] = s;
     const uint8_t *src = c->bank + (uint64_t(layer) * c->E + e) * eb;
-    FT_HIP(hipMemcpyAsync(c->pool + uint64_t(s) * eb, src, eb, hipMemcpyHostToDevice, c->copy_stream));
+    const int q = fills % kFillStreams;
+    if (!used[q]) {
+      FT_HIP(hipStreamWaitEvent(c->fill[q], c->ev_lru, 0));
+      used[q] = true;
+    }
+    FT_HIP(hipMemcpyAsync(c->pool + uint64_t(s) * eb, src, eb, hipMemcpyHostToDevice, c->fill[q]));
     ++fills;
   }
-  if (fills) {
-    FT_HIP(hipEventRecord(c->ev_copy, c->copy_stream));
-    FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_copy, 0));
+  for (int q = 0; q < kFillStreams; ++q) {
+    if (!used[q]) continue;
+    FT_HIP(hipEventRecord(c->ev_fill[q], c->fill[q]));
+    FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
   }
   c->stats.accesses += uint64_t(r.n_needed);
   c->stats.hits += uint64_t(r.n_hits);
@@ -349,6 +374,94 @@ extern "C" ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, con
   c->stats.evictions += uint64_t(r.n_evictions);
   c->stats.bytes_h2d += uint64_t(fills) * eb;
   c->stats.steps += 1;
+  clear_error();
+  return FT_OK;
+}
+
+// Resize at a safe point (the pages: the runtime resizes and rebuilds the GPU
+// expert cache at safe points of its scheduler when the available GPU memory
+// changes; FreeToken quantization page, "Flujo de configuración de la
+// cuantización de FreeToken"; FreeToken 290b model page, "Caché elástica").
+// Rule (the pages give none): keep the min(new capacity, resident) most
+// recently used entries, compacted into slots 0.. in ascending order of their
+// old slot (an entry never moves to a higher slot, so the move is safe inside
+// one allocation), stamps and clock unchanged, the rest dropped (evictions).
+// A rare, host-driven operation: it waits for the cache's streams, reads the
+// small state, rebuilds it for the new capacity and copies the kept blobs.
+extern "C" ft_status ft_expert_cache_resize(ft_expert_cache *c, int32_t new_capacity, void *new_slot_pool,
+                                            hipStream_t stream) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_resize: cache is NULL");
+  FT_REQUIRE(new_capacity >= 1, "ft_expert_cache_resize: capacity must be positive");
+  FT_SUPPORTED(new_capacity <= kLruMaxC, "ft_expert_cache_resize: capacity > 65536");
+  FT_REQUIRE(new_slot_pool != nullptr && aligned(new_slot_pool, 256),
+             "ft_expert_cache_resize: new_slot_pool must be a 256-byte aligned device buffer");
+  hipPointerAttribute_t pa{};
+  FT_HIP(hipPointerGetAttributes(&pa, new_slot_pool));
+  FT_REQUIRE(pa.type == hipMemoryTypeDevice, "ft_expert_cache_resize: new_slot_pool is not device memory");
+  for (int q = 0; q < kFillStreams; ++q) FT_HIP(hipStreamSynchronize(c->fill[q]));
+  FT_HIP(hipStreamSynchronize(stream));
+  const int C = c->C, C2 = new_capacity;
+  const size_t keys = size_t(c->n_layers) * c->E;
+  std::vector<uint64_t> stamp(C);
+  std::vector<int32_t> owner(C);
+  uint64_t clock = 0;
+  FT_HIP(hipMemcpy(stamp.data(), c->st.stamp, size_t(C) * 8, hipMemcpyDeviceToHost));
+  FT_HIP(hipMemcpy(owner.data(), c->st.owner, size_t(C) * 4, hipMemcpyDeviceToHost));
+  FT_HIP(hipMemcpy(&clock, c->st.clock, 8, hipMemcpyDeviceToHost));
+  // keep the C2 largest stamps among occupied slots (stamps of occupied slots are distinct)
+  std::vector<int> used;
+  for (int s = 0; s < C; ++s)
+    if (owner[s] >= 0) used.push_back(s);
+  std::vector<int> by_age(used);
+  std::sort(by_age.begin(), by_age.end(), [&](int a, int b) { return stamp[a] > stamp[b]; });
+  std::vector<char> keep(C, 0);
+  for (size_t i = 0; i < by_age.size() && i < size_t(C2); ++i) keep[by_age[i]] = 1;
+  std::vector<uint64_t> stamp2(C2, 0);
+  std::vector<int32_t> owner2(C2, -1);
+  std::vector<int32_t> map2(keys, -1);
+  uint8_t *pool2 = static_cast<uint8_t *>(new_slot_pool);
+  const uint64_t eb = c->L.expert_bytes;
+  int nxt = 0;
+  uint64_t dropped = 0;
+  for (int s : used) {  // ascending old slot
+    if (!keep[s]) {
+      ++dropped;
+      continue;
+    }
+    owner2[nxt] = owner[s];
+    stamp2[nxt] = stamp[s];
+    map2[size_t(owner[s])] = nxt;
+    if (pool2 != c->pool || nxt != s)
+      FT_HIP(hipMemcpyAsync(pool2 + uint64_t(nxt) * eb, c->pool + uint64_t(s) * eb, eb, hipMemcpyDeviceToDevice,
+                            stream));
+    ++nxt;
+  }
+  // new device state for the new capacity (same layout as at creation)
+  void *state2 = nullptr;
+  const size_t bytes = keys * 4 + size_t(C2) * 4 + size_t(C2) * 8 + 64;
+  FT_HIP(hipMalloc(&state2, bytes));
+  uint8_t *p = static_cast<uint8_t *>(state2);
+  LruState st2;
+  st2.stamp = reinterpret_cast<uint64_t *>(p);
+  st2.clock = reinterpret_cast<uint64_t *>(p + size_t(C2) * 8);
+  st2.map = reinterpret_cast<int32_t *>(p + size_t(C2) * 8 + 64);
+  st2.owner = st2.map + keys;
+  hipError_t e = hipMemcpy(st2.stamp, stamp2.data(), size_t(C2) * 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(st2.clock, &clock, 8, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(st2.map, map2.data(), keys * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(st2.owner, owner2.data(), size_t(C2) * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipFree(state2);
+    return fail(FT_EHIP, std::string("ft_expert_cache_resize: ") + hipGetErrorString(e));
+  }
+  (void)hipFree(c->dev_state);
+  c->dev_state = state2;
+  c->st = st2;
+  c->C = C2;
+  c->pool = pool2;
+  c->map_mirror = map2;
+  c->stats.evictions += dropped;
   clear_error();
   return FT_OK;
 }
@@ -386,7 +499,13 @@ extern "C" ft_status ft_expert_cache_destroy(ft_expert_cache *c) {
     clear_error();
     return FT_OK;
   }
-  hipError_t e1 = hipStreamSynchronize(c->copy_stream);
+  hipError_t e1 = hipSuccess;
+  for (int q = 0; q < kFillStreams; ++q) {
+    const hipError_t eq = hipStreamSynchronize(c->fill[q]);
+    if (e1 == hipSuccess) e1 = eq;
+    if (q > 0) (void)hipStreamDestroy(c->fill[q]);
+    (void)hipEventDestroy(c->ev_fill[q]);
+  }
   (void)hipFree(c->dev_state);
   (void)hipHostFree(c->res_host);
   (void)hipEventDestroy(c->ev_lru);

@@ -115,6 +115,13 @@ class ExpertCache:
 
     step = ft_expert_cache_step
 
+    def ft_expert_cache_resize(self, capacity: int, slot_pool, stream=None) -> None:
+        _check(_lib.lib().ft_expert_cache_resize(self._h, capacity, _ptr(slot_pool), _stream(stream)))
+        self.capacity = capacity
+        self._keep = (slot_pool,) + tuple(self._keep[1:])
+
+    resize = ft_expert_cache_resize
+
     def stats(self) -> dict:
         s = CacheStats()
         _check(_lib.lib().ft_expert_cache_stats(self._h, C.byref(s)))

@@ -333,6 +333,28 @@ ft_status ft_expert_cache_trace(const ft_expert_cache *c, void *host_buf, size_t
 ft_status ft_expert_cache_lookup(const ft_expert_cache *c, int32_t layer, int32_t expert,
                                  int32_t *slot);
 
+/*
+ * ft_expert_cache_resize -- change the number of slots at a safe point (the
+ * runtime resizes and rebuilds the GPU expert cache at safe points of its
+ * scheduler when the GPU memory budget changes: FreeToken quantization page,
+ * "Flujo de configuración de la cuantización de FreeToken"; FreeToken 290b
+ * model page, "Caché elástica").  The min(new_capacity, resident) most
+ * recently used entries are kept and compacted into slots 0.. in ascending
+ * order of their old slot; the others are dropped (counted as evictions);
+ * recency and later decisions continue as if the cache had always had the
+ * kept entries in those slots.  Kept blobs are copied into new_slot_pool
+ * (device, new_capacity * expert_bytes, caller-owned; it may be the current
+ * pool when that allocation holds new_capacity slots -- entries only move to
+ * lower slots, so the copies are safe in place).  The cache borrows
+ * new_slot_pool from then on.  The call waits for `stream` (the stream the
+ * cache steps run on) and the copy stream, and returns when the new state
+ * and the copies are complete: a rare call, not for the per-token path.
+ * Errors: new_capacity < 1 or a non-device pool -> FT_EINVAL; above 65536
+ * slots -> FT_ENOTSUP; on FT_EHIP the cache is unchanged.
+ */
+ft_status ft_expert_cache_resize(ft_expert_cache *c, int32_t new_capacity, void *new_slot_pool,
+                                 hipStream_t stream);
+
 /* Free the cache's own state.  Waits for its pending copies first. */
 ft_status ft_expert_cache_destroy(ft_expert_cache *c);
 

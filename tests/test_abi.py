@@ -145,5 +145,6 @@ def test_cache_validation():
     assert lib.ft_expert_cache_create(C.byref(L), 1, 8, 4, 256, 256, None, C.byref(h)) == -1   # NULL stream
     assert lib.ft_expert_cache_step(None, 0, None, 1, 1, None, None) == -1
     assert lib.ft_expert_cache_stats(None, None) == -1
+    assert lib.ft_expert_cache_resize(None, 4, 256, None) == -1
     assert lib.ft_expert_cache_destroy(None) == 0
     assert b"NULL" in lib.ft_last_error() or lib.ft_last_error() == b""

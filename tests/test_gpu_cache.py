@@ -46,6 +46,13 @@ class Rig:
         d = torch.from_numpy(ids).cuda() if ids.size else torch.zeros(1, dtype=torch.int32, device="cuda")
         self.cache.step(layer, d, ids.size, 1, self.slot_of)
 
+    def resize(self, C, in_place):
+        """Resize to C slots: in the current pool (C <= its slots) or into a fresh one."""
+        if not in_place:
+            self.pool = torch.zeros((C, self.eb), dtype=torch.uint8, device="cuda")
+        self.cache.resize(C, self.pool)
+        self.C = C
+
 
 def events_by_step(trace):
     out = {}
@@ -59,11 +66,15 @@ def test_hand_traced_sequences_on_device(env, golden_dir):
     for tr in _traces(golden_dir):
         print(f"trace {tr['name']}", flush=True)
         rig = Rig(ops, tr["L"], tr["E"], tr["C"], fill=False)
-        for _, layer, ids, _ in tr["steps"]:
-            rig.step(layer, ids)
+        for kind, layer, ids, _ in tr["steps"]:
+            if kind == "resize":
+                rig.resize(layer, in_place=layer <= rig.C)
+            else:
+                rig.step(layer, ids)
         got = events_by_step(rig.cache.trace())
         E = tr["E"]
-        for i, (_, layer, ids, want) in enumerate(tr["steps"]):
+        accesses = [st for st in tr["steps"] if st[0] != "resize"]
+        for i, (_, layer, ids, want) in enumerate(accesses):
             want_k = [(e, h, s, None if ev is None else ev[0] * E + ev[1]) for e, h, s, ev in want]
             assert got[i] == want_k, (tr["name"], i)
         st = rig.cache.stats()
@@ -131,6 +142,44 @@ def test_random_multi_token_traces(env):
         steps.append((layer, np.array(ids, np.int32).reshape(-1)))
     steps.insert(40, (1, np.arange(12, dtype=np.int32)))   # 12 distinct > 9 slots -> capacity error
     _compare_run(rig, steps)
+    rig.cache.destroy()
+
+
+def test_resize_against_the_simulator(env):
+    """Shrink in place, grow into a new pool, shrink into a new pool, between random steps:
+    slot table, the bytes of every resident slot, later events and totals follow the oracle."""
+    ops, _ = env
+    rng = np.random.default_rng(17)
+    L, E = 3, 24
+    rig = Rig(ops, L, E, 12)
+    sim = ExpertLRU(L, E, 12)
+
+    def check_resident():
+        for (layer, e), slot in sim.where.items():
+            assert rig.cache.lookup(layer, e) == slot
+            assert torch.equal(rig.pool[slot].cpu(), rig.bank[layer * E + e])
+        n_res = sum(rig.cache.lookup(l, e) >= 0 for l in range(L) for e in range(E))
+        assert n_res == len(sim.where)
+
+    plan = {25: (5, True), 50: (16, False), 80: (7, False), 95: (7, True)}
+    for t in range(120):
+        if t in plan:
+            C, in_place = plan[t]
+            sim.resize(C)
+            rig.resize(C, in_place)
+            check_resident()
+        layer = int(rng.integers(L))
+        ids = rng.choice(E, size=int(rng.integers(1, 4)), replace=False).astype(np.int32)
+        want = sim.step(layer, ids)
+        rig.step(layer, ids)
+        torch.cuda.synchronize()
+        assert rig.slot_of.cpu().numpy().tolist() == sim.slot_of_expert(layer)
+        for ev in want:
+            if not ev.hit:
+                assert torch.equal(rig.pool[ev.slot].cpu(), rig.bank[layer * E + ev.expert])
+    st = rig.cache.stats()
+    assert (st["accesses"], st["hits"], st["misses"], st["evictions"]) == \
+        (sim.accesses, sim.hits, sim.misses, sim.evictions)
     rig.cache.destroy()
 
 
