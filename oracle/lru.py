@@ -34,6 +34,16 @@ most recently used entries and drops the rest (counted as evictions); the
 kept entries move to slots 0, 1, ... in ascending order of their old slot
 (never to a higher slot, so the move is safe in place), keep their stamps,
 and the clock is unchanged; new slots are empty.
+
+Full-layer prefetch: in prefill the runtime double-buffers whole layers --
+while the GPU computes one layer, the experts of the next are streamed over
+PCIe, when the cache has room for them (FreeToken linux page, "Cómo gestiona
+FreeToken la memoria MoE"; FreeToken rtx 4090 page, "Prefill"; FreeToken 290b
+model page, "Cómo gestiona FreeToken el prellenado y la decodificación"), in
+the same cache that serves decode (FreeToken linux page, same section).
+Reading taken here: a prefetch of layer l updates the LRU exactly like a step
+of layer l whose needed set is all of its experts, but it is not a routed
+access: it adds fills and evictions, not accesses, hits or misses.
 """
 from __future__ import annotations
 
@@ -75,6 +85,7 @@ class ExpertLRU:
         self.hits = 0
         self.misses = 0
         self.evictions = 0
+        self.prefetch_fills = 0
 
     def lookup(self, layer: int, expert: int) -> int:
         """Slot holding (layer, expert), or -1."""
@@ -82,6 +93,20 @@ class ExpertLRU:
 
     def step(self, layer: int, ids) -> list[Event]:
         """Serve one layer of one step; returns events in ascending expert id."""
+        needed = self._needed(layer, ids)
+        events = self._serve(layer, needed)
+        self.accesses += len(needed)
+        self.hits += sum(1 for ev in events if ev.hit)
+        self.misses += sum(1 for ev in events if not ev.hit)
+        return events
+
+    def prefetch(self, layer: int) -> list[Event]:
+        """Bring every expert of ``layer`` in (full-layer prefetch); events ascending."""
+        events = self._serve(layer, self._needed(layer, range(self.n_experts)))
+        self.prefetch_fills += sum(1 for ev in events if not ev.hit)
+        return events
+
+    def _needed(self, layer: int, ids) -> list[int]:
         if not 0 <= layer < self.n_layers:
             raise ValueError("layer out of range")
         needed = sorted({int(e) for e in list(ids)})
@@ -90,7 +115,9 @@ class ExpertLRU:
                 raise ValueError("expert id out of range")
         if len(needed) > self.capacity:
             raise CapacityError(f"{len(needed)} distinct experts > {self.capacity} slots")
+        return needed
 
+    def _serve(self, layer: int, needed: list[int]) -> list[Event]:
         events: dict[int, Event] = {}
         # Phase 1: every hit becomes most recently used, ascending expert id.
         for e in needed:
@@ -120,10 +147,6 @@ class ExpertLRU:
             self.clock += 1
             self.stamp[best] = self.clock
             events[e] = Event(e, False, best, evicted)
-
-        self.accesses += len(needed)
-        self.hits += sum(1 for ev in events.values() if ev.hit)
-        self.misses += sum(1 for ev in events.values() if not ev.hit)
         return [events[e] for e in needed]
 
     def resize(self, capacity: int) -> tuple[list[tuple[int, int]], list[tuple]]:

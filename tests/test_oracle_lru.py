@@ -38,6 +38,20 @@ def _traces(golden_dir):
                         s, evicted = rest, None
                     evs.append((int(e), hm == "H", int(s), evicted))
                 cur["steps"].append((int(lw[1]), int(lw[3]), ids, evs))
+            elif w[0] == "prefetch":
+                left, right = line.split(":", 1)
+                evs = []
+                for tok in right.split():
+                    e, rest = tok.split(":")
+                    hm, rest = rest.split("@")
+                    if "/" in rest:
+                        s_, ev = rest.split("/")
+                        evl, eve = ev.split(".")
+                        evicted = (int(evl), int(eve))
+                    else:
+                        s_, evicted = rest, None
+                    evs.append((int(e), hm == "H", int(s_), evicted))
+                cur["steps"].append(("prefetch", int(left.split()[1]), None, evs))
             elif w[0] == "resize":
                 left, right = line.split(":", 1)
                 rw = right.split()
@@ -56,16 +70,16 @@ def _traces(golden_dir):
 
 def test_hand_traced_sequences(golden_dir):
     traces = _traces(golden_dir)
-    assert [t["name"] for t in traces] == ["A", "B", "C", "D", "E"]
+    assert [t["name"] for t in traces] == ["A", "B", "C", "D", "E", "F"]
     for tr in traces:
         lru = ExpertLRU(tr["L"], tr["E"], tr["C"])
         for step, layer, ids, want in tr["steps"]:
             if step == "resize":
                 assert lru.resize(layer) == (ids, want), (tr["name"], "resize", layer)
                 continue
-            got = lru.step(layer, ids)
+            got = lru.prefetch(layer) if step == "prefetch" else lru.step(layer, ids)
             assert [(e.expert, e.hit, e.slot, e.evicted) for e in got] == want, (tr["name"], step, layer)
-        assert lru.stats() == tr["totals"], tr["name"]
+        assert {k: getattr(lru, k) for k in tr["totals"]} == tr["totals"], tr["name"]
         assert lru.stamp == tr["stamps"], tr["name"]
 
 
@@ -179,6 +193,23 @@ def test_resize_grow_moves_nothing_and_shrink_never_moves_up():
     moves, dropped = lru.resize(7)
     assert len(dropped) == 13 and all(b <= a for a, b in moves)
     assert lru.evictions >= 13 and len(lru.where) == 7 and lru.owner.count(None) == 0
+
+
+def test_prefetched_layer_steps_are_all_hits():
+    # with room for two layers and the order route(l) -> prefetch(l+1) -> compute(l),
+    # every routed access of layer l+1 is a hit, whatever its routing, and a prefetch
+    # never evicts the layer being computed
+    rng = np.random.default_rng(13)
+    L, E = 5, 10
+    lru = ExpertLRU(L, E, 2 * E)
+    lru.prefetch(0)
+    for l in range(L):
+        ids = rng.integers(0, E, size=12)
+        assert all(ev.hit for ev in lru.step(l, ids))
+        if l + 1 < L:
+            evs = lru.prefetch(l + 1)
+            assert all(ev.evicted is None or ev.evicted[0] != l for ev in evs)
+    assert lru.misses == 0 and lru.prefetch_fills == L * E
 
 
 def test_miss_split_policy():
