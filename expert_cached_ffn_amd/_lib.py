@@ -22,7 +22,7 @@ EXPORTS = [
     "ft_moe_grouped_ffn", "ft_moe_combine", "ft_expert_cache_create", "ft_expert_cache_step",
     "ft_expert_cache_stats", "ft_expert_cache_trace", "ft_expert_cache_lookup",
     "ft_expert_cache_destroy", "ft_workspace_bytes", "ft_mxfp8_quantize", "ft_moe_route_permute",
-    "ft_expert_cache_resize",
+    "ft_expert_cache_resize", "ft_expert_cache_prefetch_layer",
 ]
 
 
@@ -37,7 +37,7 @@ class ExpertLayout(C.Structure):
 
 class CacheStats(C.Structure):
     _fields_ = [(n, C.c_uint64) for n in
-                ("accesses", "hits", "misses", "evictions", "bytes_h2d", "steps")]
+                ("accesses", "hits", "misses", "evictions", "bytes_h2d", "steps", "prefetch_fills")]
 
 
 class CacheEvent(C.Structure):
@@ -73,6 +73,8 @@ def lib() -> C.CDLL:
     L.ft_moe_grouped_ffn.restype = i32
     L.ft_moe_grouped_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, p, p, i32, i32, i32, i32, p, p, p, p,
                                      i32, p, sz, p]
+    L.ft_expert_cache_prefetch_layer.restype = i32
+    L.ft_expert_cache_prefetch_layer.argtypes = [p, i32, p]
     L.ft_expert_cache_resize.restype = i32
     L.ft_expert_cache_resize.argtypes = [p, i32, p, p]
     L.ft_moe_route_permute.restype = i32

@@ -229,6 +229,9 @@ struct ft_expert_cache {
   hipStream_t copy_stream;
   hipStream_t fill[kFillStreams];   // fill[0] = copy_stream; the others are the cache's own
   hipEvent_t ev_fill[kFillStreams];
+  bool pending[kFillStreams];       // a layer prefetch's fills on this queue not yet waited for
+  int32_t *iota;                    // device [E]: 0..E-1 (the needed set of a layer prefetch)
+  int32_t *pf_slots;                // device [E]: slot table a prefetch writes (unused)
   LruState st;
   void *dev_state;
   LruResult *res_host;   // pinned
@@ -281,6 +284,7 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
       if (c->ev_fill[i]) (void)hipEventDestroy(c->ev_fill[i]);
     }
     if (c->dev_state) (void)hipFree(c->dev_state);
+    if (c->iota) (void)hipFree(c->iota);
     if (c->res_host) (void)hipHostFree(c->res_host);
     if (c->ev_lru) (void)hipEventDestroy(c->ev_lru);
     if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
@@ -312,9 +316,95 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
       return cleanup(FT_EHIP, "ft_expert_cache_create: stream or event creation failed");
   }
   if (hipDeviceSynchronize() != hipSuccess) return cleanup(FT_EHIP, "ft_expert_cache_create: sync failed");
+  {
+    std::vector<int32_t> iota(E);
+    for (int e = 0; e < E; ++e) iota[e] = e;
+    if (hipMalloc(&c->iota, size_t(E) * 8) != hipSuccess)
+      return cleanup(FT_EHIP, "ft_expert_cache_create: hipMalloc failed");
+    c->pf_slots = c->iota + E;
+    if (hipMemcpy(c->iota, iota.data(), size_t(E) * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return cleanup(FT_EHIP, "ft_expert_cache_create: hipMemcpy failed");
+  }
   c->stats = ft_cache_stats{};
   c->map_mirror.assign(keys, -1);
   *out = c;
+  clear_error();
+  return FT_OK;
+}
+
+// One LRU update (a step, or a layer prefetch with every expert of the layer
+// needed) and its fills.
+static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *ids, int R, int32_t *slot_of_expert,
+                             hipStream_t compute_stream, bool prefetch, const char *who) {
+  c->res_host->status = -1;
+  hipLaunchKernelGGL(lru_step_kernel, dim3(1), dim3(kLruThreads), 0, compute_stream, c->st, layer, ids, R, c->E,
+                     c->C, slot_of_expert, c->res_dev);
+  FT_LAUNCHED("lru_step_kernel");
+  FT_HIP(hipEventRecord(c->ev_lru, compute_stream));
+  FT_HIP(hipEventSynchronize(c->ev_lru));
+  const LruResult &r = *c->res_host;
+  if (r.status == LRU_BAD_ID) return fail(FT_EINVAL, std::string(who) + ": expert id out of range");
+  if (r.status == LRU_CAPACITY)
+    return fail(FT_ECAPACITY, std::string(who) + ": " + std::to_string(r.n_needed) + " distinct experts > " +
+                                  std::to_string(c->C) + " slots");
+  if (r.status != LRU_OK) return fail(FT_EHIP, std::string(who) + ": LRU kernel did not report");
+  // Fills that an earlier layer prefetch left in flight come first: the compute
+  // stream waits for them (its reads) and so does every queue this call uses
+  // (a slot refilled here may be one the prefetch is still writing).
+  bool had_pending = false;
+  for (int q = 0; q < kFillStreams; ++q) had_pending |= c->pending[q];
+  if (had_pending && !prefetch) {
+    for (int q = 0; q < kFillStreams; ++q)
+      if (c->pending[q]) FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
+  }
+  const int32_t step = int32_t(c->stats.steps);
+  const uint64_t eb = c->L.expert_bytes;
+  // Fills go round-robin over kFillStreams copy queues (one queue does not
+  // reach the host link's bandwidth).  Each queue first waits for the compute
+  // stream up to the LRU kernel: a victim slot may still be read by earlier
+  // work enqueued there.
+  int fills = 0;
+  bool used[kFillStreams] = {};
+  for (int i = 0; i < r.n_needed; ++i) {
+    const int e = r.ev[i][0], hit = r.ev[i][1], s = r.ev[i][2], ek = r.ev[i][3];
+    c->log.push_back(ft_cache_event{step, layer, e, prefetch ? (hit ? 3 : 2) : hit, s, ek});
+    if (hit) continue;
+    if (ek >= 0) c->map_mirror[size_t(ek)] = -1;
+    c->map_mirror[size_t(layer) * c->E + e] = s;
+    const uint8_t *src = c->bank + (uint64_t(layer) * c->E + e) * eb;
+    const int q = fills % kFillStreams;
+    if (!used[q]) {
+      FT_HIP(hipStreamWaitEvent(c->fill[q], c->ev_lru, 0));
+      if (had_pending)
+        for (int q2 = 0; q2 < kFillStreams; ++q2)
+          if (c->pending[q2] && q2 != q) FT_HIP(hipStreamWaitEvent(c->fill[q], c->ev_fill[q2], 0));
+      used[q] = true;
+    }
+    FT_HIP(hipMemcpyAsync(c->pool + uint64_t(s) * eb, src, eb, hipMemcpyHostToDevice, c->fill[q]));
+    ++fills;
+  }
+  if (prefetch) {
+    // left in flight; the next step waits for them
+    for (int q = 0; q < kFillStreams; ++q)
+      if (used[q]) {
+        FT_HIP(hipEventRecord(c->ev_fill[q], c->fill[q]));
+        c->pending[q] = true;
+      }
+    c->stats.prefetch_fills += uint64_t(fills);
+  } else {
+    for (int q = 0; q < kFillStreams; ++q) c->pending[q] = false;  // waited for above
+    for (int q = 0; q < kFillStreams; ++q) {
+      if (!used[q]) continue;
+      FT_HIP(hipEventRecord(c->ev_fill[q], c->fill[q]));
+      FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
+    }
+    c->stats.accesses += uint64_t(r.n_needed);
+    c->stats.hits += uint64_t(r.n_hits);
+    c->stats.misses += uint64_t(r.n_misses);
+    c->stats.steps += 1;
+  }
+  c->stats.evictions += uint64_t(r.n_evictions);
+  c->stats.bytes_h2d += uint64_t(fills) * eb;
   clear_error();
   return FT_OK;
 }
@@ -328,54 +418,13 @@ extern "C" ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, con
   FT_REQUIRE(slot_of_expert != nullptr, "ft_expert_cache_step: slot_of_expert is NULL");
   const int R = T * k;
   FT_REQUIRE(R == 0 || topk_ids != nullptr, "ft_expert_cache_step: topk_ids is NULL");
-  c->res_host->status = -1;
-  hipLaunchKernelGGL(lru_step_kernel, dim3(1), dim3(kLruThreads), 0, compute_stream, c->st, layer, topk_ids, R,
-                     c->E, c->C, slot_of_expert, c->res_dev);
-  FT_LAUNCHED("lru_step_kernel");
-  FT_HIP(hipEventRecord(c->ev_lru, compute_stream));
-  FT_HIP(hipEventSynchronize(c->ev_lru));
-  const LruResult &r = *c->res_host;
-  if (r.status == LRU_BAD_ID) return fail(FT_EINVAL, "ft_expert_cache_step: expert id out of range");
-  if (r.status == LRU_CAPACITY)
-    return fail(FT_ECAPACITY, "ft_expert_cache_step: " + std::to_string(r.n_needed) + " distinct experts > " +
-                                  std::to_string(c->C) + " slots");
-  if (r.status != LRU_OK) return fail(FT_EHIP, "ft_expert_cache_step: LRU kernel did not report");
-  const int32_t step = int32_t(c->stats.steps);
-  const uint64_t eb = c->L.expert_bytes;
-  // Fills go round-robin over kFillStreams copy queues (one queue does not
-  // reach the host link's bandwidth).  Each queue first waits for the compute
-  // stream up to the LRU kernel: a victim slot may still be read by earlier
-  // work enqueued there.  The compute stream then waits for every queue used.
-  int fills = 0;
-  bool used[kFillStreams] = {};
-  for (int i = 0; i < r.n_needed; ++i) {
-    const int e = r.ev[i][0], hit = r.ev[i][1], s = r.ev[i][2], ek = r.ev[i][3];
-    c->log.push_back(ft_cache_event{step, layer, e, hit, s, ek});
-    if (hit) continue;
-    if (ek >= 0) c->map_mirror[size_t(ek)] = -1;
-    c->map_mirror[size_t(layer) * c->E + e] = s;
-    const uint8_t *src = c->bank + (uint64_t(layer) * c->E + e) * eb;
-    const int q = fills % kFillStreams;
-    if (!used[q]) {
-      FT_HIP(hipStreamWaitEvent(c->fill[q], c->ev_lru, 0));
-      used[q] = true;
-    }
-    FT_HIP(hipMemcpyAsync(c->pool + uint64_t(s) * eb, src, eb, hipMemcpyHostToDevice, c->fill[q]));
-    ++fills;
-  }
-  for (int q = 0; q < kFillStreams; ++q) {
-    if (!used[q]) continue;
-    FT_HIP(hipEventRecord(c->ev_fill[q], c->fill[q]));
-    FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
-  }
-  c->stats.accesses += uint64_t(r.n_needed);
-  c->stats.hits += uint64_t(r.n_hits);
-  c->stats.misses += uint64_t(r.n_misses);
-  c->stats.evictions += uint64_t(r.n_evictions);
-  c->stats.bytes_h2d += uint64_t(fills) * eb;
-  c->stats.steps += 1;
-  clear_error();
-  return FT_OK;
+  return cache_serve(c, layer, topk_ids, R, slot_of_expert, compute_stream, false, "ft_expert_cache_step");
+}
+
+extern "C" ft_status ft_expert_cache_prefetch_layer(ft_expert_cache *c, int32_t layer, hipStream_t compute_stream) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_prefetch_layer: cache is NULL");
+  FT_REQUIRE(layer >= 0 && layer < c->n_layers, "ft_expert_cache_prefetch_layer: layer out of range");
+  return cache_serve(c, layer, c->iota, c->E, c->pf_slots, compute_stream, true, "ft_expert_cache_prefetch_layer");
 }
 
 // Resize at a safe point (the pages: the runtime resizes and rebuilds the GPU
@@ -400,6 +449,7 @@ extern "C" ft_status ft_expert_cache_resize(ft_expert_cache *c, int32_t new_capa
   FT_REQUIRE(pa.type == hipMemoryTypeDevice, "ft_expert_cache_resize: new_slot_pool is not device memory");
   for (int q = 0; q < kFillStreams; ++q) FT_HIP(hipStreamSynchronize(c->fill[q]));
   FT_HIP(hipStreamSynchronize(stream));
+  for (int q = 0; q < kFillStreams; ++q) c->pending[q] = false;  // every fill has landed
   const int C = c->C, C2 = new_capacity;
   const size_t keys = size_t(c->n_layers) * c->E;
   std::vector<uint64_t> stamp(C);
@@ -507,6 +557,7 @@ extern "C" ft_status ft_expert_cache_destroy(ft_expert_cache *c) {
     (void)hipEventDestroy(c->ev_fill[q]);
   }
   (void)hipFree(c->dev_state);
+  (void)hipFree(c->iota);
   (void)hipHostFree(c->res_host);
   (void)hipEventDestroy(c->ev_lru);
   (void)hipEventDestroy(c->ev_copy);

@@ -115,6 +115,11 @@ class ExpertCache:
 
     step = ft_expert_cache_step
 
+    def ft_expert_cache_prefetch_layer(self, layer: int, stream=None) -> None:
+        _check(_lib.lib().ft_expert_cache_prefetch_layer(self._h, layer, _stream(stream)))
+
+    prefetch_layer = ft_expert_cache_prefetch_layer
+
     def ft_expert_cache_resize(self, capacity: int, slot_pool, stream=None) -> None:
         _check(_lib.lib().ft_expert_cache_resize(self._h, capacity, _ptr(slot_pool), _stream(stream)))
         self.capacity = capacity

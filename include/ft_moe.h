@@ -265,16 +265,18 @@ typedef struct ft_expert_cache ft_expert_cache;  /* opaque */
 typedef struct {
   uint64_t accesses;   /* distinct (layer, expert) reads, summed over steps */
   uint64_t hits, misses, evictions;
-  uint64_t bytes_h2d;  /* bytes copied host -> device by miss fills         */
+  uint64_t bytes_h2d;  /* bytes copied host -> device (miss and prefetch fills) */
   uint64_t steps;      /* successful ft_expert_cache_step calls             */
+  uint64_t prefetch_fills;  /* entries brought in by ft_expert_cache_prefetch_layer */
 } ft_cache_stats;
 
-/* One cache event, as recorded by the step that produced it. */
+/* One cache event, as recorded by the step (or layer prefetch) that produced it. */
 typedef struct {
-  int32_t step;        /* index of the ft_expert_cache_step call (from 0)    */
+  int32_t step;        /* index of the ft_expert_cache_step call (from 0); a
+                          prefetch records the number of steps before it    */
   int32_t layer;
   int32_t expert;
-  int32_t hit;         /* 1 hit, 0 miss                                      */
+  int32_t hit;         /* 1 hit, 0 miss; prefetch: 3 already resident, 2 filled */
   int32_t slot;
   int32_t evicted;     /* key layer*E + expert of the entry evicted, or -1    */
 } ft_cache_event;
@@ -332,6 +334,25 @@ ft_status ft_expert_cache_trace(const ft_expert_cache *c, void *host_buf, size_t
  * completed step (-1 if not resident), written to *slot (host). */
 ft_status ft_expert_cache_lookup(const ft_expert_cache *c, int32_t layer, int32_t expert,
                                  int32_t *slot);
+
+/*
+ * ft_expert_cache_prefetch_layer -- bring every expert of `layer` into the
+ * cache ahead of its step: full-layer double buffering in prefill (while the
+ * GPU computes one layer, the next layer's experts stream over PCIe, when the
+ * cache has room: FreeToken linux page, "Cómo gestiona FreeToken la memoria
+ * MoE"; FreeToken 290b model page, "Cómo gestiona FreeToken el prellenado y la
+ * decodificación"; the same cache serves prefill and decode).  The LRU is
+ * updated as by a step of `layer` whose routing uses all E experts, but the
+ * prefetch is not a routed access: it adds fills, bytes and evictions, not
+ * accesses, hits or misses.  The LRU kernel runs on compute_stream (the host
+ * waits for it, as in a step); the fills go to the copy queues and are NOT
+ * waited for here: the next ft_expert_cache_step makes its compute stream
+ * (and its own fills) wait for them.  Intended order per layer l: step(l),
+ * prefetch(l+1), then the FFN of layer l -- with room for two layers the
+ * prefetch then evicts only entries of earlier layers.
+ * Errors: E > capacity -> FT_ECAPACITY (cache unchanged); as for a step.
+ */
+ft_status ft_expert_cache_prefetch_layer(ft_expert_cache *c, int32_t layer, hipStream_t compute_stream);
 
 /*
  * ft_expert_cache_resize -- change the number of slots at a safe point (the

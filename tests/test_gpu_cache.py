@@ -66,19 +66,23 @@ def test_hand_traced_sequences_on_device(env, golden_dir):
     for tr in _traces(golden_dir):
         print(f"trace {tr['name']}", flush=True)
         rig = Rig(ops, tr["L"], tr["E"], tr["C"], fill=False)
-        for kind, layer, ids, _ in tr["steps"]:
+        E = tr["E"]
+        want, n_steps = [], 0
+        for kind, layer, ids, evs in tr["steps"]:
             if kind == "resize":
                 rig.resize(layer, in_place=layer <= rig.C)
+                continue
+            if kind == "prefetch":
+                rig.cache.prefetch_layer(layer)
+                code = {True: 3, False: 2}
             else:
                 rig.step(layer, ids)
-        got = events_by_step(rig.cache.trace())
-        E = tr["E"]
-        accesses = [st for st in tr["steps"] if st[0] != "resize"]
-        for i, (_, layer, ids, want) in enumerate(accesses):
-            want_k = [(e, h, s, None if ev is None else ev[0] * E + ev[1]) for e, h, s, ev in want]
-            assert got[i] == want_k, (tr["name"], i)
+                code = {True: 1, False: 0}
+            want += [(n_steps, layer, e, code[h], s, -1 if ev is None else ev[0] * E + ev[1]) for e, h, s, ev in evs]
+            n_steps += kind != "prefetch"
+        assert rig.cache.trace() == want, tr["name"]
         st = rig.cache.stats()
-        assert {k: st[k] for k in ("accesses", "hits", "misses", "evictions")} == tr["totals"]
+        assert {k: st[k] for k in tr["totals"]} == tr["totals"]
         rig.cache.destroy()
 
 
@@ -262,4 +266,53 @@ def test_layer_outputs_through_the_cache(env):
             check_close(got[None, :], ref[None, :], bf16_out=True, what=f"step {s} layer {l}")
     st = cache.stats()
     assert st["misses"] > 0 and st["hits"] > 0
+    cache.destroy()
+
+
+def test_prefill_double_buffered_through_the_cache(env):
+    """Full-layer double buffering: route(l) -> cache step(l) -> prefetch(l+1) -> FFN(l) from the slots.
+    With room for two layers every routed access hits; outputs match the oracle; LRU events match."""
+    ops, Lm = env
+    cfg = synth.shrink(synth.CONFIGS[4], H=512, I=512, E=16, k=4, n_layers=3, capacity=32)
+    T = 200
+    shape = Lm.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize, True)
+    layer = Lm.MoELayer(shape, T)
+    lay = layer.layout
+    eb = int(lay.expert_bytes)
+    ex = [Experts(cfg, l) for l in range(cfg.n_layers)]
+    bank = torch.empty((cfg.n_layers * cfg.E, eb), dtype=torch.uint8, pin_memory=True)
+    for l in range(cfg.n_layers):
+        for e in range(cfg.E):
+            Lm.pack_expert(lay, ex[l].raw(e).arrays, bank.numpy()[l * cfg.E + e])
+    shared = [Lm.as_device_u8([Lm.pack_expert(lay, ex[l].raw(cfg.E).arrays)])[0] for l in range(cfg.n_layers)]
+    pool = torch.zeros((cfg.capacity, eb), dtype=torch.uint8, device="cuda")
+    cache = ops.ExpertCache(lay, cfg.n_layers, cfg.E, cfg.capacity, pool, bank, torch.cuda.Stream())
+    slot_of = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    sim = ExpertLRU(cfg.n_layers, cfg.E, cfg.capacity)
+    cache.prefetch_layer(0)
+    sim.prefetch(0)
+    for l in range(cfg.n_layers):
+        print(f"prefill layer {l}", flush=True)
+        x = synth.tokens(cfg, T, layer=l)
+        logits = synth.prefill_logits(cfg, T, layer=l)
+        layer.route_permute(T, logits=Lm.to_device(logits))
+        cache.step(l, layer.ids, T, cfg.k, slot_of)
+        ids = moe.topk(logits, cfg.k)
+        assert all(ev.hit for ev in sim.step(l, ids.ravel()))
+        if l + 1 < cfg.n_layers:
+            cache.prefetch_layer(l + 1)
+            sim.prefetch(l + 1)
+        layer.ffn(T, Lm.to_device(x), pool, slot_of_expert=slot_of, shared_blob=shared[l])
+        layer.combine(T)
+        torch.cuda.synchronize()
+        got = formats.bf16_to_f64(layer.out[:T].cpu().numpy().view(np.uint16))
+        w = moe.gating_weights(logits, ids, cfg.gating, cfg.renormalize)
+        x64 = formats.activations_to_f64(cfg.xdtype, x)
+        toks = [0, 77, T - 1]
+        ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex[l].f64, ex[l].f64(cfg.E)) for t in toks])
+        check_close(got[toks], ref, bf16_out=True, what=f"layer {l}")
+    st = cache.stats()
+    assert st["misses"] == 0 and st["hits"] == st["accesses"] == sim.accesses
+    assert st["prefetch_fills"] == sim.prefetch_fills == cfg.n_layers * cfg.E
+    assert st["evictions"] == sim.evictions and st["bytes_h2d"] == cfg.n_layers * cfg.E * eb
     cache.destroy()
