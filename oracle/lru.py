@@ -35,6 +35,14 @@ kept entries move to slots 0, 1, ... in ascending order of their old slot
 (never to a higher slot, so the move is safe in place), keep their stamps,
 and the clock is unchanged; new slots are empty.
 
+Hybrid execution: a step's misses are either filled into the GPU cache or
+run on the CPU, by a split derived from measured bandwidths (FreeToken 290b
+model page, "Ejecución híbrida" and "Cómo gestiona FreeToken el prellenado y
+la decodificación"; the count is `policy.miss_split`).  Reading taken here:
+the lowest expert ids among the misses are filled (as `policy.split_misses`);
+the others stay non-resident -- no slot, no eviction, no recency -- and are
+still misses.
+
 Full-layer prefetch: in prefill the runtime double-buffers whole layers --
 while the GPU computes one layer, the experts of the next are streamed over
 PCIe, when the cache has room for them (FreeToken linux page, "Cómo gestiona
@@ -86,15 +94,19 @@ class ExpertLRU:
         self.misses = 0
         self.evictions = 0
         self.prefetch_fills = 0
+        self.cpu_misses = 0
 
     def lookup(self, layer: int, expert: int) -> int:
         """Slot holding (layer, expert), or -1."""
         return self.where.get((layer, expert), -1)
 
-    def step(self, layer: int, ids) -> list[Event]:
-        """Serve one layer of one step; returns events in ascending expert id."""
+    def step(self, layer: int, ids, fill_limit: int | None = None) -> list[Event]:
+        """Serve one layer of one step; returns events in ascending expert id.
+
+        fill_limit: at most this many of the step's misses (the lowest ids) are
+        filled; the others run on the CPU (events with slot -1)."""
         needed = self._needed(layer, ids)
-        events = self._serve(layer, needed)
+        events = self._serve(layer, needed, fill_limit)
         self.accesses += len(needed)
         self.hits += sum(1 for ev in events if ev.hit)
         self.misses += sum(1 for ev in events if not ev.hit)
@@ -117,7 +129,7 @@ class ExpertLRU:
             raise CapacityError(f"{len(needed)} distinct experts > {self.capacity} slots")
         return needed
 
-    def _serve(self, layer: int, needed: list[int]) -> list[Event]:
+    def _serve(self, layer: int, needed: list[int], fill_limit: int | None = None) -> list[Event]:
         events: dict[int, Event] = {}
         # Phase 1: every hit becomes most recently used, ascending expert id.
         for e in needed:
@@ -129,9 +141,15 @@ class ExpertLRU:
         # Phase 2: each miss takes the least recently used slot that holds no
         # member of the needed set, ascending expert id.
         needed_keys = {(layer, e) for e in needed}
+        filled = 0
         for e in needed:
             if e in events:
                 continue
+            if fill_limit is not None and filled >= fill_limit:
+                events[e] = Event(e, False, -1, None)   # runs on the CPU
+                self.cpu_misses += 1
+                continue
+            filled += 1
             best = None
             for s in range(self.capacity):
                 if self.owner[s] in needed_keys:

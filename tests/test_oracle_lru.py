@@ -27,7 +27,12 @@ def _traces(golden_dir):
                 lw = left.split()
                 ids = [int(v) for v in lw[5].split(",")]
                 evs = []
-                for tok in right.split():
+                rt = right.split()
+                fill = None
+                if "fill" in rt:
+                    fill = int(rt[rt.index("fill") + 1])
+                    rt = rt[:rt.index("fill")]
+                for tok in rt:
                     e, rest = tok.split(":")
                     hm, rest = rest.split("@")
                     if "/" in rest:
@@ -38,6 +43,7 @@ def _traces(golden_dir):
                         s, evicted = rest, None
                     evs.append((int(e), hm == "H", int(s), evicted))
                 cur["steps"].append((int(lw[1]), int(lw[3]), ids, evs))
+                cur.setdefault("fill", {})[len(cur["steps"]) - 1] = fill
             elif w[0] == "prefetch":
                 left, right = line.split(":", 1)
                 evs = []
@@ -70,14 +76,15 @@ def _traces(golden_dir):
 
 def test_hand_traced_sequences(golden_dir):
     traces = _traces(golden_dir)
-    assert [t["name"] for t in traces] == ["A", "B", "C", "D", "E", "F"]
+    assert [t["name"] for t in traces] == ["A", "B", "C", "D", "E", "F", "G"]
     for tr in traces:
         lru = ExpertLRU(tr["L"], tr["E"], tr["C"])
-        for step, layer, ids, want in tr["steps"]:
+        for i, (step, layer, ids, want) in enumerate(tr["steps"]):
             if step == "resize":
                 assert lru.resize(layer) == (ids, want), (tr["name"], "resize", layer)
                 continue
-            got = lru.prefetch(layer) if step == "prefetch" else lru.step(layer, ids)
+            fill = tr.get("fill", {}).get(i)
+            got = lru.prefetch(layer) if step == "prefetch" else lru.step(layer, ids, fill)
             assert [(e.expert, e.hit, e.slot, e.evicted) for e in got] == want, (tr["name"], step, layer)
         assert {k: getattr(lru, k) for k in tr["totals"]} == tr["totals"], tr["name"]
         assert lru.stamp == tr["stamps"], tr["name"]
@@ -210,6 +217,34 @@ def test_prefetched_layer_steps_are_all_hits():
             evs = lru.prefetch(l + 1)
             assert all(ev.evicted is None or ev.evicted[0] != l for ev in evs)
     assert lru.misses == 0 and lru.prefetch_fills == L * E
+
+
+def test_fill_limit_split():
+    # an unlimited step is the plain step; the filled misses are the lowest ids;
+    # CPU misses leave the cache exactly as it was
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        a, b = ExpertLRU(2, 30, 8), ExpertLRU(2, 30, 8)
+        for t in range(30):
+            layer = int(rng.integers(2))
+            ids = rng.choice(30, size=int(rng.integers(1, 6)), replace=False)
+            ea = a.step(layer, ids)
+            eb = b.step(layer, ids, fill_limit=len(ids))
+            assert ea == eb
+        before = (dict(b.where), list(b.stamp), b.clock)
+        ids = rng.choice(30, size=6, replace=False)
+        misses = sorted(int(e) for e in ids if (0, int(e)) not in b.where)
+        evs = b.step(0, ids, fill_limit=0)
+        hits = [e for e in evs if e.hit]
+        assert [e.expert for e in evs if not e.hit] == misses and all(e.slot == -1 for e in evs if not e.hit)
+        if not hits:
+            assert (dict(b.where), list(b.stamp), b.clock) == before
+        q = int(rng.integers(0, len(misses) + 1))
+        c = ExpertLRU(1, 30, 8)
+        evs = c.step(0, ids, fill_limit=q)
+        filled = [e.expert for e in evs if not e.hit and e.slot >= 0]
+        assert filled == sorted(int(e) for e in ids)[:q]
+        assert c.cpu_misses == len(ids) - q and c.misses == len(ids)
 
 
 def test_miss_split_policy():
