@@ -358,13 +358,19 @@ def run_cache_trace(args, cfg):
     log(f"pinned H2D bandwidth B_p = {b_p:.1f} GB/s through the cache's fills "
         f"({b_p1:.1f} GB/s for back-to-back torch copies on one stream)")
 
-    def run(steps, cache):
+    n_threads = min(16, len(os.sched_getaffinity(0)))
+
+    def run(steps, cache, hybrid=False):
         for st in range(steps):
             for l in range(Lyr):
                 i = st * Lyr + l
                 layer.route_permute(1, logits=logits[i:i + 1])
                 cache.step(l, layer.ids, 1, cfg.k, slot_of)
+                if hybrid:
+                    layer.stage_cpu_misses(cache, 1, xs[i])
                 layer.ffn(1, xs[i], pool, slot_of_expert=slot_of, shared_blob=shared[l])
+                if hybrid:
+                    layer.run_cpu_misses(cache, n_threads=n_threads)
                 layer.combine(1)
 
     warm = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
@@ -394,6 +400,48 @@ def run_cache_trace(args, cfg):
     log(f"elastic resize: {C} -> {C // 2} slots in place {shrink_ms:.1f} ms, back to {C} {grow_ms:.1f} ms; "
         f"hit rate over 64 steps at {C // 2} slots {half_hit:.4f}")
     cache.destroy()
+    # hybrid miss execution: B_h of the host expert kernel (one token, distinct experts,
+    # so the weights stream from DRAM), then the same cold-start trace with the split on
+    x1 = xs[0][:1].cpu().numpy().view(np.uint16)
+    y1 = np.empty((1, cfg.H), np.float32)
+    ops.ft_cpu_expert_ffn(layer.layout, hb[0], x1, 1, y1, n_threads)
+    th = time.perf_counter()
+    n_h = 24
+    for j in range(n_h):
+        ops.ft_cpu_expert_ffn(layer.layout, hb[(j * 37 + 5) % (Lyr * E)], x1, 1, y1, n_threads)
+    b_h = n_h * eb / (time.perf_counter() - th) / 1e9
+    cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
+    cache.set_split(b_p, b_h)
+    run(min(args.warmup, S), cache, hybrid=True)  # warm the host path
+    torch.cuda.synchronize()
+    cache.destroy()
+    def hybrid_run(bh):
+        cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
+        cache.set_split(b_p, bh)
+        torch.cuda.synchronize()
+        t4 = time.perf_counter()
+        run(S, cache, hybrid=True)
+        torch.cuda.synchronize()
+        dth = time.perf_counter() - t4
+        sth = cache.stats()
+        cache.destroy()
+        in_loop = sth["cpu_misses"] * eb / max(1, sth["cpu_ns"])  # bytes/ns = GB/s
+        out = dict(tokens_per_s=S / dth, ms_per_step=dth / S * 1e3, b_h_split_GBps=bh,
+                   b_h_in_loop_GBps=in_loop, hit_rate=sth["hits"] / max(1, sth["accesses"]),
+                   cpu_misses_per_step=sth["cpu_misses"] / S,
+                   filled_per_step=(sth["misses"] - sth["cpu_misses"]) / S, bytes_h2d=sth["bytes_h2d"],
+                   speedup=(S / dth) / (S / dt))
+        log(f"hybrid miss execution, split at B_p {b_p:.1f} / B_h {bh:.1f} GB/s: {S / dth:.1f} tok/s "
+            f"({out['speedup']:.2f}x the fill-only run), hit rate {out['hit_rate']:.4f}, "
+            f"{out['cpu_misses_per_step']:.2f} misses/step on the CPU, {out['filled_per_step']:.2f} filled; "
+            f"CPU path in the loop {in_loop:.1f} GB/s")
+        return out
+    # the split from the stand-alone B_h, then again from the rate the whole CPU path (staging
+    # wait, expert kernel, copy back) reached in that run
+    first = hybrid_run(b_h)
+    second = hybrid_run(first["b_h_in_loop_GBps"])
+    hybrid = dict(b_h_standalone_GBps=b_h, cpu_threads=n_threads, cpu_isa=ops.ft_cpu_isa(-1),
+                  split_standalone=first, split_in_loop=second)
     hit = st["hits"] / max(1, st["accesses"])
     # lower bound of a step: resident expert reads at 8 TB/s vs fills at the measured B_p
     resident = Lyr * (cfg.k + 1) * eb
@@ -401,7 +449,7 @@ def run_cache_trace(args, cfg):
     res = dict(tokens_per_s=S / dt, ms_per_step=dt / S * 1e3, hit_rate=hit, misses_per_step=st["misses"] / S,
                bytes_h2d=st["bytes_h2d"], h2d_GBps=st["bytes_h2d"] / dt / 1e9, b_p_GBps=b_p,
                bound_ms_per_step=bound * 1e3, frac_of_bound=bound / (dt / S), stats=st, b_p_torch_copy_GBps=b_p1,
-               resize={"shrink_ms": shrink_ms, "grow_ms": grow_ms, "from_slots": C, "to_slots": C // 2,
+               hybrid=hybrid, resize={"shrink_ms": shrink_ms, "grow_ms": grow_ms, "from_slots": C, "to_slots": C // 2,
                        "hit_rate_64_steps_at_half": half_hit})
     log(f"cache trace: {S} steps x {Lyr} layers in {dt:.2f}s = {S / dt:.1f} tok/s, hit rate {hit:.4f}, "
         f"{res['misses_per_step']:.2f} misses/step, fills {res['h2d_GBps']:.1f} GB/s (B_p {b_p:.1f}), "

@@ -15,6 +15,7 @@ FT_F32, FT_BF16, FT_MXFP4 = 0, 1, 2
 FT_SOFTMAX, FT_SIGMOID = 0, 1
 FT_WS_PERMUTE, FT_WS_FFN, FT_WS_ROUTE_PERMUTE = 1, 2, 3
 FT_FFN_EXACT, FT_FFN_NATIVE_MX = 0, 1
+FT_CPU_ISA_QUERY, FT_CPU_ISA_BEST, FT_CPU_AVX2, FT_CPU_AVX512_BF16 = -1, 0, 1, 2
 FT_FFN_GATE_UP_ONLY, FT_FFN_DOWN_ONLY = 0x100, 0x200
 
 EXPORTS = [
@@ -22,7 +23,9 @@ EXPORTS = [
     "ft_moe_grouped_ffn", "ft_moe_combine", "ft_expert_cache_create", "ft_expert_cache_step",
     "ft_expert_cache_stats", "ft_expert_cache_trace", "ft_expert_cache_lookup",
     "ft_expert_cache_destroy", "ft_workspace_bytes", "ft_mxfp8_quantize", "ft_moe_route_permute",
-    "ft_expert_cache_resize", "ft_expert_cache_prefetch_layer",
+    "ft_expert_cache_resize", "ft_expert_cache_prefetch_layer", "ft_expert_cache_set_split",
+    "ft_expert_cache_cpu_misses", "ft_cpu_expert_ffn", "ft_cpu_miss_rows", "ft_cpu_isa",
+    "ft_expert_cache_stage_cpu_misses", "ft_expert_cache_run_cpu_misses",
 ]
 
 
@@ -37,7 +40,8 @@ class ExpertLayout(C.Structure):
 
 class CacheStats(C.Structure):
     _fields_ = [(n, C.c_uint64) for n in
-                ("accesses", "hits", "misses", "evictions", "bytes_h2d", "steps", "prefetch_fills")]
+                ("accesses", "hits", "misses", "evictions", "bytes_h2d", "steps", "prefetch_fills",
+                 "cpu_misses", "cpu_ns")]
 
 
 class CacheEvent(C.Structure):
@@ -73,6 +77,20 @@ def lib() -> C.CDLL:
     L.ft_moe_grouped_ffn.restype = i32
     L.ft_moe_grouped_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, p, p, i32, i32, i32, i32, p, p, p, p,
                                      i32, p, sz, p]
+    L.ft_cpu_expert_ffn.restype = i32
+    L.ft_cpu_expert_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, i32, p, i32]
+    L.ft_cpu_miss_rows.restype = i32
+    L.ft_cpu_isa.restype = i32
+    L.ft_expert_cache_stage_cpu_misses.restype = i32
+    L.ft_expert_cache_stage_cpu_misses.argtypes = [p, p, i32, i32, i32, p, p, p]
+    L.ft_expert_cache_run_cpu_misses.restype = i32
+    L.ft_expert_cache_run_cpu_misses.argtypes = [p, p, p, i32]
+    L.ft_cpu_isa.argtypes = [i32, p]
+    L.ft_cpu_miss_rows.argtypes = [C.POINTER(ExpertLayout), p, i32, i32, p, i32, p, p, i32, i32, p, p, i32]
+    L.ft_expert_cache_set_split.restype = i32
+    L.ft_expert_cache_set_split.argtypes = [p, C.c_double, C.c_double]
+    L.ft_expert_cache_cpu_misses.restype = i32
+    L.ft_expert_cache_cpu_misses.argtypes = [p, p, i32, p]
     L.ft_expert_cache_prefetch_layer.restype = i32
     L.ft_expert_cache_prefetch_layer.argtypes = [p, i32, p]
     L.ft_expert_cache_resize.restype = i32

@@ -2,8 +2,10 @@
 
     python -m expert_cached_ffn_amd.build        # or __graft_entry__.build()
 
-Every ``csrc/*.hip`` file is compiled with hipcc for gfx950 (one object per
-file, in parallel) and linked into ``expert_cached_ffn_amd/libftmoe.so``.
+Every ``csrc/*.hip`` file is compiled with hipcc for gfx950 and every
+``csrc/*.cpp`` file (host code: the CPU expert kernel) with the host compiler
+for x86-64-v3 (AVX2 + FMA), one object per file, in parallel, and linked into
+``expert_cached_ffn_amd/libftmoe.so``.
 """
 from __future__ import annotations
 
@@ -31,9 +33,19 @@ CFLAGS = [
 ]
 
 
+CXX = shutil.which("g++") or "g++"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", "-march=x86-64-v3", "-I", os.path.join(ROOT, "include"),
+            "-I", os.path.join(ROCM, "include"), "-D__HIP_PLATFORM_AMD__",
+            "-Wall", "-Wno-unused-function"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
@@ -45,14 +57,14 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     """Compile every HIP source and link the library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -16,6 +16,7 @@
 // the least recently used slot that holds no member of the step's set (empty
 // slots are oldest, lowest index first).
 #include <algorithm>
+#include <chrono>
 #include <vector>
 
 #include "ft_internal.hpp"
@@ -33,8 +34,8 @@ enum { LRU_OK = 0, LRU_CAPACITY = 1, LRU_BAD_ID = 2 };
 // the kernel has finished.
 struct LruResult {
   int32_t status;
-  int32_t n_needed, n_hits, n_misses, n_evictions;
-  int32_t pad[3];
+  int32_t n_needed, n_hits, n_misses, n_evictions, n_cpu;
+  int32_t pad[2];
   int32_t ev[kLruMaxE][4];  // expert, hit, slot, evicted key (-1 none); ascending expert
 };
 
@@ -52,8 +53,27 @@ __device__ __forceinline__ bool older(uint64_t sa, int a, uint64_t sb, int b) {
 // One workgroup.  Stamps and the slot table are read before any of them is
 // written (selection works on the pre-step stamps plus an LDS "taken" bitmap),
 // so the kernel never reads its own global writes.
+// Number of a step's m misses to fill when the others can run on the host
+// CPU: the q in 0..m minimising max(q / b_pcie, (m - q) / b_host), ties to the
+// larger q (the miss-split reading of the pages' formula, FreeToken 290b model
+// page, "Cómo gestiona FreeToken el prellenado y la decodificación"); b_host
+// <= 0: every miss is filled.  Plain double arithmetic, so the decision is the
+// same on any IEEE machine.
+__device__ inline int miss_split(int m, double b_pcie, double b_host) {
+  if (b_host <= 0.0 || m == 0) return m;
+  auto t = [&](int q) {
+    const double fill = q ? (b_pcie > 0.0 ? double(q) / b_pcie : __builtin_inf()) : 0.0;
+    const double cpu = (m - q) ? double(m - q) / b_host : 0.0;
+    return fill > cpu ? fill : cpu;
+  };
+  int best = 0;
+  for (int q = 0; q <= m; ++q)
+    if (t(q) <= t(best)) best = q;
+  return best;
+}
+
 __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int layer, const int32_t *__restrict__ ids,
-                                                              int R, int E, int C,
+                                                              int R, int E, int C, double b_pcie, double b_host,
                                                               int32_t *__restrict__ slot_of_expert,
                                                               LruResult *__restrict__ res) {
   __shared__ int s_need[kLruMaxE];     // flag, then position in the needed list
@@ -66,7 +86,7 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
   __shared__ int s_wcnt[kLruThreads / 64 + 1];
   __shared__ uint64_t s_wst[kLruThreads / 64];
   __shared__ int s_wsl[kLruThreads / 64];
-  __shared__ int s_bad, s_n, s_h;
+  __shared__ int s_bad, s_n, s_h, s_q;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NW = kLruThreads / 64;
@@ -134,10 +154,18 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
     __syncthreads();
   }
   const int h = hbase;
-  // Phase 2: misses in ascending expert order, each taking the oldest free slot.
+  if (tid == 0) s_q = miss_split(n - h, b_pcie, b_host);
+  __syncthreads();
+  const int q = s_q;
+  // Phase 2: misses in ascending expert order, each of the first q taking the
+  // oldest free slot; the others run on the CPU (no slot).
   int mi = 0;
   for (int i = 0; i < n; ++i) {
     if (s_hit[i]) continue;  // uniform across the workgroup
+    if (mi >= q) {  // runs on the CPU: slot and evicted key stay -1 (set in phase 1)
+      ++mi;
+      continue;
+    }
     uint64_t bs = ~uint64_t(0);
     int bsl = 0x7fffffff;
     for (int s = tid; s < C; s += kLruThreads) {
@@ -178,18 +206,21 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
     ++mi;
   }
   // Apply: stamps of victims, owner / map updates, the layer's slot table.
+  __syncthreads();
   int n_evict = 0;
   if (tid == 0) {
-    int j = 0;
+    int j = 0, n_cpu = 0, rank = 0;
     for (int i = 0; i < n; ++i) {
       const int e = s_list[i];
       const int s = s_slot[i];
       const bool hit = s_hit[i] != 0;
+      const bool cpu = !hit && rank++ >= q;  // misses beyond the first q run on the CPU
       res->ev[i][0] = e;
-      res->ev[i][1] = hit ? 1 : 0;
+      res->ev[i][1] = hit ? 1 : (cpu ? 4 : 0);
       res->ev[i][2] = s;
       res->ev[i][3] = s_evk[i];
-      if (!hit) {
+      if (cpu) ++n_cpu;
+      if (!hit && !cpu) {
         st.stamp[s] = clk + uint64_t(h + j) + 1;
         ++j;
         const int ek = s_evk[i];
@@ -203,11 +234,12 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
         s_out[e] = s;
       }
     }
-    *st.clock = clk + uint64_t(n);
+    *st.clock = clk + uint64_t(h + j);
     res->n_needed = n;
     res->n_hits = h;
     res->n_misses = mi;
     res->n_evictions = n_evict;
+    res->n_cpu = n_cpu;
   }
   __syncthreads();
   for (int e = tid; e < E; e += kLruThreads) slot_of_expert[e] = s_out[e];
@@ -221,6 +253,59 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
 
 using namespace ft;
 
+// Pinned host memory that kernels read and write through its device address.
+struct MappedBuf {
+  void *host = nullptr;
+  void *dev = nullptr;
+  size_t bytes = 0;
+  ft_status reserve(size_t need) {  // contents are not kept
+    if (need <= bytes) return FT_OK;
+    release();
+    const size_t b = (need + 65535) & ~size_t(65535);
+    if (hipHostMalloc(&host, b, hipHostMallocMapped) != hipSuccess) {
+      host = nullptr;
+      return FT_EHIP;
+    }
+    if (hipHostGetDevicePointer(&dev, host, 0) != hipSuccess) {
+      release();
+      return FT_EHIP;
+    }
+    bytes = b;
+    return FT_OK;
+  }
+  void release() {
+    if (host) (void)hipHostFree(host);
+    host = dev = nullptr;
+    bytes = 0;
+  }
+};
+
+// Hybrid misses on the host CPU.  The activations and the permutation of a
+// step with CPU misses reach host memory through a kernel that writes
+// host-mapped memory, and the CPU's rows come back through a kernel that reads
+// it: DMA copies on the compute stream would queue behind the step's miss
+// fills on the copy engines, and the CPU would first wait for fills it does
+// not need.
+__global__ void stage_kernel(const uint4 *__restrict__ x, int nx, const int32_t *__restrict__ off, int noff,
+                             const int32_t *__restrict__ rows, int nrows, uint4 *hx, int32_t *hoff, int32_t *hrows) {
+  const int total = nx + noff + nrows;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    if (i < nx)
+      hx[i] = x[i];
+    else if (i < nx + noff)
+      hoff[i - nx] = off[i - nx];
+    else
+      hrows[i - nx - noff] = rows[i - nx - noff];
+  }
+}
+
+// y[list[b]] = hy[list[b]] for workgroup b (rows of H4 float4).
+__global__ void patch_kernel(const float4 *__restrict__ hy, const int32_t *__restrict__ list, int H4,
+                             float4 *__restrict__ y) {
+  const size_t row = size_t(list[blockIdx.x]);
+  for (int j = threadIdx.x; j < H4; j += blockDim.x) y[row * H4 + j] = hy[row * H4 + j];
+}
+
 struct ft_expert_cache {
   ft_expert_layout L;
   int n_layers, E, C;
@@ -231,6 +316,16 @@ struct ft_expert_cache {
   hipEvent_t ev_fill[kFillStreams];
   bool pending[kFillStreams];       // a layer prefetch's fills on this queue not yet waited for
   int32_t *iota;                    // device [E]: 0..E-1 (the needed set of a layer prefetch)
+  double b_pcie = 0.0, b_host = 0.0;  // hybrid split (b_host <= 0: every miss is filled)
+  std::vector<int32_t> cpu_list;      // the last step's misses left to the CPU
+  int32_t cpu_layer = -1;             // ... and its layer
+  // host-mapped buffers of the CPU misses (grown on demand, device address beside)
+  uint64_t staged_step = ~uint64_t(0);
+  int32_t staged_T = 0, staged_k = 0;
+  size_t stage_x_bytes = 0, stage_off_bytes = 0;
+  MappedBuf stage, ybuf, list;
+  hipEvent_t ev_stage = nullptr, ev_patch = nullptr;
+  bool stage_pending = false, patch_pending = false;
   int32_t *pf_slots;                // device [E]: slot table a prefetch writes (unused)
   LruState st;
   void *dev_state;
@@ -338,7 +433,7 @@ static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *i
                              hipStream_t compute_stream, bool prefetch, const char *who) {
   c->res_host->status = -1;
   hipLaunchKernelGGL(lru_step_kernel, dim3(1), dim3(kLruThreads), 0, compute_stream, c->st, layer, ids, R, c->E,
-                     c->C, slot_of_expert, c->res_dev);
+                     c->C, prefetch ? 0.0 : c->b_pcie, prefetch ? 0.0 : c->b_host, slot_of_expert, c->res_dev);
   FT_LAUNCHED("lru_step_kernel");
   FT_HIP(hipEventRecord(c->ev_lru, compute_stream));
   FT_HIP(hipEventSynchronize(c->ev_lru));
@@ -365,9 +460,18 @@ static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *i
   // work enqueued there.
   int fills = 0;
   bool used[kFillStreams] = {};
+  if (!prefetch) {
+    c->cpu_list.clear();
+    c->cpu_layer = layer;
+  }
   for (int i = 0; i < r.n_needed; ++i) {
-    const int e = r.ev[i][0], hit = r.ev[i][1], s = r.ev[i][2], ek = r.ev[i][3];
-    c->log.push_back(ft_cache_event{step, layer, e, prefetch ? (hit ? 3 : 2) : hit, s, ek});
+    const int e = r.ev[i][0], code = r.ev[i][1], s = r.ev[i][2], ek = r.ev[i][3];
+    const bool hit = code == 1;
+    c->log.push_back(ft_cache_event{step, layer, e, prefetch ? (hit ? 3 : 2) : code, s, ek});
+    if (code == 4) {
+      c->cpu_list.push_back(e);
+      continue;
+    }
     if (hit) continue;
     if (ek >= 0) c->map_mirror[size_t(ek)] = -1;
     c->map_mirror[size_t(layer) * c->E + e] = s;
@@ -401,6 +505,7 @@ static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *i
     c->stats.accesses += uint64_t(r.n_needed);
     c->stats.hits += uint64_t(r.n_hits);
     c->stats.misses += uint64_t(r.n_misses);
+    c->stats.cpu_misses += uint64_t(r.n_cpu);
     c->stats.steps += 1;
   }
   c->stats.evictions += uint64_t(r.n_evictions);
@@ -425,6 +530,112 @@ extern "C" ft_status ft_expert_cache_prefetch_layer(ft_expert_cache *c, int32_t 
   FT_REQUIRE(c != nullptr, "ft_expert_cache_prefetch_layer: cache is NULL");
   FT_REQUIRE(layer >= 0 && layer < c->n_layers, "ft_expert_cache_prefetch_layer: layer out of range");
   return cache_serve(c, layer, c->iota, c->E, c->pf_slots, compute_stream, true, "ft_expert_cache_prefetch_layer");
+}
+
+extern "C" ft_status ft_expert_cache_set_split(ft_expert_cache *c, double b_pcie, double b_host) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_set_split: cache is NULL");
+  FT_REQUIRE(b_pcie >= 0.0 && b_host >= 0.0 && b_pcie == b_pcie && b_host == b_host,
+             "ft_expert_cache_set_split: bandwidths must be non-negative numbers");
+  FT_REQUIRE(b_host == 0.0 || b_pcie > 0.0 || b_host > 0.0, "ft_expert_cache_set_split: both bandwidths are zero");
+  c->b_pcie = b_pcie;
+  c->b_host = b_host;
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_cpu_misses(const ft_expert_cache *c, int32_t *experts, int32_t capacity,
+                                                int32_t *n) {
+  FT_REQUIRE(c != nullptr && n != nullptr, "ft_expert_cache_cpu_misses: NULL argument");
+  FT_REQUIRE(capacity >= 0 && (capacity == 0 || experts != nullptr), "ft_expert_cache_cpu_misses: bad buffer");
+  *n = int32_t(c->cpu_list.size());
+  for (int i = 0; i < *n && i < capacity; ++i) experts[i] = c->cpu_list[size_t(i)];
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_stage_cpu_misses(ft_expert_cache *c, const void *x, int32_t x_dtype, int32_t T,
+                                                      int32_t k, const int32_t *expert_offsets,
+                                                      const int32_t *sorted_rows, hipStream_t stream) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_stage_cpu_misses: cache is NULL");
+  if (c->cpu_list.empty()) {
+    clear_error();
+    return FT_OK;
+  }
+  FT_SUPPORTED(x_dtype == FT_BF16, "ft_expert_cache_stage_cpu_misses: CPU misses take bf16 activations");
+  FT_REQUIRE(T >= 1 && k >= 1 && int64_t(T) * k <= (int64_t(1) << 28),
+             "ft_expert_cache_stage_cpu_misses: bad T or k");
+  FT_REQUIRE(x != nullptr && expert_offsets != nullptr && sorted_rows != nullptr,
+             "ft_expert_cache_stage_cpu_misses: NULL pointer argument");
+  FT_REQUIRE(aligned(x, 16), "ft_expert_cache_stage_cpu_misses: x must be 16-byte aligned");
+  const int H = c->L.H, E = c->E, R = T * k;
+  const size_t xb = size_t(T) * H * 2;                      // a multiple of 256 (H % 32 == 0)
+  const size_t ob = (size_t(E + 1) * 4 + 255) & ~size_t(255);
+  const size_t need = xb + ob + size_t(R) * 4;
+  if (need > c->stage.bytes) {
+    if (c->stage_pending) FT_HIP(hipEventSynchronize(c->ev_stage));
+    if (c->stage.reserve(need) != FT_OK) return fail(FT_EHIP, "ft_expert_cache_stage_cpu_misses: hipHostMalloc failed");
+  }
+  if (c->ev_stage == nullptr) FT_HIP(hipEventCreateWithFlags(&c->ev_stage, hipEventDisableTiming));
+  const int nx = int(xb / 16), total = nx + (E + 1) + R;
+  const int grid = std::min(1024, (total + 255) / 256);
+  uint8_t *d = static_cast<uint8_t *>(c->stage.dev);
+  hipLaunchKernelGGL(stage_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint4 *>(x), nx,
+                     expert_offsets, E + 1, sorted_rows, R, reinterpret_cast<uint4 *>(d),
+                     reinterpret_cast<int32_t *>(d + xb), reinterpret_cast<int32_t *>(d + xb + ob));
+  FT_LAUNCHED("stage_kernel");
+  FT_HIP(hipEventRecord(c->ev_stage, stream));
+  c->stage_pending = true;
+  c->staged_step = c->stats.steps;
+  c->staged_T = T;
+  c->staged_k = k;
+  c->stage_x_bytes = xb;
+  c->stage_off_bytes = ob;
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_run_cpu_misses(ft_expert_cache *c, float *y_rows, hipStream_t stream,
+                                                    int32_t n_threads) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_run_cpu_misses: cache is NULL");
+  if (c->cpu_list.empty()) {
+    clear_error();
+    return FT_OK;
+  }
+  FT_REQUIRE(c->stage_pending && c->staged_step == c->stats.steps,
+             "ft_expert_cache_run_cpu_misses: call ft_expert_cache_stage_cpu_misses for this step first");
+  FT_REQUIRE(y_rows != nullptr && aligned(y_rows, 16), "ft_expert_cache_run_cpu_misses: y_rows NULL or unaligned");
+  FT_REQUIRE(n_threads >= 0, "ft_expert_cache_run_cpu_misses: n_threads must be non-negative");
+  const int T = c->staged_T, k = c->staged_k, R = T * k, H = c->L.H;
+  const auto t0 = std::chrono::steady_clock::now();
+  FT_HIP(hipEventSynchronize(c->ev_stage));  // the staged inputs are in host memory
+  c->stage_pending = false;
+  if (c->patch_pending) FT_HIP(hipEventSynchronize(c->ev_patch));  // the last patch has read ybuf / list
+  c->patch_pending = false;
+  if (c->ybuf.reserve(size_t(R) * H * 4) != FT_OK || c->list.reserve(size_t(R) * 4) != FT_OK)
+    return fail(FT_EHIP, "ft_expert_cache_run_cpu_misses: hipHostMalloc failed");
+  if (c->ev_patch == nullptr) FT_HIP(hipEventCreateWithFlags(&c->ev_patch, hipEventDisableTiming));
+  const uint8_t *h = static_cast<const uint8_t *>(c->stage.host);
+  const int32_t *hoff = reinterpret_cast<const int32_t *>(h + c->stage_x_bytes);
+  const int32_t *hrows = reinterpret_cast<const int32_t *>(h + c->stage_x_bytes + c->stage_off_bytes);
+  float *hy = static_cast<float *>(c->ybuf.host);
+  const ft_status st = ft_cpu_miss_rows(&c->L, c->bank, c->cpu_layer, c->E, c->cpu_list.data(),
+                                        int32_t(c->cpu_list.size()), hoff, hrows, T, k, h, hy, n_threads);
+  if (st != FT_OK) return st;  // its message is kept
+  int32_t *hl = static_cast<int32_t *>(c->list.host);
+  int n = 0;
+  for (const int32_t e : c->cpu_list)
+    for (int r = hoff[e]; r < hoff[e + 1]; ++r) hl[n++] = r;
+  if (n > 0) {
+    hipLaunchKernelGGL(patch_kernel, dim3(n), dim3(256), 0, stream, static_cast<const float4 *>(c->ybuf.dev),
+                       static_cast<const int32_t *>(c->list.dev), H / 4, reinterpret_cast<float4 *>(y_rows));
+    FT_LAUNCHED("patch_kernel");
+    FT_HIP(hipEventRecord(c->ev_patch, stream));
+    c->patch_pending = true;
+  }
+  c->stats.cpu_ns += uint64_t(
+      std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count());
+  clear_error();
+  return FT_OK;
 }
 
 // Resize at a safe point (the pages: the runtime resizes and rebuilds the GPU
@@ -556,6 +767,17 @@ extern "C" ft_status ft_expert_cache_destroy(ft_expert_cache *c) {
     if (q > 0) (void)hipStreamDestroy(c->fill[q]);
     (void)hipEventDestroy(c->ev_fill[q]);
   }
+  if (c->ev_stage) {
+    (void)hipEventSynchronize(c->ev_stage);
+    (void)hipEventDestroy(c->ev_stage);
+  }
+  if (c->ev_patch) {
+    (void)hipEventSynchronize(c->ev_patch);
+    (void)hipEventDestroy(c->ev_patch);
+  }
+  c->stage.release();
+  c->ybuf.release();
+  c->list.release();
   (void)hipFree(c->dev_state);
   (void)hipFree(c->iota);
   (void)hipHostFree(c->res_host);

@@ -125,6 +125,14 @@ class MoELayer:
         ys = self.y_shared if (with_shared and self.y_shared is not None) else None
         ops.ft_moe_combine(self.y_rows, w, self.row_pos, ys, T, s.k, s.H, out_dt, self.out, stream=stream)
 
+    def stage_cpu_misses(self, cache, T, x, stream=None):
+        """After the cache step, before ffn(): stage this step's inputs of the CPU misses."""
+        cache.stage_cpu_misses(x, DTYPES[self.s.xdtype], T, self.s.k, self.offsets, self.sorted_rows, stream=stream)
+
+    def run_cpu_misses(self, cache, stream=None, n_threads=0):
+        """After ffn(): the CPU misses' rows on the host, copied into y_rows on the stream."""
+        cache.run_cpu_misses(self.y_rows, stream=stream, n_threads=n_threads)
+
     def forward(self, T, x, pool, w_router=None, logits=None, slot_of_expert=None, shared_blob=None,
                 stream=None, mode=0):
         """route -> permute -> grouped FFN -> combine, all enqueued on one stream."""

@@ -31,7 +31,9 @@ def _ptr(t) -> int | None:
         return None
     if isinstance(t, int):
         return t
-    return t.data_ptr()
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data  # numpy array (host)
 
 
 def _stream(stream) -> int:
@@ -86,6 +88,26 @@ def ft_moe_grouped_ffn(layout: ExpertLayout, slot_pool, slot_of_expert, shared_b
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def ft_cpu_expert_ffn(layout: ExpertLayout, blob, x, n: int, y, n_threads: int = 0) -> None:
+    """Host pointers (numpy arrays or pinned tensors) for blob, x (bf16 bits) and y (float32)."""
+    _check(_lib.lib().ft_cpu_expert_ffn(C.byref(layout), _ptr(blob), _ptr(x), n, _ptr(y), n_threads))
+
+
+def ft_cpu_isa(request: int = -1) -> int:
+    """Select the host kernel's instruction path (-1: query); returns the path in use."""
+    active = C.c_int32()
+    _check(_lib.lib().ft_cpu_isa(request, C.byref(active)))
+    return active.value
+
+
+def ft_cpu_miss_rows(layout: ExpertLayout, bank, layer: int, E: int, experts, n_experts: int, expert_offsets,
+                     sorted_rows, T: int, k: int, x, y_rows, n_threads: int = 0) -> None:
+    """Host rows of a step's CPU misses (all pointers host)."""
+    _check(_lib.lib().ft_cpu_miss_rows(C.byref(layout), _ptr(bank), layer, E, _ptr(experts), n_experts,
+                                       _ptr(expert_offsets), _ptr(sorted_rows), T, k, _ptr(x), _ptr(y_rows),
+                                       n_threads))
+
+
 def ft_mxfp8_quantize(x, ldx: int, n: int, K: int, codes, scales, stream=None) -> None:
     _check(_lib.lib().ft_mxfp8_quantize(_ptr(x), ldx, n, K, _ptr(codes), _ptr(scales), _stream(stream)))
 
@@ -114,6 +136,31 @@ class ExpertCache:
                                                _stream(stream)))
 
     step = ft_expert_cache_step
+
+    def ft_expert_cache_set_split(self, b_pcie: float, b_host: float) -> None:
+        _check(_lib.lib().ft_expert_cache_set_split(self._h, float(b_pcie), float(b_host)))
+
+    set_split = ft_expert_cache_set_split
+
+    def ft_expert_cache_cpu_misses(self) -> list[int]:
+        n = C.c_int32()
+        buf = (C.c_int32 * 4096)()
+        _check(_lib.lib().ft_expert_cache_cpu_misses(self._h, buf, 4096, C.byref(n)))
+        return list(buf[:n.value])
+
+    cpu_misses = ft_expert_cache_cpu_misses
+
+    def ft_expert_cache_stage_cpu_misses(self, x, x_dtype: int, T: int, k: int, expert_offsets, sorted_rows,
+                                         stream=None) -> None:
+        _check(_lib.lib().ft_expert_cache_stage_cpu_misses(self._h, _ptr(x), x_dtype, T, k, _ptr(expert_offsets),
+                                                           _ptr(sorted_rows), _stream(stream)))
+
+    stage_cpu_misses = ft_expert_cache_stage_cpu_misses
+
+    def ft_expert_cache_run_cpu_misses(self, y_rows, stream=None, n_threads: int = 0) -> None:
+        _check(_lib.lib().ft_expert_cache_run_cpu_misses(self._h, _ptr(y_rows), _stream(stream), n_threads))
+
+    run_cpu_misses = ft_expert_cache_run_cpu_misses
 
     def ft_expert_cache_prefetch_layer(self, layer: int, stream=None) -> None:
         _check(_lib.lib().ft_expert_cache_prefetch_layer(self._h, layer, _stream(stream)))

@@ -213,6 +213,63 @@ ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Instruction paths of the host expert kernel (ft_cpu_expert_ffn,
+ * ft_cpu_miss_rows).  Both compute the same products; they differ only in the
+ * order of fp32 additions.
+ */
+enum {
+  FT_CPU_ISA_QUERY = -1,  /* ft_cpu_isa: report only */
+  FT_CPU_ISA_BEST = 0,    /* the best the host supports (the default) */
+  FT_CPU_AVX2 = 1,        /* AVX2 + FMA: activations widened to fp32 */
+  FT_CPU_AVX512_BF16 = 2  /* AVX-512 BF16: bf16 pair dot products into fp32 */
+};
+
+/* Select (or query, FT_CPU_ISA_QUERY) the host kernel's path for the process;
+ * *active (may be NULL) receives the path in use.  A path the host lacks ->
+ * FT_ENOTSUP, nothing changed; an unknown request -> FT_EINVAL. */
+ft_status ft_cpu_isa(int32_t request, int32_t *active);
+
+/*
+ * ft_cpu_expert_ffn -- one expert's SwiGLU FFN on the host CPU, for misses the
+ * hybrid split leaves to the CPU (FreeToken 290b model page, "Ejecución
+ * híbrida": a miss may run directly on the CPU; the CPU expert kernel's
+ * effective host bandwidth is the B_h of the split).  Same arithmetic as the
+ * exact GPU mode: weights decoded exactly, fp32 accumulation, the hidden
+ * vector rounded to bf16 before the down projection.
+ * blob: HOST pointer to one expert blob in layout L (e.g. inside the pinned
+ *   host bank), FT_BF16 or FT_MXFP4 weights with H and I multiples of 128
+ *   (else FT_ENOTSUP).
+ * x: HOST bf16 [n, H]; y: HOST fp32 [n, H] (written).  n >= 0.
+ * n_threads: host threads (0: FTMOE_CPU_THREADS or all hardware threads); a
+ *   persistent pool per thread count is kept for the process.
+ * Synchronous: returns when y is written.  No GPU call is made.
+ */
+ft_status ft_cpu_expert_ffn(const ft_expert_layout *L, const void *blob, const void *x, int32_t n, float *y,
+                            int32_t n_threads);
+
+/*
+ * ft_cpu_miss_rows -- the rows of a layer step's CPU misses (the experts
+ * ft_expert_cache_cpu_misses lists) computed on the host, in the permuted
+ * order of ft_moe_grouped_ffn's y_rows (same page and arithmetic as
+ * ft_cpu_expert_ffn).  For each listed expert e, row i in
+ * expert_offsets[e] .. expert_offsets[e+1]-1 is token sorted_rows[i] / k run
+ * through expert (layer, e); y_rows[i] is written, no other row is touched.
+ * All pointers are HOST pointers:
+ *   bank: the host expert bank, blob (layer * E + e) at byte offset
+ *     (layer * E + e) * L->expert_bytes (the layout ft_expert_cache_create takes);
+ *   experts [n_experts], ids in [0, E); expert_offsets [E+1] with
+ *     expert_offsets[0] = 0 and expert_offsets[E] = T*k, sorted_rows [T*k]
+ *     (host copies of ft_moe_permute's outputs);
+ *   x: bf16 [T, H]; y_rows: fp32 [T*k, H].
+ * Errors: bad sizes, ids or offsets -> FT_EINVAL (nothing written); weights
+ * other than bf16 / MXFP4 -> FT_ENOTSUP.  Synchronous; no GPU call is made.
+ */
+ft_status ft_cpu_miss_rows(const ft_expert_layout *L, const void *bank, int32_t layer, int32_t E,
+                           const int32_t *experts, int32_t n_experts, const int32_t *expert_offsets,
+                           const int32_t *sorted_rows, int32_t T, int32_t k, const void *x, float *y_rows,
+                           int32_t n_threads);
+
+/*
  * ft_mxfp8_quantize -- bf16 rows to MXFP8, the activation format of the native
  * MXFP4 mode (the pages name natively MXFP4-quantized routed experts, FreeToken
  * quantization page, "Formatos compatibles, hardware y perfil de rendimiento";
@@ -268,6 +325,10 @@ typedef struct {
   uint64_t bytes_h2d;  /* bytes copied host -> device (miss and prefetch fills) */
   uint64_t steps;      /* successful ft_expert_cache_step calls             */
   uint64_t prefetch_fills;  /* entries brought in by ft_expert_cache_prefetch_layer */
+  uint64_t cpu_misses;  /* misses left to the host CPU by the hybrid split (also in misses) */
+  uint64_t cpu_ns;      /* host wall time inside ft_expert_cache_run_cpu_misses (waiting for the staged
+                           inputs, the expert kernel, enqueueing the copy back): cpu_misses *
+                           expert_bytes / cpu_ns is the effective B_h the decode loop sees */
 } ft_cache_stats;
 
 /* One cache event, as recorded by the step (or layer prefetch) that produced it. */
@@ -276,7 +337,8 @@ typedef struct {
                           prefetch records the number of steps before it    */
   int32_t layer;
   int32_t expert;
-  int32_t hit;         /* 1 hit, 0 miss; prefetch: 3 already resident, 2 filled */
+  int32_t hit;         /* 1 hit, 0 miss (filled), 4 miss left to the host CPU
+                          (slot -1); prefetch: 3 already resident, 2 filled  */
   int32_t slot;
   int32_t evicted;     /* key layer*E + expert of the entry evicted, or -1    */
 } ft_cache_event;
@@ -334,6 +396,57 @@ ft_status ft_expert_cache_trace(const ft_expert_cache *c, void *host_buf, size_t
  * completed step (-1 if not resident), written to *slot (host). */
 ft_status ft_expert_cache_lookup(const ft_expert_cache *c, int32_t layer, int32_t expert,
                                  int32_t *slot);
+
+/*
+ * ft_expert_cache_set_split -- hybrid execution of misses (FreeToken 290b model
+ * page, "Ejecución híbrida" and "Cómo gestiona FreeToken el prellenado y la
+ * decodificación": misses are either filled over PCIe or run on the CPU, by a
+ * split derived from two measured bandwidths).  From the next step on, of a
+ * step's m misses only q are filled: the q in 0..m minimising
+ * max(q / b_pcie, (m - q) / b_host), ties to the larger q (b_pcie: pinned
+ * host-to-device expert bandwidth; b_host: bandwidth the host CPU expert
+ * kernel achieves, both in the same unit); the lowest expert ids are filled.
+ * The others stay non-resident (slot -1 in slot_of_expert, no eviction, no
+ * recency; still counted as misses) and are listed by
+ * ft_expert_cache_cpu_misses; ft_expert_cache_stage_cpu_misses and
+ * ft_expert_cache_run_cpu_misses compute their rows on the host and write
+ * them into y_rows after ft_moe_grouped_ffn (which writes NaN there).  b_host = 0 turns the split off (every miss filled, the default).
+ * Errors: negative or NaN bandwidths -> FT_EINVAL.
+ */
+ft_status ft_expert_cache_set_split(ft_expert_cache *c, double b_pcie, double b_host);
+
+/* The last step's misses left to the CPU, ascending expert id: *n (host)
+ * receives their number, experts (host) the first min(*n, capacity) ids. */
+ft_status ft_expert_cache_cpu_misses(const ft_expert_cache *c, int32_t *experts, int32_t capacity,
+                                     int32_t *n);
+
+/*
+ * Running the last step's CPU misses (FreeToken 290b model page, "Ejecución
+ * híbrida"), in two calls around ft_moe_grouped_ffn on the compute stream:
+ *
+ *   ft_expert_cache_step -> ft_expert_cache_stage_cpu_misses ->
+ *   ft_moe_grouped_ffn -> ft_expert_cache_run_cpu_misses -> ft_moe_combine
+ *
+ * stage: enqueues on `stream` a kernel that copies x [T, H] (DEVICE, bf16,
+ *   16-byte aligned), expert_offsets [E+1] and sorted_rows [T*k] (DEVICE, the
+ *   step's ft_moe_permute outputs) into host-mapped memory the cache owns
+ *   (grown on demand).  A kernel, not a DMA copy: it does not wait behind the
+ *   step's miss fills on the copy engines.  Returns at once.
+ * run: waits for that kernel only, computes the rows of every CPU miss on the
+ *   host (ft_cpu_miss_rows over the cache's host bank, n_threads as there),
+ *   then enqueues on `stream` a kernel that copies them from host-mapped
+ *   memory into y_rows [T*k, H] (DEVICE, fp32, 16-byte aligned), replacing
+ *   the NaN rows ft_moe_grouped_ffn left there; enqueue it after that FFN.
+ * Both are no-ops (FT_OK) when the last step left no miss to the CPU.
+ * Errors: run without a stage of the same step -> FT_EINVAL; activations
+ *   other than bf16 -> FT_ENOTSUP; the host kernel's errors as there.
+ * A later stage or run waits for the previous one's kernels before it reuses
+ * the host buffers.
+ */
+ft_status ft_expert_cache_stage_cpu_misses(ft_expert_cache *c, const void *x, int32_t x_dtype, int32_t T, int32_t k,
+                                           const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                           hipStream_t stream);
+ft_status ft_expert_cache_run_cpu_misses(ft_expert_cache *c, float *y_rows, hipStream_t stream, int32_t n_threads);
 
 /*
  * ft_expert_cache_prefetch_layer -- bring every expert of `layer` into the

@@ -7,7 +7,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import synth
-from oracle import formats, moe
+from oracle import formats, moe, policy
 from oracle.lru import CapacityError, ExpertLRU
 from tests.helpers import Experts, check_close
 from tests.test_oracle_lru import _traces
@@ -54,6 +54,14 @@ class Rig:
         self.C = C
 
 
+def _split_for(q, m):
+    """Bandwidths (b_pcie, b_host) for which the miss split of m misses is exactly q
+    (q = None or q = m: every miss filled; the split is then off)."""
+    if q is None or q == m:
+        return 1.0, 0.0
+    return float(q), float(m - q)
+
+
 def events_by_step(trace):
     out = {}
     for step, layer, e, hit, slot, ev in trace:
@@ -68,7 +76,7 @@ def test_hand_traced_sequences_on_device(env, golden_dir):
         rig = Rig(ops, tr["L"], tr["E"], tr["C"], fill=False)
         E = tr["E"]
         want, n_steps = [], 0
-        for kind, layer, ids, evs in tr["steps"]:
+        for i, (kind, layer, ids, evs) in enumerate(tr["steps"]):
             if kind == "resize":
                 rig.resize(layer, in_place=layer <= rig.C)
                 continue
@@ -76,9 +84,11 @@ def test_hand_traced_sequences_on_device(env, golden_dir):
                 rig.cache.prefetch_layer(layer)
                 code = {True: 3, False: 2}
             else:
+                rig.cache.set_split(*_split_for(tr.get("fill", {}).get(i), sum(not h for _, h, _, _ in evs)))
                 rig.step(layer, ids)
                 code = {True: 1, False: 0}
-            want += [(n_steps, layer, e, code[h], s, -1 if ev is None else ev[0] * E + ev[1]) for e, h, s, ev in evs]
+            want += [(n_steps, layer, e, code[h] if s >= 0 or h else 4, s, -1 if ev is None else ev[0] * E + ev[1])
+                     for e, h, s, ev in evs]
             n_steps += kind != "prefetch"
         assert rig.cache.trace() == want, tr["name"]
         st = rig.cache.stats()
@@ -316,3 +326,122 @@ def test_prefill_double_buffered_through_the_cache(env):
     assert st["prefetch_fills"] == sim.prefetch_fills == cfg.n_layers * cfg.E
     assert st["evictions"] == sim.evictions and st["bytes_h2d"] == cfg.n_layers * cfg.E * eb
     cache.destroy()
+
+
+def test_split_bandwidths_give_the_intended_fill_count():
+    for m in range(0, 9):
+        for q in range(0, m + 1):
+            bp, bh = _split_for(q, m)
+            assert (m if bh == 0 else policy.miss_split(m, bp, bh)) == q
+
+
+def test_hybrid_split_against_the_simulator(env):
+    """Random steps under changing bandwidth pairs: events (CPU misses code 4, slot -1), the CPU
+    miss list, slot tables, filled bytes and totals follow the oracle's fill-limited steps."""
+    ops, _ = env
+    rng = np.random.default_rng(23)
+    L, E, C = 3, 24, 10
+    rig = Rig(ops, L, E, C)
+    sim = ExpertLRU(L, E, C)
+    pairs = [(49.3, 0.0), (49.3, 30.0), (25.0, 50.0), (0.0, 10.0), (10.0, 10.0), (3.0, 1.0)]
+    want_log = []
+    for t in range(160):
+        layer = int(rng.integers(L))
+        T = int(rng.integers(0, 4))
+        ids = np.array([rng.choice(E, size=3, replace=False) for _ in range(T)], np.int32).reshape(-1)
+        bp, bh = pairs[int(rng.integers(len(pairs)))]
+        needed = sorted(set(ids.tolist()))
+        m = sum(sim.slot_of_expert(layer)[e] < 0 for e in needed)
+        q = m if bh == 0 else policy.miss_split(m, bp, bh)
+        evs = sim.step(layer, ids, fill_limit=q)
+        rig.cache.set_split(bp, bh)
+        rig.step(layer, ids)
+        torch.cuda.synchronize()
+        cpu = [e.expert for e in evs if not e.hit and e.slot < 0]
+        assert rig.cache.cpu_misses() == cpu
+        assert len(cpu) == m - q
+        assert rig.slot_of.cpu().numpy().tolist() == sim.slot_of_expert(layer)
+        for ev in evs:
+            if not ev.hit and ev.slot >= 0:
+                assert torch.equal(rig.pool[ev.slot].cpu(), rig.bank[layer * E + ev.expert])
+        want_log += [(t, layer, e.expert, 1 if e.hit else (0 if e.slot >= 0 else 4), e.slot,
+                      -1 if e.evicted is None else e.evicted[0] * E + e.evicted[1]) for e in evs]
+    assert rig.cache.trace() == want_log
+    st = rig.cache.stats()
+    assert (st["accesses"], st["hits"], st["misses"], st["evictions"], st["cpu_misses"]) == \
+        (sim.accesses, sim.hits, sim.misses, sim.evictions, sim.cpu_misses)
+    assert sim.cpu_misses > 20
+    assert st["bytes_h2d"] == (sim.misses - sim.cpu_misses) * rig.eb
+    rig.cache.destroy()
+
+
+@pytest.mark.parametrize("T,C", [(1, 10), (5, 30)])
+def test_hybrid_layer_outputs(env, T, C):
+    """Decode through the cache with the miss split on: the CPU misses' rows come from the host
+    kernel, the rest from the slots; every layer output matches the oracle."""
+    ops, Lm = env
+    cfg = synth.shrink(synth.CONFIGS[5], H=512, I=512, E=32, n_layers=2, capacity=C, steps=12)
+    shape = Lm.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize, True)
+    layer = Lm.MoELayer(shape, T)
+    lay = layer.layout
+    eb = int(lay.expert_bytes)
+    ex = [Experts(cfg, l) for l in range(cfg.n_layers)]
+    bank = torch.empty((cfg.n_layers * cfg.E, eb), dtype=torch.uint8, pin_memory=True)
+    for l in range(cfg.n_layers):
+        for e in range(cfg.E):
+            Lm.pack_expert(lay, ex[l].raw(e).arrays, bank.numpy()[l * cfg.E + e])
+    shared = [Lm.as_device_u8([Lm.pack_expert(lay, ex[l].raw(cfg.E).arrays)])[0] for l in range(cfg.n_layers)]
+    pool = torch.zeros((cfg.capacity, eb), dtype=torch.uint8, device="cuda")
+    cache = ops.ExpertCache(lay, cfg.n_layers, cfg.E, cfg.capacity, pool, bank, torch.cuda.Stream())
+    cache.set_split(2.0, 1.0)  # a third of each step's misses on the CPU
+    slot_of = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    n_cpu = 0
+    for s in range(cfg.steps):
+        for l in range(cfg.n_layers):
+            x = synth.tokens(cfg, T, layer=l, step=s)
+            logits = synth.prefill_logits(cfg, T, case=s, layer=l)
+            xd = Lm.to_device(x)
+            layer.route_permute(T, logits=Lm.to_device(logits))
+            cache.step(l, layer.ids, T, cfg.k, slot_of)
+            cpu = cache.cpu_misses()
+            n_cpu += len(cpu)
+            layer.stage_cpu_misses(cache, T, xd)
+            layer.ffn(T, xd, pool, slot_of_expert=slot_of, shared_blob=shared[l])
+            layer.run_cpu_misses(cache, n_threads=4)
+            layer.combine(T)
+            torch.cuda.synchronize()
+            got = formats.bf16_to_f64(layer.out[:T].cpu().numpy().view(np.uint16))
+            ids = moe.topk(logits, cfg.k)
+            w = moe.gating_weights(logits, ids, cfg.gating, cfg.renormalize)
+            x64 = formats.activations_to_f64(cfg.xdtype, x)
+            ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex[l].f64, ex[l].f64(cfg.E)) for t in range(T)])
+            check_close(got, ref, bf16_out=True, what=f"step {s} layer {l} cpu {cpu}")
+    st = cache.stats()
+    assert n_cpu == st["cpu_misses"] > 0 and st["misses"] > st["cpu_misses"]
+    assert st["cpu_ns"] > 0
+    cache.destroy()
+
+
+def test_cpu_miss_calls_validate(env):
+    """Run without a stage of the same step, and f32 activations, are refused; no-ops without CPU misses."""
+    ops, Lm = env
+    rig = Rig(ops, 1, 8, 4, H=256, I=256)
+    x = torch.zeros((2, 256), dtype=torch.int16, device="cuda")
+    off = torch.tensor([0, 1, 2, 2, 2, 2, 2, 2, 2], dtype=torch.int32, device="cuda")
+    rows = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    y = torch.zeros((2, 256), dtype=torch.float32, device="cuda")
+    rig.step(0, [0, 1])
+    rig.cache.stage_cpu_misses(x, Lm.DTYPES["bf16"], 2, 1, off, rows)  # no CPU miss: nothing happens
+    rig.cache.run_cpu_misses(y)
+    rig.cache.set_split(0.0, 1.0)                                   # every miss on the CPU
+    rig.step(0, [2, 3])
+    assert rig.cache.cpu_misses() == [2, 3]
+    with pytest.raises(ops.FtError) as e:
+        rig.cache.run_cpu_misses(y)
+    assert e.value.status == -1
+    with pytest.raises(ops.FtError) as e:
+        rig.cache.stage_cpu_misses(x, Lm.DTYPES["f32"], 2, 1, off, rows)
+    assert e.value.status == -2
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+    rig.cache.destroy()
