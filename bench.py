@@ -42,14 +42,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources (and build flags) the FFN kernels are compiled from: a change to
+# any of them invalidates committed counter readings of those kernels
+FFN_KERNEL_SOURCES = ("csrc/ffn.hip", "csrc/ft_internal.hpp", "csrc/stream_persist.hpp", "csrc/stream_gemm.hpp",
+                      "csrc/gemm_prefill.hpp", "csrc/gemm_mx.hpp", "csrc/mx.hip", "build.py")
+
+
 def kernel_sources_hash():
-    """Short sha256 over the HIP sources (names and contents) of the library."""
-    import glob
+    """Short sha256 over the FFN kernels' sources (names and contents)."""
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "expert_cached_ffn_amd", "csrc", "*"))):
-        h.update(os.path.basename(p).encode())
-        with open(p, "rb") as f:
+    for rel in FFN_KERNEL_SOURCES:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, "expert_cached_ffn_amd", rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
