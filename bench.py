@@ -696,7 +696,7 @@ def main():
     res = run_decode(args, cfg, batches, main_T)
     m = res[main_T]
     ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
-    kname = "ffn_persist_kernel<%s, gate_up>" % ("bf16" if cfg.wdtype == "bf16" else "mxfp4")
+    kname = "ffn_persist_kernel<bf16, gate_up>" if cfg.wdtype == "bf16" else "ffn_persist_xs_kernel<mxfp4, gate_up>"
     traffic = None
     if args.workload == "decode-bf16" and main_T == 64:
         traffic = measured_traffic("decode-bf16-T64_hbm_traffic.json", "void ft::ffn_persist_kernel<0, true,")

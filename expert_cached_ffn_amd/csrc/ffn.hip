@@ -197,6 +197,18 @@ static ft_status launch_stream(const FfnArgs &a, int a_max, int T, hipStream_t s
 
 // ------------------------------------------------------------------ persistent decode path
 
+// Weight register sets in flight for the x-stationary kernel, per shape.
+#ifndef FT_XS_NB
+#define FT_XS_NB(WF, GLU, WAVES, KPW) ((GLU) ? ((WAVES) >= 16 || (KPW) == 2 ? 2 : 4) : ((KPW) == 2 ? 4 : 6))
+#endif
+
+template <int WF, bool GLU, int WAVES, int KPW>
+__global__ __launch_bounds__(WAVES * 64) void ffn_persist_xs_kernel(PersistArgs a) {
+  __shared__ float s_red[WAVES * (GLU ? 2 : 1) * 256];
+  constexpr int NB = FT_XS_NB(WF, GLU, WAVES, KPW);
+  stream_persist_xs<WF, GLU, WAVES, KPW, NB>(a, s_red);
+}
+
 template <int WF, bool GLU, int WAVES, int KPW>
 __global__ __launch_bounds__(WAVES * 64) void ffn_persist_kernel(PersistArgs a) {
   __shared__ float s_red[WAVES * (GLU ? 2 : 1) * 256];
@@ -267,12 +279,27 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
   int waves, kpw;
   persist_shape(a.K / stream_kblock<WF>(), &waves, &kpw);
   persist_override(GLU, a.K / stream_kblock<WF>(), &waves, &kpw);
-#define FT_PERSIST(W, C)                                                                    \
-  if (waves == W && kpw == C) {                                                             \
-    const void *kern = reinterpret_cast<const void *>(&ffn_persist_kernel<WF, GLU, W, C>); \
-    const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));           \
-    hipLaunchKernelGGL((ffn_persist_kernel<WF, GLU, W, C>), dim3(g), dim3(W * 64), 0, stream, a); \
-    return true;                                                                            \
+  // x-stationary runs for MXFP4 weights (measured 1.65x at 32 tokens: a 16-row
+  // FP4 tile is half the bytes of a bf16 one, so the freed activation
+  // registers matter); bf16 tiles keep the strided order, measured faster
+  // there.  FTMOE_PERSIST_XS=0/1 overrides for tuning.
+  static const int xs_env = [] {
+    const char *v = getenv("FTMOE_PERSIST_XS");
+    return v == nullptr ? -1 : (atoi(v) != 0);
+  }();
+  const bool xs = xs_env < 0 ? WF == WF_FP4 : xs_env != 0;
+#define FT_PERSIST(W, C)                                                                          \
+  if (waves == W && kpw == C) {                                                                   \
+    if (xs) {                                                                                     \
+      const void *kern = reinterpret_cast<const void *>(&ffn_persist_xs_kernel<WF, GLU, W, C>); \
+      const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));                 \
+      hipLaunchKernelGGL((ffn_persist_xs_kernel<WF, GLU, W, C>), dim3(g), dim3(W * 64), 0, stream, a); \
+    } else {                                                                                      \
+      const void *kern = reinterpret_cast<const void *>(&ffn_persist_kernel<WF, GLU, W, C>);      \
+      const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));                 \
+      hipLaunchKernelGGL((ffn_persist_kernel<WF, GLU, W, C>), dim3(g), dim3(W * 64), 0, stream, a); \
+    }                                                                                             \
+    return true;                                                                                  \
   }
   FT_PERSIST(16, 1)
   FT_PERSIST(12, 1)

@@ -289,4 +289,241 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
   }
 }
 
+// X-stationary variant.  A workgroup owns a contiguous run of units ordered
+// (active expert, group of <= 16 tokens, 16-row weight tile), so the group's
+// activations are loaded once and stay in registers while its tiles stream
+// through a ring of NB weight register sets: the registers a per-unit
+// activation copy would take hold more weights in flight instead.  A group
+// change drains the ring once (one HBM round trip per group and workgroup).
+constexpr int kPersistMaxGroups = kPersistMaxE + 1 + kPersistMaxRows / 16;
+
+template <int WF, bool GLU, int WAVES, int KPW, int NB>
+__device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s_red) {
+  static_assert(NB >= 2, "the ring needs two register sets");
+  constexpr int THREADS = WAVES * 64;
+  constexpr int NW = WAVES;
+  constexpr int MATS = GLU ? 2 : 1;
+  constexpr int KB = stream_kblock<WF>();
+  constexpr int DL = WFrag<WF, MATS>::DL;
+  constexpr int DX = WF == WF_BF16 ? 4 : 8;
+  __shared__ int s_e[kPersistMaxE + 1];      // expert id (E = shared expert)
+  __shared__ int s_pos[kPersistMaxE + 1];    // first permuted row of its segment
+  __shared__ int s_m[kPersistMaxE + 1];      // rows of its segment
+  __shared__ int s_slot[kPersistMaxE + 1];
+  __shared__ int s_gbase[kPersistMaxE + 1];  // first token group of active expert i
+  __shared__ int s_gexp[kPersistMaxGroups];  // active expert of token group g
+  __shared__ int s_cnt[NW];
+  __shared__ int s_tok[kPersistMaxRows];     // token of every routed row (gather mode)
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (a.sorted_rows != nullptr)
+    for (int p = tid; p < a.T * a.k; p += THREADS) s_tok[p] = a.sorted_rows[p] / a.k;
+  const int r = lane & 15, q = lane >> 4;
+
+  // ---- active-expert table (ascending expert id, then the shared expert)
+  int base = 0;
+  for (int c0 = 0; c0 < a.E; c0 += THREADS) {
+    const int e = c0 + tid;
+    int lo = 0, cnt = 0;
+    if (e < a.E) {
+      lo = a.offsets[e];
+      cnt = a.offsets[e + 1] - lo;
+    }
+    const bool f = cnt > 0;
+    const uint64_t mask = __ballot(f);
+    if (lane == 0) s_cnt[wave] = __popcll(mask);
+    __syncthreads();
+    int before = base, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) before += s_cnt[w];
+      total += s_cnt[w];
+    }
+    if (f) {
+      const int i = before + __popcll(mask & ((uint64_t(1) << lane) - 1));
+      s_e[i] = e;
+      s_pos[i] = lo;
+      s_m[i] = cnt;
+      s_slot[i] = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    }
+    base += total;
+    __syncthreads();
+  }
+  int n_act = base;
+  if (a.shared_blob != nullptr) {
+    if (tid == 0) {
+      s_e[n_act] = a.E;
+      s_pos[n_act] = a.T * a.k;
+      s_m[n_act] = a.T;
+      s_slot[n_act] = 0;
+    }
+    ++n_act;
+    __syncthreads();
+  }
+  // ---- token groups: ceil(m / 16) per active expert, prefix-summed
+  int n_groups = 0;
+  for (int c0 = 0; c0 < n_act; c0 += THREADS) {
+    const int i = c0 + tid;
+    const int g = i < n_act ? (s_m[i] + 15) >> 4 : 0;
+    int v = g;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off);
+      if (lane >= off) v += t;
+    }
+    if (lane == 63) s_cnt[wave] = v;
+    __syncthreads();
+    int before = n_groups, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) before += s_cnt[w];
+      total += s_cnt[w];
+    }
+    if (i < n_act) {
+      const int gb = before + v - g;
+      s_gbase[i] = gb;
+      for (int j = 0; j < g && gb + j < kPersistMaxGroups; ++j) s_gexp[gb + j] = i;  // <= 1220 groups for T <= 64
+    }
+    n_groups += total;
+    __syncthreads();
+  }
+
+  // ---- this workgroup's run of units
+  const int n_units = n_groups * a.n_tiles;
+  const int u_begin = int(int64_t(n_units) * blockIdx.x / gridDim.x);
+  const int u_end = int(int64_t(n_units) * (blockIdx.x + 1) / gridDim.x);
+
+  const uint32_t wpitch = (WF == WF_BF16) ? uint32_t(a.K) * 2 : uint32_t(a.K) / 2;
+  const uint32_t spitch = uint32_t(a.K) / 32;
+  const uint32_t wbytes = uint32_t(a.N) * wpitch, sbytes = uint32_t(a.N) * spitch;
+  const rsrc_t xres = make_rsrc(a.X, a.x_bytes);
+
+  // Weights of tile `tile` of active expert ai (tile < 0: past the run; the
+  // loads still issue, at an offset past the buffer, so every ring step
+  // issues the same number of loads).
+  auto issue_w = [&](int ai, int tile, WFrag<WF, MATS> (&f)[KPW]) {
+    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]);
+    const uint8_t *blob = e == a.E ? a.shared_blob : a.pool + uint64_t(max(slot, 0)) * a.expert_bytes;
+    rsrc_t wres[MATS], sres[MATS];
+    wres[0] = make_rsrc(blob + a.off_w0, wbytes);
+    sres[0] = make_rsrc(blob + a.off_s0, sbytes);
+    if constexpr (GLU) {
+      wres[MATS - 1] = make_rsrc(blob + a.off_w1, wbytes);
+      sres[MATS - 1] = make_rsrc(blob + a.off_s1, sbytes);
+    }
+    const uint32_t wo = tile >= 0 ? uint32_t(tile * 16 + r) * wpitch + uint32_t(q) * 16 : kOOB;
+    const uint32_t so = tile >= 0 ? uint32_t(tile * 16 + r) * spitch : kOOB;
+#pragma unroll
+    for (int c = 0; c < KPW; ++c) {
+      const int kb = wave + c * WAVES;
+#pragma unroll
+      for (int mt = 0; mt < MATS; ++mt) {
+#pragma unroll
+        for (int d = 0; d < DL; ++d) f[c].w[mt][d] = bld16(wres[mt], wo + uint32_t(kb) * (DL * 64) + d * 64);
+        if constexpr (WF == WF_FP4) f[c].s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);
+      }
+    }
+  };
+  // Activations of token group (ai, g0): this lane's token row.
+  auto issue_x = [&](int ai, int g0, u32x4 (&xb)[KPW][DX]) {
+    const int e = uniform(s_e[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
+    const int j = g0 + r;
+    int row = -1;
+    if (j < m) {
+      if (a.sorted_rows == nullptr) row = pos + j;      // hidden row p
+      else row = e == a.E ? j : s_tok[pos + j];         // token of the shared / routed expert
+    }
+    const uint32_t xo = row >= 0 ? uint32_t(row) * uint32_t(a.ldx) * 2u : kOOB;
+#pragma unroll
+    for (int c = 0; c < KPW; ++c) {
+      const int kb = wave + c * WAVES;
+#pragma unroll
+      for (int dx = 0; dx < DX; ++dx) {
+        const int ko = WF == WF_BF16 ? kb * KB + 32 * dx + 8 * q : kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3);
+        xb[c][dx] = bld16(xres, xo + uint32_t(ko) * 2u);
+      }
+    }
+  };
+  // Multiply one tile of group (ai, g0), sum the wave partials in LDS, write
+  // its 16x16 output tile.
+  auto finish = [&](int ai, int g0, int tile, const WFrag<WF, MATS> (&f)[KPW], const u32x4 (&xcur)[KPW][DX]) {
+    const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
+    const bool shared = e == a.E;
+    const bool missing = !shared && slot < 0;
+    f32x4 acc[MATS];
+#pragma unroll
+    for (int mt = 0; mt < MATS; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KPW; ++c) {
+      if constexpr (WF == WF_BF16) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int mt = 0; mt < MATS; ++mt) acc[mt] = mfma16(as_bf16x8(f[c].w[mt][d]), as_bf16x8(xcur[c][d]), acc[mt]);
+      } else {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          float sc[MATS];
+#pragma unroll
+          for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32((f[c].s[mt][d] >> (8 * q)) & 0xffu);
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+            for (int mt = 0; mt < MATS; ++mt)
+              acc[mt] = mfma16(fp4x8_to_bf16x8(f[c].w[mt][d][mm], sc[mt]), as_bf16x8(xcur[c][4 * d + mm]), acc[mt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MATS; ++mt)
+      *reinterpret_cast<f32x4 *>(&s_red[((wave * MATS + mt) * 64 + lane) * 4]) = acc[mt];
+    __syncthreads();
+    if (tid < 256) {
+      const int ln = tid >> 2, v = tid & 3;
+      const int jj = g0 + (ln & 15);
+      const int n = tile * 16 + 4 * (ln >> 4) + v;
+      float g = 0.f, uu = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        g += s_red[((w * MATS + 0) * 64 + ln) * 4 + v];
+        if constexpr (GLU) uu += s_red[((w * MATS + 1) * 64 + ln) * 4 + v];
+      }
+      if (jj < m && n < a.N) {
+        const int p = pos + jj;  // permuted row; hidden rows of the shared expert follow the routed ones
+        if constexpr (GLU) {
+          reinterpret_cast<uint16_t *>(a.out)[int64_t(p) * a.ldo + n] =
+              missing ? uint16_t(0x7fc0) : f32_to_bf16_rne(silu(g) * uu);
+        } else {
+          float *yp = shared ? a.out_shared + int64_t(jj) * a.ldo : reinterpret_cast<float *>(a.out) + int64_t(p) * a.ldo;
+          yp[n] = missing ? __builtin_nanf("") : g;
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  WFrag<WF, MATS> ring[NB][KPW];
+  u32x4 xcur[KPW][DX];
+  int u = u_begin;
+  while (u < u_end) {
+    const int gi = u / a.n_tiles;
+    const int t_begin = u - gi * a.n_tiles;
+    const int t_end = min(a.n_tiles, u_end - gi * a.n_tiles);
+    const int ai = uniform(s_gexp[gi]);
+    const int g0 = (gi - uniform(s_gbase[ai])) * 16;
+    issue_x(ai, g0, xcur);
+#pragma unroll
+    for (int s = 0; s < NB - 1; ++s) issue_w(ai, t_begin + s < t_end ? t_begin + s : -1, ring[s]);
+    for (int t = t_begin; t < t_end; t += NB) {
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        const int ta = t + s + NB - 1;  // the tile issued at this step
+        issue_w(ai, ta < t_end ? ta : -1, ring[(s + NB - 1) % NB]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + s < t_end) finish(ai, g0, t + s, ring[s], xcur);
+      }
+    }
+    u = gi * a.n_tiles + t_end;
+  }
+}
+
 }  // namespace ft

@@ -260,6 +260,8 @@ FFN_CASES = [
     ("fp4-small", 3, dict(H=1024, I=512, E=6, k=2), 37),
     ("fp4-long-segment", 3, dict(H=512, I=1024, E=2, k=1), 150),
     ("fp4-cfg3-T1", 3, {}, 1),
+    ("fp4-decode-multigroup", 3, dict(H=512, I=256, E=3, k=2), 60),     # ~40 tokens per expert: 3 groups each
+    ("fp4-decode-T64-E16", 3, dict(H=1024, I=1024, E=16, k=4), 64),
     ("bf16-gemm-ragged", 2, dict(H=512, I=384, E=8, k=2), 200),
     ("fp4-gemm-many-tiles", 3, dict(H=512, I=768, E=24, k=3), 700),
 ]
