@@ -16,6 +16,13 @@ neither format.  Both are taken from their published definitions:
 Storage layout read here (the repository's reading, fixed for both sides):
 element 2i of a row is the low nibble of byte i, element 2i+1 the high nibble;
 scale j of a row covers elements 32j .. 32j+31 of that row.
+
+The pages also name NVFP4 (the Qwen3.6 laptop build and GLM-5.2's routed
+experts: FreeToken quantization page, results and hardware tables) without
+defining it.  Taken from NVIDIA's published description of the format: FP4
+E2M1 elements in blocks of 16 that share one FP8 E4M3 scale, and one FP32
+scale per tensor; an element is E2M1 x E4M3(block scale) x tensor scale.
+Same nibble order as MXFP4; scale j of a row covers elements 16j .. 16j+15.
 """
 from __future__ import annotations
 
@@ -72,6 +79,28 @@ def mxfp4_to_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return vals * sc
 
 
+def nvfp4_to_f64(codes: np.ndarray, scales: np.ndarray, tensor_scale) -> np.ndarray:
+    """Decode one NVFP4 matrix.
+
+    codes [rows, K/2] uint8, scales [rows, K/16] uint8 (E4M3 codes), tensor_scale
+    (a float32 value) -> float64 [rows, K]: E2M1(nibble) * E4M3(block scale) *
+    tensor_scale.
+    """
+    from .mx import e4m3_to_f64
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    rows, half = codes.shape
+    K = 2 * half
+    if scales.shape != (rows, K // 16) or K % 16:
+        raise ValueError("scale array does not match the code array")
+    nib = np.empty((rows, K), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    vals = e2m1_to_f64(nib)
+    sc = np.repeat(e4m3_to_f64(scales), 16, axis=1)
+    return vals * sc * float(np.float32(tensor_scale))
+
+
 def expert_to_f64(fmt: str, arrays: dict) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """An expert's (W_gate [I,H], W_up [I,H], W_down [H,I]) as float64."""
     if fmt == "f32":
@@ -82,6 +111,10 @@ def expert_to_f64(fmt: str, arrays: dict) -> tuple[np.ndarray, np.ndarray, np.nd
     if fmt == "mxfp4":
         return tuple(mxfp4_to_f64(arrays[f"{n}_codes"], arrays[f"{n}_scales"])
                      for n in ("gate", "up", "down"))
+    if fmt == "nvfp4":
+        ts = np.asarray(arrays["tensor_scales"], dtype=np.float32)
+        return tuple(nvfp4_to_f64(arrays[f"{n}_codes"], arrays[f"{n}_scales"], ts[i])
+                     for i, n in enumerate(("gate", "up", "down")))
     raise ValueError(fmt)
 
 

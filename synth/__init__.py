@@ -47,7 +47,7 @@ class LayerConfig:
     I: int                 # expert intermediate size (contraction axis of down)
     E: int                 # routed experts per layer
     k: int                 # experts selected per token
-    wdtype: str            # 'f32' | 'bf16' | 'mxfp4'
+    wdtype: str            # 'f32' | 'bf16' | 'mxfp4' | 'nvfp4'
     xdtype: str            # 'f32' | 'bf16'
     gating: str            # 'softmax' | 'sigmoid'
     renormalize: bool
@@ -62,6 +62,8 @@ class LayerConfig:
     w_std: float = 0.02
     x_std: float = 1.0
     scale_bytes: tuple = (119, 123)  # inclusive range of E8M0 scale bytes
+    nv_scale_codes: tuple = (0x30, 0x40)  # inclusive range of E4M3 block-scale codes (0.5 .. 2.0)
+    nv_tensor_scale: tuple = (0.01, 0.03)  # range of the per-tensor fp32 scale
 
 
 CONFIGS = {
@@ -80,6 +82,12 @@ CONFIGS = {
                    wdtype="mxfp4", xdtype="bf16", gating="sigmoid", renormalize=False,
                    shared=True, batches=(1,), logits_given=True, n_layers=8,
                    capacity=512, steps=512, zipf_s=1.1, reuse_p=0.6),
+    6: LayerConfig(6, "qwen3-a3b-shaped-nvfp4-decode", H=2048, I=768, E=128, k=8,
+                   wdtype="nvfp4", xdtype="bf16", gating="softmax", renormalize=True,
+                   shared=False, batches=(1, 16, 64)),
+    7: LayerConfig(7, "qwen3-a3b-shaped-nvfp4-prefill", H=2048, I=768, E=128, k=8,
+                   wdtype="nvfp4", xdtype="bf16", gating="softmax", renormalize=True,
+                   shared=False, batches=(8192,), logits_given=True, zipf_s=1.1),
 }
 
 
@@ -142,6 +150,8 @@ class ExpertWeights:
     Dense formats: ``wg``/``wu`` [I, H], ``wd`` [H, I] (row-major, contraction
     axis contiguous).  MXFP4: ``*_codes`` [rows, K/2] uint8 and ``*_scales``
     [rows, K/32] uint8 with K the contraction axis of that projection.
+    NVFP4: the same codes, ``*_scales`` [rows, K/16] uint8 (E4M3 codes) and
+    ``tensor_scales`` float32 [3] (gate, up, down).
     """
 
     fmt: str
@@ -172,6 +182,19 @@ def expert_weights(cfg: LayerConfig, layer: int, expert: int) -> ExpertWeights:
             "down_scales": rng.integers(lo, hi + 1, size=(H, I // 32), dtype=np.uint8),
         }
         return ExpertWeights("mxfp4", a)
+    if cfg.wdtype == "nvfp4":
+        lo, hi = cfg.nv_scale_codes
+        t_lo, t_hi = cfg.nv_tensor_scale
+        a = {
+            "gate_codes": rng.integers(0, 256, size=(I, H // 2), dtype=np.uint8),
+            "up_codes": rng.integers(0, 256, size=(I, H // 2), dtype=np.uint8),
+            "down_codes": rng.integers(0, 256, size=(H, I // 2), dtype=np.uint8),
+            "gate_scales": rng.integers(lo, hi + 1, size=(I, H // 16), dtype=np.uint8),
+            "up_scales": rng.integers(lo, hi + 1, size=(I, H // 16), dtype=np.uint8),
+            "down_scales": rng.integers(lo, hi + 1, size=(H, I // 16), dtype=np.uint8),
+            "tensor_scales": rng.uniform(t_lo, t_hi, size=3).astype(np.float32),
+        }
+        return ExpertWeights("nvfp4", a)
     raise ValueError(cfg.wdtype)
 
 

@@ -42,3 +42,14 @@ def test_prefill_logits_are_skewed():
     counts = np.bincount(ids.ravel(), minlength=cfg.E)
     top = synth.rank_to_expert(cfg, 0)[0]
     assert counts.argmax() == top and counts[top] > 0.7 * 2048
+
+
+def test_nvfp4_shapes_and_ranges():
+    cfg = synth.shrink(synth.CONFIGS[6], H=128, I=64, E=8)
+    w = synth.expert_weights(cfg, 0, 2)
+    assert w.fmt == "nvfp4"
+    assert w["gate_codes"].shape == (64, 64) and w["down_codes"].shape == (128, 32)
+    assert w["gate_scales"].shape == (64, 8) and w["down_scales"].shape == (128, 4)
+    assert w["gate_scales"].min() >= 0x30 and w["gate_scales"].max() <= 0x40
+    ts = w["tensor_scales"]
+    assert ts.dtype == np.float32 and ts.shape == (3,) and (ts >= 0.01).all() and (ts <= 0.03).all()
