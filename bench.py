@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """MoE-layer throughput on one MI355X, with the roofline of its dominant kernel.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode-bf16|decode-mxfp4|prefill-mxfp4|cache-trace]
+    python bench.py [--steps K] [--warmup W] [--workload decode-bf16|decode-mxfp4|decode-nvfp4|prefill-mxfp4|...]
 
 A step is one pass of the whole layer -- route, permute, grouped SwiGLU FFN
 (weights through the slot table), combine; plus the cache step for the
@@ -95,6 +95,8 @@ def expert_weight_bytes(cfg, part):
     n = cfg.H * cfg.I
     if cfg.wdtype == "mxfp4":
         one = n // 2 + n // 32
+    elif cfg.wdtype == "nvfp4":
+        one = n // 2 + n // 16 + 4   # codes, E4M3 block scales, the fp32 tensor scale
     elif cfg.wdtype == "bf16":
         one = 2 * n
     else:
@@ -242,13 +244,14 @@ def run_prefill(args, cfg, T, mode=0):
     layer = L.MoELayer(shape, T)
     t0 = time.time()
     pool = build_pool(L, layer, cfg, range(cfg.E), cfg.E)
-    shared = L.as_device_u8([L.pack_expert(layer.layout, synth.expert_weights(cfg, 0, cfg.E).arrays)])[0]
+    shared = L.as_device_u8([L.pack_expert(layer.layout, synth.expert_weights(cfg, 0, cfg.E).arrays)])[0] \
+        if cfg.shared else None
     n_sets = 2
     xs = [L.to_device(synth.tokens(cfg, T, case=r)) for r in range(n_sets)]
     lg = [L.to_device(synth.prefill_logits(cfg, T, case=r)) for r in range(n_sets)]
     torch.cuda.synchronize()
     log(f"prefill inputs built in {time.time() - t0:.1f}s")
-    rows = T * cfg.k + T
+    rows = T * cfg.k + (T if cfg.shared else 0)
     flops_gu = 2.0 * 2 * cfg.H * cfg.I * rows
     flops_all = 3.0 * 2 * cfg.H * cfg.I * rows
 
@@ -621,6 +624,10 @@ WORKLOADS = {
                        "renormalised, SwiGLU)"),
     "decode-mxfp4": (3, "dsv4-flash-shaped MXFP4 decode MoE layer (H=4096, I=2048, 256 experts top-6 sigmoid "
                         "+ 1 shared, SwiGLU)"),
+    "decode-nvfp4": (6, "qwen3-a3b-shaped NVFP4 decode MoE layer (H=2048, I=768, 128 experts, top-8 softmax "
+                        "renormalised, SwiGLU)"),
+    "prefill-nvfp4": (7, "qwen3-a3b-shaped NVFP4 prefill MoE layer (8192 tokens, H=2048, I=768, 128 experts "
+                         "top-8 softmax renormalised with Zipf(1.1) popularity, SwiGLU)"),
 }
 
 
@@ -683,10 +690,10 @@ def main():
         out = {
             "metric": METRIC, "value": p["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": p["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "mxfp8-a/mxfp4-w" if native else "mxfp4-w/bf16", "data": "synthetic",
+            "vs_baseline": None, "dtype": "mxfp8-a/mxfp4-w" if native else f"{cfg.wdtype}-w/bf16", "data": "synthetic",
             "config": {"workload": desc, "batch_tokens": T},
             "roofline": {"bound": "mfma",
-                         "kernel": "ffn_mx_gemm_kernel<gate_up>" if native else "ffn_gemm_kernel<mxfp4, gate_up>",
+                         "kernel": "ffn_mx_gemm_kernel<gate_up>" if native else f"ffn_gemm_kernel<{cfg.wdtype}, gate_up>",
                          "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
                          "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"]},
             "ffn_TFLOPs": p["flops_ffn"] / ((p["gate_up_ms"] + p["down_ms"]) * 1e-3) / 1e12,
@@ -696,7 +703,8 @@ def main():
     res = run_decode(args, cfg, batches, main_T)
     m = res[main_T]
     ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
-    kname = "ffn_persist_kernel<bf16, gate_up>" if cfg.wdtype == "bf16" else "ffn_persist_xs_kernel<mxfp4, gate_up>"
+    kname = "ffn_persist_kernel<bf16, gate_up>" if cfg.wdtype == "bf16" else \
+        f"ffn_persist_xs_kernel<{cfg.wdtype}, gate_up>"
     traffic = None
     if args.workload == "decode-bf16" and main_T == 64:
         traffic = measured_traffic("decode-bf16-T64_hbm_traffic.json", "void ft::ffn_persist_kernel<0, true,")
@@ -711,7 +719,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.wdtype == "bf16" else "mxfp4-w/bf16",
+        "dtype": "bf16" if cfg.wdtype == "bf16" else f"{cfg.wdtype}-w/bf16",
         "data": "synthetic",
         "config": {"workload": desc, "batch_tokens": main_T, "input_sets": N_INPUT_SETS,
                    "distinct_experts_per_step": m["distinct_experts"]},

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(PKG, "libftmoe.so")
 FT_OK, FT_EINVAL, FT_ENOTSUP, FT_ECAPACITY, FT_EHIP = 0, -1, -2, -3, -4
 STATUS_NAMES = {0: "FT_OK", -1: "FT_EINVAL", -2: "FT_ENOTSUP", -3: "FT_ECAPACITY", -4: "FT_EHIP"}
 # dtypes / gating / workspace selectors
-FT_F32, FT_BF16, FT_MXFP4 = 0, 1, 2
+FT_F32, FT_BF16, FT_MXFP4, FT_NVFP4 = 0, 1, 2, 3
 FT_SOFTMAX, FT_SIGMOID = 0, 1
 FT_WS_PERMUTE, FT_WS_FFN, FT_WS_ROUTE_PERMUTE = 1, 2, 3
 FT_FFN_EXACT, FT_FFN_NATIVE_MX = 0, 1
@@ -35,6 +35,7 @@ class ExpertLayout(C.Structure):
         ("expert_bytes", C.c_uint64),
         ("off_gate", C.c_uint64), ("off_up", C.c_uint64), ("off_down", C.c_uint64),
         ("off_sgate", C.c_uint64), ("off_sup", C.c_uint64), ("off_sdown", C.c_uint64),
+        ("off_tscale", C.c_uint64),
     ]
 
 

@@ -56,6 +56,17 @@ extern "C" ft_status ft_expert_layout_init(int32_t wdtype, int32_t H, int32_t I,
       L.off_sup = place(n / 32);
       L.off_sdown = place(n / 32);
       break;
+    case FT_NVFP4:
+      FT_REQUIRE(H % 16 == 0 && I % 16 == 0,
+                 "ft_expert_layout_init: NVFP4 needs H and I multiples of 16");
+      L.off_gate = place(n / 2);
+      L.off_up = place(n / 2);
+      L.off_down = place(n / 2);
+      L.off_sgate = place(n / 16);
+      L.off_sup = place(n / 16);
+      L.off_sdown = place(n / 16);
+      L.off_tscale = place(3 * 4);
+      break;
     default:
       return ft::fail(FT_EINVAL, "ft_expert_layout_init: unknown weight dtype");
   }

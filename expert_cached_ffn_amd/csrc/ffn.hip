@@ -199,7 +199,10 @@ static ft_status launch_stream(const FfnArgs &a, int a_max, int T, hipStream_t s
 
 // Weight register sets in flight for the x-stationary kernel, per shape.
 #ifndef FT_XS_NB
-#define FT_XS_NB(WF, GLU, WAVES, KPW) ((GLU) ? ((WAVES) >= 16 || (KPW) == 2 ? 2 : 4) : ((KPW) == 2 ? 4 : 6))
+// (NVFP4 tiles hold half the MXFP4 weight registers: deeper rings)
+#define FT_XS_NB(WF, GLU, WAVES, KPW)                                                     \
+  ((WF) == WF_NV4 ? ((GLU) ? ((WAVES) >= 16 ? 2 : 4) : 6)                                  \
+                  : ((GLU) ? ((WAVES) >= 16 || (KPW) == 2 ? 2 : 4) : ((KPW) == 2 ? 4 : 6)))
 #endif
 
 template <int WF, bool GLU, int WAVES, int KPW>
@@ -274,6 +277,15 @@ static void persist_override(bool glu, int nkb, int *waves, int *kpw) {
   }
 }
 
+// A persistent shape covers a contraction length K of weight format WF.
+template <int WF>
+static bool persist_covers(int K) {
+  if (K % stream_kblock<WF>() != 0) return false;
+  int waves, kpw;
+  persist_shape(K / stream_kblock<WF>(), &waves, &kpw);
+  return waves > 0;
+}
+
 template <int WF, bool GLU>
 static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stream) {
   int waves, kpw;
@@ -287,14 +299,14 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
     const char *v = getenv("FTMOE_PERSIST_XS");
     return v == nullptr ? -1 : (atoi(v) != 0);
   }();
-  const bool xs = xs_env < 0 ? WF == WF_FP4 : xs_env != 0;
+  const bool xs = WF == WF_NV4 || (xs_env < 0 ? WF == WF_FP4 : xs_env != 0);  // NVFP4: x-stationary only
 #define FT_PERSIST(W, C)                                                                          \
   if (waves == W && kpw == C) {                                                                   \
     if (xs) {                                                                                     \
       const void *kern = reinterpret_cast<const void *>(&ffn_persist_xs_kernel<WF, GLU, W, C>); \
       const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));                 \
       hipLaunchKernelGGL((ffn_persist_xs_kernel<WF, GLU, W, C>), dim3(g), dim3(W * 64), 0, stream, a); \
-    } else {                                                                                      \
+    } else if constexpr (WF != WF_NV4) {                                                          \
       const void *kern = reinterpret_cast<const void *>(&ffn_persist_kernel<WF, GLU, W, C>);      \
       const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));                 \
       hipLaunchKernelGGL((ffn_persist_kernel<WF, GLU, W, C>), dim3(g), dim3(W * 64), 0, stream, a); \
@@ -321,7 +333,7 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
 // need four times the weight registers: one workgroup per CU, so that
 // nothing spills.
 template <int WF, bool GLU>
-__global__ __launch_bounds__(kGemmThreads, WF == WF_BF16 ? 1 : 2) void ffn_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, WF == WF_FP4 ? 2 : 1) void ffn_gemm_kernel(GemmArgs a) {
   constexpr int B = kGemmBM * kGemmPitch;
   __shared__ __attribute__((aligned(16))) uint8_t l0[B];
   __shared__ __attribute__((aligned(16))) uint8_t l1[B];
@@ -499,6 +511,9 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   } else if (wd == FT_MXFP4) {
     FT_REQUIRE(x_dtype == FT_BF16, "ft_moe_grouped_ffn: MXFP4 weights need bf16 activations");
     FT_SUPPORTED(H % 256 == 0 && I % 256 == 0, "ft_moe_grouped_ffn: MXFP4 weights need H, I multiples of 256");
+  } else if (wd == FT_NVFP4) {
+    FT_REQUIRE(x_dtype == FT_BF16, "ft_moe_grouped_ffn: NVFP4 weights need bf16 activations");
+    FT_SUPPORTED(H % 128 == 0 && I % 128 == 0, "ft_moe_grouped_ffn: NVFP4 weights need H, I multiples of 128");
   } else {
     return fail(FT_EINVAL, "ft_moe_grouped_ffn: unknown weight dtype in layout");
   }
@@ -668,6 +683,8 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     p1.off_w1 = L->off_up;
     p1.off_s0 = L->off_sgate;
     p1.off_s1 = L->off_sup;
+    p1.off_t0 = L->off_tscale;
+    p1.off_t1 = L->off_tscale + 4;
     p1.K = H;
     p1.N = I;
     p1.sorted_rows = sorted_rows;
@@ -679,6 +696,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     p1.n_tiles = cdiv(I, 16);
     p2.off_w0 = p2.off_w1 = L->off_down;
     p2.off_s0 = p2.off_s1 = L->off_sdown;
+    p2.off_t0 = p2.off_t1 = L->off_tscale + 8;
     p2.K = I;
     p2.N = H;
     p2.sorted_rows = nullptr;
@@ -691,7 +709,13 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     p2.n_tiles = cdiv(H, 16);
     const int groups = cdiv(T, 16);
     // stage by stage; a contraction length no persistent shape covers uses the general kernel
-    if (wd == FT_BF16) {
+    // (NVFP4 has none: such shapes are not supported)
+    if (wd == FT_NVFP4) {
+      FT_SUPPORTED((!run1 || persist_covers<WF_NV4>(p1.K)) && (!run2 || persist_covers<WF_NV4>(p2.K)),
+                   "ft_moe_grouped_ffn: NVFP4 decode needs H/128 and I/128 in {4, 6, 8, 12, 16}");
+      if (run1) launch_persist<WF_NV4, true>(p1, a_max * p1.n_tiles * groups, stream);
+      if (run2) launch_persist<WF_NV4, false>(p2, a_max * p2.n_tiles * groups, stream);
+    } else if (wd == FT_BF16) {
       if (run1 && !launch_persist<WF_BF16, true>(p1, a_max * p1.n_tiles * groups, stream)) {
         const ft_status st = launch_stream<WF_BF16, true>(s1, a_max, T, stream, "ffn_stream_kernel<bf16, gate_up>");
         if (st != FT_OK) return st;
@@ -730,6 +754,8 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     g1.off_w1 = L->off_up;
     g1.off_s0 = L->off_sgate;
     g1.off_s1 = L->off_sup;
+    g1.off_t0 = L->off_tscale;
+    g1.off_t1 = L->off_tscale + 4;
     g1.K = H;
     g1.N = I;
     g1.sorted_rows = sorted_rows;
@@ -740,6 +766,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     g1.ldo = I;
     g2.off_w0 = g2.off_w1 = L->off_down;
     g2.off_s0 = g2.off_s1 = L->off_sdown;
+    g2.off_t0 = g2.off_t1 = L->off_tscale + 8;
     g2.K = I;
     g2.N = H;
     g2.sorted_rows = nullptr;
@@ -753,6 +780,9 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     if (wd == FT_BF16) {
       if (run1 && (st = launch_gemm<WF_BF16, true>(g1, stream, "ffn_gemm_kernel<bf16, gate_up>")) != FT_OK) return st;
       if (run2 && (st = launch_gemm<WF_BF16, false>(g2, stream, "ffn_gemm_kernel<bf16, down>")) != FT_OK) return st;
+    } else if (wd == FT_NVFP4) {
+      if (run1 && (st = launch_gemm<WF_NV4, true>(g1, stream, "ffn_gemm_kernel<nvfp4, gate_up>")) != FT_OK) return st;
+      if (run2 && (st = launch_gemm<WF_NV4, false>(g2, stream, "ffn_gemm_kernel<nvfp4, down>")) != FT_OK) return st;
     } else {
       if (run1 && (st = launch_gemm<WF_FP4, true>(g1, stream, "ffn_gemm_kernel<mxfp4, gate_up>")) != FT_OK) return st;
       if (run2 && (st = launch_gemm<WF_FP4, false>(g2, stream, "ffn_gemm_kernel<mxfp4, down>")) != FT_OK) return st;

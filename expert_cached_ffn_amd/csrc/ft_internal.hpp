@@ -95,6 +95,32 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t codes, float scale) {
   return r;
 }
 
+// FP8 E4M3 code (OCP, the low byte of `b`) -> fp32: v_cvt_f32_fp8 on gfx950
+// decodes OCP E4M3 (checked against the bit-field definition on all 256 codes).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8(int(b), 0); }
+
+// Eight NVFP4 codes (one dword) times an E4M3 block scale -> eight bf16.  The
+// scaled conversion instructions take only the exponent of their scale, so
+// the codes are converted to fp32 unscaled and multiplied by the full scale;
+// every E2M1 x E4M3 product has at most 6 significant bits, so the multiply
+// and the bf16 packing are exact.
+__device__ __forceinline__ bf16x8 nvfp4x8_to_bf16x8(uint32_t codes, float scale) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(p0[0] * scale);
+  r[1] = static_cast<__bf16>(p0[1] * scale);
+  r[2] = static_cast<__bf16>(p1[0] * scale);
+  r[3] = static_cast<__bf16>(p1[1] * scale);
+  r[4] = static_cast<__bf16>(p2[0] * scale);
+  r[5] = static_cast<__bf16>(p2[1] * scale);
+  r[6] = static_cast<__bf16>(p3[0] * scale);
+  r[7] = static_cast<__bf16>(p3[1] * scale);
+  return r;
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -51,6 +51,7 @@ struct GemmArgs {
   uint64_t expert_bytes;
   const uint8_t *shared_blob;     // NULL: none
   uint64_t off_w0, off_w1, off_s0, off_s1;
+  uint64_t off_t0, off_t1;        // NVFP4: byte offsets of the fp32 tensor scales of matrix 0 / 1
   int K, N;                       // contraction length, weight rows of one matrix
   const int32_t *offsets;         // [E+1]
   int E, T, k;
@@ -207,7 +208,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
 
   // ---- weights of this wave
   const uint32_t wpitch = (WF == WF_BF16) ? uint32_t(a.K) * 2 : uint32_t(a.K) / 2;
-  const uint32_t spitch = uint32_t(a.K) / 32;
+  const uint32_t spitch = uint32_t(a.K) / (WF == WF_NV4 ? 16 : 32);
   const uint32_t wbytes = uint32_t(a.N) * wpitch, sbytes = uint32_t(a.N) * spitch;
   rsrc_t wres[NT], sres[NT];
   uint32_t wrow[NT];
@@ -232,7 +233,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
   constexpr int DLW = WF == WF_BF16 ? 4 : 1;  // 16-byte weight loads per tile per chunk
   struct BFrag {
     u32x4 w[NT][DLW];
-    uint32_t s[NT];
+    std::conditional_t<WF == WF_NV4, u32x2, uint32_t> s[NT];  // the chunk's block scales (4 E8M0 / 8 E4M3)
   };
   const int nch = a.K / kGemmBK;
   // A chunk past the end is still issued, with out-of-range offsets (no memory
@@ -248,7 +249,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
           f.w[t][d] = bld16(wres[t], live ? wrow[t] * wpitch + uint32_t(c) * 256u + d * 64 + q * 16 : kOOB);
       } else {
         f.w[t][0] = bld16(wres[t], live ? wrow[t] * wpitch + uint32_t(c) * 64u + q * 16 : kOOB);
-        f.s[t] = bld4(sres[t], live ? wrow[t] * spitch + uint32_t(c) * 4u : kOOB);
+        if constexpr (WF == WF_NV4)
+          f.s[t] = bld8(sres[t], live ? wrow[t] * spitch + uint32_t(c) * 8u : kOOB);
+        else
+          f.s[t] = bld4(sres[t], live ? wrow[t] * spitch + uint32_t(c) * 4u : kOOB);
       }
     }
   };
@@ -301,8 +305,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
         bf16x8 bw[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          if constexpr (WF == WF_BF16) bw[t] = as_bf16x8(f.w[t][ks]);
-          else bw[t] = fp4x8_to_bf16x8(f.w[t][0][ks], e8m0_to_f32((f.s[t] >> (8 * q)) & 0xffu));
+          if constexpr (WF == WF_BF16) {
+            bw[t] = as_bf16x8(f.w[t][ks]);
+          } else if constexpr (WF == WF_FP4) {
+            bw[t] = fp4x8_to_bf16x8(f.w[t][0][ks], e8m0_to_f32((f.s[t] >> (8 * q)) & 0xffu));
+          } else {  // NVFP4: elements 32q + 8ks .. +7 lie in 16-element block 2q + ks/2
+            const uint32_t sw = (q >> 1) ? f.s[t][1] : f.s[t][0];
+            bw[t] = nvfp4x8_to_bf16x8(f.w[t][0][ks], e4m3_to_f32(sw >> (8 * ((2 * q + (ks >> 1)) & 3))));
+          }
         }
         const int j = WF == WF_BF16 ? 4 * ks + q : 4 * q + ks;  // 16-byte chunk of the row
 #pragma unroll
@@ -321,6 +331,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
   wait_vmcnt<0>();
 
   // ---- epilogue: lane holds D[token 4q+v][weight row r] of each tile
+  float ts0 = 1.f, ts1 = 1.f;  // NVFP4: the per-tensor scales, on the fp32 sums
+  if constexpr (WF == WF_NV4) {
+    ts0 = *reinterpret_cast<const float *>(blob + a.off_t0);
+    ts1 = *reinterpret_cast<const float *>(blob + a.off_t1);
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -333,7 +348,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int col = nt_idx * (kGemmBN / 2) + wave * 32 + t * 16 + r;
-          if (col < a.N) hp[col] = f32_to_bf16_rne(silu(acc[i][t][v]) * acc[i][t + 2][v]);
+          if (col < a.N) hp[col] = f32_to_bf16_rne(silu(acc[i][t][v] * ts0) * (acc[i][t + 2][v] * ts1));
         }
       } else {
         float *yp = shared ? a.out_shared + int64_t(row0 + rr) * a.ldo
@@ -341,7 +356,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int col = nt_idx * kGemmBN + wave * 64 + t * 16 + r;
-          if (col < a.N) yp[col] = acc[i][t][v];
+          if (col < a.N) yp[col] = acc[i][t][v] * ts0;
         }
       }
     }

@@ -37,13 +37,14 @@
 
 namespace ft {
 
-enum { WF_BF16 = 0, WF_FP4 = 1 };
+// weight formats of the streaming kernels: bf16, MXFP4, NVFP4
+enum { WF_BF16 = 0, WF_FP4 = 1, WF_NV4 = 2 };
 
 constexpr int kStreamMaxTok = 64;  // tokens per pass (4 MFMA column tiles)
 
 // Elements of the contraction axis per k-block.
 template <int WF>
-constexpr int stream_kblock() { return WF == WF_BF16 ? 128 : 256; }
+constexpr int stream_kblock() { return WF == WF_FP4 ? 256 : 128; }
 
 // LDS floats needed by stream_tile<.., GLU, NT, WAVES>.
 template <bool GLU, int NT, int WAVES>
@@ -51,7 +52,7 @@ constexpr int stream_red_floats() { return WAVES * (GLU ? 2 : 1) * NT * 256; }
 
 template <int WF, int MATS>
 struct WFrag {
-  static constexpr int DL = WF == WF_BF16 ? 4 : 2;  // 16-byte weight loads per lane per k-block
+  static constexpr int DL = WF == WF_BF16 ? 4 : (WF == WF_FP4 ? 2 : 1);  // 16-byte weight loads per lane per k-block
   u32x4 w[MATS][DL];
   u32x2 s[MATS];
 };

@@ -28,6 +28,7 @@ struct PersistArgs {
   uint64_t expert_bytes;
   const uint8_t *shared_blob;     // NULL: none
   uint64_t off_w0, off_w1, off_s0, off_s1;
+  uint64_t off_t0, off_t1;        // NVFP4: byte offsets of the fp32 tensor scales of matrix 0 / 1
   int K, N;                       // contraction length, weight rows
   const int32_t *offsets;         // [E+1]
   int E, T, k;
@@ -305,7 +306,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
   constexpr int MATS = GLU ? 2 : 1;
   constexpr int KB = stream_kblock<WF>();
   constexpr int DL = WFrag<WF, MATS>::DL;
-  constexpr int DX = WF == WF_BF16 ? 4 : 8;
+  constexpr int DX = WF == WF_FP4 ? 8 : 4;
   __shared__ int s_e[kPersistMaxE + 1];      // expert id (E = shared expert)
   __shared__ int s_pos[kPersistMaxE + 1];    // first permuted row of its segment
   __shared__ int s_m[kPersistMaxE + 1];      // rows of its segment
@@ -393,7 +394,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
   const int u_end = int(int64_t(n_units) * (blockIdx.x + 1) / gridDim.x);
 
   const uint32_t wpitch = (WF == WF_BF16) ? uint32_t(a.K) * 2 : uint32_t(a.K) / 2;
-  const uint32_t spitch = uint32_t(a.K) / 32;
+  const uint32_t spitch = uint32_t(a.K) / (WF == WF_NV4 ? 16 : 32);
   const uint32_t wbytes = uint32_t(a.N) * wpitch, sbytes = uint32_t(a.N) * spitch;
   const rsrc_t xres = make_rsrc(a.X, a.x_bytes);
 
@@ -419,7 +420,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
       for (int mt = 0; mt < MATS; ++mt) {
 #pragma unroll
         for (int d = 0; d < DL; ++d) f[c].w[mt][d] = bld16(wres[mt], wo + uint32_t(kb) * (DL * 64) + d * 64);
-        if constexpr (WF == WF_FP4) f[c].s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);
+        if constexpr (WF != WF_BF16) f[c].s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);  // 8 blocks
       }
     }
   };
@@ -438,14 +439,17 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
       const int kb = wave + c * WAVES;
 #pragma unroll
       for (int dx = 0; dx < DX; ++dx) {
-        const int ko = WF == WF_BF16 ? kb * KB + 32 * dx + 8 * q : kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3);
+        const int ko = WF == WF_BF16  ? kb * KB + 32 * dx + 8 * q
+                       : WF == WF_FP4 ? kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3)
+                                      : kb * KB + 32 * q + 8 * dx;
         xb[c][dx] = bld16(xres, xo + uint32_t(ko) * 2u);
       }
     }
   };
   // Multiply one tile of group (ai, g0), sum the wave partials in LDS, write
   // its 16x16 output tile.
-  auto finish = [&](int ai, int g0, int tile, const WFrag<WF, MATS> (&f)[KPW], const u32x4 (&xcur)[KPW][DX]) {
+  auto finish = [&](int ai, int g0, int tile, const WFrag<WF, MATS> (&f)[KPW], const u32x4 (&xcur)[KPW][DX],
+                    float ts0, float ts1) {
     const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]), pos = uniform(s_pos[ai]), m = uniform(s_m[ai]);
     const bool shared = e == a.E;
     const bool missing = !shared && slot < 0;
@@ -459,7 +463,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
         for (int d = 0; d < 4; ++d)
 #pragma unroll
           for (int mt = 0; mt < MATS; ++mt) acc[mt] = mfma16(as_bf16x8(f[c].w[mt][d]), as_bf16x8(xcur[c][d]), acc[mt]);
-      } else {
+      } else if constexpr (WF == WF_FP4) {
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
           float sc[MATS];
@@ -471,6 +475,17 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
             for (int mt = 0; mt < MATS; ++mt)
               acc[mt] = mfma16(fp4x8_to_bf16x8(f[c].w[mt][d][mm], sc[mt]), as_bf16x8(xcur[c][4 * d + mm]), acc[mt]);
         }
+      } else {
+        // NVFP4: lane (r, q) holds elements 32q .. 32q+31 of the k-block (16-element
+        // blocks 2q and 2q+1); word mm covers 32q + 8mm .. +7, block 2q + mm/2.
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+          for (int mt = 0; mt < MATS; ++mt) {
+            const uint32_t sw = (q >> 1) ? f[c].s[mt][1] : f[c].s[mt][0];
+            const float sc = e4m3_to_f32(sw >> (8 * ((2 * q + (mm >> 1)) & 3)));
+            acc[mt] = mfma16(nvfp4x8_to_bf16x8(f[c].w[mt][0][mm], sc), as_bf16x8(xcur[c][mm]), acc[mt]);
+          }
       }
     }
 #pragma unroll
@@ -486,6 +501,10 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
       for (int w = 0; w < WAVES; ++w) {
         g += s_red[((w * MATS + 0) * 64 + ln) * 4 + v];
         if constexpr (GLU) uu += s_red[((w * MATS + 1) * 64 + ln) * 4 + v];
+      }
+      if constexpr (WF == WF_NV4) {  // the per-tensor scales, on the fp32 sums
+        g *= ts0;
+        if constexpr (GLU) uu *= ts1;
       }
       if (jj < m && n < a.N) {
         const int p = pos + jj;  // permuted row; hidden rows of the shared expert follow the routed ones
@@ -510,6 +529,13 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     const int t_end = min(a.n_tiles, u_end - gi * a.n_tiles);
     const int ai = uniform(s_gexp[gi]);
     const int g0 = (gi - uniform(s_gbase[ai])) * 16;
+    float ts0 = 1.f, ts1 = 1.f;  // NVFP4 tensor scales of this expert, loaded once per group
+    if constexpr (WF == WF_NV4) {
+      const int e = uniform(s_e[ai]), slot = uniform(s_slot[ai]);
+      const uint8_t *blob = e == a.E ? a.shared_blob : a.pool + uint64_t(max(slot, 0)) * a.expert_bytes;
+      ts0 = *reinterpret_cast<const float *>(blob + a.off_t0);
+      if constexpr (GLU) ts1 = *reinterpret_cast<const float *>(blob + a.off_t1);
+    }
     issue_x(ai, g0, xcur);
 #pragma unroll
     for (int s = 0; s < NB - 1; ++s) issue_w(ai, t_begin + s < t_end ? t_begin + s : -1, ring[s]);
@@ -519,7 +545,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
         const int ta = t + s + NB - 1;  // the tile issued at this step
         issue_w(ai, ta < t_end ? ta : -1, ring[(s + NB - 1) % NB]);
         __builtin_amdgcn_sched_barrier(0);
-        if (t + s < t_end) finish(ai, g0, t + s, ring[s], xcur);
+        if (t + s < t_end) finish(ai, g0, t + s, ring[s], xcur, ts0, ts1);
       }
     }
     u = gi * a.n_tiles + t_end;

@@ -14,7 +14,7 @@ import torch
 
 from . import _lib, ops
 
-DTYPES = {"f32": _lib.FT_F32, "bf16": _lib.FT_BF16, "mxfp4": _lib.FT_MXFP4}
+DTYPES = {"f32": _lib.FT_F32, "bf16": _lib.FT_BF16, "mxfp4": _lib.FT_MXFP4, "nvfp4": _lib.FT_NVFP4}
 GATING = {"softmax": _lib.FT_SOFTMAX, "sigmoid": _lib.FT_SIGMOID}
 
 _DENSE_PARTS = (("wg", "off_gate"), ("wu", "off_up"), ("wd", "off_down"))
@@ -26,7 +26,9 @@ def pack_expert(layout, arrays: dict, out: np.ndarray | None = None) -> np.ndarr
     """One expert's storage arrays -> its blob bytes (uint8 [expert_bytes])."""
     eb = int(layout.expert_bytes)
     blob = np.zeros(eb, np.uint8) if out is None else out
-    parts = _FP4_PARTS if layout.wdtype == _lib.FT_MXFP4 else _DENSE_PARTS
+    parts = _FP4_PARTS if layout.wdtype in (_lib.FT_MXFP4, _lib.FT_NVFP4) else _DENSE_PARTS
+    if layout.wdtype == _lib.FT_NVFP4:
+        parts = parts + (("tensor_scales", "off_tscale"),)
     for name, off in parts:
         a = np.ascontiguousarray(arrays[name]).view(np.uint8).ravel()
         o = int(getattr(layout, off))

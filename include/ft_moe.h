@@ -63,7 +63,7 @@ const char *ft_last_error(void);
 /* Library version string, e.g. "ftmoe 0.1 gfx950". */
 const char *ft_version(void);
 
-typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2 } ft_dtype;
+typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2, FT_NVFP4 = 3 } ft_dtype;
 typedef enum { FT_SOFTMAX = 0, FT_SIGMOID = 1 } ft_gating;
 
 /* ------------------------------------------------------------------------ */
@@ -84,6 +84,11 @@ typedef enum { FT_SOFTMAX = 0, FT_SIGMOID = 1 } ft_gating;
  *   bits 3:0 and element 2i+1 in bits 7:4 of byte i, FP4 E2M1 values;
  *   scales [rows, K/32] bytes, E8M0 (2^(byte-127)), one per 32 consecutive
  *   elements of a row along its contraction axis K.
+ * FT_NVFP4 (named on FreeToken's quantization page, results and hardware
+ *   tables; format as NVIDIA publishes it): the same codes; scales
+ *   [rows, K/16] bytes, FP8 E4M3 (OCP), one per 16 consecutive elements; and
+ *   three fp32 tensor scales (gate, up, down) at off_tscale.  Element =
+ *   E2M1 x E4M3(block scale) x tensor scale.
  */
 typedef struct {
   int32_t wdtype;        /* ft_dtype of the expert weights                     */
@@ -91,12 +96,13 @@ typedef struct {
   int32_t reserved;
   uint64_t expert_bytes; /* bytes of one blob (a multiple of 4096)             */
   uint64_t off_gate, off_up, off_down;      /* byte offsets of the three parts */
-  uint64_t off_sgate, off_sup, off_sdown;   /* MXFP4 scale parts (0 otherwise) */
+  uint64_t off_sgate, off_sup, off_sdown;   /* MXFP4 / NVFP4 scale parts (0 otherwise) */
+  uint64_t off_tscale;   /* NVFP4: 3 fp32 tensor scales (gate, up, down); 0 otherwise */
 } ft_expert_layout;
 
 /* Fill *out for experts of type wdtype.  Host only, pure.
  * Errors: FT_EINVAL (out NULL, H or I < 1, unknown dtype, MXFP4 with H or I
- * not a multiple of 32). */
+ * not a multiple of 32, NVFP4 with H or I not a multiple of 16). */
 ft_status ft_expert_layout_init(int32_t wdtype, int32_t H, int32_t I, ft_expert_layout *out);
 
 /* ------------------------------------------------------------------------ */

@@ -53,7 +53,12 @@ def test_layouts():
     assert L.expert_bytes == 9_437_184 and L.off_up == 3_145_728 and L.off_down == 6_291_456
     L = ops.ft_expert_layout_init(0, 256, 128)
     assert L.expert_bytes == 393_216
-    for bad in [(2, 100, 64), (7, 64, 64), (1, 0, 64)]:
+    L = ops.ft_expert_layout_init(3, 2048, 768)    # NVFP4 on the Qwen3-A3B shape
+    assert (L.off_gate, L.off_up, L.off_down) == (0, 786_432, 1_572_864)
+    assert (L.off_sgate, L.off_sup, L.off_sdown) == (2_359_296, 2_457_600, 2_555_904)  # K/16 scale bytes per row
+    assert L.off_tscale == 2_654_208 and L.expert_bytes == 2_658_304
+    assert ops.ft_expert_layout_init(2, 2048, 768).off_tscale == 0
+    for bad in [(2, 100, 64), (7, 64, 64), (1, 0, 64), (3, 2040, 768)]:
         with pytest.raises(ops.FtError) as e:
             ops.ft_expert_layout_init(*bad)
         assert e.value.status == -1
@@ -113,6 +118,10 @@ def test_ffn_validation():
     assert _err(f, L4, 256, None, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 0,
                 workspace=256, workspace_bytes=16, stream=0) == -1                                # workspace
     assert _err(f, L4, 256, None, None, 256, 1, 1, 7, 6, 256, 256, 256, None, 0, **ok) == -2     # k > E
+    Lnv = ops.ft_expert_layout_init(3, 2048, 768)
+    assert _err(f, Lnv, 256, None, None, 256, 1, 1, 8, 128, 256, 256, 256, None, 1, **ok) == -2  # mode 1, NVFP4
+    assert _err(f, ops.ft_expert_layout_init(3, 2048, 784), 256, None, None, 256, 1, 1, 8, 128, 256, 256, 256,
+                None, 0, **ok) == -2                                                              # NVFP4 I % 128
 
 
 def test_mxfp8_quantize_validation():

@@ -72,10 +72,11 @@ def test_cpu_expert_matches_oracle(ops, isa, name, cfg_id, over, n):
 
 def test_cpu_expert_validation(ops):
     from expert_cached_ffn_amd.layer import DTYPES
-    lay = ops.ft_expert_layout_init(DTYPES["f32"], 256, 128)
-    with pytest.raises(ops.FtError) as e:
-        ops.ft_cpu_expert_ffn(lay, np.zeros(8, np.uint8), np.zeros(8, np.uint16), 1, np.zeros(8, np.float32))
-    assert e.value.status == -2
+    for wd in ("f32", "nvfp4"):
+        lay = ops.ft_expert_layout_init(DTYPES[wd], 256, 128)
+        with pytest.raises(ops.FtError) as e:
+            ops.ft_cpu_expert_ffn(lay, np.zeros(8, np.uint8), np.zeros(8, np.uint16), 1, np.zeros(8, np.float32))
+        assert e.value.status == -2
     lay = ops.ft_expert_layout_init(DTYPES["mxfp4"], 512, 256)
     with pytest.raises(ops.FtError) as e:
         ops.ft_cpu_expert_ffn(lay, None, np.zeros(8, np.uint16), 1, np.zeros(8, np.float32))

@@ -45,7 +45,7 @@ def out_f64(layer, cfg, T):
 
 
 @pytest.mark.parametrize("cfg_id,T,sample", [(1, 8, None), (2, 1, None), (2, 16, None), (2, 64, 12),
-                                             (3, 1, None), (3, 8, 4), (3, 32, 4)])
+                                             (3, 1, None), (3, 8, 4), (3, 32, 4), (6, 1, None), (6, 64, 12)])
 def test_layer_router_gemv(L, cfg_id, T, sample):
     cfg = synth.CONFIGS[cfg_id]
     print(f"layer cfg{cfg_id} T={T}", flush=True)
@@ -111,3 +111,32 @@ def test_layer_prefill_given_logits(L):
                         what="prefill mode 1 sampled tokens", allow=np.stack([p[1] for p in pairs]))
             yref, allow = native_mx_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
             check_close(yr, yref, what=f"prefill mode 1 segment of expert {e}", allow=allow)
+
+
+def test_layer_prefill_nvfp4(L):
+    """NVFP4 prefill workload (8192 tokens on the Qwen3-A3B shape): sampled tokens and one expert's segment."""
+    cfg = synth.CONFIGS[7]
+    T = 8192
+    ex = Experts(cfg)
+    x = synth.tokens(cfg, T)
+    logits = synth.prefill_logits(cfg, T)
+    ids = moe.topk(logits, cfg.k)
+    w = moe.gating_weights(logits, ids, cfg.gating, cfg.renormalize)
+    layer = make_layer(L, cfg, T)
+    print("nvfp4 prefill: packing 128 experts", flush=True)
+    pool = build_pool(L, layer, ex, range(cfg.E), cfg.E)
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    layer.forward(T, L.to_device(x), pool, logits=L.to_device(logits))
+    torch.cuda.synchronize()
+    assert np.array_equal(layer.ids[:T].cpu().numpy(), ids)
+    got = out_f64(layer, cfg, T)
+    assert np.all(np.isfinite(got))
+    toks = [0, 3000, T - 1]
+    ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64) for t in toks])
+    check_close(got[toks], ref, bf16_out=True, what="nvfp4 prefill sampled tokens")
+    off_ref, rows_ref, _ = moe.permute(ids, cfg.E)
+    sizes = np.diff(off_ref)
+    e = int(np.argmax(sizes))                                  # the most popular expert: many token tiles
+    a, b = int(off_ref[e]), int(off_ref[e + 1])
+    yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
+    check_close(layer.y_rows[a:b].cpu().numpy(), yref, what=f"nvfp4 prefill segment of expert {e}")

@@ -262,6 +262,12 @@ FFN_CASES = [
     ("fp4-cfg3-T1", 3, {}, 1),
     ("fp4-decode-multigroup", 3, dict(H=512, I=256, E=3, k=2), 60),     # ~40 tokens per expert: 3 groups each
     ("fp4-decode-T64-E16", 3, dict(H=1024, I=1024, E=16, k=4), 64),
+    ("nv4-decode-small", 6, dict(H=512, I=512, E=6, k=2), 37),
+    ("nv4-decode-shared", 6, dict(H=1024, I=768, E=8, k=2, shared=True), 9),
+    ("nv4-decode-multigroup", 6, dict(H=512, I=768, E=3, k=2), 60),
+    ("nv4-decode-cfg6-T16", 6, {}, 16),
+    ("nv4-prefill-ragged", 6, dict(H=512, I=384, E=8, k=2, shared=True), 200),
+    ("nv4-prefill-many-tiles", 6, dict(H=512, I=768, E=24, k=3), 700),
     ("bf16-gemm-ragged", 2, dict(H=512, I=384, E=8, k=2), 200),
     ("fp4-gemm-many-tiles", 3, dict(H=512, I=768, E=24, k=3), 700),
 ]
@@ -434,3 +440,13 @@ def test_combine_parity(ops, T, k, H, shared, bf16):
     else:
         got = out.cpu().numpy().astype(np.float64)
         np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+def test_grouped_ffn_nvfp4_decode_shape_not_covered(ops):
+    """NVFP4 decode needs a persistent shape for H/128 and I/128: others are refused, nothing written."""
+    cfg = synth.shrink(synth.CONFIGS[6], H=256, I=512, E=4, k=1)
+    T = 3
+    ids = synth.routing_ids_uniform(cfg, T)
+    with pytest.raises(ops.FtError) as e:
+        _ffn_case(ops, cfg, T, ids)
+    assert e.value.status == -2
