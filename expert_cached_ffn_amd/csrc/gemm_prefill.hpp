@@ -151,12 +151,17 @@ __device__ __forceinline__ void unroll_ring(F &&f, std::integer_sequence<int, J.
   (f(std::integral_constant<int, J>{}), ...);
 }
 
+// The multiply of one work item, with MT 16-row token sub-tiles per wave: a
+// segment's last tile often holds a few dozen rows, and running it with
+// MT = 4 or 2 skips the MFMAs of the sub-tiles that would only hold padding
+// (the loads of those rows are out of range anyway: no traffic).
+template <int WF, bool GLU, int NBUF, int MT>
+__device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, int nt_idx, int row0, int m,
+                                          bool shared, const uint8_t *blob);
+
 template <int WF, bool GLU, int NBUF>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
-  constexpr int NT = 4;   // weight tiles (16 rows) per wave
-  constexpr int MT = 8;   // token tiles (16 rows) per wave
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = lane & 15, q = lane >> 4;
+  const int tid = threadIdx.x;
 
   // ---- work item: block ids go round-robin over the 8 XCDs; give each XCD a
   // contiguous range of items (the grid is a multiple of 8)
@@ -189,6 +194,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
     blob = a.pool + uint64_t(slot) * a.expert_bytes;
   }
 
+  if (m > 64)
+    gemm_body<WF, GLU, NBUF, 8>(a, L, nt_idx, row0, m, shared, blob);
+  else if (m > 32)
+    gemm_body<WF, GLU, NBUF, 4>(a, L, nt_idx, row0, m, shared, blob);
+  else
+    gemm_body<WF, GLU, NBUF, 2>(a, L, nt_idx, row0, m, shared, blob);
+}
+
+template <int WF, bool GLU, int NBUF, int MT>
+__device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, int nt_idx, int row0, int m,
+                                          bool shared, const uint8_t *blob) {
+  constexpr int NT = 4;   // weight tiles (16 rows) per wave
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, q = lane >> 4;
   // ---- token rows: wave w fills rows 32w..32w+31 of a chunk buffer with 8
   // direct loads of 4 rows each; lane i covers row 4t + i/16, slot i%16
   const rsrc_t xres = make_rsrc(a.X, a.x_bytes);
