@@ -13,6 +13,7 @@
 // fp32 weights use a plain FMA kernel.
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <unordered_map>
 
@@ -294,12 +295,11 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
   // x-stationary runs for MXFP4 weights (measured 1.65x at 32 tokens: a 16-row
   // FP4 tile is half the bytes of a bf16 one, so the freed activation
   // registers matter); bf16 tiles keep the strided order, measured faster
-  // there.  FTMOE_PERSIST_XS=0/1 overrides for tuning.
-  static const int xs_env = [] {
-    const char *v = getenv("FTMOE_PERSIST_XS");
-    return v == nullptr ? -1 : (atoi(v) != 0);
-  }();
-  const bool xs = WF == WF_NV4 || (xs_env < 0 ? WF == WF_FP4 : xs_env != 0);  // NVFP4: x-stationary only
+  // there.
+  // FTMOE_PERSIST_XS = "<gate/up><down>", each 0 or 1 (e.g. "01").
+  static const char *xs_env = getenv("FTMOE_PERSIST_XS");
+  const int xs_req = (xs_env && strlen(xs_env) == 2) ? xs_env[GLU ? 0 : 1] - '0' : -1;
+  const bool xs = WF == WF_NV4 || (xs_req < 0 ? WF == WF_FP4 : xs_req != 0);  // NVFP4: x-stationary only
 #define FT_PERSIST(W, C)                                                                          \
   if (waves == W && kpw == C) {                                                                   \
     if (xs) {                                                                                     \

@@ -159,22 +159,24 @@ template <int WF, bool GLU, int NBUF, int MT>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, int nt_idx, int row0, int m,
                                           bool shared, const uint8_t *blob);
 
-template <int WF, bool GLU, int NBUF>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
+// This workgroup's work item: the weight tile, the token tile's first row
+// and row count, the expert's blob.  False if there is none, or if the expert
+// is not resident (its outputs of this tile were then marked NaN).
+template <bool GLU>
+__device__ __forceinline__ bool gemm_setup(const GemmArgs &a, int &nt_idx, int &row0, int &m, bool &shared,
+                                           const uint8_t *&blob) {
   const int tid = threadIdx.x;
-
   // ---- work item: block ids go round-robin over the 8 XCDs; give each XCD a
   // contiguous range of items (the grid is a multiple of 8)
   const int G = int(gridDim.x), b = int(blockIdx.x);
   const int per = G / 8;
   const int logical = (b % 8) * per + b / 8;
-  if (logical >= a.n_items) return;
-  int nt_idx, mi;
-  if (!gemm_item(a, logical, &nt_idx, &mi)) return;
-  int e, row0, m;
-  if (!gemm_find_mtile<kGemmThreads>(a, mi, &e, &row0, &m)) return;
-  const bool shared = e == a.E;
-  const uint8_t *blob;
+  if (logical >= a.n_items) return false;
+  int mi;
+  if (!gemm_item(a, logical, &nt_idx, &mi)) return false;
+  int e;
+  if (!gemm_find_mtile<kGemmThreads>(a, mi, &e, &row0, &m)) return false;
+  shared = e == a.E;
   if (shared) {
     blob = a.shared_blob;
   } else {
@@ -189,11 +191,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
         if (GLU) reinterpret_cast<uint16_t *>(a.out)[int64_t(row0 + rr) * a.ldo + cc] = 0x7fc0;
         else reinterpret_cast<float *>(a.out)[int64_t(row0 + rr) * a.ldo + cc] = __builtin_nanf("");
       }
-      return;
+      return false;
     }
     blob = a.pool + uint64_t(slot) * a.expert_bytes;
   }
+  return true;
+}
 
+template <int WF, bool GLU, int NBUF>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, LdsRing<NBUF> L) {
+  int nt_idx, row0, m;
+  bool shared;
+  const uint8_t *blob;
+  if (!gemm_setup<GLU>(a, nt_idx, row0, m, shared, blob)) return;
   if (m > 64)
     gemm_body<WF, GLU, NBUF, 8>(a, L, nt_idx, row0, m, shared, blob);
   else if (m > 32)
