@@ -153,6 +153,8 @@ def run_decode(args, cfg, batches, main_T):
 
         def step(i, tm=None):
             x = xs[i % N_INPUT_SETS]
+            if tm is not None:
+                tm.mark()
             layer.route_permute(T, x=x, w_router=wr)
             if tm is not None:
                 tm.mark()
@@ -175,7 +177,9 @@ def run_decode(args, cfg, batches, main_T):
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
         ms = total_ms / args.steps
-        k_ms = [tm.ev[2 * i].elapsed_time(tm.ev[2 * i + 1]) for i in range(args.steps)]
+        k_ms = [tm.ev[3 * i + 1].elapsed_time(tm.ev[3 * i + 2]) for i in range(args.steps)]
+        step_ms = [tm.ev[3 * i].elapsed_time(tm.ev[3 * (i + 1)] if i + 1 < args.steps else end)
+                   for i in range(args.steps)]
         k_avg = float(np.mean(k_ms))
         act = np.array([n_act[i % N_INPUT_SETS] for i in range(args.steps)], np.float64)
         bytes_gu = float(np.mean((act + (1 if cfg.shared else 0)) * expert_weight_bytes(cfg, "gate_up")))
@@ -206,6 +210,7 @@ def run_decode(args, cfg, batches, main_T):
             torch.cuda.synchronize()
             graph_ms = start.elapsed_time(end) / args.steps
         results[T] = dict(ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), gate_up_ms=k_avg,
+                          step_ms_p10_p50_p90=[float(v) for v in np.percentile(step_ms, [10, 50, 90])],
                           gate_up_bytes=bytes_gu, layer_weight_bytes=layer_bytes,
                           distinct_experts=float(np.mean(n_act)), graph_ms_per_step=graph_ms)
         gtxt = f"{graph_ms * 1e3:.1f} us" if graph_ms is not None else "n/a"
@@ -227,6 +232,39 @@ def copy_calibration(nbytes=1 << 30, reps=3):
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"copy calibration: {reps} x {nbytes} B device copy")
+
+
+def achievable_peaks():
+    """What this machine reaches outside the library: a 1 GiB device copy (read + write bytes / time) and an
+    8192^3 bf16 GEMM through torch's BLAS (hipBLASLt); best of a few runs."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(5):
+        s.record()
+        b.copy_(a)
+        e.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * n / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del a, b
+    m = 8192
+    x = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    y = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    x @ y
+    torch.cuda.synchronize()
+    tf = 0.0
+    for _ in range(5):
+        s.record()
+        x @ y
+        e.record()
+        torch.cuda.synchronize()
+        tf = max(tf, 2 * m ** 3 / (s.elapsed_time(e) * 1e-3) / 1e12)
+    del x, y
+    log(f"achievable on this box: device copy {best:,.0f} GB/s (read + write), bf16 GEMM {tf:,.0f} TFLOP/s")
+    return {"copy_GBps": best, "bf16_gemm_TFLOPs": tf}
 
 
 def run_prefill(args, cfg, T, mode=0):
@@ -283,11 +321,13 @@ def run_prefill(args, cfg, T, mode=0):
     ms = start.elapsed_time(end) / args.steps
     gu = float(np.mean([tm.ev[3 * i].elapsed_time(tm.ev[3 * i + 1]) for i in range(args.steps)]))
     dn = float(np.mean([tm.ev[3 * i + 1].elapsed_time(tm.ev[3 * i + 2]) for i in range(args.steps)]))
+    ffn_ms = [tm.ev[3 * i].elapsed_time(tm.ev[3 * i + 2]) for i in range(args.steps)]
     log(f"prefill mode {mode} T={T}: {ms:.3f} ms/step ({T / (ms * 1e-3):,.0f} tok/s); gate/up {gu:.3f} ms = "
         f"{flops_gu / (gu * 1e-3) / 1e12:.0f} TFLOP/s, down {dn:.3f} ms = "
         f"{flops_all / 3 / (dn * 1e-3) / 1e12:.0f} TFLOP/s; FFN {flops_all / ((gu + dn) * 1e-3) / 1e12:.0f} TFLOP/s")
     return dict(ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), gate_up_ms=gu, down_ms=dn,
-                flops_gate_up=flops_gu, flops_ffn=flops_all)
+                flops_gate_up=flops_gu, flops_ffn=flops_all,
+                ffn_ms_p10_p50_p90=[float(v) for v in np.percentile(ffn_ms, [10, 50, 90])])
 
 
 def pinned_h2d_bandwidth(expert_bytes, n=32, n_streams=1):
@@ -642,6 +682,8 @@ def main():
                     help="time only the main batch (profiling runs: one kernel shape per kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak probes (device copy, bf16 GEMM); implied by --only-main-batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -687,6 +729,7 @@ def main():
         p = run_prefill(args, cfg, T, mode=1 if native else 0)
         ach = p["flops_gate_up"] / (p["gate_up_ms"] * 1e-3) / 1e12
         peak = FP8_PEAK_TFLOPS if native else BF16_PEAK_TFLOPS
+        peaks = None if args.no_peaks else achievable_peaks()
         out = {
             "metric": METRIC, "value": p["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": p["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -695,12 +738,17 @@ def main():
             "roofline": {"bound": "mfma",
                          "kernel": "ffn_mx_gemm_kernel<gate_up>" if native else f"ffn_gemm_kernel<{cfg.wdtype}, gate_up>",
                          "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
-                         "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"]},
+                         "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"],
+                         "frac_of_achievable_bf16_gemm": (ach / peaks["bf16_gemm_TFLOPs"]
+                                                          if peaks and not native else None)},
             "ffn_TFLOPs": p["flops_ffn"] / ((p["gate_up_ms"] + p["down_ms"]) * 1e-3) / 1e12,
+            "ffn_ms_p10_p50_p90": p["ffn_ms_p10_p50_p90"],
+            "achievable": peaks,
         }
         print(json.dumps(out), flush=True)
         return
     res = run_decode(args, cfg, batches, main_T)
+    peaks = None if (args.no_peaks or args.only_main_batch) else achievable_peaks()
     m = res[main_T]
     ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
     kname = "ffn_persist_kernel<bf16, gate_up>" if cfg.wdtype == "bf16" else \
@@ -725,11 +773,15 @@ def main():
                    "distinct_experts_per_step": m["distinct_experts"]},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "avg_launch_us": m["gate_up_ms"] * 1e3,
-                     "algorithmic_bytes_per_launch": m["gate_up_bytes"]},
+                     "algorithmic_bytes_per_launch": m["gate_up_bytes"],
+                     "frac_of_achievable_copy": ach / peaks["copy_GBps"] if peaks else None},
+        "achievable": peaks,
+        "step_ms_p10_p50_p90": m["step_ms_p10_p50_p90"],
         "layer_weight_GBps": m["layer_weight_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9,
         "graph_ms_per_step": m["graph_ms_per_step"],
         "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                              "graph_ms_per_step": r["graph_ms_per_step"],
+                             "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
                              "gate_up_GBps": r["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9,
                              "layer_weight_GBps": r["layer_weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9}
                     for T, r in sorted(res.items())},
