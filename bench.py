@@ -408,30 +408,55 @@ def run_cache_trace(args, cfg):
 
     n_threads = min(16, len(os.sched_getaffinity(0)))
 
-    def run(steps, cache, hybrid=False):
+    slot_hits = torch.empty(E, dtype=torch.int32, device="cuda")
+
+    def run(steps, cache, hybrid=False, hits_first=False):
+        """hits_first: the hits' FFN (and the shared expert's) is enqueued before the step's fills
+        land, the filled misses' FFN after them; otherwise one FFN waits for every fill."""
         for st in range(steps):
             for l in range(Lyr):
                 i = st * Lyr + l
                 layer.route_permute(1, logits=logits[i:i + 1])
-                cache.step(l, layer.ids, 1, cfg.k, slot_of)
+                if hits_first:
+                    n_fill = cache.step_split(l, layer.ids, 1, cfg.k, slot_hits, slot_of)
+                else:
+                    cache.step(l, layer.ids, 1, cfg.k, slot_of)
                 if hybrid:
                     layer.stage_cpu_misses(cache, 1, xs[i])
-                layer.ffn(1, xs[i], pool, slot_of_expert=slot_of, shared_blob=shared[l])
+                if hits_first:
+                    layer.ffn(1, xs[i], pool, slot_of_expert=slot_hits, shared_blob=shared[l])
+                    cache.wait_fills()
+                    if n_fill or (hybrid and cache.cpu_misses()):
+                        layer.ffn(1, xs[i], pool, slot_of_expert=slot_of)
+                else:
+                    layer.ffn(1, xs[i], pool, slot_of_expert=slot_of, shared_blob=shared[l])
                 if hybrid:
                     layer.run_cpu_misses(cache, n_threads=n_threads)
                 layer.combine(1)
 
     warm = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
-    run(min(args.warmup, S), warm)
+    run(min(args.warmup, S), warm, hits_first=True)
     torch.cuda.synchronize()
     warm.destroy()
     cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)  # cold start
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    run(S, cache)
+    run(S, cache, hits_first=True)  # the pages' decode order: a hit runs at once, a miss after its fill
     torch.cuda.synchronize()
     dt = time.perf_counter() - t1
     st = cache.stats()
+    cache.destroy()
+    # the same cold-start trace with one FFN that waits for every fill of its layer-step
+    cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
+    torch.cuda.synchronize()
+    t5 = time.perf_counter()
+    run(S, cache)
+    torch.cuda.synchronize()
+    dt_ser = time.perf_counter() - t5
+    st_ser = cache.stats()
+    assert (st_ser["hits"], st_ser["misses"]) == (st["hits"], st["misses"])  # the same LRU decisions
+    log(f"hits-first step {S / dt:.1f} tok/s vs {S / dt_ser:.1f} tok/s with the FFN waiting for every fill "
+        f"({dt_ser / dt:.2f}x)")
     # elastic resize at a safe point: halve the slots in place (the most recent
     # entries stay), run the first 64 steps again, grow back in the same pool
     t2 = time.perf_counter()
@@ -460,7 +485,7 @@ def run_cache_trace(args, cfg):
     b_h = n_h * eb / (time.perf_counter() - th) / 1e9
     cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
     cache.set_split(b_p, b_h)
-    run(min(args.warmup, S), cache, hybrid=True)  # warm the host path
+    run(min(args.warmup, S), cache, hybrid=True, hits_first=True)  # warm the host path
     torch.cuda.synchronize()
     cache.destroy()
     def hybrid_run(bh):
@@ -468,7 +493,7 @@ def run_cache_trace(args, cfg):
         cache.set_split(b_p, bh)
         torch.cuda.synchronize()
         t4 = time.perf_counter()
-        run(S, cache, hybrid=True)
+        run(S, cache, hybrid=True, hits_first=True)
         torch.cuda.synchronize()
         dth = time.perf_counter() - t4
         sth = cache.stats()
@@ -497,6 +522,8 @@ def run_cache_trace(args, cfg):
     res = dict(tokens_per_s=S / dt, ms_per_step=dt / S * 1e3, hit_rate=hit, misses_per_step=st["misses"] / S,
                bytes_h2d=st["bytes_h2d"], h2d_GBps=st["bytes_h2d"] / dt / 1e9, b_p_GBps=b_p,
                bound_ms_per_step=bound * 1e3, frac_of_bound=bound / (dt / S), stats=st, b_p_torch_copy_GBps=b_p1,
+               serialised_step={"tokens_per_s": S / dt_ser, "ms_per_step": dt_ser / S * 1e3,
+                                "hits_first_speedup": dt_ser / dt},
                hybrid=hybrid, resize={"shrink_ms": shrink_ms, "grow_ms": grow_ms, "from_slots": C, "to_slots": C // 2,
                        "hit_rate_64_steps_at_half": half_hit})
     log(f"cache trace: {S} steps x {Lyr} layers in {dt:.2f}s = {S / dt:.1f} tok/s, hit rate {hit:.4f}, "

@@ -15,6 +15,7 @@ FT_F32, FT_BF16, FT_MXFP4, FT_NVFP4 = 0, 1, 2, 3
 FT_SOFTMAX, FT_SIGMOID = 0, 1
 FT_WS_PERMUTE, FT_WS_FFN, FT_WS_ROUTE_PERMUTE = 1, 2, 3
 FT_FFN_EXACT, FT_FFN_NATIVE_MX = 0, 1
+FT_SLOT_SKIP = -2
 FT_CPU_ISA_QUERY, FT_CPU_ISA_BEST, FT_CPU_AVX2, FT_CPU_AVX512_BF16 = -1, 0, 1, 2
 FT_FFN_GATE_UP_ONLY, FT_FFN_DOWN_ONLY = 0x100, 0x200
 
@@ -25,7 +26,8 @@ EXPORTS = [
     "ft_expert_cache_destroy", "ft_workspace_bytes", "ft_mxfp8_quantize", "ft_moe_route_permute",
     "ft_expert_cache_resize", "ft_expert_cache_prefetch_layer", "ft_expert_cache_set_split",
     "ft_expert_cache_cpu_misses", "ft_cpu_expert_ffn", "ft_cpu_miss_rows", "ft_cpu_isa",
-    "ft_expert_cache_stage_cpu_misses", "ft_expert_cache_run_cpu_misses",
+    "ft_expert_cache_stage_cpu_misses", "ft_expert_cache_run_cpu_misses", "ft_expert_cache_step_split",
+    "ft_expert_cache_wait_fills",
 ]
 
 
@@ -84,6 +86,10 @@ def lib() -> C.CDLL:
     L.ft_cpu_isa.restype = i32
     L.ft_expert_cache_stage_cpu_misses.restype = i32
     L.ft_expert_cache_stage_cpu_misses.argtypes = [p, p, i32, i32, i32, p, p, p]
+    L.ft_expert_cache_step_split.restype = i32
+    L.ft_expert_cache_step_split.argtypes = [p, i32, p, i32, i32, p, p, C.POINTER(C.c_int32), p]
+    L.ft_expert_cache_wait_fills.restype = i32
+    L.ft_expert_cache_wait_fills.argtypes = [p, p]
     L.ft_expert_cache_run_cpu_misses.restype = i32
     L.ft_expert_cache_run_cpu_misses.argtypes = [p, p, p, i32]
     L.ft_cpu_isa.argtypes = [i32, p]

@@ -75,8 +75,9 @@ __device__ inline int miss_split(int m, double b_pcie, double b_host) {
 __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int layer, const int32_t *__restrict__ ids,
                                                               int R, int E, int C, double b_pcie, double b_host,
                                                               int32_t *__restrict__ slot_of_expert,
+                                                              int32_t *__restrict__ slot_hits,
                                                               LruResult *__restrict__ res) {
-  __shared__ int s_need[kLruMaxE];     // flag, then position in the needed list
+  __shared__ int s_need[kLruMaxE];     // needed flag, then its class: 1 hit, 2 filled, 3 left to the CPU
   __shared__ int s_list[kLruMaxE];     // needed experts, ascending
   __shared__ int s_slot[kLruMaxE];     // slot of needed expert i (hit) or victim (miss)
   __shared__ int s_evk[kLruMaxE];      // evicted key of needed expert i, or -1
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
       res->ev[i][2] = s;
       res->ev[i][3] = s_evk[i];
       if (cpu) ++n_cpu;
+      s_need[e] = hit ? 1 : (cpu ? 3 : 2);
       if (!hit && !cpu) {
         st.stamp[s] = clk + uint64_t(h + j) + 1;
         ++j;
@@ -242,7 +244,15 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
     res->n_cpu = n_cpu;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kLruThreads) slot_of_expert[e] = s_out[e];
+  if (slot_hits == nullptr) {
+    for (int e = tid; e < E; e += kLruThreads) slot_of_expert[e] = s_out[e];
+  } else {  // split tables: hits now, filled misses after the fills (the other needed experts skipped)
+    for (int e = tid; e < E; e += kLruThreads) {
+      const int cls = s_need[e];
+      slot_hits[e] = cls == 1 ? s_out[e] : (cls ? FT_SLOT_SKIP : -1);
+      slot_of_expert[e] = cls == 2 ? s_out[e] : (cls == 1 ? FT_SLOT_SKIP : -1);
+    }
+  }
   if (tid == 0) {
     __threadfence_system();
     res->status = LRU_OK;
@@ -315,6 +325,8 @@ struct ft_expert_cache {
   hipStream_t fill[kFillStreams];   // fill[0] = copy_stream; the others are the cache's own
   hipEvent_t ev_fill[kFillStreams];
   bool pending[kFillStreams];       // a layer prefetch's fills on this queue not yet waited for
+  bool unwaited[kFillStreams] = {}; // a split step's fills on this queue (ft_expert_cache_wait_fills)
+  int32_t last_filled = 0;          // misses the last step filled
   int32_t *iota;                    // device [E]: 0..E-1 (the needed set of a layer prefetch)
   double b_pcie = 0.0, b_host = 0.0;  // hybrid split (b_host <= 0: every miss is filled)
   std::vector<int32_t> cpu_list;      // the last step's misses left to the CPU
@@ -430,10 +442,17 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
 // One LRU update (a step, or a layer prefetch with every expert of the layer
 // needed) and its fills.
 static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *ids, int R, int32_t *slot_of_expert,
-                             hipStream_t compute_stream, bool prefetch, const char *who) {
+                             int32_t *slot_hits, hipStream_t compute_stream, bool prefetch, const char *who) {
+  // fills of a split step that the caller did not wait for: order this call's work after them
+  for (int q = 0; q < kFillStreams; ++q)
+    if (c->unwaited[q]) {
+      FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
+      c->unwaited[q] = false;
+    }
   c->res_host->status = -1;
   hipLaunchKernelGGL(lru_step_kernel, dim3(1), dim3(kLruThreads), 0, compute_stream, c->st, layer, ids, R, c->E,
-                     c->C, prefetch ? 0.0 : c->b_pcie, prefetch ? 0.0 : c->b_host, slot_of_expert, c->res_dev);
+                     c->C, prefetch ? 0.0 : c->b_pcie, prefetch ? 0.0 : c->b_host, slot_of_expert, slot_hits,
+                     c->res_dev);
   FT_LAUNCHED("lru_step_kernel");
   FT_HIP(hipEventRecord(c->ev_lru, compute_stream));
   FT_HIP(hipEventSynchronize(c->ev_lru));
@@ -497,10 +516,15 @@ static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *i
     c->stats.prefetch_fills += uint64_t(fills);
   } else {
     for (int q = 0; q < kFillStreams; ++q) c->pending[q] = false;  // waited for above
+    c->last_filled = fills;
     for (int q = 0; q < kFillStreams; ++q) {
+      c->unwaited[q] = false;
       if (!used[q]) continue;
       FT_HIP(hipEventRecord(c->ev_fill[q], c->fill[q]));
-      FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
+      if (slot_hits == nullptr)
+        FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
+      else
+        c->unwaited[q] = true;  // ft_expert_cache_wait_fills
     }
     c->stats.accesses += uint64_t(r.n_needed);
     c->stats.hits += uint64_t(r.n_hits);
@@ -523,13 +547,42 @@ extern "C" ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, con
   FT_REQUIRE(slot_of_expert != nullptr, "ft_expert_cache_step: slot_of_expert is NULL");
   const int R = T * k;
   FT_REQUIRE(R == 0 || topk_ids != nullptr, "ft_expert_cache_step: topk_ids is NULL");
-  return cache_serve(c, layer, topk_ids, R, slot_of_expert, compute_stream, false, "ft_expert_cache_step");
+  return cache_serve(c, layer, topk_ids, R, slot_of_expert, nullptr, compute_stream, false, "ft_expert_cache_step");
+}
+
+extern "C" ft_status ft_expert_cache_step_split(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids, int32_t T,
+                                                int32_t k, int32_t *slot_hits, int32_t *slot_misses,
+                                                int32_t *n_filled, hipStream_t compute_stream) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_step_split: cache is NULL");
+  FT_REQUIRE(layer >= 0 && layer < c->n_layers, "ft_expert_cache_step_split: layer out of range");
+  FT_REQUIRE(T >= 0 && k >= 1, "ft_expert_cache_step_split: need T >= 0, k >= 1");
+  FT_REQUIRE(int64_t(T) * k < (int64_t(1) << 31), "ft_expert_cache_step_split: T*k too large");
+  FT_REQUIRE(slot_hits != nullptr && slot_misses != nullptr && slot_hits != slot_misses,
+             "ft_expert_cache_step_split: slot_hits and slot_misses must be two tables");
+  const int R = T * k;
+  FT_REQUIRE(R == 0 || topk_ids != nullptr, "ft_expert_cache_step_split: topk_ids is NULL");
+  const ft_status st =
+      cache_serve(c, layer, topk_ids, R, slot_misses, slot_hits, compute_stream, false, "ft_expert_cache_step_split");
+  if (st == FT_OK && n_filled != nullptr) *n_filled = c->last_filled;
+  return st;
+}
+
+extern "C" ft_status ft_expert_cache_wait_fills(ft_expert_cache *c, hipStream_t compute_stream) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_wait_fills: cache is NULL");
+  for (int q = 0; q < kFillStreams; ++q)
+    if (c->unwaited[q]) {
+      FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
+      c->unwaited[q] = false;
+    }
+  clear_error();
+  return FT_OK;
 }
 
 extern "C" ft_status ft_expert_cache_prefetch_layer(ft_expert_cache *c, int32_t layer, hipStream_t compute_stream) {
   FT_REQUIRE(c != nullptr, "ft_expert_cache_prefetch_layer: cache is NULL");
   FT_REQUIRE(layer >= 0 && layer < c->n_layers, "ft_expert_cache_prefetch_layer: layer out of range");
-  return cache_serve(c, layer, c->iota, c->E, c->pf_slots, compute_stream, true, "ft_expert_cache_prefetch_layer");
+  return cache_serve(c, layer, c->iota, c->E, c->pf_slots, nullptr, compute_stream, true,
+                     "ft_expert_cache_prefetch_layer");
 }
 
 extern "C" ft_status ft_expert_cache_set_split(ft_expert_cache *c, double b_pcie, double b_host) {
@@ -660,7 +713,7 @@ extern "C" ft_status ft_expert_cache_resize(ft_expert_cache *c, int32_t new_capa
   FT_REQUIRE(pa.type == hipMemoryTypeDevice, "ft_expert_cache_resize: new_slot_pool is not device memory");
   for (int q = 0; q < kFillStreams; ++q) FT_HIP(hipStreamSynchronize(c->fill[q]));
   FT_HIP(hipStreamSynchronize(stream));
-  for (int q = 0; q < kFillStreams; ++q) c->pending[q] = false;  // every fill has landed
+  for (int q = 0; q < kFillStreams; ++q) c->pending[q] = c->unwaited[q] = false;  // every fill has landed
   const int C = c->C, C2 = new_capacity;
   const size_t keys = size_t(c->n_layers) * c->E;
   std::vector<uint64_t> stamp(C);

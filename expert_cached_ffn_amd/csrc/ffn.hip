@@ -129,6 +129,7 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
     const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
     pos0 = a.offsets[e];
     m = a.offsets[e + 1] - pos0;
+    if (slot == FT_SLOT_SKIP) return;  // another call computes these rows
     if (slot < 0) {
       // Caller error: the expert is not resident.  Mark its rows NaN.
       const int row0 = tile * 16;
@@ -415,9 +416,11 @@ __device__ __forceinline__ int expert_of_row(const int32_t *off, int E, int p) {
   return lo;
 }
 
-__device__ __forceinline__ const float *f32_blob(const FfnF32Args &a, int p, int *tok, bool *ok) {
+// The blob of permuted row p; *ok false: not resident (NaN rows); *skip: FT_SLOT_SKIP (row left untouched).
+__device__ __forceinline__ const float *f32_blob(const FfnF32Args &a, int p, int *tok, bool *ok, bool *skip) {
   const int routed = a.T * a.k;
   *ok = true;
+  *skip = false;
   if (p >= routed) {
     *tok = p - routed;
     return reinterpret_cast<const float *>(a.shared_blob);
@@ -427,6 +430,7 @@ __device__ __forceinline__ const float *f32_blob(const FfnF32Args &a, int p, int
   const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
   if (slot < 0) {
     *ok = false;
+    *skip = slot == FT_SLOT_SKIP;
     return nullptr;
   }
   return reinterpret_cast<const float *>(a.pool + uint64_t(slot) * a.expert_bytes);
@@ -437,10 +441,10 @@ __global__ __launch_bounds__(256) void ffn_f32_stage1(FfnF32Args a) {
   if (idx >= int64_t(a.rows) * a.I) return;
   const int p = int(idx / a.I), i = int(idx % a.I);
   int tok;
-  bool ok;
-  const float *b = f32_blob(a, p, &tok, &ok);
+  bool ok, skip;
+  const float *b = f32_blob(a, p, &tok, &ok, &skip);
   if (!ok) {
-    a.h[idx] = __builtin_nanf("");
+    if (!skip) a.h[idx] = __builtin_nanf("");
     return;
   }
   const float *wg = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(b) + a.off_gate) + int64_t(i) * a.H;
@@ -459,12 +463,12 @@ __global__ __launch_bounds__(256) void ffn_f32_stage2(FfnF32Args a) {
   if (idx >= int64_t(a.rows) * a.H) return;
   const int p = int(idx / a.H), n = int(idx % a.H);
   int tok;
-  bool ok;
-  const float *b = f32_blob(a, p, &tok, &ok);
+  bool ok, skip;
+  const float *b = f32_blob(a, p, &tok, &ok, &skip);
   const int routed = a.T * a.k;
   float *dst = p >= routed ? (a.y_shared + int64_t(tok) * a.H + n) : (a.y_rows + int64_t(p) * a.H + n);
   if (!ok) {
-    *dst = __builtin_nanf("");
+    if (!skip) *dst = __builtin_nanf("");
     return;
   }
   const float *wd = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(b) + a.off_down) + int64_t(n) * a.I;

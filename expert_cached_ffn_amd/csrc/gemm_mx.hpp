@@ -73,6 +73,7 @@ __device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, LdsRing<kMxSt
     blob = a.shared_blob;
   } else {
     const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    if (slot == FT_SLOT_SKIP) return;  // another call computes these rows
     if (slot < 0) {
       const int cols = GLU ? kGemmBN / 2 : kGemmBN;
       const int c0 = nt_idx * cols;

@@ -181,6 +181,7 @@ __device__ __forceinline__ bool gemm_setup(const GemmArgs &a, int &nt_idx, int &
     blob = a.shared_blob;
   } else {
     const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    if (slot == FT_SLOT_SKIP) return false;  // another call computes these rows
     if (slot < 0) {
       // not resident: mark this tile's outputs NaN
       const int cols = GLU ? kGemmBN / 2 : kGemmBN;

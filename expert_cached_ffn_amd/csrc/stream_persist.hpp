@@ -77,6 +77,7 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
     if (e < a.E) {
       lo = a.offsets[e];
       cnt = a.offsets[e + 1] - lo;
+      if (cnt > 0 && a.slot_of_expert != nullptr && a.slot_of_expert[e] == FT_SLOT_SKIP) cnt = 0;  // another call's
     }
     const bool f = cnt > 0;
     const uint64_t mask = __ballot(f);
@@ -328,6 +329,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     if (e < a.E) {
       lo = a.offsets[e];
       cnt = a.offsets[e + 1] - lo;
+      if (cnt > 0 && a.slot_of_expert != nullptr && a.slot_of_expert[e] == FT_SLOT_SKIP) cnt = 0;  // another call's
     }
     const bool f = cnt > 0;
     const uint64_t mask = __ballot(f);

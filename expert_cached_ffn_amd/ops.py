@@ -137,6 +137,21 @@ class ExpertCache:
 
     step = ft_expert_cache_step
 
+    def ft_expert_cache_step_split(self, layer: int, topk_ids, T: int, k: int, slot_hits, slot_misses,
+                                   stream=None) -> int:
+        """Hits-first step: returns the number of fills (wait for them with wait_fills)."""
+        n = C.c_int32()
+        _check(_lib.lib().ft_expert_cache_step_split(self._h, layer, _ptr(topk_ids), T, k, _ptr(slot_hits),
+                                                     _ptr(slot_misses), C.byref(n), _stream(stream)))
+        return n.value
+
+    step_split = ft_expert_cache_step_split
+
+    def ft_expert_cache_wait_fills(self, stream=None) -> None:
+        _check(_lib.lib().ft_expert_cache_wait_fills(self._h, _stream(stream)))
+
+    wait_fills = ft_expert_cache_wait_fills
+
     def ft_expert_cache_set_split(self, b_pcie: float, b_host: float) -> None:
         _check(_lib.lib().ft_expert_cache_set_split(self._h, float(b_pcie), float(b_host)))
 

@@ -66,6 +66,11 @@ const char *ft_version(void);
 typedef enum { FT_F32 = 0, FT_BF16 = 1, FT_MXFP4 = 2, FT_NVFP4 = 3 } ft_dtype;
 typedef enum { FT_SOFTMAX = 0, FT_SIGMOID = 1 } ft_gating;
 
+/* slot_of_expert value for an expert whose rows a grouped-FFN call must leave
+ * untouched (another call computes them; see ft_expert_cache_step_split).
+ * Any other negative slot means "not resident": its rows are written as NaN. */
+#define FT_SLOT_SKIP (-2)
+
 /* ------------------------------------------------------------------------ */
 /* Expert blob layout                                                        */
 /* ------------------------------------------------------------------------ */
@@ -175,8 +180,10 @@ ft_status ft_moe_route_permute(const void *x, int32_t x_dtype, const void *w_rou
  * Segment e = rows expert_offsets[e] .. expert_offsets[e+1]-1 of the permuted
  * order; its row i is token sorted_rows[i] / k.  Expert e's blob starts at
  *   slot_pool + slot_of_expert[e] * L->expert_bytes
- * (slot_of_expert == NULL means slot e).  A non-empty segment whose slot is
- * negative is a caller error; its y rows are written as NaN.
+ * (slot_of_expert == NULL means slot e).  A segment whose slot is
+ * FT_SLOT_SKIP is left untouched (its hidden and y rows are not written); a
+ * non-empty segment with another negative slot is a caller error, its y rows
+ * are written as NaN.
  * x [T, H] of x_dtype (FT_F32 with FT_F32 weights, FT_BF16 with FT_BF16 or
  *   FT_MXFP4 weights).
  * y_rows [T*k, H] fp32, permuted order (row i belongs to sorted_rows[i]).
@@ -388,6 +395,32 @@ ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n_layers, in
 ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids,
                                int32_t T, int32_t k, int32_t *slot_of_expert,
                                hipStream_t compute_stream);
+
+/*
+ * ft_expert_cache_step_split -- the same LRU update and fills, but hits run
+ * before the fills land (FreeToken 290b model page, "Cómo gestiona FreeToken
+ * el prellenado y la decodificación": a hit runs on the GPU at once, a miss
+ * is filled first).  Two slot tables (DEVICE, [E] each) replace
+ * slot_of_expert: slot_hits gives the slot of every hit and FT_SLOT_SKIP for
+ * the step's other needed experts; slot_misses gives the slot of every filled
+ * miss, FT_SLOT_SKIP for the hits and -1 for misses left to the CPU; experts
+ * not needed are -1 in both.  *n_filled (host, may be NULL) receives the
+ * number of fills.  compute_stream is NOT made to wait for the fills:
+ *
+ *   step_split -> ft_moe_grouped_ffn(slot_hits, shared expert) ->
+ *   ft_expert_cache_wait_fills -> ft_moe_grouped_ffn(slot_misses, no shared
+ *   expert; only if *n_filled > 0) -> [CPU misses] -> ft_moe_combine
+ *
+ * The next step, resize or destroy still orders itself after the fills.
+ * Errors as ft_expert_cache_step; slot_hits == slot_misses -> FT_EINVAL.
+ */
+ft_status ft_expert_cache_step_split(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids, int32_t T, int32_t k,
+                                     int32_t *slot_hits, int32_t *slot_misses, int32_t *n_filled,
+                                     hipStream_t compute_stream);
+
+/* Makes compute_stream wait for the fills of the last ft_expert_cache_step_split
+ * (a no-op when it had none or they were already waited for). */
+ft_status ft_expert_cache_wait_fills(ft_expert_cache *c, hipStream_t compute_stream);
 
 /* Totals since create (host).  */
 ft_status ft_expert_cache_stats(const ft_expert_cache *c, ft_cache_stats *out);

@@ -375,10 +375,12 @@ def test_hybrid_split_against_the_simulator(env):
     rig.cache.destroy()
 
 
-@pytest.mark.parametrize("T,C", [(1, 10), (5, 30)])
-def test_hybrid_layer_outputs(env, T, C):
-    """Decode through the cache with the miss split on: the CPU misses' rows come from the host
-    kernel, the rest from the slots; every layer output matches the oracle."""
+@pytest.mark.parametrize("T,C,hybrid,hits_first", [(1, 10, True, False), (5, 30, True, False),
+                                                   (1, 10, False, True), (5, 30, True, True)])
+def test_hybrid_layer_outputs(env, T, C, hybrid, hits_first):
+    """Decode through the cache, with the CPU miss split (hybrid) and/or the hits-first step (the
+    hits' FFN before the fills land, the filled misses' FFN after): every layer output matches the
+    oracle."""
     ops, Lm = env
     cfg = synth.shrink(synth.CONFIGS[5], H=512, I=512, E=32, n_layers=2, capacity=C, steps=12)
     shape = Lm.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize, True)
@@ -393,20 +395,32 @@ def test_hybrid_layer_outputs(env, T, C):
     shared = [Lm.as_device_u8([Lm.pack_expert(lay, ex[l].raw(cfg.E).arrays)])[0] for l in range(cfg.n_layers)]
     pool = torch.zeros((cfg.capacity, eb), dtype=torch.uint8, device="cuda")
     cache = ops.ExpertCache(lay, cfg.n_layers, cfg.E, cfg.capacity, pool, bank, torch.cuda.Stream())
-    cache.set_split(2.0, 1.0)  # a third of each step's misses on the CPU
+    if hybrid:
+        cache.set_split(2.0, 1.0)  # a third of each step's misses on the CPU
     slot_of = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
-    n_cpu = 0
+    slot_hits = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    n_cpu = n_two_pass = 0
     for s in range(cfg.steps):
         for l in range(cfg.n_layers):
             x = synth.tokens(cfg, T, layer=l, step=s)
             logits = synth.prefill_logits(cfg, T, case=s, layer=l)
             xd = Lm.to_device(x)
             layer.route_permute(T, logits=Lm.to_device(logits))
-            cache.step(l, layer.ids, T, cfg.k, slot_of)
+            if hits_first:
+                n_fill = cache.step_split(l, layer.ids, T, cfg.k, slot_hits, slot_of)
+            else:
+                cache.step(l, layer.ids, T, cfg.k, slot_of)
             cpu = cache.cpu_misses()
             n_cpu += len(cpu)
             layer.stage_cpu_misses(cache, T, xd)
-            layer.ffn(T, xd, pool, slot_of_expert=slot_of, shared_blob=shared[l])
+            if hits_first:
+                layer.ffn(T, xd, pool, slot_of_expert=slot_hits, shared_blob=shared[l])
+                cache.wait_fills()
+                if n_fill or cpu:  # the filled misses (and NaN rows for the CPU's, patched next)
+                    layer.ffn(T, xd, pool, slot_of_expert=slot_of)
+                    n_two_pass += 1
+            else:
+                layer.ffn(T, xd, pool, slot_of_expert=slot_of, shared_blob=shared[l])
             layer.run_cpu_misses(cache, n_threads=4)
             layer.combine(T)
             torch.cuda.synchronize()
@@ -417,8 +431,9 @@ def test_hybrid_layer_outputs(env, T, C):
             ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex[l].f64, ex[l].f64(cfg.E)) for t in range(T)])
             check_close(got, ref, bf16_out=True, what=f"step {s} layer {l} cpu {cpu}")
     st = cache.stats()
-    assert n_cpu == st["cpu_misses"] > 0 and st["misses"] > st["cpu_misses"]
-    assert st["cpu_ns"] > 0
+    assert n_cpu == st["cpu_misses"] and st["misses"] > st["cpu_misses"]
+    assert (n_cpu > 0 and st["cpu_ns"] > 0) if hybrid else n_cpu == 0
+    assert n_two_pass > 0 or not hits_first
     cache.destroy()
 
 
@@ -444,4 +459,48 @@ def test_cpu_miss_calls_validate(env):
     assert e.value.status == -2
     torch.cuda.synchronize()
     assert (y == 0).all()
+    rig.cache.destroy()
+
+
+def test_split_step_tables_against_the_simulator(env):
+    """Hits-first steps (with and without the CPU split): slot_hits holds the hits' slots, slot_misses
+    the filled misses' slots, FT_SLOT_SKIP marks the other needed experts, -1 the rest; n_filled counts
+    the fills; events and totals follow the oracle."""
+    ops, _ = env
+    from expert_cached_ffn_amd import _lib
+    SKIP = _lib.FT_SLOT_SKIP
+    rng = np.random.default_rng(31)
+    L, E, C = 3, 24, 10
+    rig = Rig(ops, L, E, C)
+    sim = ExpertLRU(L, E, C)
+    hits_t = torch.empty(E, dtype=torch.int32, device="cuda")
+    for t in range(120):
+        layer = int(rng.integers(L))
+        ids = rng.choice(E, size=int(rng.integers(1, 7)), replace=False).astype(np.int32)
+        bp, bh = [(1.0, 0.0), (2.0, 1.0), (0.0, 1.0)][t % 3]
+        needed = sorted(set(ids.tolist()))
+        m = sum(sim.slot_of_expert(layer)[e] < 0 for e in needed)
+        q = m if bh == 0 else policy.miss_split(m, bp, bh)
+        evs = {ev.expert: ev for ev in sim.step(layer, ids, fill_limit=q)}
+        rig.cache.set_split(bp, bh)
+        d = torch.from_numpy(ids).cuda()
+        n_filled = rig.cache.step_split(layer, d, ids.size, 1, hits_t, rig.slot_of)
+        rig.cache.wait_fills()
+        torch.cuda.synchronize()
+        hits, misses = hits_t.cpu().numpy(), rig.slot_of.cpu().numpy()
+        assert n_filled == sum(1 for ev in evs.values() if not ev.hit and ev.slot >= 0)
+        for e in range(E):
+            ev = evs.get(e)
+            if ev is None:
+                assert hits[e] == -1 and misses[e] == -1
+            elif ev.hit:
+                assert hits[e] == ev.slot and misses[e] == SKIP
+            elif ev.slot >= 0:
+                assert hits[e] == SKIP and misses[e] == ev.slot
+                assert torch.equal(rig.pool[ev.slot].cpu(), rig.bank[layer * E + e])
+            else:
+                assert hits[e] == SKIP and misses[e] == -1
+    st = rig.cache.stats()
+    assert (st["accesses"], st["hits"], st["misses"], st["evictions"], st["cpu_misses"]) == \
+        (sim.accesses, sim.hits, sim.misses, sim.evictions, sim.cpu_misses)
     rig.cache.destroy()

@@ -197,7 +197,7 @@ def test_permute_bit_exact(ops, T, k, E, kind):
 class _FfnRig:
     """Device inputs of one grouped-FFN case built from oracle permutation data."""
 
-    def __init__(self, ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None):
+    def __init__(self, ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None, skip=None):
         from expert_cached_ffn_amd.layer import DTYPES, pack_expert
         self.ops, self.cfg, self.T = ops, cfg, T
         self.with_shared = cfg.shared if with_shared is None else with_shared
@@ -215,6 +215,8 @@ class _FfnRig:
             pack_expert(lay, ex.raw(e).arrays, pool[s])
         if missing is not None:
             slot_of[missing] = -1
+        if skip is not None:
+            slot_of[skip] = -2  # FT_SLOT_SKIP
         self.x = synth.tokens(cfg, T)
         self.x64 = formats.activations_to_f64(cfg.xdtype, self.x)
         self.shared_blob = dev(pack_expert(lay, ex.raw(cfg.E).arrays)) if self.with_shared else None
@@ -292,6 +294,43 @@ def test_grouped_ffn_missing_slot_gives_nan(ops):
     assert np.all(np.isnan(y[a:b]))
     keep = np.r_[0:a, b:len(y)]
     check_close(y[keep], y_ref[keep], what="other experts")
+
+
+SKIP_CASES = [("bf16-decode", 2, dict(H=512, I=512, E=6, k=2), 9, 0),
+              ("bf16-stream", 2, dict(H=256, I=256, E=6, k=2), 9, 0),
+              ("fp4-decode-xs", 3, dict(H=512, I=512, E=6, k=2, shared=False), 9, 0),
+              ("nv4-decode-xs", 6, dict(H=512, I=512, E=6, k=2), 9, 0),
+              ("fp4-gemm", 3, dict(H=512, I=512, E=6, k=2, shared=False), 150, 0),
+              ("f32", 1, dict(E=6), 9, 0),
+              ("fp4-native", 3, dict(H=512, I=512, E=6, k=2, shared=False), 150, 1)]
+
+
+@pytest.mark.parametrize("name,cfg_id,over,T,mode", SKIP_CASES, ids=[c[0] for c in SKIP_CASES])
+def test_grouped_ffn_skip_slot_leaves_rows(ops, name, cfg_id, over, T, mode):
+    """FT_SLOT_SKIP experts: their y rows keep what was there (NaN sentinels here), the others are right."""
+    cfg = synth.shrink(synth.CONFIGS[cfg_id], **over)
+    ids = synth.routing_ids_uniform(cfg, T)
+    used = sorted(set(ids.ravel().tolist()))
+    skip = used[::2]
+    rig = _FfnRig(ops, cfg, T, ids, skip=skip)
+    rig.run(mode)
+    fn = moe.swiglu_expert_mx if mode == 1 else moe.swiglu_expert
+    y_ref = moe.grouped_ffn(rig.x64, cfg.k, rig.off, rig.rows, rig.ex.f64, fn)
+    y = rig.y.cpu().numpy()
+    skipped = np.zeros(len(y), bool)
+    for e in skip:
+        skipped[int(rig.off[e]):int(rig.off[e + 1])] = True
+    assert skipped.any() and (~skipped).any()
+    assert np.all(np.isnan(y[skipped]))
+    if mode == 1:
+        from tests.helpers import native_mx_expert
+        allow = np.zeros_like(y_ref)
+        for e in sorted(set(used) - set(skip)):
+            a, b = int(rig.off[e]), int(rig.off[e + 1])
+            _, allow[a:b] = native_mx_expert(rig.x64[rig.rows[a:b] // cfg.k], *rig.ex.f64(e))
+        check_close(y[~skipped], y_ref[~skipped], what=f"{name} computed experts", allow=allow[~skipped])
+    else:
+        check_close(y[~skipped], y_ref[~skipped], what=f"{name} computed experts")
 
 
 # ----------------------------------------------------------------------------- native MXFP4 mode
