@@ -489,3 +489,29 @@ def test_grouped_ffn_nvfp4_decode_shape_not_covered(ops):
     with pytest.raises(ops.FtError) as e:
         _ffn_case(ops, cfg, T, ids)
     assert e.value.status == -2
+
+
+EDGE_ROUTINGS = [
+    # name, cfg id, overrides, T, routing
+    ("one-expert-decode-fp4", 3, dict(H=512, I=512, E=8, k=1, shared=True), 64, "one"),
+    ("one-expert-decode-bf16", 2, dict(H=512, I=512, E=8, k=1), 64, "one"),
+    ("one-expert-prefill-fp4", 3, dict(H=512, I=512, E=8, k=1, shared=False), 1000, "one"),
+    ("k-equals-E-fp4", 3, dict(H=512, I=512, E=4, k=4, shared=True), 20, "all"),
+    ("k-equals-E-nv4-prefill", 6, dict(H=512, I=512, E=4, k=4), 90, "all"),
+    ("single-token-k1-nv4", 6, dict(H=512, I=512, E=8, k=1), 1, "one"),
+]
+
+
+@pytest.mark.parametrize("name,cfg_id,over,T,kind", EDGE_ROUTINGS, ids=[c[0] for c in EDGE_ROUTINGS])
+def test_grouped_ffn_edge_routings(ops, name, cfg_id, over, T, kind):
+    """Degenerate routings: every token on one expert (one long segment, the rest empty), and k = E
+    (every expert takes every token)."""
+    cfg = synth.shrink(synth.CONFIGS[cfg_id], **over)
+    if kind == "one":
+        ids = np.full((T, cfg.k), cfg.E - 1, np.int32)
+    else:
+        ids = np.tile(np.arange(cfg.E, dtype=np.int32)[::-1], (T, 1))
+    y, ys, y_ref, ys_ref, off = _ffn_case(ops, cfg, T, ids)
+    check_close(y, y_ref, what=f"{name} y_rows")
+    if ys_ref is not None:
+        check_close(ys, ys_ref, what=f"{name} y_shared")
