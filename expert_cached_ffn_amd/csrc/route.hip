@@ -76,6 +76,11 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The logit an order key was made from (-0.0 comes back as +0.0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // Top-k and gating of token t by one wave (all 64 lanes call it).  ids / w
 // receive the picks at [t * k + j]; ids_lds (nullable) gets the same ids.
 template <int VPL>
@@ -96,8 +101,12 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
   // k rounds of wave arg-max; pick j ends up in lane j % 64, slot j / 64
   constexpr int KS = kMaxK / 64;
   int pid[KS];
+  float pval[KS];  // the picks' logits, recovered from their keys (no second read of the logits)
 #pragma unroll
-  for (int s2 = 0; s2 < KS; ++s2) pid[s2] = -1;
+  for (int s2 = 0; s2 < KS; ++s2) {
+    pid[s2] = -1;
+    pval[s2] = 0.f;
+  }
   for (int j = 0; j < k; ++j) {
     uint64_t best = key[0];
 #pragma unroll
@@ -113,7 +122,10 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
       if (key[i] == best) key[i] = 0;  // the owner drops its pick
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
-      if ((j >> 6) == s2 && lane == (j & 63)) pid[s2] = e;
+      if ((j >> 6) == s2 && lane == (j & 63)) {
+        pid[s2] = e;
+        pval[s2] = key_value(uint32_t(best >> 32));
+      }
   }
   // Gating.  softmax: p_e = exp(l_e - max) / sum_E exp(l - max); sigmoid: 1/(1+exp(-l)).
   float mx = v[0];
@@ -135,8 +147,7 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
   for (int s2 = 0; s2 < KS; ++s2) {
     p[s2] = 0.f;
     if (pid[s2] >= 0) {
-      float x = lr[pid[s2]];
-      if (x == 0.0f) x = 0.0f;
+      const float x = pval[s2];
       p[s2] = gating == FT_SOFTMAX ? expf(x - mx) / denom : 1.0f / (1.0f + expf(-x));
       local += p[s2];
     }
