@@ -368,16 +368,15 @@ static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
 
 // ------------------------------------------------------------------ native MXFP4 mode GEMM
 
-// Four pipeline stages at one workgroup per CU (68 KiB of LDS; three stages at
-// two workgroups per CU would spill).
+// Three pipeline stages of 256-element chunks at one workgroup per CU (99 KiB
+// of LDS; a fourth weight register set would spill).
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mx_gemm_kernel(MxGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kMxBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds2[kMxBufBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[kMxBufBytes];
-  static_assert(kMxStages == 4, "one array per stage");
-  gemm_mx_tile<GLU>(a, LdsRing<kMxStages>{{lds0, lds1, lds2, lds3}});
+  static_assert(kMxStages == 3, "one array per stage");
+  gemm_mx_tile<GLU>(a, LdsRing<kMxStages>{{lds0, lds1, lds2}});
 }
 
 template <bool GLU>
