@@ -235,8 +235,8 @@ def copy_calibration(nbytes=1 << 30, reps=3):
 
 
 def achievable_peaks():
-    """What this machine reaches outside the library: a 1 GiB device copy (read + write bytes / time) and an
-    8192^3 bf16 GEMM through torch's BLAS (hipBLASLt); best of a few runs."""
+    """What this machine reaches outside the library: a 1 GiB device copy (read + write bytes / time), an
+    8192^3 bf16 GEMM through torch's BLAS (hipBLASLt) and the same GEMM in FP8; best of a few runs."""
     import torch
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -262,9 +262,29 @@ def achievable_peaks():
         e.record()
         torch.cuda.synchronize()
         tf = max(tf, 2 * m ** 3 / (s.elapsed_time(e) * 1e-3) / 1e12)
+    # the same GEMM in OCP FP8 E4M3 with per-tensor scales (torch._scaled_mm): the library's context for
+    # the scaled FP8 x FP4 MFMA mode; None where this torch build has no FP8 GEMM for the device
+    tf8 = None
+    try:
+        x8 = x.to(torch.float8_e4m3fn)
+        y8 = y.t().contiguous().to(torch.float8_e4m3fn).t()      # column-major right operand
+        one = torch.ones((), dtype=torch.float32, device="cuda")
+        torch._scaled_mm(x8, y8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        tf8 = 0.0
+        for _ in range(5):
+            s.record()
+            torch._scaled_mm(x8, y8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            e.record()
+            torch.cuda.synchronize()
+            tf8 = max(tf8, 2 * m ** 3 / (s.elapsed_time(e) * 1e-3) / 1e12)
+        del x8, y8
+    except (RuntimeError, AttributeError, TypeError) as err:
+        log(f"fp8 GEMM through torch unavailable: {err}")
     del x, y
-    log(f"achievable on this box: device copy {best:,.0f} GB/s (read + write), bf16 GEMM {tf:,.0f} TFLOP/s")
-    return {"copy_GBps": best, "bf16_gemm_TFLOPs": tf}
+    fp8_txt = f", fp8 GEMM {tf8:,.0f} TFLOP/s" if tf8 else ""
+    log(f"achievable on this box: device copy {best:,.0f} GB/s (read + write), bf16 GEMM {tf:,.0f} TFLOP/s{fp8_txt}")
+    return {"copy_GBps": best, "bf16_gemm_TFLOPs": tf, "fp8_gemm_TFLOPs": tf8}
 
 
 def run_prefill(args, cfg, T, mode=0):
@@ -767,7 +787,9 @@ def main():
                          "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
                          "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"],
                          "frac_of_achievable_bf16_gemm": (ach / peaks["bf16_gemm_TFLOPs"]
-                                                          if peaks and not native else None)},
+                                                          if peaks and not native else None),
+                         "frac_of_achievable_fp8_gemm": (ach / peaks["fp8_gemm_TFLOPs"]
+                                                         if peaks and native and peaks["fp8_gemm_TFLOPs"] else None)},
             "ffn_TFLOPs": p["flops_ffn"] / ((p["gate_up_ms"] + p["down_ms"]) * 1e-3) / 1e12,
             "ffn_ms_p10_p50_p90": p["ffn_ms_p10_p50_p90"],
             "achievable": peaks,

@@ -27,9 +27,9 @@
 //
 // Work items: (weight tile, token tile) pairs, token tiles counted per expert
 // segment (ragged: the last tile of a segment is partial, rows past it load
-// zeros and are not written).  Block ids are remapped so that consecutive
-// items -- the token tiles of one weight tile -- run on the same XCD and share
-// its L2.
+// zeros and are not written).  Items are ordered expert by expert and block
+// ids are remapped so that consecutive items run on the same XCD and share its
+// L2 (the order is described at gemm_find_item).
 #pragma once
 
 #include <type_traits>
@@ -67,38 +67,77 @@ struct GemmArgs {
   int n_items;                    // work items
 };
 
-// Work items are weight-tile major: consecutive items are the token tiles of
-// one weight tile, so the workgroups an XCD runs at once share that weight
-// tile through its L2 and the weights stream from HBM about once.  (Blocks of
-// 8 token x 4 weight tiles were measured slower: the weights of the large
-// experts are then re-read, and the tokens come from the MALL anyway.)
+// Work items are expert-major: the items of expert e (its token tiles x the
+// weight tiles) are consecutive, ascending expert, the shared expert last;
+// within an expert they are weight-tile major (the token tiles of one weight
+// tile are consecutive).  Each XCD takes a contiguous range of the items
+// actually present, so a small expert -- a few token tiles -- runs whole on
+// one XCD: its token rows are fetched into that XCD's L2 once and shared by
+// all its weight tiles, and each weight tile is shared by the expert's token
+// tiles.  (Weight-tile major over all experts fetched every token row once per
+// weight tile: about 2.5x the bytes past L2 at the 8192-token prefill.)
 __host__ __device__ inline int gemm_item_count(int n_mtiles, int n_ntiles) { return n_mtiles * n_ntiles; }
-__device__ inline bool gemm_item(const GemmArgs &a, int logical, int *nt, int *mi) {
-  *nt = logical / a.n_mtiles;
-  *mi = logical % a.n_mtiles;
-  return *nt < a.n_ntiles;
-}
 
-// Block-wide: map token-tile index mi (counted over the experts' segments in
-// ascending expert order, then the shared expert) to its expert and first row.
+// Block-wide: this block's work item -- weight tile, expert, first row of the
+// token tile and its row count.  False if the block has none.
 template <int THREADS>
-__device__ bool gemm_find_mtile(const GemmArgs &a, int mi, int *e_out, int *row0_out, int *m_out) {
+__device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *row0_out, int *m_out) {
   constexpr int NW = THREADS / 64;
   __shared__ int s_cnt[NW];
-  __shared__ int s_e, s_r0, s_m;
+  __shared__ int s_e, s_first, s_lo, s_rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int NT = a.n_ntiles;
+  auto rows_of = [&](int e, int *lo) -> int {
+    if (e >= a.E) return 0;
+    *lo = a.offsets[e];
+    return a.offsets[e + 1] - *lo;
+  };
+  // pass 1: the number of items present (the first THREADS experts' rows are
+  // kept for pass 2)
+  int total = 0, lo_c0 = 0, rows_c0 = 0;
+  for (int c0 = 0; c0 < a.E; c0 += THREADS) {
+    int lo = 0;
+    const int rows = rows_of(c0 + tid, &lo);
+    if (c0 == 0) {
+      lo_c0 = lo;
+      rows_c0 = rows;
+    }
+    int v = (rows + kGemmBM - 1) / kGemmBM;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) s_cnt[wave] = v;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total += s_cnt[w];
+    __syncthreads();
+  }
+  const int routed_items = total * NT;
+  const int shared_tiles = a.shared_blob != nullptr ? (a.T + kGemmBM - 1) / kGemmBM : 0;
+  const int n_items = routed_items + shared_tiles * NT;
+  // this block's item: block ids go round-robin over the 8 XCDs; XCD x takes
+  // items [x per, (x + 1) per)
+  const int b = int(blockIdx.x);
+  const int per = (n_items + 7) / 8;
+  const int logical = (b % 8) * per + b / 8;
+  if (b / 8 >= per || logical >= n_items) return false;
+  if (logical >= routed_items) {
+    const int local = logical - routed_items;
+    const int ms = local % shared_tiles;
+    *nt_out = local / shared_tiles;
+    *e_out = a.E;
+    *row0_out = ms * kGemmBM;  // token index of the first row
+    *m_out = min(kGemmBM, a.T - ms * kGemmBM);
+    return true;
+  }
+  // pass 2: the expert whose items hold it (inclusive scan of items)
   if (tid == 0) s_e = -1;
   int base = 0;
   for (int c0 = 0; c0 < a.E; c0 += THREADS) {
     const int e = c0 + tid;
-    int lo = 0, cnt = 0;
-    if (e < a.E) {
-      lo = a.offsets[e];
-      cnt = a.offsets[e + 1] - lo;
-    }
-    const int tiles = (cnt + kGemmBM - 1) / kGemmBM;
-    // inclusive wave scan of tiles
-    int v = tiles;
+    int lo = lo_c0;
+    const int rows = c0 == 0 ? rows_c0 : rows_of(e, &lo);
+    const int items = (rows + kGemmBM - 1) / kGemmBM * NT;
+    int v = items;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(v, off);
@@ -106,35 +145,33 @@ __device__ bool gemm_find_mtile(const GemmArgs &a, int mi, int *e_out, int *row0
     }
     if (lane == 63) s_cnt[wave] = v;
     __syncthreads();
-    int before = base, total = 0;
+    int before = base, sum = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       if (w < wave) before += s_cnt[w];
-      total += s_cnt[w];
+      sum += s_cnt[w];
     }
-    const int first = before + v - tiles;  // exclusive
-    if (tiles > 0 && mi >= first && mi < first + tiles) {
+    const int first = before + v - items;  // exclusive
+    if (items > 0 && logical >= first && logical < first + items) {
       s_e = e;
-      s_r0 = lo + (mi - first) * kGemmBM;
-      s_m = min(kGemmBM, cnt - (mi - first) * kGemmBM);
+      s_first = first;
+      s_lo = lo;
+      s_rows = rows;
     }
-    base += total;
+    base += sum;
     __syncthreads();
+    if (s_e >= 0) break;
   }
-  if (s_e < 0 && a.shared_blob != nullptr) {
-    const int ms = mi - base;
-    if (ms >= 0 && ms * kGemmBM < a.T) {
-      *e_out = a.E;
-      *row0_out = ms * kGemmBM;  // token index of the first row
-      *m_out = min(kGemmBM, a.T - ms * kGemmBM);
-      return true;
-    }
-    return false;
-  }
-  if (s_e < 0) return false;
-  *e_out = s_e;
-  *row0_out = s_r0;
-  *m_out = s_m;
+  const int e = s_e;
+  if (e < 0) return false;
+  const int lo = s_lo, cnt = s_rows;
+  const int tiles = (cnt + kGemmBM - 1) / kGemmBM;
+  const int local = logical - s_first;
+  const int mi = local % tiles;
+  *nt_out = local / tiles;
+  *e_out = e;
+  *row0_out = lo + mi * kGemmBM;
+  *m_out = min(kGemmBM, cnt - mi * kGemmBM);
   return true;
 }
 
@@ -166,16 +203,8 @@ template <bool GLU>
 __device__ __forceinline__ bool gemm_setup(const GemmArgs &a, int &nt_idx, int &row0, int &m, bool &shared,
                                            const uint8_t *&blob) {
   const int tid = threadIdx.x;
-  // ---- work item: block ids go round-robin over the 8 XCDs; give each XCD a
-  // contiguous range of items (the grid is a multiple of 8)
-  const int G = int(gridDim.x), b = int(blockIdx.x);
-  const int per = G / 8;
-  const int logical = (b % 8) * per + b / 8;
-  if (logical >= a.n_items) return false;
-  int mi;
-  if (!gemm_item(a, logical, &nt_idx, &mi)) return false;
   int e;
-  if (!gemm_find_mtile<kGemmThreads>(a, mi, &e, &row0, &m)) return false;
+  if (!gemm_find_item<kGemmThreads>(a, &nt_idx, &e, &row0, &m)) return false;
   shared = e == a.E;
   if (shared) {
     blob = a.shared_blob;
