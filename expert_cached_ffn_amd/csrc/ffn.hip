@@ -368,15 +368,17 @@ static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
 
 // ------------------------------------------------------------------ native MXFP4 mode GEMM
 
-// Three pipeline stages of 256-element chunks at one workgroup per CU (99 KiB
-// of LDS; a fourth weight register set would spill).
+// Three pipeline stages of 256-element chunks and the two scale windows at one
+// workgroup per CU (144 KiB of LDS).
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mx_gemm_kernel(MxGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxBufBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[kMxBufBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[kMxBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxCodeBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[kMxCodeBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[kMxCodeBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wsc[kMxWScaleBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t xsc[kMxXScaleBytes];
   static_assert(kMxStages == 3, "one array per stage");
-  gemm_mx_tile<GLU>(a, LdsRing<kMxStages>{{lds0, lds1, lds2}});
+  gemm_mx_tile<GLU>(a, MxLds{LdsRing<kMxStages>{{lds0, lds1, lds2}}, wsc, xsc});
 }
 
 template <bool GLU>

@@ -370,6 +370,8 @@ MX_CASES = [
     ("mx-ragged-tiles", dict(H=512, I=768, E=5, k=3), 300),
     ("mx-cfg3-T1", {}, 1),
     ("mx-cfg3-T8", {}, 8),
+    # rows of more than 4096 elements: the block scales come in two windows
+    ("mx-two-scale-windows", dict(H=4608, I=4352, E=2, k=1), 24),
 ]
 
 
