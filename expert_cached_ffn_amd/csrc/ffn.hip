@@ -347,10 +347,10 @@ __global__ __launch_bounds__(kGemmThreads, WF == WF_FP4 ? 2 : 1) void ffn_gemm_k
   gemm_tile<WF, GLU, 2>(a, LdsRing<2>{{l0, l1}});
 }
 
-// Upper bound of token tiles over all segments (+ the shared expert).
-static int gemm_mtiles_bound(int T, int k, int E, bool shared) {
+// Upper bound of token tiles of BM rows over all segments (+ the shared expert).
+static int gemm_mtiles_bound(int T, int k, int E, bool shared, int BM = kGemmBM) {
   const int64_t routed = int64_t(T) * k;
-  return int(routed / kGemmBM + std::min<int64_t>(E, routed) + (shared ? cdiv(T, kGemmBM) : 0));
+  return int(routed / BM + std::min<int64_t>(E, routed) + (shared ? cdiv(T, BM) : 0));
 }
 
 template <int WF, bool GLU>
@@ -368,8 +368,8 @@ static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
 
 // ------------------------------------------------------------------ native MXFP4 mode GEMM
 
-// Three pipeline stages of 256-element chunks and the two scale windows at one
-// workgroup per CU (144 KiB of LDS).
+// Three pipeline stages of 128-element chunks of 256 token rows and the two
+// scale windows at one workgroup per CU (128 KiB of LDS).
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mx_gemm_kernel(MxGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxCodeBytes];
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void ffn_mx_gemm_kernel(MxGemmArgs
 template <bool GLU>
 static ft_status launch_mx_gemm(MxGemmArgs a, hipStream_t stream, const char *name) {
   const int nt = GLU ? cdiv(a.g.N, kGemmBN / 2) : cdiv(a.g.N, kGemmBN);
-  const int mb = gemm_mtiles_bound(a.g.T, a.g.k, a.g.E, a.g.shared_blob != nullptr);
+  const int mb = gemm_mtiles_bound(a.g.T, a.g.k, a.g.E, a.g.shared_blob != nullptr, kMxBM);
   a.g.n_ntiles = nt;
   a.g.n_mtiles = mb;
   a.g.n_items = gemm_item_count(mb, nt);

@@ -8,40 +8,41 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 (A = tokens, B = weights); nothing is
 // decoded in registers.
 //
-// Workgroup = 4 waves; tile = 128 segment rows (tokens) x 256 weight rows, the
-// same split as the exact-mode GEMM: stage 1 gives each wave 32 gate rows and
-// the same 32 up rows, stage 2 64 weight rows; per wave 8 token tiles x 4
-// weight tiles of 16x16 accumulators.  A chunk is 256 contraction elements,
-// two MFMA steps, so the workgroup meets at a barrier once per 256 elements.
-// Token codes of a chunk (128 rows x 256 bytes) are gathered into LDS by
-// direct buffer-to-LDS loads.  Weights go from global memory straight to
-// registers (each weight row is used by one wave).  Two chunks are in flight
-// while one is multiplied (three LDS buffers, three weight register sets); one
-// workgroup per CU, the accumulators in AGPRs.
+// Workgroup = 4 waves; tile = 256 segment rows (tokens) x 256 weight rows:
+// stage 1 gives each wave 32 gate rows and the same 32 up rows, stage 2 64
+// weight rows; per wave 16 token tiles x 4 weight tiles of 16x16 accumulators
+// (all 256 AGPRs).  The tall token tile is what keeps the CUs fed: each chunk
+// brings 48 KiB into the CU for 2 x 256 x 256 x 128 flops, and the vector
+// memory path of a CU, not the MFMA, is what limits this kernel.  A chunk is
+// 128 contraction elements (one MFMA step); the token codes of a chunk (256
+// rows x 128 bytes) are gathered into LDS by direct buffer-to-LDS loads, the
+// weights go from global memory straight to registers (each weight row is used
+// by one wave).  Two chunks are in flight while one is multiplied (three LDS
+// buffers, three weight register sets); one workgroup per CU.
 //
-// Block scales are not fetched per chunk: a chunk needs 8 bytes of each row,
-// and fetching them one chunk at a time costs the L1 a request per row for 8
-// bytes.  Instead each row's scales of a window of 16 chunks (128 bytes, one
-// cache line) are copied into LDS once -- for the 256 weight rows and the 128
-// token rows of the tile -- and every chunk reads its 8 bytes per row from
-// there.  A window covers K <= 4096 whole; longer rows load the next window
-// at its first chunk, with the pipeline drained around that load.
+// Block scales are not fetched per chunk: a chunk needs 4 bytes of each row,
+// and fetching them one chunk at a time costs the L1 a request per row for 4
+// bytes.  Instead each row's scales of a window of 16 chunks (64 bytes) are
+// copied into LDS once -- for the 256 weight rows and the 256 token rows of the
+// tile -- and every chunk reads its 4 bytes per row from there.  A window
+// covers K <= 2048 whole; longer rows load the next window at its first chunk,
+// with the pipeline drained around that load.
 //
-// Index maps per chunk c (MFMA steps s = 0, 1), lane (r, g):
-//   token operand: row r of the 16-row tile, row bytes 128 s + 16 g .. +15 and
-//                  128 s + 64 + 16 g .. +15; 16-byte piece j of a row is stored
-//                  in slot j ^ (row % 16), so the 16 rows an MFMA operand reads
-//                  hit distinct banks.
-//   weight operand: row r of the tile, code bytes 128 c + 64 s + 16 g .. +15
-//                   (elements 256 c + 128 s + 32 g .. +31).
-//   scales (either operand): byte 8 c + 4 s + g of the row's scales.  In the
-//                  LDS copy a row takes P bytes (128, or the row's scale bytes
+// Index maps per chunk c, lane (r, g):
+//   token operand: row r of the 16-row tile, row bytes 16 g .. +15 and
+//                  64 + 16 g .. +15 of the chunk; 16-byte piece j of a row is
+//                  stored in slot j ^ ((row / 2) % 8), so the 16 rows an MFMA
+//                  operand reads hit distinct banks.
+//   weight operand: row r of the tile, code bytes 64 c + 16 g .. +15
+//                   (elements 128 c + 32 g .. +31).
+//   scales (either operand): byte 4 c + g of the row's scales.  In the LDS
+//                  copy a row takes P bytes (64, or the row's scale bytes
 //                  rounded up to a power of two >= 16 when they are fewer), and
 //                  its 16-byte piece j is stored in slot j ^ f(row % 16) with
 //                  f(R) = (R / (16 / (P/16))) mod (P/16), so that the 16 rows
 //                  one read touches sit in distinct banks.
-// A segment's last tile runs with 4 or 2 of its 8 token sub-tiles when it
-// holds <= 64 or <= 32 rows (the others would only multiply padding).
+// A segment's last tile runs with 8, 4 or 2 of its 16 token sub-tiles when it
+// holds <= 128, <= 64 or <= 32 rows (the others would only multiply padding).
 #pragma once
 
 #include <type_traits>
@@ -51,13 +52,14 @@
 
 namespace ft {
 
-constexpr int kMxBK = 256;                        // contraction elements per chunk (two MFMA steps)
-constexpr int kMxPitch = 256;                     // LDS bytes per token row (codes of one chunk)
-constexpr int kMxCodeBytes = kGemmBM * kMxPitch;  // 32 KiB per buffer
+constexpr int kMxBM = 256;                        // token rows per tile
+constexpr int kMxBK = 128;                        // contraction elements per chunk (one MFMA step)
+constexpr int kMxPitch = 128;                     // LDS bytes per token row (codes of one chunk)
+constexpr int kMxCodeBytes = kMxBM * kMxPitch;    // 32 KiB per buffer
 constexpr int kMxStages = 3;                      // LDS code buffers (chunks in flight + 1)
-constexpr int kMxSWin = 128;                      // scale bytes per row in one window (16 chunks)
-constexpr int kMxWScaleBytes = kGemmBN * kMxSWin; // weight scales of a window: 32 KiB
-constexpr int kMxXScaleBytes = kGemmBM * kMxSWin; // token scales of a window: 16 KiB
+constexpr int kMxSWin = 64;                       // scale bytes per row in one window (16 chunks)
+constexpr int kMxWScaleBytes = kGemmBN * kMxSWin; // weight scales of a window: 16 KiB
+constexpr int kMxXScaleBytes = kMxBM * kMxSWin;   // token scales of a window: 16 KiB
 
 struct MxGemmArgs {
   GemmArgs g;          // shapes, weights, segments and outputs (g.X, g.ldx, g.x_bytes unused)
@@ -69,8 +71,8 @@ struct MxGemmArgs {
 // LDS of one workgroup: the code ring and the two scale windows.
 struct MxLds {
   LdsRing<kMxStages> code;
-  uint8_t *wsc;  // [4 waves][64 rows][P], 8 KiB per wave
-  uint8_t *xsc;  // [4 waves][32 rows][P], 4 KiB per wave
+  uint8_t *wsc;  // [4 waves][64 rows][P], 4 KiB per wave
+  uint8_t *xsc;  // [4 waves][64 rows][P], 4 KiB per wave
 };
 
 template <bool GLU, int MT>
@@ -82,8 +84,10 @@ __device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, const MxLds &
   int nt_idx, row0, m;
   bool shared;
   const uint8_t *blob;
-  if (!gemm_setup<GLU>(ma.g, nt_idx, row0, m, shared, blob)) return;
-  if (m > 64)
+  if (!gemm_setup<GLU, kMxBM>(ma.g, nt_idx, row0, m, shared, blob)) return;
+  if (m > 128)
+    gemm_mx_body<GLU, 16>(ma, L, nt_idx, row0, m, shared, blob);
+  else if (m > 64)
     gemm_mx_body<GLU, 8>(ma, L, nt_idx, row0, m, shared, blob);
   else if (m > 32)
     gemm_mx_body<GLU, 4>(ma, L, nt_idx, row0, m, shared, blob);
@@ -106,16 +110,16 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
     return a.sorted_rows[row0 + rr] / a.k;                                    // gathered token
   };
 
-  // ---- token codes: wave w fills rows 32w..32w+31 with 8 direct loads of 4
-  // rows each (lane i: row 4t + i/16, slot i%16)
+  // ---- token codes: wave w fills rows 64w..64w+63 with 8 direct loads of 8
+  // rows each (lane i: row 8t + i/8, slot i%8)
   const uint32_t kq = uint32_t(a.K);
   const rsrc_t qres = make_rsrc(ma.Xq, ma.xq_bytes);
   uint32_t qsrc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const int rr = wave * 32 + t * 4 + (lane >> 4);
+    const int rr = wave * 64 + t * 8 + (lane >> 3);
     const int src = src_row(rr);
-    const int j = (lane & 15) ^ (rr & 15);
+    const int j = (lane & 7) ^ ((rr >> 1) & 7);
     qsrc[t] = src >= 0 ? uint32_t(src) * kq + uint32_t(j) * 16u : kOOB;
   }
 
@@ -146,15 +150,15 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
     P = 16;
     while (P < srow) P <<= 1;
   }
-  const int ppr = P / 16;  // pieces per row: 1, 2, 4 or 8
+  const int ppr = P / 16;  // pieces per row: 1, 2 or 4
   auto fsw = [&](int R) { return (R / (16 / ppr)) & (ppr - 1); };
   const rsrc_t bres = make_rsrc(blob, uint32_t(a.expert_bytes));
   const rsrc_t xsres = make_rsrc(ma.Xs, ma.xs_bytes);
   uint8_t *const wsc_w = L.wsc + wave * (64 * kMxSWin);
-  uint8_t *const xsc_w = L.xsc + wave * (32 * kMxSWin);
-  // window win of this wave's 64 weight rows (ppr loads of 1 KiB) and 32 token
-  // rows (max(1, ppr / 2) loads); lane i of load n covers row (64 n + i) / ppr,
-  // slot (64 n + i) % ppr
+  uint8_t *const xsc_w = L.xsc + wave * (64 * kMxSWin);
+  // window win of this wave's 64 weight rows and 64 token rows (ppr loads of
+  // 1 KiB each); lane i of load n covers row (64 n + i) / ppr, slot
+  // (64 n + i) % ppr
   auto load_scales = [&](int win) {
     const uint32_t woff = uint32_t(win) * kMxSWin;
     for (int n = 0; n < ppr; ++n) {
@@ -174,24 +178,23 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (__attribute__((address_space(3))) void *)(wsc_w + n * 1024), 16,
                                                off, 0, 0, 0);
     }
-    const int nx = ppr > 2 ? ppr / 2 : 1;
-    for (int n = 0; n < nx; ++n) {
+    for (int n = 0; n < ppr; ++n) {
       const int u = n * 64 + lane, rho = u / ppr, j = u % ppr;
       const int piece = j ^ fsw(rho & 15);
-      const int src = rho < 32 ? src_row(wave * 32 + rho) : -1;
+      const int src = src_row(wave * 64 + rho);
       const uint32_t off = src >= 0 ? uint32_t(src) * uint32_t(srow) + woff + uint32_t(piece) * 16u : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xsres, (__attribute__((address_space(3))) void *)(xsc_w + n * 1024),
                                                16, off, 0, 0, 0);
     }
   };
   // this lane's scale rows in LDS: weight tile t adds 16 t P; token tile i
-  // adds (i / 2) 4096 (the wave area of its rows) + (i % 2) 16 P
+  // adds (i / 4) 4096 (the wave area of its rows) + (i % 4) 16 P
   const int f_r = fsw(r);
   const uint8_t *const wsc_t = L.wsc + wave * (64 * kMxSWin) + r * P;
   const uint8_t *const xsc_t = L.xsc + r * P;
 
   struct BFrag {
-    u32x4 w[NT][2];  // MFMA steps 0, 1 of the chunk
+    u32x4 w[NT];
   };
   const int nch = a.K / kMxBK;
   // A chunk past the end is still issued, with out-of-range offsets (no memory
@@ -204,18 +207,15 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
   auto load_b = [&](int c, BFrag &f) {
     const uint32_t dead = dead_bit(c);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f.w[t][0] = bld16(wres[t], (wbase[t] + uint32_t(c) * 128u) | dead);
-      f.w[t][1] = bld16(wres[t], (wbase[t] + uint32_t(c) * 128u + 64u) | dead);
-    }
+    for (int t = 0; t < NT; ++t) f.w[t] = bld16(wres[t], (wbase[t] + uint32_t(c) * 64u) | dead);
   };
   auto load_a = [&](int c, uint8_t *base) {
     const uint32_t dead = dead_bit(c);
-    uint8_t *cb = base + wave * 32 * kMxPitch;
+    uint8_t *cb = base + wave * 64 * kMxPitch;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qres, (__attribute__((address_space(3))) void *)(cb + t * 4 * kMxPitch),
-                                               16, (qsrc[t] + uint32_t(c) * 256u) | dead, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qres, (__attribute__((address_space(3))) void *)(cb + t * 8 * kMxPitch),
+                                               16, (qsrc[t] + uint32_t(c) * 128u) | dead, 0, 0, 0);
   };
 
   f32x4 acc[MT][NT];
@@ -225,20 +225,17 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // this lane's LDS read addresses of token codes in buffer 0, tile 0: the two
-  // 16-byte pieces of its row for each MFMA step; tile i adds i * 16 rows (the
-  // slot map depends on row % 16 only)
-  int oa_lo[2], oa_hi[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    oa_lo[st] = r * kMxPitch + (((8 * st + q) ^ r) << 4);
-    oa_hi[st] = r * kMxPitch + (((8 * st + 4 + q) ^ r) << 4);
-  }
+  // 16-byte pieces of its row; tile i adds i * 16 rows (the slot map depends on
+  // row % 16 only)
+  const int sw = (r >> 1) & 7;
+  const int oa_lo = r * kMxPitch + ((q ^ sw) << 4);
+  const int oa_hi = r * kMxPitch + (((4 + q) ^ sw) << 4);
   // ---- pipeline: PF chunks in flight ahead of the one being multiplied, in
   // PF + 1 LDS buffers and PF + 1 weight register sets (a ring, unrolled so the
   // register set of every step is fixed at compile time)
   constexpr int NBUF = kMxStages;
   constexpr int PF = NBUF - 1;
-  constexpr int LOADS = 8 + 2 * NT;  // vector-memory instructions per chunk and wave
+  constexpr int LOADS = 8 + NT;  // vector-memory instructions per chunk and wave
   BFrag fr[NBUF];
   // The vmcnt arithmetic needs the loads issued window first, then chunk by
   // chunk: keep the scheduler from interleaving them (it would, and the waits
@@ -255,11 +252,11 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
   wait_vmcnt<(PF - 1) * LOADS>();  // the window and chunk 0 have landed
   lds_barrier();
 
-  constexpr int kChunksPerWin = kMxSWin / 8;
+  constexpr int kChunksPerWin = kMxSWin / 4;
   auto body = [&](auto jc, int c) {
     constexpr int J = decltype(jc)::value;
     if (c > 0 && c < nch && c % kChunksPerWin == 0) {
-      // next scale window (rows longer than 4096): every wave is past the
+      // next scale window (rows longer than 2048): every wave is past the
       // previous chunk's reads; drain, load, and meet again
       lds_barrier();
       load_scales(c / kChunksPerWin);
@@ -272,40 +269,46 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
     if (c < nch) {
       const BFrag &f = fr[J];
       const uint8_t *buf = L.code.b[J];
-      // this chunk's 8 scale bytes of a row: piece (c mod 16) / 2, half c mod 2
+      // this chunk's scale byte of a row for lane group g: piece (c mod 16) / 4,
+      // byte 4 (c mod 4) + g; each lane reads its own byte, so it needs no shift
       const int cw = c % kChunksPerWin;
-      const int soff = (((cw >> 1) ^ f_r) << 4) + ((cw & 1) << 3);
-      u32x2 ws[NT];
+      const int soff = (((cw >> 2) ^ f_r) << 4) + ((cw & 3) << 2) + q;
+      i32x8 bw[NT];
+      int bs[NT], as[MT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) ws[t] = *reinterpret_cast<const u32x2 *>(wsc_t + t * 16 * P + soff);
+      for (int t = 0; t < NT; ++t) {
+        // FP4 operands use the low four dwords only
+        bw[t] = __builtin_bit_cast(i32x8, __builtin_shufflevector(f.w[t], f.w[t], 0, 1, 2, 3, -1, -1, -1, -1));
+        bs[t] = wsc_t[t * 16 * P + soff];
+      }
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        i32x8 bw[NT];
-        int bs[NT];
+      for (int i = 0; i < MT; ++i) as[i] = xsc_t[(i >> 2) * (64 * kMxSWin) + (i & 3) * 16 * P + soff];
+      // token operands read from LDS two sub-tiles ahead of their MFMAs: with
+      // one wave per SIMD nothing else hides an LDS read's latency, and the
+      // four MFMAs of one sub-tile are shorter than it under load
+      constexpr int D = MT < 2 ? MT : 2;
+      u32x4 alo[MT], ahi[MT];
+      auto read_a = [&](int i) {
+        alo[i] = *reinterpret_cast<const u32x4 *>(buf + oa_lo + i * 16 * kMxPitch);
+        ahi[i] = *reinterpret_cast<const u32x4 *>(buf + oa_hi + i * 16 * kMxPitch);
+      };
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          // FP4 operands use the low four dwords only
-          bw[t] = __builtin_bit_cast(i32x8,
-                                     __builtin_shufflevector(f.w[t][st], f.w[t][st], 0, 1, 2, 3, -1, -1, -1, -1));
-          bs[t] = int(ws[t][st] >> (8 * q));
-        }
+      for (int i = 0; i < D; ++i) read_a(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, NT + MT + 2 * D, 0);  // scale bytes, sub-tiles 0 .. D-1
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const u32x4 lo = *reinterpret_cast<const u32x4 *>(buf + oa_lo[st] + i * 16 * kMxPitch);
-          const u32x4 hi = *reinterpret_cast<const u32x4 *>(buf + oa_hi[st] + i * 16 * kMxPitch);
-          const int as = int(*reinterpret_cast<const uint32_t *>(xsc_t + (i >> 1) * (32 * kMxSWin) +
-                                                                 (i & 1) * 16 * P + soff + 4 * st) >>
-                             (8 * q));
-          const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int i = 0; i < MT; ++i) {
+        if (i + D < MT) read_a(i + D);
+        const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(alo[i], ahi[i], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int t = 0; t < NT; ++t) acc[i][t] = mfma_mx(av, bw[t], acc[i][t], as, bs[t]);
-        }
+        for (int t = 0; t < NT; ++t) acc[i][t] = mfma_mx(av, bw[t], acc[i][t], as[i], bs[t]);
+        if (i + D < MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // operand of sub-tile i + D
+        __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);                 // MFMAs of sub-tile i
       }
     }
     wait_vmcnt<(PF - 1) * LOADS>();  // chunk c + 1 has landed; c + 2 .. c + PF may still fly
     lds_barrier();
   };
-  static_assert(8 + 4 + PF * LOADS < 64, "vmcnt is six bits");
+  static_assert(2 * 4 + PF * LOADS < 64, "vmcnt is six bits");
   for (int c = 0; c < nch; c += NBUF)
     unroll_ring([&](auto jc) { body(jc, c + decltype(jc)::value); }, std::make_integer_sequence<int, NBUF>{});
   wait_vmcnt<0>();

@@ -79,8 +79,8 @@ struct GemmArgs {
 __host__ __device__ inline int gemm_item_count(int n_mtiles, int n_ntiles) { return n_mtiles * n_ntiles; }
 
 // Block-wide: this block's work item -- weight tile, expert, first row of the
-// token tile and its row count.  False if the block has none.
-template <int THREADS>
+// token tile (BM rows) and its row count.  False if the block has none.
+template <int THREADS, int BM = kGemmBM>
 __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *row0_out, int *m_out) {
   constexpr int NW = THREADS / 64;
   __shared__ int s_cnt[NW];
@@ -102,7 +102,7 @@ __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *
       lo_c0 = lo;
       rows_c0 = rows;
     }
-    int v = (rows + kGemmBM - 1) / kGemmBM;
+    int v = (rows + BM - 1) / BM;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     if (lane == 0) s_cnt[wave] = v;
@@ -112,7 +112,7 @@ __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *
     __syncthreads();
   }
   const int routed_items = total * NT;
-  const int shared_tiles = a.shared_blob != nullptr ? (a.T + kGemmBM - 1) / kGemmBM : 0;
+  const int shared_tiles = a.shared_blob != nullptr ? (a.T + BM - 1) / BM : 0;
   const int n_items = routed_items + shared_tiles * NT;
   // this block's item: block ids go round-robin over the 8 XCDs; XCD x takes
   // items [x per, (x + 1) per)
@@ -125,8 +125,8 @@ __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *
     const int ms = local % shared_tiles;
     *nt_out = local / shared_tiles;
     *e_out = a.E;
-    *row0_out = ms * kGemmBM;  // token index of the first row
-    *m_out = min(kGemmBM, a.T - ms * kGemmBM);
+    *row0_out = ms * BM;  // token index of the first row
+    *m_out = min(BM, a.T - ms * BM);
     return true;
   }
   // pass 2: the expert whose items hold it (inclusive scan of items)
@@ -136,7 +136,7 @@ __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *
     const int e = c0 + tid;
     int lo = lo_c0;
     const int rows = c0 == 0 ? rows_c0 : rows_of(e, &lo);
-    const int items = (rows + kGemmBM - 1) / kGemmBM * NT;
+    const int items = (rows + BM - 1) / BM * NT;
     int v = items;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -165,13 +165,13 @@ __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *
   const int e = s_e;
   if (e < 0) return false;
   const int lo = s_lo, cnt = s_rows;
-  const int tiles = (cnt + kGemmBM - 1) / kGemmBM;
+  const int tiles = (cnt + BM - 1) / BM;
   const int local = logical - s_first;
   const int mi = local % tiles;
   *nt_out = local / tiles;
   *e_out = e;
-  *row0_out = lo + mi * kGemmBM;
-  *m_out = min(kGemmBM, cnt - mi * kGemmBM);
+  *row0_out = lo + mi * BM;
+  *m_out = min(BM, cnt - mi * BM);
   return true;
 }
 
@@ -199,12 +199,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, in
 // This workgroup's work item: the weight tile, the token tile's first row
 // and row count, the expert's blob.  False if there is none, or if the expert
 // is not resident (its outputs of this tile were then marked NaN).
-template <bool GLU>
+template <bool GLU, int BM = kGemmBM>
 __device__ __forceinline__ bool gemm_setup(const GemmArgs &a, int &nt_idx, int &row0, int &m, bool &shared,
                                            const uint8_t *&blob) {
   const int tid = threadIdx.x;
   int e;
-  if (!gemm_find_item<kGemmThreads>(a, &nt_idx, &e, &row0, &m)) return false;
+  if (!gemm_find_item<kGemmThreads, BM>(a, &nt_idx, &e, &row0, &m)) return false;
   shared = e == a.E;
   if (shared) {
     blob = a.shared_blob;
