@@ -368,17 +368,16 @@ static ft_status launch_gemm(GemmArgs a, hipStream_t stream, const char *name) {
 
 // ------------------------------------------------------------------ native MXFP4 mode GEMM
 
-// Three pipeline stages of 128-element chunks of 256 token rows and the two
-// scale windows at one workgroup per CU (128 KiB of LDS).
+// Three pipeline stages of 128-element chunks of 128 token rows and the two
+// scale windows: 72 KiB of LDS, two workgroups per CU.
 template <bool GLU>
-__global__ __launch_bounds__(kGemmThreads, 1) void ffn_mx_gemm_kernel(MxGemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, 2) void ffn_mx_gemm_kernel(MxGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxCodeBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds1[kMxCodeBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[kMxCodeBytes];
   __shared__ __attribute__((aligned(16))) uint8_t wsc[kMxWScaleBytes];
   __shared__ __attribute__((aligned(16))) uint8_t xsc[kMxXScaleBytes];
-  static_assert(kMxStages == 3, "one array per stage");
-  gemm_mx_tile<GLU>(a, MxLds{LdsRing<kMxStages>{{lds0, lds1, lds2}}, wsc, xsc});
+  static_assert(kMxStages == 2, "one array per stage");
+  gemm_mx_tile<GLU>(a, MxLds{LdsRing<kMxStages>{{lds0, lds1}}, wsc, xsc});
 }
 
 template <bool GLU>

@@ -8,22 +8,24 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 (A = tokens, B = weights); nothing is
 // decoded in registers.
 //
-// Workgroup = 4 waves; tile = 256 segment rows (tokens) x 256 weight rows:
+// Workgroup = 4 waves; tile = 128 segment rows (tokens) x 256 weight rows:
 // stage 1 gives each wave 32 gate rows and the same 32 up rows, stage 2 64
-// weight rows; per wave 16 token tiles x 4 weight tiles of 16x16 accumulators
-// (all 256 AGPRs).  The tall token tile is what keeps the CUs fed: each chunk
-// brings 48 KiB into the CU for 2 x 256 x 256 x 128 flops, and the vector
-// memory path of a CU, not the MFMA, is what limits this kernel.  A chunk is
-// 128 contraction elements (one MFMA step); the token codes of a chunk (256
-// rows x 128 bytes) are gathered into LDS by direct buffer-to-LDS loads, the
-// weights go from global memory straight to registers (each weight row is used
-// by one wave).  Two chunks are in flight while one is multiplied (three LDS
-// buffers, three weight register sets); one workgroup per CU.
+// weight rows; per wave 8 token tiles x 4 weight tiles of 16x16 accumulators.
+// Two workgroups share a CU (two waves per SIMD): with one wave per SIMD the
+// MFMA pipe idled through every wait of that wave -- measured, the kernel then
+// ran at a quarter of the MFMA rate whether or not its loads hit in cache --
+// and that is what sizes everything else: 128 accumulators, two weight
+// register sets and 56 KiB of LDS per workgroup.  A chunk is 128 contraction
+// elements (one MFMA step); the token codes of a chunk (128 rows x 128 bytes)
+// are gathered into LDS by direct buffer-to-LDS loads, the weights go from
+// global memory straight to registers (each weight row is used by one wave).
+// One chunk is in flight while one is multiplied (two LDS buffers, two weight
+// register sets).
 //
 // Block scales are not fetched per chunk: a chunk needs 4 bytes of each row,
 // and fetching them one chunk at a time costs the L1 a request per row for 4
 // bytes.  Instead each row's scales of a window of 16 chunks (64 bytes) are
-// copied into LDS once -- for the 256 weight rows and the 256 token rows of the
+// copied into LDS once -- for the 256 weight rows and the 128 token rows of the
 // tile -- and every chunk reads its 4 bytes per row from there.  A window
 // covers K <= 2048 whole; longer rows load the next window at its first chunk,
 // with the pipeline drained around that load.
@@ -41,8 +43,8 @@
 //                  its 16-byte piece j is stored in slot j ^ f(row % 16) with
 //                  f(R) = (R / (16 / (P/16))) mod (P/16), so that the 16 rows
 //                  one read touches sit in distinct banks.
-// A segment's last tile runs with 8, 4 or 2 of its 16 token sub-tiles when it
-// holds <= 128, <= 64 or <= 32 rows (the others would only multiply padding).
+// A segment's last tile runs with 4 or 2 of its 8 token sub-tiles when it
+// holds <= 64 or <= 32 rows (the others would only multiply padding).
 #pragma once
 
 #include <type_traits>
@@ -52,14 +54,15 @@
 
 namespace ft {
 
-constexpr int kMxBM = 256;                        // token rows per tile
+constexpr int kMxBM = 128;                        // token rows per tile
+constexpr int kMxRW = kMxBM / 4;                  // token rows each wave loads
 constexpr int kMxBK = 128;                        // contraction elements per chunk (one MFMA step)
 constexpr int kMxPitch = 128;                     // LDS bytes per token row (codes of one chunk)
-constexpr int kMxCodeBytes = kMxBM * kMxPitch;    // 32 KiB per buffer
-constexpr int kMxStages = 3;                      // LDS code buffers (chunks in flight + 1)
+constexpr int kMxCodeBytes = kMxBM * kMxPitch;    // 16 KiB per buffer
+constexpr int kMxStages = 2;                      // LDS code buffers (chunks in flight + 1)
 constexpr int kMxSWin = 64;                       // scale bytes per row in one window (16 chunks)
 constexpr int kMxWScaleBytes = kGemmBN * kMxSWin; // weight scales of a window: 16 KiB
-constexpr int kMxXScaleBytes = kMxBM * kMxSWin;   // token scales of a window: 16 KiB
+constexpr int kMxXScaleBytes = kMxBM * kMxSWin;   // token scales of a window: 8 KiB
 
 struct MxGemmArgs {
   GemmArgs g;          // shapes, weights, segments and outputs (g.X, g.ldx, g.x_bytes unused)
@@ -72,7 +75,7 @@ struct MxGemmArgs {
 struct MxLds {
   LdsRing<kMxStages> code;
   uint8_t *wsc;  // [4 waves][64 rows][P], 4 KiB per wave
-  uint8_t *xsc;  // [4 waves][64 rows][P], 4 KiB per wave
+  uint8_t *xsc;  // [4 waves][32 rows][P], 2 KiB per wave
 };
 
 template <bool GLU, int MT>
@@ -85,9 +88,7 @@ __device__ __forceinline__ void gemm_mx_tile(const MxGemmArgs &ma, const MxLds &
   bool shared;
   const uint8_t *blob;
   if (!gemm_setup<GLU, kMxBM>(ma.g, nt_idx, row0, m, shared, blob)) return;
-  if (m > 128)
-    gemm_mx_body<GLU, 16>(ma, L, nt_idx, row0, m, shared, blob);
-  else if (m > 64)
+  if (m > 64)
     gemm_mx_body<GLU, 8>(ma, L, nt_idx, row0, m, shared, blob);
   else if (m > 32)
     gemm_mx_body<GLU, 4>(ma, L, nt_idx, row0, m, shared, blob);
@@ -114,10 +115,11 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
   // rows each (lane i: row 8t + i/8, slot i%8)
   const uint32_t kq = uint32_t(a.K);
   const rsrc_t qres = make_rsrc(ma.Xq, ma.xq_bytes);
-  uint32_t qsrc[8];
+  constexpr int TL = kMxRW / 8;  // token-code loads per wave and chunk
+  uint32_t qsrc[TL];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int rr = wave * 64 + t * 8 + (lane >> 3);
+  for (int t = 0; t < TL; ++t) {
+    const int rr = wave * kMxRW + t * 8 + (lane >> 3);
     const int src = src_row(rr);
     const int j = (lane & 7) ^ ((rr >> 1) & 7);
     qsrc[t] = src >= 0 ? uint32_t(src) * kq + uint32_t(j) * 16u : kOOB;
@@ -155,7 +157,7 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
   const rsrc_t bres = make_rsrc(blob, uint32_t(a.expert_bytes));
   const rsrc_t xsres = make_rsrc(ma.Xs, ma.xs_bytes);
   uint8_t *const wsc_w = L.wsc + wave * (64 * kMxSWin);
-  uint8_t *const xsc_w = L.xsc + wave * (64 * kMxSWin);
+  uint8_t *const xsc_w = L.xsc + wave * (kMxRW * kMxSWin);
   // window win of this wave's 64 weight rows and 64 token rows (ppr loads of
   // 1 KiB each); lane i of load n covers row (64 n + i) / ppr, slot
   // (64 n + i) % ppr
@@ -178,10 +180,11 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (__attribute__((address_space(3))) void *)(wsc_w + n * 1024), 16,
                                                off, 0, 0, 0);
     }
-    for (int n = 0; n < ppr; ++n) {
+    const int nx = (kMxRW * ppr + 63) / 64;
+    for (int n = 0; n < nx; ++n) {
       const int u = n * 64 + lane, rho = u / ppr, j = u % ppr;
       const int piece = j ^ fsw(rho & 15);
-      const int src = src_row(wave * 64 + rho);
+      const int src = rho < kMxRW ? src_row(wave * kMxRW + rho) : -1;
       const uint32_t off = src >= 0 ? uint32_t(src) * uint32_t(srow) + woff + uint32_t(piece) * 16u : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xsres, (__attribute__((address_space(3))) void *)(xsc_w + n * 1024),
                                                16, off, 0, 0, 0);
@@ -211,9 +214,9 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
   };
   auto load_a = [&](int c, uint8_t *base) {
     const uint32_t dead = dead_bit(c);
-    uint8_t *cb = base + wave * 64 * kMxPitch;
+    uint8_t *cb = base + wave * kMxRW * kMxPitch;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < TL; ++t)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qres, (__attribute__((address_space(3))) void *)(cb + t * 8 * kMxPitch),
                                                16, (qsrc[t] + uint32_t(c) * 128u) | dead, 0, 0, 0);
   };
@@ -235,7 +238,7 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
   // register set of every step is fixed at compile time)
   constexpr int NBUF = kMxStages;
   constexpr int PF = NBUF - 1;
-  constexpr int LOADS = 8 + NT;  // vector-memory instructions per chunk and wave
+  constexpr int LOADS = TL + NT;  // vector-memory instructions per chunk and wave
   BFrag fr[NBUF];
   // The vmcnt arithmetic needs the loads issued window first, then chunk by
   // chunk: keep the scheduler from interleaving them (it would, and the waits
@@ -282,11 +285,10 @@ __device__ __forceinline__ void gemm_mx_body(const MxGemmArgs &ma, const MxLds &
         bs[t] = wsc_t[t * 16 * P + soff];
       }
 #pragma unroll
-      for (int i = 0; i < MT; ++i) as[i] = xsc_t[(i >> 2) * (64 * kMxSWin) + (i & 3) * 16 * P + soff];
-      // token operands read from LDS two sub-tiles ahead of their MFMAs: with
-      // one wave per SIMD nothing else hides an LDS read's latency, and the
-      // four MFMAs of one sub-tile are shorter than it under load
-      constexpr int D = MT < 2 ? MT : 2;
+      for (int i = 0; i < MT; ++i)
+        as[i] = xsc_t[(i / (kMxRW / 16)) * (kMxRW * kMxSWin) + (i % (kMxRW / 16)) * 16 * P + soff];
+      // token operands read from LDS one sub-tile ahead of their MFMAs
+      constexpr int D = 1;
       u32x4 alo[MT], ahi[MT];
       auto read_a = [&](int i) {
         alo[i] = *reinterpret_cast<const u32x4 *>(buf + oa_lo + i * 16 * kMxPitch);
