@@ -334,13 +334,14 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
 
 // ------------------------------------------------------------------ prefill grouped GEMM
 
-// Two pipeline stages.  MXFP4 weights: two workgroups per CU (measured
-// faster than four stages at one workgroup per CU: the second wave on each
-// SIMD hides the FP4 decode and the MFMA dependency chains).  bf16 weights
-// need four times the weight registers: one workgroup per CU, so that
-// nothing spills.
+// Two pipeline stages.  MXFP4 and NVFP4 weights: two workgroups per CU
+// (measured faster than four stages at one workgroup per CU: the second wave
+// on each SIMD hides the 4-bit decode and the MFMA dependency chains; NVFP4
+// went from 1.57 to 1.12 ms per 8192-token layer when its scales stopped
+// taking a register set per stage).  bf16 weights need four times the weight
+// registers: one workgroup per CU, so that nothing spills.
 template <int WF, bool GLU>
-__global__ __launch_bounds__(kGemmThreads, WF == WF_FP4 ? 2 : 1) void ffn_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, WF == WF_BF16 ? 1 : 2) void ffn_gemm_kernel(GemmArgs a) {
   constexpr int B = kGemmBM * kGemmPitch;
   __shared__ __attribute__((aligned(16))) uint8_t l0[B];
   __shared__ __attribute__((aligned(16))) uint8_t l1[B];

@@ -292,8 +292,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, in
   constexpr int DLW = WF == WF_BF16 ? 4 : 1;  // 16-byte weight loads per tile per chunk
   struct BFrag {
     u32x4 w[NT][DLW];
-    std::conditional_t<WF == WF_NV4, u32x2, uint32_t> s[NT];  // the chunk's block scales (4 E8M0 / 8 E4M3)
   };
+  // Block scales (4 E8M0 or 8 E4M3 bytes per row and chunk) come four chunks
+  // at a time: lane group g loads the scales of chunk c0 + g, so the four
+  // lanes of a row fetch 16 or 32 contiguous bytes in one request (one load
+  // per chunk and row cost a request for 4 or 8 bytes), and a chunk's step
+  // takes its row's scales from lane group c mod 4.
+  using SWord = std::conditional_t<WF == WF_NV4, u32x2, uint32_t>;
+  constexpr int SB = WF == WF_NV4 ? 8 : 4;  // scale bytes per row and chunk
   const int nch = a.K / kGemmBK;
   // A chunk past the end is still issued, with out-of-range offsets (no memory
   // traffic, zeros): every step then has the same loads in flight, and the
@@ -308,10 +314,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, in
           f.w[t][d] = bld16(wres[t], live ? wrow[t] * wpitch + uint32_t(c) * 256u + d * 64 + q * 16 : kOOB);
       } else {
         f.w[t][0] = bld16(wres[t], live ? wrow[t] * wpitch + uint32_t(c) * 64u + q * 16 : kOOB);
-        if constexpr (WF == WF_NV4)
-          f.s[t] = bld8(sres[t], live ? wrow[t] * spitch + uint32_t(c) * 8u : kOOB);
-        else
-          f.s[t] = bld4(sres[t], live ? wrow[t] * spitch + uint32_t(c) * 4u : kOOB);
       }
     }
   };
@@ -323,6 +325,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, in
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void *)(base + t * 4 * kGemmPitch), 16,
           (xsrc[t] == kOOB || !live) ? kOOB : xsrc[t] + uint32_t(c) * 256u, 0, 0, 0);
+  };
+
+  auto load_s = [&](int c0, SWord *g) {
+    const bool live = c0 + q < nch;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t off = live ? wrow[t] * spitch + uint32_t(c0 + q) * SB : kOOB;
+      if constexpr (WF == WF_NV4)
+        g[t] = bld8(sres[t], off);
+      else
+        g[t] = bld4(sres[t], off);
+    }
   };
 
   f32x4 acc[MT][NT];
@@ -338,27 +352,45 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, in
   // (every wave passed the barrier that ended step c - 1), multiplies chunk c,
   // then waits until chunk c + 1 has landed and meets the other waves.
   constexpr int P = NBUF - 1;
-  constexpr int LOADS = 8 + NT * (WF == WF_BF16 ? 4 : 2);  // vector-memory instructions per chunk and wave
-  static_assert((P - 1) * LOADS < 64, "vmcnt is six bits");
+  static_assert(P == 1, "every step waits for all of its loads");
+  constexpr int UNR = WF == WF_BF16 ? NBUF : 4;  // steps per loop pass: a multiple of NBUF and of 4
+  static_assert(UNR % NBUF == 0, "ring");
   BFrag fr[NBUF];
+  SWord sg[NT], sgn[NT];  // scales of chunks c0 .. c0+3 (lane group g: c0 + g), and of the next four
+  if constexpr (WF != WF_BF16) {
+    load_s(0, sg);
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    load_a(p, L.b[p]);
-    load_b(p, fr[p]);
+    for (int t = 0; t < NT; ++t) sgn[t] = sg[t];
   }
-  wait_vmcnt<(P - 1) * LOADS>();  // chunk 0 has landed
+  load_a(0, L.b[0]);
+  load_b(0, fr[0]);
+  wait_vmcnt<0>();  // chunk 0 has landed
   lds_barrier();
   auto step = [&](auto jc, int c) {
-    constexpr int J = decltype(jc)::value;
-    // with one chunk in flight every wait is a full one, so the past-the-end
-    // chunk need not be issued
-    if (P > 1 || c + P < nch) {
+    constexpr int JU = decltype(jc)::value;
+    constexpr int J = JU % NBUF;
+    if (c + P < nch) {
       load_a(c + P, L.b[(J + P) % NBUF]);
       load_b(c + P, fr[(J + P) % NBUF]);
+      if constexpr (WF != WF_BF16 && JU % 4 == 3) load_s(c + 1, sgn);
     }
     if (c < nch) {
       const BFrag &f = fr[J];
       const uint8_t *abuf = L.b[J];
+      // this chunk's scales of the lane's row, from lane group c mod 4
+      SWord cs[NT];
+      if constexpr (WF != WF_BF16) {
+        const int src = (r + 16 * (JU % 4)) * 4;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (WF == WF_NV4) {
+            cs[t][0] = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(sg[t][0])));
+            cs[t][1] = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(sg[t][1])));
+          } else {
+            cs[t] = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(sg[t])));
+          }
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8 bw[NT];
@@ -367,9 +399,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, in
           if constexpr (WF == WF_BF16) {
             bw[t] = as_bf16x8(f.w[t][ks]);
           } else if constexpr (WF == WF_FP4) {
-            bw[t] = fp4x8_to_bf16x8(f.w[t][0][ks], e8m0_to_f32((f.s[t] >> (8 * q)) & 0xffu));
+            bw[t] = fp4x8_to_bf16x8(f.w[t][0][ks], e8m0_to_f32((cs[t] >> (8 * q)) & 0xffu));
           } else {  // NVFP4: elements 32q + 8ks .. +7 lie in 16-element block 2q + ks/2
-            const uint32_t sw = (q >> 1) ? f.s[t][1] : f.s[t][0];
+            const uint32_t sw = (q >> 1) ? cs[t][1] : cs[t][0];
             bw[t] = nvfp4x8_to_bf16x8(f.w[t][0][ks], e4m3_to_f32(sw >> (8 * ((2 * q + (ks >> 1)) & 3))));
           }
         }
@@ -382,11 +414,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, LdsRing<NBUF> L, in
         }
       }
     }
-    wait_vmcnt<(P - 1) * LOADS>();  // chunk c + 1 has landed; c + 2 .. c + P may still fly
+    wait_vmcnt<0>();  // chunk c + 1 (and the next scales) have landed
     lds_barrier();
+    if constexpr (WF != WF_BF16 && JU % 4 == 3) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sg[t] = sgn[t];
+    }
   };
-  for (int c = 0; c < nch; c += NBUF)
-    unroll_ring([&](auto jc) { step(jc, c + decltype(jc)::value); }, std::make_integer_sequence<int, NBUF>{});
+  for (int c = 0; c < nch; c += UNR)
+    unroll_ring([&](auto jc) { step(jc, c + decltype(jc)::value); }, std::make_integer_sequence<int, UNR>{});
   wait_vmcnt<0>();
 
   // ---- epilogue: lane holds D[token 4q+v][weight row r] of each tile
