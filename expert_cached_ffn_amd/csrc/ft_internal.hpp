@@ -185,4 +185,90 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4
 template <typename T>
 __host__ __device__ __forceinline__ T cdiv(T a, T b) { return (a + b - 1) / b; }
 
+// ---- wave-wide reductions and scans on DPP lane moves.  A shuffle through
+// ds_bpermute is an LDS round trip; the reductions below stay in the VALU.
+// Every lane of the wave must be active.  DPP controls used: quad_perm
+// [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E), row_shr:n (0x110 + n), row_ror:n
+// (0x120 + n), row_mirror (0x140), row_half_mirror (0x141), row_bcast:15
+// (0x142, written to rows 1 and 3) and row_bcast:31 (0x143, rows 2 and 3).
+// A lane whose source is outside its row, or whose row is masked off, gets
+// `old`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(src), CTRL, ROW_MASK, 0xf, false));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint64_t dpp_max_u64_step(uint64_t x) {
+  const uint32_t lo = uint32_t(x), hi = uint32_t(x >> 32);
+  const uint64_t o = (uint64_t(dpp_u32<CTRL, ROW_MASK>(hi, hi)) << 32) | dpp_u32<CTRL, ROW_MASK>(lo, lo);
+  return o > x ? o : x;
+}
+
+// Maximum over the wave, in every lane: quads, half rows and rows by
+// butterflies (max is idempotent, so mirrors serve), then rows 0+1 and 2+3 by
+// broadcasts, the total landing in lane 63.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = dpp_max_u64_step<0xB1>(x);
+  x = dpp_max_u64_step<0x4E>(x);
+  x = dpp_max_u64_step<0x141>(x);
+  x = dpp_max_u64_step<0x140>(x);
+  x = dpp_max_u64_step<0x142, 0xA>(x);
+  x = dpp_max_u64_step<0x143, 0xC>(x);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x)), 63));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x >> 32)), 63));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float old, float src) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL, ROW_MASK>(__builtin_bit_cast(uint32_t, old),
+                                                           __builtin_bit_cast(uint32_t, src)));
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x, x));
+  x = fmaxf(x, dpp_f32<0x4E>(x, x));
+  x = fmaxf(x, dpp_f32<0x141>(x, x));
+  x = fmaxf(x, dpp_f32<0x140>(x, x));
+  x = fmaxf(x, dpp_f32<0x142, 0xA>(x, x));
+  x = fmaxf(x, dpp_f32<0x143, 0xC>(x, x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Sum over the wave, in every lane: quad butterflies, then each lane adds the
+// quad 4 and the pair of quads 8 lanes around its row (row sums), then the
+// row broadcasts as above.
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += dpp_f32<0xB1>(x, x);
+  x += dpp_f32<0x4E>(x, x);
+  x += dpp_f32<0x124>(x, x);
+  x += dpp_f32<0x128>(x, x);
+  x += dpp_f32<0x142, 0xA>(0.f, x);
+  x += dpp_f32<0x143, 0xC>(0.f, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  x += int(dpp_u32<0xB1>(uint32_t(x), uint32_t(x)));
+  x += int(dpp_u32<0x4E>(uint32_t(x), uint32_t(x)));
+  x += int(dpp_u32<0x124>(uint32_t(x), uint32_t(x)));
+  x += int(dpp_u32<0x128>(uint32_t(x), uint32_t(x)));
+  x += int(dpp_u32<0x142, 0xA>(0u, uint32_t(x)));
+  x += int(dpp_u32<0x143, 0xC>(0u, uint32_t(x)));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Inclusive prefix sum over the lanes: a shift-and-add scan within each row of
+// 16 lanes, then the rows' totals carried by the row broadcasts.
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  x += int(dpp_u32<0x111>(0u, uint32_t(x)));
+  x += int(dpp_u32<0x112>(0u, uint32_t(x)));
+  x += int(dpp_u32<0x114>(0u, uint32_t(x)));
+  x += int(dpp_u32<0x118>(0u, uint32_t(x)));
+  x += int(dpp_u32<0x142, 0xA>(0u, uint32_t(x)));
+  x += int(dpp_u32<0x143, 0xC>(0u, uint32_t(x)));
+  return x;
+}
+
 }  // namespace ft

@@ -102,9 +102,7 @@ __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *
       lo_c0 = lo;
       rows_c0 = rows;
     }
-    int v = (rows + BM - 1) / BM;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int v = wave_sum_i32((rows + BM - 1) / BM);
     if (lane == 0) s_cnt[wave] = v;
     __syncthreads();
 #pragma unroll
@@ -137,12 +135,7 @@ __device__ bool gemm_find_item(const GemmArgs &a, int *nt_out, int *e_out, int *
     int lo = lo_c0;
     const int rows = c0 == 0 ? rows_c0 : rows_of(e, &lo);
     const int items = (rows + BM - 1) / BM * NT;
-    int v = items;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(v, off);
-      if (lane >= off) v += o;
-    }
+    const int v = wave_incl_scan_i32(items);
     if (lane == 63) s_cnt[wave] = v;
     __syncthreads();
     int before = base, sum = 0;

@@ -52,11 +52,7 @@ __device__ inline int block_exclusive_scan(int *s, int n, int *s_tmp /* >= 32 in
   for (int i = a; i < b; ++i) local += s[i];
   // inclusive scan of `local` across the block
   const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
-  int v = local;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+  const int v = wave_incl_scan_i32(local);
   if (lane == 63) s_tmp[wave] = v;
   __syncthreads();
   if (tid == 0) {

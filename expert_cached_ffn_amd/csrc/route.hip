@@ -57,11 +57,7 @@ __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum_f32(v); }
 
 // One wave per token.  Lane l holds the token's logits l, l+64, ... as 64-bit
 // keys: the logit mapped to an unsigned integer of the same order (-0.0 taken
@@ -111,11 +107,7 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
     uint64_t best = key[0];
 #pragma unroll
     for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint64_t o = __shfl_xor(best, off);
-      best = o > best ? o : best;
-    }
+    best = wave_max_u64(best);
     const int e = int(~uint32_t(best));
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
@@ -131,8 +123,7 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
   float mx = v[0];
 #pragma unroll
   for (int i = 1; i < VPL; ++i) mx = fmaxf(mx, v[i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = wave_max_f32(mx);
   float denom = 1.0f;
   if (gating == FT_SOFTMAX) {
     float s = 0.f;

@@ -367,12 +367,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
   for (int c0 = 0; c0 < n_act; c0 += THREADS) {
     const int i = c0 + tid;
     const int g = i < n_act ? (s_m[i] + 15) >> 4 : 0;
-    int v = g;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(v, off);
-      if (lane >= off) v += t;
-    }
+    const int v = wave_incl_scan_i32(g);
     if (lane == 63) s_cnt[wave] = v;
     __syncthreads();
     int before = n_groups, total = 0;
