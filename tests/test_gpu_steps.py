@@ -261,6 +261,8 @@ FFN_CASES = [
     ("bf16-cfg2-T16", 2, {}, 16),
     ("fp4-small", 3, dict(H=1024, I=512, E=6, k=2), 37),
     ("fp4-long-segment", 3, dict(H=512, I=1024, E=2, k=1), 150),
+    # prefill GEMM over 6 chunks a stage: the block-scale groups of 4 chunks end part-way
+    ("fp4-prefill-six-chunks", 3, dict(H=768, I=768, E=5, k=3), 130),
     ("fp4-cfg3-T1", 3, {}, 1),
     ("fp4-decode-multigroup", 3, dict(H=512, I=256, E=3, k=2), 60),     # ~40 tokens per expert: 3 groups each
     ("fp4-decode-T64-E16", 3, dict(H=1024, I=1024, E=16, k=4), 64),
