@@ -98,4 +98,45 @@ __device__ inline void permute_block(const int32_t *ids, int R, int E, int *s_cn
   if (tid < 64) wave_scatter(ids, 0, R, E, s_cnt, sorted_rows, row_pos);
 }
 
+// Stable counting sort of R <= 64 routed rows by one wave, without a block
+// barrier: lane i ranks row i by per-bit ballots -- the rows with a smaller
+// expert id (counted among the lanes that agree with it on the higher bits and
+// hold a 0 where it holds a 1) plus the rows of its own expert in lower lanes
+// -- and writes its place; each expert's segment start is then the lower
+// bound of its id in the sorted ids (s_sorted, 64 ints of LDS).  ids may be
+// global or LDS; every id must lie in [0, E).
+__device__ inline void permute_wave64(const int32_t *ids, int R, int E, int32_t *s_sorted,
+                                      int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
+                                      int32_t *__restrict__ row_pos) {
+  const int lane = threadIdx.x & 63;
+  const bool act = lane < R;
+  const int key = act ? ids[lane] : 0;
+  uint64_t eq = __ballot(act);
+  int less = 0;
+  for (int b = bits_for(E) - 1; b >= 0; --b) {
+    const int bit = (key >> b) & 1;
+    const uint64_t ones = __ballot(bit);
+    if (bit) less += __popcll(eq & ~ones);
+    eq &= bit ? ones : ~ones;
+  }
+  const int pos = less + __popcll(eq & ((uint64_t(1) << lane) - 1));
+  if (act) {
+    sorted_rows[pos] = lane;
+    row_pos[lane] = pos;
+    s_sorted[pos] = key;
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e <= E; e += 64) {
+    int lo = 0, hi = R;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_sorted[mid] < e)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    offsets[e] = lo;
+  }
+}
+
 }  // namespace ft

@@ -183,11 +183,17 @@ __device__ __forceinline__ void route_tail(const FusedRouteArgs &a, int32_t *s_i
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int t = wave; t < a.T; t += nw) topk_token<VPL>(a.logits, t, a.E, a.k, a.gating, a.renorm, a.ids, a.w, s_ids);
   __syncthreads();
-  permute_block(s_ids, a.T * a.k, a.E, s_cnt, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
+  if (a.T * a.k <= 64) {
+    if (wave == 0) permute_wave64(s_ids, a.T * a.k, a.E, s_cnt, a.offsets, a.sorted_rows, a.row_pos);
+  } else {
+    permute_block(s_ids, a.T * a.k, a.E, s_cnt, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
+  }
 }
 
 // Top-k, gating and permutation of all T tokens in one workgroup (small decode
-// batches, T <= 16): one launch after the router instead of two.  (A single
+// batches, T <= 16): one launch after the router instead of two.  Up to 64
+// routed rows the workgroup is one wave per token and wave 0 sorts the rows
+// alone (no block-wide histogram, scan and barriers).  (A single
 // launch with the router, its last workgroup doing this, was measured
 // slower: the device-scope fences that publish the logits write back and
 // invalidate the L2 of every XCD.)
@@ -323,9 +329,11 @@ extern "C" ft_status ft_moe_route_permute(const void *x, int32_t x_dtype, const 
   a.sorted_rows = sorted_rows;
   a.row_pos = row_pos;
   const int vpl = cdiv(E, 64);
-  if (vpl <= 2) hipLaunchKernelGGL(route_tail_kernel<2>, dim3(1), dim3(1024), 0, stream, a);
-  else if (vpl <= 4) hipLaunchKernelGGL(route_tail_kernel<4>, dim3(1), dim3(1024), 0, stream, a);
-  else hipLaunchKernelGGL(route_tail_kernel<16>, dim3(1), dim3(1024), 0, stream, a);
+  // up to 64 routed rows one wave sorts them: one wave per token is enough
+  const dim3 blk(T * k <= 64 ? 64 * T : 1024);
+  if (vpl <= 2) hipLaunchKernelGGL(route_tail_kernel<2>, dim3(1), blk, 0, stream, a);
+  else if (vpl <= 4) hipLaunchKernelGGL(route_tail_kernel<4>, dim3(1), blk, 0, stream, a);
+  else hipLaunchKernelGGL(route_tail_kernel<16>, dim3(1), blk, 0, stream, a);
   FT_LAUNCHED("route_tail_kernel");
   clear_error();
   return FT_OK;

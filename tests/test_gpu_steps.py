@@ -149,7 +149,8 @@ def test_route_permute_with_router(ops, cfg_id, T):
         _check_permutation(ids, off, rows, pos, cfg.E, ids_ref)
 
 
-@pytest.mark.parametrize("E,k,T", [(128, 8, 1), (256, 6, 64), (16, 16, 9), (1000, 2, 33), (256, 6, 300)])
+@pytest.mark.parametrize("E,k,T", [(128, 8, 1), (256, 6, 64), (16, 16, 9), (1000, 2, 33), (256, 6, 300),
+                                   (16, 16, 4), (1000, 2, 16), (256, 6, 10)])
 def test_route_permute_given_logits_bit_exact(ops, E, k, T):
     cfg = synth.shrink(synth.CONFIGS[3], E=E, k=k, shared=False)
     rng = np.random.default_rng(E + k + T)
