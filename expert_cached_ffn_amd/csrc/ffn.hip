@@ -298,6 +298,14 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
     waves = 4;
     kpw = 2;
   }
+  // NVFP4 over 16 k-blocks: 16 waves x 1 block (90 VGPRs, four waves per SIMD)
+  // instead of 8 x 2 (172 VGPRs, two): its decode's dependent VALU chains
+  // need the waves; measured 70.6 -> 61.1 us for the gate/up stage at 64
+  // tokens.  (MXFP4 and bf16 measured no gain.)
+  if (WF == WF_NV4 && waves == 8 && kpw == 2) {
+    waves = 16;
+    kpw = 1;
+  }
   persist_override(GLU, a.K / stream_kblock<WF>(), &waves, &kpw);
   // x-stationary runs for MXFP4 weights (measured 1.65x at 32 tokens: a 16-row
   // FP4 tile is half the bytes of a bf16 one, so the freed activation
