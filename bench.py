@@ -431,20 +431,22 @@ def run_cache_trace(args, cfg):
     slot_hits = torch.empty(E, dtype=torch.int32, device="cuda")
 
     def run(steps, cache, hybrid=False, hits_first=False):
-        """hits_first: the hits' FFN (and the shared expert's) is enqueued before the step's fills
-        land, the filled misses' FFN after them; otherwise one FFN waits for every fill."""
+        """hits_first: the hits' FFN (and the shared expert's) is enqueued right after the LRU update,
+        before the host waits for it (ft_expert_cache_plan, then ft_expert_cache_fill) and before the
+        step's fills land; the filled misses' FFN after them.  Otherwise one FFN waits for every fill."""
         for st in range(steps):
             for l in range(Lyr):
                 i = st * Lyr + l
                 layer.route_permute(1, logits=logits[i:i + 1])
                 if hits_first:
-                    n_fill = cache.step_split(l, layer.ids, 1, cfg.k, slot_hits, slot_of)
+                    cache.plan(l, layer.ids, 1, cfg.k, slot_hits, slot_of)
+                    layer.ffn(1, xs[i], pool, slot_of_expert=slot_hits, shared_blob=shared[l])
+                    n_fill = cache.fill()
                 else:
                     cache.step(l, layer.ids, 1, cfg.k, slot_of)
                 if hybrid:
                     layer.stage_cpu_misses(cache, 1, xs[i])
                 if hits_first:
-                    layer.ffn(1, xs[i], pool, slot_of_expert=slot_hits, shared_blob=shared[l])
                     cache.wait_fills()
                     if n_fill or (hybrid and cache.cpu_misses()):
                         layer.ffn(1, xs[i], pool, slot_of_expert=slot_of)

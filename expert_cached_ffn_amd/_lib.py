@@ -27,7 +27,7 @@ EXPORTS = [
     "ft_expert_cache_resize", "ft_expert_cache_prefetch_layer", "ft_expert_cache_set_split",
     "ft_expert_cache_cpu_misses", "ft_cpu_expert_ffn", "ft_cpu_miss_rows", "ft_cpu_isa",
     "ft_expert_cache_stage_cpu_misses", "ft_expert_cache_run_cpu_misses", "ft_expert_cache_step_split",
-    "ft_expert_cache_wait_fills",
+    "ft_expert_cache_wait_fills", "ft_expert_cache_plan", "ft_expert_cache_fill",
 ]
 
 
@@ -90,6 +90,10 @@ def lib() -> C.CDLL:
     L.ft_expert_cache_step_split.argtypes = [p, i32, p, i32, i32, p, p, C.POINTER(C.c_int32), p]
     L.ft_expert_cache_wait_fills.restype = i32
     L.ft_expert_cache_wait_fills.argtypes = [p, p]
+    L.ft_expert_cache_plan.restype = i32
+    L.ft_expert_cache_plan.argtypes = [p, i32, p, i32, i32, p, p, p]
+    L.ft_expert_cache_fill.restype = i32
+    L.ft_expert_cache_fill.argtypes = [p, C.POINTER(C.c_int32)]
     L.ft_expert_cache_run_cpu_misses.restype = i32
     L.ft_expert_cache_run_cpu_misses.argtypes = [p, p, p, i32]
     L.ft_cpu_isa.argtypes = [i32, p]

@@ -327,6 +327,11 @@ struct ft_expert_cache {
   bool pending[kFillStreams];       // a layer prefetch's fills on this queue not yet waited for
   bool unwaited[kFillStreams] = {}; // a split step's fills on this queue (ft_expert_cache_wait_fills)
   int32_t last_filled = 0;          // misses the last step filled
+  // a split step launched by ft_expert_cache_plan, waiting for ft_expert_cache_fill
+  bool planned = false;
+  int32_t plan_layer = 0;
+  int32_t *plan_hits = nullptr;
+  hipStream_t plan_stream = nullptr;
   int32_t *iota;                    // device [E]: 0..E-1 (the needed set of a layer prefetch)
   double b_pcie = 0.0, b_host = 0.0;  // hybrid split (b_host <= 0: every miss is filled)
   std::vector<int32_t> cpu_list;      // the last step's misses left to the CPU
@@ -441,20 +446,33 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
 
 // One LRU update (a step, or a layer prefetch with every expert of the layer
 // needed) and its fills.
-static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *ids, int R, int32_t *slot_of_expert,
-                             int32_t *slot_hits, hipStream_t compute_stream, bool prefetch, const char *who) {
+// A cache step in two halves: cache_launch enqueues the LRU kernel and records
+// ev_lru; cache_collect waits for it on the host and acts on its result (the
+// event log, the fills, the statistics).  `early`: the compute stream waits
+// for a layer prefetch's fills before the LRU kernel rather than after it --
+// for a plan, whose caller queues reads of the hit slots before the collect.
+static ft_status cache_launch(ft_expert_cache *c, int32_t layer, const int32_t *ids, int R, int32_t *slot_of_expert,
+                              int32_t *slot_hits, hipStream_t compute_stream, bool prefetch, bool early) {
   // fills of a split step that the caller did not wait for: order this call's work after them
   for (int q = 0; q < kFillStreams; ++q)
     if (c->unwaited[q]) {
       FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
       c->unwaited[q] = false;
     }
+  if (early)
+    for (int q = 0; q < kFillStreams; ++q)
+      if (c->pending[q]) FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
   c->res_host->status = -1;
   hipLaunchKernelGGL(lru_step_kernel, dim3(1), dim3(kLruThreads), 0, compute_stream, c->st, layer, ids, R, c->E,
                      c->C, prefetch ? 0.0 : c->b_pcie, prefetch ? 0.0 : c->b_host, slot_of_expert, slot_hits,
                      c->res_dev);
   FT_LAUNCHED("lru_step_kernel");
   FT_HIP(hipEventRecord(c->ev_lru, compute_stream));
+  return FT_OK;
+}
+
+static ft_status cache_collect(ft_expert_cache *c, int32_t layer, int32_t *slot_hits, hipStream_t compute_stream,
+                               bool prefetch, const char *who) {
   FT_HIP(hipEventSynchronize(c->ev_lru));
   const LruResult &r = *c->res_host;
   if (r.status == LRU_BAD_ID) return fail(FT_EINVAL, std::string(who) + ": expert id out of range");
@@ -538,6 +556,14 @@ static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *i
   return FT_OK;
 }
 
+static ft_status cache_serve(ft_expert_cache *c, int32_t layer, const int32_t *ids, int R, int32_t *slot_of_expert,
+                             int32_t *slot_hits, hipStream_t compute_stream, bool prefetch, const char *who) {
+  FT_REQUIRE(!c->planned, std::string(who) + ": a planned step is waiting for ft_expert_cache_fill");
+  const ft_status st = cache_launch(c, layer, ids, R, slot_of_expert, slot_hits, compute_stream, prefetch, false);
+  if (st != FT_OK) return st;
+  return cache_collect(c, layer, slot_hits, compute_stream, prefetch, who);
+}
+
 extern "C" ft_status ft_expert_cache_step(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids, int32_t T,
                                           int32_t k, int32_t *slot_of_expert, hipStream_t compute_stream) {
   FT_REQUIRE(c != nullptr, "ft_expert_cache_step: cache is NULL");
@@ -563,6 +589,37 @@ extern "C" ft_status ft_expert_cache_step_split(ft_expert_cache *c, int32_t laye
   FT_REQUIRE(R == 0 || topk_ids != nullptr, "ft_expert_cache_step_split: topk_ids is NULL");
   const ft_status st =
       cache_serve(c, layer, topk_ids, R, slot_misses, slot_hits, compute_stream, false, "ft_expert_cache_step_split");
+  if (st == FT_OK && n_filled != nullptr) *n_filled = c->last_filled;
+  return st;
+}
+
+extern "C" ft_status ft_expert_cache_plan(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids, int32_t T,
+                                          int32_t k, int32_t *slot_hits, int32_t *slot_misses,
+                                          hipStream_t compute_stream) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_plan: cache is NULL");
+  FT_REQUIRE(!c->planned, "ft_expert_cache_plan: the previous plan is waiting for ft_expert_cache_fill");
+  FT_REQUIRE(layer >= 0 && layer < c->n_layers, "ft_expert_cache_plan: layer out of range");
+  FT_REQUIRE(T >= 0 && k >= 1, "ft_expert_cache_plan: need T >= 0, k >= 1");
+  FT_REQUIRE(int64_t(T) * k < (int64_t(1) << 31), "ft_expert_cache_plan: T*k too large");
+  FT_REQUIRE(slot_hits != nullptr && slot_misses != nullptr && slot_hits != slot_misses,
+             "ft_expert_cache_plan: slot_hits and slot_misses must be two tables");
+  const int R = T * k;
+  FT_REQUIRE(R == 0 || topk_ids != nullptr, "ft_expert_cache_plan: topk_ids is NULL");
+  const ft_status st = cache_launch(c, layer, topk_ids, R, slot_misses, slot_hits, compute_stream, false, true);
+  if (st != FT_OK) return st;
+  c->planned = true;
+  c->plan_layer = layer;
+  c->plan_hits = slot_hits;
+  c->plan_stream = compute_stream;
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_fill(ft_expert_cache *c, int32_t *n_filled) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_fill: cache is NULL");
+  FT_REQUIRE(c->planned, "ft_expert_cache_fill: no planned step");
+  c->planned = false;
+  const ft_status st = cache_collect(c, c->plan_layer, c->plan_hits, c->plan_stream, false, "ft_expert_cache_fill");
   if (st == FT_OK && n_filled != nullptr) *n_filled = c->last_filled;
   return st;
 }
@@ -610,6 +667,7 @@ extern "C" ft_status ft_expert_cache_stage_cpu_misses(ft_expert_cache *c, const 
                                                       int32_t k, const int32_t *expert_offsets,
                                                       const int32_t *sorted_rows, hipStream_t stream) {
   FT_REQUIRE(c != nullptr, "ft_expert_cache_stage_cpu_misses: cache is NULL");
+  FT_REQUIRE(!c->planned, "ft_expert_cache_stage_cpu_misses: a planned step is waiting for ft_expert_cache_fill");
   if (c->cpu_list.empty()) {
     clear_error();
     return FT_OK;
@@ -650,6 +708,7 @@ extern "C" ft_status ft_expert_cache_stage_cpu_misses(ft_expert_cache *c, const 
 extern "C" ft_status ft_expert_cache_run_cpu_misses(ft_expert_cache *c, float *y_rows, hipStream_t stream,
                                                     int32_t n_threads) {
   FT_REQUIRE(c != nullptr, "ft_expert_cache_run_cpu_misses: cache is NULL");
+  FT_REQUIRE(!c->planned, "ft_expert_cache_run_cpu_misses: a planned step is waiting for ft_expert_cache_fill");
   if (c->cpu_list.empty()) {
     clear_error();
     return FT_OK;
@@ -704,6 +763,7 @@ extern "C" ft_status ft_expert_cache_run_cpu_misses(ft_expert_cache *c, float *y
 extern "C" ft_status ft_expert_cache_resize(ft_expert_cache *c, int32_t new_capacity, void *new_slot_pool,
                                             hipStream_t stream) {
   FT_REQUIRE(c != nullptr, "ft_expert_cache_resize: cache is NULL");
+  FT_REQUIRE(!c->planned, "ft_expert_cache_resize: a planned step is waiting for ft_expert_cache_fill");
   FT_REQUIRE(new_capacity >= 1, "ft_expert_cache_resize: capacity must be positive");
   FT_SUPPORTED(new_capacity <= kLruMaxC, "ft_expert_cache_resize: capacity > 65536");
   FT_REQUIRE(new_slot_pool != nullptr && aligned(new_slot_pool, 256),

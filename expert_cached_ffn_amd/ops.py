@@ -147,6 +147,22 @@ class ExpertCache:
 
     step_split = ft_expert_cache_step_split
 
+    def ft_expert_cache_plan(self, layer: int, topk_ids, T: int, k: int, slot_hits, slot_misses,
+                             stream=None) -> None:
+        """First half of a hits-first step: enqueue the LRU update and return without waiting."""
+        _check(_lib.lib().ft_expert_cache_plan(self._h, layer, _ptr(topk_ids), T, k, _ptr(slot_hits),
+                                               _ptr(slot_misses), _stream(stream)))
+
+    plan = ft_expert_cache_plan
+
+    def ft_expert_cache_fill(self) -> int:
+        """Second half: wait for the planned LRU update, enqueue the fills; returns their number."""
+        n = C.c_int32()
+        _check(_lib.lib().ft_expert_cache_fill(self._h, C.byref(n)))
+        return n.value
+
+    fill = ft_expert_cache_fill
+
     def ft_expert_cache_wait_fills(self, stream=None) -> None:
         _check(_lib.lib().ft_expert_cache_wait_fills(self._h, _stream(stream)))
 

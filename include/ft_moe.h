@@ -418,8 +418,33 @@ ft_status ft_expert_cache_step_split(ft_expert_cache *c, int32_t layer, const in
                                      int32_t *slot_hits, int32_t *slot_misses, int32_t *n_filled,
                                      hipStream_t compute_stream);
 
-/* Makes compute_stream wait for the fills of the last ft_expert_cache_step_split
- * (a no-op when it had none or they were already waited for). */
+/*
+ * ft_expert_cache_plan + ft_expert_cache_fill -- ft_expert_cache_step_split in
+ * two calls, so that the hits' FFN is queued before the host waits for the
+ * LRU kernel (the same page and section: hits run at once).  plan validates,
+ * makes compute_stream wait for an earlier layer prefetch's fills, enqueues
+ * the LRU update writing slot_hits and slot_misses (as step_split) and
+ * returns without waiting.  Between the two calls the caller may enqueue on
+ * compute_stream work that reads slot_hits and the hit slots (not
+ * slot_misses); fill (host) waits for the LRU kernel, enqueues the misses'
+ * fills and writes their number to *n_filled (host, may be NULL):
+ *
+ *   plan -> ft_moe_grouped_ffn(slot_hits, shared expert) -> fill ->
+ *   ft_expert_cache_wait_fills -> ft_moe_grouped_ffn(slot_misses) -> ...
+ *
+ * A plan must be followed by its fill before any other call that changes the
+ * cache (step, step_split, plan, prefetch, resize, CPU-miss staging):
+ * those return FT_EINVAL meanwhile, as does fill without a plan.  Errors of
+ * the LRU update (FT_ECAPACITY, ids out of range) are returned by fill; the
+ * cache state is then unchanged and the work queued since the plan read
+ * tables that are not valid (discard its outputs).
+ */
+ft_status ft_expert_cache_plan(ft_expert_cache *c, int32_t layer, const int32_t *topk_ids, int32_t T, int32_t k,
+                               int32_t *slot_hits, int32_t *slot_misses, hipStream_t compute_stream);
+ft_status ft_expert_cache_fill(ft_expert_cache *c, int32_t *n_filled);
+
+/* Makes compute_stream wait for the fills of the last split step (step_split or
+ * plan + fill; a no-op when it had none or they were already waited for). */
 ft_status ft_expert_cache_wait_fills(ft_expert_cache *c, hipStream_t compute_stream);
 
 /* Totals since create (host).  */

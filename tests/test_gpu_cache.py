@@ -376,11 +376,12 @@ def test_hybrid_split_against_the_simulator(env):
 
 
 @pytest.mark.parametrize("T,C,hybrid,hits_first", [(1, 10, True, False), (5, 30, True, False),
-                                                   (1, 10, False, True), (5, 30, True, True)])
+                                                   (1, 10, False, True), (5, 30, True, True),
+                                                   (1, 10, False, "plan"), (5, 30, True, "plan")])
 def test_hybrid_layer_outputs(env, T, C, hybrid, hits_first):
     """Decode through the cache, with the CPU miss split (hybrid) and/or the hits-first step (the
-    hits' FFN before the fills land, the filled misses' FFN after): every layer output matches the
-    oracle."""
+    hits' FFN before the fills land, the filled misses' FFN after; "plan": the hits' FFN queued
+    between ft_expert_cache_plan and ft_expert_cache_fill): every layer output matches the oracle."""
     ops, Lm = env
     cfg = synth.shrink(synth.CONFIGS[5], H=512, I=512, E=32, n_layers=2, capacity=C, steps=12)
     shape = Lm.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize, True)
@@ -406,7 +407,11 @@ def test_hybrid_layer_outputs(env, T, C, hybrid, hits_first):
             logits = synth.prefill_logits(cfg, T, case=s, layer=l)
             xd = Lm.to_device(x)
             layer.route_permute(T, logits=Lm.to_device(logits))
-            if hits_first:
+            if hits_first == "plan":
+                cache.plan(l, layer.ids, T, cfg.k, slot_hits, slot_of)
+                layer.ffn(T, xd, pool, slot_of_expert=slot_hits, shared_blob=shared[l])
+                n_fill = cache.fill()
+            elif hits_first:
                 n_fill = cache.step_split(l, layer.ids, T, cfg.k, slot_hits, slot_of)
             else:
                 cache.step(l, layer.ids, T, cfg.k, slot_of)
@@ -414,7 +419,8 @@ def test_hybrid_layer_outputs(env, T, C, hybrid, hits_first):
             n_cpu += len(cpu)
             layer.stage_cpu_misses(cache, T, xd)
             if hits_first:
-                layer.ffn(T, xd, pool, slot_of_expert=slot_hits, shared_blob=shared[l])
+                if hits_first != "plan":
+                    layer.ffn(T, xd, pool, slot_of_expert=slot_hits, shared_blob=shared[l])
                 cache.wait_fills()
                 if n_fill or cpu:  # the filled misses (and NaN rows for the CPU's, patched next)
                     layer.ffn(T, xd, pool, slot_of_expert=slot_of)
@@ -463,9 +469,10 @@ def test_cpu_miss_calls_validate(env):
 
 
 def test_split_step_tables_against_the_simulator(env):
-    """Hits-first steps (with and without the CPU split): slot_hits holds the hits' slots, slot_misses
-    the filled misses' slots, FT_SLOT_SKIP marks the other needed experts, -1 the rest; n_filled counts
-    the fills; events and totals follow the oracle."""
+    """Hits-first steps (with and without the CPU split; step_split and plan + fill alternating):
+    slot_hits holds the hits' slots, slot_misses the filled misses' slots, FT_SLOT_SKIP marks the
+    other needed experts, -1 the rest; n_filled counts the fills; events and totals follow the
+    oracle."""
     ops, _ = env
     from expert_cached_ffn_amd import _lib
     SKIP = _lib.FT_SLOT_SKIP
@@ -484,7 +491,11 @@ def test_split_step_tables_against_the_simulator(env):
         evs = {ev.expert: ev for ev in sim.step(layer, ids, fill_limit=q)}
         rig.cache.set_split(bp, bh)
         d = torch.from_numpy(ids).cuda()
-        n_filled = rig.cache.step_split(layer, d, ids.size, 1, hits_t, rig.slot_of)
+        if t % 2:
+            n_filled = rig.cache.step_split(layer, d, ids.size, 1, hits_t, rig.slot_of)
+        else:  # the same step in two calls
+            rig.cache.plan(layer, d, ids.size, 1, hits_t, rig.slot_of)
+            n_filled = rig.cache.fill()
         rig.cache.wait_fills()
         torch.cuda.synchronize()
         hits, misses = hits_t.cpu().numpy(), rig.slot_of.cpu().numpy()
@@ -503,4 +514,36 @@ def test_split_step_tables_against_the_simulator(env):
     st = rig.cache.stats()
     assert (st["accesses"], st["hits"], st["misses"], st["evictions"], st["cpu_misses"]) == \
         (sim.accesses, sim.hits, sim.misses, sim.evictions, sim.cpu_misses)
+    rig.cache.destroy()
+
+
+def test_plan_and_fill_call_order(env):
+    """fill without a plan, a second plan, and cache-changing calls while a plan waits are refused;
+    an LRU error surfaces at fill and leaves the state as it was."""
+    ops, _ = env
+    rig = Rig(ops, 1, 8, 3)
+    hits_t = torch.empty(8, dtype=torch.int32, device="cuda")
+    d = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    with pytest.raises(ops.FtError) as e:
+        rig.cache.fill()
+    assert e.value.status == -1
+    rig.cache.plan(0, d, 2, 1, hits_t, rig.slot_of)
+    for call in (lambda: rig.cache.plan(0, d, 2, 1, hits_t, rig.slot_of),
+                 lambda: rig.cache.step(0, d, 2, 1, rig.slot_of),
+                 lambda: rig.cache.step_split(0, d, 2, 1, hits_t, rig.slot_of)):
+        with pytest.raises(ops.FtError) as e:
+            call()
+        assert e.value.status == -1
+    assert rig.cache.fill() == 2
+    rig.cache.wait_fills()
+    before = rig.cache.stats()
+    big = torch.tensor([2, 3, 4, 5], dtype=torch.int32, device="cuda")  # 4 distinct experts > 3 slots
+    rig.cache.plan(0, big, 4, 1, hits_t, rig.slot_of)
+    with pytest.raises(ops.FtError) as e:
+        rig.cache.fill()
+    assert e.value.status == -3
+    assert rig.cache.stats() == before
+    rig.cache.plan(0, d, 2, 1, hits_t, rig.slot_of)      # the cache is usable again: two hits
+    assert rig.cache.fill() == 0
+    torch.cuda.synchronize()
     rig.cache.destroy()
