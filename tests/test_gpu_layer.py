@@ -140,3 +140,36 @@ def test_layer_prefill_nvfp4(L):
     a, b = int(off_ref[e]), int(off_ref[e + 1])
     yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
     check_close(layer.y_rows[a:b].cpu().numpy(), yref, what=f"nvfp4 prefill segment of expert {e}")
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3])
+def test_layer_empty_batch_then_small(L, cfg_id):
+    """A step of zero tokens through all four calls launches nothing and writes nothing: the
+    permutation offsets come back all zero, the output buffer keeps its contents, and the next
+    (non-empty) step on the same buffers is still exact."""
+    cfg = synth.shrink(synth.CONFIGS[cfg_id], H=512, I=256, E=8, k=2)
+    print(f"empty batch cfg{cfg_id}", flush=True)
+    ex = Experts(cfg)
+    T = 3
+    x = synth.tokens(cfg, T)
+    wr = synth.router_weight(cfg)
+    layer = make_layer(L, cfg, T)
+    pool = build_pool(L, layer, ex, range(cfg.E), cfg.E)
+    shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
+    xd, wrd = L.to_device(x), L.to_device(wr)
+    layer.offsets.fill_(-7)
+    layer.out.fill_(1234)
+    layer.forward(0, xd, pool, w_router=wrd, shared_blob=shared)
+    torch.cuda.synchronize()
+    assert layer.offsets.cpu().numpy().tolist() == [0] * (cfg.E + 1)
+    assert bool((layer.out == 1234).all())
+    layer.forward(T, xd, pool, w_router=wrd, shared_blob=shared)
+    torch.cuda.synchronize()
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    logits, ids, w, margin = route_oracle(cfg, x64, formats.activations_to_f64(cfg.xdtype, wr))
+    sure = np.flatnonzero(margin > 1e-4)
+    assert len(sure) >= 1
+    assert np.array_equal(layer.ids[:T].cpu().numpy()[sure], ids[sure])
+    ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E) if cfg.shared else None)
+                    for t in sure])
+    check_close(out_f64(layer, cfg, T)[sure], ref, bf16_out=cfg.xdtype == "bf16", what=f"cfg{cfg_id} after empty")
