@@ -21,6 +21,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -107,18 +108,37 @@ def expert_weight_bytes(cfg, part):
 # ----------------------------------------------------------------------------- timing
 
 class Timer:
-    """HIP events on the current stream."""
+    """HIP events on the current stream.  ``n`` events are created (and recorded once) up front, so
+    that no event creation falls inside a timed region."""
 
-    def __init__(self):
+    def __init__(self, n=0):
         import torch
         self.torch = torch
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.pool:
+            e.record()
+        torch.cuda.synchronize()
         self.ev = []
 
     def mark(self):
-        e = self.torch.cuda.Event(enable_timing=True)
+        i = len(self.ev)
+        e = self.pool[i] if i < len(self.pool) else self.torch.cuda.Event(enable_timing=True)
         e.record()
         self.ev.append(e)
         return e
+
+
+class no_gc:
+    """Python's cyclic garbage collector paused for a timed region (a collection pass would stall
+    the host thread that enqueues the launches)."""
+
+    def __enter__(self):
+        self.was = gc.isenabled()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        if self.was:
+            gc.enable()
 
 
 def run_decode(args, cfg, batches, main_T):
@@ -167,13 +187,14 @@ def run_decode(args, cfg, batches, main_T):
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
-        tm = Timer()
+        tm = Timer(3 * args.steps)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
-        start.record()
-        for i in range(args.steps):
-            step(i, tm)
-        end.record()
+        with no_gc():
+            start.record()
+            for i in range(args.steps):
+                step(i, tm)
+            end.record()
         torch.cuda.synchronize()
         total_ms = start.elapsed_time(end)
         ms = total_ms / args.steps
@@ -203,10 +224,11 @@ def run_decode(args, cfg, batches, main_T):
             for i in range(args.warmup):
                 graphs[i % N_INPUT_SETS].replay()
             torch.cuda.synchronize()
-            start.record()
-            for i in range(args.steps):
-                graphs[i % N_INPUT_SETS].replay()
-            end.record()
+            with no_gc():
+                start.record()
+                for i in range(args.steps):
+                    graphs[i % N_INPUT_SETS].replay()
+                end.record()
             torch.cuda.synchronize()
             graph_ms = start.elapsed_time(end) / args.steps
         results[T] = dict(ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), gate_up_ms=k_avg,
@@ -330,13 +352,14 @@ def run_prefill(args, cfg, T, mode=0):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    tm = Timer()
+    tm = Timer(3 * args.steps)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        step(i, tm)
-    end.record()
+    with no_gc():
+        start.record()
+        for i in range(args.steps):
+            step(i, tm)
+        end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     gu = float(np.mean([tm.ev[3 * i].elapsed_time(tm.ev[3 * i + 1]) for i in range(args.steps)]))

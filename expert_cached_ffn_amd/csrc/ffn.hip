@@ -201,10 +201,12 @@ static ft_status launch_stream(const FfnArgs &a, int a_max, int T, hipStream_t s
 
 // Weight register sets in flight for the x-stationary kernel, per shape.
 #ifndef FT_XS_NB
-// (NVFP4 tiles hold half the MXFP4 weight registers: deeper rings)
+// (NVFP4 tiles hold half the MXFP4 weight registers: deeper rings.  bf16 down
+// tiles: 4, not 6, keeps 99 VGPRs and four waves per SIMD; measured 244 vs 247
+// us per 64-token step, and 2 or 3 sets were slower)
 #define FT_XS_NB(WF, GLU, WAVES, KPW)                                                     \
   ((WF) == WF_NV4 ? ((GLU) ? ((WAVES) >= 16 ? 2 : 4) : 6)                                  \
-                  : ((GLU) ? ((WAVES) >= 16 || (KPW) == 2 ? 2 : 4) : ((KPW) == 2 ? 4 : 6)))
+                  : ((GLU) ? ((WAVES) >= 16 || (KPW) == 2 ? 2 : 4) : ((KPW) == 2 || (WF) == WF_BF16 ? 4 : 6)))
 #endif
 
 template <int WF, bool GLU, int WAVES, int KPW>
@@ -309,12 +311,15 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
   persist_override(GLU, a.K / stream_kblock<WF>(), &waves, &kpw);
   // x-stationary runs for MXFP4 weights (measured 1.65x at 32 tokens: a 16-row
   // FP4 tile is half the bytes of a bf16 one, so the freed activation
-  // registers matter); bf16 tiles keep the strided order, measured faster
-  // there.
+  // registers matter).  bf16 gate/up tiles keep the strided order (measured
+  // faster); the bf16 down stage goes x-stationary once there are as many
+  // routed rows as experts (128 experts, top-8: 167.7 -> 164.8 us per step at
+  // 16 tokens, 253.0 -> 244.1 at 64; at 1 token it measured 2 us slower).
   // FTMOE_PERSIST_XS = "<gate/up><down>", each 0 or 1 (e.g. "01").
   static const char *xs_env = getenv("FTMOE_PERSIST_XS");
   const int xs_req = (xs_env && strlen(xs_env) == 2) ? xs_env[GLU ? 0 : 1] - '0' : -1;
-  const bool xs = WF == WF_NV4 || (xs_req < 0 ? WF == WF_FP4 : xs_req != 0);  // NVFP4: x-stationary only
+  const bool xs_auto = WF == WF_FP4 || (!GLU && int64_t(a.T) * a.k >= int64_t(a.E));
+  const bool xs = WF == WF_NV4 || (xs_req < 0 ? xs_auto : xs_req != 0);  // NVFP4: x-stationary only
 #define FT_PERSIST(W, C)                                                                          \
   if (waves == W && kpw == C) {                                                                   \
     if (xs) {                                                                                     \
