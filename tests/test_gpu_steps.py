@@ -150,7 +150,8 @@ def test_route_permute_with_router(ops, cfg_id, T):
 
 
 @pytest.mark.parametrize("E,k,T", [(128, 8, 1), (256, 6, 64), (16, 16, 9), (1000, 2, 33), (256, 6, 300),
-                                   (16, 16, 4), (1000, 2, 16), (256, 6, 10)])
+                                   (16, 16, 4), (1000, 2, 16), (256, 6, 10),
+                                   (1024, 4, 16), (1024, 3, 40)])   # the routing kernels' 1024-expert limit
 def test_route_permute_given_logits_bit_exact(ops, E, k, T):
     cfg = synth.shrink(synth.CONFIGS[3], E=E, k=k, shared=False)
     rng = np.random.default_rng(E + k + T)
@@ -275,6 +276,11 @@ FFN_CASES = [
     ("nv4-prefill-many-tiles", 6, dict(H=512, I=768, E=24, k=3), 700),
     ("bf16-gemm-ragged", 2, dict(H=512, I=384, E=8, k=2), 200),
     ("fp4-gemm-many-tiles", 3, dict(H=512, I=768, E=24, k=3), 700),
+    # the persistent decode kernels' expert-table limit (1024 experts), and one past it (grouped GEMM)
+    ("bf16-decode-E1024-limit", 2, dict(H=512, I=768, E=1024, k=8), 64),
+    ("fp4-decode-E1024-shared", 3, dict(H=1024, I=1024, E=1024, k=6, shared=True), 64),
+    ("bf16-decode-E1100-past-limit", 2, dict(H=512, I=384, E=1100, k=4), 16),
+    ("bf16-E4096-max", 2, dict(H=256, I=256, E=4096, k=2), 40),                  # the grouped FFN's expert limit
 ]
 
 
