@@ -209,11 +209,18 @@ static ft_status launch_stream(const FfnArgs &a, int a_max, int T, hipStream_t s
                   : ((GLU) ? ((WAVES) >= 16 || (KPW) == 2 ? 2 : 4) : ((KPW) == 2 || (WF) == WF_BF16 ? 4 : 6)))
 #endif
 
-template <int WF, bool GLU, int WAVES, int KPW>
+// Register sets for two-row-tile units (RT = 2, NVFP4 down stage): 3 sets
+// measured 118.3 us per 64-token step against 121.0 / 120.3 / 133.8 us with
+// 2 / 4 / 6 sets (111 VGPRs at 4 sets).
+#ifndef FT_XS_NB_RT2
+#define FT_XS_NB_RT2 3
+#endif
+
+template <int WF, bool GLU, int WAVES, int KPW, int RT = 1>
 __global__ __launch_bounds__(WAVES * 64) void ffn_persist_xs_kernel(PersistArgs a) {
-  __shared__ float s_red[WAVES * (GLU ? 2 : 1) * 256];
-  constexpr int NB = FT_XS_NB(WF, GLU, WAVES, KPW);
-  stream_persist_xs<WF, GLU, WAVES, KPW, NB>(a, s_red);
+  __shared__ float s_red[WAVES * (GLU ? 2 : RT) * 256];
+  constexpr int NB = RT == 2 ? FT_XS_NB_RT2 : FT_XS_NB(WF, GLU, WAVES, KPW);
+  stream_persist_xs<WF, GLU, WAVES, KPW, NB, RT>(a, s_red);
 }
 
 template <int WF, bool GLU, int WAVES, int KPW>
@@ -320,8 +327,23 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
   const int xs_req = (xs_env && strlen(xs_env) == 2) ? xs_env[GLU ? 0 : 1] - '0' : -1;
   const bool xs_auto = WF == WF_FP4 || (!GLU && int64_t(a.T) * a.k >= int64_t(a.E));
   const bool xs = WF == WF_NV4 || (xs_req < 0 ? xs_auto : xs_req != 0);  // NVFP4: x-stationary only
+  // NVFP4 down stage: two 16-row tiles per unit (a 16-row tile of a 768-long
+  // contraction is 6.75 KB, so the per-unit LDS round and barriers dominated:
+  // 46.4 -> 35.7 us per launch at 64 tokens, 129.4 -> 118.3 us per step).  bf16
+  // down tiles measured equal with two, so they keep one.  FTMOE_PERSIST_RT =
+  // "1" keeps one tile for NVFP4 too.
+  static const char *rt_env = getenv("FTMOE_PERSIST_RT");
+  const bool rt2 = WF == WF_NV4 && !GLU && !(rt_env && rt_env[0] == '1');
 #define FT_PERSIST(W, C)                                                                          \
   if (waves == W && kpw == C) {                                                                   \
+    if constexpr (WF == WF_NV4 && !GLU) {                                                         \
+      if (rt2) {                                                                                  \
+        const void *kern = reinterpret_cast<const void *>(&ffn_persist_xs_kernel<WF, GLU, W, C, 2>); \
+        const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));               \
+        hipLaunchKernelGGL((ffn_persist_xs_kernel<WF, GLU, W, C, 2>), dim3(g), dim3(W * 64), 0, stream, a); \
+        return true;                                                                              \
+      }                                                                                           \
+    }                                                                                             \
     if (xs) {                                                                                     \
       const void *kern = reinterpret_cast<const void *>(&ffn_persist_xs_kernel<WF, GLU, W, C>); \
       const int g = std::max(1, std::min(max_units, resident_grid(kern, W * 64)));                 \

@@ -299,12 +299,18 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
 // change drains the ring once (one HBM round trip per group and workgroup).
 constexpr int kPersistMaxGroups = kPersistMaxE + 1 + kPersistMaxRows / 16;
 
-template <int WF, bool GLU, int WAVES, int KPW, int NB>
+//
+// RT = 2 (down stage only): a unit is two adjacent 16-row tiles, multiplied
+// with the same activation registers and summed in one LDS round, which
+// halves the barriers per weight byte where a tile is small (NVFP4 tiles of a
+// short contraction).
+template <int WF, bool GLU, int WAVES, int KPW, int NB, int RT = 1>
 __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s_red) {
   static_assert(NB >= 2, "the ring needs two register sets");
+  static_assert(RT == 1 || (RT == 2 && !GLU), "two row tiles per unit: down stage only");
   constexpr int THREADS = WAVES * 64;
   constexpr int NW = WAVES;
-  constexpr int MATS = GLU ? 2 : 1;
+  constexpr int MATS = GLU ? 2 : RT;
   constexpr int KB = stream_kblock<WF>();
   constexpr int DL = WFrag<WF, MATS>::DL;
   constexpr int DX = WF == WF_FP4 ? 8 : 4;
@@ -386,7 +392,8 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
   }
 
   // ---- this workgroup's run of units
-  const int n_units = n_groups * a.n_tiles;
+  const int n_tiles = RT == 1 ? a.n_tiles : (a.N + 16 * RT - 1) / (16 * RT);  // units per token group
+  const int n_units = n_groups * n_tiles;
   const int u_begin = int(int64_t(n_units) * blockIdx.x / gridDim.x);
   const int u_end = int(int64_t(n_units) * (blockIdx.x + 1) / gridDim.x);
 
@@ -407,17 +414,26 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     if constexpr (GLU) {
       wres[MATS - 1] = make_rsrc(blob + a.off_w1, wbytes);
       sres[MATS - 1] = make_rsrc(blob + a.off_s1, sbytes);
+    } else if constexpr (RT == 2) {
+      wres[1] = wres[0];
+      sres[1] = sres[0];
     }
-    const uint32_t wo = tile >= 0 ? uint32_t(tile * 16 + r) * wpitch + uint32_t(q) * 16 : kOOB;
-    const uint32_t so = tile >= 0 ? uint32_t(tile * 16 + r) * spitch : kOOB;
+    uint32_t wo[MATS], so[MATS];
+#pragma unroll
+    for (int mt = 0; mt < MATS; ++mt) {
+      // rows past N fall outside the buffer (zeros, no traffic)
+      const int row = tile * 16 * RT + (GLU ? 0 : 16 * mt) + r;
+      wo[mt] = tile >= 0 ? uint32_t(row) * wpitch + uint32_t(q) * 16 : kOOB;
+      so[mt] = tile >= 0 ? uint32_t(row) * spitch : kOOB;
+    }
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
       const int kb = wave + c * WAVES;
 #pragma unroll
       for (int mt = 0; mt < MATS; ++mt) {
 #pragma unroll
-        for (int d = 0; d < DL; ++d) f[c].w[mt][d] = bld16(wres[mt], wo + uint32_t(kb) * (DL * 64) + d * 64);
-        if constexpr (WF != WF_BF16) f[c].s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);  // 8 blocks
+        for (int d = 0; d < DL; ++d) f[c].w[mt][d] = bld16(wres[mt], wo[mt] + uint32_t(kb) * (DL * 64) + d * 64);
+        if constexpr (WF != WF_BF16) f[c].s[mt] = bld8(sres[mt], so[mt] + uint32_t(kb) * 8);  // 8 blocks
       }
     }
   };
@@ -492,16 +508,17 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     if (tid < 256) {
       const int ln = tid >> 2, v = tid & 3;
       const int jj = g0 + (ln & 15);
-      const int n = tile * 16 + 4 * (ln >> 4) + v;
+      const int n = tile * 16 * RT + 4 * (ln >> 4) + v;  // RT = 2: uu is row n + 16
       float g = 0.f, uu = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
         g += s_red[((w * MATS + 0) * 64 + ln) * 4 + v];
-        if constexpr (GLU) uu += s_red[((w * MATS + 1) * 64 + ln) * 4 + v];
+        if constexpr (MATS == 2) uu += s_red[((w * MATS + 1) * 64 + ln) * 4 + v];
       }
       if constexpr (WF == WF_NV4) {  // the per-tensor scales, on the fp32 sums
         g *= ts0;
         if constexpr (GLU) uu *= ts1;
+        else if constexpr (RT == 2) uu *= ts0;
       }
       if (jj < m && n < a.N) {
         const int p = pos + jj;  // permuted row; hidden rows of the shared expert follow the routed ones
@@ -511,6 +528,8 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
         } else {
           float *yp = shared ? a.out_shared + int64_t(jj) * a.ldo : reinterpret_cast<float *>(a.out) + int64_t(p) * a.ldo;
           yp[n] = missing ? __builtin_nanf("") : g;
+          if constexpr (RT == 2)
+            if (n + 16 < a.N) yp[n + 16] = missing ? __builtin_nanf("") : uu;
         }
       }
     }
@@ -521,9 +540,9 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
   u32x4 xcur[KPW][DX];
   int u = u_begin;
   while (u < u_end) {
-    const int gi = u / a.n_tiles;
-    const int t_begin = u - gi * a.n_tiles;
-    const int t_end = min(a.n_tiles, u_end - gi * a.n_tiles);
+    const int gi = u / n_tiles;
+    const int t_begin = u - gi * n_tiles;
+    const int t_end = min(n_tiles, u_end - gi * n_tiles);
     const int ai = uniform(s_gexp[gi]);
     const int g0 = (gi - uniform(s_gbase[ai])) * 16;
     float ts0 = 1.f, ts1 = 1.f;  // NVFP4 tensor scales of this expert, loaded once per group
@@ -545,7 +564,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
         if (t + s < t_end) finish(ai, g0, t + s, ring[s], xcur, ts0, ts1);
       }
     }
-    u = gi * a.n_tiles + t_end;
+    u = gi * n_tiles + t_end;
   }
 }
 
