@@ -32,7 +32,7 @@ def x_dtype(cfg):
 
 # ----------------------------------------------------------------------------- route
 
-ROUTE_CASES = [(1, 8), (2, 1), (2, 16), (2, 64), (3, 1), (3, 8), (3, 32), (3, 100)]
+ROUTE_CASES = [(1, 8), (2, 1), (2, 3), (2, 16), (2, 64), (3, 1), (3, 2), (3, 3), (3, 4), (3, 5), (3, 8), (3, 32), (3, 100)]
 
 
 @pytest.mark.parametrize("cfg_id,T", ROUTE_CASES)
