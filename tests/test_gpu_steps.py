@@ -295,10 +295,13 @@ def test_grouped_ffn_parity(ops, name, cfg_id, over, T):
         check_close(ys, ys_ref, what=f"{name} y_shared")
 
 
-def test_grouped_ffn_missing_slot_gives_nan(ops):
-    cfg = synth.shrink(synth.CONFIGS[3], H=512, I=512, E=4, k=1, shared=False)
-    ids = np.array([[0], [1], [2], [1]], np.int32)
-    y, _, y_ref, _, off = _ffn_case(ops, cfg, 4, ids, missing=1)
+@pytest.mark.parametrize("cfg_id,T", [(3, 4), (6, 4), (2, 4), (3, 150)])
+def test_grouped_ffn_missing_slot_gives_nan(ops, cfg_id, T):
+    """A routed expert with no slot: its rows are NaN (decode kernels of every weight format, and the
+    prefill GEMM), the other experts' rows are exact."""
+    cfg = synth.shrink(synth.CONFIGS[cfg_id], H=512, I=512, E=4, k=1, shared=False)
+    ids = np.array([[0], [1], [2], [1]] * (T // 4) + [[3]] * (T % 4), np.int32)
+    y, _, y_ref, _, off = _ffn_case(ops, cfg, T, ids, missing=1)
     a, b = int(off[1]), int(off[2])
     assert np.all(np.isnan(y[a:b]))
     keep = np.r_[0:a, b:len(y)]
