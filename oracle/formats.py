@@ -59,6 +59,28 @@ def e8m0_to_f64(byte: np.ndarray) -> np.ndarray:
     return np.where(b == 255, np.nan, v)
 
 
+def _e2m1_byte_pairs() -> np.ndarray:
+    """[256, 2] float64: the (element 2i, element 2i+1) values a code byte holds.
+
+    Built from e2m1_to_f64 on the low and the high nibble of every byte value,
+    so a matrix decodes by one table lookup per byte.
+    """
+    b = np.arange(256)
+    return np.stack([e2m1_to_f64(b & 0x0F), e2m1_to_f64(b >> 4)], axis=1)
+
+
+_E2M1_PAIRS = _e2m1_byte_pairs()
+
+
+def _fp4_block_decode(codes: np.ndarray, block_scale: np.ndarray, block: int) -> np.ndarray:
+    """E2M1 codes [rows, K/2] times one scale per `block` consecutive elements -> [rows, K]."""
+    rows, half = codes.shape
+    K = 2 * half
+    vals = _E2M1_PAIRS[codes].reshape(rows, K)
+    vals.reshape(rows, K // block, block)[...] *= block_scale[:, :, None]
+    return vals
+
+
 def mxfp4_to_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """Decode one MXFP4 matrix.
 
@@ -71,12 +93,7 @@ def mxfp4_to_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     K = 2 * half
     if scales.shape != (rows, K // 32) or K % 32:
         raise ValueError("scale array does not match the code array")
-    nib = np.empty((rows, K), dtype=np.uint8)
-    nib[:, 0::2] = codes & 0x0F
-    nib[:, 1::2] = codes >> 4
-    vals = e2m1_to_f64(nib)
-    sc = np.repeat(e8m0_to_f64(scales), 32, axis=1)
-    return vals * sc
+    return _fp4_block_decode(codes, e8m0_to_f64(scales), 32)
 
 
 def nvfp4_to_f64(codes: np.ndarray, scales: np.ndarray, tensor_scale) -> np.ndarray:
@@ -93,12 +110,7 @@ def nvfp4_to_f64(codes: np.ndarray, scales: np.ndarray, tensor_scale) -> np.ndar
     K = 2 * half
     if scales.shape != (rows, K // 16) or K % 16:
         raise ValueError("scale array does not match the code array")
-    nib = np.empty((rows, K), dtype=np.uint8)
-    nib[:, 0::2] = codes & 0x0F
-    nib[:, 1::2] = codes >> 4
-    vals = e2m1_to_f64(nib)
-    sc = np.repeat(e4m3_to_f64(scales), 16, axis=1)
-    return vals * sc * float(np.float32(tensor_scale))
+    return _fp4_block_decode(codes, e4m3_to_f64(scales), 16) * float(np.float32(tensor_scale))
 
 
 def expert_to_f64(fmt: str, arrays: dict) -> tuple[np.ndarray, np.ndarray, np.ndarray]:

@@ -51,7 +51,13 @@ model page, "Cómo gestiona FreeToken el prellenado y la decodificación"), in
 the same cache that serves decode (FreeToken linux page, same section).
 Reading taken here: a prefetch of layer l updates the LRU exactly like a step
 of layer l whose needed set is all of its experts, but it is not a routed
-access: it adds fills and evictions, not accesses, hits or misses.
+access: it adds fills and evictions, not accesses, hits or misses.  "When the
+cache has room" is read as: the prefetch never takes the slot of an entry the
+most recent routed step needed (that step's expert computation may still be
+reading it: the intended order is step(l), prefetch(l+1), compute(l)); when no
+other slot is left, the remaining experts of the layer (the higher ids) are
+not prefetched -- no slot, no eviction, no recency -- and are served as
+ordinary misses by their own step.
 """
 from __future__ import annotations
 
@@ -95,6 +101,7 @@ class ExpertLRU:
         self.evictions = 0
         self.prefetch_fills = 0
         self.cpu_misses = 0
+        self.protected: set[tuple] = set()   # keys the most recent routed step needed (resident)
 
     def lookup(self, layer: int, expert: int) -> int:
         """Slot holding (layer, expert), or -1."""
@@ -107,15 +114,17 @@ class ExpertLRU:
         filled; the others run on the CPU (events with slot -1)."""
         needed = self._needed(layer, ids)
         events = self._serve(layer, needed, fill_limit)
+        self.protected = {(layer, ev.expert) for ev in events if ev.slot >= 0}
         self.accesses += len(needed)
         self.hits += sum(1 for ev in events if ev.hit)
         self.misses += sum(1 for ev in events if not ev.hit)
         return events
 
     def prefetch(self, layer: int) -> list[Event]:
-        """Bring every expert of ``layer`` in (full-layer prefetch); events ascending."""
-        events = self._serve(layer, self._needed(layer, range(self.n_experts)))
-        self.prefetch_fills += sum(1 for ev in events if not ev.hit)
+        """Bring the experts of ``layer`` in (full-layer prefetch), as many as fit without taking a
+        slot of the most recent step's needed entries; events ascending, slot -1 = not prefetched."""
+        events = self._serve(layer, self._needed(layer, range(self.n_experts)), protect=self.protected)
+        self.prefetch_fills += sum(1 for ev in events if not ev.hit and ev.slot >= 0)
         return events
 
     def _needed(self, layer: int, ids) -> list[int]:
@@ -129,7 +138,8 @@ class ExpertLRU:
             raise CapacityError(f"{len(needed)} distinct experts > {self.capacity} slots")
         return needed
 
-    def _serve(self, layer: int, needed: list[int], fill_limit: int | None = None) -> list[Event]:
+    def _serve(self, layer: int, needed: list[int], fill_limit: int | None = None,
+               protect: set | None = None) -> list[Event]:
         events: dict[int, Event] = {}
         # Phase 1: every hit becomes most recently used, ascending expert id.
         for e in needed:
@@ -139,8 +149,10 @@ class ExpertLRU:
                 self.stamp[s] = self.clock
                 events[e] = Event(e, True, s, None)
         # Phase 2: each miss takes the least recently used slot that holds no
-        # member of the needed set, ascending expert id.
+        # member of the needed set (nor, for a prefetch, a protected entry),
+        # ascending expert id.
         needed_keys = {(layer, e) for e in needed}
+        protect = protect or set()
         filled = 0
         for e in needed:
             if e in events:
@@ -149,13 +161,16 @@ class ExpertLRU:
                 events[e] = Event(e, False, -1, None)   # runs on the CPU
                 self.cpu_misses += 1
                 continue
-            filled += 1
             best = None
             for s in range(self.capacity):
-                if self.owner[s] in needed_keys:
+                if self.owner[s] in needed_keys or self.owner[s] in protect:
                     continue
                 if best is None or (self.stamp[s], s) < (self.stamp[best], best):
                     best = s
+            if best is None:                          # prefetch only: no room left
+                events[e] = Event(e, False, -1, None)
+                continue
+            filled += 1
             evicted = self.owner[best]
             if evicted is not None:
                 del self.where[evicted]

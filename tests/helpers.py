@@ -21,7 +21,10 @@ def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
 
 def check_close(got, ref, bf16_out=False, what="", allow=None):
     """Assert rel-L2 <= 5e-3 and max |got-ref| <= 2e-2 rms(ref) (+ half ulp for bf16 outputs,
-    + ``allow``, an element-wise bound on deviations the reference cannot pin down)."""
+    + ``allow``, an element-wise bound on deviations the reference cannot pin down).
+
+    Prints one line per comparison with the literal max |got-ref| beside the relative bound, so a
+    run with ``-s`` (or ``-rP``) lists both readings of the max-abs tolerance."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -32,9 +35,43 @@ def check_close(got, ref, bf16_out=False, what="", allow=None):
     rms = nref / np.sqrt(max(ref.size, 1))
     bound = MAX_ABS_RMS * rms + (bf16_half_ulp(ref) if bf16_out else 0.0) + (0.0 if allow is None else allow)
     worst = np.max(np.abs(diff) - bound) if ref.size else -1
+    max_abs = float(np.max(np.abs(diff))) if ref.size else 0.0
+    print(f"PARITY {what}: n={ref.size} rel-L2 {rel:.3e} (<= {REL_L2}) max-abs {max_abs:.3e} "
+          f"(literal 2e-2: {'ok' if max_abs <= 2e-2 else 'over'}; bound 2e-2*rms = {MAX_ABS_RMS * rms:.3e}) "
+          f"rms(ref) {rms:.3e}", flush=True)
     assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e} > {REL_L2}"
-    assert worst <= 0, f"{what}: max-abs exceeds bound by {worst:.3e} (rms {rms:.3e}, max abs {np.max(np.abs(diff)):.3e})"
-    return rel, float(np.max(np.abs(diff))) if ref.size else 0.0
+    assert worst <= 0, f"{what}: max-abs exceeds bound by {worst:.3e} (rms {rms:.3e}, max abs {max_abs:.3e})"
+    return rel, max_abs
+
+
+# Top-k margin below which the router's own fp32 logits may order two experts
+# differently from the float64 oracle (the routing exactness rule).
+TOPK_MARGIN = 1e-4
+
+
+def check_topk_valid(got_ids, logits_ref, k, tol=TOPK_MARGIN, what=""):
+    """Where several top-k results are correct (near-tied logits), check what is unique and that
+    the rest is valid: per token k distinct experts in range, every picked expert's oracle logit
+    within ``tol`` of the oracle's k-th largest or above it, and every expert left out within
+    ``tol`` of it or below.  Returns the tokens whose ids differ from the oracle's own top-k."""
+    got_ids = np.asarray(got_ids)
+    l = np.asarray(logits_ref, np.float64)
+    T, E = l.shape
+    assert got_ids.shape == (T, k), (what, got_ids.shape)
+    assert np.all((got_ids >= 0) & (got_ids < E)), f"{what}: id out of range"
+    kth = -np.sort(-l, axis=1)[:, k - 1]
+    differ = []
+    for t in range(T):
+        ids = got_ids[t].astype(np.int64)
+        assert len(set(ids.tolist())) == k, f"{what}: token {t} picks an expert twice"
+        assert np.all(l[t, ids] >= kth[t] - tol), f"{what}: token {t} picks an expert below the k-th logit"
+        out = np.setdiff1d(np.arange(E), ids)
+        assert np.all(l[t, out] <= kth[t] + tol), f"{what}: token {t} leaves out an expert above the k-th logit"
+    ref_ids = moe.topk(l.astype(np.float32), k)
+    for t in range(T):
+        if not np.array_equal(got_ids[t], ref_ids[t]):
+            differ.append(t)
+    return np.array(differ, dtype=np.int64)
 
 
 # Native MXFP4 mode: the GPU forms the SwiGLU hidden vector in fp32 (relative
@@ -97,6 +134,12 @@ class Experts:
         if e not in self._f64:
             self._f64[e] = formats.expert_to_f64(self.cfg.wdtype, self.raw(e).arrays)
         return self._f64[e]
+
+    def fresh(self, e: int):
+        """Expert e's float64 weights decoded now and not kept (for sweeps over many experts)."""
+        if e in self._f64:
+            return self._f64[e]
+        return formats.expert_to_f64(self.cfg.wdtype, synth.expert_weights(self.cfg, self.layer, e).arrays)
 
     def drop(self):
         self._f64.clear()

@@ -76,7 +76,7 @@ def _traces(golden_dir):
 
 def test_hand_traced_sequences(golden_dir):
     traces = _traces(golden_dir)
-    assert [t["name"] for t in traces] == ["A", "B", "C", "D", "E", "F", "G"]
+    assert [t["name"] for t in traces] == ["A", "B", "C", "D", "E", "F", "G", "H"]
     for tr in traces:
         lru = ExpertLRU(tr["L"], tr["E"], tr["C"])
         for i, (step, layer, ids, want) in enumerate(tr["steps"]):
@@ -270,3 +270,29 @@ def test_miss_split_policy():
     # m=7, Bp=Bh: q=3 -> max(3, 4)=4, q=4 -> max(4, 3)=4: tie -> more fills
     assert policy.miss_split(7, 1.0, 1.0) == 4
     assert policy.split_misses([9, 2, 5], 1.0, 1.0) == ([2, 5], [9])
+
+
+def test_prefetch_never_takes_the_last_steps_slots():
+    # capacity between E and 2E: a prefetch evicts no entry the last routed step needed, fills
+    # exactly min(missing, free-of-protection slots) experts (the lowest missing ids), and an
+    # expert it leaves out is simply a miss of its own step later
+    rng = np.random.default_rng(17)
+    for trial in range(60):
+        L, E = 3, int(rng.integers(3, 9))
+        C = int(rng.integers(E, 2 * E))
+        lru = ExpertLRU(L, E, C)
+        for st in range(12):
+            l = st % L
+            ids = rng.integers(0, E, size=int(rng.integers(1, min(E, C) + 1)))
+            lru.step(l, ids)
+            needed = {(l, int(e)) for e in ids}
+            slots_needed = {lru.where[k] for k in needed}
+            missing = [e for e in range(E) if ((l + 1) % L, e) not in lru.where]
+            room = sum(1 for s in range(C)
+                       if lru.owner[s] not in needed and (lru.owner[s] is None or lru.owner[s][0] != (l + 1) % L))
+            evs = lru.prefetch((l + 1) % L)
+            filled = [ev.expert for ev in evs if not ev.hit and ev.slot >= 0]
+            skipped = [ev.expert for ev in evs if not ev.hit and ev.slot < 0]
+            assert filled == missing[:min(len(missing), room)] and skipped == missing[len(filled):]
+            assert all(ev.slot not in slots_needed for ev in evs if not ev.hit and ev.slot >= 0)
+            assert all(lru.where.get(k) is not None for k in needed)      # still resident
