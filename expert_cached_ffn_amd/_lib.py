@@ -5,7 +5,8 @@ import ctypes as C
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libftmoe.so")
+# FTMOE_LIB: another build of the same library (e.g. the sanitizer build of build.py)
+LIB_PATH = os.environ.get("FTMOE_LIB") or os.path.join(PKG, "libftmoe.so")
 
 # status codes
 FT_OK, FT_EINVAL, FT_ENOTSUP, FT_ECAPACITY, FT_EHIP = 0, -1, -2, -3, -4
@@ -27,7 +28,7 @@ EXPORTS = [
     "ft_expert_cache_resize", "ft_expert_cache_prefetch_layer", "ft_expert_cache_set_split",
     "ft_expert_cache_cpu_misses", "ft_cpu_expert_ffn", "ft_cpu_miss_rows", "ft_cpu_isa",
     "ft_expert_cache_stage_cpu_misses", "ft_expert_cache_run_cpu_misses", "ft_expert_cache_step_split",
-    "ft_expert_cache_wait_fills", "ft_expert_cache_plan", "ft_expert_cache_fill",
+    "ft_expert_cache_wait_fills", "ft_expert_cache_plan", "ft_expert_cache_fill", "ft_expert_cache_set_trace",
 ]
 
 
@@ -44,7 +45,7 @@ class ExpertLayout(C.Structure):
 class CacheStats(C.Structure):
     _fields_ = [(n, C.c_uint64) for n in
                 ("accesses", "hits", "misses", "evictions", "bytes_h2d", "steps", "prefetch_fills",
-                 "cpu_misses", "cpu_ns")]
+                 "cpu_misses", "cpu_ns", "trace_dropped")]
 
 
 class CacheEvent(C.Structure):
@@ -78,7 +79,7 @@ def lib() -> C.CDLL:
     L.ft_moe_permute.restype = i32
     L.ft_moe_permute.argtypes = [p, i32, i32, i32, p, p, p, p, sz, p]
     L.ft_moe_grouped_ffn.restype = i32
-    L.ft_moe_grouped_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, p, p, i32, i32, i32, i32, p, p, p, p,
+    L.ft_moe_grouped_ffn.argtypes = [C.POINTER(ExpertLayout), p, i32, p, p, p, i32, i32, i32, i32, p, p, p, p,
                                      i32, p, sz, p]
     L.ft_cpu_expert_ffn.restype = i32
     L.ft_cpu_expert_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, i32, p, i32]
@@ -99,7 +100,9 @@ def lib() -> C.CDLL:
     L.ft_cpu_isa.argtypes = [i32, p]
     L.ft_cpu_miss_rows.argtypes = [C.POINTER(ExpertLayout), p, i32, i32, p, i32, p, p, i32, i32, p, p, i32]
     L.ft_expert_cache_set_split.restype = i32
-    L.ft_expert_cache_set_split.argtypes = [p, C.c_double, C.c_double]
+    L.ft_expert_cache_set_split.argtypes = [p, C.c_double, C.c_double, i32, i32]
+    L.ft_expert_cache_set_trace.restype = i32
+    L.ft_expert_cache_set_trace.argtypes = [p, C.c_int64]
     L.ft_expert_cache_cpu_misses.restype = i32
     L.ft_expert_cache_cpu_misses.argtypes = [p, p, i32, p]
     L.ft_expert_cache_prefetch_layer.restype = i32

@@ -44,7 +44,26 @@ struct LruState {
   int32_t *owner;    // [C]   slot -> key or -1
   uint64_t *stamp;   // [C]   last use (0 = never)
   uint64_t *clock;   // [1]
+  int32_t *protect;  // [E]   keys the last routed step left resident (hits and fills), ascending
+  int32_t *n_protect;  // [1]
 };
+
+// Device state layout (one allocation): stamps [C] u64, clock (64 B), map
+// [L*E] i32, owner [C] i32, protect [E] i32, n_protect (64 B).
+inline size_t lru_state_bytes(size_t keys, int C, int E) {
+  return size_t(C) * 8 + 64 + keys * 4 + size_t(C) * 4 + size_t(E) * 4 + 64;
+}
+inline LruState lru_state_at(void *base, size_t keys, int C, int E) {
+  uint8_t *p = static_cast<uint8_t *>(base);
+  LruState st;
+  st.stamp = reinterpret_cast<uint64_t *>(p);
+  st.clock = reinterpret_cast<uint64_t *>(p + size_t(C) * 8);
+  st.map = reinterpret_cast<int32_t *>(p + size_t(C) * 8 + 64);
+  st.owner = st.map + keys;
+  st.protect = st.owner + C;
+  st.n_protect = st.protect + E;
+  return st;
+}
 
 __device__ __forceinline__ bool older(uint64_t sa, int a, uint64_t sb, int b) {
   return sa < sb || (sa == sb && a < b);
@@ -53,6 +72,14 @@ __device__ __forceinline__ bool older(uint64_t sa, int a, uint64_t sb, int b) {
 // One workgroup.  Stamps and the slot table are read before any of them is
 // written (selection works on the pre-step stamps plus an LDS "taken" bitmap),
 // so the kernel never reads its own global writes.
+//
+// prefetch != 0: a full-layer prefetch (ids = every expert of the layer).  The
+// entries the last routed step left resident are taken out of the victim
+// choice -- that step's expert FFN may still be reading them (the pages stream
+// the next layer in only when the cache has room: FreeToken quantization page,
+// "Cómo se desplazan los pesos MoE cuantizados por la memoria") -- and a miss
+// that finds no other slot, and every later one, is not prefetched (code 5).
+// A routed step records its resident needed keys as the new protected set.
 // Number of a step's m misses to fill when the others can run on the host
 // CPU: the q in 0..m minimising max(q / b_pcie, (m - q) / b_host), ties to the
 // larger q (the miss-split reading of the pages' formula, FreeToken 290b model
@@ -73,7 +100,8 @@ __device__ inline int miss_split(int m, double b_pcie, double b_host) {
 }
 
 __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int layer, const int32_t *__restrict__ ids,
-                                                              int R, int E, int C, double b_pcie, double b_host,
+                                                              int R, int E, int C, int prefetch, double b_pcie,
+                                                              double b_host,
                                                               int32_t *__restrict__ slot_of_expert,
                                                               int32_t *__restrict__ slot_hits,
                                                               LruResult *__restrict__ res) {
@@ -87,7 +115,7 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
   __shared__ int s_wcnt[kLruThreads / 64 + 1];
   __shared__ uint64_t s_wst[kLruThreads / 64];
   __shared__ int s_wsl[kLruThreads / 64];
-  __shared__ int s_bad, s_n, s_h, s_q;
+  __shared__ int s_bad, s_n, s_h, s_q, s_full;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NW = kLruThreads / 64;
@@ -155,7 +183,17 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
     __syncthreads();
   }
   const int h = hbase;
-  if (tid == 0) s_q = miss_split(n - h, b_pcie, b_host);
+  if (prefetch) {  // the last routed step's entries are not victims
+    const int np = *st.n_protect;
+    for (int i = tid; i < np; i += kLruThreads) {
+      const int s = st.map[st.protect[i]];
+      if (s >= 0) atomicOr(&s_taken[s >> 5], 1u << (s & 31));
+    }
+  }
+  if (tid == 0) {
+    s_q = miss_split(n - h, b_pcie, b_host);
+    s_full = 0;
+  }
   __syncthreads();
   const int q = s_q;
   // Phase 2: misses in ascending expert order, each of the first q taking the
@@ -163,7 +201,7 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
   int mi = 0;
   for (int i = 0; i < n; ++i) {
     if (s_hit[i]) continue;  // uniform across the workgroup
-    if (mi >= q) {  // runs on the CPU: slot and evicted key stay -1 (set in phase 1)
+    if (mi >= q || s_full) {  // runs on the CPU / no room for a prefetch: slot and evicted key stay -1
       ++mi;
       continue;
     }
@@ -199,9 +237,13 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
           b = s_wst[w];
           v = s_wsl[w];
         }
-      s_slot[i] = v;
-      s_taken[v >> 5] |= 1u << (v & 31);
-      s_evk[i] = st.owner[v];
+      if (v >= C) {  // every slot is needed or protected (a prefetch only)
+        s_full = 1;
+      } else {
+        s_slot[i] = v;
+        s_taken[v >> 5] |= 1u << (v & 31);
+        s_evk[i] = st.owner[v];
+      }
     }
     __syncthreads();
     ++mi;
@@ -210,19 +252,21 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
   __syncthreads();
   int n_evict = 0;
   if (tid == 0) {
-    int j = 0, n_cpu = 0, rank = 0;
+    int j = 0, n_cpu = 0, rank = 0, np = 0;
     for (int i = 0; i < n; ++i) {
       const int e = s_list[i];
       const int s = s_slot[i];
       const bool hit = s_hit[i] != 0;
       const bool cpu = !hit && rank++ >= q;  // misses beyond the first q run on the CPU
+      const bool noroom = !hit && !cpu && s < 0;  // a prefetch that found no slot
       res->ev[i][0] = e;
-      res->ev[i][1] = hit ? 1 : (cpu ? 4 : 0);
+      res->ev[i][1] = hit ? 1 : (cpu ? 4 : (noroom ? 5 : 0));
       res->ev[i][2] = s;
       res->ev[i][3] = s_evk[i];
       if (cpu) ++n_cpu;
-      s_need[e] = hit ? 1 : (cpu ? 3 : 2);
-      if (!hit && !cpu) {
+      s_need[e] = hit ? 1 : (cpu || noroom ? 3 : 2);
+      if (!prefetch && !cpu) st.protect[np++] = layer * E + e;
+      if (!hit && !cpu && !noroom) {
         st.stamp[s] = clk + uint64_t(h + j) + 1;
         ++j;
         const int ek = s_evk[i];
@@ -237,6 +281,7 @@ __global__ __launch_bounds__(kLruThreads) void lru_step_kernel(LruState st, int 
       }
     }
     *st.clock = clk + uint64_t(h + j);
+    if (!prefetch) *st.n_protect = np;
     res->n_needed = n;
     res->n_hits = h;
     res->n_misses = mi;
@@ -351,9 +396,24 @@ struct ft_expert_cache {
   hipEvent_t ev_lru, ev_copy;
   int device;
   ft_cache_stats stats;
+  // event log: a ring of trace_cap records (0 = off), allocated by ft_expert_cache_set_trace
   std::vector<ft_cache_event> log;
+  size_t trace_cap = 0, log_head = 0, log_count = 0;
   std::vector<int32_t> map_mirror;
+  // CPU-miss buffers sized by ft_expert_cache_set_split for steps of up to cpu_T tokens x cpu_k picks
+  int32_t cpu_T = 0, cpu_k = 0;
 };
+
+static void log_event(ft_expert_cache *c, const ft_cache_event &ev) {
+  if (c->trace_cap == 0) return;
+  c->log[(c->log_head + c->log_count) % c->trace_cap] = ev;
+  if (c->log_count < c->trace_cap) {
+    ++c->log_count;
+  } else {
+    c->log_head = (c->log_head + 1) % c->trace_cap;
+    ++c->stats.trace_dropped;
+  }
+}
 
 extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n_layers, int32_t E,
                                             int32_t capacity, void *slot_pool, const void *host_bank,
@@ -389,7 +449,7 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
   c->copy_stream = copy_stream;
   c->device = dev;
   const size_t keys = size_t(n_layers) * E;
-  const size_t bytes = keys * 4 + size_t(capacity) * 4 + size_t(capacity) * 8 + 64;
+  const size_t bytes = lru_state_bytes(keys, capacity, E);
   auto cleanup = [&](ft_status st, const std::string &msg) {
     for (int i = 0; i < kFillStreams; ++i) {
       if (i > 0 && c->fill[i]) (void)hipStreamDestroy(c->fill[i]);
@@ -404,14 +464,11 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
     return fail(st, msg);
   };
   if (hipMalloc(&c->dev_state, bytes) != hipSuccess) return cleanup(FT_EHIP, "ft_expert_cache_create: hipMalloc failed");
-  uint8_t *p = static_cast<uint8_t *>(c->dev_state);
-  c->st.stamp = reinterpret_cast<uint64_t *>(p);
-  c->st.clock = reinterpret_cast<uint64_t *>(p + size_t(capacity) * 8);
-  c->st.map = reinterpret_cast<int32_t *>(p + size_t(capacity) * 8 + 64);
-  c->st.owner = c->st.map + keys;
-  // Empty cache: every key unmapped, every slot free with stamp 0, clock 0.
+  c->st = lru_state_at(c->dev_state, keys, capacity, E);
+  // Empty cache: every key unmapped, every slot free with stamp 0, clock 0, nothing protected.
   if (hipMemset(c->st.map, 0xff, (keys + capacity) * 4) != hipSuccess ||
-      hipMemset(c->dev_state, 0, size_t(capacity) * 8 + 64) != hipSuccess)
+      hipMemset(c->dev_state, 0, size_t(capacity) * 8 + 64) != hipSuccess ||
+      hipMemset(c->st.protect, 0, size_t(E) * 4 + 64) != hipSuccess)
     return cleanup(FT_EHIP, "ft_expert_cache_create: hipMemset failed");
   if (hipHostMalloc(reinterpret_cast<void **>(&c->res_host), sizeof(LruResult), hipHostMallocMapped) != hipSuccess)
     return cleanup(FT_EHIP, "ft_expert_cache_create: hipHostMalloc failed");
@@ -439,6 +496,7 @@ extern "C" ft_status ft_expert_cache_create(const ft_expert_layout *L, int32_t n
   }
   c->stats = ft_cache_stats{};
   c->map_mirror.assign(keys, -1);
+  c->cpu_list.reserve(size_t(E));  // a step's CPU misses are at most E: the list never grows past this
   *out = c;
   clear_error();
   return FT_OK;
@@ -464,8 +522,8 @@ static ft_status cache_launch(ft_expert_cache *c, int32_t layer, const int32_t *
       if (c->pending[q]) FT_HIP(hipStreamWaitEvent(compute_stream, c->ev_fill[q], 0));
   c->res_host->status = -1;
   hipLaunchKernelGGL(lru_step_kernel, dim3(1), dim3(kLruThreads), 0, compute_stream, c->st, layer, ids, R, c->E,
-                     c->C, prefetch ? 0.0 : c->b_pcie, prefetch ? 0.0 : c->b_host, slot_of_expert, slot_hits,
-                     c->res_dev);
+                     c->C, prefetch ? 1 : 0, prefetch ? 0.0 : c->b_pcie, prefetch ? 0.0 : c->b_host, slot_of_expert,
+                     slot_hits, c->res_dev);
   FT_LAUNCHED("lru_step_kernel");
   FT_HIP(hipEventRecord(c->ev_lru, compute_stream));
   return FT_OK;
@@ -504,12 +562,12 @@ static ft_status cache_collect(ft_expert_cache *c, int32_t layer, int32_t *slot_
   for (int i = 0; i < r.n_needed; ++i) {
     const int e = r.ev[i][0], code = r.ev[i][1], s = r.ev[i][2], ek = r.ev[i][3];
     const bool hit = code == 1;
-    c->log.push_back(ft_cache_event{step, layer, e, prefetch ? (hit ? 3 : 2) : code, s, ek});
+    log_event(c, ft_cache_event{step, layer, e, prefetch ? (hit ? 3 : (code == 5 ? 5 : 2)) : code, s, ek});
     if (code == 4) {
-      c->cpu_list.push_back(e);
+      c->cpu_list.push_back(e);  // capacity E reserved at create: no allocation
       continue;
     }
-    if (hit) continue;
+    if (hit || code == 5) continue;
     if (ek >= 0) c->map_mirror[size_t(ek)] = -1;
     c->map_mirror[size_t(layer) * c->E + e] = s;
     const uint8_t *src = c->bank + (uint64_t(layer) * c->E + e) * eb;
@@ -642,13 +700,50 @@ extern "C" ft_status ft_expert_cache_prefetch_layer(ft_expert_cache *c, int32_t 
                      "ft_expert_cache_prefetch_layer");
 }
 
-extern "C" ft_status ft_expert_cache_set_split(ft_expert_cache *c, double b_pcie, double b_host) {
+extern "C" ft_status ft_expert_cache_set_split(ft_expert_cache *c, double b_pcie, double b_host, int32_t T_max,
+                                               int32_t k) {
   FT_REQUIRE(c != nullptr, "ft_expert_cache_set_split: cache is NULL");
   FT_REQUIRE(b_pcie >= 0.0 && b_host >= 0.0 && b_pcie == b_pcie && b_host == b_host,
              "ft_expert_cache_set_split: bandwidths must be non-negative numbers");
   FT_REQUIRE(b_host == 0.0 || b_pcie > 0.0 || b_host > 0.0, "ft_expert_cache_set_split: both bandwidths are zero");
+  FT_REQUIRE(!c->planned, "ft_expert_cache_set_split: a planned step is waiting for ft_expert_cache_fill");
+  if (b_host > 0.0) {
+    FT_REQUIRE(T_max >= 1 && k >= 1 && int64_t(T_max) * k <= (int64_t(1) << 28),
+               "ft_expert_cache_set_split: need 1 <= T_max, 1 <= k, T_max*k <= 2^28");
+    // the host-mapped buffers of the CPU misses, sized once here (the per-step calls never allocate)
+    if (c->stage_pending) FT_HIP(hipEventSynchronize(c->ev_stage));
+    if (c->patch_pending) FT_HIP(hipEventSynchronize(c->ev_patch));
+    c->stage_pending = c->patch_pending = false;
+    const int H = c->L.H;
+    const size_t R = size_t(T_max) * k;
+    const size_t ob = (size_t(c->E + 1) * 4 + 255) & ~size_t(255);
+    if (c->stage.reserve(size_t(T_max) * H * 2 + ob + R * 4) != FT_OK || c->ybuf.reserve(R * H * 4) != FT_OK ||
+        c->list.reserve(R * 4) != FT_OK)
+      return fail(FT_EHIP, "ft_expert_cache_set_split: hipHostMalloc failed");
+    if (c->ev_stage == nullptr) FT_HIP(hipEventCreateWithFlags(&c->ev_stage, hipEventDisableTiming));
+    if (c->ev_patch == nullptr) FT_HIP(hipEventCreateWithFlags(&c->ev_patch, hipEventDisableTiming));
+    c->cpu_T = T_max;
+    c->cpu_k = k;
+  }
   c->b_pcie = b_pcie;
   c->b_host = b_host;
+  clear_error();
+  return FT_OK;
+}
+
+extern "C" ft_status ft_expert_cache_set_trace(ft_expert_cache *c, int64_t max_events) {
+  FT_REQUIRE(c != nullptr, "ft_expert_cache_set_trace: cache is NULL");
+  FT_REQUIRE(max_events >= 0 && max_events <= (int64_t(1) << 28),
+             "ft_expert_cache_set_trace: max_events must be in 0..2^28");
+  std::vector<ft_cache_event> ring;
+  try {
+    ring.resize(size_t(max_events));
+  } catch (const std::bad_alloc &) {
+    return fail(FT_EINVAL, "ft_expert_cache_set_trace: cannot allocate the event ring");
+  }
+  c->log.swap(ring);
+  c->trace_cap = size_t(max_events);
+  c->log_head = c->log_count = 0;
   clear_error();
   return FT_OK;
 }
@@ -678,15 +773,14 @@ extern "C" ft_status ft_expert_cache_stage_cpu_misses(ft_expert_cache *c, const 
   FT_REQUIRE(x != nullptr && expert_offsets != nullptr && sorted_rows != nullptr,
              "ft_expert_cache_stage_cpu_misses: NULL pointer argument");
   FT_REQUIRE(aligned(x, 16), "ft_expert_cache_stage_cpu_misses: x must be 16-byte aligned");
+  if (T > c->cpu_T || int64_t(T) * k > int64_t(c->cpu_T) * c->cpu_k)
+    return fail(FT_ECAPACITY, "ft_expert_cache_stage_cpu_misses: step larger than the T_max x k given to "
+                              "ft_expert_cache_set_split");
   const int H = c->L.H, E = c->E, R = T * k;
   const size_t xb = size_t(T) * H * 2;                      // a multiple of 256 (H % 32 == 0)
   const size_t ob = (size_t(E + 1) * 4 + 255) & ~size_t(255);
-  const size_t need = xb + ob + size_t(R) * 4;
-  if (need > c->stage.bytes) {
-    if (c->stage_pending) FT_HIP(hipEventSynchronize(c->ev_stage));
-    if (c->stage.reserve(need) != FT_OK) return fail(FT_EHIP, "ft_expert_cache_stage_cpu_misses: hipHostMalloc failed");
-  }
-  if (c->ev_stage == nullptr) FT_HIP(hipEventCreateWithFlags(&c->ev_stage, hipEventDisableTiming));
+  // the previous stage's kernel must have written its inputs out before they are replaced
+  if (c->stage_pending) FT_HIP(hipEventSynchronize(c->ev_stage));
   const int nx = int(xb / 16), total = nx + (E + 1) + R;
   const int grid = std::min(1024, (total + 255) / 256);
   uint8_t *d = static_cast<uint8_t *>(c->stage.dev);
@@ -723,9 +817,7 @@ extern "C" ft_status ft_expert_cache_run_cpu_misses(ft_expert_cache *c, float *y
   c->stage_pending = false;
   if (c->patch_pending) FT_HIP(hipEventSynchronize(c->ev_patch));  // the last patch has read ybuf / list
   c->patch_pending = false;
-  if (c->ybuf.reserve(size_t(R) * H * 4) != FT_OK || c->list.reserve(size_t(R) * 4) != FT_OK)
-    return fail(FT_EHIP, "ft_expert_cache_run_cpu_misses: hipHostMalloc failed");
-  if (c->ev_patch == nullptr) FT_HIP(hipEventCreateWithFlags(&c->ev_patch, hipEventDisableTiming));
+  // ybuf and list hold T*k rows: sized by ft_expert_cache_set_split, checked by the stage call
   const uint8_t *h = static_cast<const uint8_t *>(c->stage.host);
   const int32_t *hoff = reinterpret_cast<const int32_t *>(h + c->stage_x_bytes);
   const int32_t *hrows = reinterpret_cast<const int32_t *>(h + c->stage_x_bytes + c->stage_off_bytes);
@@ -778,10 +870,12 @@ extern "C" ft_status ft_expert_cache_resize(ft_expert_cache *c, int32_t new_capa
   const size_t keys = size_t(c->n_layers) * c->E;
   std::vector<uint64_t> stamp(C);
   std::vector<int32_t> owner(C);
+  std::vector<int32_t> protect(size_t(c->E) + 16);  // the protected keys and their count (keys stay valid)
   uint64_t clock = 0;
   FT_HIP(hipMemcpy(stamp.data(), c->st.stamp, size_t(C) * 8, hipMemcpyDeviceToHost));
   FT_HIP(hipMemcpy(owner.data(), c->st.owner, size_t(C) * 4, hipMemcpyDeviceToHost));
   FT_HIP(hipMemcpy(&clock, c->st.clock, 8, hipMemcpyDeviceToHost));
+  FT_HIP(hipMemcpy(protect.data(), c->st.protect, (size_t(c->E) + 16) * 4, hipMemcpyDeviceToHost));
   // keep the C2 largest stamps among occupied slots (stamps of occupied slots are distinct)
   std::vector<int> used;
   for (int s = 0; s < C; ++s)
@@ -812,18 +906,13 @@ extern "C" ft_status ft_expert_cache_resize(ft_expert_cache *c, int32_t new_capa
   }
   // new device state for the new capacity (same layout as at creation)
   void *state2 = nullptr;
-  const size_t bytes = keys * 4 + size_t(C2) * 4 + size_t(C2) * 8 + 64;
-  FT_HIP(hipMalloc(&state2, bytes));
-  uint8_t *p = static_cast<uint8_t *>(state2);
-  LruState st2;
-  st2.stamp = reinterpret_cast<uint64_t *>(p);
-  st2.clock = reinterpret_cast<uint64_t *>(p + size_t(C2) * 8);
-  st2.map = reinterpret_cast<int32_t *>(p + size_t(C2) * 8 + 64);
-  st2.owner = st2.map + keys;
+  FT_HIP(hipMalloc(&state2, lru_state_bytes(keys, C2, c->E)));
+  const LruState st2 = lru_state_at(state2, keys, C2, c->E);
   hipError_t e = hipMemcpy(st2.stamp, stamp2.data(), size_t(C2) * 8, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(st2.clock, &clock, 8, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(st2.map, map2.data(), keys * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(st2.owner, owner2.data(), size_t(C2) * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(st2.protect, protect.data(), (size_t(c->E) + 16) * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     (void)hipFree(state2);
@@ -849,11 +938,12 @@ extern "C" ft_status ft_expert_cache_stats(const ft_expert_cache *c, ft_cache_st
 
 extern "C" ft_status ft_expert_cache_trace(const ft_expert_cache *c, void *host_buf, size_t bytes, size_t *needed) {
   FT_REQUIRE(c != nullptr, "ft_expert_cache_trace: cache is NULL");
-  const size_t all = c->log.size() * sizeof(ft_cache_event);
+  const size_t all = c->log_count * sizeof(ft_cache_event);
   if (needed) *needed = all;
   if (host_buf != nullptr && bytes > 0) {
-    const size_t n = std::min(c->log.size(), bytes / sizeof(ft_cache_event));
-    std::copy(c->log.begin(), c->log.begin() + n, static_cast<ft_cache_event *>(host_buf));
+    const size_t n = std::min(c->log_count, bytes / sizeof(ft_cache_event));
+    ft_cache_event *out = static_cast<ft_cache_event *>(host_buf);
+    for (size_t i = 0; i < n; ++i) out[i] = c->log[(c->log_head + i) % c->trace_cap];
   }
   clear_error();
   return FT_OK;

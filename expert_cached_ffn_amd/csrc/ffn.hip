@@ -88,6 +88,7 @@ __device__ int find_active_expert(const int32_t *__restrict__ off, int E, int ai
 struct FfnArgs {
   const uint8_t *pool;
   const int32_t *slot_of_expert;
+  int32_t n_slots;
   uint64_t expert_bytes;
   const uint8_t *shared_blob;
   uint64_t off_w0, off_w1, off_s0, off_s1;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
     pos0 = a.T * a.k;
     m = a.T;
   } else {
-    const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    const int slot = table_slot(a.slot_of_expert, e, a.n_slots);
     pos0 = a.offsets[e];
     m = a.offsets[e + 1] - pos0;
     if (slot == FT_SLOT_SKIP) return;  // another call computes these rows
@@ -434,6 +435,7 @@ static ft_status launch_mx_gemm(MxGemmArgs a, hipStream_t stream, const char *na
 struct FfnF32Args {
   const uint8_t *pool;
   const int32_t *slot_of_expert;
+  int32_t n_slots;
   uint64_t expert_bytes;
   const uint8_t *shared_blob;
   uint64_t off_gate, off_up, off_down;
@@ -469,7 +471,7 @@ __device__ __forceinline__ const float *f32_blob(const FfnF32Args &a, int p, int
   }
   const int e = expert_of_row(a.offsets, a.E, p);
   *tok = a.sorted_rows[p] / a.k;
-  const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+  const int slot = table_slot(a.slot_of_expert, e, a.n_slots);
   if (slot < 0) {
     *ok = false;
     *skip = slot == FT_SLOT_SKIP;
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(256) void ffn_f32_stage2(FfnF32Args a) {
 
 using namespace ft;
 
-extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
+extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
                                         const int32_t *slot_of_expert, const void *shared_blob,
                                         const void *x, int32_t x_dtype, int32_t T, int32_t k,
                                         int32_t E, const int32_t *expert_offsets,
@@ -571,6 +573,8 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   }
   FT_REQUIRE(slot_pool && x && expert_offsets && sorted_rows && y_rows,
              "ft_moe_grouped_ffn: NULL pointer argument");
+  FT_REQUIRE(n_slots >= 1 && (slot_of_expert != nullptr || n_slots >= E),
+             "ft_moe_grouped_ffn: n_slots must be >= 1, and >= E when slot_of_expert is NULL");
   FT_REQUIRE((shared_blob == nullptr) == (y_shared == nullptr),
              "ft_moe_grouped_ffn: shared_blob and y_shared must both be given or both be NULL");
   FT_REQUIRE(aligned(slot_pool, 256) && (!shared_blob || aligned(shared_blob, 256)) &&
@@ -593,6 +597,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     GemmArgs g1{};
     g1.pool = static_cast<const uint8_t *>(slot_pool);
     g1.slot_of_expert = slot_of_expert;
+    g1.n_slots = n_slots;
     g1.expert_bytes = L->expert_bytes;
     g1.shared_blob = static_cast<const uint8_t *>(shared_blob);
     g1.offsets = expert_offsets;
@@ -639,6 +644,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     FfnF32Args a{};
     a.pool = static_cast<const uint8_t *>(slot_pool);
     a.slot_of_expert = slot_of_expert;
+    a.n_slots = n_slots;
     a.expert_bytes = L->expert_bytes;
     a.shared_blob = static_cast<const uint8_t *>(shared_blob);
     a.off_gate = L->off_gate;
@@ -673,6 +679,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   FfnArgs a{};
   a.pool = static_cast<const uint8_t *>(slot_pool);
   a.slot_of_expert = slot_of_expert;
+  a.n_slots = n_slots;
   a.expert_bytes = L->expert_bytes;
   a.shared_blob = static_cast<const uint8_t *>(shared_blob);
   a.offsets = expert_offsets;
@@ -718,6 +725,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     PersistArgs p1{};
     p1.pool = a.pool;
     p1.slot_of_expert = slot_of_expert;
+    p1.n_slots = n_slots;
     p1.expert_bytes = L->expert_bytes;
     p1.shared_blob = a.shared_blob;
     p1.offsets = expert_offsets;
@@ -759,8 +767,12 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     if (wd == FT_NVFP4) {
       FT_SUPPORTED((!run1 || persist_covers<WF_NV4>(p1.K)) && (!run2 || persist_covers<WF_NV4>(p2.K)),
                    "ft_moe_grouped_ffn: NVFP4 decode needs H/128 and I/128 in {4, 6, 8, 12, 16}");
-      if (run1) launch_persist<WF_NV4, true>(p1, a_max * p1.n_tiles * groups, stream);
-      if (run2) launch_persist<WF_NV4, false>(p2, a_max * p2.n_tiles * groups, stream);
+      // a tuning override naming a shape with no kernel instance launches nothing: refuse rather
+      // than leave the stage's outputs unwritten
+      if (run1 && !launch_persist<WF_NV4, true>(p1, a_max * p1.n_tiles * groups, stream))
+        return fail(FT_ENOTSUP, "ft_moe_grouped_ffn: no NVFP4 gate/up kernel for this persistent shape");
+      if (run2 && !launch_persist<WF_NV4, false>(p2, a_max * p2.n_tiles * groups, stream))
+        return fail(FT_ENOTSUP, "ft_moe_grouped_ffn: no NVFP4 down kernel for this persistent shape");
     } else if (wd == FT_BF16) {
       if (run1 && !launch_persist<WF_BF16, true>(p1, a_max * p1.n_tiles * groups, stream)) {
         const ft_status st = launch_stream<WF_BF16, true>(s1, a_max, T, stream, "ffn_stream_kernel<bf16, gate_up>");
@@ -789,6 +801,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     GemmArgs g1{};
     g1.pool = a.pool;
     g1.slot_of_expert = slot_of_expert;
+    g1.n_slots = n_slots;
     g1.expert_bytes = L->expert_bytes;
     g1.shared_blob = a.shared_blob;
     g1.offsets = expert_offsets;

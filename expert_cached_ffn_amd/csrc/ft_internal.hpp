@@ -144,6 +144,14 @@ __device__ __forceinline__ f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int 
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Slot of expert e in a slot table (NULL: slot e).  A value at or past the
+// pool's n_slots reads as -1, like any slot of an expert that is not
+// resident, so a bad table never addresses memory outside the pool.
+__device__ __forceinline__ int table_slot(const int32_t *slot_of_expert, int e, int n_slots) {
+  const int s = slot_of_expert ? slot_of_expert[e] : e;
+  return s >= n_slots ? -1 : s;
+}
+
 // Raw buffer loads (gfx9 descriptor: 32-bit data format word 0x00020000).  An
 // offset at or past `bytes` returns zero and touches no memory, which is how
 // padding rows and token columns are masked without branches.

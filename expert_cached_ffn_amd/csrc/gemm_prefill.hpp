@@ -48,6 +48,7 @@ constexpr int kGemmThreads = 256;
 struct GemmArgs {
   const uint8_t *pool;
   const int32_t *slot_of_expert;  // NULL: slot e
+  int32_t n_slots;                // slots in the pool (a larger table value reads as not resident)
   uint64_t expert_bytes;
   const uint8_t *shared_blob;     // NULL: none
   uint64_t off_w0, off_w1, off_s0, off_s1;
@@ -202,7 +203,7 @@ __device__ __forceinline__ bool gemm_setup(const GemmArgs &a, int &nt_idx, int &
   if (shared) {
     blob = a.shared_blob;
   } else {
-    const int slot = a.slot_of_expert ? a.slot_of_expert[e] : e;
+    const int slot = table_slot(a.slot_of_expert, e, a.n_slots);
     if (slot == FT_SLOT_SKIP) return false;  // another call computes these rows
     if (slot < 0) {
       // not resident: mark this tile's outputs NaN

@@ -25,6 +25,7 @@ constexpr int kPersistMaxRows = 4096;  // routed rows whose token indices fit th
 struct PersistArgs {
   const uint8_t *pool;
   const int32_t *slot_of_expert;  // NULL: slot e
+  int32_t n_slots;                // slots in the pool (a larger table value reads as not resident)
   uint64_t expert_bytes;
   const uint8_t *shared_blob;     // NULL: none
   uint64_t off_w0, off_w1, off_s0, off_s1;
@@ -94,7 +95,7 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
       s_e[i] = e;
       s_pos[i] = lo;
       s_m[i] = cnt;
-      s_slot[i] = a.slot_of_expert ? a.slot_of_expert[e] : e;
+      s_slot[i] = table_slot(a.slot_of_expert, e, a.n_slots);
     }
     base += total;
     __syncthreads();
@@ -352,7 +353,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
       s_e[i] = e;
       s_pos[i] = lo;
       s_m[i] = cnt;
-      s_slot[i] = a.slot_of_expert ? a.slot_of_expert[e] : e;
+      s_slot[i] = table_slot(a.slot_of_expert, e, a.n_slots);
     }
     base += total;
     __syncthreads();

@@ -81,8 +81,14 @@ def ft_moe_permute(topk_ids, T: int, k: int, E: int, expert_offsets, sorted_rows
 
 def ft_moe_grouped_ffn(layout: ExpertLayout, slot_pool, slot_of_expert, shared_blob, x, x_dtype: int,
                        T: int, k: int, E: int, expert_offsets, sorted_rows, y_rows, y_shared,
-                       mode: int = 0, workspace=None, workspace_bytes: int = 0, stream=None) -> None:
-    _check(_lib.lib().ft_moe_grouped_ffn(C.byref(layout), _ptr(slot_pool), _ptr(slot_of_expert),
+                       mode: int = 0, workspace=None, workspace_bytes: int = 0, stream=None,
+                       n_slots: int | None = None) -> None:
+    """n_slots: blobs in slot_pool; by default the pool tensor's size over the layout's blob size
+    (E for a raw pointer)."""
+    if n_slots is None:
+        n_slots = slot_pool.numel() * slot_pool.element_size() // int(layout.expert_bytes) \
+            if hasattr(slot_pool, "numel") else E
+    _check(_lib.lib().ft_moe_grouped_ffn(C.byref(layout), _ptr(slot_pool), int(n_slots), _ptr(slot_of_expert),
                                          _ptr(shared_blob), _ptr(x), x_dtype, T, k, E, _ptr(expert_offsets),
                                          _ptr(sorted_rows), _ptr(y_rows), _ptr(y_shared), mode,
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
@@ -122,7 +128,8 @@ class ExpertCache:
     """Owner of one ``ft_expert_cache`` handle (create / step / stats / trace / destroy)."""
 
     def __init__(self, layout: ExpertLayout, n_layers: int, E: int, capacity: int, slot_pool, host_bank,
-                 copy_stream):
+                 copy_stream, trace_events: int = 0):
+        """trace_events > 0 keeps an event ring of that many records (ft_expert_cache_set_trace)."""
         self.layout = layout
         self.n_layers, self.E, self.capacity = n_layers, E, capacity
         self._keep = (slot_pool, host_bank, copy_stream)
@@ -130,6 +137,13 @@ class ExpertCache:
         _check(_lib.lib().ft_expert_cache_create(C.byref(layout), n_layers, E, capacity, _ptr(slot_pool),
                                                  _ptr(host_bank), _stream(copy_stream), C.byref(h)))
         self._h = h
+        if trace_events:
+            self.set_trace(trace_events)
+
+    def ft_expert_cache_set_trace(self, max_events: int) -> None:
+        _check(_lib.lib().ft_expert_cache_set_trace(self._h, int(max_events)))
+
+    set_trace = ft_expert_cache_set_trace
 
     def ft_expert_cache_step(self, layer: int, topk_ids, T: int, k: int, slot_of_expert, stream=None) -> None:
         _check(_lib.lib().ft_expert_cache_step(self._h, layer, _ptr(topk_ids), T, k, _ptr(slot_of_expert),
@@ -168,8 +182,9 @@ class ExpertCache:
 
     wait_fills = ft_expert_cache_wait_fills
 
-    def ft_expert_cache_set_split(self, b_pcie: float, b_host: float) -> None:
-        _check(_lib.lib().ft_expert_cache_set_split(self._h, float(b_pcie), float(b_host)))
+    def ft_expert_cache_set_split(self, b_pcie: float, b_host: float, T_max: int = 0, k: int = 0) -> None:
+        """T_max, k: the largest step whose CPU misses are staged (needed when b_host > 0)."""
+        _check(_lib.lib().ft_expert_cache_set_split(self._h, float(b_pcie), float(b_host), int(T_max), int(k)))
 
     set_split = ft_expert_cache_set_split
 

@@ -33,8 +33,12 @@
  *  - Return value: FT_OK (0) or a negative ft_status.  ft_last_error() gives a
  *    text for the last failing call on the calling host thread.  Faults of
  *    enqueued work surface at the caller's next synchronisation.
- *  - Hot-path calls never allocate device or host memory.  Scratch memory is
- *    passed in as `workspace`, sized by ft_workspace_bytes().
+ *  - Hot-path calls (route, permute, grouped FFN, combine, the cache's step,
+ *    plan / fill, prefetch and CPU-miss calls) never allocate device or host
+ *    memory.  Scratch memory is passed in as `workspace`, sized by
+ *    ft_workspace_bytes(); the cache allocates its state at create, its
+ *    event ring at ft_expert_cache_set_trace and its CPU-miss buffers at
+ *    ft_expert_cache_set_split.
  *  - Row-major layouts throughout; [a, b] means a rows of b contiguous elements.
  */
 #ifndef FT_MOE_H
@@ -180,10 +184,11 @@ ft_status ft_moe_route_permute(const void *x, int32_t x_dtype, const void *w_rou
  * Segment e = rows expert_offsets[e] .. expert_offsets[e+1]-1 of the permuted
  * order; its row i is token sorted_rows[i] / k.  Expert e's blob starts at
  *   slot_pool + slot_of_expert[e] * L->expert_bytes
- * (slot_of_expert == NULL means slot e).  A segment whose slot is
+ * (slot_of_expert == NULL means slot e).  slot_pool holds n_slots blobs
+ * (n_slots >= 1; >= E when slot_of_expert is NULL).  A segment whose slot is
  * FT_SLOT_SKIP is left untouched (its hidden and y rows are not written); a
- * non-empty segment with another negative slot is a caller error, its y rows
- * are written as NaN.
+ * non-empty segment with another negative slot, or a slot >= n_slots, is a
+ * caller error: nothing is read for it and its y rows are written as NaN.
  * x [T, H] of x_dtype (FT_F32 with FT_F32 weights, FT_BF16 with FT_BF16 or
  *   FT_MXFP4 weights).
  * y_rows [T*k, H] fp32, permuted order (row i belongs to sorted_rows[i]).
@@ -218,7 +223,7 @@ ft_status ft_moe_route_permute(const void *x, int32_t x_dtype, const void *w_rou
  */
 enum { FT_FFN_EXACT = 0, FT_FFN_NATIVE_MX = 1 };
 enum { FT_FFN_GATE_UP_ONLY = 0x100, FT_FFN_DOWN_ONLY = 0x200 };
-ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool,
+ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
                              const int32_t *slot_of_expert, const void *shared_blob,
                              const void *x, int32_t x_dtype, int32_t T, int32_t k, int32_t E,
                              const int32_t *expert_offsets, const int32_t *sorted_rows,
@@ -342,6 +347,7 @@ typedef struct {
   uint64_t cpu_ns;      /* host wall time inside ft_expert_cache_run_cpu_misses (waiting for the staged
                            inputs, the expert kernel, enqueueing the copy back): cpu_misses *
                            expert_bytes / cpu_ns is the effective B_h the decode loop sees */
+  uint64_t trace_dropped;  /* events overwritten in the event ring (ft_expert_cache_set_trace) */
 } ft_cache_stats;
 
 /* One cache event, as recorded by the step (or layer prefetch) that produced it. */
@@ -351,7 +357,8 @@ typedef struct {
   int32_t layer;
   int32_t expert;
   int32_t hit;         /* 1 hit, 0 miss (filled), 4 miss left to the host CPU
-                          (slot -1); prefetch: 3 already resident, 2 filled  */
+                          (slot -1); prefetch: 3 already resident, 2 filled,
+                          5 not prefetched for lack of room (slot -1)        */
   int32_t slot;
   int32_t evicted;     /* key layer*E + expert of the entry evicted, or -1    */
 } ft_cache_event;
@@ -450,9 +457,20 @@ ft_status ft_expert_cache_wait_fills(ft_expert_cache *c, hipStream_t compute_str
 /* Totals since create (host).  */
 ft_status ft_expert_cache_stats(const ft_expert_cache *c, ft_cache_stats *out);
 
-/* Copy the event log into host_buf (host) as ft_cache_event records, events of
- * one step in ascending expert id.  *needed (host, optional) receives the bytes
- * the whole log takes; at most `bytes` are written (whole records only). */
+/*
+ * ft_expert_cache_set_trace -- keep an event log (for parity checks of the
+ * cache's decisions against a simulator).  Off by default.  max_events > 0
+ * allocates a ring of that many ft_cache_event records (host memory, here and
+ * nowhere else) and empties it; once full, each new event overwrites the
+ * oldest (counted in ft_cache_stats.trace_dropped).  0 turns the log off and
+ * frees it.  Errors: max_events outside 0..2^28 or no memory -> FT_EINVAL.
+ */
+ft_status ft_expert_cache_set_trace(ft_expert_cache *c, int64_t max_events);
+
+/* Copy the events the ring holds into host_buf (host) as ft_cache_event
+ * records, oldest first, events of one step in ascending expert id.  *needed
+ * (host, optional) receives the bytes they take; at most `bytes` are written
+ * (whole records only).  Nothing is recorded while the log is off. */
 ft_status ft_expert_cache_trace(const ft_expert_cache *c, void *host_buf, size_t bytes,
                                 size_t *needed);
 
@@ -475,9 +493,15 @@ ft_status ft_expert_cache_lookup(const ft_expert_cache *c, int32_t layer, int32_
  * ft_expert_cache_cpu_misses; ft_expert_cache_stage_cpu_misses and
  * ft_expert_cache_run_cpu_misses compute their rows on the host and write
  * them into y_rows after ft_moe_grouped_ffn (which writes NaN there).  b_host = 0 turns the split off (every miss filled, the default).
- * Errors: negative or NaN bandwidths -> FT_EINVAL.
+ * With b_host > 0 the host-mapped buffers of the CPU misses are allocated
+ * here, for steps of up to T_max tokens with k picks each (a later call with
+ * larger sizes replaces them); a stage call for a larger step returns
+ * FT_ECAPACITY.  With b_host = 0, T_max and k are ignored.
+ * Errors: negative or NaN bandwidths, or (b_host > 0) T_max < 1, k < 1 or
+ * T_max*k > 2^28 -> FT_EINVAL; a planned step waiting for its fill ->
+ * FT_EINVAL; FT_EHIP if the pinned allocation fails.
  */
-ft_status ft_expert_cache_set_split(ft_expert_cache *c, double b_pcie, double b_host);
+ft_status ft_expert_cache_set_split(ft_expert_cache *c, double b_pcie, double b_host, int32_t T_max, int32_t k);
 
 /* The last step's misses left to the CPU, ascending expert id: *n (host)
  * receives their number, experts (host) the first min(*n, capacity) ids. */
@@ -494,8 +518,9 @@ ft_status ft_expert_cache_cpu_misses(const ft_expert_cache *c, int32_t *experts,
  * stage: enqueues on `stream` a kernel that copies x [T, H] (DEVICE, bf16,
  *   16-byte aligned), expert_offsets [E+1] and sorted_rows [T*k] (DEVICE, the
  *   step's ft_moe_permute outputs) into host-mapped memory the cache owns
- *   (grown on demand).  A kernel, not a DMA copy: it does not wait behind the
- *   step's miss fills on the copy engines.  Returns at once.
+ *   (sized by ft_expert_cache_set_split).  A kernel, not a DMA copy: it does
+ *   not wait behind the step's miss fills on the copy engines.  Returns at
+ *   once, after waiting for the previous stage's kernel if it is still queued.
  * run: waits for that kernel only, computes the rows of every CPU miss on the
  *   host (ft_cpu_miss_rows over the cache's host bank, n_threads as there),
  *   then enqueues on `stream` a kernel that copies them from host-mapped
@@ -503,7 +528,8 @@ ft_status ft_expert_cache_cpu_misses(const ft_expert_cache *c, int32_t *experts,
  *   the NaN rows ft_moe_grouped_ffn left there; enqueue it after that FFN.
  * Both are no-ops (FT_OK) when the last step left no miss to the CPU.
  * Errors: run without a stage of the same step -> FT_EINVAL; activations
- *   other than bf16 -> FT_ENOTSUP; the host kernel's errors as there.
+ *   other than bf16 -> FT_ENOTSUP; a step larger than set_split's T_max x k
+ *   -> FT_ECAPACITY (stage); the host kernel's errors as there.
  * A later stage or run waits for the previous one's kernels before it reuses
  * the host buffers.
  */
@@ -525,8 +551,13 @@ ft_status ft_expert_cache_run_cpu_misses(ft_expert_cache *c, float *y_rows, hipS
  * waits for it, as in a step); the fills go to the copy queues and are NOT
  * waited for here: the next ft_expert_cache_step makes its compute stream
  * (and its own fills) wait for them.  Intended order per layer l: step(l),
- * prefetch(l+1), then the FFN of layer l -- with room for two layers the
- * prefetch then evicts only entries of earlier layers.
+ * prefetch(l+1), then the FFN of layer l.  The pages double-buffer only when
+ * the cache has room: the prefetch never takes the slot of an entry the most
+ * recent step (step, step_split or plan + fill) left resident for its
+ * routing, so the FFN of layer l still reads its own experts; the layer's
+ * experts are visited in ascending id, and once no other slot is left the
+ * rest are not prefetched (event code 5) and miss in their own step.  With
+ * room for two layers every expert is prefetched.
  * Errors: E > capacity -> FT_ECAPACITY (cache unchanged); as for a step.
  */
 ft_status ft_expert_cache_prefetch_layer(ft_expert_cache *c, int32_t layer, hipStream_t compute_stream);

@@ -118,6 +118,9 @@ def test_ffn_validation():
     assert _err(f, L4, 256, None, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 0,
                 workspace=256, workspace_bytes=16, stream=0) == -1                                # workspace
     assert _err(f, L4, 256, None, None, 256, 1, 1, 7, 6, 256, 256, 256, None, 0, **ok) == -2     # k > E
+    assert _err(f, L4, 256, None, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 0, n_slots=255,
+                **ok) == -1                                                # identity table, fewer slots than E
+    assert _err(f, L4, 256, 256, None, 256, 1, 1, 6, 256, 256, 256, 256, None, 0, n_slots=0, **ok) == -1
     Lnv = ops.ft_expert_layout_init(3, 2048, 768)
     assert _err(f, Lnv, 256, None, None, 256, 1, 1, 8, 128, 256, 256, 256, None, 1, **ok) == -2  # mode 1, NVFP4
     assert _err(f, ops.ft_expert_layout_init(3, 2048, 784), 256, None, None, 256, 1, 1, 8, 128, 256, 256, 256,

@@ -38,8 +38,13 @@ class Rig:
             self.bank.numpy()[:] = rng.integers(0, 256, size=self.bank.shape, dtype=np.uint8)
         self.pool = torch.zeros((C, self.eb), dtype=torch.uint8, device="cuda")
         self.copy_stream = torch.cuda.Stream()
-        self.cache = ops.ExpertCache(self.lay, n_layers, E, C, self.pool, self.bank, self.copy_stream)
+        self.cache = ops.ExpertCache(self.lay, n_layers, E, C, self.pool, self.bank, self.copy_stream,
+                                     trace_events=1 << 20)
         self.slot_of = torch.empty(E, dtype=torch.int32, device="cuda")
+
+    def set_split(self, b_pcie, b_host):
+        """Steps of this rig have k = 1 and at most 64 ids."""
+        self.cache.set_split(b_pcie, b_host, 64, 1)
 
     def step(self, layer, ids):
         ids = np.asarray(ids, np.int32).reshape(-1)
@@ -82,13 +87,13 @@ def test_hand_traced_sequences_on_device(env, golden_dir):
                 continue
             if kind == "prefetch":
                 rig.cache.prefetch_layer(layer)
-                code = {True: 3, False: 2}
+                code = {True: 3, False: 2, None: 5}       # 5: not prefetched for lack of room
             else:
-                rig.cache.set_split(*_split_for(tr.get("fill", {}).get(i), sum(not h for _, h, _, _ in evs)))
+                rig.set_split(*_split_for(tr.get("fill", {}).get(i), sum(not h for _, h, _, _ in evs)))
                 rig.step(layer, ids)
-                code = {True: 1, False: 0}
-            want += [(n_steps, layer, e, code[h] if s >= 0 or h else 4, s, -1 if ev is None else ev[0] * E + ev[1])
-                     for e, h, s, ev in evs]
+                code = {True: 1, False: 0, None: 4}       # 4: left to the host CPU
+            want += [(n_steps, layer, e, code[h if s >= 0 or h else None], s,
+                      -1 if ev is None else ev[0] * E + ev[1]) for e, h, s, ev in evs]
             n_steps += kind != "prefetch"
         assert rig.cache.trace() == want, tr["name"]
         st = rig.cache.stats()
@@ -354,7 +359,7 @@ def test_hybrid_split_against_the_simulator(env):
         m = sum(sim.slot_of_expert(layer)[e] < 0 for e in needed)
         q = m if bh == 0 else policy.miss_split(m, bp, bh)
         evs = sim.step(layer, ids, fill_limit=q)
-        rig.cache.set_split(bp, bh)
+        rig.set_split(bp, bh)
         rig.step(layer, ids)
         torch.cuda.synchronize()
         cpu = [e.expert for e in evs if not e.hit and e.slot < 0]
@@ -397,7 +402,7 @@ def test_hybrid_layer_outputs(env, T, C, hybrid, hits_first):
     pool = torch.zeros((cfg.capacity, eb), dtype=torch.uint8, device="cuda")
     cache = ops.ExpertCache(lay, cfg.n_layers, cfg.E, cfg.capacity, pool, bank, torch.cuda.Stream())
     if hybrid:
-        cache.set_split(2.0, 1.0)  # a third of each step's misses on the CPU
+        cache.set_split(2.0, 1.0, T, cfg.k)  # a third of each step's misses on the CPU
     slot_of = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
     slot_hits = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
     n_cpu = n_two_pass = 0
@@ -454,9 +459,12 @@ def test_cpu_miss_calls_validate(env):
     rig.step(0, [0, 1])
     rig.cache.stage_cpu_misses(x, Lm.DTYPES["bf16"], 2, 1, off, rows)  # no CPU miss: nothing happens
     rig.cache.run_cpu_misses(y)
-    rig.cache.set_split(0.0, 1.0)                                   # every miss on the CPU
+    rig.cache.set_split(0.0, 1.0, 2, 1)                             # every miss on the CPU
     rig.step(0, [2, 3])
     assert rig.cache.cpu_misses() == [2, 3]
+    with pytest.raises(ops.FtError) as e:                           # larger than set_split's T_max x k
+        rig.cache.stage_cpu_misses(x, Lm.DTYPES["bf16"], 2, 2, off, rows)
+    assert e.value.status == -3
     with pytest.raises(ops.FtError) as e:
         rig.cache.run_cpu_misses(y)
     assert e.value.status == -1
@@ -489,7 +497,7 @@ def test_split_step_tables_against_the_simulator(env):
         m = sum(sim.slot_of_expert(layer)[e] < 0 for e in needed)
         q = m if bh == 0 else policy.miss_split(m, bp, bh)
         evs = {ev.expert: ev for ev in sim.step(layer, ids, fill_limit=q)}
-        rig.cache.set_split(bp, bh)
+        rig.set_split(bp, bh)
         d = torch.from_numpy(ids).cuda()
         if t % 2:
             n_filled = rig.cache.step_split(layer, d, ids.size, 1, hits_t, rig.slot_of)
@@ -546,4 +554,96 @@ def test_plan_and_fill_call_order(env):
     rig.cache.plan(0, d, 2, 1, hits_t, rig.slot_of)      # the cache is usable again: two hits
     assert rig.cache.fill() == 0
     torch.cuda.synchronize()
+    rig.cache.destroy()
+
+
+def test_prefetch_with_room_for_less_than_two_layers(env):
+    """Capacity between E and 2E, order route(l) -> cache step(l) -> prefetch(l+1) -> FFN(l): the
+    prefetch keeps the slots layer l's FFN reads and fills only what fits (events, fills and totals
+    follow the simulator, some experts are not prefetched), and every token of every layer matches the
+    oracle layer evaluated expert-major."""
+    ops, Lm = env
+    cfg = synth.shrink(synth.CONFIGS[4], H=512, I=512, E=16, k=4, n_layers=4, capacity=22)
+    T = 160
+    shape = Lm.LayerShape(cfg.H, cfg.I, cfg.E, cfg.k, cfg.wdtype, cfg.xdtype, cfg.gating, cfg.renormalize, True)
+    layer = Lm.MoELayer(shape, T)
+    lay = layer.layout
+    eb = int(lay.expert_bytes)
+    ex = [Experts(cfg, l) for l in range(cfg.n_layers)]
+    bank = torch.empty((cfg.n_layers * cfg.E, eb), dtype=torch.uint8, pin_memory=True)
+    for l in range(cfg.n_layers):
+        for e in range(cfg.E):
+            Lm.pack_expert(lay, ex[l].raw(e).arrays, bank.numpy()[l * cfg.E + e])
+    shared = [Lm.as_device_u8([Lm.pack_expert(lay, ex[l].raw(cfg.E).arrays)])[0] for l in range(cfg.n_layers)]
+    pool = torch.zeros((cfg.capacity, eb), dtype=torch.uint8, device="cuda")
+    cache = ops.ExpertCache(lay, cfg.n_layers, cfg.E, cfg.capacity, pool, bank, torch.cuda.Stream(),
+                            trace_events=4096)
+    slot_of = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    sim = ExpertLRU(cfg.n_layers, cfg.E, cfg.capacity)
+    want, n_steps, skipped = [], 0, 0
+
+    def log(kind, l, evs):
+        nonlocal skipped
+        for e in evs:
+            if kind == "prefetch":
+                code = 3 if e.hit else (2 if e.slot >= 0 else 5)
+                skipped += code == 5
+            else:
+                code = 1 if e.hit else 0
+            want.append((n_steps, l, e.expert, code, e.slot,
+                         -1 if e.evicted is None else e.evicted[0] * cfg.E + e.evicted[1]))
+
+    cache.prefetch_layer(0)
+    log("prefetch", 0, sim.prefetch(0))
+    for l in range(cfg.n_layers):
+        print(f"prefetch regime: layer {l}", flush=True)
+        x = synth.tokens(cfg, T, layer=l)
+        logits = synth.prefill_logits(cfg, T, layer=l)
+        layer.route_permute(T, logits=Lm.to_device(logits))
+        cache.step(l, layer.ids, T, cfg.k, slot_of)
+        ids = moe.topk(logits, cfg.k)
+        log("step", l, sim.step(l, ids.ravel()))
+        table_want = sim.slot_of_expert(l)
+        n_steps += 1
+        if l + 1 < cfg.n_layers:
+            cache.prefetch_layer(l + 1)
+            log("prefetch", l + 1, sim.prefetch(l + 1))
+        layer.ffn(T, Lm.to_device(x), pool, slot_of_expert=slot_of, shared_blob=shared[l])
+        layer.combine(T)
+        torch.cuda.synchronize()
+        assert slot_of.cpu().numpy().tolist() == table_want
+        got = formats.bf16_to_f64(layer.out[:T].cpu().numpy().view(np.uint16))
+        x64 = formats.activations_to_f64(cfg.xdtype, x)
+        ref = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                            experts=ex[l].f64, shared=ex[l].f64(cfg.E), logits=logits)
+        check_close(got, ref["out"], bf16_out=True, what=f"prefetch regime layer {l}, every token")
+    assert cache.trace() == want
+    st = cache.stats()
+    assert skipped > 0                                   # the regime: some experts found no room
+    assert (st["accesses"], st["hits"], st["misses"], st["evictions"], st["prefetch_fills"]) == \
+        (sim.accesses, sim.hits, sim.misses, sim.evictions, sim.prefetch_fills)
+    assert st["bytes_h2d"] == (sim.misses + sim.prefetch_fills) * eb
+    cache.destroy()
+
+
+def test_event_ring(env):
+    """The event log is off by default; a ring keeps the newest events oldest first and counts the
+    ones it overwrote."""
+    ops, _ = env
+    rig = Rig(ops, 1, 16, 4)
+    rig.cache.set_trace(0)
+    rig.step(0, [1, 2])
+    assert rig.cache.trace() == []
+    rig.cache.set_trace(5)
+    sim = ExpertLRU(1, 16, 4)
+    sim.step(0, [1, 2])
+    want = []
+    for i, ids in enumerate([[1, 3], [4, 5, 6], [2, 7]]):
+        want += [(i + 1, 0, e.expert, int(e.hit), e.slot, -1 if e.evicted is None else e.evicted[1])
+                 for e in sim.step(0, ids)]
+        rig.step(0, ids)
+    assert rig.cache.trace() == want[-5:]
+    assert rig.cache.stats()["trace_dropped"] == len(want) - 5
+    with pytest.raises(ops.FtError):
+        rig.cache.set_trace(-1)
     rig.cache.destroy()
