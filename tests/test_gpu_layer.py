@@ -6,7 +6,8 @@ torch = pytest.importorskip("torch")
 
 import synth
 from oracle import formats, moe
-from tests.helpers import Experts, check_close, native_mx_expert, native_mx_token, route_oracle
+from tests.helpers import (TOPK_MARGIN, Experts, check_close, check_topk_valid, native_mx_expert,
+                           native_mx_token, route_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,9 +45,31 @@ def out_f64(layer, cfg, T):
     return formats.bf16_to_f64(o.view(np.uint16)) if cfg.xdtype == "bf16" else o.astype(np.float64)
 
 
-@pytest.mark.parametrize("cfg_id,T,sample", [(1, 8, None), (2, 1, None), (2, 16, None), (2, 64, 12),
-                                             (3, 1, None), (3, 8, 4), (3, 32, 4), (6, 1, None), (6, 64, 12)])
-def test_layer_router_gemv(L, cfg_id, T, sample):
+def check_routing(cfg, got_logits, got_ids, got_w, ref, wr64, x64, what):
+    """Routing of a layer call against the oracle's: the GPU's logits within the fp32-accumulation
+    bound, its top-k exact on its own logits, bit-exact ids where the oracle margin exceeds 1e-4 and a
+    valid top-k elsewhere; gating weights equal to the oracle's at the GPU's ids.  Returns the tokens
+    whose ids differ from the oracle's (near ties only) and the oracle weights at the GPU's ids."""
+    scale = np.abs(x64) @ np.abs(wr64).T
+    assert np.all(np.abs(got_logits - ref["logits"]) <= 3e-5 * scale + 1e-6), f"{what}: logits"
+    assert np.array_equal(got_ids, moe.topk(got_logits.astype(np.float32), cfg.k)), f"{what}: top-k of own logits"
+    sure = ref["margin"] > TOPK_MARGIN
+    assert sure.mean() >= 0.9
+    assert np.array_equal(got_ids[sure], ref["ids"][sure]), f"{what}: ids above the margin"
+    differ = check_topk_valid(got_ids, ref["logits"], cfg.k, what=what)
+    assert set(differ.tolist()) <= set(np.flatnonzero(~sure).tolist())
+    w_at = moe.gating_weights(ref["logits"], got_ids, cfg.gating, cfg.renormalize)
+    np.testing.assert_allclose(got_w, w_at, rtol=1e-4, atol=1e-6)
+    print(f"ROUTING {what}: {int((~sure).sum())} of {len(sure)} tokens at or below the 1e-4 margin, "
+          f"{len(differ)} with ids other than the oracle's (valid top-k, compared at the GPU's ids)", flush=True)
+    return differ, w_at
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg_id,T", [(1, 8), (2, 1), (2, 16), (2, 64), (3, 1), (3, 8), (3, 32), (6, 1), (6, 64)])
+def test_layer_router_gemv(L, cfg_id, T):
+    """Every token of the layer call against the oracle layer, evaluated expert-major (each expert's
+    weights decoded once for all its tokens); tokens whose routing is a near tie at the GPU's own ids."""
     cfg = synth.CONFIGS[cfg_id]
     print(f"layer cfg{cfg_id} T={T}", flush=True)
     ex = Experts(cfg)
@@ -54,25 +77,38 @@ def test_layer_router_gemv(L, cfg_id, T, sample):
     wr = synth.router_weight(cfg)
     x64 = formats.activations_to_f64(cfg.xdtype, x)
     wr64 = formats.activations_to_f64(cfg.xdtype, wr)
-    logits, ids, w, margin = route_oracle(cfg, x64, wr64)
+    ids0 = moe.topk(moe.router_logits(x64, wr64), cfg.k)
     layer = make_layer(L, cfg, T)
-    pool = build_pool(L, layer, ex, sorted(set(ids.ravel().tolist())), cfg.E)
+    pool = build_pool(L, layer, ex, sorted(set(ids0.ravel().tolist())), cfg.E)
     shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
     layer.forward(T, L.to_device(x), pool, w_router=L.to_device(wr), shared_blob=shared)
     torch.cuda.synchronize()
     got = out_f64(layer, cfg, T)
     got_ids = layer.ids[:T].cpu().numpy()
-    sure = np.flatnonzero(margin > 1e-4)
-    assert len(sure) >= 0.9 * T
-    assert np.array_equal(got_ids[sure], ids[sure])
-    toks = sure if sample is None else np.random.default_rng(T).choice(sure, size=min(sample, len(sure)), replace=False)
-    ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E) if cfg.shared else None)
-                    for t in toks])
-    check_close(got[toks], ref, bf16_out=cfg.xdtype == "bf16", what=f"cfg{cfg_id} T={T} out")
+    got_logits = layer.logits[:T].cpu().numpy().astype(np.float64)
+    got_w = layer.w[:T].cpu().numpy()
+    sh = ex.f64(cfg.E) if cfg.shared else None
+    ref = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                        experts=ex.fresh, shared=sh, w_router=wr64)
+    differ, w_at = check_routing(cfg, got_logits, got_ids, got_w, ref, wr64, x64, f"cfg{cfg_id} T={T}")
+    out_ref = ref["out"].copy()
+    for t in differ:
+        out_ref[t] = moe.token_output(x64[t], got_ids[t], w_at[t], ex.fresh, sh)
+    check_close(got, out_ref, bf16_out=cfg.xdtype == "bf16", what=f"cfg{cfg_id} T={T} every token")
 
 
+def _prefill_segments(off_ref):
+    """The most and the least popular non-empty experts of a routing."""
+    sizes = np.diff(off_ref)
+    big = int(np.argmax(sizes))
+    small = int(np.argmin(np.where(sizes > 0, sizes, 10 ** 9)))
+    return [big, small]
+
+
+@pytest.mark.timeout(900)
 def test_layer_prefill_given_logits(L):
-    """Prefill workload (8192 tokens, Zipf-skewed segments), sampled tokens + whole-output properties."""
+    """Prefill workload (8192 tokens, Zipf-skewed segments), both modes: the whole segments of the
+    most and the least popular expert, the shared expert's rows of every token, sampled outputs."""
     cfg = synth.CONFIGS[4]
     T = 8192
     ex = Experts(cfg)
@@ -86,35 +122,48 @@ def test_layer_prefill_given_logits(L):
     shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0]
     x64 = formats.activations_to_f64(cfg.xdtype, x)
     off_ref, rows_ref, _ = moe.permute(ids, cfg.E)
-    sizes = np.diff(off_ref)
-    e = int(np.argmin(np.where(sizes > 0, sizes, 10 ** 9)))   # the least popular non-empty expert
-    a, b = int(off_ref[e]), int(off_ref[e + 1])
-    toks = [0, 4097, T - 1]
+    segs = _prefill_segments(off_ref)
+    toks = [0, 1, 4097, 5000, T - 1]
     for mode in (0, 1):      # exact bf16 MFMA, then the native MXFP4 scaled MFMA
         print(f"prefill: running mode {mode}", flush=True)
         layer.forward(T, L.to_device(x), pool, logits=L.to_device(logits), shared_blob=shared, mode=mode)
         torch.cuda.synchronize()
         assert np.array_equal(layer.ids[:T].cpu().numpy(), ids)
         assert np.array_equal(layer.offsets.cpu().numpy(), off_ref)
+        assert np.array_equal(layer.sorted_rows[:T * cfg.k].cpu().numpy(), rows_ref)
         got = out_f64(layer, cfg, T)
         assert np.all(np.isfinite(got))
-        yr = layer.y_rows[a:b].cpu().numpy()
+        assert np.all(np.isfinite(layer.y_rows[:T * cfg.k].cpu().numpy()))
+        for e in segs:
+            a, b = int(off_ref[e]), int(off_ref[e + 1])
+            print(f"prefill mode {mode}: expert {e}, {b - a} rows", flush=True)
+            yr = layer.y_rows[a:b].cpu().numpy()
+            X = x64[rows_ref[a:b] // cfg.k]
+            if mode == 0:
+                check_close(yr, moe.swiglu_expert(X, *ex.f64(e)), what=f"prefill mode 0 segment of expert {e}")
+            else:
+                yref, allow = native_mx_expert(X, *ex.f64(e))
+                check_close(yr, yref, what=f"prefill mode 1 segment of expert {e}", allow=allow)
+        ysh = layer.y_shared[:T].cpu().numpy()
         if mode == 0:
+            check_close(ysh, moe.swiglu_expert(x64, *ex.f64(cfg.E)), what="prefill mode 0 shared expert, every token")
             ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E)) for t in toks])
             check_close(got[toks], ref, bf16_out=True, what="prefill mode 0 sampled tokens")
-            # one expert's whole segment in the permuted expert rows
-            yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
-            check_close(yr, yref, what=f"prefill mode 0 segment of expert {e}")
         else:
+            yref, allow = native_mx_expert(x64, *ex.f64(cfg.E))
+            check_close(ysh, yref, what="prefill mode 1 shared expert, every token", allow=allow)
             pairs = [native_mx_token(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E)) for t in toks]
             check_close(got[toks], np.stack([p[0] for p in pairs]), bf16_out=True,
                         what="prefill mode 1 sampled tokens", allow=np.stack([p[1] for p in pairs]))
-            yref, allow = native_mx_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
-            check_close(yr, yref, what=f"prefill mode 1 segment of expert {e}", allow=allow)
+        ex.drop()
+        for e in segs + [cfg.E]:
+            ex.f64(e)            # keep only the compared experts for the next mode
 
 
+@pytest.mark.timeout(600)
 def test_layer_prefill_nvfp4(L):
-    """NVFP4 prefill workload (8192 tokens on the Qwen3-A3B shape): sampled tokens and one expert's segment."""
+    """NVFP4 prefill workload (8192 tokens on the Qwen3-A3B shape): the whole segments of the most and
+    the least popular expert, and sampled tokens."""
     cfg = synth.CONFIGS[7]
     T = 8192
     ex = Experts(cfg)
@@ -135,11 +184,10 @@ def test_layer_prefill_nvfp4(L):
     ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64) for t in toks])
     check_close(got[toks], ref, bf16_out=True, what="nvfp4 prefill sampled tokens")
     off_ref, rows_ref, _ = moe.permute(ids, cfg.E)
-    sizes = np.diff(off_ref)
-    e = int(np.argmax(sizes))                                  # the most popular expert: many token tiles
-    a, b = int(off_ref[e]), int(off_ref[e + 1])
-    yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
-    check_close(layer.y_rows[a:b].cpu().numpy(), yref, what=f"nvfp4 prefill segment of expert {e}")
+    for e in _prefill_segments(off_ref):
+        a, b = int(off_ref[e]), int(off_ref[e + 1])
+        yref = moe.swiglu_expert(x64[rows_ref[a:b] // cfg.k], *ex.f64(e))
+        check_close(layer.y_rows[a:b].cpu().numpy(), yref, what=f"nvfp4 prefill segment of expert {e}")
 
 
 @pytest.mark.parametrize("cfg_id", [2, 3])
@@ -173,3 +221,65 @@ def test_layer_empty_batch_then_small(L, cfg_id):
     ref = np.stack([moe.token_output(x64[t], ids[t], w[t], ex.f64, ex.f64(cfg.E) if cfg.shared else None)
                     for t in sure])
     check_close(out_f64(layer, cfg, T)[sure], ref, bf16_out=cfg.xdtype == "bf16", what=f"cfg{cfg_id} after empty")
+
+
+def _near_tie_router(cfg, x64, rng):
+    """Router weights [E, H] (bf16 bits) that give the token a near tie at the top-k boundary: experts
+    0..k-2 far ahead, then two experts whose rows differ by one bf16 step at the token's smallest
+    activation, so their logits differ by far less than the 1e-4 margin (fp32 rounding of the GPU's
+    sum may order them either way)."""
+    E, H, k = cfg.E, cfg.H, cfg.k
+    w = rng.standard_normal((E, H)).astype(np.float32) * np.float32(cfg.w_std)
+    sgn = np.sign(x64[0]).astype(np.float32)
+    order = rng.permutation(E)
+    lead, (a, b) = order[:k - 1], order[k - 1:k + 1]
+    for j, e in enumerate(lead):
+        w[e] = sgn * np.float32(0.05 + 0.002 * j)
+    w[a] = sgn * np.float32(0.01)
+    bits = synth.f32_to_bf16_bits(w)
+    h = int(np.argmin(np.abs(x64[0])))
+    bits[b] = bits[a]
+    bits[b, h] = bits[a, h] + 1           # one bf16 step (same sign: the magnitude grows by one ulp)
+    return bits, int(a), int(b)
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3])
+def test_layer_near_tie_routing(L, cfg_id):
+    """Planted near ties at the top-k boundary: the GPU's ids are a valid top-k of the oracle logits
+    (checked against the margin rule), and the token's output equals the oracle's at the GPU's own
+    ids and weights."""
+    cfg = synth.CONFIGS[cfg_id]
+    ex = Experts(cfg)
+    layer = make_layer(L, cfg, 1)
+    n_tie = n_differ = 0
+    for case in range(6):
+        x = synth.tokens(cfg, 1, case=100 + case)
+        x64 = formats.activations_to_f64(cfg.xdtype, x)
+        wr, a, b = _near_tie_router(cfg, x64, np.random.default_rng(case))
+        wr64 = formats.activations_to_f64(cfg.xdtype, wr)
+        logits = moe.router_logits(x64, wr64)
+        ids0 = moe.topk(logits, cfg.k)
+        used = sorted(set(ids0.ravel().tolist()) | {a, b})
+        pool = build_pool(L, layer, ex, used, cfg.E)
+        shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
+        layer.forward(1, L.to_device(x), pool, w_router=L.to_device(wr), shared_blob=shared)
+        torch.cuda.synchronize()
+        got_ids = layer.ids[:1].cpu().numpy()
+        got_logits = layer.logits[:1].cpu().numpy().astype(np.float64)
+        sh = ex.f64(cfg.E) if cfg.shared else None
+        ref = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                            experts=ex.f64, shared=sh, w_router=wr64)
+        assert ref["margin"][0] <= TOPK_MARGIN           # the planted near tie
+        n_tie += 1
+        assert set(got_ids[0].tolist()) & {a, b}         # one of the tied pair made the cut
+        scale = np.abs(x64) @ np.abs(wr64).T
+        assert np.all(np.abs(got_logits - ref["logits"]) <= 3e-5 * scale + 1e-6)
+        assert np.array_equal(got_ids, moe.topk(got_logits.astype(np.float32), cfg.k))
+        differ = check_topk_valid(got_ids, ref["logits"], cfg.k, what=f"near tie case {case}")
+        n_differ += len(differ)
+        w_at = moe.gating_weights(ref["logits"], got_ids, cfg.gating, cfg.renormalize)
+        np.testing.assert_allclose(layer.w[:1].cpu().numpy(), w_at, rtol=1e-4, atol=1e-6)
+        want = moe.token_output(x64[0], got_ids[0], w_at[0], ex.f64, sh)[None, :]
+        check_close(out_f64(layer, cfg, 1), want, bf16_out=True, what=f"cfg{cfg_id} near tie case {case}")
+        ex.drop()
+    print(f"NEAR-TIE cfg{cfg_id}: {n_tie} planted ties, {n_differ} with ids other than the oracle's", flush=True)

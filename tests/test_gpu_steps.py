@@ -6,7 +6,7 @@ torch = pytest.importorskip("torch")
 
 import synth
 from oracle import formats, moe
-from tests.helpers import Experts, check_close, route_oracle
+from tests.helpers import Experts, check_close, check_topk_valid, route_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +57,12 @@ def test_route_with_router_gemv(ops, cfg_id, T):
     sure = margin > 1e-4
     assert sure.mean() > 0.9
     got_ids = ids.cpu().numpy()
+    assert np.array_equal(got_ids, moe.topk(lg.astype(np.float32), cfg.k))   # exact on its own logits
     assert np.array_equal(got_ids[sure], ids_ref[sure])
+    differ = check_topk_valid(got_ids, l_ref, cfg.k, what=f"cfg{cfg_id} T={T}")   # near ties: a valid top-k
+    assert set(differ.tolist()) <= set(np.flatnonzero(~sure).tolist())
     w_at = moe.gating_weights(l_ref, got_ids, cfg.gating, cfg.renormalize)
-    np.testing.assert_allclose(w.cpu().numpy()[sure], w_at[sure], rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(w.cpu().numpy(), w_at, rtol=1e-4, atol=1e-6)
 
 
 @pytest.mark.parametrize("gating,renorm,E,k,T", [("sigmoid", False, 256, 6, 8192), ("softmax", True, 128, 8, 333),
@@ -143,9 +146,12 @@ def test_route_permute_with_router(ops, cfg_id, T):
         scale = np.abs(x64) @ np.abs(wr64).T
         assert np.all(np.abs(lg - l_ref) <= 3e-5 * scale + 1e-6)
         sure = margin > 1e-4
+        assert np.array_equal(ids, moe.topk(lg.astype(np.float32), cfg.k))
         assert np.array_equal(ids[sure], ids_ref[sure])
+        differ = check_topk_valid(ids, l_ref, cfg.k, what=f"cfg{cfg_id} T={T} rep {rep}")
+        assert set(differ.tolist()) <= set(np.flatnonzero(~sure).tolist())
         w_at = moe.gating_weights(l_ref, ids, cfg.gating, cfg.renormalize)
-        np.testing.assert_allclose(w[sure], w_at[sure], rtol=1e-4, atol=1e-6)
+        np.testing.assert_allclose(w, w_at, rtol=1e-4, atol=1e-6)
         _check_permutation(ids, off, rows, pos, cfg.E, ids_ref)
 
 
@@ -199,7 +205,8 @@ def test_permute_bit_exact(ops, T, k, E, kind):
 class _FfnRig:
     """Device inputs of one grouped-FFN case built from oracle permutation data."""
 
-    def __init__(self, ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None, skip=None):
+    def __init__(self, ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None, skip=None,
+                 beyond=None):
         from expert_cached_ffn_amd.layer import DTYPES, pack_expert
         self.ops, self.cfg, self.T = ops, cfg, T
         self.with_shared = cfg.shared if with_shared is None else with_shared
@@ -219,6 +226,8 @@ class _FfnRig:
             slot_of[missing] = -1
         if skip is not None:
             slot_of[skip] = -2  # FT_SLOT_SKIP
+        if beyond is not None:
+            slot_of[beyond] = n_slots + 7  # past the end of the pool
         self.x = synth.tokens(cfg, T)
         self.x64 = formats.activations_to_f64(cfg.xdtype, self.x)
         self.shared_blob = dev(pack_expert(lay, ex.raw(cfg.E).arrays)) if self.with_shared else None
@@ -243,11 +252,11 @@ class _FfnRig:
         return formats.bf16_to_f64(b.reshape(n_rows, self.cfg.I))
 
 
-def _ffn_case(ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None, mode=0):
+def _ffn_case(ops, cfg, T, ids, shuffle_slots=True, with_shared=None, missing=None, mode=0, beyond=None):
     """Run the GPU grouped FFN on oracle permutation data; return (gpu y_rows, y_shared, oracle ...).
 
     mode 1 (native MXFP4) is compared with the oracle's native-mode expert."""
-    rig = _FfnRig(ops, cfg, T, ids, shuffle_slots, with_shared, missing)
+    rig = _FfnRig(ops, cfg, T, ids, shuffle_slots, with_shared, missing, beyond=beyond)
     rig.run(mode)
     fn = moe.swiglu_expert_mx if mode == 1 else moe.swiglu_expert
     y_ref = moe.grouped_ffn(rig.x64, cfg.k, rig.off, rig.rows, rig.ex.f64, fn)
@@ -295,13 +304,18 @@ def test_grouped_ffn_parity(ops, name, cfg_id, over, T):
         check_close(ys, ys_ref, what=f"{name} y_shared")
 
 
-@pytest.mark.parametrize("cfg_id,T", [(3, 4), (6, 4), (2, 4), (3, 150)])
-def test_grouped_ffn_missing_slot_gives_nan(ops, cfg_id, T):
-    """A routed expert with no slot: its rows are NaN (decode kernels of every weight format, and the
-    prefill GEMM), the other experts' rows are exact."""
-    cfg = synth.shrink(synth.CONFIGS[cfg_id], H=512, I=512, E=4, k=1, shared=False)
+@pytest.mark.parametrize("cfg_id,T,how", [(3, 4, "missing"), (6, 4, "missing"), (2, 4, "missing"),
+                                         (3, 150, "missing"), (3, 4, "beyond"), (6, 4, "beyond"),
+                                         (2, 4, "beyond"), (3, 150, "beyond"), (2, 150, "beyond"),
+                                         (1, 8, "beyond")])
+def test_grouped_ffn_missing_slot_gives_nan(ops, cfg_id, T, how):
+    """A routed expert with no slot (-1), or with a slot past the end of the pool: nothing is read for
+    it and its rows are NaN (decode kernels of every weight format, the prefill GEMM, the fp32 path);
+    the other experts' rows are exact."""
+    over = dict(E=4, k=1, shared=False) if cfg_id == 1 else dict(H=512, I=512, E=4, k=1, shared=False)
+    cfg = synth.shrink(synth.CONFIGS[cfg_id], **over)
     ids = np.array([[0], [1], [2], [1]] * (T // 4) + [[3]] * (T % 4), np.int32)
-    y, _, y_ref, _, off = _ffn_case(ops, cfg, T, ids, missing=1)
+    y, _, y_ref, _, off = _ffn_case(ops, cfg, T, ids, **{how: 1})
     a, b = int(off[1]), int(off[2])
     assert np.all(np.isnan(y[a:b]))
     keep = np.r_[0:a, b:len(y)]
@@ -454,11 +468,12 @@ def test_grouped_ffn_stages_through_the_workspace(ops, mode):
     check_close(rig.ys.cpu().numpy(), h_in[R:] @ rig.ex.f64(cfg.E)[2].T, what=f"mode {mode} shared down")
 
 
-def test_grouped_ffn_native_mx_missing_slot_gives_nan(ops):
+@pytest.mark.parametrize("how", ["missing", "beyond"])
+def test_grouped_ffn_native_mx_missing_slot_gives_nan(ops, how):
     from tests.helpers import native_mx_expert
     cfg = synth.shrink(synth.CONFIGS[3], H=512, I=512, E=4, k=1, shared=False)
     ids = np.array([[0], [1], [2], [1]], np.int32)
-    rig = _FfnRig(ops, cfg, 4, ids, missing=1)
+    rig = _FfnRig(ops, cfg, 4, ids, **{how: 1})
     rig.run(1)
     y = rig.y.cpu().numpy()
     a, b = int(rig.off[1]), int(rig.off[2])
