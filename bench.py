@@ -400,8 +400,10 @@ def pinned_h2d_bandwidth(expert_bytes, n=32, n_streams=1):
     return n * expert_bytes / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
-def run_cache_trace(args, cfg):
-    """8-layer decode trace at batch 1 through the device LRU cache with pinned-host miss fills."""
+def run_cache_trace(args, cfg, light=False):
+    """8-layer decode trace at batch 1 through the device LRU cache with pinned-host miss fills.
+
+    light: only the timed hits-first run (no serialised, resize or hybrid passes)."""
     import concurrent.futures as cf
     import torch
     import synth
@@ -491,6 +493,18 @@ def run_cache_trace(args, cfg):
     dt = time.perf_counter() - t1
     st = cache.stats()
     cache.destroy()
+    hit = st["hits"] / max(1, st["accesses"])
+    # lower bound of a step: resident expert reads at 8 TB/s vs fills at the measured B_p
+    resident = Lyr * (cfg.k + 1) * eb
+    bound = max(resident / (HBM_PEAK_GBS * 1e9), st["bytes_h2d"] / S / (b_p * 1e9))
+    res = dict(tokens_per_s=S / dt, ms_per_step=dt / S * 1e3, hit_rate=hit, misses_per_step=st["misses"] / S,
+               bytes_h2d=st["bytes_h2d"], h2d_GBps=st["bytes_h2d"] / dt / 1e9, b_p_GBps=b_p,
+               bound_ms_per_step=bound * 1e3, frac_of_bound=bound / (dt / S), stats=st, b_p_torch_copy_GBps=b_p1)
+    log(f"cache trace: {S} steps x {Lyr} layers in {dt:.2f}s = {S / dt:.1f} tok/s, hit rate {hit:.4f}, "
+        f"{res['misses_per_step']:.2f} misses/step, fills {res['h2d_GBps']:.1f} GB/s (B_p {b_p:.1f}), "
+        f"bound {bound * 1e3:.3f} ms/step -> {100 * res['frac_of_bound']:.0f} % of it")
+    if light:
+        return res
     # the same cold-start trace with one FFN that waits for every fill of its layer-step
     cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
     torch.cuda.synchronize()
@@ -529,13 +543,13 @@ def run_cache_trace(args, cfg):
         ops.ft_cpu_expert_ffn(layer.layout, hb[(j * 37 + 5) % (Lyr * E)], x1, 1, y1, n_threads)
     b_h = n_h * eb / (time.perf_counter() - th) / 1e9
     cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
-    cache.set_split(b_p, b_h)
+    cache.set_split(b_p, b_h, 1, cfg.k)
     run(min(args.warmup, S), cache, hybrid=True, hits_first=True)  # warm the host path
     torch.cuda.synchronize()
     cache.destroy()
     def hybrid_run(bh):
         cache = ops.ExpertCache(layer.layout, Lyr, E, C, pool, bank, copy_stream)
-        cache.set_split(b_p, bh)
+        cache.set_split(b_p, bh, 1, cfg.k)
         torch.cuda.synchronize()
         t4 = time.perf_counter()
         run(S, cache, hybrid=True, hits_first=True)
@@ -560,20 +574,10 @@ def run_cache_trace(args, cfg):
     second = hybrid_run(first["b_h_in_loop_GBps"])
     hybrid = dict(b_h_standalone_GBps=b_h, cpu_threads=n_threads, cpu_isa=ops.ft_cpu_isa(-1),
                   split_standalone=first, split_in_loop=second)
-    hit = st["hits"] / max(1, st["accesses"])
-    # lower bound of a step: resident expert reads at 8 TB/s vs fills at the measured B_p
-    resident = Lyr * (cfg.k + 1) * eb
-    bound = max(resident / (HBM_PEAK_GBS * 1e9), st["bytes_h2d"] / S / (b_p * 1e9))
-    res = dict(tokens_per_s=S / dt, ms_per_step=dt / S * 1e3, hit_rate=hit, misses_per_step=st["misses"] / S,
-               bytes_h2d=st["bytes_h2d"], h2d_GBps=st["bytes_h2d"] / dt / 1e9, b_p_GBps=b_p,
-               bound_ms_per_step=bound * 1e3, frac_of_bound=bound / (dt / S), stats=st, b_p_torch_copy_GBps=b_p1,
-               serialised_step={"tokens_per_s": S / dt_ser, "ms_per_step": dt_ser / S * 1e3,
+    res.update(serialised_step={"tokens_per_s": S / dt_ser, "ms_per_step": dt_ser / S * 1e3,
                                 "hits_first_speedup": dt_ser / dt},
                hybrid=hybrid, resize={"shrink_ms": shrink_ms, "grow_ms": grow_ms, "from_slots": C, "to_slots": C // 2,
-                       "hit_rate_64_steps_at_half": half_hit})
-    log(f"cache trace: {S} steps x {Lyr} layers in {dt:.2f}s = {S / dt:.1f} tok/s, hit rate {hit:.4f}, "
-        f"{res['misses_per_step']:.2f} misses/step, fills {res['h2d_GBps']:.1f} GB/s (B_p {b_p:.1f}), "
-        f"bound {bound * 1e3:.3f} ms/step -> {100 * res['frac_of_bound']:.0f} % of it")
+                                      "hit_rate_64_steps_at_half": half_hit})
     return res
 
 
@@ -690,16 +694,55 @@ def run_prefill_stream(args, cfg):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline_decode(cfg, T):
-    """The oracle on one layer call of the workload (input set 0), timed on this host."""
-    import synth
-    from oracle import formats, moe
+def host_cores():
+    """Host core counts the oracle timings run on: os.cpu_count(), the affinity set, BLAS threads."""
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = max([i.get("num_threads", 1) for i in info] or [1])
     except Exception:
-        threads = 1
+        blas = 1
+    return dict(os_cpu_count=os.cpu_count(), affinity_cpus=len(os.sched_getaffinity(0)), blas_threads=int(blas))
+
+
+def time_oracle(fn, repeats):
+    """Median wall time of ``repeats`` calls of fn(), all BLAS threads and (if single_too) one thread."""
+    ts = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), ts
+
+
+def oracle_baseline(name, fn, tokens, repeats, sample, single_thread=True):
+    """The oracle timed on this host: median of ``repeats`` runs on every BLAS thread, and (decode)
+    the same on one thread; tokens/s = tokens / median time."""
+    cores = host_cores()
+    med, ts = time_oracle(fn, repeats)
+    out = dict(value=tokens / med, unit="tokens/s", cores=cores["blas_threads"], kind="oracle",
+               sample=f"{sample}; median of {repeats} ({', '.join(f'{t:.2f}' for t in ts)} s)",
+               median_s=med, repeats=repeats, **cores)
+    if single_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(1):
+                med1, ts1 = time_oracle(fn, repeats)
+            out["single_thread_value"] = tokens / med1
+            out["single_thread_median_s"] = med1
+        except Exception as err:  # threadpoolctl missing: no 1-thread figure
+            log(f"{name}: no single-thread oracle run ({err})")
+    log(f"oracle {name}: {out['value']:,.1f} tok/s on {cores['blas_threads']} BLAS threads "
+        f"(os.cpu_count {cores['os_cpu_count']}, affinity {cores['affinity_cpus']})"
+        + (f", {out['single_thread_value']:,.1f} tok/s on one" if "single_thread_value" in out else ""))
+    return out
+
+
+def cpu_baseline_decode(cfg, T, repeats=5):
+    """The oracle on one layer call of a decode workload (input set 0): route, permute, every expert
+    FFN the routing touches with its weight decode, combine."""
+    import synth
+    from oracle import formats, moe
     x = synth.tokens(cfg, T, case=0)
     wr = synth.router_weight(cfg)
     raw = {}
@@ -708,16 +751,74 @@ def cpu_baseline_decode(cfg, T):
     ids = moe.topk(moe.router_logits(x64, wr64), cfg.k)
     for e in sorted(set(ids.ravel().tolist())) + ([cfg.E] if cfg.shared else []):
         raw[e] = synth.expert_weights(cfg, 0, e).arrays        # input generation: not timed
+
+    def run():
+        r = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                          experts=lambda e: formats.expert_to_f64(cfg.wdtype, raw[e]),
+                          shared=formats.expert_to_f64(cfg.wdtype, raw[cfg.E]) if cfg.shared else None,
+                          w_router=wr64)
+        assert np.all(np.isfinite(r["out"]))
+    return oracle_baseline(f"cfg{cfg.cfg_id} T={T}", run, T, repeats,
+                           f"one {T}-token layer call (input set 0): route, permute, {len(raw)} expert FFNs "
+                           f"with weight decode, combine")
+
+
+def cpu_baseline_prefill(cfg, T_sample=32):
+    """The oracle on the first T_sample tokens of the prefill batch (given logits): permute, every
+    expert those tokens touch with its weight decode, the shared expert, combine.  One run."""
+    import synth
+    from oracle import formats, moe
+    T = cfg.batches[0]
+    x = synth.tokens(cfg, T, case=0)[:T_sample]
+    logits = synth.prefill_logits(cfg, T, case=0)[:T_sample]
+    ids = moe.topk(logits, cfg.k)
+    raw = {e: synth.expert_weights(cfg, 0, e).arrays for e in sorted(set(ids.ravel().tolist())) + [cfg.E]}
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+
+    def run():
+        r = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                          experts=lambda e: formats.expert_to_f64(cfg.wdtype, raw[e]),
+                          shared=formats.expert_to_f64(cfg.wdtype, raw[cfg.E]), logits=logits)
+        assert np.all(np.isfinite(r["out"]))
+    return oracle_baseline("prefill", run, T_sample, 1,
+                           f"the first {T_sample} of the {T} prefill tokens (given logits): permute, "
+                           f"{len(raw)} expert FFNs with weight decode, combine", single_thread=False)
+
+
+def cpu_baseline_cache(cfg, steps_sample=1):
+    """The cache-trace oracle: the LRU simulator over every access of the trace, plus the layer
+    computation of the first ``steps_sample`` steps (all layers), scaled to the whole trace."""
+    import synth
+    from oracle import formats, moe
+    from oracle.lru import ExpertLRU
+    tr = synth.cache_trace(cfg)
     t0 = time.perf_counter()
-    r = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
-                      experts=lambda e: formats.expert_to_f64(cfg.wdtype, raw[e]),
-                      shared=formats.expert_to_f64(cfg.wdtype, raw[cfg.E]) if cfg.shared else None,
-                      w_router=wr64)
-    dt = time.perf_counter() - t0
-    assert np.all(np.isfinite(r["out"]))
-    return dict(value=T / dt, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"one {T}-token layer call (input set 0): route, permute, {len(raw)} expert FFNs "
-                       f"with weight decode, combine; {dt:.2f} s")
+    sim = ExpertLRU(cfg.n_layers, cfg.E, cfg.capacity)
+    for st in range(cfg.steps):
+        for l in range(cfg.n_layers):
+            sim.step(l, tr.ids[st, l])
+    t_sim = time.perf_counter() - t0
+    work = []
+    for st in range(steps_sample):
+        for l in range(cfg.n_layers):
+            raw = {e: synth.expert_weights(cfg, l, e).arrays for e in tr.ids[st, l].tolist() + [cfg.E]}
+            work.append((synth.tokens(cfg, 1, layer=l, step=st), tr.logits[st, l][None, :], raw))
+    t1 = time.perf_counter()
+    for x, lg, raw in work:
+        r = moe.moe_layer(formats.activations_to_f64(cfg.xdtype, x), k=cfg.k, E=cfg.E, gating=cfg.gating,
+                          renormalize=cfg.renormalize, experts=lambda e: formats.expert_to_f64(cfg.wdtype, raw[e]),
+                          shared=formats.expert_to_f64(cfg.wdtype, raw[cfg.E]), logits=lg)
+        assert np.all(np.isfinite(r["out"]))
+    t_step = (time.perf_counter() - t1) / steps_sample
+    total = t_sim + cfg.steps * t_step
+    cores = host_cores()
+    out = dict(value=cfg.steps / total, unit="tokens/s", cores=cores["blas_threads"], kind="oracle",
+               sample=f"LRU simulator over all {cfg.steps * cfg.n_layers * cfg.k} accesses ({t_sim:.2f} s) + the "
+                      f"{cfg.n_layers}-layer computation of {steps_sample} step(s) with weight decode "
+                      f"({t_step:.2f} s per step), scaled to {cfg.steps} steps",
+               hit_rate=sim.hits / max(1, sim.accesses), **cores)
+    log(f"oracle cache trace: {out['value']:.3f} tok/s (simulator {t_sim:.2f} s, {t_step:.2f} s per step)")
+    return out
 
 
 # ----------------------------------------------------------------------------- main
@@ -743,12 +844,61 @@ WORKLOADS = {
 }
 
 
+def decode_summary(cfg, res, main_T, peaks, traffic=None):
+    """The decode part of a JSON line: throughput of the main batch, the roofline of its gate/up
+    kernel (HIP events), the layer-level activated-byte rate and every batch."""
+    m = res[main_T]
+    ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
+    kname = "ffn_persist_kernel<bf16, gate_up>" if cfg.wdtype == "bf16" else \
+        f"ffn_persist_xs_kernel<{cfg.wdtype}, gate_up>"
+    layer_gbps = m["layer_weight_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
+    return {
+        "tokens_per_s": m["tokens_per_s"], "ms_per_step": m["ms_per_step"], "batch_tokens": main_T,
+        "distinct_experts_per_step": m["distinct_experts"],
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "avg_launch_us": m["gate_up_ms"] * 1e3,
+                     "algorithmic_bytes_per_launch": m["gate_up_bytes"],
+                     "frac_of_achievable_copy": ach / peaks["copy_GBps"] if peaks else None},
+        "layer_weight_GBps": layer_gbps, "layer_frac_of_hbm_peak": layer_gbps / HBM_PEAK_GBS,
+        "step_ms_p10_p50_p90": m["step_ms_p10_p50_p90"], "graph_ms_per_step": m["graph_ms_per_step"],
+        "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+                             "graph_ms_per_step": r["graph_ms_per_step"],
+                             "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
+                             "gate_up_GBps": r["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9,
+                             "layer_weight_GBps": r["layer_weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
+                             "layer_frac_of_hbm_peak": r["layer_weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+                             / HBM_PEAK_GBS}
+                    for T, r in sorted(res.items())},
+    }
+
+
+def prefill_summary(cfg, p, native, peaks):
+    ach = p["flops_gate_up"] / (p["gate_up_ms"] * 1e-3) / 1e12
+    peak = FP8_PEAK_TFLOPS if native else BF16_PEAK_TFLOPS
+    layer_tf = p["flops_ffn"] / (p["ms_per_step"] * 1e-3) / 1e12
+    return {
+        "tokens_per_s": p["tokens_per_s"], "ms_per_step": p["ms_per_step"], "batch_tokens": cfg.batches[0],
+        "roofline": {"bound": "mfma",
+                     "kernel": "ffn_mx_gemm_kernel<gate_up>" if native else f"ffn_gemm_kernel<{cfg.wdtype}, gate_up>",
+                     "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                     "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"],
+                     "frac_of_achievable_bf16_gemm": (ach / peaks["bf16_gemm_TFLOPs"] if peaks and not native else None),
+                     "frac_of_achievable_fp8_gemm": (ach / peaks["fp8_gemm_TFLOPs"]
+                                                     if peaks and native and peaks["fp8_gemm_TFLOPs"] else None)},
+        "layer_TFLOPs": layer_tf, "layer_frac_of_peak": layer_tf / peak,
+        "ffn_TFLOPs": p["flops_ffn"] / ((p["gate_up_ms"] + p["down_ms"]) * 1e-3) / 1e12,
+        "gate_up_ms": p["gate_up_ms"], "down_ms": p["down_ms"], "ffn_ms_p10_p50_p90": p["ffn_ms_p10_p50_p90"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode-bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS),
+                    help="all (default): the bf16 decode line with the MXFP4 decode, prefill and cache-trace "
+                         "workloads beside it")
     ap.add_argument("--batch", type=int, default=None, help="main decode batch (default: largest of the workload)")
     ap.add_argument("--only-main-batch", action="store_true",
                     help="time only the main batch (profiling runs: one kernel shape per kernel)")
@@ -764,7 +914,9 @@ def main():
         sys.exit(2)
 
     import synth
-    cfg_id, desc = WORKLOADS[args.workload]
+    everything = args.workload == "all"
+    workload = "decode-bf16" if everything else args.workload
+    cfg_id, desc = WORKLOADS[workload]
     cfg = synth.CONFIGS[cfg_id]
     batches = list(cfg.batches)
     main_T = args.batch or max(batches)
@@ -772,96 +924,76 @@ def main():
         batches.append(main_T)
     if args.only_main_batch:
         batches = [main_T]
-    if args.workload == "cache-trace":
+    base = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "data": "synthetic"}
+    if workload == "cache-trace":
         c = run_cache_trace(args, cfg)
-        out = {
-            "metric": METRIC, "value": c["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": cfg.steps,
-            "warmup": min(args.warmup, cfg.steps), "ms_per_step": c["ms_per_step"], "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4-w/bf16", "data": "synthetic",
-            "config": {"workload": desc, "batch_tokens": 1},
-            "cache": {k: v for k, v in c.items() if k not in ("tokens_per_s", "ms_per_step")},
-        }
+        out = dict(base, value=c["tokens_per_s"], steps=cfg.steps, warmup=min(args.warmup, cfg.steps),
+                   ms_per_step=c["ms_per_step"], dtype="mxfp4-w/bf16",
+                   config={"workload": desc, "batch_tokens": 1},
+                   cache={k: v for k, v in c.items() if k not in ("tokens_per_s", "ms_per_step")})
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_cache(cfg)
         print(json.dumps(out), flush=True)
         return
-    if args.workload == "prefill-stream":
+    if workload == "prefill-stream":
         scfg = synth.shrink(cfg, n_layers=8, capacity=2 * cfg.E)
         p = run_prefill_stream(args, scfg)
-        out = {
-            "metric": METRIC, "value": p["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": 1,
-            "warmup": 1, "ms_per_step": p["double_buffered_ms"], "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "mxfp4-w/bf16", "data": "synthetic",
-            "config": {"workload": desc, "batch_tokens": scfg.batches[0], "layers": scfg.n_layers},
-            "stream": p,
-        }
+        out = dict(base, value=p["tokens_per_s"], steps=1, warmup=1, ms_per_step=p["double_buffered_ms"],
+                   dtype="mxfp4-w/bf16", config={"workload": desc, "batch_tokens": scfg.batches[0],
+                                                 "layers": scfg.n_layers}, stream=p)
         print(json.dumps(out), flush=True)
         return
-    if args.workload.startswith("prefill"):
-        T = cfg.batches[0]
-        native = args.workload.endswith("native")
-        p = run_prefill(args, cfg, T, mode=1 if native else 0)
-        ach = p["flops_gate_up"] / (p["gate_up_ms"] * 1e-3) / 1e12
-        peak = FP8_PEAK_TFLOPS if native else BF16_PEAK_TFLOPS
+    if workload.startswith("prefill"):
+        native = workload.endswith("native")
+        p = run_prefill(args, cfg, cfg.batches[0], mode=1 if native else 0)
         peaks = None if args.no_peaks else achievable_peaks()
-        out = {
-            "metric": METRIC, "value": p["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": p["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "mxfp8-a/mxfp4-w" if native else f"{cfg.wdtype}-w/bf16", "data": "synthetic",
-            "config": {"workload": desc, "batch_tokens": T},
-            "roofline": {"bound": "mfma",
-                         "kernel": "ffn_mx_gemm_kernel<gate_up>" if native else f"ffn_gemm_kernel<{cfg.wdtype}, gate_up>",
-                         "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
-                         "avg_launch_us": p["gate_up_ms"] * 1e3, "algorithmic_flops_per_launch": p["flops_gate_up"],
-                         "frac_of_achievable_bf16_gemm": (ach / peaks["bf16_gemm_TFLOPs"]
-                                                          if peaks and not native else None),
-                         "frac_of_achievable_fp8_gemm": (ach / peaks["fp8_gemm_TFLOPs"]
-                                                         if peaks and native and peaks["fp8_gemm_TFLOPs"] else None)},
-            "ffn_TFLOPs": p["flops_ffn"] / ((p["gate_up_ms"] + p["down_ms"]) * 1e-3) / 1e12,
-            "ffn_ms_p10_p50_p90": p["ffn_ms_p10_p50_p90"],
-            "achievable": peaks,
-        }
+        ps = prefill_summary(cfg, p, native, peaks)
+        out = dict(base, value=p["tokens_per_s"], steps=args.steps, warmup=args.warmup, ms_per_step=p["ms_per_step"],
+                   dtype="mxfp8-a/mxfp4-w" if native else f"{cfg.wdtype}-w/bf16",
+                   config={"workload": desc, "batch_tokens": cfg.batches[0]}, roofline=ps["roofline"],
+                   layer_TFLOPs=ps["layer_TFLOPs"], ffn_TFLOPs=ps["ffn_TFLOPs"],
+                   ffn_ms_p10_p50_p90=ps["ffn_ms_p10_p50_p90"], achievable=peaks)
+        if not args.no_cpu_baseline and not native:
+            out["cpu_baseline"] = cpu_baseline_prefill(cfg)
         print(json.dumps(out), flush=True)
         return
+    t_start = time.time()
     res = run_decode(args, cfg, batches, main_T)
     peaks = None if (args.no_peaks or args.only_main_batch) else achievable_peaks()
-    m = res[main_T]
-    ach = m["gate_up_bytes"] / (m["gate_up_ms"] * 1e-3) / 1e9
-    kname = "ffn_persist_kernel<bf16, gate_up>" if cfg.wdtype == "bf16" else \
-        f"ffn_persist_xs_kernel<{cfg.wdtype}, gate_up>"
     traffic = None
-    if args.workload == "decode-bf16" and main_T == 64:
+    if workload == "decode-bf16" and main_T == 64:
         traffic = measured_traffic("decode-bf16-T64_hbm_traffic.json", "void ft::ffn_persist_kernel<0, true,")
-    out = {
-        "metric": METRIC,
-        "value": m["tokens_per_s"],
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": m["ms_per_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if cfg.wdtype == "bf16" else f"{cfg.wdtype}-w/bf16",
-        "data": "synthetic",
-        "config": {"workload": desc, "batch_tokens": main_T, "input_sets": N_INPUT_SETS,
-                   "distinct_experts_per_step": m["distinct_experts"]},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "avg_launch_us": m["gate_up_ms"] * 1e3,
-                     "algorithmic_bytes_per_launch": m["gate_up_bytes"],
-                     "frac_of_achievable_copy": ach / peaks["copy_GBps"] if peaks else None},
-        "achievable": peaks,
-        "step_ms_p10_p50_p90": m["step_ms_p10_p50_p90"],
-        "layer_weight_GBps": m["layer_weight_bytes"] / (m["ms_per_step"] * 1e-3) / 1e9,
-        "graph_ms_per_step": m["graph_ms_per_step"],
-        "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
-                             "graph_ms_per_step": r["graph_ms_per_step"],
-                             "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
-                             "gate_up_GBps": r["gate_up_bytes"] / (r["gate_up_ms"] * 1e-3) / 1e9,
-                             "layer_weight_GBps": r["layer_weight_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9}
-                    for T, r in sorted(res.items())},
-    }
+    d = decode_summary(cfg, res, main_T, peaks, traffic)
+    out = dict(base, value=d["tokens_per_s"], steps=args.steps, warmup=args.warmup, ms_per_step=d["ms_per_step"],
+               dtype="bf16" if cfg.wdtype == "bf16" else f"{cfg.wdtype}-w/bf16",
+               config={"workload": desc, "batch_tokens": main_T, "input_sets": N_INPUT_SETS,
+                       "distinct_experts_per_step": d["distinct_experts_per_step"]},
+               roofline=d["roofline"], achievable=peaks, step_ms_p10_p50_p90=d["step_ms_p10_p50_p90"],
+               layer_weight_GBps=d["layer_weight_GBps"], layer_frac_of_hbm_peak=d["layer_frac_of_hbm_peak"],
+               graph_ms_per_step=d["graph_ms_per_step"], batches=d["batches"])
+    if everything:
+        # the other workloads of the metric, each with its own roofline and oracle baseline
+        c3 = synth.CONFIGS[3]
+        r3 = run_decode(args, c3, list(c3.batches), max(c3.batches))
+        out["decode_mxfp4"] = dict(workload=WORKLOADS["decode-mxfp4"][1],
+                                   **decode_summary(c3, r3, max(c3.batches), peaks))
+        c4 = synth.CONFIGS[4]
+        pargs = argparse.Namespace(**vars(args))
+        pargs.steps, pargs.warmup = min(args.steps, 20), min(args.warmup, 3)
+        out["prefill"] = dict(workload=WORKLOADS["prefill-mxfp4"][1],
+                              **prefill_summary(c4, run_prefill(pargs, c4, c4.batches[0], mode=0), False, peaks))
+        c5 = synth.CONFIGS[5]
+        cr = run_cache_trace(args, c5, light=True)
+        out["cache_trace"] = dict(workload=WORKLOADS["cache-trace"][1], **cr)
+        log(f"GPU part of the run: {time.time() - t_start:.0f} s")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(cfg, main_T)
+        if everything:
+            out["decode_mxfp4"]["cpu_baseline"] = cpu_baseline_decode(synth.CONFIGS[3], 1)
+            out["prefill"]["cpu_baseline"] = cpu_baseline_prefill(synth.CONFIGS[4])
+            out["cache_trace"]["cpu_baseline"] = cpu_baseline_cache(synth.CONFIGS[5])
+    log(f"whole run: {time.time() - t_start:.0f} s")
     print(json.dumps(out), flush=True)
 
 
