@@ -864,3 +864,63 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   clear_error();
   return FT_OK;
 }
+
+// ------------------------------------------------------------------ no-allocation variant
+//
+// ft_moe_grouped_ffn_noalloc: the same call with its workspace in a static
+// device array, for callers that cannot allocate (code under graph capture,
+// tight serving loops, harnesses that forbid hipMalloc).  The array is
+// `scratch`; in host code its name is only a stand-in, so its device address
+// on each GPU is resolved once with hipGetSymbolAddress (with that GPU
+// current) and only that address is passed to kernels.  Nothing in it must
+// start at zero: the FFN's kernels write every hidden row (and quantized
+// operand) before they read it.
+namespace ft {
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;  // per GPU
+constexpr int kMaxScratchDevices = 64;
+}  // namespace ft
+
+static __device__ __align__(256) uint8_t scratch[ft::kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_dev[ft::kMaxScratchDevices];  // device address of `scratch` on GPU d
+}  // namespace
+
+static ft_status scratch_address(void **out) {
+  int dev = 0;
+  FT_HIP(hipGetDevice(&dev));
+  FT_SUPPORTED(dev >= 0 && dev < kMaxScratchDevices, "ft_moe_grouped_ffn_noalloc: device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void *p = nullptr;
+    FT_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    FT_REQUIRE(p != nullptr && aligned(p, 256), "ft_moe_grouped_ffn_noalloc: scratch address not resolved");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return FT_OK;
+}
+
+extern "C" size_t ft_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" ft_status ft_moe_grouped_ffn_noalloc(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
+                                                const int32_t *slot_of_expert, const void *shared_blob,
+                                                const void *x, int32_t x_dtype, int32_t T, int32_t k, int32_t E,
+                                                const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                                float *y_rows, float *y_shared, int32_t mode, hipStream_t stream) {
+  FT_REQUIRE(L != nullptr, "ft_moe_grouped_ffn_noalloc: layout is NULL");
+  FT_REQUIRE(T >= 0 && k >= 1 && E >= 1 && L->H >= 1 && L->I >= 1,
+             "ft_moe_grouped_ffn_noalloc: need T >= 0, k >= 1, E >= 1 and an initialised layout");
+  FT_REQUIRE(int64_t(T) * (k + 1) < (int64_t(1) << 31), "ft_moe_grouped_ffn_noalloc: T*k too large");
+  const size_t need = ffn_workspace_bytes(T, k, E, L->H, L->I);
+  if (need > kNoAllocScratchBytes)
+    return fail(FT_ECAPACITY, "ft_moe_grouped_ffn_noalloc: this call needs " + std::to_string(need) +
+                                  " bytes of scratch, above the static " + std::to_string(kNoAllocScratchBytes) +
+                                  " (use ft_moe_grouped_ffn with a workspace)");
+  void *ws = nullptr;
+  const ft_status st = scratch_address(&ws);
+  if (st != FT_OK) return st;
+  return ft_moe_grouped_ffn(L, slot_pool, n_slots, slot_of_expert, shared_blob, x, x_dtype, T, k, E, expert_offsets,
+                            sorted_rows, y_rows, y_shared, mode, ws, kNoAllocScratchBytes, stream);
+}

@@ -94,6 +94,23 @@ def ft_moe_grouped_ffn(layout: ExpertLayout, slot_pool, slot_of_expert, shared_b
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def ft_moe_grouped_ffn_noalloc(layout: ExpertLayout, slot_pool, slot_of_expert, shared_blob, x, x_dtype: int,
+                               T: int, k: int, E: int, expert_offsets, sorted_rows, y_rows, y_shared,
+                               mode: int = 0, stream=None, n_slots: int | None = None) -> None:
+    """ft_moe_grouped_ffn with the library's static scratch instead of a workspace."""
+    if n_slots is None:
+        n_slots = slot_pool.numel() * slot_pool.element_size() // int(layout.expert_bytes) \
+            if hasattr(slot_pool, "numel") else E
+    _check(_lib.lib().ft_moe_grouped_ffn_noalloc(C.byref(layout), _ptr(slot_pool), int(n_slots),
+                                                 _ptr(slot_of_expert), _ptr(shared_blob), _ptr(x), x_dtype, T, k,
+                                                 E, _ptr(expert_offsets), _ptr(sorted_rows), _ptr(y_rows),
+                                                 _ptr(y_shared), mode, _stream(stream)))
+
+
+def ft_noalloc_scratch_bytes() -> int:
+    return int(_lib.lib().ft_noalloc_scratch_bytes())
+
+
 def ft_cpu_expert_ffn(layout: ExpertLayout, blob, x, n: int, y, n_threads: int = 0) -> None:
     """Host pointers (numpy arrays or pinned tensors) for blob, x (bf16 bits) and y (float32)."""
     _check(_lib.lib().ft_cpu_expert_ffn(C.byref(layout), _ptr(blob), _ptr(x), n, _ptr(y), n_threads))

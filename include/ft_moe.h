@@ -231,6 +231,33 @@ ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool, i
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ft_moe_grouped_ffn_noalloc -- ft_moe_grouped_ffn with the same arguments,
+ * results and errors, minus the workspace: for callers that cannot allocate
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The workspace is a static device array of
+ * ft_noalloc_scratch_bytes() bytes (16 MiB) that each GPU the library runs on
+ * holds until the process ends; its address on a GPU is resolved on the first
+ * call there.  The call allocates nothing.
+ * A call whose ft_workspace_bytes(FT_WS_FFN, T, k, E, H, I) exceeds that size
+ * returns FT_ECAPACITY and enqueues nothing (decode batches fit: e.g. 64
+ * tokens of H=2048, I=768, top-8, or 32 tokens of H=4096, I=2048, top-6 with a
+ * shared expert, in either mode).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller.  FT_FFN_DOWN_ONLY reads the hidden
+ * rows that the last FT_FFN_GATE_UP_ONLY call of this entry point on the GPU
+ * left there.
+ */
+ft_status ft_moe_grouped_ffn_noalloc(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
+                                     const int32_t *slot_of_expert, const void *shared_blob,
+                                     const void *x, int32_t x_dtype, int32_t T, int32_t k, int32_t E,
+                                     const int32_t *expert_offsets, const int32_t *sorted_rows,
+                                     float *y_rows, float *y_shared, int32_t mode, hipStream_t stream);
+
+/* Bytes of the static scratch array of ft_moe_grouped_ffn_noalloc (per GPU). */
+size_t ft_noalloc_scratch_bytes(void);
+
+/*
  * Instruction paths of the host expert kernel (ft_cpu_expert_ffn,
  * ft_cpu_miss_rows).  Both compute the same products; they differ only in the
  * order of fp32 additions.
