@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "FT_OK", -1: "FT_EINVAL", -2: "FT_ENOTSUP", -3: "FT_ECAPACITY
 # dtypes / gating / workspace selectors
 FT_F32, FT_BF16, FT_MXFP4, FT_NVFP4 = 0, 1, 2, 3
 FT_SOFTMAX, FT_SIGMOID = 0, 1
-FT_WS_PERMUTE, FT_WS_FFN, FT_WS_ROUTE_PERMUTE = 1, 2, 3
+FT_WS_PERMUTE, FT_WS_FFN, FT_WS_ROUTE_PERMUTE, FT_WS_LAYER = 1, 2, 3, 4
 FT_FFN_EXACT, FT_FFN_NATIVE_MX = 0, 1
 FT_SLOT_SKIP = -2
 FT_CPU_ISA_QUERY, FT_CPU_ISA_BEST, FT_CPU_AVX2, FT_CPU_AVX512_BF16 = -1, 0, 1, 2
@@ -29,7 +29,7 @@ EXPORTS = [
     "ft_expert_cache_cpu_misses", "ft_cpu_expert_ffn", "ft_cpu_miss_rows", "ft_cpu_isa",
     "ft_expert_cache_stage_cpu_misses", "ft_expert_cache_run_cpu_misses", "ft_expert_cache_step_split",
     "ft_expert_cache_wait_fills", "ft_expert_cache_plan", "ft_expert_cache_fill", "ft_expert_cache_set_trace",
-    "ft_moe_grouped_ffn_noalloc", "ft_noalloc_scratch_bytes",
+    "ft_moe_grouped_ffn_noalloc", "ft_noalloc_scratch_bytes", "ft_moe_layer",
 ]
 
 
@@ -82,6 +82,9 @@ def lib() -> C.CDLL:
     L.ft_moe_grouped_ffn.restype = i32
     L.ft_moe_grouped_ffn.argtypes = [C.POINTER(ExpertLayout), p, i32, p, p, p, i32, i32, i32, i32, p, p, p, p,
                                      i32, p, sz, p]
+    L.ft_moe_layer.restype = i32
+    L.ft_moe_layer.argtypes = [C.POINTER(ExpertLayout), p, i32, p, p, p, i32, p, p, i32, i32, i32, i32, i32,
+                               p, p, p, p, p, p, p, i32, i32, p, p, sz, p]
     L.ft_moe_grouped_ffn_noalloc.restype = i32
     L.ft_moe_grouped_ffn_noalloc.argtypes = [C.POINTER(ExpertLayout), p, i32, p, p, p, i32, i32, i32, i32, p, p,
                                              p, p, i32, p]

@@ -86,6 +86,10 @@ extern "C" size_t ft_workspace_bytes(int32_t which, int32_t T, int32_t k, int32_
       return ft::ffn_workspace_bytes(T, k, E, H, I);
     case FT_WS_ROUTE_PERMUTE:
       return ft::permute_workspace_bytes(T, k, E);
+    case FT_WS_LAYER: {  // the one-token kernel's wait words, then the permutation's counts or the FFN's rows
+      const size_t a = ft::permute_workspace_bytes(T, k, E), b = ft::ffn_workspace_bytes(T, k, E, H, I);
+      return ft::kLayerWaitBytes + (a > b ? a : b);
+    }
     default:
       return 0;
   }

@@ -20,6 +20,8 @@
 #include "ft_internal.hpp"
 #include "stream_gemm.hpp"
 #include "stream_persist.hpp"
+#include "stream_combine.hpp"
+#include "gemv_token.hpp"
 #include "gemm_prefill.hpp"
 #include "gemm_mx.hpp"
 
@@ -368,6 +370,208 @@ static bool launch_persist(const PersistArgs &a, int max_units, hipStream_t stre
   return false;
 }
 
+// ------------------------------------------------------------------ fused layer call (a few tokens)
+
+// Gate/up of the fused layer call: routing prologue, then the x-stationary
+// weight stream (rows per tile in a.tile_rows).
+template <int WF, int WAVES, int KPW>
+__global__ __launch_bounds__(WAVES * 64) void ffn_route_gate_up_kernel(PersistArgs a) {
+  __shared__ float s_red[WAVES * 2 * 256];
+  constexpr int NB = FT_XS_NB(WF, true, WAVES, KPW);
+  stream_persist_xs<WF, true, WAVES, KPW, NB, 1, true>(a, s_red);
+}
+
+// Down projection with the combine folded in.  Register sets per step: bf16
+// 32 VGPRs (weights + hidden row), MXFP4 42, NVFP4 22 at one k-block per wave.
+template <int WF, int WAVES, int KPW>
+__global__ __launch_bounds__(WAVES * 64) void ffn_down_combine_kernel(PersistArgs a) {
+  __shared__ float s_red[WAVES * 256];
+  constexpr int NB = KPW == 2 ? 2 : (WF == WF_FP4 ? 3 : 4);
+  stream_combine_xs<WF, WAVES, KPW, NB>(a, s_red);
+}
+
+// The persistent shape of the fused kernels for a contraction of nkb k-blocks
+// (the decode path's choice; NVFP4 gate/up as 16 waves x 1), or false.
+template <int WF>
+static bool fused_shape(bool glu, int nkb, int *waves, int *kpw) {
+  persist_shape(nkb, waves, kpw);
+  if (WF == WF_NV4 && glu && *waves == 8 && *kpw == 2) {
+    *waves = 16;
+    *kpw = 1;
+  }
+  return *waves > 0 && !(*waves == 16 && !glu);
+}
+
+// Rows per tile (16 or 8) that finish `units16` 16-row units soonest on `grid`
+// workgroups: ceil(units / grid) * rows, ties to 16.
+// FTMOE_FUSED_TR = "8" or "16" forces the choice (tuning measurements).
+static int tile_rows_for(int units16, int grid) {
+  static const char *env = getenv("FTMOE_FUSED_TR");
+  if (env && (env[0] == '8' || (env[0] == '1' && env[1] == '6'))) return env[0] == '8' ? 8 : 16;
+  // 8-row tiles only when they at least halve the time in rows streamed (measured: at equal cost the
+  // extra per-tile reductions made them slower)
+  const int t16 = cdiv(units16, grid) * 16, t8 = cdiv(2 * units16, grid) * 8;
+  return 2 * t8 <= t16 ? 8 : 16;
+}
+
+template <int WF, bool GLU>
+static ft_status launch_fused(PersistArgs a, int units16, int groups, hipStream_t stream) {
+  int waves = 0, kpw = 0;
+  if (!fused_shape<WF>(GLU, a.K / stream_kblock<WF>(), &waves, &kpw))
+    return fail(FT_ENOTSUP, "ft_moe_layer: no fused kernel for this contraction length");
+#define FT_FUSED(W, C)                                                                                     \
+  if (waves == W && kpw == C) {                                                                           \
+    const void *kern = nullptr;                                                                           \
+    if constexpr (GLU)                                                                                    \
+      kern = reinterpret_cast<const void *>(&ffn_route_gate_up_kernel<WF, W, C>);                         \
+    else                                                                                                  \
+      kern = reinterpret_cast<const void *>(&ffn_down_combine_kernel<WF, W, C>);                          \
+    const int rg = resident_grid(kern, W * 64);                                                           \
+    a.tile_rows = tile_rows_for(units16, rg);                                                             \
+    a.n_tiles = cdiv(a.N, a.tile_rows);                                                                   \
+    const int g = std::max(1, std::min(units16 * (16 / a.tile_rows) * groups, rg));                        \
+    if constexpr (GLU)                                                                                    \
+      hipLaunchKernelGGL((ffn_route_gate_up_kernel<WF, W, C>), dim3(g), dim3(W * 64), 0, stream, a);      \
+    else                                                                                                  \
+      hipLaunchKernelGGL((ffn_down_combine_kernel<WF, W, C>), dim3(g), dim3(W * 64), 0, stream, a);       \
+    FT_LAUNCHED((GLU ? "ffn_route_gate_up_kernel" : "ffn_down_combine_kernel"));                           \
+    return FT_OK;                                                                                         \
+  }
+  if constexpr (WF == WF_NV4 && GLU) FT_FUSED(16, 1)
+  FT_FUSED(8, 2)
+  FT_FUSED(12, 1)
+  FT_FUSED(8, 1)
+  FT_FUSED(6, 1)
+  FT_FUSED(4, 1)
+#undef FT_FUSED
+  return fail(FT_ENOTSUP, "ft_moe_layer: no fused kernel for this persistent shape");
+}
+
+// ------------------------------------------------------------------ one-token layer call (GEMV)
+
+template <int WF, int NCH, int RPW>
+__global__ __launch_bounds__(kGemvGuThreads) __attribute__((amdgpu_waves_per_eu(2))) void ffn_token_gate_up_kernel(
+    PersistArgs a) {
+  gemv_gate_up<WF, NCH, RPW>(a);
+}
+
+template <int WF, int NCH, int RPW, int NCHD, int RB>
+__global__ __launch_bounds__(kGemvGuThreads) __attribute__((amdgpu_waves_per_eu(2))) void ffn_token_layer_kernel(
+    PersistArgs a, PersistArgs d, uint32_t *wait_words) {
+  gemv_gate_up<WF, NCH, RPW, NCHD, RB>(a, &d, wait_words);
+}
+
+template <int WF, int NCH, int RPW, int SPW>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(2))) void ffn_token_down_combine_kernel(
+    PersistArgs a) {
+  gemv_down_combine<WF, NCH, RPW, SPW>(a);
+}
+
+// Code bytes of one weight row of K elements.
+template <int WF>
+static int row_code_bytes(int K) { return WF == WF_BF16 ? 2 * K : K / 2; }
+
+// 1 KiB chunks per row rounded up to 1, 2 or 4 (0: rows longer than 4 KiB).
+static int gemv_chunks(int row_bytes) {
+  const int c = cdiv(row_bytes, 1024);
+  return c <= 1 ? 1 : (c <= 2 ? 2 : (c <= 4 ? 4 : 0));
+}
+
+// The one-token kernels cover this layer: routing limits of the prologue, rows of at most
+// 4 KiB of codes, at most 12 down steps (k routed + shared; 3 per wave).
+template <int WF>
+static bool token_gemv_covers(int H, int I, int E, int k, bool shared) {
+  return E <= kRouteMaxE && k <= kFusedMaxK && k + (shared ? 1 : 0) <= 12 && gemv_chunks(row_code_bytes<WF>(H)) > 0 &&
+         gemv_chunks(row_code_bytes<WF>(I)) > 0;
+}
+
+// The one-launch layer kernel for gate/up chunks C, down chunks CD: rows per down block 4, or 8
+// where 4-row blocks would outnumber the workgroups that fit (not with 4-chunk down rows, whose
+// 8-row blocks do not fit in registers; there workgroups take several blocks); the grid is at most
+// the workgroups that fit at once (the grid-wide wait needs them all resident).
+template <int WF, int C, int R, int CD, int RB>
+static void launch_token_layer_rb(const PersistArgs &p1, const PersistArgs &p2, uint32_t *wait_words, int grid,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL((ffn_token_layer_kernel<WF, C, R, CD, RB>), dim3(grid), dim3(kGemvGuThreads), 0, stream, p1, p2,
+                     wait_words);
+}
+
+template <int WF, int C, int R, int CD>
+static void launch_token_layer(const PersistArgs &p1, const PersistArgs &p2, uint32_t *wait_words, int jobs,
+                               hipStream_t stream) {
+  const int r4 = resident_grid(reinterpret_cast<const void *>(&ffn_token_layer_kernel<WF, C, R, CD, 4>),
+                               kGemvGuThreads);
+  const int want = cdiv(jobs, kGemvGuThreads / 64);
+  if constexpr (CD < 4) {
+    if (cdiv(p2.N, 4) > r4) {
+      const int r8 = resident_grid(reinterpret_cast<const void *>(&ffn_token_layer_kernel<WF, C, R, CD, 8>),
+                                   kGemvGuThreads);
+      launch_token_layer_rb<WF, C, R, CD, 8>(p1, p2, wait_words, std::max(1, std::min(r8, std::max(want, cdiv(p2.N, 8)))),
+                                             stream);
+      return;
+    }
+  }
+  launch_token_layer_rb<WF, C, R, CD, 4>(p1, p2, wait_words, std::max(1, std::min(r4, std::max(want, cdiv(p2.N, 4)))),
+                                         stream);
+}
+
+template <int WF>
+static ft_status launch_token_gemv(const PersistArgs &p1, const PersistArgs &p2, uint32_t *wait_words,
+                                   hipStream_t stream) {
+  // gate/up: 4 / NCH row pairs per wave job (8 loads of 16 bytes per lane, two jobs in flight);
+  // the grid: the workgroups that fit at once, or fewer if there are fewer jobs
+  const int c1 = gemv_chunks(row_code_bytes<WF>(p1.K));
+  const int acts = std::min(p1.E, p1.k) + (p1.shared_blob != nullptr ? 1 : 0);
+  const int c2 = gemv_chunks(row_code_bytes<WF>(p2.K));
+  if (acts <= kGemvGuThreads / 64) {
+    // every down step has a wave of its own: gate/up and down + combine in one launch
+    const int jobs = acts * cdiv(p1.N, 4 / c1);
+#define FT_TLY(C, R, CD) \
+  if (c1 == C && c2 == CD) launch_token_layer<WF, C, R, CD>(p1, p2, wait_words, jobs, stream);
+    FT_TLY(1, 4, 1)
+    FT_TLY(1, 4, 2)
+    FT_TLY(1, 4, 4)
+    FT_TLY(2, 2, 1)
+    FT_TLY(2, 2, 2)
+    FT_TLY(2, 2, 4)
+    FT_TLY(4, 1, 1)
+    FT_TLY(4, 1, 2)
+    FT_TLY(4, 1, 4)
+#undef FT_TLY
+    FT_LAUNCHED("ffn_token_layer_kernel");
+    return FT_OK;
+  }
+#define FT_TGU(C, R)                                                                                     \
+  if (c1 == C) {                                                                                         \
+    const void *kern = reinterpret_cast<const void *>(&ffn_token_gate_up_kernel<WF, C, R>);             \
+    const int grid = std::max(1, std::min(resident_grid(kern, kGemvGuThreads),                          \
+                                          cdiv(acts * cdiv(p1.N, R), kGemvGuThreads / 64)));              \
+    hipLaunchKernelGGL((ffn_token_gate_up_kernel<WF, C, R>), dim3(grid), dim3(kGemvGuThreads), 0, stream, p1); \
+  }
+  FT_TGU(1, 4)
+  FT_TGU(2, 2)
+  FT_TGU(4, 1)
+#undef FT_TGU
+  FT_LAUNCHED("ffn_token_gate_up_kernel");
+  // down + combine: the waves split the steps (2 or 3 each); rows per workgroup so that about
+  // 16 weight pieces per lane are in flight
+  const int spw = (p2.k + (p2.shared_blob != nullptr ? 1 : 0)) <= 8 ? 2 : 3;
+#define FT_TDN(C, R, SP)                                                                                 \
+  if (c2 == C && spw == SP) {                                                                            \
+    const int grid = cdiv(p2.N, R);                                                                      \
+    hipLaunchKernelGGL((ffn_token_down_combine_kernel<WF, C, R, SP>), dim3(grid), dim3(kGemvThreads), 0, stream, p2); \
+  }
+  FT_TDN(1, 8, 2)
+  FT_TDN(1, 4, 3)
+  FT_TDN(2, 4, 2)
+  FT_TDN(2, 2, 3)
+  FT_TDN(4, 2, 2)
+  FT_TDN(4, 1, 3)
+#undef FT_TDN
+  FT_LAUNCHED("ffn_token_down_combine_kernel");
+  return FT_OK;
+}
+
 // ------------------------------------------------------------------ prefill grouped GEMM
 
 // Two pipeline stages.  MXFP4 and NVFP4 weights: two workgroups per CU
@@ -526,13 +730,12 @@ __global__ __launch_bounds__(256) void ffn_f32_stage2(FfnF32Args a) {
 
 using namespace ft;
 
-extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
-                                        const int32_t *slot_of_expert, const void *shared_blob,
-                                        const void *x, int32_t x_dtype, int32_t T, int32_t k,
-                                        int32_t E, const int32_t *expert_offsets,
-                                        const int32_t *sorted_rows, float *y_rows, float *y_shared,
-                                        int32_t mode, void *workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
+// The argument checks of ft_moe_grouped_ffn (FT_OK for a valid call, T = 0 included).
+static ft_status ffn_check(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
+                           const int32_t *slot_of_expert, const void *shared_blob, const void *x, int32_t x_dtype,
+                           int32_t T, int32_t k, int32_t E, const int32_t *expert_offsets,
+                           const int32_t *sorted_rows, const float *y_rows, const float *y_shared, int32_t mode,
+                           const void *workspace, size_t workspace_bytes) {
   FT_REQUIRE(L != nullptr, "ft_moe_grouped_ffn: layout is NULL");
   FT_REQUIRE(T >= 0 && k >= 1 && E >= 1, "ft_moe_grouped_ffn: need T >= 0, k >= 1, E >= 1");
   FT_REQUIRE(int64_t(T) * (k + 1) < (int64_t(1) << 31), "ft_moe_grouped_ffn: T*k too large");
@@ -547,7 +750,6 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   FT_REQUIRE((mode & ~0x3ff) == 0, "ft_moe_grouped_ffn: unknown mode bits");
   const int variant = mode & 0xff;
   FT_SUPPORTED(variant == FT_FFN_EXACT || variant == FT_FFN_NATIVE_MX, "ft_moe_grouped_ffn: unknown mode");
-  const bool run1 = stages != FT_FFN_DOWN_ONLY, run2 = stages != FT_FFN_GATE_UP_ONLY;
   const int H = L->H, I = L->I;
   FT_REQUIRE(H >= 1 && I >= 1 && L->expert_bytes > 0, "ft_moe_grouped_ffn: layout not initialised");
   const int wd = L->wdtype;
@@ -567,10 +769,7 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   }
   FT_SUPPORTED(variant == FT_FFN_EXACT || wd == FT_MXFP4,
                "ft_moe_grouped_ffn: the native scaled-MFMA mode needs MXFP4 weights");
-  if (T == 0) {
-    clear_error();
-    return FT_OK;
-  }
+  if (T == 0) return FT_OK;
   FT_REQUIRE(slot_pool && x && expert_offsets && sorted_rows && y_rows,
              "ft_moe_grouped_ffn: NULL pointer argument");
   FT_REQUIRE(n_slots >= 1 && (slot_of_expert != nullptr || n_slots >= E),
@@ -586,6 +785,28 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
   const size_t need = ffn_workspace_bytes(T, k, E, H, I);
   FT_REQUIRE(workspace != nullptr && workspace_bytes >= need,
              "ft_moe_grouped_ffn: workspace too small (see ft_workspace_bytes)");
+  return FT_OK;
+}
+
+extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
+                                        const int32_t *slot_of_expert, const void *shared_blob,
+                                        const void *x, int32_t x_dtype, int32_t T, int32_t k,
+                                        int32_t E, const int32_t *expert_offsets,
+                                        const int32_t *sorted_rows, float *y_rows, float *y_shared,
+                                        int32_t mode, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  const ft_status cst = ffn_check(L, slot_pool, n_slots, slot_of_expert, shared_blob, x, x_dtype, T, k, E,
+                                  expert_offsets, sorted_rows, y_rows, y_shared, mode, workspace, workspace_bytes);
+  if (cst != FT_OK) return cst;
+  if (T == 0) {
+    clear_error();
+    return FT_OK;
+  }
+  const int stages = mode & (FT_FFN_GATE_UP_ONLY | FT_FFN_DOWN_ONLY);
+  const int variant = mode & 0xff;
+  const bool run1 = stages != FT_FFN_DOWN_ONLY, run2 = stages != FT_FFN_GATE_UP_ONLY;
+  const int H = L->H, I = L->I;
+  const int wd = L->wdtype;
 
   const bool has_shared = shared_blob != nullptr;
   const int routed = T * k;
@@ -861,6 +1082,148 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
     if (run2 && (st = launch_stream<WF_FP4, false>(s2, a_max, T, stream, "ffn_stream_kernel<mxfp4, down>")) != FT_OK)
       return st;
   }
+  clear_error();
+  return FT_OK;
+}
+
+// ------------------------------------------------------------------ the whole layer in one call
+
+extern "C" ft_status ft_moe_layer(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
+                                  const int32_t *slot_of_expert, const void *shared_blob, const void *x,
+                                  int32_t x_dtype, const void *w_router, float *logits, int32_t T, int32_t E,
+                                  int32_t k, int32_t gating, int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                                  int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos, float *y_rows,
+                                  float *y_shared, int32_t mode, int32_t out_dtype, void *out, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  // every step's checks before anything is enqueued
+  FT_REQUIRE(L != nullptr, "ft_moe_layer: layout is NULL");
+  FT_REQUIRE((mode & ~0xff) == 0, "ft_moe_layer: stage bits are not taken (the call runs the whole layer)");
+  FT_REQUIRE(out_dtype == FT_F32 || out_dtype == FT_BF16, "ft_moe_layer: out_dtype must be FT_F32 or FT_BF16");
+  ft_status st = route_logits(x, x_dtype, w_router, logits, T, L->H, E, k, gating, topk_ids, topk_w, stream, false);
+  if (st != FT_OK) return st;
+  FT_SUPPORTED(k <= 64, "ft_moe_layer: k > 64");
+  FT_SUPPORTED(L->H % 4 == 0, "ft_moe_layer: H must be a multiple of 4");
+  FT_REQUIRE(T <= 65535, "ft_moe_layer: T > 65535");
+  if (T > 0) {
+    FT_REQUIRE(expert_offsets && sorted_rows && row_pos && out && aligned(out, 16),
+               "ft_moe_layer: NULL or misaligned permutation or output buffer");
+    FT_REQUIRE(workspace != nullptr && aligned(workspace, 256) &&
+                   workspace_bytes >= kLayerWaitBytes + permute_workspace_bytes(T, k, E),
+               "ft_moe_layer: workspace NULL, not 256-byte aligned or too small "
+               "(see ft_workspace_bytes(FT_WS_LAYER, ...))");
+  }
+  // the wait words first, then the workspace of the steps
+  uint32_t *wait_words = static_cast<uint32_t *>(workspace);
+  void *ws = T > 0 ? static_cast<uint8_t *>(workspace) + kLayerWaitBytes : workspace;
+  const size_t ws_bytes = T > 0 ? workspace_bytes - kLayerWaitBytes : workspace_bytes;
+  st = ffn_check(L, slot_pool, n_slots, slot_of_expert, shared_blob, x, x_dtype, T, k, E, expert_offsets,
+                 sorted_rows, y_rows, y_shared, mode, ws, ws_bytes);
+  if (st != FT_OK) return st;
+  if (T == 0) {
+    clear_error();
+    return FT_OK;
+  }
+  const int H = L->H, I = L->I, wd = L->wdtype;
+  const bool has_shared = shared_blob != nullptr;
+  int w1 = 0, c1 = 0, w2 = 0, c2 = 0;
+  const bool shapes = wd == FT_BF16   ? fused_shape<WF_BF16>(true, H / stream_kblock<WF_BF16>(), &w1, &c1) &&
+                                          fused_shape<WF_BF16>(false, I / stream_kblock<WF_BF16>(), &w2, &c2)
+                      : wd == FT_MXFP4 ? fused_shape<WF_FP4>(true, H / stream_kblock<WF_FP4>(), &w1, &c1) &&
+                                          fused_shape<WF_FP4>(false, I / stream_kblock<WF_FP4>(), &w2, &c2)
+                      : wd == FT_NVFP4 ? fused_shape<WF_NV4>(true, H / stream_kblock<WF_NV4>(), &w1, &c1) &&
+                                          fused_shape<WF_NV4>(false, I / stream_kblock<WF_NV4>(), &w2, &c2)
+                                       : false;
+  const bool exact = (mode & 0xff) == FT_FFN_EXACT;
+  const bool gemv = T == 1 && exact &&
+                    (wd == FT_BF16    ? token_gemv_covers<WF_BF16>(H, I, E, k, has_shared)
+                     : wd == FT_MXFP4 ? token_gemv_covers<WF_FP4>(H, I, E, k, has_shared)
+                     : wd == FT_NVFP4 ? token_gemv_covers<WF_NV4>(H, I, E, k, has_shared)
+                                      : false);
+  const bool fused = gemv || (T <= kRouteMaxT && exact && shapes && E <= kRouteMaxE && k <= kFusedMaxK &&
+                              T * k <= kRouteMaxRows && w1 >= T);
+  if (!fused) {
+    // route + permute, the grouped FFN and the combine, one call after the other
+    st = ft_moe_route_permute(x, x_dtype, w_router, logits, T, H, E, k, gating, renormalize, topk_ids, topk_w,
+                              expert_offsets, sorted_rows, row_pos, ws, ws_bytes, stream);
+    if (st != FT_OK) return st;
+    st = ft_moe_grouped_ffn(L, slot_pool, n_slots, slot_of_expert, shared_blob, x, x_dtype, T, k, E,
+                            expert_offsets, sorted_rows, y_rows, y_shared, mode, ws, ws_bytes, stream);
+    if (st != FT_OK) return st;
+    return ft_moe_combine(y_rows, topk_w, row_pos, y_shared, T, k, H, out_dtype, out, stream);
+  }
+  // A few tokens: the router, then gate/up with top-k, gating and the permutation done in every
+  // workgroup (the routing kernel's launch saved), then the down projection with the combine folded
+  // in (the combine's launch and the y rows' round trip saved).  y_rows / y_shared are not written.
+  st = route_logits(x, x_dtype, w_router, logits, T, H, E, k, gating, topk_ids, topk_w, stream, true);
+  if (st != FT_OK) return st;
+  const int rows = T * k + (has_shared ? T : 0);
+  uint16_t *hbuf = static_cast<uint16_t *>(ws);
+  PersistArgs p1{};
+  p1.pool = static_cast<const uint8_t *>(slot_pool);
+  p1.slot_of_expert = slot_of_expert;
+  p1.n_slots = n_slots;
+  p1.expert_bytes = L->expert_bytes;
+  p1.shared_blob = static_cast<const uint8_t *>(shared_blob);
+  p1.E = E;
+  p1.T = T;
+  p1.k = k;
+  PersistArgs p2 = p1;
+  p1.off_w0 = L->off_gate;
+  p1.off_w1 = L->off_up;
+  p1.off_s0 = L->off_sgate;
+  p1.off_s1 = L->off_sup;
+  p1.off_t0 = L->off_tscale;
+  p1.off_t1 = L->off_tscale + 4;
+  p1.K = H;
+  p1.N = I;
+  p1.X = static_cast<const uint16_t *>(x);
+  p1.ldx = H;
+  p1.x_bytes = uint32_t(uint64_t(T) * H * 2);
+  p1.out = hbuf;
+  p1.ldo = I;
+  p1.logits = logits;
+  p1.gating = gating;
+  p1.renorm = renormalize ? 1 : 0;
+  p1.ids_out = topk_ids;
+  p1.w_out = topk_w;
+  p1.off_out = expert_offsets;
+  p1.rows_out = sorted_rows;
+  p1.pos_out = row_pos;
+  p2.off_w0 = p2.off_w1 = L->off_down;
+  p2.off_s0 = p2.off_s1 = L->off_sdown;
+  p2.off_t0 = p2.off_t1 = L->off_tscale + 8;
+  p2.K = I;
+  p2.N = H;
+  p2.X = hbuf;
+  p2.ldx = I;
+  p2.x_bytes = uint32_t(uint64_t(rows) * I * 2);
+  p2.ids = topk_ids;
+  p2.topk_w = topk_w;
+  p2.row_pos = row_pos;
+  p2.comb_out = out;
+  p2.comb_bf16 = out_dtype == FT_BF16 ? 1 : 0;
+  p2.ldo = H;
+  if (gemv) {  // one token: the matrix-vector kernels
+    st = wd == FT_BF16    ? launch_token_gemv<WF_BF16>(p1, p2, wait_words, stream)
+         : wd == FT_MXFP4 ? launch_token_gemv<WF_FP4>(p1, p2, wait_words, stream)
+                          : launch_token_gemv<WF_NV4>(p1, p2, wait_words, stream);
+    if (st != FT_OK) return st;
+    clear_error();
+    return FT_OK;
+  }
+  const int units1 = (std::min(E, T * k) + (has_shared ? 1 : 0)) * cdiv(I, 16);  // 16-row gate/up units, at most
+  const int units2 = T * cdiv(H, 16);
+  if (wd == FT_BF16) {
+    if ((st = launch_fused<WF_BF16, true>(p1, units1, 1, stream)) != FT_OK) return st;
+    st = launch_fused<WF_BF16, false>(p2, units2, 1, stream);
+  } else if (wd == FT_MXFP4) {
+    if ((st = launch_fused<WF_FP4, true>(p1, units1, 1, stream)) != FT_OK) return st;
+    st = launch_fused<WF_FP4, false>(p2, units2, 1, stream);
+  } else {
+    if ((st = launch_fused<WF_NV4, true>(p1, units1, 1, stream)) != FT_OK) return st;
+    st = launch_fused<WF_NV4, false>(p2, units2, 1, stream);
+  }
+  if (st != FT_OK) return st;
   clear_error();
   return FT_OK;
 }

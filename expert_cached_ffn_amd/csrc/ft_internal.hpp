@@ -13,6 +13,11 @@
 // ---------------------------------------------------------------------------
 namespace ft {
 
+// Bytes at the start of the layer call's workspace reserved for the one-token
+// kernel's grid-wide wait (counters on separate 128-byte lines); the rest of
+// the workspace follows.
+constexpr size_t kLayerWaitBytes = 8192;
+
 void set_error(const std::string &msg);
 void clear_error();
 
@@ -26,6 +31,12 @@ inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 // Workspace sizes (bytes) of the calls that take one.
 size_t permute_workspace_bytes(int32_t T, int32_t k, int32_t E);
 size_t ffn_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t I);
+
+// Validates the routing arguments of ft_moe_route and (launch) enqueues the
+// router logits when w_router != NULL; nothing else.
+ft_status route_logits(const void *x, int32_t x_dtype, const void *w_router, float *logits, int32_t T, int32_t H,
+                       int32_t E, int32_t k, int32_t gating, int32_t *topk_ids, float *topk_w, hipStream_t stream,
+                       bool launch = true);
 
 }  // namespace ft
 
@@ -81,6 +92,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// One dword as a bf16 pair.  Takes the dword by value: __builtin_bit_cast applied directly to an
+// element of a u32x4 (v[i]) compiles to a read of element 0 whatever i is.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
 // Eight FP4 E2M1 codes (one dword, element 2i in the low nibble of byte i)
 // times a power-of-two scale -> eight bf16, in element order.
@@ -242,6 +256,16 @@ __device__ __forceinline__ float wave_max_f32(float x) {
   x = fmaxf(x, dpp_f32<0x142, 0xA>(x, x));
   x = fmaxf(x, dpp_f32<0x143, 0xC>(x, x));
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0xB1>(x, x));
+  x = max(x, dpp_u32<0x4E>(x, x));
+  x = max(x, dpp_u32<0x141>(x, x));
+  x = max(x, dpp_u32<0x140>(x, x));
+  x = max(x, dpp_u32<0x142, 0xA>(x, x));
+  x = max(x, dpp_u32<0x143, 0xC>(x, x));
+  return uint32_t(__builtin_amdgcn_readlane(int(x), 63));
 }
 
 // Sum over the wave, in every lane: quad butterflies, then each lane adds the

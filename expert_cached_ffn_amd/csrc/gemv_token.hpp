@@ -1,0 +1,600 @@
+// One-token decode as matrix-vector products (the fused layer call at T = 1).
+//
+// With one token every expert matrix is read once and multiplied by one
+// vector: HBM-bound work with no reuse, so no MFMA tile.  A workgroup owns a
+// fixed block of weight rows, issues all of their 16-byte loads at once (the
+// whole block in flight, one HBM round trip), and each wave reduces its rows'
+// dot products with DPP lane moves.  Many small workgroups rather than a
+// persistent grid: at one token a persistent unit (expert table, LDS
+// reduction, barriers per 16-row tile) costs more than its weight stream.
+//
+// The kernels that wrap these bodies ask for at least two waves per SIMD
+// (up to 256 registers), so a wave's whole block of loads stays in registers;
+// with the default budget the compiler waited for early loads before issuing
+// the rest.
+//
+// Row layout: 64 lanes cover 1 KiB of a row's codes per "chunk" (lane l holds
+// bytes 16 l .. 16 l + 15 of chunk c, i.e. byte 1024 c + 16 l); a row of B
+// code bytes has ceil(B / 1024) chunks, the last possibly partial.
+//   bf16  : 16 bytes = 8 elements
+//   MXFP4 : 16 bytes = 32 elements = one E8M0 block (scale byte 64 c + l)
+//   NVFP4 : 16 bytes = 32 elements = two E4M3 blocks (scale bytes 2 (64 c + l), +1)
+#pragma once
+
+#include "stream_persist.hpp"
+
+namespace ft {
+
+constexpr int kGemvThreads = 256;   // down + combine: 4 waves
+constexpr int kGemvGuThreads = 512; // gate/up: 8 waves
+constexpr int kGemvMaxChunks = 4;   // rows of at most 4 KiB of codes
+
+template <int WF>
+struct GemvFmt {
+  static constexpr int EPC = WF == WF_BF16 ? 8 : 32;    // elements per 16-byte chunk piece
+  static constexpr int XV = EPC / 8;                    // u32x4 of bf16 activations per piece
+};
+
+// fp32 dot of one 16-byte weight piece with its activations (bf16 pairs, element order).  The
+// products run on v_dot2 (two bf16 products added to an fp32 accumulator); FP4 codes are widened
+// to bf16 pairs first, which is exact: an E2M1 value has 2 significant bits, times a power of two
+// (MXFP4, applied in the conversion) or later times an E4M3 scale of 4 significant bits (NVFP4,
+// applied to each 16-element block's sum, since the scaled conversions use only the exponent of
+// their scale).
+template <int WF>
+__device__ __forceinline__ float piece_dot(const u32x4 w, const uint32_t sc, const u32x4 *x, float acc) {
+  if constexpr (WF == WF_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[i]), as_bf16x2(x[0][i]), acc, false);
+  } else if constexpr (WF == WF_FP4) {
+    // dword d holds elements 8d .. 8d+7, byte b of it elements 8d+2b, 8d+2b+1 (low nibble first);
+    // activations dword x[d][b] holds the same two elements (the selector operand must be a literal)
+    const float s = e8m0_to_f32(sc & 0xffu);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 0), as_bf16x2(x[d][0]), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 1), as_bf16x2(x[d][1]), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 2), as_bf16x2(x[d][2]), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 3), as_bf16x2(x[d][3]), acc, false);
+    }
+  } else {
+    // two 16-element blocks (dwords 0-1: scale byte 0, dwords 2-3: byte 1), each summed unscaled
+    float blk[2] = {0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float &b = blk[d >> 1];
+      b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 0), as_bf16x2(x[d][0]), b, false);
+      b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 1), as_bf16x2(x[d][1]), b, false);
+      b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 2), as_bf16x2(x[d][2]), b, false);
+      b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 3), as_bf16x2(x[d][3]), b, false);
+    }
+    acc = fmaf(e4m3_to_f32(sc & 0xffu), blk[0], acc);
+    acc = fmaf(e4m3_to_f32((sc >> 8) & 0xffu), blk[1], acc);
+  }
+  return acc;
+}
+
+// Scale bits of piece `piece` of the row whose scales start at byte `so` of `sres` (the 4-bit
+// formats), read as the aligned dword that holds them (no per-lane byte loads; an offset at or past
+// the buffer gives 0).  MXFP4: one byte; NVFP4: two bytes, elements 0..15 then 16..31.
+template <int WF>
+__device__ __forceinline__ uint32_t piece_scale(rsrc_t sres, uint32_t so, int piece, bool ok) {
+  if constexpr (WF == WF_BF16) {
+    return 0u;
+  } else {
+    const uint32_t b = WF == WF_FP4 ? uint32_t(piece) : 2u * uint32_t(piece);
+    const uint32_t word = bld4(sres, ok ? so + (b & ~3u) : kOOB);
+    return word >> (8 * (b & 3u));
+  }
+}
+
+// ---------------------------------------------------------------- routing of the one token
+
+// Top-k, gating and permutation of one token by one wave (all 64 lanes call
+// it); lane j < k ends with pick j.  The order is topk_token's: descending
+// logit, the lower expert index first among equal logits, softmax over all E
+// or element-wise sigmoid, optionally renormalised over the picks.  A round
+// is a 32-bit wave max of the logits' order keys and one ballot per logit
+// slot for the lowest index holding it (topk_token carries the index in a
+// 64-bit key instead, which doubles every butterfly step).  The picks are
+// distinct experts, so the token's permuted rows are the picks in ascending
+// id and a pick's row is its rank among them.
+struct TokenPick {
+  int id;     // expert (lanes >= k: -1)
+  float w;    // gating weight
+  int rank;   // position of the pick among the picks in ascending expert id = its permuted row
+};
+
+__device__ __forceinline__ TokenPick one_token_route(const float *__restrict__ lr, int E, int k, int gating,
+                                                     int renorm) {
+  constexpr int VPL = kRouteMaxE / 64;
+  const int lane = threadIdx.x & 63;
+  float v[VPL];
+  uint32_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) v[i] = lr[lane + 64 * i < E ? lane + 64 * i : 0];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    // 0 marks "absent or already picked": real keys start at 1 (only the all-ones NaN maps to 0)
+    const uint32_t kk = order_key(v[i]);
+    key[i] = lane + 64 * i < E ? (kk == 0u ? 1u : kk) : 0u;
+  }
+  int pid = -1;
+  float pval = 0.f, mx = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < VPL; ++i) m = max(m, key[i]);
+    m = wave_max_u32(m);
+    int e = -1;  // the lowest expert index whose key is m (scalar)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const uint64_t b = __ballot(key[i] == m);
+      if (e < 0 && b != 0) e = 64 * i + int(__builtin_ctzll(b));
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) key[i] = lane + 64 * i == e ? 0u : key[i];
+    if (j == 0) mx = key_value(m);  // the largest logit
+    if (lane == j) {
+      pid = e;
+      pval = key_value(m);
+    }
+  }
+  float denom = 1.0f;
+  if (gating == FT_SOFTMAX) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (lane + 64 * i < E) s += expf(v[i] - mx);
+    denom = wave_sum_f32(s);
+  }
+  float p = 0.f;
+  if (lane < k) p = gating == FT_SOFTMAX ? expf(pval - mx) / denom : 1.0f / (1.0f + expf(-pval));
+  const float wsum = renorm ? wave_sum_f32(p) : 1.0f;
+  int rank = 0;
+  for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(pid, i) < pid ? 1 : 0;
+  return TokenPick{pid, renorm ? p / wsum : p, rank};
+}
+
+// ---------------------------------------------------------------- one-token layer kernel: the wait
+
+// The one-token layer kernel runs gate/up and then down + combine in one
+// launch; the down stage needs every hidden value, so the workgroups meet at a
+// grid-wide wait in between.  The grid never exceeds the workgroups that fit
+// on the device at once, so every workgroup is resident and the wait ends.
+//
+// The wait is two-level, so that no memory word takes more than a few dozen
+// atomic adds (one word for all workgroups measured about 20 us): workgroup b
+// counts itself in group b % 16; the last of a group counts the group in the
+// top counter; the last group bumps the 16 copies of the round number, each
+// group polling its own copy.  Counters and copies sit on separate 128-byte
+// lines.  The last arrival at each counter clears it, so all counters are zero
+// again for the next launch.
+//
+// The hidden values cross the compute dies' separate L2 caches: they are
+// stored and loaded with agent-scope coherence (the sc1 cache policy), and a
+// wave waits for its stores to complete before its workgroup arrives.  (An
+// agent-scope release / acquire fence would write back and invalidate the
+// whole L2 instead, thousands of times per launch: measured about 150 us.)
+// The wait is bounded: after kBarrierPolls polls of the round copy it gives
+// up and reports false (the caller then writes NaN).
+constexpr int kBarrierPolls = 1 << 16;
+constexpr int kCoherentAgent = 16;  // buffer cache policy: sc1 (agent scope)
+constexpr int kWaitGroups = 16;
+constexpr int kWaitStride = 32;     // words between counters: one 128-byte line each
+static_assert(kWaitStride * 4 * (2 * kWaitGroups + 1) <= int(kLayerWaitBytes), "wait words fit their area");
+
+// PENDING: vector memory operations this wave issued after its last hidden store (they may stay in
+// flight; everything before them, the stores included, has completed when the wave arrives).
+template <int PENDING>
+__device__ __forceinline__ bool grid_wait(uint32_t *bar) {
+  __shared__ int s_ok;
+  wait_vmcnt<PENDING>();
+  lds_barrier();  // (__syncthreads would also wait for the loads left in flight)
+  if (threadIdx.x == 0) {
+    const int G = int(gridDim.x), b = int(blockIdx.x);
+    const int ng = G < kWaitGroups ? G : kWaitGroups;
+    const int grp = b % ng;
+    const uint32_t gs = uint32_t((G - grp + ng - 1) / ng);  // workgroups in this group
+    uint32_t *cnt = bar + kWaitStride * grp, *top = bar + kWaitStride * kWaitGroups;
+    uint32_t *rnd = bar + kWaitStride * (kWaitGroups + 1 + grp);
+    const uint32_t round = __hip_atomic_load(rnd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gs - 1) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == uint32_t(ng - 1)) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = 0; g < ng; ++g)
+          __hip_atomic_fetch_add(bar + kWaitStride * (kWaitGroups + 1 + g), 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    int ok = 1, n = 0;
+    while (__hip_atomic_load(rnd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == round) {
+      if (++n >= kBarrierPolls) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    s_ok = ok;
+  }
+  lds_barrier();
+  return s_ok != 0;
+}
+
+// Down + combine of the one token after the wait.  Wave w takes step w -- the
+// pick of rank w (hidden row w) or, at w = k, the shared expert -- for the
+// workgroup's blocks of RB output rows; the step weights of the first block
+// are loaded before the wait (they depend only on the routing, which every
+// workgroup holds in LDS), the hidden row after it.  Per row the waves'
+// weighted dots meet in LDS and are added in wave order.
+template <int WF, int NCHD, int RB>
+__device__ __forceinline__ void token_down_after_wait(const PersistArgs &d, uint32_t *bar, const int *s_act,
+                                                      const float *s_w, const int *s_slot, int S) {
+  constexpr int WAVES = kGemvGuThreads / 64;
+  using F = GemvFmt<WF>;
+  __shared__ float s_part[WAVES][RB];
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const uint32_t rbytes = WF == WF_BF16 ? uint32_t(d.K) * 2 : uint32_t(d.K) / 2;
+  const uint32_t sbytes = WF == WF_FP4 ? uint32_t(d.K) / 32 : (WF == WF_NV4 ? uint32_t(d.K) / 16 : 0u);
+  const bool live = wave < S;
+  const int e = live ? uniform(s_act[wave]) : -1;
+  const bool shared = e == d.E;
+  const int slot = (e < 0 || shared) ? 0 : uniform(s_slot[e]);
+  const bool missing = live && !shared && slot < 0;
+  const uint8_t *blob = shared ? d.shared_blob : d.pool + uint64_t(slot < 0 ? 0 : slot) * d.expert_bytes;
+  const float wgt = !live ? 0.f : (shared ? 1.f : s_w[wave]);
+  const rsrc_t wres = make_rsrc(blob + d.off_w0, uint32_t(d.N) * rbytes);
+  const rsrc_t sres = make_rsrc(blob + d.off_s0, uint32_t(d.N) * sbytes);
+  float ts = 1.f;
+  if constexpr (WF == WF_NV4)
+    if (live) ts = *reinterpret_cast<const float *>(blob + d.off_t0);
+  const int blocks = (d.N + RB - 1) / RB;
+  u32x4 w[RB][NCHD];
+  uint32_t sc[RB][NCHD];
+  auto issue = [&](int rb) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int c = 0; c < NCHD; ++c) {
+        const int row = rb * RB + r;
+        const uint32_t cb = 1024u * c + 16u * lane;
+        const bool ok = live && row < d.N && cb < rbytes;
+        w[r][c] = bld16(wres, ok ? uint32_t(row) * rbytes + cb : kOOB);
+        sc[r][c] = piece_scale<WF>(sres, uint32_t(row) * sbytes, int(cb >> 4), ok);
+      }
+  };
+  // the first block's loads always issue (past the rows: offsets past the buffers), so the wait
+  // knows how many of this wave's memory operations follow its hidden stores
+  int rb = int(blockIdx.x);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(rb);
+  __builtin_amdgcn_sched_barrier(0);
+  const bool ok = grid_wait<RB * NCHD * (WF == WF_BF16 ? 1 : 2)>(bar);
+  const rsrc_t hres = make_rsrc(d.X, d.x_bytes);
+  u32x4 hv[NCHD][F::XV];
+#pragma unroll
+  for (int c = 0; c < NCHD; ++c)
+#pragma unroll
+    for (int v = 0; v < F::XV; ++v) {
+      const uint32_t el = uint32_t(64 * c + lane) * F::EPC + 8u * v;
+      hv[c][v] = __builtin_amdgcn_raw_buffer_load_b128(
+          hres, (live && el < uint32_t(d.K)) ? (uint32_t(wave) * uint32_t(d.ldx) + el) * 2u : kOOB, 0, kCoherentAgent);
+    }
+  for (; rb < blocks; rb += int(gridDim.x)) {
+    if (rb != int(blockIdx.x)) issue(rb);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      float dd = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCHD; ++c) dd = piece_dot<WF>(w[r][c], sc[r][c], hv[c], dd);
+      dd = wave_sum_f32(dd);
+      if (lane == 0) s_part[wave][r] = missing ? __builtin_nanf("") : wgt * (ts * dd);
+    }
+    __syncthreads();
+    if (tid < RB) {
+      const int row = rb * RB + tid;
+      float v = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < WAVES; ++w2) v += s_part[w2][tid];
+      if (!ok) v = __builtin_nanf("");
+      if (row < d.N) {
+        if (d.comb_bf16) reinterpret_cast<uint16_t *>(d.comb_out)[row] = f32_to_bf16_rne(v);
+        else reinterpret_cast<float *>(d.comb_out)[row] = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- gate/up + SwiGLU, one token
+
+// Work is a list of wave jobs: RPW consecutive (gate row, up row) pairs of one
+// expert, the routed experts' in ascending id, then the shared expert's.
+// Every workgroup routes the token itself (one_token_route; workgroup 0
+// publishes the result); its waves then walk the job
+// list with a stride of all the grid's waves, the next job's loads issued
+// before the current job is multiplied.  The grid is sized to the workgroups
+// that fit on the device at once, so no workgroup pays the prologue in a
+// second round.
+//
+// Data every wave reads is fetched once per workgroup: the token's
+// activations go through LDS (per wave they would be the same few KiB read
+// by thousands of waves from the few L2 channels that hold them), issued
+// together with the slot table entries before the top-k waits on the router
+// logits.  Large (8-wave) workgroups keep that shared traffic small.
+template <int WF, int NCH, int RPW, int NCHD = 0, int RB = 0>
+__device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const PersistArgs *d = nullptr,
+                                             uint32_t *bar = nullptr) {
+  constexpr int THREADS = kGemvGuThreads, WAVES = THREADS / 64;
+  static_assert(kRouteMaxE <= THREADS, "one slot table entry per thread");
+  using F = GemvFmt<WF>;
+  constexpr int XN = NCH * 64 * F::XV;            // u32x4 of activations the lanes' pieces cover
+  constexpr int XPT = (XN + THREADS - 1) / THREADS;
+  __shared__ int s_act[kFusedMaxK + 1];     // the picks in ascending id (= their rows), then the shared expert
+  __shared__ float s_w[kFusedMaxK + 1];     // their gating weights
+  __shared__ int s_slot[kRouteMaxE];        // slot of every expert (-1: not resident)
+  __shared__ int s_nact;
+  __shared__ u32x4 s_x[XN];                 // the token's activations, u32x4 i = elements 8i .. 8i+7
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const uint32_t rbytes = WF == WF_BF16 ? uint32_t(a.K) * 2 : uint32_t(a.K) / 2;  // code bytes of a row
+  const uint32_t sbytes = WF == WF_FP4 ? uint32_t(a.K) / 32 : (WF == WF_NV4 ? uint32_t(a.K) / 16 : 0u);
+  // Raw buffer loads throughout: an offset past the buffer reads zero without a branch, so a job's
+  // loads are all issued before the first wait.
+  const rsrc_t xres = make_rsrc(a.X, uint32_t(a.K) * 2u);
+  u32x4 xg[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const uint32_t u = uint32_t(tid + THREADS * i);
+    xg[i] = bld16(xres, u < uint32_t(XN) ? u * 16u : kOOB);
+  }
+  const int my_slot = tid < a.E ? table_slot(a.slot_of_expert, tid, a.n_slots) : -1;
+
+  if (wave == 0) {  // the routing; workgroup 0 publishes it (ids, weights, offsets, rows) for the down stage
+    const TokenPick pk = one_token_route(a.logits, a.E, a.k, a.gating, a.renorm);
+    if (lane < a.k) {
+      s_act[pk.rank] = pk.id;
+      s_w[pk.rank] = pk.w;
+    }
+    if (lane == 0) {
+      const bool sh = a.shared_blob != nullptr;
+      if (sh) s_act[a.k] = a.E;
+      s_nact = a.k + (sh ? 1 : 0);
+    }
+    if (blockIdx.x == 0) {
+      if (lane < a.k) {
+        a.ids_out[lane] = pk.id;
+        a.w_out[lane] = pk.w;
+        a.rows_out[pk.rank] = lane;
+        a.pos_out[lane] = pk.rank;
+      }
+      for (int e = lane; e <= a.E; e += 64) {  // expert e's segment starts after the picks below e
+        int c = 0;
+        for (int i = 0; i < a.k; ++i) c += __builtin_amdgcn_readlane(pk.id, i) < e ? 1 : 0;
+        a.off_out[e] = c;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < XPT; ++i)
+    if (tid + THREADS * i < XN) s_x[tid + THREADS * i] = xg[i];
+  if (tid < kRouteMaxE) s_slot[tid] = my_slot;
+  __syncthreads();
+  // this lane's activations: piece (c, v) = elements (64 c + lane) * EPC + 8 v ..
+  u32x4 xv[NCH][F::XV];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int v = 0; v < F::XV; ++v) xv[c][v] = s_x[(64 * c + lane) * F::XV + v];
+  const int jobs_per_expert = (a.N + RPW - 1) / RPW;
+  const int n_jobs = s_nact * jobs_per_expert;
+  const int stride = int(gridDim.x) * WAVES;
+  const rsrc_t hres_out = make_rsrc(a.out, uint32_t(s_nact * a.ldo) * 2u);  // the hidden rows
+
+  struct Job {
+    u32x4 wg[RPW][NCH], wu[RPW][NCH];
+    uint32_t sg[RPW][NCH], su[RPW][NCH];
+    float ts0, ts1;  // NVFP4 tensor scales
+  };
+  // the loads of job j (j >= n_jobs: offsets past the buffers, nothing read)
+  auto issue = [&](int j, Job &J) {
+    const bool live = j < n_jobs;
+    const int jj = live ? j : 0;
+    const int ai = jj / jobs_per_expert, row0 = (jj - ai * jobs_per_expert) * RPW;
+    const int e = uniform(s_act[ai]);
+    const int slot = e == a.E ? 0 : uniform(s_slot[e]);
+    const uint8_t *blob = e == a.E ? a.shared_blob : a.pool + uint64_t(slot < 0 ? 0 : slot) * a.expert_bytes;
+    const rsrc_t gres = make_rsrc(blob + a.off_w0, uint32_t(a.N) * rbytes);
+    const rsrc_t ures = make_rsrc(blob + a.off_w1, uint32_t(a.N) * rbytes);
+    const rsrc_t gsres = make_rsrc(blob + a.off_s0, uint32_t(a.N) * sbytes);
+    const rsrc_t usres = make_rsrc(blob + a.off_s1, uint32_t(a.N) * sbytes);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row0 + r;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t cb = 1024u * c + 16u * lane;
+        const bool ok = live && row < a.N && cb < rbytes;
+        const uint32_t wo = ok ? uint32_t(row) * rbytes + cb : kOOB;
+        J.wg[r][c] = bld16(gres, wo);
+        J.wu[r][c] = bld16(ures, wo);
+        J.sg[r][c] = piece_scale<WF>(gsres, uint32_t(row) * sbytes, int(cb >> 4), ok);
+        J.su[r][c] = piece_scale<WF>(usres, uint32_t(row) * sbytes, int(cb >> 4), ok);
+      }
+    }
+    J.ts0 = J.ts1 = 1.f;
+    if constexpr (WF == WF_NV4) {
+      J.ts0 = *reinterpret_cast<const float *>(blob + a.off_t0);
+      J.ts1 = *reinterpret_cast<const float *>(blob + a.off_t1);
+    }
+  };
+  // multiply job j and write its hidden values
+  auto finish = [&](int j, const Job &J) {
+    const int ai = j / jobs_per_expert, row0 = (j - ai * jobs_per_expert) * RPW;
+    const int e = uniform(s_act[ai]);
+    const bool shared = e == a.E;
+    const bool missing = !shared && uniform(s_slot[e]) < 0;
+    const int p = shared ? a.k : ai;  // the token's permuted row of this expert: its rank among the picks
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        g = piece_dot<WF>(J.wg[r][c], J.sg[r][c], xv[c], g);
+        u = piece_dot<WF>(J.wu[r][c], J.su[r][c], xv[c], u);
+      }
+      g = wave_sum_f32(g) * J.ts0;
+      u = wave_sum_f32(u) * J.ts1;
+      const int row = row0 + r;
+      const uint16_t hval = missing ? uint16_t(0x7fc0) : f32_to_bf16_rne(silu(g) * u);
+      if (lane == 0 && row < a.N) {
+        if constexpr (NCHD > 0)  // read by other workgroups in this launch: stored coherent at agent scope
+          __builtin_amdgcn_raw_buffer_store_b16(hval, hres_out, uint32_t(p * a.ldo + row) * 2u, 0, kCoherentAgent);
+        else
+          reinterpret_cast<uint16_t *>(a.out)[int64_t(p) * a.ldo + row] = hval;
+      }
+    }
+  };
+  Job ring[2];
+  int j = int(blockIdx.x) * WAVES + wave;
+  issue(j, ring[0]);
+  while (j < n_jobs) {
+    issue(j + stride, ring[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(j, ring[0]);
+    j += stride;
+    if (j >= n_jobs) break;
+    issue(j + stride, ring[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(j, ring[1]);
+    j += stride;
+  }
+  if constexpr (NCHD > 0) token_down_after_wait<WF, NCHD, RB>(*d, bar, s_act, s_w, s_slot, s_nact);
+}
+
+// ---------------------------------------------------------------- down + combine, one token
+
+// Workgroup = block of RPW output rows; its 4 waves split the token's S = k
+// (+1 shared) steps (wave w takes steps w, w + 4, ...; at most SPW each).  A
+// wave issues every load of its steps at once -- the hidden row pieces and the
+// weight pieces of its rows -- so one HBM round trip covers them; the lane sums
+// w_s * (piece dot) over its steps, each row gets one wave sum, and the four
+// waves' sums meet in LDS (wave 0 adds them in wave order and writes out).
+template <int WF, int NCH, int RPW, int SPW>
+__device__ __forceinline__ void gemv_down_combine(const PersistArgs &a) {
+  using F = GemvFmt<WF>;
+  __shared__ float s_part[4][RPW];
+  // the wave index as a scalar: the steps, their expert blobs and buffer descriptors stay scalar
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const bool has_shared = a.shared_blob != nullptr;
+  const int S = a.k + (has_shared ? 1 : 0);
+  const int K = a.K;  // the hidden (contraction) length
+  const uint32_t rbytes = WF == WF_BF16 ? uint32_t(K) * 2 : uint32_t(K) / 2;
+  const uint32_t sbytes = WF == WF_FP4 ? uint32_t(K) / 32 : (WF == WF_NV4 ? uint32_t(K) / 16 : 0u);
+  const rsrc_t hres = make_rsrc(a.X, uint32_t(a.x_bytes));
+  const int row0 = int(blockIdx.x) * RPW;
+  // the slot table, loaded with the routing below in one round trip (lane l holds experts l, l+64, ...)
+  constexpr int VPL = kRouteMaxE / 64;
+  int st[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    st[i] = e < a.E ? table_slot(a.slot_of_expert, e, a.n_slots) : -1;
+  }
+  // this wave's steps: expert blob, hidden row, combine weight (scalar loads: uniform per wave)
+  const uint8_t *blob[SPW];
+  int kind[SPW], hrow[SPW];
+  float wgt[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int s = wave + 4 * j;
+    kind[j] = 3;  // past the steps: no loads, no contribution
+    blob[j] = a.pool;
+    hrow[j] = 0;
+    wgt[j] = 0.f;
+    if (s < a.k) {
+      const int e = a.ids[s];
+      int slot = -1;
+      if (e >= 0 && e < a.E) {  // expert e's entry: lane e % 64 of st[e / 64]
+        int v = st[0];
+#pragma unroll
+        for (int i = 1; i < VPL; ++i) v = (e >> 6) == i ? st[i] : v;
+        slot = __builtin_amdgcn_readlane(v, e & 63);
+      }
+      kind[j] = slot >= 0 ? 0 : 2;
+      blob[j] = a.pool + uint64_t(slot >= 0 ? slot : 0) * a.expert_bytes;
+      hrow[j] = a.row_pos[s];
+      wgt[j] = a.topk_w[s];
+    } else if (s < S) {
+      kind[j] = 1;
+      blob[j] = a.shared_blob;
+      hrow[j] = a.T * a.k;
+      wgt[j] = 1.f;
+    }
+  }
+  // every load of this wave's steps in flight at once
+  u32x4 hv[SPW][NCH][F::XV];
+  u32x4 w[SPW][RPW][NCH];
+  uint32_t sc[SPW][RPW][NCH];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const bool live = kind[j] != 3;
+    const rsrc_t wres = make_rsrc(blob[j] + a.off_w0, uint32_t(a.N) * rbytes);
+    const rsrc_t sres = make_rsrc(blob[j] + a.off_s0, uint32_t(a.N) * sbytes);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int v = 0; v < F::XV; ++v) {
+        const uint32_t el = uint32_t(64 * c + lane) * F::EPC + 8u * v;
+        hv[j][c][v] = bld16(hres, (live && el < uint32_t(K)) ? (uint32_t(hrow[j]) * uint32_t(a.ldx) + el) * 2u : kOOB);
+      }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int row = row0 + r;
+        const uint32_t cb = 1024u * c + 16u * lane;
+        const bool ok = live && row < a.N && cb < rbytes;
+        w[j][r][c] = bld16(wres, ok ? uint32_t(row) * rbytes + cb : kOOB);
+        sc[j][r][c] = piece_scale<WF>(sres, uint32_t(row) * sbytes, int(cb >> 4), ok);
+      }
+  }
+  float ts[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    ts[j] = 1.f;
+    if constexpr (WF == WF_NV4)
+      if (kind[j] == 0 || kind[j] == 1) ts[j] = *reinterpret_cast<const float *>(blob[j] + a.off_t0);
+  }
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    if (kind[j] == 3) continue;  // uniform per wave
+    const float ws = wgt[j] * ts[j];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      float d = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) d = piece_dot<WF>(w[j][r][c], sc[j][r][c], hv[j][c], d);
+      acc[r] = fmaf(ws, kind[j] == 2 ? __builtin_nanf("") : d, acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float v = wave_sum_f32(acc[r]);
+    if (lane == 0) s_part[wave][r] = v;
+  }
+  __syncthreads();
+  if (tid < RPW) {
+    const int row = row0 + tid;
+    const float v = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+    if (row < a.N) {
+      if (a.comb_bf16) reinterpret_cast<uint16_t *>(a.comb_out)[row] = f32_to_bf16_rne(v);
+      else reinterpret_cast<float *>(a.comb_out)[row] = v;
+    }
+  }
+}
+
+}  // namespace ft

@@ -10,6 +10,7 @@
 
 #include "ft_internal.hpp"
 #include "permute_util.hpp"
+#include "topk_util.hpp"
 #include "stream_gemm.hpp"
 
 namespace ft {
@@ -37,31 +38,38 @@ __global__ __launch_bounds__(WAVES * 64) void router_logits_bf16(const uint16_t 
 // bf16, a few tokens (T <= TT <= 4): one single-wave workgroup per expert,
 // so the router weights stream through E compute units instead of the E/16
 // workgroups of the MFMA tile.  Lane l dots the 8-element pieces l, l+64, ...
-// of the expert's row with the tokens' rows (fp32 fused multiply-adds), then
-// one wave sum per token.
+// of the expert's row with the tokens' rows (v_dot2: pairs of bf16 products
+// added into an fp32 sum), every piece of a 4096-element pass loaded before
+// the first product, then one wave sum per token.
 template <int TT>
 __global__ __launch_bounds__(64) void router_logits_gemv_bf16(const uint16_t *__restrict__ x,
                                                              const uint16_t *__restrict__ wr,
                                                              float *__restrict__ logits, int T, int H, int E) {
+  constexpr int NP = 8;  // 16-byte pieces per lane per pass: 4096 elements of the row, all loads in flight
   const int e = blockIdx.x, lane = threadIdx.x;
-  const uint16_t *w = wr + int64_t(e) * H;
+  // raw buffer loads: a piece past the row (or a token past T) reads zero without a branch
+  const rsrc_t wres = make_rsrc(wr + int64_t(e) * H, uint32_t(H) * 2u);
+  const rsrc_t xres = make_rsrc(x, uint32_t(T) * uint32_t(H) * 2u);
   float acc[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.f;
-#pragma unroll 4
-  for (int h = lane * 8; h < H; h += 512) {
-    const u32x4 wv = *reinterpret_cast<const u32x4 *>(w + h);
+  for (int h0 = 0; h0 < H; h0 += NP * 512) {
+    u32x4 wv[NP], xv[TT][NP];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      if (t < T) {
-        const u32x4 xv = *reinterpret_cast<const u32x4 *>(x + int64_t(t) * H + h);
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t h = uint32_t(h0 + 512 * p + 8 * lane);
+      wv[p] = bld16(wres, h < uint32_t(H) ? h * 2u : kOOB);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[t] = fmaf(__uint_as_float(wv[i] << 16), __uint_as_float(xv[i] << 16), acc[t]);
-          acc[t] = fmaf(__uint_as_float(wv[i] & 0xffff0000u), __uint_as_float(xv[i] & 0xffff0000u), acc[t]);
-        }
-      }
+      for (int t = 0; t < TT; ++t)
+        xv[t][p] = bld16(xres, (t < T && h < uint32_t(H)) ? (uint32_t(t) * uint32_t(H) + h) * 2u : kOOB);
     }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[t] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wv[p][i]), as_bf16x2(xv[t][p][i]), acc[t], false);
   }
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
@@ -86,110 +94,6 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float *__restrict
 // ------------------------------------------------------------------ top-k
 
 constexpr int kTopkWaves = 4;
-constexpr int kMaxE = 1024;  // 16 logits per lane
-constexpr int kMaxK = 256;
-
-__device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
-  return a > b || (a == b && ia < ib);
-}
-
-__device__ __forceinline__ float wave_sum(float v) { return wave_sum_f32(v); }
-
-// One wave per token.  Lane l holds the token's logits l, l+64, ... as 64-bit
-// keys: the logit mapped to an unsigned integer of the same order (-0.0 taken
-// as +0.0) in the high half, the complement of the expert index in the low
-// half, so that the largest key is the largest logit and, among equal logits,
-// the lowest index; all keys differ.  Pick j is found by one wave-wide max
-// (a lane-local max, then six butterfly steps) and its owner then drops it:
-// k rounds.  Then the gating weights of the picked experts.
-__device__ __forceinline__ uint32_t order_key(float x) {
-  if (x == 0.0f) x = 0.0f;  // -0.0 and +0.0 are the same key
-  const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// The logit an order key was made from (-0.0 comes back as +0.0).
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-// Top-k and gating of token t by one wave (all 64 lanes call it).  ids / w
-// receive the picks at [t * k + j]; ids_lds (nullable) gets the same ids.
-template <int VPL>
-__device__ __forceinline__ void topk_token(const float *__restrict__ logits, int t, int E, int k, int gating,
-                                           int renorm, int32_t *__restrict__ ids, float *__restrict__ w,
-                                           int32_t *ids_lds) {
-  const int lane = threadIdx.x & 63;
-  const float *lr = logits + int64_t(t) * E;
-  float v[VPL];
-  uint64_t key[VPL];
-  static_assert(kMaxK % 64 == 0, "picks are held 64 per slot");
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? lr[e] : -INFINITY;
-    key[i] = e < E ? (uint64_t(order_key(v[i])) << 32) | uint32_t(~e) : 0;  // 0: below every real key
-  }
-  // k rounds of wave arg-max; pick j ends up in lane j % 64, slot j / 64
-  constexpr int KS = kMaxK / 64;
-  int pid[KS];
-  float pval[KS];  // the picks' logits, recovered from their keys (no second read of the logits)
-#pragma unroll
-  for (int s2 = 0; s2 < KS; ++s2) {
-    pid[s2] = -1;
-    pval[s2] = 0.f;
-  }
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = int(~uint32_t(best));
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (key[i] == best) key[i] = 0;  // the owner drops its pick
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
-      if ((j >> 6) == s2 && lane == (j & 63)) {
-        pid[s2] = e;
-        pval[s2] = key_value(uint32_t(best >> 32));
-      }
-  }
-  // Gating.  softmax: p_e = exp(l_e - max) / sum_E exp(l - max); sigmoid: 1/(1+exp(-l)).
-  float mx = v[0];
-#pragma unroll
-  for (int i = 1; i < VPL; ++i) mx = fmaxf(mx, v[i]);
-  mx = wave_max_f32(mx);
-  float denom = 1.0f;
-  if (gating == FT_SOFTMAX) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (lane + 64 * i < E) s += expf(v[i] - mx);
-    denom = wave_sum(s);
-  }
-  float p[KS];
-  float local = 0.f;
-#pragma unroll
-  for (int s2 = 0; s2 < KS; ++s2) {
-    p[s2] = 0.f;
-    if (pid[s2] >= 0) {
-      const float x = pval[s2];
-      p[s2] = gating == FT_SOFTMAX ? expf(x - mx) / denom : 1.0f / (1.0f + expf(-x));
-      local += p[s2];
-    }
-  }
-  const float wsum = renorm ? wave_sum(local) : 1.0f;
-#pragma unroll
-  for (int s2 = 0; s2 < KS; ++s2) {
-    if (pid[s2] >= 0) {
-      const int jj = lane + 64 * s2;
-      ids[int64_t(t) * k + jj] = pid[s2];
-      w[int64_t(t) * k + jj] = renorm ? p[s2] / wsum : p[s2];
-      if (ids_lds) ids_lds[t * k + jj] = pid[s2];
-    }
-  }
-}
 
 template <int VPL>
 __global__ __launch_bounds__(64 * kTopkWaves) void topk_gating_kernel(const float *__restrict__ logits,
@@ -247,9 +151,9 @@ using namespace ft;
 
 // Checks the arguments of a routing call and launches the router logits
 // kernel when there is a router (FT_OK with nothing launched when T == 0).
-static ft_status route_logits(const void *x, int32_t x_dtype, const void *w_router, float *logits, int32_t T,
+ft_status ft::route_logits(const void *x, int32_t x_dtype, const void *w_router, float *logits, int32_t T,
                               int32_t H, int32_t E, int32_t k, int32_t gating, int32_t *topk_ids, float *topk_w,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool launch) {
   FT_REQUIRE(T >= 0 && E >= 1 && k >= 1, "ft_moe_route: need T >= 0, E >= 1, k >= 1");
   FT_SUPPORTED(k <= E, "ft_moe_route: k > E");
   FT_SUPPORTED(E <= kMaxE, "ft_moe_route: E > 1024");
@@ -275,13 +179,13 @@ static ft_status route_logits(const void *x, int32_t x_dtype, const void *w_rout
   if (w_router != nullptr) {
     FT_REQUIRE(x != nullptr, "ft_moe_route: x is NULL");
     FT_REQUIRE(aligned(x, 16) && aligned(w_router, 16), "ft_moe_route: x / w_router must be 16-byte aligned");
+    if (!launch) return FT_OK;
     if (x_dtype == FT_BF16) {
       const uint16_t *xb = static_cast<const uint16_t *>(x);
       const uint8_t *wb = static_cast<const uint8_t *>(w_router);
-      // One wave per expert for a few tokens and a large router (1-token decode,
-      // 256 x 4096 router: 54.7 against 56.4 us per step); at 128 x 2048 the
-      // MFMA tile measured 0.4 us faster, so it keeps those.
-      if (T <= 4 && int64_t(E) * H >= (int64_t(1) << 20)) {
+      // One wave per expert for a few tokens (one-token decode, 256 x 4096 router: 3.2 us against
+      // 5.1 us for the MFMA tile).
+      if (T <= 4) {
         const uint16_t *wh = static_cast<const uint16_t *>(w_router);
         if (T == 1)
           hipLaunchKernelGGL(router_logits_gemv_bf16<1>, dim3(unsigned(E)), dim3(64), 0, stream, xb, wh, logits, T, H, E);

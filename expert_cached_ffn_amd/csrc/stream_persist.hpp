@@ -15,12 +15,20 @@
 // buffer loads; out-of-range offsets return zero without memory traffic).
 #pragma once
 
+#include "permute_util.hpp"
 #include "stream_gemm.hpp"
+#include "topk_util.hpp"
 
 namespace ft {
 
 constexpr int kPersistMaxE = 1024;     // experts the LDS table holds (larger E uses the plain kernel)
 constexpr int kPersistMaxRows = 4096;  // routed rows whose token indices fit the LDS copy
+
+// Small decode batches routed inside the FFN (the layer call's fused path).
+constexpr int kRouteMaxT = 4;          // tokens (one wave each in the routing prologue)
+constexpr int kRouteMaxE = 256;        // experts (four logits per lane)
+constexpr int kRouteMaxRows = 64;      // routed rows (one wave sorts them)
+constexpr int kFusedMaxK = 16;       // picks per token of the fused combine
 
 struct PersistArgs {
   const uint8_t *pool;
@@ -40,8 +48,46 @@ struct PersistArgs {
   void *out;                      // GLU: bf16 hidden rows; else fp32 rows
   int64_t ldo;
   float *out_shared;              // non-GLU: rows of the shared expert go here (by token)
-  int n_tiles;                    // ceil(N / 16)
+  int n_tiles;                    // ceil(N / tile rows)
+  int tile_rows;                  // fused layer call: weight rows per tile, 16 or 8 (other kernels: 16)
+  // routing prologue (gate/up of the fused layer call): every workgroup takes top-k, gating and the
+  // permutation of the T tokens from the logits; workgroup 0 also writes them out
+  const float *logits;            // [T, E]
+  int gating, renorm;
+  int32_t *ids_out, *off_out, *rows_out, *pos_out;
+  float *w_out;
+  // combine folded into the down stage (fused layer call): out[t] = sum_j w[t, j] y_j (+ shared)
+  const int32_t *ids;             // [T, k]
+  const float *topk_w;            // [T, k]
+  const int32_t *row_pos;         // [T*k]: hidden row of pick (t, j)
+  void *comb_out;                 // [T, ldo] bf16 or fp32
+  int comb_bf16;
 };
+
+// Top-k, gating and the permutation of the batch's T <= kRouteMaxT tokens by
+// one workgroup (wave t takes token t; wave 0 then sorts the T*k <= 64 rows),
+// into LDS; workgroup 0 also writes ids, weights, offsets, sorted rows and
+// row positions out for the down stage, the combine and the caller.
+template <int THREADS>
+__device__ __forceinline__ void route_prologue(const PersistArgs &a, int32_t *s_ids, int32_t *s_off,
+                                               int32_t *s_rows, int32_t *s_pos, int32_t *s_sorted) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const bool pub = blockIdx.x == 0;
+  if (wave < a.T)
+    topk_token<kRouteMaxE / 64>(a.logits, wave, a.E, a.k, a.gating, a.renorm, pub ? a.ids_out : nullptr,
+                                pub ? a.w_out : nullptr, s_ids);
+  __syncthreads();
+  const int R = a.T * a.k;
+  if (wave == 0) permute_wave64(s_ids, R, a.E, s_sorted, s_off, s_rows, s_pos);
+  __syncthreads();
+  if (pub) {
+    for (int e = tid; e <= a.E; e += THREADS) a.off_out[e] = s_off[e];
+    for (int p = tid; p < R; p += THREADS) {
+      a.rows_out[p] = s_rows[p];
+      a.pos_out[p] = s_pos[p];
+    }
+  }
+}
 
 // A value every lane of the wave holds (an LDS table entry read at a uniform
 // index) moved to a scalar register, so descriptors built from it stay scalar.
@@ -305,10 +351,18 @@ constexpr int kPersistMaxGroups = kPersistMaxE + 1 + kPersistMaxRows / 16;
 // with the same activation registers and summed in one LDS round, which
 // halves the barriers per weight byte where a tile is small (NVFP4 tiles of a
 // short contraction).
-template <int WF, bool GLU, int WAVES, int KPW, int NB, int RT = 1>
+//
+// ROUTE: the gate/up stage of the fused layer call -- the segments come from
+// route_prologue instead of offsets / sorted rows in memory.
+// With ROUTE the weight rows per tile are a.tile_rows, 16 or 8 (8: rows 8..15
+// of the MFMA operand load nothing; twice the units, for batches whose 16-row
+// units would not spread evenly over the compute units).
+template <int WF, bool GLU, int WAVES, int KPW, int NB, int RT = 1, bool ROUTE = false>
 __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s_red) {
   static_assert(NB >= 2, "the ring needs two register sets");
   static_assert(RT == 1 || (RT == 2 && !GLU), "two row tiles per unit: down stage only");
+  static_assert(!ROUTE || GLU, "the routing prologue feeds the gate/up stage");
+  const int TR = ROUTE ? a.tile_rows : 16;
   constexpr int THREADS = WAVES * 64;
   constexpr int NW = WAVES;
   constexpr int MATS = GLU ? 2 : RT;
@@ -323,9 +377,18 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
   __shared__ int s_gexp[kPersistMaxGroups];  // active expert of token group g
   __shared__ int s_cnt[NW];
   __shared__ int s_tok[kPersistMaxRows];     // token of every routed row (gather mode)
+  constexpr int RE = ROUTE ? kRouteMaxE + 1 : 1, RR = ROUTE ? kRouteMaxRows : 1;
+  __shared__ int32_t s_roff[RE], s_rids[RR], s_rrows[RR], s_rpos[RR], s_rsorted[RR];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (a.sorted_rows != nullptr)
-    for (int p = tid; p < a.T * a.k; p += THREADS) s_tok[p] = a.sorted_rows[p] / a.k;
+  const int32_t *offs = a.offsets, *srows = a.sorted_rows;
+  if constexpr (ROUTE) {
+    route_prologue<THREADS>(a, s_rids, s_roff, s_rrows, s_rpos, s_rsorted);
+    offs = s_roff;
+    srows = s_rrows;
+  }
+  const bool gather = srows != nullptr;
+  if (gather)
+    for (int p = tid; p < a.T * a.k; p += THREADS) s_tok[p] = srows[p] / a.k;
   const int r = lane & 15, q = lane >> 4;
 
   // ---- active-expert table (ascending expert id, then the shared expert)
@@ -334,8 +397,8 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     const int e = c0 + tid;
     int lo = 0, cnt = 0;
     if (e < a.E) {
-      lo = a.offsets[e];
-      cnt = a.offsets[e + 1] - lo;
+      lo = offs[e];
+      cnt = offs[e + 1] - lo;
       if (cnt > 0 && a.slot_of_expert != nullptr && a.slot_of_expert[e] == FT_SLOT_SKIP) cnt = 0;  // another call's
     }
     const bool f = cnt > 0;
@@ -422,10 +485,11 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     uint32_t wo[MATS], so[MATS];
 #pragma unroll
     for (int mt = 0; mt < MATS; ++mt) {
-      // rows past N fall outside the buffer (zeros, no traffic)
-      const int row = tile * 16 * RT + (GLU ? 0 : 16 * mt) + r;
-      wo[mt] = tile >= 0 ? uint32_t(row) * wpitch + uint32_t(q) * 16 : kOOB;
-      so[mt] = tile >= 0 ? uint32_t(row) * spitch : kOOB;
+      // rows past N fall outside the buffer (zeros, no traffic); so do operand rows past TR
+      const int row = tile * TR * RT + (GLU ? 0 : 16 * mt) + r;
+      const bool live = tile >= 0 && r < TR;
+      wo[mt] = live ? uint32_t(row) * wpitch + uint32_t(q) * 16 : kOOB;
+      so[mt] = live ? uint32_t(row) * spitch : kOOB;
     }
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
@@ -444,7 +508,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     const int j = g0 + r;
     int row = -1;
     if (j < m) {
-      if (a.sorted_rows == nullptr) row = pos + j;      // hidden row p
+      if (!gather) row = pos + j;                        // hidden row p
       else row = e == a.E ? j : s_tok[pos + j];         // token of the shared / routed expert
     }
     const uint32_t xo = row >= 0 ? uint32_t(row) * uint32_t(a.ldx) * 2u : kOOB;
@@ -509,7 +573,8 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     if (tid < 256) {
       const int ln = tid >> 2, v = tid & 3;
       const int jj = g0 + (ln & 15);
-      const int n = tile * 16 * RT + 4 * (ln >> 4) + v;  // RT = 2: uu is row n + 16
+      const int nr = 4 * (ln >> 4) + v;                 // row inside the tile
+      const int n = tile * TR * RT + nr;                 // RT = 2: uu is row n + 16
       float g = 0.f, uu = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
@@ -521,7 +586,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
         if constexpr (GLU) uu *= ts1;
         else if constexpr (RT == 2) uu *= ts0;
       }
-      if (jj < m && n < a.N) {
+      if (jj < m && n < a.N && nr < TR) {
         const int p = pos + jj;  // permuted row; hidden rows of the shared expert follow the routed ones
         if constexpr (GLU) {
           reinterpret_cast<uint16_t *>(a.out)[int64_t(p) * a.ldo + n] =

@@ -89,6 +89,9 @@ class MoELayer:
         self.ws_rp_bytes = ops.ft_workspace_bytes(_lib.FT_WS_ROUTE_PERMUTE, T_max, k, E)
         self.ws_rp = torch.empty(max(256, self.ws_rp_bytes), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty(max(256, self.ws_ffn_bytes), dtype=torch.uint8, device=dev)
+        self.ws_layer_bytes = ops.ft_workspace_bytes(_lib.FT_WS_LAYER, T_max, k, E, H, shape.I)
+        # zeroed: its first 256 bytes are the one-token kernel's wait words (every call leaves them zero)
+        self.ws_layer = torch.zeros(max(256, self.ws_layer_bytes), dtype=torch.uint8, device=dev)
 
     def route(self, T, x=None, w_router=None, logits=None, stream=None):
         s = self.s
@@ -134,6 +137,21 @@ class MoELayer:
     def run_cpu_misses(self, cache, stream=None, n_threads=0):
         """After ffn(): the CPU misses' rows on the host, copied into y_rows on the stream."""
         cache.run_cpu_misses(self.y_rows, stream=stream, n_threads=n_threads)
+
+    def forward_layer(self, T, x, pool, w_router=None, logits=None, slot_of_expert=None, shared_blob=None,
+                      stream=None, mode=0):
+        """The whole layer through ft_moe_layer (three launches for a few tokens)."""
+        s = self.s
+        if logits is not None:
+            self.logits[:T].copy_(logits[:T])
+            w_router = None
+        out_dt = _lib.FT_F32 if s.xdtype == "f32" else _lib.FT_BF16
+        ops.ft_moe_layer(self.layout, pool, slot_of_expert, shared_blob, x, DTYPES[s.xdtype], w_router, self.logits,
+                         T, s.E, s.k, GATING[s.gating], s.renormalize, self.ids, self.w, self.offsets,
+                         self.sorted_rows, self.row_pos, self.y_rows,
+                         self.y_shared if shared_blob is not None else None, mode, out_dt, self.out,
+                         self.ws_layer, self.ws_layer_bytes, stream=stream)
+        return self.out[:T]
 
     def forward(self, T, x, pool, w_router=None, logits=None, slot_of_expert=None, shared_blob=None,
                 stream=None, mode=0):

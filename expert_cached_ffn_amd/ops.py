@@ -94,6 +94,20 @@ def ft_moe_grouped_ffn(layout: ExpertLayout, slot_pool, slot_of_expert, shared_b
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def ft_moe_layer(layout: ExpertLayout, slot_pool, slot_of_expert, shared_blob, x, x_dtype: int, w_router, logits,
+                 T: int, E: int, k: int, gating: int, renormalize: int, topk_ids, topk_w, expert_offsets,
+                 sorted_rows, row_pos, y_rows, y_shared, mode: int, out_dtype: int, out, workspace,
+                 workspace_bytes: int, stream=None, n_slots: int | None = None) -> None:
+    if n_slots is None:
+        n_slots = slot_pool.numel() * slot_pool.element_size() // int(layout.expert_bytes) \
+            if hasattr(slot_pool, "numel") else E
+    _check(_lib.lib().ft_moe_layer(C.byref(layout), _ptr(slot_pool), int(n_slots), _ptr(slot_of_expert),
+                                   _ptr(shared_blob), _ptr(x), x_dtype, _ptr(w_router), _ptr(logits), T, E, k,
+                                   gating, int(renormalize), _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                                   _ptr(sorted_rows), _ptr(row_pos), _ptr(y_rows), _ptr(y_shared), mode,
+                                   out_dtype, _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def ft_moe_grouped_ffn_noalloc(layout: ExpertLayout, slot_pool, slot_of_expert, shared_blob, x, x_dtype: int,
                                T: int, k: int, E: int, expert_offsets, sorted_rows, y_rows, y_shared,
                                mode: int = 0, stream=None, n_slots: int | None = None) -> None:

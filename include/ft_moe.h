@@ -343,6 +343,48 @@ ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t
                          const float *y_shared, int32_t T, int32_t k, int32_t H,
                          int32_t out_dtype, void *out, hipStream_t stream);
 
+/*
+ * ft_moe_layer -- the whole routed MoE layer in one call: ft_moe_route_permute,
+ * ft_moe_grouped_ffn and ft_moe_combine with the arguments below, the same
+ * results (the routing outputs, out) and the same errors, all checked before
+ * anything is enqueued.  The pages' decode produces tokens one at a time
+ * (FreeToken 290b model page, "Cómo gestiona FreeToken el prellenado y la
+ * decodificación"); with 1 <= T <= 4 tokens, exact mode, bf16 / MXFP4 / NVFP4
+ * weights, E <= 256, k <= 16 and a contraction length the persistent decode
+ * kernels cover, the layer runs as three launches instead of five:
+ *   1. the router logits (when w_router != NULL);
+ *   2. gate/up + SwiGLU, each workgroup taking top-k, gating and the
+ *      permutation from the logits itself (one workgroup writes topk_ids,
+ *      topk_w, expert_offsets, sorted_rows and row_pos);
+ *   3. the down projection with the combine folded in: each output element
+ *      is sum_j topk_w[t, j] * y_j (+ the shared expert's) in fp32, rounded
+ *      once -- y_rows and y_shared are then NOT written.
+ * With T = 1 and at most 8 down steps (k routed + the shared expert), steps 2
+ * and 3 are one launch whose workgroups meet at a grid-wide wait.  Other
+ * calls make the three calls in turn (y_rows / y_shared written as there).
+ * An expert whose slot is negative (FT_SLOT_SKIP included) or >= n_slots
+ * gives NaN outputs for the tokens that picked it.
+ * Arguments: as for the three calls (x, x_dtype, w_router, logits, T, E, k,
+ * gating, renormalize, topk_ids, topk_w, expert_offsets, sorted_rows, row_pos
+ * as ft_moe_route_permute; L, slot_pool, n_slots, slot_of_expert,
+ * shared_blob, y_rows, y_shared, mode as ft_moe_grouped_ffn -- mode without
+ * stage bits; out_dtype, out as ft_moe_combine, H = L->H).
+ * workspace: ft_workspace_bytes(FT_WS_LAYER, T, k, E, H, I) bytes, 256-byte
+ * aligned.  Its first 8192 bytes hold the grid-wide wait's counters: zero them
+ * once before the first call on a workspace (every call leaves them zero; a
+ * wait that gives up -- it never should -- writes NaN outputs and may leave
+ * them non-zero).  The rest is the steps' workspace; after the call its start
+ * (byte 8192) holds the bf16 hidden rows, as for ft_moe_grouped_ffn.  Calls
+ * that share a workspace must not overlap.
+ */
+ft_status ft_moe_layer(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
+                       const int32_t *slot_of_expert, const void *shared_blob, const void *x, int32_t x_dtype,
+                       const void *w_router, float *logits, int32_t T, int32_t E, int32_t k, int32_t gating,
+                       int32_t renormalize, int32_t *topk_ids, float *topk_w, int32_t *expert_offsets,
+                       int32_t *sorted_rows, int32_t *row_pos, float *y_rows, float *y_shared, int32_t mode,
+                       int32_t out_dtype, void *out, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Expert cache                                                               */
 /* ------------------------------------------------------------------------ */
@@ -617,7 +659,7 @@ ft_status ft_expert_cache_destroy(ft_expert_cache *c);
 /* ------------------------------------------------------------------------ */
 /* Workspace sizes                                                            */
 /* ------------------------------------------------------------------------ */
-enum { FT_WS_PERMUTE = 1, FT_WS_FFN = 2, FT_WS_ROUTE_PERMUTE = 3 };
+enum { FT_WS_PERMUTE = 1, FT_WS_FFN = 2, FT_WS_ROUTE_PERMUTE = 3, FT_WS_LAYER = 4 };
 
 /* Bytes of workspace the call `which` needs for these sizes (0 if none).
  * For FT_WS_FFN, H and I are those of the layout and the shared expert is

