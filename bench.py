@@ -239,6 +239,15 @@ def run_decode(args, cfg, batches, main_T):
         for i in range(args.warmup):
             lstep(i)
         torch.cuda.synchronize()
+        # the mean from events around the whole run; the spread from a second run with an event
+        # between every two steps (those markers add a little time of their own)
+        with no_gc():
+            start.record()
+            for i in range(args.steps):
+                lstep(i)
+            end.record()
+        torch.cuda.synchronize()
+        lms = start.elapsed_time(end) / args.steps
         lt = Timer(args.steps + 1)
         with no_gc():
             for i in range(args.steps):
@@ -247,8 +256,7 @@ def run_decode(args, cfg, batches, main_T):
             lt.mark()
         torch.cuda.synchronize()
         lstep_ms = [lt.ev[i].elapsed_time(lt.ev[i + 1]) for i in range(args.steps)]
-        lms = lt.ev[0].elapsed_time(lt.ev[args.steps]) / args.steps
-        lgraph_ms = None
+        lgraph_ms = lgraph8_ms = None
         if not args.no_graph:
             lgraphs = []
             s = torch.cuda.Stream()
@@ -270,15 +278,36 @@ def run_decode(args, cfg, batches, main_T):
                 end.record()
             torch.cuda.synchronize()
             lgraph_ms = start.elapsed_time(end) / args.steps
+            # one graph holding a layer call for each of the input sets in turn, as a decode step's
+            # graph holds its model's layers one after another: per-replay costs spread over them
+            g8 = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g8, stream=s):
+                    for r in range(N_INPUT_SETS):
+                        lstep(r)
+            torch.cuda.current_stream().wait_stream(s)
+            reps = max(1, args.steps // N_INPUT_SETS)
+            for i in range(max(1, args.warmup // N_INPUT_SETS)):
+                g8.replay()
+            torch.cuda.synchronize()
+            with no_gc():
+                start.record()
+                for i in range(reps):
+                    g8.replay()
+                end.record()
+            torch.cuda.synchronize()
+            lgraph8_ms = start.elapsed_time(end) / (reps * N_INPUT_SETS)
         # one layer call is the unit of work: its time gives tokens/s; the four calls (with events
         # around the gate/up launch for the roofline) are reported beside it
         results[T] = dict(ms_per_step=lms, tokens_per_s=T / (lms * 1e-3), gate_up_ms=k_avg,
                           step_ms_p10_p50_p90=[float(v) for v in np.percentile(lstep_ms, [10, 50, 90])],
                           gate_up_bytes=bytes_gu, layer_weight_bytes=layer_bytes,
                           distinct_experts=float(np.mean(n_act)), graph_ms_per_step=lgraph_ms,
+                          graph_of_8_steps_ms_per_step=lgraph8_ms,
                           four_calls_ms_per_step=ms, four_calls_graph_ms_per_step=graph_ms,
                           four_calls_step_ms_p10_p50_p90=[float(v) for v in np.percentile(step_ms, [10, 50, 90])])
-        gtxt = f"{lgraph_ms * 1e3:.1f} us" if lgraph_ms is not None else "n/a"
+        gtxt = (f"{lgraph_ms * 1e3:.1f} us (8 steps per graph {lgraph8_ms * 1e3:.1f} us)"
+                if lgraph_ms is not None else "n/a")
         g4 = f"{graph_ms * 1e3:.1f} us" if graph_ms is not None else "n/a"
         log(f"T={T}: layer call {lms * 1e3:.1f} us/step ({T / (lms * 1e-3):,.0f} tok/s), graph {gtxt}; four calls "
             f"{ms * 1e3:.1f} us, graph {g4}; gate/up {k_avg * 1e3:.1f} us = {bytes_gu / (k_avg * 1e-3) / 1e9:,.0f} GB/s, "
@@ -907,6 +936,7 @@ def decode_summary(cfg, res, main_T, peaks, traffic=None):
         "step_ms_p10_p50_p90": m["step_ms_p10_p50_p90"], "graph_ms_per_step": m["graph_ms_per_step"],
         "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
                              "graph_ms_per_step": r["graph_ms_per_step"],
+                             "graph_of_8_steps_ms_per_step": r["graph_of_8_steps_ms_per_step"],
                              "four_calls_ms_per_step": r["four_calls_ms_per_step"],
                              "four_calls_graph_ms_per_step": r["four_calls_graph_ms_per_step"],
                              "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],

@@ -41,50 +41,69 @@ struct GemvFmt {
 // (MXFP4, applied in the conversion) or later times an E4M3 scale of 4 significant bits (NVFP4,
 // applied to each 16-element block's sum, since the scaled conversions use only the exponent of
 // their scale).
+// Four partial sums per dot product, one per dword of the piece, so that consecutive v_dot2 do not
+// wait on each other (a single accumulator chained 16 of them per MXFP4 piece: measured 3 us of a
+// 27 us one-token layer in the products).
+struct Acc4 {
+  float a[4];
+  __device__ __forceinline__ Acc4() : a{0.f, 0.f, 0.f, 0.f} {}
+  __device__ __forceinline__ float sum() const { return (a[0] + a[1]) + (a[2] + a[3]); }
+};
+
 template <int WF>
-__device__ __forceinline__ float piece_dot(const u32x4 w, const uint32_t sc, const u32x4 *x, float acc) {
+__device__ __forceinline__ void piece_dot(const u32x4 w, const uint32_t scw, const u32x4 *x, Acc4 &acc) {
+  // the lane's scale bits in the dword piece_scale loaded (piece 64 c + lane: byte lane % 4 for
+  // MXFP4, bytes 2 (lane % 2) and up for NVFP4)
+  const uint32_t sc = WF == WF_FP4 ? scw >> (8 * (threadIdx.x & 3)) : scw >> (16 * (threadIdx.x & 1));
   if constexpr (WF == WF_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[i]), as_bf16x2(x[0][i]), acc, false);
+    for (int i = 0; i < 4; ++i)
+      acc.a[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[i]), as_bf16x2(x[0][i]), acc.a[i], false);
   } else if constexpr (WF == WF_FP4) {
     // dword d holds elements 8d .. 8d+7, byte b of it elements 8d+2b, 8d+2b+1 (low nibble first);
     // activations dword x[d][b] holds the same two elements (the selector operand must be a literal)
     const float s = e8m0_to_f32(sc & 0xffu);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 0), as_bf16x2(x[d][0]), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 1), as_bf16x2(x[d][1]), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 2), as_bf16x2(x[d][2]), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 3), as_bf16x2(x[d][3]), acc, false);
+      float t = acc.a[d];
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 0), as_bf16x2(x[d][0]), t, false);
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 1), as_bf16x2(x[d][1]), t, false);
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 2), as_bf16x2(x[d][2]), t, false);
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 3), as_bf16x2(x[d][3]), t, false);
+      acc.a[d] = t;
     }
   } else {
     // two 16-element blocks (dwords 0-1: scale byte 0, dwords 2-3: byte 1), each summed unscaled
-    float blk[2] = {0.f, 0.f};
+    float blk[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      float &b = blk[d >> 1];
+      float b = 0.f;
       b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 0), as_bf16x2(x[d][0]), b, false);
       b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 1), as_bf16x2(x[d][1]), b, false);
       b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 2), as_bf16x2(x[d][2]), b, false);
       b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 3), as_bf16x2(x[d][3]), b, false);
+      blk[d] = b;
     }
-    acc = fmaf(e4m3_to_f32(sc & 0xffu), blk[0], acc);
-    acc = fmaf(e4m3_to_f32((sc >> 8) & 0xffu), blk[1], acc);
+    const float s0 = e4m3_to_f32(sc & 0xffu), s1 = e4m3_to_f32((sc >> 8) & 0xffu);
+    acc.a[0] = fmaf(s0, blk[0], acc.a[0]);
+    acc.a[1] = fmaf(s0, blk[1], acc.a[1]);
+    acc.a[2] = fmaf(s1, blk[2], acc.a[2]);
+    acc.a[3] = fmaf(s1, blk[3], acc.a[3]);
   }
-  return acc;
 }
 
-// Scale bits of piece `piece` of the row whose scales start at byte `so` of `sres` (the 4-bit
-// formats), read as the aligned dword that holds them (no per-lane byte loads; an offset at or past
-// the buffer gives 0).  MXFP4: one byte; NVFP4: two bytes, elements 0..15 then 16..31.
+// The aligned dword holding the scale bits of piece `piece` (= 64 c + lane) of the row whose scales
+// start at byte `so` of `sres` (the 4-bit formats; no per-lane byte loads; an offset at or past the
+// buffer gives 0).  MXFP4: one byte; NVFP4: two bytes, elements 0..15 then 16..31.  The word is
+// returned as loaded: piece_dot shifts the lane's bits out where it uses them, so that issuing a
+// job's loads never waits for one of them.
 template <int WF>
 __device__ __forceinline__ uint32_t piece_scale(rsrc_t sres, uint32_t so, int piece, bool ok) {
   if constexpr (WF == WF_BF16) {
     return 0u;
   } else {
     const uint32_t b = WF == WF_FP4 ? uint32_t(piece) : 2u * uint32_t(piece);
-    const uint32_t word = bld4(sres, ok ? so + (b & ~3u) : kOOB);
-    return word >> (8 * (b & 3u));
+    return bld4(sres, ok ? so + (b & ~3u) : kOOB);
   }
 }
 
@@ -105,14 +124,27 @@ struct TokenPick {
   int rank;   // position of the pick among the picks in ascending expert id = its permuted row
 };
 
-__device__ __forceinline__ TokenPick one_token_route(const float *__restrict__ lr, int E, int k, int gating,
+// The token's logits, lane l holding experts l, l + 64, ... (separate from the routing so that loads
+// which do not depend on it can be issued between the two).
+struct TokenLogits {
+  float v[kRouteMaxE / 64];
+};
+
+__device__ __forceinline__ TokenLogits one_token_logits(const float *__restrict__ lr, int E) {
+  const int lane = threadIdx.x & 63;
+  const rsrc_t res = make_rsrc(lr, uint32_t(E) * 4u);  // past E: 0 (masked by the routing)
+  TokenLogits t;
+#pragma unroll
+  for (int i = 0; i < kRouteMaxE / 64; ++i) t.v[i] = __uint_as_float(bld4(res, uint32_t(lane + 64 * i) * 4u));
+  return t;
+}
+
+__device__ __forceinline__ TokenPick one_token_route(const TokenLogits &lg, int E, int k, int gating,
                                                      int renorm) {
   constexpr int VPL = kRouteMaxE / 64;
   const int lane = threadIdx.x & 63;
-  float v[VPL];
+  const float *v = lg.v;
   uint32_t key[VPL];
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) v[i] = lr[lane + 64 * i < E ? lane + 64 * i : 0];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     // 0 marks "absent or already picked": real keys start at 1 (only the all-ones NaN maps to 0)
@@ -283,14 +315,17 @@ __device__ __forceinline__ void token_down_after_wait(const PersistArgs &d, uint
     }
   for (; rb < blocks; rb += int(gridDim.x)) {
     if (rb != int(blockIdx.x)) issue(rb);
+    float dv[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-      float dd = 0.f;
+      Acc4 dd;
 #pragma unroll
-      for (int c = 0; c < NCHD; ++c) dd = piece_dot<WF>(w[r][c], sc[r][c], hv[c], dd);
-      dd = wave_sum_f32(dd);
-      if (lane == 0) s_part[wave][r] = missing ? __builtin_nanf("") : wgt * (ts * dd);
+      for (int c = 0; c < NCHD; ++c) piece_dot<WF>(w[r][c], sc[r][c], hv[c], dd);
+      dv[r] = dd.sum();
     }
+    const float tot = wave_sums<RB>(dv);
+    if ((lane & (RB == 8 ? 7 : 15)) == 0)  // the first lane of each group holds one row's total
+      s_part[wave][wave_sums_index<RB>(lane)] = missing ? __builtin_nanf("") : wgt * (ts * tot);
     __syncthreads();
     if (tid < RB) {
       const int row = rb * RB + tid;
@@ -310,27 +345,28 @@ __device__ __forceinline__ void token_down_after_wait(const PersistArgs &d, uint
 // ---------------------------------------------------------------- gate/up + SwiGLU, one token
 
 // Work is a list of wave jobs: RPW consecutive (gate row, up row) pairs of one
-// expert, the routed experts' in ascending id, then the shared expert's.
-// Every workgroup routes the token itself (one_token_route; workgroup 0
-// publishes the result); its waves then walk the job
-// list with a stride of all the grid's waves, the next job's loads issued
-// before the current job is multiplied.  The grid is sized to the workgroups
-// that fit on the device at once, so no workgroup pays the prologue in a
-// second round.
+// expert, the shared expert's first (when there is one), then the routed
+// experts' in ascending id.  Every workgroup routes the token itself
+// (one_token_route; workgroup 0 publishes the result); its waves then walk
+// the job list with a stride of all the grid's waves, the next job's loads
+// issued before the current job is multiplied.  The grid is sized to the
+// workgroups that fit on the device at once, so no workgroup pays the
+// prologue in a second round.
 //
-// Data every wave reads is fetched once per workgroup: the token's
-// activations go through LDS (per wave they would be the same few KiB read
-// by thousands of waves from the few L2 channels that hold them), issued
-// together with the slot table entries before the top-k waits on the router
-// logits.  Large (8-wave) workgroups keep that shared traffic small.
+// What does not depend on the routing is in flight before it: the token's
+// activations, the slot table entries and, for waves whose first job is a
+// shared-expert job, that job's weights -- issued after the logits' loads, so
+// the top-k waits only for the logits.  Data every wave reads is fetched once
+// per workgroup: the activations go through LDS (per wave they would be the
+// same few KiB read by thousands of waves from the few L2 channels that hold
+// them), and large (8-wave) workgroups keep that shared traffic small.
 template <int WF, int NCH, int RPW, int NCHD = 0, int RB = 0>
 __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const PersistArgs *d = nullptr,
                                              uint32_t *bar = nullptr) {
   constexpr int THREADS = kGemvGuThreads, WAVES = THREADS / 64;
-  static_assert(kRouteMaxE <= THREADS, "one slot table entry per thread");
   using F = GemvFmt<WF>;
   constexpr int XN = NCH * 64 * F::XV;            // u32x4 of activations the lanes' pieces cover
-  constexpr int XPT = (XN + THREADS - 1) / THREADS;
+  constexpr int XPL = (XN + 63) / 64;             // of them per lane of wave 0
   __shared__ int s_act[kFusedMaxK + 1];     // the picks in ascending id (= their rows), then the shared expert
   __shared__ float s_w[kFusedMaxK + 1];     // their gating weights
   __shared__ int s_slot[kRouteMaxE];        // slot of every expert (-1: not resident)
@@ -341,17 +377,85 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
   const uint32_t sbytes = WF == WF_FP4 ? uint32_t(a.K) / 32 : (WF == WF_NV4 ? uint32_t(a.K) / 16 : 0u);
   // Raw buffer loads throughout: an offset past the buffer reads zero without a branch, so a job's
   // loads are all issued before the first wait.
+  // Wave 0 loads what the workgroup shares -- activations, slot table, logits -- and routes; the
+  // other waves meanwhile issue their first job when it is a shared-expert job.
   const rsrc_t xres = make_rsrc(a.X, uint32_t(a.K) * 2u);
-  u32x4 xg[XPT];
+  constexpr int SPL = kRouteMaxE / 64;
+  u32x4 xg[XPL];
+  int sl[SPL];
+  TokenLogits lg;
+  if (wave == 0) {
 #pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const uint32_t u = uint32_t(tid + THREADS * i);
-    xg[i] = bld16(xres, u < uint32_t(XN) ? u * 16u : kOOB);
+    for (int i = 0; i < XPL; ++i) {
+      const uint32_t u = uint32_t(lane + 64 * i);
+      xg[i] = bld16(xres, u < uint32_t(XN) ? u * 16u : kOOB);
+    }
+    // the slot table as raw words (a buffer of no bytes when there is none): no wait before the
+    // logits' loads are issued
+    const rsrc_t stres = make_rsrc(a.slot_of_expert, a.slot_of_expert != nullptr ? uint32_t(a.E) * 4u : 0u);
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) sl[i] = int(bld4(stres, uint32_t(lane + 64 * i) * 4u));
+    lg = one_token_logits(a.logits, a.E);
   }
-  const int my_slot = tid < a.E ? table_slot(a.slot_of_expert, tid, a.n_slots) : -1;
+
+  const int has_shared = a.shared_blob != nullptr ? 1 : 0;
+  const int jobs_per_expert = (a.N + RPW - 1) / RPW;
+  struct Job {
+    u32x4 wg[RPW][NCH], wu[RPW][NCH];
+    uint32_t sg[RPW][NCH], su[RPW][NCH];
+    float ts0, ts1;  // NVFP4 tensor scales
+  };
+  // job list entry ai: the shared expert at 0 (reads no LDS), then the picks by rank (= hidden row)
+  auto job_expert = [&](int ai) { return has_shared && ai == 0 ? a.E : uniform(s_act[ai - has_shared]); };
+  auto job_row = [&](int ai) { return has_shared && ai == 0 ? a.k : ai - has_shared; };
+  // the loads of job j (live false: offsets past the buffers, nothing read)
+  auto issue = [&](int j, bool live, Job &J) {
+    const int jj = live ? j : 0;
+    const int ai = jj / jobs_per_expert, row0 = (jj - ai * jobs_per_expert) * RPW;
+    const int e = live ? job_expert(ai) : -1;  // -1: no job, the loads stay past the pool's first blob
+    const int slot = e < 0 || e == a.E ? 0 : uniform(s_slot[e]);
+    const uint8_t *blob = e == a.E ? a.shared_blob : a.pool + uint64_t(slot < 0 ? 0 : slot) * a.expert_bytes;
+    const rsrc_t gres = make_rsrc(blob + a.off_w0, uint32_t(a.N) * rbytes);
+    const rsrc_t ures = make_rsrc(blob + a.off_w1, uint32_t(a.N) * rbytes);
+    const rsrc_t gsres = make_rsrc(blob + a.off_s0, uint32_t(a.N) * sbytes);
+    const rsrc_t usres = make_rsrc(blob + a.off_s1, uint32_t(a.N) * sbytes);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row0 + r;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t cb = 1024u * c + 16u * lane;
+        const bool ok = live && row < a.N && cb < rbytes;
+        const uint32_t wo = ok ? uint32_t(row) * rbytes + cb : kOOB;
+        J.wg[r][c] = bld16(gres, wo);
+        J.wu[r][c] = bld16(ures, wo);
+        J.sg[r][c] = piece_scale<WF>(gsres, uint32_t(row) * sbytes, int(cb >> 4), ok);
+        J.su[r][c] = piece_scale<WF>(usres, uint32_t(row) * sbytes, int(cb >> 4), ok);
+      }
+    }
+    J.ts0 = J.ts1 = 1.f;
+    if constexpr (WF == WF_NV4)
+      if (live) {
+        J.ts0 = *reinterpret_cast<const float *>(blob + a.off_t0);
+        J.ts1 = *reinterpret_cast<const float *>(blob + a.off_t1);
+      }
+  };
+  Job ring[2];
+  int j = int(blockIdx.x) * WAVES + wave;
+  const bool early = wave != 0 && has_shared && j < jobs_per_expert;  // a shared-expert job: no routing needed
+  if (early) issue(j, true, ring[0]);
 
   if (wave == 0) {  // the routing; workgroup 0 publishes it (ids, weights, offsets, rows) for the down stage
-    const TokenPick pk = one_token_route(a.logits, a.E, a.k, a.gating, a.renorm);
+#pragma unroll
+    for (int i = 0; i < XPL; ++i)
+      if (lane + 64 * i < XN) s_x[lane + 64 * i] = xg[i];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {  // table_slot's reading of the words
+      const int e = lane + 64 * i;
+      const int sv = a.slot_of_expert != nullptr ? sl[i] : e;
+      s_slot[e] = e < a.E && sv < a.n_slots ? sv : -1;
+    }
+    const TokenPick pk = one_token_route(lg, a.E, a.k, a.gating, a.renorm);
     if (lane < a.k) {
       s_act[pk.rank] = pk.id;
       s_w[pk.rank] = pk.w;
@@ -375,96 +479,68 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < XPT; ++i)
-    if (tid + THREADS * i < XN) s_x[tid + THREADS * i] = xg[i];
-  if (tid < kRouteMaxE) s_slot[tid] = my_slot;
-  __syncthreads();
+  lds_barrier();  // (__syncthreads would also wait for the early weights)
   // this lane's activations: piece (c, v) = elements (64 c + lane) * EPC + 8 v ..
   u32x4 xv[NCH][F::XV];
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
 #pragma unroll
     for (int v = 0; v < F::XV; ++v) xv[c][v] = s_x[(64 * c + lane) * F::XV + v];
-  const int jobs_per_expert = (a.N + RPW - 1) / RPW;
   const int n_jobs = s_nact * jobs_per_expert;
   const int stride = int(gridDim.x) * WAVES;
   const rsrc_t hres_out = make_rsrc(a.out, uint32_t(s_nact * a.ldo) * 2u);  // the hidden rows
 
-  struct Job {
-    u32x4 wg[RPW][NCH], wu[RPW][NCH];
-    uint32_t sg[RPW][NCH], su[RPW][NCH];
-    float ts0, ts1;  // NVFP4 tensor scales
-  };
-  // the loads of job j (j >= n_jobs: offsets past the buffers, nothing read)
-  auto issue = [&](int j, Job &J) {
-    const bool live = j < n_jobs;
-    const int jj = live ? j : 0;
-    const int ai = jj / jobs_per_expert, row0 = (jj - ai * jobs_per_expert) * RPW;
-    const int e = uniform(s_act[ai]);
-    const int slot = e == a.E ? 0 : uniform(s_slot[e]);
-    const uint8_t *blob = e == a.E ? a.shared_blob : a.pool + uint64_t(slot < 0 ? 0 : slot) * a.expert_bytes;
-    const rsrc_t gres = make_rsrc(blob + a.off_w0, uint32_t(a.N) * rbytes);
-    const rsrc_t ures = make_rsrc(blob + a.off_w1, uint32_t(a.N) * rbytes);
-    const rsrc_t gsres = make_rsrc(blob + a.off_s0, uint32_t(a.N) * sbytes);
-    const rsrc_t usres = make_rsrc(blob + a.off_s1, uint32_t(a.N) * sbytes);
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int row = row0 + r;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const uint32_t cb = 1024u * c + 16u * lane;
-        const bool ok = live && row < a.N && cb < rbytes;
-        const uint32_t wo = ok ? uint32_t(row) * rbytes + cb : kOOB;
-        J.wg[r][c] = bld16(gres, wo);
-        J.wu[r][c] = bld16(ures, wo);
-        J.sg[r][c] = piece_scale<WF>(gsres, uint32_t(row) * sbytes, int(cb >> 4), ok);
-        J.su[r][c] = piece_scale<WF>(usres, uint32_t(row) * sbytes, int(cb >> 4), ok);
-      }
-    }
-    J.ts0 = J.ts1 = 1.f;
-    if constexpr (WF == WF_NV4) {
-      J.ts0 = *reinterpret_cast<const float *>(blob + a.off_t0);
-      J.ts1 = *reinterpret_cast<const float *>(blob + a.off_t1);
-    }
-  };
   // multiply job j and write its hidden values
   auto finish = [&](int j, const Job &J) {
     const int ai = j / jobs_per_expert, row0 = (j - ai * jobs_per_expert) * RPW;
-    const int e = uniform(s_act[ai]);
+    const int e = job_expert(ai);
     const bool shared = e == a.E;
     const bool missing = !shared && uniform(s_slot[e]) < 0;
-    const int p = shared ? a.k : ai;  // the token's permuted row of this expert: its rank among the picks
+    const int p = job_row(ai);  // the token's permuted row of this expert: its rank among the picks
+    // the job's 2 RPW dot products: gate rows first, then up rows, summed over the wave at once
+    float v[2 * RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      float g = 0.f, u = 0.f;
+      Acc4 g, u;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        g = piece_dot<WF>(J.wg[r][c], J.sg[r][c], xv[c], g);
-        u = piece_dot<WF>(J.wu[r][c], J.su[r][c], xv[c], u);
+        piece_dot<WF>(J.wg[r][c], J.sg[r][c], xv[c], g);
+        piece_dot<WF>(J.wu[r][c], J.su[r][c], xv[c], u);
       }
-      g = wave_sum_f32(g) * J.ts0;
-      u = wave_sum_f32(u) * J.ts1;
-      const int row = row0 + r;
-      const uint16_t hval = missing ? uint16_t(0x7fc0) : f32_to_bf16_rne(silu(g) * u);
-      if (lane == 0 && row < a.N) {
-        if constexpr (NCHD > 0)  // read by other workgroups in this launch: stored coherent at agent scope
-          __builtin_amdgcn_raw_buffer_store_b16(hval, hres_out, uint32_t(p * a.ldo + row) * 2u, 0, kCoherentAgent);
-        else
-          reinterpret_cast<uint16_t *>(a.out)[int64_t(p) * a.ldo + row] = hval;
-      }
+      v[r] = g.sum();
+      v[RPW + r] = u.sum();
+    }
+    const float tot = wave_sums<2 * RPW>(v);
+    // gate total of row r sits in lanes holding value r; its up total (value RPW + r) in lane
+    // l + 32 (RPW 1), l + 16 (RPW 2) or l ^ 8 (RPW 4)
+    float other;
+    if constexpr (RPW == 4) {
+      other = dpp_f32<0x128>(tot, tot);
+    } else {
+      const auto sw = RPW == 2 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(tot), __float_as_uint(tot), false, false)
+                               : __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
+      other = __uint_as_float(sw[1]);
+    }
+    const int r = wave_sums_index<2 * RPW>(lane);
+    const int row = row0 + r;
+    const uint16_t hval = missing ? uint16_t(0x7fc0) : f32_to_bf16_rne(silu(tot * J.ts0) * (other * J.ts1));
+    // one writer per row: the first lane of each group holding a gate total
+    const bool writer = (lane & (RPW == 4 ? 15 : (RPW == 2 ? 31 : 63))) == 0 && r < RPW;
+    if (writer && row < a.N) {
+      if constexpr (NCHD > 0)  // read by other workgroups in this launch: stored coherent at agent scope
+        __builtin_amdgcn_raw_buffer_store_b16(hval, hres_out, uint32_t(p * a.ldo + row) * 2u, 0, kCoherentAgent);
+      else
+        reinterpret_cast<uint16_t *>(a.out)[int64_t(p) * a.ldo + row] = hval;
     }
   };
-  Job ring[2];
-  int j = int(blockIdx.x) * WAVES + wave;
-  issue(j, ring[0]);
+  if (!early) issue(j, j < n_jobs, ring[0]);
   while (j < n_jobs) {
-    issue(j + stride, ring[1]);
+    issue(j + stride, j + stride < n_jobs, ring[1]);
     __builtin_amdgcn_sched_barrier(0);
     finish(j, ring[0]);
     j += stride;
     if (j >= n_jobs) break;
-    issue(j + stride, ring[0]);
+    issue(j + stride, j + stride < n_jobs, ring[0]);
     __builtin_amdgcn_sched_barrier(0);
     finish(j, ring[1]);
     j += stride;
@@ -575,10 +651,10 @@ __device__ __forceinline__ void gemv_down_combine(const PersistArgs &a) {
     const float ws = wgt[j] * ts[j];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      float d = 0.f;
+      Acc4 pd;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) d = piece_dot<WF>(w[j][r][c], sc[j][r][c], hv[j][c], d);
-      acc[r] = fmaf(ws, kind[j] == 2 ? __builtin_nanf("") : d, acc[r]);
+      for (int c = 0; c < NCH; ++c) piece_dot<WF>(w[j][r][c], sc[j][r][c], hv[j][c], pd);
+      acc[r] = fmaf(ws, kind[j] == 2 ? __builtin_nanf("") : pd.sum(), acc[r]);
     }
   }
 #pragma unroll
