@@ -19,13 +19,15 @@ constexpr int kMaxK = 256;
 
 __device__ __forceinline__ float wave_sum(float v) { return wave_sum_f32(v); }
 
-// One wave per token.  Lane l holds the token's logits l, l+64, ... as 64-bit
-// keys: the logit mapped to an unsigned integer of the same order (-0.0 taken
-// as +0.0) in the high half, the complement of the expert index in the low
-// half, so that the largest key is the largest logit and, among equal logits,
-// the lowest index; all keys differ.  Pick j is found by one wave-wide max
-// (a lane-local max, then six butterfly steps) and its owner then drops it:
-// k rounds.  Then the gating weights of the picked experts.
+// One wave per token.  Lane l holds the token's logits l, l+64, ... as 32-bit
+// order keys: the logit mapped to an unsigned integer of the same order (-0.0
+// taken as +0.0), so the largest key is the largest logit.  Pick j is found by
+// one wave-wide maximum (a lane-local max, then six butterfly steps) and one
+// ballot per logit slot, which names the lowest expert index holding that key
+// (ties go to the lower index); its owner then drops it: k rounds.  Key 0
+// marks an absent or already picked logit, so real keys start at 1 (the one
+// logit bit pattern whose key would be 0, the all-ones NaN, ranks with the
+// next-lowest NaN).  Then the gating weights of the picked experts.
 __device__ __forceinline__ uint32_t order_key(float x) {
   if (x == 0.0f) x = 0.0f;  // -0.0 and +0.0 are the same key
   const uint32_t u = __float_as_uint(x);
@@ -46,7 +48,7 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
   const int lane = threadIdx.x & 63;
   const float *lr = logits + int64_t(t) * E;
   float v[VPL];
-  uint64_t key[VPL];
+  uint32_t key[VPL];
   static_assert(kMaxK % 64 == 0, "picks are held 64 per slot");
 #pragma unroll
   for (int i = 0; i < VPL; ++i) v[i] = lr[lane + 64 * i < E ? lane + 64 * i : 0];
@@ -56,7 +58,8 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
     v[i] = e < E ? v[i] : -INFINITY;
-    key[i] = e < E ? (uint64_t(order_key(v[i])) << 32) | uint32_t(~e) : 0;  // 0: below every real key
+    const uint32_t kk = order_key(v[i]);
+    key[i] = e < E ? (kk == 0u ? 1u : kk) : 0u;  // 0: below every real key
   }
   // k rounds of wave arg-max; pick j ends up in lane j % 64, slot j / 64
   constexpr int KS = kMaxK / 64;
@@ -68,19 +71,23 @@ __device__ __forceinline__ void topk_token(const float *__restrict__ logits, int
     pval[s2] = 0.f;
   }
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint32_t m = key[0];
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = int(~uint32_t(best));
+    for (int i = 1; i < VPL; ++i) m = max(m, key[i]);
+    m = wave_max_u32(m);
+    int e = -1;  // the lowest expert index holding key m (scalar)
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (key[i] == best) key[i] = 0;  // the owner drops its pick
+    for (int i = 0; i < VPL; ++i) {
+      const uint64_t b = __ballot(key[i] == m);
+      if (e < 0 && b != 0) e = 64 * i + int(__builtin_ctzll(b));
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) key[i] = lane + 64 * i == e ? 0u : key[i];  // the owner drops its pick
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2)
       if ((j >> 6) == s2 && lane == (j & 63)) {
         pid[s2] = e;
-        pval[s2] = key_value(uint32_t(best >> 32));
+        pval[s2] = key_value(m);
       }
   }
   // Gating.  softmax: p_e = exp(l_e - max) / sum_E exp(l - max); sigmoid: 1/(1+exp(-l)).
