@@ -98,6 +98,61 @@ __device__ inline void permute_block(const int32_t *ids, int R, int E, int *s_cn
   if (tid < 64) wave_scatter(ids, 0, R, E, s_cnt, sorted_rows, row_pos);
 }
 
+// Stable counting sort of 64 < R <= kChunkPermMaxRows routed rows over E <=
+// kChunkPermMaxE experts by one workgroup of at least R / 64 waves: wave c
+// ranks the 64 rows of chunk c among themselves by per-bit ballots, the
+// first row of each (chunk, expert) group records the group's size, a prefix
+// over the chunks turns each expert's counts into chunk bases, a block scan
+// turns the experts' totals into segment starts, and a row's place is its
+// segment start + its chunk base + its rank in the chunk (rows stay
+// ascending inside a segment).  ids in LDS; a row whose id lies outside
+// [0, E) is left out (it gets no place).  s_cc: kChunkPermMaxRows / 64 *
+// kChunkPermMaxE ints; s_seg: E ints.
+constexpr int kChunkPermMaxRows = 1024, kChunkPermMaxE = 256;
+
+__device__ inline void permute_chunks(const int32_t *s_ids, int R, int E, int *s_cc, int *s_seg, int *s_tmp,
+                                      int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
+                                      int32_t *__restrict__ row_pos) {
+  const int tid = threadIdx.x, nt = blockDim.x, wave = tid >> 6, lane = tid & 63;
+  const int nch = (R + 63) / 64;
+  for (int i = tid; i < nch * kChunkPermMaxE; i += nt) s_cc[i] = 0;
+  __syncthreads();
+  const int r = 64 * wave + lane;
+  const int id = wave < nch && r < R ? s_ids[r] : -1;
+  const bool act = id >= 0 && id < E;
+  const int key = act ? id : 0;
+  int rank = 0;
+  if (wave < nch) {
+    uint64_t same = __ballot(act);
+    for (int b = bits_for(E) - 1; b >= 0; --b) {
+      const int bit = (key >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
+    }
+    rank = __popcll(same & ((uint64_t(1) << lane) - 1));
+    if (act && rank == 0) s_cc[wave * kChunkPermMaxE + key] = __popcll(same);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {
+    int run = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int v = s_cc[c * kChunkPermMaxE + e];
+      s_cc[c * kChunkPermMaxE + e] = run;
+      run += v;
+    }
+    s_seg[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(s_seg, E, s_tmp);  // ends with a barrier
+  for (int e = tid; e < E; e += nt) offsets[e] = s_seg[e];
+  if (tid == 0) offsets[E] = total;
+  if (act) {
+    const int pos = s_seg[key] + s_cc[wave * kChunkPermMaxE + key] + rank;
+    sorted_rows[pos] = r;
+    row_pos[r] = pos;
+  }
+}
+
 // Stable counting sort of R <= 64 routed rows by one wave, without a block
 // barrier: lane i ranks row i by per-bit ballots -- the rows with a smaller
 // expert id (counted among the lanes that agree with it on the higher bits and

@@ -106,7 +106,8 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_gating_kernel(const floa
 
 // ------------------------------------------------------------------ fused decode routing
 
-constexpr int kFusedMaxT = 16;      // tokens of the fused path (one per wave; more is slower than two launches)
+constexpr int kFusedMaxT = 16;      // tokens of the fused path (one workgroup: at 64 tokens its top-k,
+                                     // VALU-bound on one CU, took 16 us against 4.7 us over 16 CUs)
 constexpr int kFusedMaxRows = 2048; // routed rows (T * k) of the fused path
 
 struct FusedRouteArgs {
@@ -119,21 +120,26 @@ struct FusedRouteArgs {
 
 // Top-k, gating and the permutation of all T tokens by one workgroup.
 template <int VPL>
-__device__ __forceinline__ void route_tail(const FusedRouteArgs &a, int32_t *s_ids, int *s_cnt, int *s_tmp) {
+__device__ __forceinline__ void route_tail(const FusedRouteArgs &a, int32_t *s_ids, int *s_cnt, int *s_cc,
+                                           int *s_tmp) {
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int t = wave; t < a.T; t += nw) topk_token<VPL>(a.logits, t, a.E, a.k, a.gating, a.renorm, a.ids, a.w, s_ids);
   __syncthreads();
-  if (a.T * a.k <= 64) {
-    if (wave == 0) permute_wave64(s_ids, a.T * a.k, a.E, s_cnt, a.offsets, a.sorted_rows, a.row_pos);
+  const int R = a.T * a.k;
+  if (R <= 64) {
+    if (wave == 0) permute_wave64(s_ids, R, a.E, s_cnt, a.offsets, a.sorted_rows, a.row_pos);
+  } else if (R <= kChunkPermMaxRows && a.E <= kChunkPermMaxE && R <= 64 * nw) {
+    permute_chunks(s_ids, R, a.E, s_cc, s_cnt, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
   } else {
-    permute_block(s_ids, a.T * a.k, a.E, s_cnt, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
+    permute_block(s_ids, R, a.E, s_cnt, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
   }
 }
 
-// Top-k, gating and permutation of all T tokens in one workgroup (small decode
-// batches, T <= 16): one launch after the router instead of two.  Up to 64
-// routed rows the workgroup is one wave per token and wave 0 sorts the rows
-// alone (no block-wide histogram, scan and barriers).  (A single
+// Top-k, gating and permutation of all T tokens in one workgroup (small
+// decode batches, T <= 16): one launch after the router instead of two.  Up to
+// 64 routed rows the workgroup is one wave per token and wave 0 sorts the rows
+// alone (no block-wide histogram, scan and barriers); above that the rows are
+// sorted chunk-parallel.  (A single
 // launch with the router, its last workgroup doing this, was measured
 // slower: the device-scope fences that publish the logits write back and
 // invalidate the L2 of every XCD.)
@@ -141,8 +147,9 @@ template <int VPL>
 __global__ __launch_bounds__(1024) void route_tail_kernel(FusedRouteArgs a) {
   __shared__ int32_t s_ids[kFusedMaxRows];
   __shared__ int s_cnt[kMaxE];
+  __shared__ int s_cc[kChunkPermMaxRows / 64 * kChunkPermMaxE];
   __shared__ int s_tmp[32];
-  route_tail<VPL>(a, s_ids, s_cnt, s_tmp);
+  route_tail<VPL>(a, s_ids, s_cnt, s_cc, s_tmp);
 }
 
 }  // namespace ft
@@ -283,7 +290,7 @@ extern "C" ft_status ft_moe_route_permute(const void *x, int32_t x_dtype, const 
   a.sorted_rows = sorted_rows;
   a.row_pos = row_pos;
   const int vpl = cdiv(E, 64);
-  // up to 64 routed rows one wave sorts them: one wave per token is enough
+  // up to 64 routed rows one wave sorts them: one wave per token is enough; above that 16 waves
   const dim3 blk(T * k <= 64 ? 64 * T : 1024);
   if (vpl <= 2) hipLaunchKernelGGL(route_tail_kernel<2>, dim3(1), blk, 0, stream, a);
   else if (vpl <= 4) hipLaunchKernelGGL(route_tail_kernel<4>, dim3(1), blk, 0, stream, a);

@@ -157,6 +157,9 @@ def test_route_permute_with_router(ops, cfg_id, T):
 
 @pytest.mark.parametrize("E,k,T", [(128, 8, 1), (256, 6, 64), (16, 16, 9), (1000, 2, 33), (256, 6, 300),
                                    (16, 16, 4), (1000, 2, 16), (256, 6, 10),
+                                   # the one-workgroup tail's chunk sort at its 1024-row limit, one past it
+                                   # (block sort), and 64 one-pick tokens (16 waves of 4 tokens, wave sort)
+                                   (256, 16, 64), (64, 17, 64), (128, 1, 64),
                                    (1024, 4, 16), (1024, 3, 40)])   # the routing kernels' 1024-expert limit
 def test_route_permute_given_logits_bit_exact(ops, E, k, T):
     cfg = synth.shrink(synth.CONFIGS[3], E=E, k=k, shared=False)
@@ -175,6 +178,8 @@ def test_route_permute_given_logits_bit_exact(ops, E, k, T):
 # ----------------------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,k,E,kind", [(1, 8, 128, "u"), (16, 8, 128, "u"), (64, 8, 128, "u"), (5, 2, 16, "u"),
+                                        (128, 8, 256, "u"), (129, 8, 256, "u"), (40, 2, 257, "u"),  # chunk sort
+                                        # at its 1024-row and 256-expert limits and one past each
                                         (300, 6, 256, "u"), (2048, 6, 256, "zipf"), (8192, 6, 256, "zipf"),
                                         (3000, 3, 4096, "u"), (1, 1, 1, "u"), (0, 4, 8, "u")])
 def test_permute_bit_exact(ops, T, k, E, kind):
