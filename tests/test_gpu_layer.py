@@ -293,6 +293,13 @@ LAYER_CALL_CASES = [
     ("mxfp4-T3", 3, {}, 3),
     ("nvfp4-T1", 6, {}, 1),
     ("nvfp4-T4", 6, {}, 4),
+    # one token: one launch for gate/up + down (k + shared <= 8), in every row-chunk shape ...
+    ("bf16-T1-rows4k", 2, dict(I=2048), 1),                            # 4 KiB gate/up and down rows
+    ("mxfp4-T1-small", 3, dict(H=512, I=512, E=8, k=2), 1),            # a grid of a few workgroups
+    ("nvfp4-T1-shared", 6, dict(shared=True), 1),
+    # ... two launches with 9 to 12 down steps, the MFMA kernels past 12
+    ("bf16-T1-k10", 2, dict(k=10), 1),
+    ("bf16-T1-k16", 2, dict(k=16), 1),
     ("bf16-small-4x1", 2, dict(H=512, I=512, E=8, k=2), 3),            # 4 waves x 1 k-block both stages
     ("bf16-E256-k16", 2, dict(H=512, I=768, E=256, k=16), 4),          # the fused path's E and k limits
     ("mxfp4-no-shared", 3, dict(shared=False), 2),
