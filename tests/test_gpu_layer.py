@@ -372,3 +372,47 @@ def test_layer_call_missing_expert_gives_nan(L, cfg_id):
     got = out_f64(layer, cfg, T)
     assert np.all(np.isnan(got[0]))
     check_close(got[1:], ref["out"][1:], bf16_out=True, what=f"cfg{cfg_id} token beside a missing expert")
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3])
+def test_layer_call_graph_replays(L, cfg_id):
+    """The one-token layer call captured in a HIP graph: every replay, with eager calls on other inputs
+    between them, gives the eager output bit for bit (the grid-wide wait's counters start each replay
+    at zero and the hidden rows are read after every workgroup wrote them)."""
+    cfg = synth.CONFIGS[cfg_id]
+    print(f"layer call graph cfg{cfg_id}", flush=True)
+    ex = Experts(cfg)
+    xs = [synth.tokens(cfg, 1, case=c) for c in (11, 12)]
+    wr = synth.router_weight(cfg)
+    wr64 = formats.activations_to_f64(cfg.xdtype, wr)
+    used = set()
+    for x in xs:
+        used |= set(moe.topk(moe.router_logits(formats.activations_to_f64(cfg.xdtype, x), wr64), cfg.k).ravel())
+    layer = make_layer(L, cfg, 1)
+    pool = build_pool(L, layer, ex, sorted(used), cfg.E)
+    shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
+    xd = [L.to_device(x) for x in xs]
+    wrd = L.to_device(wr)
+    eager = []
+    for x in xd:
+        layer.forward_layer(1, x, pool, w_router=wrd, shared_blob=shared)
+        torch.cuda.synchronize()
+        eager.append(layer.out[:1].clone())
+    assert not torch.equal(eager[0], eager[1])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            layer.forward_layer(1, xd[0], pool, w_router=wrd, shared_blob=shared)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        layer.out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out[:1], eager[0]), f"replay {rep}"
+        layer.forward_layer(1, xd[1], pool, w_router=wrd, shared_blob=shared)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out[:1], eager[1]), f"eager call after replay {rep}"
+    print(f"PARITY cfg{cfg_id} graph replays: bit-identical to the eager call", flush=True)
