@@ -139,8 +139,11 @@ __device__ __forceinline__ TokenLogits one_token_logits(const float *__restrict_
   return t;
 }
 
+// s_pick / s_npicks (LDS, nullable): pick j's expert is stored as soon as it is found, then the count
+// of picks found, so that other waves can start on pick j's weights while later picks are searched.
 __device__ __forceinline__ TokenPick one_token_route(const TokenLogits &lg, int E, int k, int gating,
-                                                     int renorm) {
+                                                     int renorm, int *s_pick = nullptr,
+                                                     int *s_npicks = nullptr) {
   constexpr int VPL = kRouteMaxE / 64;
   const int lane = threadIdx.x & 63;
   const float *v = lg.v;
@@ -158,14 +161,20 @@ __device__ __forceinline__ TokenPick one_token_route(const TokenLogits &lg, int 
 #pragma unroll
     for (int i = 1; i < VPL; ++i) m = max(m, key[i]);
     m = wave_max_u32(m);
-    int e = -1;  // the lowest expert index whose key is m (scalar)
+    int e = 1 << 30;  // the lowest expert index whose key is m (scalar); lower slots hold lower indices
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
+    for (int i = VPL - 1; i >= 0; --i) {
       const uint64_t b = __ballot(key[i] == m);
-      if (e < 0 && b != 0) e = 64 * i + int(__builtin_ctzll(b));
+      e = b != 0 ? 64 * i + int(__builtin_ctzll(b)) : e;
     }
 #pragma unroll
     for (int i = 0; i < VPL; ++i) key[i] = lane + 64 * i == e ? 0u : key[i];
+    if (s_pick != nullptr && lane == 0) {
+      s_pick[j] = e;
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): the pick lands first
+      __hip_atomic_store(s_npicks, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if (j == 0) mx = key_value(m);  // the largest logit
     if (lane == j) {
       pid = e;
@@ -222,7 +231,7 @@ template <int PENDING>
 __device__ __forceinline__ bool grid_wait(uint32_t *bar) {
   __shared__ int s_ok;
   wait_vmcnt<PENDING>();
-  lds_barrier();  // (__syncthreads would also wait for the loads left in flight)
+  lds_barrier();  // orders LDS only: the loads left in flight stay in flight
   if (threadIdx.x == 0) {
     const int G = int(gridDim.x), b = int(blockIdx.x);
     const int ng = G < kWaitGroups ? G : kWaitGroups;
@@ -346,17 +355,18 @@ __device__ __forceinline__ void token_down_after_wait(const PersistArgs &d, uint
 
 // Work is a list of wave jobs: RPW consecutive (gate row, up row) pairs of one
 // expert, the shared expert's first (when there is one), then the routed
-// experts' in ascending id.  Every workgroup routes the token itself
-// (one_token_route; workgroup 0 publishes the result); its waves then walk
-// the job list with a stride of all the grid's waves, the next job's loads
-// issued before the current job is multiplied.  The grid is sized to the
-// workgroups that fit on the device at once, so no workgroup pays the
-// prologue in a second round.
+// experts' in pick order.  Every workgroup routes the token itself
+// (one_token_route in wave 0; workgroup 0 publishes the result); each wave
+// takes a contiguous run of the job list, the next job's loads issued before
+// the current job is multiplied.  The grid is sized to the workgroups that
+// fit on the device at once, so no workgroup pays the prologue in a second
+// round.
 //
-// What does not depend on the routing is in flight before it: the token's
-// activations, the slot table entries and, for waves whose first job is a
-// shared-expert job, that job's weights -- issued after the logits' loads, so
-// the top-k waits only for the logits.  Data every wave reads is fetched once
+// The routing overlaps the weight stream: wave 0 stores each pick in LDS as
+// soon as its top-k round finds it, and a wave issues a job as soon as the
+// job's expert is known (a shared-expert job at once).  Wave 0's loads of
+// the activations, slot table entries and logits go out first, in one round
+// trip.  Data every wave reads is fetched once
 // per workgroup: the activations go through LDS (per wave they would be the
 // same few KiB read by thousands of waves from the few L2 channels that hold
 // them), and large (8-wave) workgroups keep that shared traffic small.
@@ -367,12 +377,18 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
   using F = GemvFmt<WF>;
   constexpr int XN = NCH * 64 * F::XV;            // u32x4 of activations the lanes' pieces cover
   constexpr int XPL = (XN + 63) / 64;             // of them per lane of wave 0
-  __shared__ int s_act[kFusedMaxK + 1];     // the picks in ascending id (= their rows), then the shared expert
+  __shared__ int s_act[kFusedMaxK + 1];     // the picks in pick order (= their hidden rows), then the shared expert
   __shared__ float s_w[kFusedMaxK + 1];     // their gating weights
   __shared__ int s_slot[kRouteMaxE];        // slot of every expert (-1: not resident)
-  __shared__ int s_nact;
+  __shared__ int s_npicks;                  // picks stored in s_act so far
+  __shared__ int s_xready;                  // s_x and s_slot written
   __shared__ u32x4 s_x[XN];                 // the token's activations, u32x4 i = elements 8i .. 8i+7
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  if (tid == 0) {
+    s_npicks = 0;
+    s_xready = 0;
+  }
+  lds_barrier();
   const uint32_t rbytes = WF == WF_BF16 ? uint32_t(a.K) * 2 : uint32_t(a.K) / 2;  // code bytes of a row
   const uint32_t sbytes = WF == WF_FP4 ? uint32_t(a.K) / 32 : (WF == WF_NV4 ? uint32_t(a.K) / 16 : 0u);
   // Raw buffer loads throughout: an offset past the buffer reads zero without a branch, so a job's
@@ -400,14 +416,34 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
 
   const int has_shared = a.shared_blob != nullptr ? 1 : 0;
   const int jobs_per_expert = (a.N + RPW - 1) / RPW;
+  const int n_act = a.k + has_shared;
+  const int n_jobs = n_act * jobs_per_expert;
+  // waits on wave 0's progress (LDS polls; wave 0 depends on no other wave, so they end)
+  // (LDS atomic loads of the flags themselves: through a pointer they became flat loads, whose wait
+  // also waited for every weight load in flight)
+  auto npicks = [&] { return __hip_atomic_load(&s_npicks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  auto xready = [&] { return __hip_atomic_load(&s_xready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); };
   struct Job {
     u32x4 wg[RPW][NCH], wu[RPW][NCH];
     uint32_t sg[RPW][NCH], su[RPW][NCH];
     float ts0, ts1;  // NVFP4 tensor scales
   };
-  // job list entry ai: the shared expert at 0 (reads no LDS), then the picks by rank (= hidden row)
+  // job list entry ai: the shared expert at 0 (reads no LDS), then the picks in pick order (= hidden row)
   auto job_expert = [&](int ai) { return has_shared && ai == 0 ? a.E : uniform(s_act[ai - has_shared]); };
   auto job_row = [&](int ai) { return has_shared && ai == 0 ? a.k : ai - has_shared; };
+  // Job j's expert is known once its pick has been found (a shared-expert job needs no routing).
+  // `known` keeps the last count seen, so consecutive jobs of one expert read no LDS (a read here
+  // also waits for this wave's own weight loads: its register may have been theirs).
+  int known = 0;
+  auto wait_job = [&](int j, int je) {
+    if (j >= je) return;
+    const int need = j / jobs_per_expert - has_shared + 1;
+    if (need <= known) return;
+    int n;
+    while ((n = __builtin_amdgcn_readfirstlane(npicks())) < need) __builtin_amdgcn_s_sleep(1);
+    known = n;
+    asm volatile("" ::: "memory");  // the pick is read after its count
+  };
   // the loads of job j (live false: offsets past the buffers, nothing read)
   auto issue = [&](int j, bool live, Job &J) {
     const int jj = live ? j : 0;
@@ -440,10 +476,17 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
         J.ts1 = *reinterpret_cast<const float *>(blob + a.off_t1);
       }
   };
+  // This wave's jobs: a contiguous run of the list (consecutive rows, mostly of one expert).
   Job ring[2];
-  int j = int(blockIdx.x) * WAVES + wave;
-  const bool early = wave != 0 && has_shared && j < jobs_per_expert;  // a shared-expert job: no routing needed
-  if (early) issue(j, true, ring[0]);
+  const int gw = int(blockIdx.x) * WAVES + wave, nw = int(gridDim.x) * WAVES;
+  int j = int(int64_t(n_jobs) * gw / nw);
+  const int je = int(int64_t(n_jobs) * (gw + 1) / nw);
+  // The other waves issue their first job as soon as its expert is known: at once for the shared
+  // expert, else once wave 0's top-k has found that pick (picks are stored as they are found).
+  if (wave != 0) {
+    wait_job(j, je);
+    issue(j, j < je, ring[0]);
+  }
 
   if (wave == 0) {  // the routing; workgroup 0 publishes it (ids, weights, offsets, rows) for the down stage
 #pragma unroll
@@ -455,15 +498,18 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
       const int sv = a.slot_of_expert != nullptr ? sl[i] : e;
       s_slot[e] = e < a.E && sv < a.n_slots ? sv : -1;
     }
-    const TokenPick pk = one_token_route(lg, a.E, a.k, a.gating, a.renorm);
-    if (lane < a.k) {
-      s_act[pk.rank] = pk.id;
-      s_w[pk.rank] = pk.w;
-    }
     if (lane == 0) {
-      const bool sh = a.shared_blob != nullptr;
-      if (sh) s_act[a.k] = a.E;
-      s_nact = a.k + (sh ? 1 : 0);
+      if (has_shared) s_act[a.k] = a.E;
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): s_x, s_slot landed
+      __hip_atomic_store(&s_xready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    const TokenPick pk = one_token_route(lg, a.E, a.k, a.gating, a.renorm, s_act, &s_npicks);
+    if (lane < a.k) s_w[lane] = pk.w;
+    if (lane == 0) {  // the routing is complete: every pick and its weight (count k + 1)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): s_w landed
+      __hip_atomic_store(&s_npicks, a.k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     if (blockIdx.x == 0) {
       if (lane < a.k) {
@@ -479,16 +525,16 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
       }
     }
   }
-  lds_barrier();  // (__syncthreads would also wait for the early weights)
+  if (wave == 0) issue(j, j < je, ring[0]);
   // this lane's activations: piece (c, v) = elements (64 c + lane) * EPC + 8 v ..
+  while (__builtin_amdgcn_readfirstlane(xready()) < 1) __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");  // s_x is read after the flag
   u32x4 xv[NCH][F::XV];
 #pragma unroll
   for (int c = 0; c < NCH; ++c)
 #pragma unroll
     for (int v = 0; v < F::XV; ++v) xv[c][v] = s_x[(64 * c + lane) * F::XV + v];
-  const int n_jobs = s_nact * jobs_per_expert;
-  const int stride = int(gridDim.x) * WAVES;
-  const rsrc_t hres_out = make_rsrc(a.out, uint32_t(s_nact * a.ldo) * 2u);  // the hidden rows
+  const rsrc_t hres_out = make_rsrc(a.out, uint32_t(n_act * a.ldo) * 2u);  // the hidden rows
 
   // multiply job j and write its hidden values
   auto finish = [&](int j, const Job &J) {
@@ -533,19 +579,25 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
         reinterpret_cast<uint16_t *>(a.out)[int64_t(p) * a.ldo + row] = hval;
     }
   };
-  if (!early) issue(j, j < n_jobs, ring[0]);
-  while (j < n_jobs) {
-    issue(j + stride, j + stride < n_jobs, ring[1]);
+  while (j < je) {
+    wait_job(j + 1, je);
+    issue(j + 1, j + 1 < je, ring[1]);
     __builtin_amdgcn_sched_barrier(0);
     finish(j, ring[0]);
-    j += stride;
-    if (j >= n_jobs) break;
-    issue(j + stride, j + stride < n_jobs, ring[0]);
+    if (++j >= je) break;
+    wait_job(j + 1, je);
+    issue(j + 1, j + 1 < je, ring[0]);
     __builtin_amdgcn_sched_barrier(0);
     finish(j, ring[1]);
-    j += stride;
+    ++j;
   }
-  if constexpr (NCHD > 0) token_down_after_wait<WF, NCHD, RB>(*d, bar, s_act, s_w, s_slot, s_nact);
+  if constexpr (NCHD > 0) {
+    // a wave may get here while wave 0 still routes (its own jobs all had early picks): the down
+    // stage reads every pick and weight
+    while (__builtin_amdgcn_readfirstlane(npicks()) < a.k + 1) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+    token_down_after_wait<WF, NCHD, RB>(*d, bar, s_act, s_w, s_slot, n_act);
+  }
 }
 
 // ---------------------------------------------------------------- down + combine, one token
@@ -599,7 +651,7 @@ __device__ __forceinline__ void gemv_down_combine(const PersistArgs &a) {
       }
       kind[j] = slot >= 0 ? 0 : 2;
       blob[j] = a.pool + uint64_t(slot >= 0 ? slot : 0) * a.expert_bytes;
-      hrow[j] = a.row_pos[s];
+      hrow[j] = s;  // the one-token gate/up writes hidden rows in pick order
       wgt[j] = a.topk_w[s];
     } else if (s < S) {
       kind[j] = 1;

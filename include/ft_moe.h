@@ -374,8 +374,9 @@ ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t
  * once before the first call on a workspace (every call leaves them zero; a
  * wait that gives up -- it never should -- writes NaN outputs and may leave
  * them non-zero).  The rest is the steps' workspace; after the call its start
- * (byte 8192) holds the bf16 hidden rows, as for ft_moe_grouped_ffn.  Calls
- * that share a workspace must not overlap.
+ * (byte 8192) holds the bf16 hidden rows, as for ft_moe_grouped_ffn (for one
+ * token on the one-token kernels: the picks' rows in pick order, then the
+ * shared expert's).  Calls that share a workspace must not overlap.
  */
 ft_status ft_moe_layer(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
                        const int32_t *slot_of_expert, const void *shared_blob, const void *x, int32_t x_dtype,
