@@ -90,7 +90,8 @@ class MoELayer:
         self.ws_rp = torch.empty(max(256, self.ws_rp_bytes), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty(max(256, self.ws_ffn_bytes), dtype=torch.uint8, device=dev)
         self.ws_layer_bytes = ops.ft_workspace_bytes(_lib.FT_WS_LAYER, T_max, k, E, H, shape.I)
-        # zeroed: its first 256 bytes are the one-token kernel's wait words (every call leaves them zero)
+        # zeroed: its first 8192 bytes are ft_moe_layer's wait area (the one-token kernel's grid-wide wait),
+        # which must be zero before the first call; every call leaves it ready for the next
         self.ws_layer = torch.zeros(max(256, self.ws_layer_bytes), dtype=torch.uint8, device=dev)
 
     def route(self, T, x=None, w_router=None, logits=None, stream=None):

@@ -370,10 +370,12 @@ ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t
  * shared_blob, y_rows, y_shared, mode as ft_moe_grouped_ffn -- mode without
  * stage bits; out_dtype, out as ft_moe_combine, H = L->H).
  * workspace: ft_workspace_bytes(FT_WS_LAYER, T, k, E, H, I) bytes, 256-byte
- * aligned.  Its first 8192 bytes hold the grid-wide wait's counters: zero them
- * once before the first call on a workspace (every call leaves them zero; a
- * wait that gives up -- it never should -- writes NaN outputs and may leave
- * them non-zero).  The rest is the steps' workspace; after the call its start
+ * aligned.  Its first 8192 bytes are the wait area of the one-token kernel's
+ * grid-wide wait.  Zero it once before the first call on a workspace; every
+ * call leaves it ready for the next (the counters back at zero, the wait's
+ * round words only counting up; a wait that gives up -- it never should --
+ * writes NaN outputs and may leave the counters non-zero).  The rest is the
+ * steps' workspace; after the call its start
  * (byte 8192) holds the bf16 hidden rows, as for ft_moe_grouped_ffn (for one
  * token on the one-token kernels: the picks' rows in pick order, then the
  * shared expert's).  Calls that share a workspace must not overlap.

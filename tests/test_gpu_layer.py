@@ -304,6 +304,8 @@ LAYER_CALL_CASES = [
     ("bf16-E256-k16", 2, dict(H=512, I=768, E=256, k=16), 4),          # the fused path's E and k limits
     ("mxfp4-no-shared", 3, dict(shared=False), 2),
     ("bf16-T5-four-calls", 2, {}, 5),                                  # past the fused path: the three calls
+    ("bf16-T64", 2, dict(H=1024, I=768, E=32), 64),                    # staged down outputs: 64-tile groups, 4 windows
+    ("bf16-T33-4x1", 2, dict(H=512, I=512, E=16, k=2), 33),            # experts with two token groups
     ("mxfp4-small-four-calls", 3, dict(H=512, I=512, E=8, k=2), 2),    # no persistent shape for H/256 = 2
     ("f32-four-calls", 1, {}, 8),
 ]
@@ -374,45 +376,57 @@ def test_layer_call_missing_expert_gives_nan(L, cfg_id):
     check_close(got[1:], ref["out"][1:], bf16_out=True, what=f"cfg{cfg_id} token beside a missing expert")
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3])
-def test_layer_call_graph_replays(L, cfg_id):
-    """The one-token layer call captured in a HIP graph: every replay, with eager calls on other inputs
-    between them, gives the eager output bit for bit (the grid-wide wait's counters start each replay
-    at zero and the hidden rows are read after every workgroup wrote them)."""
-    cfg = synth.CONFIGS[cfg_id]
-    print(f"layer call graph cfg{cfg_id}", flush=True)
+GRAPH_CASES = [
+    # name, config, overrides, T
+    ("bf16-T1", 2, {}, 1),     # one launch for gate/up + down: the grid-wide wait
+    ("mxfp4-T1", 3, {}, 1),
+    ("bf16-T64", 2, dict(H=1024, I=768, E=32), 64),  # the grouped decode kernels
+]
+
+
+@pytest.mark.parametrize("name,cfg_id,over,T", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_layer_call_graph_replays(L, name, cfg_id, over, T):
+    """The layer call captured in a HIP graph: every replay, with eager calls on other inputs between
+    them, gives the eager output bit for bit (the grid-wide wait's counters start each replay at zero
+    and the hidden rows are read after every workgroup wrote them).  With more than one token the
+    calls leave the wait area as they found it."""
+    cfg = synth.shrink(synth.CONFIGS[cfg_id], **over)
+    print(f"layer call graph {name}", flush=True)
     ex = Experts(cfg)
-    xs = [synth.tokens(cfg, 1, case=c) for c in (11, 12)]
+    xs = [synth.tokens(cfg, T, case=c) for c in (11, 12)]
     wr = synth.router_weight(cfg)
     wr64 = formats.activations_to_f64(cfg.xdtype, wr)
     used = set()
     for x in xs:
         used |= set(moe.topk(moe.router_logits(formats.activations_to_f64(cfg.xdtype, x), wr64), cfg.k).ravel())
-    layer = make_layer(L, cfg, 1)
+    layer = make_layer(L, cfg, T)
     pool = build_pool(L, layer, ex, sorted(used), cfg.E)
     shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
     xd = [L.to_device(x) for x in xs]
     wrd = L.to_device(wr)
+    wait_area = layer.ws_layer[:8192].clone()
     eager = []
     for x in xd:
-        layer.forward_layer(1, x, pool, w_router=wrd, shared_blob=shared)
+        layer.forward_layer(T, x, pool, w_router=wrd, shared_blob=shared)
         torch.cuda.synchronize()
-        eager.append(layer.out[:1].clone())
+        eager.append(layer.out[:T].clone())
     assert not torch.equal(eager[0], eager[1])
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            layer.forward_layer(1, xd[0], pool, w_router=wrd, shared_blob=shared)
+            layer.forward_layer(T, xd[0], pool, w_router=wrd, shared_blob=shared)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for rep in range(4):
         layer.out.fill_(0)
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(layer.out[:1], eager[0]), f"replay {rep}"
-        layer.forward_layer(1, xd[1], pool, w_router=wrd, shared_blob=shared)  # eager work between replays
+        assert torch.equal(layer.out[:T], eager[0]), f"replay {rep}"
+        layer.forward_layer(T, xd[1], pool, w_router=wrd, shared_blob=shared)  # eager work between replays
         torch.cuda.synchronize()
-        assert torch.equal(layer.out[:1], eager[1]), f"eager call after replay {rep}"
-    print(f"PARITY cfg{cfg_id} graph replays: bit-identical to the eager call", flush=True)
+        assert torch.equal(layer.out[:T], eager[1]), f"eager call after replay {rep}"
+    if T > 1:
+        assert torch.equal(layer.ws_layer[:8192], wait_area), "the calls left the wait area changed"
+    print(f"PARITY {name} graph replays: bit-identical to the eager call", flush=True)
