@@ -1088,6 +1088,11 @@ extern "C" ft_status ft_moe_grouped_ffn(const ft_expert_layout *L, const void *s
 
 // ------------------------------------------------------------------ the whole layer in one call
 
+// The routing's completion counter (route_permute_counted) in the layer call's zeroed wait area: the
+// line after the one-token kernel's grid-wide wait words.
+constexpr int kLayerRouteWord = kWaitStride * (2 * kWaitGroups + 1);
+static_assert((kLayerRouteWord + 1) * 4 <= int(kLayerWaitBytes), "the routing counter fits the wait area");
+
 extern "C" ft_status ft_moe_layer(const ft_expert_layout *L, const void *slot_pool, int32_t n_slots,
                                   const int32_t *slot_of_expert, const void *shared_blob, const void *x,
                                   int32_t x_dtype, const void *w_router, float *logits, int32_t T, int32_t E,
@@ -1143,8 +1148,11 @@ extern "C" ft_status ft_moe_layer(const ft_expert_layout *L, const void *slot_po
                               T * k <= kRouteMaxRows && w1 >= T);
   if (!fused) {
     // route + permute, the grouped FFN and the combine, one call after the other
-    st = ft_moe_route_permute(x, x_dtype, w_router, logits, T, H, E, k, gating, renormalize, topk_ids, topk_w,
-                              expert_offsets, sorted_rows, row_pos, ws, ws_bytes, stream);
+    st = route_permute_counted_covers(T, k, E)
+             ? route_permute_counted(x, x_dtype, w_router, logits, T, H, E, k, gating, renormalize, topk_ids, topk_w,
+                                     expert_offsets, sorted_rows, row_pos, wait_words + kLayerRouteWord, stream)
+             : ft_moe_route_permute(x, x_dtype, w_router, logits, T, H, E, k, gating, renormalize, topk_ids, topk_w,
+                                    expert_offsets, sorted_rows, row_pos, ws, ws_bytes, stream);
     if (st != FT_OK) return st;
     st = ft_moe_grouped_ffn(L, slot_pool, n_slots, slot_of_expert, shared_blob, x, x_dtype, T, k, E,
                             expert_offsets, sorted_rows, y_rows, y_shared, mode, ws, ws_bytes, stream);

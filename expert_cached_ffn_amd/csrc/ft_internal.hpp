@@ -38,6 +38,16 @@ ft_status route_logits(const void *x, int32_t x_dtype, const void *w_router, flo
                        int32_t E, int32_t k, int32_t gating, int32_t *topk_ids, float *topk_w, hipStream_t stream,
                        bool launch = true);
 
+// The routing of ft_moe_route_permute as two launches after the router instead of three (top-k over
+// the grid, the permutation by its last workgroup) for decode batches of more than 16 tokens with at
+// most 1024 routed rows over at most 256 experts; `done` is a zeroed counter, left zero.  Arguments
+// are those of ft_moe_route_permute, checked by the caller.
+bool route_permute_counted_covers(int T, int k, int E);
+ft_status route_permute_counted(const void *x, int32_t x_dtype, const void *w_router, float *logits, int32_t T,
+                                int32_t H, int32_t E, int32_t k, int32_t gating, int32_t renormalize,
+                                int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *sorted_rows,
+                                int32_t *row_pos, uint32_t *done, hipStream_t stream);
+
 }  // namespace ft
 
 #define FT_REQUIRE(cond, msg)                                   \

@@ -152,6 +152,79 @@ __global__ __launch_bounds__(1024) void route_tail_kernel(FusedRouteArgs a) {
   route_tail<VPL>(a, s_ids, s_cnt, s_cc, s_tmp);
 }
 
+// Top-k and gating over the grid, one token per wave, then the permutation by the workgroup that
+// finishes last (decode batches past the one-workgroup tail: that tail's top-k is VALU-bound on one
+// CU).  Each workgroup writes its tokens' ids through to the device-coherent level (sc1: the dies'
+// L2s are not coherent with each other), waits for those stores, and counts itself done on a zeroed
+// counter; the workgroup whose count is the last reads every id back the same way, sorts the rows
+// chunk-parallel (R <= 64 * NW) and clears the counter.  One launch instead of two.
+constexpr int kCoherent = 16;  // buffer cache policy: sc1 (agent scope)
+
+template <int VPL, int NW>
+__global__ __launch_bounds__(64 * NW) void topk_permute_kernel(FusedRouteArgs a, uint32_t *done) {
+  __shared__ int32_t s_ids[64 * NW];  // the rows' ids at their flat index t * k + j (R <= 64 * NW)
+  __shared__ int s_cc[NW * kChunkPermMaxE];
+  __shared__ int s_seg[kChunkPermMaxE];
+  __shared__ int s_tmp[32];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int t0 = int(blockIdx.x) * NW, nt = min(NW, a.T - t0);
+  const int R = a.T * a.k;
+  if (wave < nt) topk_token<VPL>(a.logits, t0 + wave, a.E, a.k, a.gating, a.renorm, nullptr, a.w, s_ids);
+  __syncthreads();
+  const rsrc_t ids = make_rsrc(a.ids, uint32_t(R) * 4u);
+  for (int p = t0 * a.k + tid; p < (t0 + nt) * a.k; p += 64 * NW)
+    __builtin_amdgcn_raw_buffer_store_b32(s_ids[p], ids, uint32_t(p) * 4u, 0, kCoherent);
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  for (int p = tid; p < R; p += 64 * NW) s_ids[p] = int32_t(__builtin_amdgcn_raw_buffer_load_b32(ids, uint32_t(p) * 4u, 0, kCoherent));
+  __syncthreads();
+  permute_chunks(s_ids, R, a.E, s_cc, s_seg, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
+  if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+bool route_permute_counted_covers(int T, int k, int E) {
+  return T > kFusedMaxT && int64_t(T) * k <= kChunkPermMaxRows && E <= kChunkPermMaxE && k <= E;
+}
+
+ft_status route_permute_counted(const void *x, int32_t x_dtype, const void *w_router, float *logits, int32_t T,
+                                int32_t H, int32_t E, int32_t k, int32_t gating, int32_t renormalize,
+                                int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *sorted_rows,
+                                int32_t *row_pos, uint32_t *done, hipStream_t stream) {
+  const ft_status st = route_logits(x, x_dtype, w_router, logits, T, H, E, k, gating, topk_ids, topk_w, stream);
+  if (st != FT_OK) return st;
+  FusedRouteArgs a{};
+  a.logits = logits;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.gating = gating;
+  a.renorm = renormalize ? 1 : 0;
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.offsets = expert_offsets;
+  a.sorted_rows = sorted_rows;
+  a.row_pos = row_pos;
+  const int R = T * k, vpl = cdiv(E, 64);
+#define FT_TOPK_PERM(V, NW) \
+  hipLaunchKernelGGL((topk_permute_kernel<V, NW>), dim3(unsigned(cdiv(T, NW))), dim3(64 * NW), 0, stream, a, done)
+  if (R <= 512) {
+    if (vpl <= 2) FT_TOPK_PERM(2, 8);
+    else FT_TOPK_PERM(4, 8);
+  } else {
+    if (vpl <= 2) FT_TOPK_PERM(2, 16);
+    else FT_TOPK_PERM(4, 16);
+  }
+#undef FT_TOPK_PERM
+  FT_LAUNCHED("topk_permute_kernel");
+  clear_error();
+  return FT_OK;
+}
+
 }  // namespace ft
 
 using namespace ft;

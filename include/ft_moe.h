@@ -361,7 +361,10 @@ ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t
  *      once -- y_rows and y_shared are then NOT written.
  * With T = 1 and at most 8 down steps (k routed + the shared expert), steps 2
  * and 3 are one launch whose workgroups meet at a grid-wide wait.  Other
- * calls make the three calls in turn (y_rows / y_shared written as there).
+ * calls make the three calls in turn (y_rows / y_shared written as there);
+ * with 17 or more tokens, at most 1024 routed rows and E <= 256, the routing
+ * after the router is one launch: top-k over the grid, the permutation by the
+ * workgroup that finishes last.
  * An expert whose slot is negative (FT_SLOT_SKIP included) or >= n_slots
  * gives NaN outputs for the tokens that picked it.
  * Arguments: as for the three calls (x, x_dtype, w_router, logits, T, E, k,
@@ -370,8 +373,10 @@ ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t
  * shared_blob, y_rows, y_shared, mode as ft_moe_grouped_ffn -- mode without
  * stage bits; out_dtype, out as ft_moe_combine, H = L->H).
  * workspace: ft_workspace_bytes(FT_WS_LAYER, T, k, E, H, I) bytes, 256-byte
- * aligned.  Its first 8192 bytes are the wait area of the one-token kernel's
- * grid-wide wait.  Zero it once before the first call on a workspace; every
+ * aligned.  Its first 8192 bytes are the wait area: the counters of the
+ * one-token kernel's grid-wide wait and of the routing of 17 to 1024/k tokens
+ * (top-k over the grid, the permutation by the workgroup that finishes
+ * last).  Zero it once before the first call on a workspace; every
  * call leaves it ready for the next (the counters back at zero, the wait's
  * round words only counting up; a wait that gives up -- it never should --
  * writes NaN outputs and may leave the counters non-zero).  The rest is the

@@ -306,6 +306,9 @@ LAYER_CALL_CASES = [
     ("bf16-T5-four-calls", 2, {}, 5),                                  # past the fused path: the three calls
     ("bf16-T64", 2, dict(H=1024, I=768, E=32), 64),                    # staged down outputs: 64-tile groups, 4 windows
     ("bf16-T33-4x1", 2, dict(H=512, I=512, E=16, k=2), 33),            # experts with two token groups
+    # ... whose routing past 16 tokens is one launch after the router (the last workgroup sorts)
+    ("bf16-T64-k16-1024rows", 2, dict(H=512, I=512, E=64, k=16), 64),  # 16-wave workgroups, 1024 rows
+    ("mxfp4-T17-E256", 3, dict(H=512, I=512), 17),                     # four logits per lane, shared expert
     ("mxfp4-small-four-calls", 3, dict(H=512, I=512, E=8, k=2), 2),    # no persistent shape for H/256 = 2
     ("f32-four-calls", 1, {}, 8),
 ]
