@@ -338,6 +338,12 @@ ft_status ft_mxfp8_quantize(const void *x, int64_t ldx, int32_t n, int32_t K, ui
  * row, in fp32; written as out_dtype (FT_F32, or FT_BF16 rounded to nearest
  * even).  y_rows [T*k, H] fp32, out [T, H].  H a multiple of 4; buffers
  * 16-byte aligned.
+ * The pages say the router activates a few experts per token (FreeToken linux
+ * page, "Cómo gestiona FreeToken la memoria MoE") but do not spell out how the
+ * experts' outputs are joined; this call takes the usual reading: the
+ * gating-weighted sum of the routed experts' rows (the scatter-add of the
+ * permuted rows back to token order, in gather form), plus the shared
+ * expert's row.
  */
 ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t *row_pos,
                          const float *y_shared, int32_t T, int32_t k, int32_t H,

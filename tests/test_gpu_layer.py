@@ -349,6 +349,53 @@ def test_layer_call(L, name, cfg_id, over, T):
     check_close(got, out_ref, bf16_out=cfg.xdtype == "bf16", what=f"layer call {name} every token")
 
 
+def _tie_logits(E, k, pattern, rng):
+    """One token's logits with exact ties (float32 values): all equal; a few repeated values; +0.0
+    and -0.0 at the top; k - 1 distinct leaders and five equal values across the top-k boundary."""
+    if pattern == "all-equal":
+        return np.full(E, 0.5, np.float32)
+    if pattern == "few-values":
+        return rng.choice(np.array([-1.0, 0.0, 0.25, 1.0], np.float32), size=E)
+    if pattern == "signed-zeros":
+        v = np.full(E, -3.0, np.float32)
+        at = rng.choice(E, size=k + 3, replace=False)
+        v[at] = np.where(np.arange(k + 3) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+        return v
+    v = rng.normal(-2.0, 0.5, size=E).astype(np.float32)  # "boundary": the k-th pick among 5 equals
+    at = rng.choice(E, size=k + 4, replace=False)
+    v[at[:k - 1]] = 2.0 + np.arange(k - 1, dtype=np.float32)
+    v[at[k - 1:]] = np.float32(1.5)
+    return v
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3])
+@pytest.mark.parametrize("pattern", ["all-equal", "few-values", "signed-zeros", "boundary"])
+def test_layer_call_one_token_exact_ties(L, cfg_id, pattern):
+    """The one-token layer kernel's routing on given logits with exact ties: ids in the order the
+    routing rule fixes (larger logit first, the lower index among equal logits, -0.0 = +0.0), its
+    gating weights, and the layer output at those ids."""
+    cfg = synth.CONFIGS[cfg_id]
+    rng = np.random.default_rng(11)
+    lg = _tie_logits(cfg.E, cfg.k, pattern, rng)[None, :]
+    ids = moe.topk(lg.astype(np.float64), cfg.k)
+    w = moe.gating_weights(lg.astype(np.float64), ids, cfg.gating, cfg.renormalize)
+    ex = Experts(cfg)
+    x = synth.tokens(cfg, 1, case=3)
+    x64 = formats.activations_to_f64(cfg.xdtype, x)
+    layer = make_layer(L, cfg, 1)
+    pool = build_pool(L, layer, ex, sorted(set(ids.ravel().tolist())), cfg.E)
+    shared = L.as_device_u8([L.pack_expert(layer.layout, ex.raw(cfg.E).arrays)])[0] if cfg.shared else None
+    print(f"one-token ties cfg{cfg_id} {pattern}", flush=True)
+    layer.forward_layer(1, L.to_device(x), pool, logits=L.to_device(lg), shared_blob=shared)
+    torch.cuda.synchronize()
+    assert np.array_equal(layer.ids[:1].cpu().numpy(), ids), f"{pattern}: ids {layer.ids[:1].cpu().numpy()} != {ids}"
+    got_w = layer.w[:1].cpu().numpy().astype(np.float64)
+    assert np.allclose(got_w, w, rtol=2e-6, atol=1e-7), f"{pattern}: gating weights"
+    sh = ex.f64(cfg.E) if cfg.shared else None
+    want = moe.token_output(x64[0], ids[0], w[0], ex.f64, sh)[None, :]
+    check_close(out_f64(layer, cfg, 1), want, bf16_out=True, what=f"cfg{cfg_id} one-token ties {pattern}")
+
+
 @pytest.mark.parametrize("cfg_id", [2, 3])
 def test_layer_call_missing_expert_gives_nan(L, cfg_id):
     """The fused path with one picked expert not resident: that token's outputs are NaN, the other
