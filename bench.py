@@ -334,9 +334,11 @@ def copy_calibration(nbytes=1 << 30, reps=3):
 
 
 def achievable_peaks():
-    """What this machine reaches outside the library: a 1 GiB device copy (read + write bytes / time), an
+    """What this machine reaches: a 1 GiB device copy (read + write bytes / time), a plain read of the same
+    1 GiB (the library's checksum, whole 128-byte lines: the ceiling of a read-only weight stream), an
     8192^3 bf16 GEMM through torch's BLAS (hipBLASLt) and the same GEMM in FP8; best of a few runs."""
     import torch
+    from expert_cached_ffn_amd import ops
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -348,6 +350,15 @@ def achievable_peaks():
         e.record()
         torch.cuda.synchronize()
         best = max(best, 2 * n / (s.elapsed_time(e) * 1e-3) / 1e9)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.ft_read_checksum(a, n, sink)
+    read = 0.0
+    for _ in range(5):
+        s.record()
+        ops.ft_read_checksum(a, n, sink)
+        e.record()
+        torch.cuda.synchronize()
+        read = max(read, n / (s.elapsed_time(e) * 1e-3) / 1e9)
     del a, b
     m = 8192
     x = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
@@ -382,8 +393,9 @@ def achievable_peaks():
         log(f"fp8 GEMM through torch unavailable: {err}")
     del x, y
     fp8_txt = f", fp8 GEMM {tf8:,.0f} TFLOP/s" if tf8 else ""
-    log(f"achievable on this box: device copy {best:,.0f} GB/s (read + write), bf16 GEMM {tf:,.0f} TFLOP/s{fp8_txt}")
-    return {"copy_GBps": best, "bf16_gemm_TFLOPs": tf, "fp8_gemm_TFLOPs": tf8}
+    log(f"achievable on this box: device copy {best:,.0f} GB/s (read + write), plain read {read:,.0f} GB/s, "
+        f"bf16 GEMM {tf:,.0f} TFLOP/s{fp8_txt}")
+    return {"copy_GBps": best, "read_GBps": read, "bf16_gemm_TFLOPs": tf, "fp8_gemm_TFLOPs": tf8}
 
 
 def run_prefill(args, cfg, T, mode=0):
@@ -935,7 +947,8 @@ def decode_summary(cfg, res, main_T, peaks, traffic=None):
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": traffic, "avg_launch_us": m["gate_up_ms"] * 1e3,
                      "algorithmic_bytes_per_launch": m["gate_up_bytes"],
-                     "frac_of_achievable_copy": ach / peaks["copy_GBps"] if peaks else None},
+                     "frac_of_achievable_copy": ach / peaks["copy_GBps"] if peaks else None,
+                     "frac_of_achievable_read": ach / peaks["read_GBps"] if peaks else None},
         "layer_weight_GBps": layer_gbps, "layer_frac_of_hbm_peak": layer_gbps / HBM_PEAK_GBS,
         "step_ms_p10_p50_p90": m["step_ms_p10_p50_p90"], "graph_ms_per_step": m["graph_ms_per_step"],
         "batches": {str(T): {"tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],

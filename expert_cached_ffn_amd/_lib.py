@@ -29,7 +29,7 @@ EXPORTS = [
     "ft_expert_cache_cpu_misses", "ft_cpu_expert_ffn", "ft_cpu_miss_rows", "ft_cpu_isa",
     "ft_expert_cache_stage_cpu_misses", "ft_expert_cache_run_cpu_misses", "ft_expert_cache_step_split",
     "ft_expert_cache_wait_fills", "ft_expert_cache_plan", "ft_expert_cache_fill", "ft_expert_cache_set_trace",
-    "ft_moe_grouped_ffn_noalloc", "ft_noalloc_scratch_bytes", "ft_moe_layer",
+    "ft_moe_grouped_ffn_noalloc", "ft_noalloc_scratch_bytes", "ft_moe_layer", "ft_read_checksum",
 ]
 
 
@@ -90,6 +90,8 @@ def lib() -> C.CDLL:
                                              p, p, i32, p]
     L.ft_noalloc_scratch_bytes.restype = sz
     L.ft_noalloc_scratch_bytes.argtypes = []
+    L.ft_read_checksum.restype = i32
+    L.ft_read_checksum.argtypes = [p, C.c_uint64, p, p]
     L.ft_cpu_expert_ffn.restype = i32
     L.ft_cpu_expert_ffn.argtypes = [C.POINTER(ExpertLayout), p, p, i32, p, i32]
     L.ft_cpu_miss_rows.restype = i32

@@ -185,6 +185,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 }
 __device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
 __device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
+// A 16-byte load of bytes read once per call, with the non-temporal bit: for loads that take whole
+// 128-byte lines (a plain 1 GiB read: 6.4 against 5.9 TB/s).  Loads that take half a line must not
+// use it: the line's other half, read by the next load, then came from HBM again (measured: the
+// multi-token decode kernels' gate/up fell from 5.6 to 4.8 TB/s).
+__device__ __forceinline__ u32x4 bld16nt(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2); }
+
 __device__ __forceinline__ uint32_t bld4(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer used here
 

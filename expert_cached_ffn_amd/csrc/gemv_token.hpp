@@ -25,6 +25,15 @@
 
 namespace ft {
 
+// Weight rows are read here 1 KiB per load (whole lines) and once per call: bf16 and MXFP4 rows with
+// the non-temporal bit (one-token layer call measured 20.8 -> 20.5 us bf16, 27.1 -> 26.5 us MXFP4);
+// NVFP4 rows without it (measured 0.2 us slower with it).
+template <int WF>
+__device__ __forceinline__ u32x4 wload(rsrc_t r, uint32_t off) {
+  if constexpr (WF == WF_NV4) return bld16(r, off);
+  else return bld16nt(r, off);
+}
+
 constexpr int kGemvThreads = 256;   // down + combine: 4 waves
 constexpr int kGemvGuThreads = 512; // gate/up: 8 waves
 constexpr int kGemvMaxChunks = 4;   // rows of at most 4 KiB of codes
@@ -301,7 +310,7 @@ __device__ __forceinline__ void token_down_after_wait(const PersistArgs &d, uint
         const int row = rb * RB + r;
         const uint32_t cb = 1024u * c + 16u * lane;
         const bool ok = live && row < d.N && cb < rbytes;
-        w[r][c] = bld16(wres, ok ? uint32_t(row) * rbytes + cb : kOOB);
+        w[r][c] = wload<WF>(wres, ok ? uint32_t(row) * rbytes + cb : kOOB);
         sc[r][c] = piece_scale<WF>(sres, uint32_t(row) * sbytes, int(cb >> 4), ok);
       }
   };
@@ -463,8 +472,8 @@ __device__ __forceinline__ void gemv_gate_up(const PersistArgs &a, const Persist
         const uint32_t cb = 1024u * c + 16u * lane;
         const bool ok = live && row < a.N && cb < rbytes;
         const uint32_t wo = ok ? uint32_t(row) * rbytes + cb : kOOB;
-        J.wg[r][c] = bld16(gres, wo);
-        J.wu[r][c] = bld16(ures, wo);
+        J.wg[r][c] = wload<WF>(gres, wo);
+        J.wu[r][c] = wload<WF>(ures, wo);
         J.sg[r][c] = piece_scale<WF>(gsres, uint32_t(row) * sbytes, int(cb >> 4), ok);
         J.su[r][c] = piece_scale<WF>(usres, uint32_t(row) * sbytes, int(cb >> 4), ok);
       }
@@ -683,7 +692,7 @@ __device__ __forceinline__ void gemv_down_combine(const PersistArgs &a) {
         const int row = row0 + r;
         const uint32_t cb = 1024u * c + 16u * lane;
         const bool ok = live && row < a.N && cb < rbytes;
-        w[j][r][c] = bld16(wres, ok ? uint32_t(row) * rbytes + cb : kOOB);
+        w[j][r][c] = wload<WF>(wres, ok ? uint32_t(row) * rbytes + cb : kOOB);
         sc[j][r][c] = piece_scale<WF>(sres, uint32_t(row) * sbytes, int(cb >> 4), ok);
       }
   }

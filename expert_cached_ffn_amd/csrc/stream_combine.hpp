@@ -93,10 +93,15 @@ __device__ __forceinline__ void stream_combine_xs(const PersistArgs &a, float *s
     const uint8_t *blob = kind == 1 ? a.shared_blob : a.pool + ((uint64_t(hi) << 32) | uint64_t(lo));
     const rsrc_t wres = make_rsrc(blob + a.off_w0, wbytes);
     const rsrc_t sres = make_rsrc(blob + a.off_s0, sbytes);
-    const int row = tile * TR + r;
-    const bool wl = live && r < TR;
-    const uint32_t wo = wl ? uint32_t(row) * wpitch + uint32_t(q) * 16 : kOOB;
-    const uint32_t so = wl ? uint32_t(row) * spitch : kOOB;
+    // rows past N fall outside the buffer; so do operand rows past TR
+    constexpr int NH = wl_halves<WF>();
+    uint32_t wo[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int rr = wl_row<WF>(lane, h);
+      wo[h] = live && rr < TR ? uint32_t(tile * TR + rr) * wpitch + wl_byte<WF>(lane, h) : kOOB;
+    }
+    const uint32_t so = live && r < TR ? uint32_t(tile * TR + r) * spitch : kOOB;
     const int hrow = uniform(s_row[m]);
     const uint32_t xo = (live && r == 0) ? uint32_t(hrow) * uint32_t(a.ldx) * 2u : kOOB;  // one token column
 #pragma unroll
@@ -104,14 +109,11 @@ __device__ __forceinline__ void stream_combine_xs(const PersistArgs &a, float *s
       const int kb = wave + c * WAVES;
 #pragma unroll
       for (int d = 0; d < WFrag<WF, 1>::DL; ++d)
-        R.f[c].w[0][d] = bld16(wres, wo + uint32_t(kb) * (WFrag<WF, 1>::DL * 64) + d * 64);
+        R.f[c].w[0][d] = wl_load<WF>(wres, wo[d % NH] + uint32_t(kb) * wl_kbytes<WF>() + wl_dcol<WF>(d));
       if constexpr (WF != WF_BF16) R.f[c].s[0] = bld8(sres, so + uint32_t(kb) * 8);
 #pragma unroll
       for (int dx = 0; dx < DX; ++dx) {
-        const int ko = WF == WF_BF16  ? kb * KB + 32 * dx + 8 * q
-                       : WF == WF_FP4 ? kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3)
-                                      : kb * KB + 32 * q + 8 * dx;
-        R.xb[c][dx] = bld16(xres, xo + uint32_t(ko) * 2u);
+        R.xb[c][dx] = bld16(xres, xo + uint32_t(kb * KB + wl_xk<WF>(dx, q)) * 2u);
       }
     }
   };
@@ -126,15 +128,17 @@ __device__ __forceinline__ void stream_combine_xs(const PersistArgs &a, float *s
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
+      WFrag<WF, 1> fc = R.f[c];
+      wfrag_fix(fc);
       if constexpr (WF == WF_BF16) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) acc = mfma16(as_bf16x8(R.f[c].w[0][d]), as_bf16x8(R.xb[c][d]), acc);
+        for (int d = 0; d < 4; ++d) acc = mfma16(as_bf16x8(fc.w[0][d]), as_bf16x8(R.xb[c][d]), acc);
       } else if constexpr (WF == WF_FP4) {
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
-          const float sc = e8m0_to_f32((R.f[c].s[0][d] >> (8 * q)) & 0xffu);
+          const float sc = e8m0_to_f32(wl_mx_scale<WF>(fc.s[0], d, q));
 #pragma unroll
-          for (int mm = 0; mm < 4; ++mm) acc = mfma16(fp4x8_to_bf16x8(R.f[c].w[0][d][mm], sc), as_bf16x8(R.xb[c][4 * d + mm]), acc);
+          for (int mm = 0; mm < 4; ++mm) acc = mfma16(fp4x8_to_bf16x8(fc.w[0][d][mm], sc), as_bf16x8(R.xb[c][4 * d + mm]), acc);
         }
       } else {
 #pragma unroll

@@ -6,8 +6,9 @@
 // Work split: one workgroup of WAVES waves owns 16 weight rows (per matrix)
 // and up to 16*NT tokens; the waves take interleaved k-blocks of the
 // contraction axis and their partial tiles are summed in LDS.  Weights stream
-// from HBM straight into MFMA A-operand registers.  In one load instruction
-// the four lanes of a row read 64 contiguous bytes, 16 rows at once.
+// from HBM straight into MFMA A-operand registers (bf16 and MXFP4: read as
+// whole 128-byte lines and moved into the operand layout in registers, see
+// wfrag_fix).
 // Activations are bf16 and are read from L2 (small, shared by every weight
 // tile).
 //
@@ -23,14 +24,15 @@
 //   A: lane l holds A[l%16][8*(l/16) .. +7], B: lane l holds B[8*(l/16) .. +7][l%16],
 //   D: lane l holds D[4*(l/16) + v][l%16], v = 0..3.
 //
-// k-block = DL 16-byte loads per lane (4 lanes per row):
-//   bf16: 256 bytes of a row = 128 elements; load d (0..3) gives lane (r, q)
-//         elements 32d + 8q .. +7 -- exactly its A operand of MFMA d.
-//   FP4 : 128 bytes of a row = 256 elements; load d (0..1) gives lane (r, q)
-//         the 32 elements 128d + 32q .. +31 (one E8M0 block); MFMA (d, m),
-//         m = 0..3, takes elements 128d + 32q + 8m .. +7.  The 8 scale bytes of
-//         the k-block come in one 8-byte load; lane q uses byte 4d + q.
-// The activations are read with the same index map, so each MFMA pairs equal k.
+// k-block = DL 16-byte loads per lane:
+//   bf16: 256 bytes of a row = 128 elements (two lines, four loads);
+//   FP4 : 128 bytes of a row = 256 elements (one line, two loads); after
+//         wfrag_fix register a of lane (r, q) holds E8M0 block 2q + a, and
+//         MFMA (a, m), m = 0..3, takes its elements 8m .. 8m+7.  The 8 scale
+//         bytes of the k-block come in one 8-byte load per row;
+//   NVFP4: 64 bytes of a row = 128 elements (one load in the operand layout).
+// The activations are read with the same element map (wl_xk), so each MFMA
+// pairs equal k.
 #pragma once
 
 #include "ft_internal.hpp"
@@ -56,6 +58,80 @@ struct WFrag {
   u32x4 w[MATS][DL];
   u32x2 s[MATS];
 };
+
+// ---- weight loads by whole 128-byte lines (bf16 and MXFP4)
+//
+// In the A-operand layout one load reads 64 bytes of each of 16 rows, half of every line it
+// touches.  Instead load d of a k-block reads tile row 8 (d & 1) + (lane & 7), bytes
+// 128 (d >> 1) + 16 (lane >> 3) .. +15 of the k-block, and wfrag_fix moves the data into the operand
+// layout (for each pair of loads a lane whose bit 3 is set swaps in the partner half through a DPP
+// rotation by 8 lanes).  Afterwards register d + a (a = 0, 1) holds at lane (r, q) row r, bytes
+// 128 (d >> 1) + 32 q + 16 a .. +15 of the k-block: bf16 elements 64 (d >> 1) + 16 q + 8 a .. +7
+// (MFMA d + a); FP4 elements 64 q + 32 a .. +31 = E8M0 block 2q + a.  wl_xk gives the activations
+// the matching element map.  The decode kernels' weight loads (wl_load) also carry the
+// non-temporal bit: each weight byte is read once per call.  Measured on MI355X (decode layer
+// steps): whole lines with the bit 231 -> 216 us (bf16, 64 tokens), 158 -> 148 us (16 tokens),
+// 367 -> 342 us (MXFP4, 32 tokens); whole lines alone or the bit alone gained nothing or lost (with
+// half-line loads the bit made the line's second half come from HBM again).  A 1 GiB read probe
+// gave 5.96 TB/s in the operand pattern, 6.85 TB/s in whole lines.  NVFP4 k-blocks are half a line
+// and keep the operand layout and plain loads.
+template <int WF>
+constexpr bool wl_lines() { return WF != WF_NV4; }
+template <int WF>
+constexpr int wl_halves() { return wl_lines<WF>() ? 2 : 1; }
+// Tile row (0..15) that this lane reads in load d of a k-block, and the byte offset inside the k-block.
+template <int WF>
+__device__ __forceinline__ int wl_row(int lane, int d) { return wl_lines<WF>() ? 8 * (d & 1) + (lane & 7) : (lane & 15); }
+template <int WF>
+__device__ __forceinline__ uint32_t wl_byte(int lane, int d) {
+  return wl_lines<WF>() ? uint32_t(128 * (d >> 1) + 16 * (lane >> 3)) : uint32_t(64 * d + 16 * (lane >> 4));
+}
+// Offset of load d relative to load d % halves of the same rows.
+template <int WF>
+__device__ __forceinline__ uint32_t wl_dcol(int d) { return wl_lines<WF>() ? uint32_t(d >> 1) * 128u : uint32_t(d) * 64u; }
+template <int WF>
+constexpr uint32_t wl_kbytes() { return WFrag<WF, 1>::DL * 64; }
+__device__ __forceinline__ uint32_t dpp_ror8(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x128, 0xf, 0xf, true));  // row_ror:8
+}
+__device__ __forceinline__ void wl_swap(u32x4 &x0, u32x4 &x1) {
+  const bool up = (threadIdx.x & 8) != 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t a = x0[c], b = x1[c];
+    const uint32_t ra = dpp_ror8(a), rb = dpp_ror8(b);
+    x0[c] = up ? rb : a;
+    x1[c] = up ? b : ra;
+  }
+}
+template <int WF, int MATS>
+__device__ __forceinline__ void wfrag_fix(WFrag<WF, MATS> &f) {
+  if constexpr (wl_lines<WF>()) {
+#pragma unroll
+    for (int mt = 0; mt < MATS; ++mt)
+#pragma unroll
+      for (int d = 0; d < WFrag<WF, MATS>::DL; d += 2) wl_swap(f.w[mt][d], f.w[mt][d + 1]);
+  }
+}
+// Element offset inside the k-block of activation load dx of lane group q (bf16: MFMA dx; FP4:
+// MFMA dx = 4 a + mm; NVFP4: word dx of lane q's 32 elements).
+template <int WF>
+__device__ __forceinline__ int wl_xk(int dx, int q) {
+  return WF == WF_BF16 ? 64 * (dx >> 1) + 16 * q + 8 * (dx & 1)
+         : WF == WF_FP4 ? 32 * (dx >> 2) + 64 * q + 8 * (dx & 3)
+                        : 32 * q + 8 * dx;
+}
+// MXFP4: the E8M0 scale of the block in register a of lane group q (block 2q + a of the row's eight).
+template <int WF>
+__device__ __forceinline__ uint32_t wl_mx_scale(const u32x2 &s, int a, int q) {
+  return ((q >> 1) ? s[1] : s[0]) >> (8 * (2 * (q & 1) + a)) & 0xffu;
+}
+// A decode kernel's weight load: whole lines with the non-temporal bit, NVFP4 half lines without.
+template <int WF>
+__device__ __forceinline__ u32x4 wl_load(rsrc_t r, uint32_t off) {
+  if constexpr (wl_lines<WF>()) return bld16nt(r, off);
+  else return bld16(r, off);
+}
 
 // One 16-row x (16*NT)-token tile.  All WAVES*64 threads must call it.
 //  w0/s0, w1/s1 : weight (codes) and scale bases of matrix 0 and 1 (row 0).
@@ -101,7 +177,6 @@ __device__ __forceinline__ void stream_tile(const uint8_t *__restrict__ w0,
   // byte pitch of one weight row and of its scale row
   const uint32_t wpitch = (WF == WF_BF16) ? uint32_t(K) * 2 : uint32_t(K) / 2;
   const uint32_t spitch = uint32_t(K) / 32;
-  const int wrow = row0 + r;  // rows past N fall outside the buffer
   rsrc_t wres[MATS], sres[MATS];
   wres[0] = make_rsrc(w0, uint32_t(N) * wpitch);
   sres[0] = make_rsrc(s0, uint32_t(N) * spitch);
@@ -109,28 +184,29 @@ __device__ __forceinline__ void stream_tile(const uint8_t *__restrict__ w0,
     wres[MATS - 1] = make_rsrc(w1, uint32_t(N) * wpitch);
     sres[MATS - 1] = make_rsrc(s1, uint32_t(N) * spitch);
   }
-  const uint32_t wo = uint32_t(wrow) * wpitch + uint32_t(q) * 16;
-  const uint32_t so = uint32_t(wrow) * spitch;
+  // rows past N fall outside the buffer; the scales are those of the lane's own operand row r
+  const uint32_t so = uint32_t(row0 + r) * spitch;
 
   auto load_w = [&](int kb, WFrag<WF, MATS> &f) {
 #pragma unroll
     for (int mt = 0; mt < MATS; ++mt) {
 #pragma unroll
-      for (int d = 0; d < DL; ++d) f.w[mt][d] = bld16(wres[mt], wo + uint32_t(kb) * (DL * 64) + d * 64);
+      for (int d = 0; d < DL; ++d)
+        f.w[mt][d] = bld16(wres[mt], uint32_t(row0 + wl_row<WF>(lane, d)) * wpitch + uint32_t(kb) * wl_kbytes<WF>() +
+                                         wl_byte<WF>(lane, d));  // plain: a router's rows serve every token tile
       if constexpr (WF == WF_FP4) f.s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);
     }
   };
   // activation element offset of this lane's load dx of k-block kb
-  auto xoff = [&](int kb, int dx) {
-    return WF == WF_BF16 ? kb * KB + 32 * dx + 8 * q : kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3);
-  };
+  auto xoff = [&](int kb, int dx) { return kb * KB + wl_xk<WF>(dx, q); };
   auto load_x = [&](int kb, u32x4 (&xb)[NT][DX]) {
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int dx = 0; dx < DX; ++dx) xb[tt][dx] = bld16(xres, xo[tt] + uint32_t(xoff(kb, dx)) * 2u);
   };
-  auto compute = [&](const WFrag<WF, MATS> &f, const u32x4 (&xb)[NT][DX]) {
+  auto compute = [&](WFrag<WF, MATS> f, const u32x4 (&xb)[NT][DX]) {
+    wfrag_fix(f);
     if constexpr (WF == WF_BF16) {
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -144,7 +220,7 @@ __device__ __forceinline__ void stream_tile(const uint8_t *__restrict__ w0,
       for (int d = 0; d < 2; ++d) {
         float sc[MATS];
 #pragma unroll
-        for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32((f.s[mt][d] >> (8 * q)) & 0xffu);
+        for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32(wl_mx_scale<WF>(f.s[mt], d, q));
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
           bf16x8 a[MATS];

@@ -195,7 +195,10 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
       wres[MATS - 1] = make_rsrc(blob + a.off_w1, wbytes);
       sres[MATS - 1] = make_rsrc(blob + a.off_s1, sbytes);
     }
-    const uint32_t wo = uint32_t(tile * 16 + r) * wpitch + uint32_t(q) * 16;
+    constexpr int NH = wl_halves<WF>();
+    uint32_t wo[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) wo[h] = uint32_t(tile * 16 + wl_row<WF>(lane, h)) * wpitch + wl_byte<WF>(lane, h);
     const uint32_t so = uint32_t(tile * 16 + r) * spitch;
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
@@ -203,7 +206,8 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
 #pragma unroll
       for (int mt = 0; mt < MATS; ++mt) {
 #pragma unroll
-        for (int d = 0; d < DL; ++d) R.f[c].w[mt][d] = bld16(wres[mt], wo + uint32_t(kb) * (DL * 64) + d * 64);
+        for (int d = 0; d < DL; ++d)
+          R.f[c].w[mt][d] = wl_load<WF>(wres[mt], wo[d % NH] + uint32_t(kb) * wl_kbytes<WF>() + wl_dcol<WF>(d));
         if constexpr (WF == WF_FP4) R.f[c].s[mt] = bld8(sres[mt], so + uint32_t(kb) * 8);
       }
     }
@@ -225,8 +229,7 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
       const int kb = wave + c * WAVES;
 #pragma unroll
       for (int dx = 0; dx < DX; ++dx) {
-        const int ko = WF == WF_BF16 ? kb * KB + 32 * dx + 8 * q : kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3);
-        xb[c][dx] = bld16(xres, xo + uint32_t(ko) * 2u);
+        xb[c][dx] = bld16(xres, xo + uint32_t(kb * KB + wl_xk<WF>(dx, q)) * 2u);
       }
     }
   };
@@ -243,7 +246,8 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
     for (int mt = 0; mt < MATS; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
-      const WFrag<WF, MATS> &f = cur.f[c];
+      WFrag<WF, MATS> f = cur.f[c];
+      wfrag_fix(f);
       if constexpr (WF == WF_BF16) {
 #pragma unroll
         for (int d = 0; d < 4; ++d)
@@ -254,7 +258,7 @@ __device__ __forceinline__ void stream_persist(const PersistArgs &a, float *s_re
         for (int d = 0; d < 2; ++d) {
           float sc[MATS];
 #pragma unroll
-          for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32((f.s[mt][d] >> (8 * q)) & 0xffu);
+          for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32(wl_mx_scale<WF>(f.s[mt], d, q));
 #pragma unroll
           for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
@@ -491,14 +495,18 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
       wres[1] = wres[0];
       sres[1] = sres[0];
     }
-    uint32_t wo[MATS], so[MATS];
+    // rows past N fall outside the buffer (zeros, no traffic); so do operand rows past TR
+    constexpr int NH = wl_halves<WF>();  // row halves of the whole-line loads (d & 1)
+    uint32_t wo[MATS][NH], so[MATS];
 #pragma unroll
     for (int mt = 0; mt < MATS; ++mt) {
-      // rows past N fall outside the buffer (zeros, no traffic); so do operand rows past TR
-      const int row = tile * TR * RT + (GLU ? 0 : 16 * mt) + r;
-      const bool live = tile >= 0 && r < TR;
-      wo[mt] = live ? uint32_t(row) * wpitch + uint32_t(q) * 16 : kOOB;
-      so[mt] = live ? uint32_t(row) * spitch : kOOB;
+      const int row0 = tile * TR * RT + (GLU ? 0 : 16 * mt);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int rr = wl_row<WF>(lane, h);
+        wo[mt][h] = tile >= 0 && rr < TR ? uint32_t(row0 + rr) * wpitch + wl_byte<WF>(lane, h) : kOOB;
+      }
+      so[mt] = tile >= 0 && r < TR ? uint32_t(row0 + r) * spitch : kOOB;
     }
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
@@ -506,7 +514,8 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
 #pragma unroll
       for (int mt = 0; mt < MATS; ++mt) {
 #pragma unroll
-        for (int d = 0; d < DL; ++d) f[c].w[mt][d] = bld16(wres[mt], wo[mt] + uint32_t(kb) * (DL * 64) + d * 64);
+        for (int d = 0; d < DL; ++d)
+          f[c].w[mt][d] = wl_load<WF>(wres[mt], wo[mt][d % NH] + uint32_t(kb) * wl_kbytes<WF>() + wl_dcol<WF>(d));
         if constexpr (WF != WF_BF16) f[c].s[mt] = bld8(sres[mt], so[mt] + uint32_t(kb) * 8);  // 8 blocks
       }
     }
@@ -526,10 +535,7 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
       const int kb = wave + c * WAVES;
 #pragma unroll
       for (int dx = 0; dx < DX; ++dx) {
-        const int ko = WF == WF_BF16  ? kb * KB + 32 * dx + 8 * q
-                       : WF == WF_FP4 ? kb * KB + 128 * (dx >> 2) + 32 * q + 8 * (dx & 3)
-                                      : kb * KB + 32 * q + 8 * dx;
-        xb[c][dx] = bld16(xres, xo + uint32_t(ko) * 2u);
+        xb[c][dx] = bld16(xres, xo + uint32_t(kb * KB + wl_xk<WF>(dx, q)) * 2u);
       }
     }
   };
@@ -546,22 +552,24 @@ __device__ __forceinline__ void stream_persist_xs(const PersistArgs &a, float *s
     for (int mt = 0; mt < MATS; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KPW; ++c) {
+      WFrag<WF, MATS> fc = f[c];
+      wfrag_fix(fc);
       if constexpr (WF == WF_BF16) {
 #pragma unroll
         for (int d = 0; d < 4; ++d)
 #pragma unroll
-          for (int mt = 0; mt < MATS; ++mt) acc[mt] = mfma16(as_bf16x8(f[c].w[mt][d]), as_bf16x8(xcur[c][d]), acc[mt]);
+          for (int mt = 0; mt < MATS; ++mt) acc[mt] = mfma16(as_bf16x8(fc.w[mt][d]), as_bf16x8(xcur[c][d]), acc[mt]);
       } else if constexpr (WF == WF_FP4) {
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
           float sc[MATS];
 #pragma unroll
-          for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32((f[c].s[mt][d] >> (8 * q)) & 0xffu);
+          for (int mt = 0; mt < MATS; ++mt) sc[mt] = e8m0_to_f32(wl_mx_scale<WF>(fc.s[mt], d, q));
 #pragma unroll
           for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
             for (int mt = 0; mt < MATS; ++mt)
-              acc[mt] = mfma16(fp4x8_to_bf16x8(f[c].w[mt][d][mm], sc[mt]), as_bf16x8(xcur[c][4 * d + mm]), acc[mt]);
+              acc[mt] = mfma16(fp4x8_to_bf16x8(fc.w[mt][d][mm], sc[mt]), as_bf16x8(xcur[c][4 * d + mm]), acc[mt]);
         }
       } else {
         // NVFP4: lane (r, q) holds elements 32q .. 32q+31 of the k-block (16-element

@@ -125,6 +125,10 @@ def ft_noalloc_scratch_bytes() -> int:
     return int(_lib.lib().ft_noalloc_scratch_bytes())
 
 
+def ft_read_checksum(buf, nbytes: int, sink, stream=None) -> None:
+    _check(_lib.lib().ft_read_checksum(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
+
+
 def ft_cpu_expert_ffn(layout: ExpertLayout, blob, x, n: int, y, n_threads: int = 0) -> None:
     """Host pointers (numpy arrays or pinned tensors) for blob, x (bf16 bits) and y (float32)."""
     _check(_lib.lib().ft_cpu_expert_ffn(C.byref(layout), _ptr(blob), _ptr(x), n, _ptr(y), n_threads))

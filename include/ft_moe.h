@@ -258,6 +258,21 @@ ft_status ft_moe_grouped_ffn_noalloc(const ft_expert_layout *L, const void *slot
 size_t ft_noalloc_scratch_bytes(void);
 
 /*
+ * ft_read_checksum -- *sink ^= the XOR of the 32-bit words of buf[0 .. bytes),
+ * on the device, the buffer read once in whole 128-byte lines.  It is the
+ * plain read that bounds a weight stream (the pages' decode reads every
+ * activated expert's weights once per token: FreeToken 290b model page, "Cómo
+ * gestiona FreeToken el prellenado y la decodificación"), timed beside the
+ * decode kernels, and a check that a copied expert blob arrived whole.
+ * buf: device memory, 16-byte aligned; bytes a multiple of 16, at most 2^31
+ * (larger buffers: checksum slices and XOR the results); sink: 4 device
+ * bytes, not cleared (start it at 0).  The result does not depend on the
+ * launch shape.  Errors before anything is enqueued: FT_EINVAL (NULL or
+ * misaligned pointer, bytes not a multiple of 16), FT_ENOTSUP (above 2 GiB).
+ */
+ft_status ft_read_checksum(const void *buf, uint64_t bytes, uint32_t *sink, hipStream_t stream);
+
+/*
  * Instruction paths of the host expert kernel (ft_cpu_expert_ffn,
  * ft_cpu_miss_rows).  Both compute the same products; they differ only in the
  * order of fp32 additions.

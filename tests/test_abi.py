@@ -146,6 +146,18 @@ def test_combine_validation():
     assert _err(f, 8, 16, 16, None, 2, 2, 64, 1, 16, stream=0) == -1        # misaligned y_rows
 
 
+def test_read_checksum_validation():
+    from expert_cached_ffn_amd import ops
+    f = ops.ft_read_checksum
+    assert _err(f, 16, 24, 16, stream=0) == -1                 # bytes not a multiple of 16
+    assert _err(f, 16, 32, None, stream=0) == -1               # no sink
+    assert _err(f, 16, 32, 18, stream=0) == -1                 # misaligned sink
+    assert _err(f, 8, 32, 16, stream=0) == -1                  # misaligned buffer
+    assert _err(f, None, 32, 16, stream=0) == -1               # no buffer
+    assert _err(f, 16, (1 << 31) + 16, 16, stream=0) == -2     # above 2 GiB
+    f(None, 0, 16, stream=0)                                   # nothing to read: FT_OK, nothing enqueued
+
+
 def test_cache_validation():
     from expert_cached_ffn_amd import ops, _lib
     L = ops.ft_expert_layout_init(1, 128, 128)
