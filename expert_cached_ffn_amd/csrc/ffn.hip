@@ -1147,8 +1147,15 @@ extern "C" ft_status ft_moe_layer(const ft_expert_layout *L, const void *slot_po
   const bool fused = gemv || (T <= kRouteMaxT && exact && shapes && E <= kRouteMaxE && k <= kFusedMaxK &&
                               T * k <= kRouteMaxRows && w1 >= T);
   if (!fused) {
-    // route + permute, the grouped FFN and the combine, one call after the other
-    st = route_permute_counted_covers(T, k, E)
+    // route + permute, the grouped FFN and the combine, one call after the other (the router split
+    // over the hidden axis when it covers the batch: its partial planes use the FFN's workspace, free
+    // until the gate/up stage; FTMOE_ROUTER_SPLIT = "0" keeps the one-pass router)
+    static const char *split_env = getenv("FTMOE_ROUTER_SPLIT");
+    const int parts = (split_env && split_env[0] == '0') ? 0 : router_split_parts(x, x_dtype, w_router, T, H, E, k, ws_bytes);
+    st = parts > 0 ? route_permute_split(x, w_router, logits, T, H, E, k, gating, renormalize, topk_ids, topk_w,
+                                         expert_offsets, sorted_rows, row_pos, parts, ws, wait_words + kLayerRouteWord,
+                                         stream)
+         : route_permute_counted_covers(T, k, E)
              ? route_permute_counted(x, x_dtype, w_router, logits, T, H, E, k, gating, renormalize, topk_ids, topk_w,
                                      expert_offsets, sorted_rows, row_pos, wait_words + kLayerRouteWord, stream)
              : ft_moe_route_permute(x, x_dtype, w_router, logits, T, H, E, k, gating, renormalize, topk_ids, topk_w,

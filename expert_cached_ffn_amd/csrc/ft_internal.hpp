@@ -43,6 +43,12 @@ ft_status route_logits(const void *x, int32_t x_dtype, const void *w_router, flo
 // most 1024 routed rows over at most 256 experts; `done` is a zeroed counter, left zero.  Arguments
 // are those of ft_moe_route_permute, checked by the caller.
 bool route_permute_counted_covers(int T, int k, int E);
+int router_split_parts(const void *x, int32_t x_dtype, const void *w_router, int T, int H, int E, int k,
+                       size_t ws_bytes);
+ft_status route_permute_split(const void *x, const void *w_router, float *logits, int32_t T, int32_t H, int32_t E,
+                              int32_t k, int32_t gating, int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                              int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos, int parts, void *ws,
+                              uint32_t *done, hipStream_t stream);
 ft_status route_permute_counted(const void *x, int32_t x_dtype, const void *w_router, float *logits, int32_t T,
                                 int32_t H, int32_t E, int32_t k, int32_t gating, int32_t renormalize,
                                 int32_t *topk_ids, float *topk_w, int32_t *expert_offsets, int32_t *sorted_rows,

@@ -78,6 +78,58 @@ __global__ __launch_bounds__(64) void router_logits_gemv_bf16(const uint16_t *__
   }
 }
 
+// bf16, split over the hidden axis (decode batches of 5+ tokens in the layer call): workgroup
+// (expert tile, token tile, part p) multiplies k-blocks p*kpp .. p*kpp + kpp - 1 of its 16 experts x
+// 16 tokens, its waves taking the k-blocks in turn, and writes the partial tile to part[p][t][e];
+// the routing tail adds the parts in p order (no atomics, a fixed order).  The unsplit tile kernel
+// streams its 16 experts' whole rows through one compute unit per tile: 32 workgroups at 64 tokens
+// and 128 experts (a 128 KiB share each), 8 at 16 tokens.
+constexpr int kSplitWaves = 4;
+
+__global__ __launch_bounds__(kSplitWaves * 64) void router_logits_split_bf16(const uint16_t *__restrict__ x,
+                                                                            const uint16_t *__restrict__ wr,
+                                                                            float *__restrict__ part, int T,
+                                                                            int H, int E, int kpp) {
+  __shared__ f32x4 s_red[kSplitWaves][64];
+  const int et = blockIdx.x, tt = blockIdx.y, p = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  // rows past E and tokens past T get an out-of-range offset: zeros, no traffic
+  const rsrc_t wres = make_rsrc(wr, uint32_t(E) * uint32_t(H) * 2u);
+  const rsrc_t xres = make_rsrc(x, uint32_t(T) * uint32_t(H) * 2u);
+  const int e = et * 16 + r, t = tt * 16 + r;
+  const uint32_t wo = e < E ? uint32_t(e) * uint32_t(H) * 2u : kOOB;
+  const uint32_t xo = t < T ? uint32_t(t) * uint32_t(H) * 2u : kOOB;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kb = p * kpp + wave; kb < (p + 1) * kpp; kb += kSplitWaves) {
+    // lane (r, q) holds elements 32d + 8q .. +7 of the k-block for MFMA d (A: expert rows, B: tokens)
+    u32x4 wa[4], xb[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t off = uint32_t(kb * 128 + 32 * d + 8 * q) * 2u;
+      wa[d] = bld16(wres, wo + off);
+      xb[d] = bld16(xres, xo + off);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) acc = mfma16(as_bf16x8(wa[d]), as_bf16x8(xb[d]), acc);
+  }
+  s_red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 sum = s_red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kSplitWaves; ++w) sum += s_red[w][lane];  // wave order
+    // lane holds D[4q + v][r]: expert et*16 + 4q + v, token tt*16 + r
+    const int tok = tt * 16 + r;
+    if (tok < T) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ee = et * 16 + 4 * q + v;
+        if (ee < E) part[(int64_t(p) * T + tok) * E + ee] = sum[v];
+      }
+    }
+  }
+}
+
 // fp32: one thread per (token, expert).
 __global__ __launch_bounds__(256) void router_logits_f32(const float *__restrict__ x,
                                                          const float *__restrict__ wr,
@@ -116,14 +168,63 @@ struct FusedRouteArgs {
   int32_t *ids;
   float *w;
   int32_t *offsets, *sorted_rows, *row_pos;
+  // non-NULL: the logits are the sum of nparts (2, 4, 8 or 16) partial planes parts[p][T][E], added in
+  // p order by the token's wave, which also writes the sums to logits_out
+  const float *parts;
+  int nparts;
+  float *logits_out;
 };
+
+// Token t's logits as the sum of NP partial planes: every load in flight before the first add.
+template <int VPL, int NP>
+__device__ __forceinline__ void sum_parts(const FusedRouteArgs &a, int t, float (&v)[VPL]) {
+  const int lane = threadIdx.x & 63;
+  float pv[NP][VPL];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      pv[p][i] = a.parts[(int64_t(p) * a.T + t) * a.E + (e < a.E ? e : 0)];
+    }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    float sum = pv[0][i];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) sum += pv[p][i];
+    const int e = lane + 64 * i;
+    if (e < a.E) a.logits_out[int64_t(t) * a.E + e] = sum;
+    v[i] = sum;
+  }
+}
+
+// Top-k and gating of token t (one wave), from the logits or from their partial sums.
+template <int VPL>
+__device__ __forceinline__ void route_token(const FusedRouteArgs &a, int t, int32_t *ids, float *w, int32_t *ids_lds) {
+  // (the split router covers E <= 256: four logits per lane at most)
+  if (VPL > 4 || a.parts == nullptr) {
+    topk_token<VPL>(a.logits, t, a.E, a.k, a.gating, a.renorm, ids, w, ids_lds);
+    return;
+  }
+  float v[1][VPL];
+  if constexpr (VPL <= 4) {
+    switch (a.nparts) {
+      case 2: sum_parts<VPL, 2>(a, t, v[0]); break;
+      case 4: sum_parts<VPL, 4>(a, t, v[0]); break;
+      case 8: sum_parts<VPL, 8>(a, t, v[0]); break;
+      default: sum_parts<VPL, 16>(a, t, v[0]); break;
+    }
+  }
+  const int tt[1] = {t};
+  topk_values<VPL, 1>(v, tt, 1, a.E, a.k, a.gating, a.renorm, ids, w, ids_lds);
+}
 
 // Top-k, gating and the permutation of all T tokens by one workgroup.
 template <int VPL>
 __device__ __forceinline__ void route_tail(const FusedRouteArgs &a, int32_t *s_ids, int *s_cnt, int *s_cc,
                                            int *s_tmp) {
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int t = wave; t < a.T; t += nw) topk_token<VPL>(a.logits, t, a.E, a.k, a.gating, a.renorm, a.ids, a.w, s_ids);
+  for (int t = wave; t < a.T; t += nw) route_token<VPL>(a, t, a.ids, a.w, s_ids);
   __syncthreads();
   const int R = a.T * a.k;
   if (R <= 64) {
@@ -170,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void topk_permute_kernel(FusedRouteArgs a,
   const int tid = threadIdx.x, wave = tid >> 6;
   const int t0 = int(blockIdx.x) * NW, nt = min(NW, a.T - t0);
   const int R = a.T * a.k;
-  if (wave < nt) topk_token<VPL>(a.logits, t0 + wave, a.E, a.k, a.gating, a.renorm, nullptr, a.w, s_ids);
+  if (wave < nt) route_token<VPL>(a, t0 + wave, nullptr, a.w, s_ids);
   __syncthreads();
   const rsrc_t ids = make_rsrc(a.ids, uint32_t(R) * 4u);
   for (int p = t0 * a.k + tid; p < (t0 + nt) * a.k; p += 64 * NW)
@@ -185,6 +286,76 @@ __global__ __launch_bounds__(64 * NW) void topk_permute_kernel(FusedRouteArgs a,
   __syncthreads();
   permute_chunks(s_ids, R, a.E, s_cc, s_seg, s_tmp, a.offsets, a.sorted_rows, a.row_pos);
   if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Parts of the split router for a layer call (0: not split).  Up to 4 tokens the one-wave-per-expert
+// router serves; the split needs bf16 tokens, H a multiple of 128, a routing tail that covers the
+// batch and room for the partial planes in the workspace.
+int router_split_parts(const void *x, int32_t x_dtype, const void *w_router, int T, int H, int E, int k,
+                       size_t ws_bytes) {
+  if (w_router == nullptr || x == nullptr || x_dtype != FT_BF16 || T <= 4 || H % 128 != 0 || E > kMaxE || k > E ||
+      int64_t(T) * k > kChunkPermMaxRows || E > kChunkPermMaxE)
+    return 0;
+  if (!(T <= kFusedMaxT && int64_t(T) * k <= kFusedMaxRows) && !route_permute_counted_covers(T, k, E)) return 0;
+  // parts: the fewest that give 128 workgroups (one per 2 CUs), a power of two dividing the k-blocks
+  const int nkb = H / 128, base = cdiv(E, 16) * cdiv(T, 16);
+  int P = 1;
+  while (P < 16 && P < nkb && base * P < 128 && nkb % (2 * P) == 0) P *= 2;
+  if (P == 1 || size_t(P) * size_t(T) * size_t(E) * 4u > ws_bytes) return 0;
+  return P;
+}
+
+// The split router (partial planes in ws), then top-k, gating and the permutation in one launch: the
+// one-workgroup tail up to 16 tokens, the grid-wide top-k with the counted sort past that.
+ft_status route_permute_split(const void *x, const void *w_router, float *logits, int32_t T, int32_t H, int32_t E,
+                              int32_t k, int32_t gating, int32_t renormalize, int32_t *topk_ids, float *topk_w,
+                              int32_t *expert_offsets, int32_t *sorted_rows, int32_t *row_pos, int parts, void *ws,
+                              uint32_t *done, hipStream_t stream) {
+  const ft_status st = route_logits(x, FT_BF16, w_router, logits, T, H, E, k, gating, topk_ids, topk_w, stream, false);
+  if (st != FT_OK) return st;
+  float *part = static_cast<float *>(ws);
+  const int nkb = H / 128;
+  hipLaunchKernelGGL(router_logits_split_bf16, dim3(unsigned(cdiv(E, 16)), unsigned(cdiv(T, 16)), unsigned(parts)),
+                     dim3(kSplitWaves * 64), 0, stream, static_cast<const uint16_t *>(x),
+                     static_cast<const uint16_t *>(w_router), part, T, H, E, nkb / parts);
+  FT_LAUNCHED("router_logits_split_bf16");
+  FusedRouteArgs a{};
+  a.logits = logits;
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.gating = gating;
+  a.renorm = renormalize ? 1 : 0;
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.offsets = expert_offsets;
+  a.sorted_rows = sorted_rows;
+  a.row_pos = row_pos;
+  a.parts = part;
+  a.nparts = parts;
+  a.logits_out = logits;
+  const int R = T * k, vpl = cdiv(E, 64);
+  if (T <= kFusedMaxT && R <= kFusedMaxRows) {
+    const dim3 blk(R <= 64 ? 64 * T : 1024);
+    if (vpl <= 2) hipLaunchKernelGGL(route_tail_kernel<2>, dim3(1), blk, 0, stream, a);
+    else if (vpl <= 4) hipLaunchKernelGGL(route_tail_kernel<4>, dim3(1), blk, 0, stream, a);
+    else hipLaunchKernelGGL(route_tail_kernel<16>, dim3(1), blk, 0, stream, a);
+    FT_LAUNCHED("route_tail_kernel");
+  } else {
+#define FT_TOPK_PERM(V, NW) \
+  hipLaunchKernelGGL((topk_permute_kernel<V, NW>), dim3(unsigned(cdiv(T, NW))), dim3(64 * NW), 0, stream, a, done)
+    if (R <= 512) {
+      if (vpl <= 2) FT_TOPK_PERM(2, 8);
+      else FT_TOPK_PERM(4, 8);
+    } else {
+      if (vpl <= 2) FT_TOPK_PERM(2, 16);
+      else FT_TOPK_PERM(4, 16);
+    }
+#undef FT_TOPK_PERM
+    FT_LAUNCHED("topk_permute_kernel");
+  }
+  clear_error();
+  return FT_OK;
 }
 
 bool route_permute_counted_covers(int T, int k, int E) {
