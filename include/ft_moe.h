@@ -385,7 +385,10 @@ ft_status ft_moe_combine(const float *y_rows, const float *topk_w, const int32_t
  * calls make the three calls in turn (y_rows / y_shared written as there);
  * with 17 or more tokens, at most 1024 routed rows and E <= 256, the routing
  * after the router is one launch: top-k over the grid, the permutation by the
- * workgroup that finishes last.
+ * workgroup that finishes last.  With 5 to 64 tokens, bf16 tokens and
+ * E <= 256 the router's logits are computed in parts over H (partial sums
+ * held at the start of the steps' workspace until the routing launch adds
+ * them, in a fixed order, and writes logits).
  * An expert whose slot is negative (FT_SLOT_SKIP included) or >= n_slots
  * gives NaN outputs for the tokens that picked it.
  * Arguments: as for the three calls (x, x_dtype, w_router, logits, T, E, k,
